@@ -1,0 +1,357 @@
+"""Pins for the oracle's number formats and codecs (CPU only).
+
+Each test checks the oracle against something other than itself: a library
+conversion routine, a hand-derived fixture under tests/golden/, an exhaustive
+closed form, or brute force.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ----------------------------------------------------------------- binary16 / bfloat16
+def test_f16_decode_exhaustive_matches_numpy():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = bits.view(np.float16).astype(np.float64)
+    got = np.array([O.f16_to_f64(int(b)) for b in bits])
+    finite = np.isfinite(ref)
+    assert np.array_equal(got[finite], ref[finite])
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    assert np.array_equal(np.isinf(got), np.isinf(ref))
+
+
+def test_f16_encode_matches_numpy_rne():
+    g = np.random.default_rng(7)
+    vals = np.concatenate([
+        g.standard_normal(4000) * 0.02,
+        g.standard_normal(2000) * 1e-6,  # subnormal range
+        g.uniform(-70000, 70000, 2000),  # includes overflow
+        # exact ties: 1 + 2^-11 (to even -> 1), 1 + 3*2^-11 (-> 1 + 2^-9), subnormal ties
+        np.array([1 + 2.0**-11, 1 + 3 * 2.0**-11, 2.0**-25, 3 * 2.0**-25, 65504.0, 65519.99, 65520.0, -0.0, 0.0]),
+    ])
+    for v in vals:
+        ref = int(np.float64(v).astype(np.float16).view(np.uint16))
+        assert O.f64_to_f16(float(v)) == ref, v
+
+
+def test_bf16_decode_matches_torch():
+    bits = np.arange(0, 65536, 97, dtype=np.uint32).astype(np.uint16)
+    ref = torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16).double().numpy()
+    got = np.array([O.bf16_to_f64(int(b)) for b in bits])
+    fin = np.isfinite(ref)
+    assert np.array_equal(got[fin], ref[fin])
+
+
+# ----------------------------------------------------------------- grid
+def test_splitmix64_published_first_output():
+    # splitmix64 from state 0 yields 0xE220A8397B1DCDAF first (the value quoted
+    # with the generator's public-domain reference implementation).
+    assert O.splitmix64_sequence(0, 1)[0] == 0xE220A8397B1DCDAF
+
+
+def test_grid_shape_distinct_and_balanced():
+    lv = O.grid_levels()
+    assert lv.shape == (256, 8)
+    assert set(np.unique(lv)) <= {0, 1, 2}
+    assert len({tuple(r) for r in lv}) == 256
+    counts = np.bincount(lv.ravel(), minlength=3)
+    # 2048 uniform draws over 3 levels: each count within 6 sigma of 682.7
+    assert np.all(np.abs(counts - 2048 / 3) < 6 * np.sqrt(2048 * 2 / 9))
+    assert np.array_equal(lv, O.grid_levels())  # deterministic
+
+
+# ----------------------------------------------------------------- CB2
+def _cb2_block(entries, d_bits=0x3C00):
+    """One 256-wide CB2 row: entries = list of (j, g, idx, code, s)."""
+    codes = np.zeros(64, dtype=np.uint8)
+    aux = np.zeros(8, dtype=np.uint64)
+    scale = {}
+    for j, g, idx, code, s in entries:
+        codes[8 * j + g] = idx
+        aux[j] |= np.uint64(code) << np.uint64(7 * g)
+        scale[j] = s
+    for j in range(8):
+        a = int(aux[j]) | (scale.get(j, 0) << 28)
+        codes[8 * j + 4: 8 * j + 8] = np.frombuffer(np.uint32(a).tobytes(), dtype=np.uint8)
+    d = np.array([d_bits], dtype=np.uint16)
+    return np.concatenate([codes, d.view(np.uint8)])
+
+
+def test_cb2_layout_golden():
+    fx = json.load(open(os.path.join(GOLDEN, "cb2_layout.json")))
+    lv = O.grid_levels()
+    entries = [(c["j"], c["g"], c["idx"], c["code"], c["s"]) for c in fx["cases"]]
+    packed = _cb2_block(entries, int(fx["d_bits"], 16))
+    # the first case's bytes, as written out by hand in the fixture
+    assert packed[24:32].tobytes() == bytes([0, 0, 7, 0]) + (0x50014000).to_bytes(4, "little")
+    w = O.cb2_dequantize(packed, 1, 256)[0]
+    for c in fx["cases"]:
+        for k in range(8):
+            K = 32 * c["j"] + 8 * c["g"] + k
+            mag = c["scale"] * (2 * int(lv[c["idx"], k]) + 1)
+            assert w[K] == (-mag if c["neg"][k] else mag), (c, k)
+
+
+def test_cb2_sign_rule_exhaustive():
+    """All 128 codes: bits 0..6 explicit, bit 7 = parity, so negatives are even."""
+    lv = O.grid_levels()
+    for code in range(128):
+        packed = _cb2_block([(0, 0, 0, code, 0)])
+        w = O.cb2_dequantize(packed, 1, 256)[0][:8]
+        neg = (w < 0).astype(int)
+        assert list(neg[:7]) == [(code >> k) & 1 for k in range(7)]
+        assert neg.sum() % 2 == 0
+        assert np.array_equal(np.abs(w), 2 * lv[0].astype(np.float32) + 1)
+
+
+def test_cb2_dequant_closed_form_all_entries_and_scales():
+    """d = 1: every (entry, scale) decodes to (2s+1) * (2*level+1)."""
+    lv = O.grid_levels()
+    for s in range(16):
+        rows = []
+        for e0 in range(0, 256, 32):
+            ent = [(j, g, e0 + 4 * j + g, 0, s) for j in range(8) for g in range(4)]
+            rows.append(_cb2_block(ent))
+        # 8 rows x 256 cols: codes planes then d planes
+        codes = np.concatenate([r[:64] for r in rows])
+        ds = np.concatenate([r[64:] for r in rows])
+        w = O.cb2_dequantize(np.concatenate([codes, ds]), 8, 256)
+        for ri, e0 in enumerate(range(0, 256, 32)):
+            for j in range(8):
+                for g in range(4):
+                    e = e0 + 4 * j + g
+                    ref = (2 * s + 1) * (2 * lv[e].astype(np.float32) + 1)
+                    assert np.array_equal(w[ri, 32 * j + 8 * g: 32 * j + 8 * g + 8], ref)
+
+
+def canonical_cb2(rng, rows):
+    """Blocks that are exactly representable and whose every quantizer division
+    is exact: d normal in [2^-14, 2^-8]; one sub-block has s = 15; every
+    sub-block has a group whose grid entry holds a level-2 (magnitude 5)."""
+    lv = O.grid_levels()
+    has5 = np.flatnonzero((lv == 2).any(axis=1))
+    nb = 1
+    codes = np.zeros((rows, nb * 64), dtype=np.uint8)
+    dpl = np.zeros((rows, nb), dtype=np.uint16)
+    for r in range(rows):
+        e = int(rng.integers(-14, -8))
+        mant = int(rng.integers(0, 1024))
+        dpl[r, 0] = ((e + 15) << 10) | mant
+        svals = rng.integers(0, 16, 8)
+        svals[rng.integers(0, 8)] = 15
+        for j in range(8):
+            idx = rng.integers(0, 256, 4)
+            idx[rng.integers(0, 4)] = rng.choice(has5)
+            cd = rng.integers(0, 128, 4)
+            aux = int(svals[j]) << 28
+            for g in range(4):
+                aux |= int(cd[g]) << (7 * g)
+            codes[r, 8 * j: 8 * j + 4] = idx
+            codes[r, 8 * j + 4: 8 * j + 8] = np.frombuffer(np.uint32(aux).tobytes(), dtype=np.uint8)
+    return np.concatenate([codes.ravel(), dpl.ravel().view(np.uint8)])
+
+
+def test_cb2_roundtrip_canonical_is_identity():
+    rng = np.random.default_rng(1)
+    packed = canonical_cb2(rng, 64)
+    w = O.cb2_dequantize(packed, 64, 256)
+    again = O.cb2_quantize(w)
+    assert np.array_equal(again, packed)
+
+
+def _cb2_score_all(R, xneg, lv):
+    """Brute force: integer score of every (entry, even-parity sign pattern)."""
+    m = (2 * lv.astype(np.int64) + 1)  # [256, 8]
+    pats = np.array([[(c >> k) & 1 for k in range(7)] + [bin(c).count("1") & 1] for c in range(128)])
+    eps = np.where(pats == xneg[None, :], 1, -1)  # [128, 8]: +1 sign kept, -1 flipped
+    base = 4096 * m * m  # [256, 8]
+    cross = 2 * R[None, None, :] * m[:, None, :] * eps[None, :, :]  # [256,128,8]
+    return (base[:, None, :] - cross).sum(-1), pats
+
+
+def test_cb2_group_search_equals_brute_force():
+    """The parity-flip shortcut finds the minimum over all 256 x 128 choices."""
+    lv = O.grid_levels()
+    rng = np.random.default_rng(3)
+    for trial in range(12):
+        x = (rng.standard_normal(256) * 0.02).astype(np.float32)
+        packed = O.cb2_quantize(x[None, :])
+        codes, dpl = O.cb2_planes(packed, 1, 256)
+        d = np.float32(np.array([dpl[0]], dtype=np.uint16).view(np.float16)[0])
+        for j in range(8):
+            aux = int.from_bytes(codes[8 * j + 4: 8 * j + 8].tobytes(), "little")
+            s = aux >> 28
+            a = np.float32(d * np.float32(2 * s + 1))
+            for g in range(4):
+                xg = x[32 * j + 8 * g: 32 * j + 8 * g + 8]
+                r = np.minimum(np.abs(xg) / a, np.float32(64.0)).astype(np.float32)
+                R = np.rint(r * np.float32(4096.0)).astype(np.int64)
+                xneg = (xg < 0).astype(int)
+                scores, pats = _cb2_score_all(R, xneg, lv)
+                idx = int(codes[8 * j + g])
+                code = (aux >> (7 * g)) & 0x7F
+                assert scores[idx, code] == scores.min(), (trial, j, g)
+
+
+# ----------------------------------------------------------------- Q2K
+def _q2k_from_fixture(b):
+    codes = np.zeros(64, dtype=np.uint8)
+    if "codes" in b:
+        codes[:] = int(b["codes"], 16)
+    for pos, hx in b.get("codes_hex_positions", {}).items():
+        codes[int(pos)] = int(hx, 16)
+    sub = np.frombuffer(bytes.fromhex(b["subscales_hex"]), dtype=np.uint8)
+    sup = np.array([int(b["d_bits"], 16), int(b["dmin_bits"], 16)], dtype=np.uint16)
+    return np.concatenate([codes, sub, sup.view(np.uint8)])
+
+
+def test_q2k_layout_golden():
+    fx = json.load(open(os.path.join(GOLDEN, "q2k_layout.json")))
+    for b in fx["blocks"]:
+        w = O.q2k_dequantize(_q2k_from_fixture(b), 1, 256)[0]
+        for k, v in b["expect"].items():
+            assert w[int(k)] == v, (b["name"], k)
+
+
+def test_q2k_dequant_closed_form_exhaustive():
+    """d = dmin = 1: every (s, m, q) decodes to s*q - m."""
+    rows = 16  # row r uses m = r; sub-block j uses s = j; element i has q = i % 4
+    codes = np.full((rows, 64), 0xE4, dtype=np.uint8)
+    sub = np.array([[j | (r << 4) for j in range(16)] for r in range(rows)], dtype=np.uint8)
+    sup = np.tile(np.array([0x3C00, 0x3C00], dtype=np.uint16), rows)
+    packed = np.concatenate([codes.ravel(), sub.ravel(), sup.view(np.uint8)])
+    w = O.q2k_dequantize(packed, rows, 256)
+    for r in range(rows):
+        for j in range(16):
+            for i in range(16):
+                assert w[r, 16 * j + i] == j * (i % 4) - r
+
+
+def canonical_q2k(rng, rows):
+    """Exactly representable blocks with exact quantizer divisions: d, dmin
+    normal and within 2^4 of each other, s_j >= 1 with one 15, one m_j = 15,
+    every sub-block uses q = 0 and q = 3."""
+    codes = np.zeros((rows, 64), dtype=np.uint8)
+    sub = np.zeros((rows, 16), dtype=np.uint8)
+    sup = np.zeros((rows, 2), dtype=np.uint16)
+    for r in range(rows):
+        e = int(rng.integers(-10, -6))
+        em = e + int(rng.integers(-2, 3))
+        sup[r, 0] = ((e + 15) << 10) | int(rng.integers(0, 1024))
+        sup[r, 1] = ((em + 15) << 10) | int(rng.integers(0, 1024))
+        s = rng.integers(1, 16, 16)
+        s[rng.integers(0, 16)] = 15
+        m = rng.integers(0, 16, 16)
+        m[rng.integers(0, 16)] = 15
+        sub[r] = (s | (m << 4)).astype(np.uint8)
+        for j in range(16):
+            q = rng.integers(0, 4, 16)
+            pos = rng.permutation(16)[:2]
+            q[pos[0]], q[pos[1]] = 0, 3
+            u = 0
+            for i in range(16):
+                u |= int(q[i]) << (2 * i)
+            codes[r, 4 * j: 4 * j + 4] = np.frombuffer(np.uint32(u).tobytes(), dtype=np.uint8)
+    return np.concatenate([codes.ravel(), sub.ravel(), sup.ravel().view(np.uint8)])
+
+
+def test_q2k_roundtrip_canonical_is_identity():
+    rng = np.random.default_rng(2)
+    packed = canonical_q2k(rng, 64)
+    w = O.q2k_dequantize(packed, 64, 256)
+    assert np.array_equal(O.q2k_quantize(w), packed)
+
+
+def test_q2k_roundtrip_without_mins():
+    """All m_j = 0 and dmin = 0 (non-negative blocks) also round-trip."""
+    rng = np.random.default_rng(5)
+    packed = canonical_q2k(rng, 16)
+    n = 16
+    sub = packed[n * 64: n * 80]
+    sub &= 0x0F
+    sup = packed[n * 80: n * 84].view(np.uint16)
+    sup[1::2] = 0
+    w = O.q2k_dequantize(packed, n, 256)
+    assert (w >= 0).all()
+    assert np.array_equal(O.q2k_quantize(w), packed)
+
+
+def test_q2k_code_choice_is_nearest_level():
+    """Brute force over the four levels of each element's sub-block."""
+    rng = np.random.default_rng(4)
+    x = (rng.standard_normal((8, 512)) * 0.02).astype(np.float32)
+    packed = O.q2k_quantize(x)
+    w = O.q2k_dequantize(packed, 8, 512)
+    codes, sub, sup = O.q2k_planes(packed, 8, 512)
+    sup = sup.reshape(8, 2, 2)
+    sub = sub.reshape(8, 2, 16)
+    for r in range(8):
+        for b in range(2):
+            d = np.float32(sup[r, b, 0:1].view(np.float16)[0])
+            dm = np.float32(sup[r, b, 1:2].view(np.float16)[0])
+            for j in range(16):
+                s, m = int(sub[r, b, j] & 15), int(sub[r, b, j] >> 4)
+                lv = np.array([np.float32(np.float32(d * np.float32(s)) * np.float32(q)) - np.float32(dm * np.float32(m))
+                               for q in range(4)], dtype=np.float32)
+                seg = slice(256 * b + 16 * j, 256 * b + 16 * j + 16)
+                err = np.abs(lv[None, :] - x[r, seg][:, None])
+                best = lv[np.argmin(err, axis=1)]
+                assert np.array_equal(w[r, seg], best)
+
+
+# ----------------------------------------------------------------- degenerate blocks
+def test_zero_blocks():
+    z = np.zeros((2, 256), dtype=np.float32)
+    p = O.cb2_quantize(z)
+    assert not p.any()
+    assert not O.cb2_dequantize(p, 2, 256).any()
+    q = O.q2k_quantize(z)
+    assert not q.any()
+    assert not O.q2k_dequantize(q, 2, 256).any()
+
+
+def test_single_spike_and_huge_values():
+    x = np.zeros((3, 256), dtype=np.float32)
+    x[0, 17] = 0.5          # one nonzero element
+    x[1, :] = 1e-9          # tiny: d underflows to a binary16 subnormal or zero
+    x[2, 5] = 3e38          # clamps d at 65504
+    x[2, 6] = -3e38
+    for quant, deq in ((O.cb2_quantize, O.cb2_dequantize), (O.q2k_quantize, O.q2k_dequantize)):
+        w = deq(quant(x), 3, 256)
+        assert np.isfinite(w).all()
+    w = O.cb2_dequantize(O.cb2_quantize(x[:1]), 1, 256)[0]
+    assert w[17] > 0 and np.count_nonzero(w[:32]) > 0
+    w = O.q2k_dequantize(O.q2k_quantize(x[:1]), 1, 256)[0]
+    assert abs(w[17] - 0.5) < 0.5 / 15
+
+
+# ----------------------------------------------------------------- quality (sanity, reported)
+def test_quantizer_quality_sanity():
+    rng = np.random.default_rng(11)
+    x = (rng.standard_normal((64, 1024)) * 0.02).astype(np.float32)
+    for quant, deq, bound in ((O.cb2_quantize, O.cb2_dequantize, 0.60), (O.q2k_quantize, O.q2k_dequantize, 0.50)):
+        w = deq(quant(x), 64, 1024)
+        rel = np.sqrt(((w - x) ** 2).mean() / (x ** 2).mean())
+        assert rel < bound, rel
+        # better than representing everything by zero
+        assert ((w - x) ** 2).sum() < (x ** 2).sum()
+
+
+def test_quantizer_is_deterministic_and_thread_independent(monkeypatch):
+    rng = np.random.default_rng(12)
+    x = (rng.standard_normal((40, 512)) * 0.02).astype(np.float32)
+    a = O.cb2_quantize(x)
+    b = O.q2k_quantize(x)
+    # rows are independent: quantizing a subset gives the same bytes
+    a2 = O.cb2_quantize(x[:7])
+    ca, da = O.cb2_planes(a, 40, 512)
+    c2, d2 = O.cb2_planes(a2, 7, 512)
+    assert np.array_equal(ca[: 7 * 2 * 64], c2) and np.array_equal(da[:14], d2)
+    assert np.array_equal(a, O.cb2_quantize(x)) and np.array_equal(b, O.q2k_quantize(x))
