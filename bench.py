@@ -1,0 +1,319 @@
+#!/usr/bin/env python3
+"""Benchmark of the routed-MoE layer (ds4moe) on one MI355X.
+
+Headline (one JSON line on stdout): decode throughput of one DeepSeek V4
+Flash-shaped MoE layer at batch 1 -- d_model 4096, 256 routed experts, top-6
++ 1 shared, expert intermediate 2048, CB2 gate/up + Q2K down, F16 router and
+shared expert, bf16 activations -- in layer-tokens per second.
+
+  * inputs are resident in HBM before timing; each step is one
+    ds4moe_forward_decode (router, top-k, grouping, gate/up, down, combine);
+  * the packed layer is replicated into --copies device copies used round
+    robin, each step with a fresh seeded token, so the 256 MB Infinity Cache
+    cannot serve the shared/router weights from one step to the next;
+  * the K timed steps are captured once into a HIP graph and replayed (the
+    launch sequence a decode loop would submit), bracketed by events on the
+    capture stream; the eager (host-launched) rate is reported beside it;
+  * "roofline" covers the dominant kernel (k_gateup_decode): algorithmic
+    bytes per launch / its mean duration from HIP events around each launch
+    during an eager pass over the same steps;
+  * "prefill" times ds4moe_forward_prefill on a 2048-token chunk with
+    Zipf-like expert loads against the dense fp16 MFMA peak;
+  * "cpu_baseline" times the CPU oracle on a bounded sample of decode tokens.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, vendor peak
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA, vendor peak
+
+METRIC = "routed-MoE layer decode tok/s + % HBM peak; 2048-tok prefill tok/s + % MFMA"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def decode_bytes(cfg, n_distinct, T=1):
+    """Algorithmic bytes of one decode step and of its kernels."""
+    from bit_quantized_routed_router_amd import ds4moe as D
+    d, f, fs, E = cfg.d, cfg.f, cfg.fs, cfg.E
+    cb = D.packed_bytes(D.FMT_CB2, f, d)
+    qb = D.packed_bytes(D.FMT_Q2K, d, f)
+    x_bytes = T * d * 2
+    router = E * d * 2
+    shared_gu = 2 * fs * d * 2
+    shared_dn = d * fs * 2
+    routed_gu = n_distinct * 2 * cb
+    routed_dn = n_distinct * qb
+    gateup = shared_gu + routed_gu + T * d * 2 + T * cfg.k * f * 2 + T * fs * 2
+    down = shared_dn + routed_dn + T * d * 4
+    total = router + shared_gu + shared_dn + routed_gu + routed_dn + x_bytes + T * d * 4
+    return dict(total=total, k_gateup_decode=gateup, k_down_decode=down)
+
+
+def make_layer(cfg, copies=1, cfg_seed=None):
+    import torch
+    from bit_quantized_routed_router_amd import ds4moe as D
+    from bit_quantized_routed_router_amd import synthetic as S
+
+    def dev(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            a = a.view(np.int16)
+        return torch.from_numpy(a).cuda()
+
+    c = cfg
+    cb = D.packed_bytes(D.FMT_CB2, c.f, c.d)
+    qb = D.packed_bytes(D.FMT_Q2K, c.d, c.f)
+    gate = torch.empty(c.E * cb, dtype=torch.uint8, device="cuda")
+    up = torch.empty(c.E * cb, dtype=torch.uint8, device="cuda")
+    down = torch.empty(c.E * qb, dtype=torch.uint8, device="cuda")
+    t0 = time.time()
+    for e0 in range(0, c.E, 16):
+        es = list(range(e0, min(c.E, e0 + 16)))
+        for e, (g, u, dn) in zip(es, S.gen_experts(c, es, threads=16, cfg_seed=cfg_seed)):
+            D.quantize(D.FMT_CB2, dev(g), c.f, c.d, gate[e * cb:(e + 1) * cb])
+            D.quantize(D.FMT_CB2, dev(u), c.f, c.d, up[e * cb:(e + 1) * cb])
+            D.quantize(D.FMT_Q2K, dev(dn), c.d, c.f, down[e * qb:(e + 1) * qb])
+        torch.cuda.synchronize()
+    log(f"[bench] {c.name}: generated and quantized {c.E} experts in {time.time() - t0:.1f}s")
+    router = dev(S.gen_router(c, cfg_seed=cfg_seed))
+    bias = S.gen_bias(c)
+    bias = None if bias is None else dev(bias)
+    sh = [dev(a) for a in S.gen_shared(c, cfg_seed=cfg_seed)]
+    layers = [D.Layer(c.d, c.E, c.k, c.f, c.fs, router, bias, sh[0], sh[1], sh[2], gate, up, down)]
+    for _ in range(1, copies):
+        layers.append(D.Layer(c.d, c.E, c.k, c.f, c.fs, router.clone(), None if bias is None else bias.clone(),
+                              sh[0].clone(), sh[1].clone(), sh[2].clone(), gate.clone(), up.clone(), down.clone()))
+    torch.cuda.synchronize()
+    return layers
+
+
+def bench_decode(args):
+    import torch
+    from bit_quantized_routed_router_amd import ds4moe as D
+    from bit_quantized_routed_router_amd import synthetic as S
+
+    cfg = S.CONFIGS["decode1"]
+    layers = make_layer(cfg, copies=args.copies)
+    nsteps = args.warmup + args.steps
+    xs = np.concatenate([S.gen_x(cfg, variant=1000 + n) for n in range(nsteps)])
+    x = torch.from_numpy(xs.view(np.int16)).cuda()
+    y = torch.empty((nsteps, cfg.d), dtype=torch.float32, device="cuda")
+    idx = torch.empty((nsteps, cfg.k), dtype=torch.int32, device="cuda")
+    w = torch.empty((nsteps, cfg.k), dtype=torch.float32, device="cuda")
+    ws, wsn = layers[0].workspace(1, D.MODE_DECODE)
+
+    def step(n, stream):
+        L = layers[n % len(layers)]
+        D.forward_decode(L.desc, x[n], D.DT_BF16, 1, y[n], idx[n], w[n], ws, wsn, stream=stream)
+
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        for n in range(args.warmup):
+            step(n, s)
+    torch.cuda.synchronize()
+
+    # eager pass over the timed steps (host-launched)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(s):
+        e0.record(s)
+        for n in range(args.warmup, nsteps):
+            step(n, s)
+        e1.record(s)
+    torch.cuda.synchronize()
+    eager_ms = e0.elapsed_time(e1) / args.steps
+    y_eager = y.clone()
+
+    # traced eager pass: per-kernel durations from events around each launch
+    D.trace_read(reset=True)
+    D.trace_enable(True)
+    with torch.cuda.stream(s):
+        for n in range(args.warmup, nsteps):
+            step(n, s)
+    torch.cuda.synchronize()
+    D.trace_enable(False)
+    kern = D.trace_read(reset=True)
+
+    # graph: the timed steps captured once, replayed
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for n in range(args.warmup, nsteps):
+            step(n, torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    g.replay()  # first replay (not timed), checked against the eager results
+    torch.cuda.synchronize()
+    if not torch.equal(y[args.warmup:], y_eager[args.warmup:]):
+        raise RuntimeError("graph replay differs from the eager run")
+    torch.cuda.synchronize()
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    g0.record(s)
+    with torch.cuda.stream(s):
+        g.replay()
+    g1.record(s)
+    torch.cuda.synchronize()
+    graph_ms = g0.elapsed_time(g1) / args.steps
+    if not torch.equal(y[args.warmup:], y_eager[args.warmup:]):
+        raise RuntimeError("graph replay differs from the eager run")
+
+    # distinct experts per step (1 token: k distinct) -> algorithmic bytes
+    nb = decode_bytes(cfg, cfg.k, T=1)
+    dom = "k_gateup_decode"
+    ms_dom, cnt_dom = kern.get(dom, (float("nan"), 0))
+    dur_us = ms_dom / max(cnt_dom, 1) * 1e3
+    achieved = nb[dom] / (dur_us * 1e-6) / 1e9
+    res = dict(ms_per_step=graph_ms, eager_ms_per_step=eager_ms, kernels={k: dict(mean_us=v[0] / max(v[1], 1) * 1e3,
+               launches=v[1]) for k, v in kern.items()},
+               roofline=dict(bound="hbm", kernel=dom, achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
+                             frac=achieved / HBM_PEAK_GBS, traffic=None, bytes_per_launch=nb[dom],
+                             mean_launch_us=dur_us),
+               layer_bytes=nb["total"], layer_gbs=nb["total"] / (graph_ms * 1e-3) / 1e9)
+    res["layer_hbm_frac"] = res["layer_gbs"] / HBM_PEAK_GBS
+    del layers, g
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_prefill(args):
+    import torch
+    from bit_quantized_routed_router_amd import ds4moe as D
+    from bit_quantized_routed_router_amd import synthetic as S
+
+    cfg = S.CONFIGS["prefill"]
+    L = make_layer(cfg)[0]
+    x = torch.from_numpy(S.gen_x(cfg).view(np.int16)).cuda()
+    T = cfg.T
+    y = torch.empty((T, cfg.d), dtype=torch.float32, device="cuda")
+    ws, wsn = L.workspace(T, D.MODE_PREFILL)
+    for _ in range(2):
+        D.forward_prefill(L.desc, x, D.DT_BF16, T, y, None, None, None, ws, wsn)
+    torch.cuda.synchronize()
+    reps = 5
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        D.forward_prefill(L.desc, x, D.DT_BF16, T, y, None, None, None, ws, wsn)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    D.trace_read(reset=True)
+    D.trace_enable(True)
+    D.forward_prefill(L.desc, x, D.DT_BF16, T, y, None, None, None, ws, wsn)
+    torch.cuda.synchronize()
+    D.trace_enable(False)
+    kern = D.trace_read(reset=True)
+    flop = 2 * T * cfg.k * 3 * cfg.d * cfg.f + 2 * T * 3 * cfg.d * cfg.fs + 2 * T * cfg.E * cfg.d
+    tflops = flop / (ms * 1e-3) / 1e12
+    del L
+    torch.cuda.empty_cache()
+    return dict(workload=f"prefill T={T}, Zipf(1.1)-shaped expert loads", tok_s=T / (ms * 1e-3), ms=ms,
+                flop=flop, tflops=tflops, mfma_frac=tflops / MFMA_F16_PEAK_TFLOPS,
+                kernels={k: dict(mean_us=v[0] / max(v[1], 1) * 1e3, launches=v[1]) for k, v in kern.items()})
+
+
+def bench_cpu_oracle(seconds: float):
+    """The CPU oracle on a bounded sample of decode1 tokens (experts the sample
+    needs are packed by the oracle beforehand, untimed)."""
+    from oracle import oracle as O
+    from bit_quantized_routed_router_amd import synthetic as S
+
+    cfg = S.CONFIGS["decode1"]
+    router = S.gen_router(cfg)
+    sh = S.gen_shared(cfg)
+    cache = {}
+
+    def expert(e):
+        if e not in cache:
+            g, u, dn = S.gen_expert(cfg, e)
+            cache[e] = (O.cb2_quantize(g), O.cb2_quantize(u), O.q2k_quantize(dn))
+        return cache[e]
+
+    L = O.Layer(cfg.d, cfg.E, cfg.k, cfg.f, cfg.fs, router, None, sh[0], sh[1], sh[2], expert)
+    ntok = 4
+    xs = [S.gen_x(cfg, variant=1000 + n) for n in range(ntok)]
+    for x in xs:  # pack the sample's experts (untimed)
+        for e in np.unique(L.route(x, "bf16")["idx"]):
+            L.expert(int(e))
+    done, t0 = 0, time.time()
+    while True:
+        for x in xs:
+            L.forward(x, "bf16")
+            done += 1
+        if time.time() - t0 >= seconds:
+            break
+    dt = time.time() - t0
+    threads = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
+    return dict(value=done / dt, unit="tok/s", cores=threads, kind="oracle",
+                sample=f"{done} decode1 tokens (T=1 layer calls over {ntok} distinct tokens), {dt:.1f}s, fp64")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=256)
+    ap.add_argument("--warmup", type=int, default=16)
+    ap.add_argument("--copies", type=int, default=8)
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures the layer on one GPU only; this build has no multi-GPU path "
+              "(run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+
+    dec = bench_decode(args)
+    log(f"[bench] decode: graph {dec['ms_per_step'] * 1e3:.1f} us/step, eager {dec['eager_ms_per_step'] * 1e3:.1f} us/step")
+    pre = None if args.no_prefill else bench_prefill(args)
+    if pre:
+        log(f"[bench] prefill: {pre['ms']:.3f} ms, {pre['tok_s']:.0f} tok/s, {pre['tflops']:.1f} TFLOP/s")
+    cpu = None if args.no_cpu_baseline else bench_cpu_oracle(args.cpu_seconds)
+    ms = dec["ms_per_step"]
+    out = {
+        "metric": METRIC,
+        "value": 1.0 / (ms * 1e-3),
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {
+            "workload": "decode1: one MoE layer, T=1, d_model 4096, 256 experts top-6 + 1 shared, f=fs=2048, "
+                        "CB2 gate/up + Q2K down, F16 router/shared, bf16 x; "
+                        f"{args.copies} layer copies round-robin, HIP-graph replay",
+            "global_batch": 1,
+            "layer_copies": args.copies,
+        },
+        "roofline": dec["roofline"],
+        "layer_hbm": {"bytes_per_step": dec["layer_bytes"], "achieved_gbs": dec["layer_gbs"],
+                      "frac": dec["layer_hbm_frac"]},
+        "eager_ms_per_step": dec["eager_ms_per_step"],
+        "kernels_us": {k: round(v["mean_us"], 2) for k, v in dec["kernels"].items()},
+        "prefill": None if pre is None else {k: pre[k] for k in ("workload", "tok_s", "ms", "tflops", "mfma_frac")},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

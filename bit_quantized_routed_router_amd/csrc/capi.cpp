@@ -1,0 +1,221 @@
+// C ABI of the ds4moe library: argument validation, workspace layout and
+// dispatch.  Nothing is enqueued unless every check passes.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstring>
+
+#include "common.h"
+#include "internal.h"
+
+namespace ds4 {
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+WsLayout ws_layout(const ds4moe_layer& L, int64_t T, int mode) {
+  WsLayout y{};
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    size_t r = o;
+    o += align256(bytes);
+    return r;
+  };
+  const int64_t d = L.d_model, E = L.n_experts, k = L.top_k, f = L.d_ff, fs = L.d_ff_shared;
+  const int64_t Tg = mode == DS4MOE_MODE_DECODE ? std::min<int64_t>(T, kDecodeGroup) : T;
+  const int64_t S = Tg * k;
+  y.x_hi = take(Tg * d * 2);
+  y.x_lo = take(Tg * d * 2);
+  y.logits = take(Tg * E * 4);
+  y.topk_idx = take(S * 4);
+  y.topk_w = take(S * 4);
+  y.counts = take(E * 4);
+  y.offsets = take((E + 1) * 4);
+  y.perm = take(S * 4);
+  y.inv = take(S * 4);
+  const int64_t dmax = std::min<int64_t>(E, std::min<int64_t>(Tg, kDecodeGroup) * k);
+  y.ndist = take(4);
+  y.distinct = take(E * 4);
+  y.tok_slot = take(dmax * kDecodeGroup * 4);
+  y.tiles = take(((S + 15) / 16 + E) * 2 * 4);
+  y.ntiles = take(4);
+  if (mode != DS4MOE_MODE_ROUTE) {  // expert buffers (not needed for routing alone)
+    y.hs16 = take(Tg * fs * 2);
+    y.hw16 = take(S * f * 2);
+    y.hsum = take(S * (f / 16) * 4);
+    if (mode == DS4MOE_MODE_PREFILL) y.yp = take(S * d * 4);
+  }
+  y.total = o;
+  return y;
+}
+
+static bool al16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+static bool dim_ok(int64_t v) { return v >= 256 && v <= kMaxDim && v % 256 == 0; }
+
+static int check_layer(const ds4moe_layer* L) {
+  if (!L) return DS4MOE_EINVAL;
+  if (!L->router_w || !L->sh_gate || !L->sh_up || !L->sh_down || !L->gate || !L->up || !L->down) return DS4MOE_EINVAL;
+  if (!dim_ok(L->d_model) || !dim_ok(L->d_ff) || !dim_ok(L->d_ff_shared)) return DS4MOE_ESHAPE;
+  if (L->n_experts < 1 || L->n_experts > kMaxExperts) return DS4MOE_ESHAPE;
+  if (L->top_k < 1 || L->top_k > L->n_experts || L->top_k > kMaxTopK) return DS4MOE_ESHAPE;
+  if (!al16(L->router_w) || !al16(L->sh_gate) || !al16(L->sh_up) || !al16(L->sh_down) || !al16(L->gate) ||
+      !al16(L->up) || !al16(L->down))
+    return DS4MOE_EALIGN;
+  if (L->router_bias && ((uintptr_t)L->router_bias & 3)) return DS4MOE_EALIGN;
+  return DS4MOE_OK;
+}
+
+static int check_io(const void* x, int x_dtype, int64_t T, const void* ws, size_t ws_bytes, size_t need) {
+  if (!x || !ws) return DS4MOE_EINVAL;
+  if (x_dtype != DS4MOE_DT_F32 && x_dtype != DS4MOE_DT_BF16) return DS4MOE_EINVAL;
+  if (T < 1) return DS4MOE_ESHAPE;
+  if (!al16(x) || ((uintptr_t)ws & 255)) return DS4MOE_EALIGN;
+  if (ws_bytes < need) return DS4MOE_EWORKSPACE;
+  return DS4MOE_OK;
+}
+
+static bool opt_al4(const void* p) { return !p || ((uintptr_t)p & 3) == 0; }
+
+static Fwd make_fwd(const ds4moe_layer* L, const void* x, int x_dtype, int64_t T, float* y, int32_t* idx_out,
+                    float* w_out, void* ws, int mode, void* stream) {
+  Fwd f{};
+  f.L = *L;
+  f.T = T;
+  f.lo = x_dtype == DS4MOE_DT_F32;
+  f.x = x;
+  f.x_dtype = x_dtype;
+  f.y = y;
+  f.idx_out = idx_out;
+  f.w_out = w_out;
+  f.ws = (char*)ws;
+  f.lay = ws_layout(*L, T, mode);
+  f.st = (hipStream_t)stream;
+  return f;
+}
+
+static int hip_status(hipError_t e) { return e == hipSuccess ? DS4MOE_OK : DS4MOE_EHIP; }
+
+}  // namespace ds4
+
+using namespace ds4;
+
+extern "C" {
+
+size_t ds4moe_packed_bytes(int fmt, int64_t rows, int64_t cols) {
+  if (rows < 0 || cols < 0) return 0;
+  if (fmt == DS4MOE_FMT_F16) return (size_t)rows * (size_t)cols * 2;
+  if (cols % QK != 0) return 0;
+  const size_t nblk = (size_t)rows * (size_t)(cols / QK);
+  if (fmt == DS4MOE_FMT_CB2) return nblk * 66;
+  if (fmt == DS4MOE_FMT_Q2K) return nblk * 84;
+  return 0;
+}
+
+int ds4moe_quantize(int fmt, const float* w, int64_t rows, int64_t cols, void* packed, void* stream) {
+  if (fmt != DS4MOE_FMT_CB2 && fmt != DS4MOE_FMT_Q2K) return DS4MOE_EINVAL;
+  if (rows < 0 || cols < 0) return DS4MOE_EINVAL;
+  if (cols % QK != 0) return DS4MOE_ESHAPE;
+  if (rows == 0 || cols == 0) return DS4MOE_OK;
+  if (!w || !packed) return DS4MOE_EINVAL;
+  if (!al16(w) || !al16(packed)) return DS4MOE_EALIGN;
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = fmt == DS4MOE_FMT_CB2 ? launch_quant_cb2(w, rows, cols, packed, st)
+                                       : launch_quant_q2k(w, rows, cols, packed, st);
+  return hip_status(e);
+}
+
+int ds4moe_dequantize(int fmt, const void* packed, int64_t rows, int64_t cols, float* w, void* stream) {
+  if (fmt != DS4MOE_FMT_CB2 && fmt != DS4MOE_FMT_Q2K) return DS4MOE_EINVAL;
+  if (rows < 0 || cols < 0) return DS4MOE_EINVAL;
+  if (cols % QK != 0) return DS4MOE_ESHAPE;
+  if (rows == 0 || cols == 0) return DS4MOE_OK;
+  if (!w || !packed) return DS4MOE_EINVAL;
+  if (!al16(w) || !al16(packed)) return DS4MOE_EALIGN;
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = fmt == DS4MOE_FMT_CB2 ? launch_dequant_cb2(packed, rows, cols, w, st)
+                                       : launch_dequant_q2k(packed, rows, cols, w, st);
+  return hip_status(e);
+}
+
+size_t ds4moe_workspace_bytes(const ds4moe_layer* L, int64_t T, int mode) {
+  if (!L || T < 1 || (mode != DS4MOE_MODE_DECODE && mode != DS4MOE_MODE_PREFILL && mode != DS4MOE_MODE_ROUTE)) return 0;
+  if (!dim_ok(L->d_model) || !dim_ok(L->d_ff) || !dim_ok(L->d_ff_shared)) return 0;
+  if (L->n_experts < 1 || L->n_experts > kMaxExperts || L->top_k < 1 || L->top_k > L->n_experts) return 0;
+  return ws_layout(*L, T, mode).total;
+}
+
+int ds4moe_route(const ds4moe_layer* L, const void* x, int x_dtype, int64_t T, int32_t* topk_idx, float* topk_w,
+                 int32_t* counts, int32_t* offsets, int32_t* perm, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_layer(L);
+  if (rc) return rc;
+  if (T > 1 << 20) return DS4MOE_ESHAPE;
+  if ((rc = check_io(x, x_dtype, T, ws, ws_bytes, ws_layout(*L, T, DS4MOE_MODE_ROUTE).total))) return rc;
+  if (!topk_idx || !topk_w) return DS4MOE_EINVAL;
+  if (!opt_al4(topk_idx) || !opt_al4(topk_w) || !opt_al4(counts) || !opt_al4(offsets) || !opt_al4(perm))
+    return DS4MOE_EALIGN;
+  Fwd f = make_fwd(L, x, x_dtype, T, nullptr, topk_idx, topk_w, ws, DS4MOE_MODE_ROUTE, stream);
+  f.counts_out = counts;
+  f.offsets_out = offsets;
+  f.perm_out = perm;
+  return hip_status(launch_route(f, T <= kDecodeGroup));
+}
+
+int ds4moe_forward_decode(const ds4moe_layer* L, const void* x, int x_dtype, int64_t T, float* y,
+                          int32_t* topk_idx_out, float* topk_w_out, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_layer(L);
+  if (rc) return rc;
+  if (T > DS4MOE_DECODE_MAX_T) return DS4MOE_ESHAPE;
+  if ((rc = check_io(x, x_dtype, T, ws, ws_bytes, ws_layout(*L, T, DS4MOE_MODE_DECODE).total))) return rc;
+  if (!y) return DS4MOE_EINVAL;
+  if (!al16(y)) return DS4MOE_EALIGN;
+  if (!opt_al4(topk_idx_out) || !opt_al4(topk_w_out)) return DS4MOE_EALIGN;
+  const size_t xes = x_dtype == DS4MOE_DT_F32 ? 4 : 2;
+  const int64_t d = L->d_model, k = L->top_k;
+  for (int64_t t0 = 0; t0 < T; t0 += kDecodeGroup) {  // groups of up to 16 tokens, in order on the stream
+    const int64_t tg = std::min<int64_t>(kDecodeGroup, T - t0);
+    Fwd f = make_fwd(L, (const char*)x + t0 * d * xes, x_dtype, tg, y + t0 * d,
+                     topk_idx_out ? topk_idx_out + t0 * k : nullptr, topk_w_out ? topk_w_out + t0 * k : nullptr, ws,
+                     DS4MOE_MODE_DECODE, stream);
+    hipError_t e = launch_route(f, true);
+    if (e == hipSuccess) e = launch_decode_experts(f);
+    if (e != hipSuccess) return DS4MOE_EHIP;
+  }
+  return DS4MOE_OK;
+}
+
+int ds4moe_forward_prefill(const ds4moe_layer* L, const void* x, int x_dtype, int64_t T, float* y,
+                           int32_t* topk_idx_out, float* topk_w_out, int32_t* perm_out, void* ws, size_t ws_bytes,
+                           void* stream) {
+  int rc = check_layer(L);
+  if (rc) return rc;
+  if (T > 65535 * 16 / 2 || (T * L->top_k + 15) / 16 + L->n_experts > 65535) return DS4MOE_ESHAPE;
+  if ((rc = check_io(x, x_dtype, T, ws, ws_bytes, ws_layout(*L, T, DS4MOE_MODE_PREFILL).total))) return rc;
+  if (!y) return DS4MOE_EINVAL;
+  if (!al16(y)) return DS4MOE_EALIGN;
+  if (!opt_al4(topk_idx_out) || !opt_al4(topk_w_out) || !opt_al4(perm_out)) return DS4MOE_EALIGN;
+  Fwd f = make_fwd(L, x, x_dtype, T, y, topk_idx_out, topk_w_out, ws, DS4MOE_MODE_PREFILL, stream);
+  f.perm_out = perm_out;
+  hipError_t e = launch_route(f, false);
+  if (e == hipSuccess) e = launch_prefill_experts(f);
+  return hip_status(e);
+}
+
+const char* ds4moe_strerror(int status) {
+  switch (status) {
+    case DS4MOE_OK: return "ok";
+    case DS4MOE_EINVAL: return "invalid argument (NULL pointer, unknown enum or negative size)";
+    case DS4MOE_ESHAPE: return "unsupported shape (dimensions must be multiples of 256, 1 <= k <= E, T in range)";
+    case DS4MOE_EALIGN: return "misaligned pointer (16 bytes for tensors, 256 for the workspace)";
+    case DS4MOE_EWORKSPACE: return "workspace smaller than ds4moe_workspace_bytes()";
+    case DS4MOE_EHIP: return "HIP runtime error at launch";
+    case DS4MOE_EUNSUPPORTED: return "not supported by this build";
+    default: return "unknown status";
+  }
+}
+
+void ds4moe_grid_levels(uint8_t* levels) {
+  if (!levels) return;
+  for (int i = 0; i < 256; ++i)
+    for (int k = 0; k < 8; ++k) levels[8 * i + k] = kGridLevels.lv[i][k];
+}
+
+}  // extern "C"

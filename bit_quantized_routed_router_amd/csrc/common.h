@@ -1,0 +1,231 @@
+// Shared device helpers for the ds4moe kernels (gfx950 / CDNA4, wave64).
+//
+// The layer is the routed mixture-of-experts feed-forward block of DeepSeek V4
+// Flash as DS4 runs it (DS4 (DwarfStar 4) wiki note, "Architecture" and "Key
+// Techniques"): an F16 router picks the top-k of E experts, one F16 shared
+// expert always runs, and the routed experts' gate/up weights are stored in a
+// 2-bit codebook format (CB2, IQ2_XXS class) and their down weights in a
+// 2-bit super-block format (Q2K, Q2_K class).  The byte layouts are the
+// library's own (the pages only name the formats); they are written out in
+// include/ds4moe.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ds4 {
+
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int QK = 256;  // super-block length along K
+constexpr int WAVE = 64;
+
+// ---------------------------------------------------------------------------
+// Codebook grid: 256 entries x 8 levels in {0,1,2} (magnitude 2*level+1),
+// drawn with splitmix64 (Steele, Lea & Flood 2014) from a fixed seed, the
+// high 32 bits of each draw taken modulo 3; an entry equal to an earlier one
+// is drawn again.  Built at compile time, so no table is ever uploaded.
+// ---------------------------------------------------------------------------
+constexpr uint64_t kGridSeed = 0x44533447524944ULL;  // ASCII "DS4GRID"
+
+constexpr uint64_t splitmix64_next(uint64_t& s) {
+  s += 0x9E3779B97F4A7C15ULL;
+  uint64_t z = s;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ULL;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBULL;
+  return z ^ (z >> 31);
+}
+
+struct GridLevels {
+  uint8_t lv[256][8];
+};
+
+constexpr GridLevels make_grid_levels() {
+  GridLevels g{};
+  uint64_t st = kGridSeed;
+  for (int i = 0; i < 256; ++i) {
+    for (;;) {
+      for (int k = 0; k < 8; ++k) g.lv[i][k] = (uint8_t)((splitmix64_next(st) >> 32) % 3);
+      bool dup = false;
+      for (int j = 0; j < i && !dup; ++j) {
+        bool same = true;
+        for (int k = 0; k < 8; ++k) same = same && (g.lv[j][k] == g.lv[i][k]);
+        dup = same;
+      }
+      if (!dup) break;
+    }
+  }
+  return g;
+}
+
+inline constexpr GridLevels kGridLevels = make_grid_levels();
+
+// Tables the kernels stage into LDS:
+//   mag[e][p]  : binary16 pair (m_{2p}, m_{2p+1}) of entry e (low, high half)
+//   sgn[c][p]  : sign bits (bit 15 / bit 31) of elements 2p, 2p+1 for the
+//                7-bit sign code c; element 7's sign is the parity of c
+//   imag[e][k] : integer magnitudes for the quantizer's search
+//   isq[e]     : sum_k 4096 * m_ek^2
+struct GridTables {
+  uint32_t mag[256][4];
+  uint32_t sgn[128][4];
+  int32_t imag[256][8];
+  int32_t isq[256];
+};
+
+constexpr uint32_t f16_of_small_odd(int m) {  // 1 -> 0x3C00, 3 -> 0x4200, 5 -> 0x4500
+  return m == 1 ? 0x3C00u : (m == 3 ? 0x4200u : 0x4500u);
+}
+
+constexpr GridTables make_grid_tables() {
+  GridTables t{};
+  for (int e = 0; e < 256; ++e) {
+    int sq = 0;
+    for (int k = 0; k < 8; ++k) {
+      int m = 2 * kGridLevels.lv[e][k] + 1;
+      t.imag[e][k] = m;
+      sq += 4096 * m * m;
+    }
+    t.isq[e] = sq;
+    for (int p = 0; p < 4; ++p)
+      t.mag[e][p] = f16_of_small_odd(t.imag[e][2 * p]) | (f16_of_small_odd(t.imag[e][2 * p + 1]) << 16);
+  }
+  for (int c = 0; c < 128; ++c) {
+    int par = 0;
+    for (int k = 0; k < 7; ++k) par ^= (c >> k) & 1;
+    for (int p = 0; p < 4; ++p) {
+      int k0 = 2 * p, k1 = 2 * p + 1;
+      uint32_t n0 = (uint32_t)((c >> k0) & 1);
+      uint32_t n1 = k1 < 7 ? (uint32_t)((c >> k1) & 1) : (uint32_t)par;
+      t.sgn[c][p] = (n0 << 15) | (n1 << 31);
+    }
+  }
+  return t;
+}
+
+// ---------------------------------------------------------------------------
+// binary16 <-> binary32 in integer arithmetic (independent of mode bits)
+// ---------------------------------------------------------------------------
+__host__ __device__ inline float f16_bits_to_f32(uint32_t h) {
+  uint32_t sign = (h & 0x8000u) << 16;
+  uint32_t e = (h >> 10) & 0x1Fu;
+  uint32_t m = h & 0x3FFu;
+  uint32_t bits;
+  if (e == 0) {
+    if (m == 0) {
+      bits = sign;
+    } else {  // subnormal: normalise
+      int sh = 0;
+      while (!(m & 0x400u)) {
+        m <<= 1;
+        ++sh;
+      }
+      m &= 0x3FFu;
+      bits = sign | ((uint32_t)(113 - sh) << 23) | (m << 13);
+    }
+  } else if (e == 31) {
+    bits = sign | 0x7F800000u | (m << 13);
+  } else {
+    bits = sign | ((e + 112u) << 23) | (m << 13);
+  }
+  return __builtin_bit_cast(float, bits);
+}
+
+// Nearest binary16 to a finite, non-negative binary32 no larger than 65504,
+// ties to even.
+__host__ __device__ inline uint32_t f32_to_f16_bits_rne(float f) {
+  uint32_t x = __builtin_bit_cast(uint32_t, f) & 0x7FFFFFFFu;
+  int e = (int)(x >> 23) - 127;
+  if (e < -25) return 0;  // below half of the smallest subnormal
+  uint32_t mant = (x & 0x7FFFFFu) | 0x800000u;  // 24 significant bits
+  if (e < -14) {  // subnormal result: quantum 2^-24
+    int sh = -1 - e;  // value = mant * 2^(e-23); count of 2^-24 = mant >> (-e-1)
+    uint32_t q = mant >> sh;
+    uint32_t rem = mant & ((1u << sh) - 1);
+    uint32_t half = 1u << (sh - 1);
+    if (rem > half || (rem == half && (q & 1))) ++q;
+    return q;  // may carry into 0x400 = smallest normal, still correct
+  }
+  uint32_t q = mant >> 13;  // 11 bits
+  uint32_t rem = mant & 0x1FFFu;
+  if (rem > 0x1000u || (rem == 0x1000u && (q & 1))) ++q;
+  uint32_t ex = (uint32_t)(e + 15);
+  if (q == 0x800u) {
+    q >>= 1;
+    ++ex;
+  }
+  return (ex << 10) | (q & 0x3FFu);
+}
+
+// ---------------------------------------------------------------------------
+// MFMA: v_mfma_f32_16x16x32_f16.  Lane l supplies row (l & 15) of A and
+// column (l & 15) of B, each with the eight K-slots 8*(l>>4) .. +7, and
+// receives D[rows 4*(l>>4) .. +3][column l & 15].
+// ---------------------------------------------------------------------------
+__device__ inline float4_t mfma16x16x32(half8_t a, half8_t b, float4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ inline half8_t as_half8(u32x4_t v) { return __builtin_bit_cast(half8_t, v); }
+__device__ inline half2_t as_half2(uint32_t v) { return __builtin_bit_cast(half2_t, v); }
+__device__ inline uint32_t as_u32(half2_t v) { return __builtin_bit_cast(uint32_t, v); }
+
+// CB2 A fragment: the 8 weights of group q of one sub-block, as binary16
+// sign * (2s+1) * m (exact integers <= 155); the super-block's d is applied
+// to the fp32 product afterwards.  mag/sgn point at the LDS tables.
+__device__ inline half8_t cb2_frag(uint32_t idxw, uint32_t aux, int q, const uint32_t* mag,
+                                   const uint32_t* sgn) {
+  uint32_t idx = (idxw >> (8 * q)) & 0xFFu;
+  uint32_t code = (aux >> (7 * q)) & 0x7Fu;
+  _Float16 S = (_Float16)(float)(2 * (aux >> 28) + 1);
+  half2_t S2 = {S, S};
+  u32x4_t m = *(const u32x4_t*)(mag + 4 * idx);
+  u32x4_t s = *(const u32x4_t*)(sgn + 4 * code);
+  u32x4_t r;
+  r.x = as_u32(as_half2(m.x ^ s.x) * S2);
+  r.y = as_u32(as_half2(m.y ^ s.y) * S2);
+  r.z = as_u32(as_half2(m.z ^ s.z) * S2);
+  r.w = as_u32(as_half2(m.w ^ s.w) * S2);
+  return as_half8(r);
+}
+
+// Q2K A fragment: 8 consecutive codes (the low or high 16 bits of a
+// sub-block's u32) as binary16 s * q (exact integers <= 45).  The min term
+// and the super-block's d/dmin are applied afterwards.
+__device__ inline half8_t q2k_frag(uint32_t u, int hi, uint32_t s) {
+  uint32_t field = hi ? (u >> 16) : (u & 0xFFFFu);
+  uint32_t v = field | (field << 14);  // code 2p at bits 4p, code 2p+1 at bits 16+4p
+  _Float16 S = (_Float16)(float)s;
+  _Float16 C = (_Float16)(-1024.0f * (float)s);
+  half2_t S2 = {S, S}, C2 = {C, C};
+  u32x4_t r;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    uint32_t pair = ((v >> (4 * p)) & 0x00030003u) | 0x64006400u;  // (1024 + q_a, 1024 + q_b)
+    half2_t t = __builtin_elementwise_fma(as_half2(pair), S2, C2);   // single rounding: exact
+    r[p] = as_u32(t);
+  }
+  return as_half8(r);
+}
+
+// binary16 (1024 + n) trick for a byte's high nibble, pairs of bytes.
+__device__ inline uint32_t nib_hi_pair_f16(uint32_t w, int byte0) {
+  uint32_t a = (w >> (8 * byte0 + 4)) & 0xFu;
+  uint32_t b = (w >> (8 * byte0 + 12)) & 0xFu;
+  half2_t t = as_half2(a | (b << 16) | 0x64006400u);
+  half2_t off = {(_Float16)1024.0f, (_Float16)1024.0f};
+  return as_u32(t - off);
+}
+
+__device__ inline half8_t zero_half8() {
+  u32x4_t z = {0u, 0u, 0u, 0u};
+  return as_half8(z);
+}
+
+__device__ inline float silu(float g) { return g / (1.0f + __expf(-g)); }
+
+}  // namespace ds4

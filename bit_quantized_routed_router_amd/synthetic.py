@@ -65,7 +65,8 @@ CONFIGS = {
     "tiny": Config("tiny", 256, 16, 2, 256, 256, 8, "f32", seed=0),
     "decode1": Config("decode1", 4096, 256, 6, 2048, 2048, 1, "bf16", seed=1),
     "decode16": Config("decode16", 4096, 256, 6, 2048, 2048, 16, "bf16", seed=3, bias="hotpool"),
-    "prefill": Config("prefill", 4096, 256, 6, 2048, 2048, 2048, "bf16", seed=4, bias="zipf"),
+    "prefill": Config("prefill", 4096, 256, 6, 2048, 2048, 2048, "bf16", seed=4, bias="zipf",
+                      router_variant=4, zipf_beta=0.546875),
     "stack43": Config("stack43", 4096, 256, 6, 2048, 2048, 1, "bf16", seed=1000, layers=43),
 }
 

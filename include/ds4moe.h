@@ -1,0 +1,176 @@
+/*
+ * ds4moe -- routed mixture-of-experts layer with 2-bit quantized experts on
+ * AMD Instinct MI355X (gfx950).  C ABI.
+ *
+ * The layer (DS4 (DwarfStar 4) wiki note, "Architecture" and "Key
+ * Techniques"; TopDigg "DwarfStar (ds4) Deep Dive", section 3.4 "Asymmetric
+ * Quantization"): an F16 router scores E experts and picks the top k; one
+ * F16 shared expert always runs; each expert is a SwiGLU block
+ * down(silu(gate x) * up x) whose routed gate/up weights are stored in the
+ * CB2 codebook format (IQ2_XXS class) and whose routed down weights are in
+ * the Q2K super-block format (Q2_K class), dequantized inside the products.
+ * DeepSeek V4 Flash's shape is d_model 4096, E 256, k 6.
+ *
+ * Readings where the pages are silent: the routing weights are the softmax
+ * of the selected logits (sum 1, no extra scale); the k selected experts of a
+ * token are listed in ascending expert index; equal logits go to the lower
+ * index; the shared expert has weight 1; silu(z) = z / (1 + e^-z).
+ *
+ * ---------------------------------------------------------------- conventions
+ * Every pointer is a device pointer owned by the caller unless marked host.
+ * Calls are asynchronous on `stream` (a hipStream_t passed as void*; NULL is
+ * the default stream).  Arguments are validated on the host before anything
+ * is enqueued: a nonzero return means nothing was launched, except
+ * DS4MOE_EHIP, which reports a launch failure.  Buffers must stay alive until
+ * the stream has passed the call.  The library allocates no device memory:
+ * the caller provides a workspace of ds4moe_workspace_bytes() bytes (256-byte
+ * aligned) for each call; calls that share a workspace must be ordered on one
+ * stream.  The codebook grid is a compile-time table; the only mutable
+ * global state is the opt-in kernel timer (ds4moe_trace_enable).
+ *
+ * ---------------------------------------------------------------- formats
+ * A matrix W [rows, cols] is quantized along cols (the input dimension) in
+ * super-blocks of 256; cols % 256 == 0, nb = cols / 256.  A packed matrix is
+ * one buffer holding its planes back to back; E experts are E packed
+ * matrices back to back (expert e at e * ds4moe_packed_bytes(...)).
+ *
+ * CB2 (2.0625 bits per weight; 66 bytes per 256 weights):
+ *   code plane  rows*nb*64 bytes: block (r, b) at (r*nb + b)*64.  Sub-block
+ *               j (32 weights) occupies bytes 8j..8j+7: bytes 8j+g (g = 0..3)
+ *               are the grid indices of its groups of 8; bytes 8j+4..8j+7 are
+ *               a little-endian u32 aux: bits 7g..7g+6 = sign code of group
+ *               g, bits 28..31 = sub-block scale s (0..15).
+ *   scale plane rows*nb binary16 d, at byte offset rows*nb*64.
+ *   Weight K = 256b + 32j + 8g + k = sign_k * (d * (2s + 1)) * m_k with
+ *   m_k = 2*level + 1 of grid entry idx, coordinate k.  sign_k (1 = negative)
+ *   is bit k of the code for k < 7 and the parity of the code for k = 7.
+ *   Grid: 256 entries x 8 levels in {0,1,2}; entry i is drawn with
+ *   splitmix64 seeded with 0x44533447524944, level = (draw >> 32) % 3, in
+ *   coordinate order; an entry equal to an earlier one is drawn again.
+ *   Every product is exact in binary32, so decoding is bit-exact.
+ *
+ * Q2K (2.625 bits per weight; 84 bytes per 256 weights):
+ *   code plane      rows*nb*64 bytes: sub-block j (16 weights) is the LE u32
+ *                   at bytes 4j..4j+3 of its block, element i at bits 2i..2i+1.
+ *   subscale plane  rows*nb*16 bytes at offset rows*nb*64: byte j =
+ *                   s_j | m_j << 4.
+ *   superscale      rows*nb pairs (binary16 d, binary16 dmin) at offset
+ *                   rows*nb*80.
+ *   Weight K = 256b + 16j + i = (d * s_j) * q - dmin * m_j; both products
+ *   are exact in binary32 and the difference is rounded once.
+ *
+ * F16 weights are plain row-major binary16 [rows, cols].
+ */
+#ifndef DS4MOE_H
+#define DS4MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  DS4MOE_OK = 0,
+  DS4MOE_EINVAL = -1,       /* NULL pointer, bad enum, negative size */
+  DS4MOE_ESHAPE = -2,       /* dimension not a multiple of 256, k > E, T out of range */
+  DS4MOE_EALIGN = -3,       /* pointer not aligned as required */
+  DS4MOE_EWORKSPACE = -4,   /* workspace smaller than ds4moe_workspace_bytes() */
+  DS4MOE_EHIP = -5,         /* the HIP runtime reported an error at launch */
+  DS4MOE_EUNSUPPORTED = -6  /* valid but not supported by this build */
+};
+
+enum { DS4MOE_FMT_F16 = 0, DS4MOE_FMT_CB2 = 1, DS4MOE_FMT_Q2K = 2 };
+enum { DS4MOE_DT_F32 = 0, DS4MOE_DT_BF16 = 1 };
+enum { DS4MOE_MODE_DECODE = 0, DS4MOE_MODE_PREFILL = 1, DS4MOE_MODE_ROUTE = 2 };
+
+/* Largest T accepted by ds4moe_forward_decode (tokens beyond 16 are run as
+ * consecutive groups of 16). */
+#define DS4MOE_DECODE_MAX_T 64
+/* Limits of this build: d_model, d_ff, d_ff_shared <= 16384; E <= 1024;
+ * k <= 16. */
+
+/* Layer descriptor.  Plain data: read during the call, not retained.
+ * Alignment: every pointer 16-byte aligned. */
+typedef struct {
+  int32_t d_model;      /* d, multiple of 256 */
+  int32_t n_experts;    /* E */
+  int32_t top_k;        /* k, 1 <= k <= E */
+  int32_t d_ff;         /* routed expert intermediate f, multiple of 256 */
+  int32_t d_ff_shared;  /* shared expert intermediate fs, multiple of 256 */
+  const uint16_t *router_w;    /* F16 [E, d] */
+  const float *router_bias;    /* fp32 [E] added to the logits, or NULL */
+  const uint16_t *sh_gate;     /* F16 [fs, d] */
+  const uint16_t *sh_up;       /* F16 [fs, d] */
+  const uint16_t *sh_down;     /* F16 [d, fs] */
+  const void *gate;            /* CB2, E packed [f, d] matrices */
+  const void *up;              /* CB2, E packed [f, d] matrices */
+  const void *down;            /* Q2K, E packed [d, f] matrices */
+} ds4moe_layer;
+
+/* Bytes of one packed [rows, cols] matrix (host function; 0 if cols % 256 != 0
+ * or fmt is unknown).  F16: rows*cols*2. */
+size_t ds4moe_packed_bytes(int fmt, int64_t rows, int64_t cols);
+
+/* Quantize fp32 [rows, cols] (row-major, finite values) into the packed
+ * matrix `packed` (ds4moe_packed_bytes bytes).  fmt: DS4MOE_FMT_CB2 or
+ * DS4MOE_FMT_Q2K.  Deterministic: the bytes equal those of the format's
+ * reference quantizer (steps in the library's documentation). */
+int ds4moe_quantize(int fmt, const float *w, int64_t rows, int64_t cols, void *packed, void *stream);
+
+/* Decode a packed matrix to fp32 [rows, cols] (bit-exact). */
+int ds4moe_dequantize(int fmt, const void *packed, int64_t rows, int64_t cols, float *w, void *stream);
+
+/* Workspace bytes for a call with T tokens (host function).  mode:
+ * DS4MOE_MODE_DECODE for ds4moe_forward_decode, DS4MOE_MODE_PREFILL for
+ * ds4moe_forward_prefill, DS4MOE_MODE_ROUTE for ds4moe_route.  0 on invalid
+ * input. */
+size_t ds4moe_workspace_bytes(const ds4moe_layer *L, int64_t T, int mode);
+
+/* Router + top-k + gate weights + token grouping for T tokens.
+ * x: [T, d] fp32 or bf16 (x_dtype).  Outputs: topk_idx [T, k] int32 (ascending
+ * expert index per token), topk_w [T, k] fp32 (softmax of the selected
+ * logits), counts [E], offsets [E+1] (exclusive scan of counts), perm [T*k]
+ * (slot ids t*k + j sorted by expert, then token).  counts/offsets/perm may
+ * be NULL (not written).  1 <= T. */
+int ds4moe_route(const ds4moe_layer *L, const void *x, int x_dtype, int64_t T, int32_t *topk_idx,
+                 float *topk_w, int32_t *counts, int32_t *offsets, int32_t *perm, void *ws,
+                 size_t ws_bytes, void *stream);
+
+/* Full layer for 1 <= T <= DS4MOE_DECODE_MAX_T tokens (batched decode).
+ * y: [T, d] fp32.  topk_idx_out / topk_w_out: optional [T, k] copies of the
+ * routing (NULL = not written). */
+int ds4moe_forward_decode(const ds4moe_layer *L, const void *x, int x_dtype, int64_t T, float *y,
+                          int32_t *topk_idx_out, float *topk_w_out, void *ws, size_t ws_bytes,
+                          void *stream);
+
+/* Full layer for any T >= 1 (prefill chunk; grouped GEMMs).  Same outputs
+ * as ds4moe_forward_decode plus the optional permutation perm_out [T*k]. */
+int ds4moe_forward_prefill(const ds4moe_layer *L, const void *x, int x_dtype, int64_t T, float *y,
+                           int32_t *topk_idx_out, float *topk_w_out, int32_t *perm_out, void *ws,
+                           size_t ws_bytes, void *stream);
+
+/* Opt-in per-kernel timing (profiling aid).  While enabled, every kernel
+ * the library launches is bracketed by two HIP events on its stream, which
+ * adds a little launch overhead.  Thread-safe. */
+int ds4moe_trace_enable(int on);
+
+/* Wait for the recorded events and accumulate them; then write, for up to
+ * `cap` kernels, the accumulated milliseconds (ms[i]) and launch counts
+ * (counts[i]), and their names as one '\n'-separated string into `names`
+ * (host buffers; any may be NULL).  reset != 0 clears the totals afterwards.
+ * Returns the number of kernels seen, or DS4MOE_EHIP. */
+int ds4moe_trace_read(char *names, size_t names_cap, double *ms, long long *counts, int cap, int reset);
+
+/* Static string for a status code. */
+const char *ds4moe_strerror(int status);
+
+/* Host copy of the codebook grid levels, levels[256*8] (entry-major). */
+void ds4moe_grid_levels(uint8_t *levels);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DS4MOE_H */

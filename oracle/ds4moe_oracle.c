@@ -128,6 +128,7 @@ void orc_grid_levels(uint8_t *levels)
 /* Magnitudes m = 2*level + 1 of the grid, filled once before any parallel
  * region by ensure_grid(). */
 static int32_t g_mag[256 * 8];
+static int32_t g_magT[8][256]; /* g_magT[k][e] = m_ek */
 static int g_grid_ready = 0;
 
 static void ensure_grid(void)
@@ -137,6 +138,9 @@ static void ensure_grid(void)
         orc_grid_levels(lv);
         for (int i = 0; i < 256 * 8; i++)
             g_mag[i] = 2 * lv[i] + 1;
+        for (int e = 0; e < 256; e++)
+            for (int k = 0; k < 8; k++)
+                g_magT[k][e] = g_mag[8 * e + k];
         g_grid_ready = 1;
     }
 }
@@ -205,6 +209,31 @@ static uint16_t f16_clamped(float v)
     return orc_f64_to_f16((double)v);
 }
 
+/* Integer score of all 256 grid entries for one group:
+ *   sum_k (4096 m_ek^2 - 2 R_k m_ek)  [+ 4 min_k R_k m_ek if odd]
+ * Values stay below 2^25, so int32 is exact. */
+
+__attribute__((target_clones("avx2", "default"))) static void search_scores(const int32_t R[8], int odd,
+                                                                           int32_t score[256])
+{
+    int32_t mn[256];
+    for (int e = 0; e < 256; e++) {
+        score[e] = 0;
+        mn[e] = INT32_MAX;
+    }
+    for (int k = 0; k < 8; k++) {
+        for (int e = 0; e < 256; e++) {
+            int32_t m = g_magT[k][e];
+            int32_t f = R[k] * m;
+            score[e] += 4096 * m * m - 2 * f;
+            mn[e] = f < mn[e] ? f : mn[e];
+        }
+    }
+    if (odd)
+        for (int e = 0; e < 256; e++)
+            score[e] += 4 * mn[e];
+}
+
 /*
  * CB2 quantizer (deterministic; its steps are this library's own, since the
  * pages give none):
@@ -264,25 +293,13 @@ static void cb2_quantize_block(const float *x, uint8_t *blk, uint16_t *dout)
                 }
             }
             int odd = nneg & 1;
+            /* score of every entry, then the lowest (lower index on ties) */
+            int32_t score[256];
+            search_scores(R, odd, score);
             int best = 0;
-            int64_t best_score = 0;
-            for (int e = 0; e < 256; e++) {
-                int64_t score = 0;
-                int64_t minflip = -1;
-                for (int k = 0; k < 8; k++) {
-                    int64_t m = grid_mag(e, k);
-                    score += 4096 * m * m - 2 * (int64_t)R[k] * m;
-                    int64_t f = (int64_t)R[k] * m;
-                    if (minflip < 0 || f < minflip)
-                        minflip = f;
-                }
-                if (odd)
-                    score += 4 * minflip;
-                if (e == 0 || score < best_score) {
+            for (int e = 1; e < 256; e++)
+                if (score[e] < score[best])
                     best = e;
-                    best_score = score;
-                }
-            }
             if (odd) {
                 int kf = 0;
                 int64_t fmin = -1;
@@ -481,12 +498,16 @@ void orc_f16_matmul(const uint16_t *w, int64_t rows, int64_t cols, const double 
 {
 #pragma omp parallel for schedule(static)
     for (int64_t r = 0; r < rows; r++) {
+        double *wrow = (double *)malloc(sizeof(double) * (size_t)cols);
+        for (int64_t i = 0; i < cols; i++)
+            wrow[i] = orc_f16_to_f64(w[r * cols + i]);
         for (int64_t t = 0; t < n; t++) {
             double acc = 0.0;
             for (int64_t i = 0; i < cols; i++)
-                acc += orc_f16_to_f64(w[r * cols + i]) * X[t * cols + i];
+                acc += wrow[i] * X[t * cols + i];
             Y[t * rows + r] = acc;
         }
+        free(wrow);
     }
 }
 

@@ -29,7 +29,7 @@ _SRC = os.path.join(_HERE, "ds4moe_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 QK = 256
 
-GCC_CMD = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-ffp-contract=off",
+GCC_CMD = ["gcc", "-O3", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-ffp-contract=off",
            "-fno-fast-math", "-Wall", "-Wextra", "-o", _LIB_PATH, _SRC, "-lm"]
 
 

@@ -1,0 +1,150 @@
+"""Helpers for the GPU parity tests: seeded layers on the device and the
+oracle's view of the same layer, plus the error metric.
+
+Weights reach the device in two ways:
+  * oracle-packed: the oracle quantizes, the bytes are uploaded (small layers);
+  * device-packed: seeded fp32 weights are uploaded and quantized by
+    ds4moe_quantize, expert by expert (full-size layers).  The oracle then
+    quantizes the experts it needs from the same fp32 weights itself, and the
+    tests check those bytes against the device's.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from oracle import oracle as O
+from bit_quantized_routed_router_amd import ds4moe as D
+from bit_quantized_routed_router_amd import synthetic as S
+
+
+def dev(a: np.ndarray) -> torch.Tensor:
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).cuda()
+
+
+def host(t: torch.Tensor, dtype=None) -> np.ndarray:
+    a = t.detach().cpu().numpy()
+    if dtype is not None:
+        a = a.view(dtype)
+    return a
+
+
+def rel_err_rows(y: np.ndarray, ref: np.ndarray) -> float:
+    """max over rows of ||y - ref||_inf / ||ref||_inf."""
+    y = np.asarray(y, dtype=np.float64).reshape(ref.shape)
+    num = np.abs(y - ref).max(axis=1)
+    den = np.abs(ref).max(axis=1)
+    return float((num / den).max())
+
+
+class SeededLayer:
+    """A synthetic layer (config cfg) held both on the device and for the oracle."""
+
+    def __init__(self, cfg: S.Config, device_quantize: bool, cfg_seed: int | None = None, chunk: int = 16):
+        self.cfg = cfg
+        self.seed = cfg.seed if cfg_seed is None else cfg_seed
+        c = cfg
+        self.router = S.gen_router(cfg, cfg_seed=cfg_seed)
+        self.bias = S.gen_bias(cfg)
+        self.sh = S.gen_shared(cfg, cfg_seed=cfg_seed)
+        cb = D.packed_bytes(D.FMT_CB2, c.f, c.d)
+        qb = D.packed_bytes(D.FMT_Q2K, c.d, c.f)
+        assert cb == O.cb2_bytes(c.f, c.d) and qb == O.q2k_bytes(c.d, c.f)
+        self.cb, self.qb = cb, qb
+        self.gate = torch.empty(c.E * cb, dtype=torch.uint8, device="cuda")
+        self.up = torch.empty(c.E * cb, dtype=torch.uint8, device="cuda")
+        self.down = torch.empty(c.E * qb, dtype=torch.uint8, device="cuda")
+        self._oracle_packed = {}
+        if device_quantize:
+            for e0 in range(0, c.E, chunk):
+                es = list(range(e0, min(c.E, e0 + chunk)))
+                mats = S.gen_experts(cfg, es, threads=16, cfg_seed=cfg_seed)
+                for e, (g, u, dn) in zip(es, mats):
+                    D.quantize(D.FMT_CB2, dev(g), c.f, c.d, self.gate[e * cb:(e + 1) * cb])
+                    D.quantize(D.FMT_CB2, dev(u), c.f, c.d, self.up[e * cb:(e + 1) * cb])
+                    D.quantize(D.FMT_Q2K, dev(dn), c.d, c.f, self.down[e * qb:(e + 1) * qb])
+                torch.cuda.synchronize()
+        else:
+            for e in range(c.E):
+                self._oracle_packed[e] = self._oracle_quantize(e)
+                gp, up, dp = self._oracle_packed[e]
+                self.gate[e * cb:(e + 1) * cb] = dev(gp)
+                self.up[e * cb:(e + 1) * cb] = dev(up)
+                self.down[e * qb:(e + 1) * qb] = dev(dp)
+        self.layer = D.Layer(c.d, c.E, c.k, c.f, c.fs, dev(self.router),
+                             None if self.bias is None else dev(self.bias),
+                             dev(self.sh[0]), dev(self.sh[1]), dev(self.sh[2]), self.gate, self.up, self.down)
+        self.oracle = O.Layer(c.d, c.E, c.k, c.f, c.fs, self.router, self.bias, self.sh[0], self.sh[1], self.sh[2],
+                              self.oracle_expert)
+
+    def _oracle_quantize(self, e):
+        g, u, dn = S.gen_expert(self.cfg, e, cfg_seed=self.seed)
+        return O.cb2_quantize(g), O.cb2_quantize(u), O.q2k_quantize(dn)
+
+    def oracle_expert(self, e):
+        """The oracle's own packing of expert e (from the seeded fp32 weights)."""
+        if e not in self._oracle_packed:
+            self._oracle_packed[e] = self._oracle_quantize(e)
+        return self._oracle_packed[e]
+
+    def device_expert_bytes(self, e):
+        cb, qb = self.cb, self.qb
+        return (host(self.gate[e * cb:(e + 1) * cb]), host(self.up[e * cb:(e + 1) * cb]),
+                host(self.down[e * qb:(e + 1) * qb]))
+
+    def x(self, T=None, variant=None):
+        return S.gen_x(self.cfg, variant=variant, T=T)
+
+    def x_dev(self, x):
+        return dev(x)
+
+    def x_dtype(self):
+        return D.DT_F32 if self.cfg.x_dtype == "f32" else D.DT_BF16
+
+    # ---------------------------------------------------------------- calls
+    def route(self, x):
+        T = x.shape[0]
+        c = self.cfg
+        ws, n = self.layer.workspace(T, D.MODE_ROUTE)
+        idx = torch.empty((T, c.k), dtype=torch.int32, device="cuda")
+        w = torch.empty((T, c.k), dtype=torch.float32, device="cuda")
+        counts = torch.empty(c.E, dtype=torch.int32, device="cuda")
+        offsets = torch.empty(c.E + 1, dtype=torch.int32, device="cuda")
+        perm = torch.empty(T * c.k, dtype=torch.int32, device="cuda")
+        D.route(self.layer.desc, self.x_dev(x), self.x_dtype(), T, idx, w, counts, offsets, perm, ws, n)
+        torch.cuda.synchronize()
+        return dict(idx=host(idx), w=host(w), counts=host(counts), offsets=host(offsets), perm=host(perm))
+
+    def forward(self, x, mode):
+        T = x.shape[0]
+        c = self.cfg
+        ws, n = self.layer.workspace(T, mode)
+        y = torch.empty((T, c.d), dtype=torch.float32, device="cuda")
+        idx = torch.empty((T, c.k), dtype=torch.int32, device="cuda")
+        w = torch.empty((T, c.k), dtype=torch.float32, device="cuda")
+        out = dict()
+        if mode == D.MODE_DECODE:
+            D.forward_decode(self.layer.desc, self.x_dev(x), self.x_dtype(), T, y, idx, w, ws, n)
+        else:
+            perm = torch.empty(T * c.k, dtype=torch.int32, device="cuda")
+            D.forward_prefill(self.layer.desc, self.x_dev(x), self.x_dtype(), T, y, idx, w, perm, ws, n)
+            out["perm"] = perm
+        torch.cuda.synchronize()
+        out = {k: host(v) for k, v in out.items()}
+        out.update(y=host(y), idx=host(idx), w=host(w))
+        return out
+
+
+def check_routing(got: dict, ref: dict, k: int, w_tol: float = 1e-5):
+    """Indices, counts, offsets and permutation bit-exact; weights within w_tol."""
+    assert np.array_equal(got["idx"], ref["idx"]), "top-k indices differ"
+    assert np.abs(got["w"] - ref["w"]).max() <= w_tol
+    assert np.abs(got["w"].sum(axis=1) - 1.0).max() <= 1e-5
+    if "counts" in got:
+        assert np.array_equal(got["counts"], ref["counts"])
+        assert np.array_equal(got["offsets"], ref["offsets"])
+    if "perm" in got:
+        assert np.array_equal(got["perm"], ref["perm"])

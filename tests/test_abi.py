@@ -1,0 +1,120 @@
+"""Host-side checks of the C ABI (no device work): the library loads, exports
+every function declared in include/ds4moe.h, sizes its buffers as the format
+prescribes, and rejects bad arguments before launching anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from bit_quantized_routed_router_amd import ds4moe as D
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ds4moe.h")
+
+A = 0x10000  # stand-in device addresses: aligned, never dereferenced
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(ds4moe_\w+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_function():
+    lib = D.lib()
+    names = header_functions()
+    assert "ds4moe_forward_decode" in names and "ds4moe_quantize" in names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) <= set(D.EXPORTS)
+
+
+def test_packed_sizes():
+    assert D.packed_bytes(D.FMT_CB2, 2048, 4096) == 2048 * 16 * 66 == 2162688
+    assert D.packed_bytes(D.FMT_Q2K, 4096, 2048) == 4096 * 8 * 84 == 2752512
+    assert D.packed_bytes(D.FMT_F16, 3, 5) == 30
+    assert D.packed_bytes(D.FMT_CB2, 4, 300) == 0
+    assert D.packed_bytes(9, 4, 256) == 0
+
+
+def desc(d=4096, E=256, k=6, f=2048, fs=2048, **ptr):
+    p = dict(router_w=A, router_bias=None, sh_gate=A, sh_up=A, sh_down=A, gate=A, up=A, down=A)
+    p.update(ptr)
+    return D.LayerDesc(d, E, k, f, fs, p["router_w"], p["router_bias"], p["sh_gate"], p["sh_up"], p["sh_down"],
+                       p["gate"], p["up"], p["down"])
+
+
+def test_workspace_sizes():
+    L = desc()
+    dec = D.workspace_bytes(L, 1, D.MODE_DECODE)
+    assert dec > 0 and dec % 256 == 0
+    assert D.workspace_bytes(L, 64, D.MODE_DECODE) == D.workspace_bytes(L, 16, D.MODE_DECODE)
+    pre = D.workspace_bytes(L, 2048, D.MODE_PREFILL)
+    assert pre >= 2048 * 6 * 4096 * 4  # per-slot fp32 outputs
+    assert D.workspace_bytes(L, 2048, D.MODE_ROUTE) < pre
+    assert D.workspace_bytes(L, 0, D.MODE_DECODE) == 0
+    assert D.workspace_bytes(desc(d=300), 1, D.MODE_DECODE) == 0
+    assert D.workspace_bytes(L, 1, 7) == 0
+
+
+def call_decode(L, x=A, dt=D.DT_BF16, T=1, y=A, ws=A * 16, nbytes=1 << 40):
+    lib = D.lib()
+    return lib.ds4moe_forward_decode(ctypes.byref(L) if L is not None else None, x, dt, T, y, None, None, ws,
+                                     nbytes, None)
+
+
+def test_forward_argument_errors():
+    L = desc()
+    assert call_decode(None) == D.EINVAL
+    assert call_decode(desc(router_w=None)) == D.EINVAL
+    assert call_decode(desc(d=4000)) == D.ESHAPE
+    assert call_decode(desc(f=100)) == D.ESHAPE
+    assert call_decode(desc(k=7, E=6)) == D.ESHAPE
+    assert call_decode(desc(k=0)) == D.ESHAPE
+    assert call_decode(desc(E=2000)) == D.ESHAPE
+    assert call_decode(desc(gate=A + 4)) == D.EALIGN
+    assert call_decode(desc(router_bias=A + 2)) == D.EALIGN
+    assert call_decode(L, T=0) == D.ESHAPE
+    assert call_decode(L, T=65) == D.ESHAPE
+    assert call_decode(L, dt=5) == D.EINVAL
+    assert call_decode(L, x=None) == D.EINVAL
+    assert call_decode(L, y=None) == D.EINVAL
+    assert call_decode(L, x=A + 8) == D.EALIGN
+    assert call_decode(L, ws=A + 16) == D.EALIGN
+    assert call_decode(L, nbytes=1024) == D.EWORKSPACE
+    lib = D.lib()
+    assert lib.ds4moe_forward_prefill(ctypes.byref(L), A, D.DT_BF16, 0, A, None, None, None, A, 1 << 40, None) == D.ESHAPE
+    assert lib.ds4moe_forward_prefill(ctypes.byref(L), A, D.DT_BF16, 10**7, A, None, None, None, A, 1 << 40, None) == D.ESHAPE
+    assert lib.ds4moe_route(ctypes.byref(L), A, D.DT_BF16, 4, None, A, None, None, None, A, 1 << 40, None) == D.EINVAL
+    assert lib.ds4moe_route(ctypes.byref(L), A, D.DT_BF16, 4, A + 2, A, None, None, None, A, 1 << 40, None) == D.EALIGN
+
+
+def test_codec_argument_errors():
+    lib = D.lib()
+    assert lib.ds4moe_quantize(7, A, 4, 256, A, None) == D.EINVAL
+    assert lib.ds4moe_quantize(D.FMT_F16, A, 4, 256, A, None) == D.EINVAL
+    assert lib.ds4moe_quantize(D.FMT_CB2, A, 4, 300, A, None) == D.ESHAPE
+    assert lib.ds4moe_quantize(D.FMT_CB2, A, -1, 256, A, None) == D.EINVAL
+    assert lib.ds4moe_quantize(D.FMT_CB2, None, 4, 256, A, None) == D.EINVAL
+    assert lib.ds4moe_quantize(D.FMT_Q2K, A + 4, 4, 256, A, None) == D.EALIGN
+    assert lib.ds4moe_quantize(D.FMT_Q2K, A, 0, 256, None, None) == D.OK  # empty: nothing to do
+    assert lib.ds4moe_dequantize(D.FMT_Q2K, A, 4, 257, A, None) == D.ESHAPE
+
+
+def test_strerror_covers_codes():
+    for c in (D.OK, D.EINVAL, D.ESHAPE, D.EALIGN, D.EWORKSPACE, D.EHIP, D.EUNSUPPORTED):
+        assert D.strerror(c) and D.strerror(c) != "unknown status"
+    assert D.strerror(12345) == "unknown status"
+
+
+def test_grid_export_matches_oracle():
+    from oracle import oracle as O
+    assert (D.grid_levels() == O.grid_levels()).all()
+
+
+def test_binding_fails_loudly_without_library(monkeypatch):
+    monkeypatch.setattr(D, "_lib", None)
+    monkeypatch.setattr(D, "_LIB_PATH", "/nonexistent/libds4moe.so")
+    with pytest.raises(RuntimeError):
+        D.lib()

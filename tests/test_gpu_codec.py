@@ -1,0 +1,100 @@
+"""GPU parity of the codecs: ds4moe_dequantize bit-exact and ds4moe_quantize
+byte-exact against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as O
+from bit_quantized_routed_router_amd import ds4moe as D
+from bit_quantized_routed_router_amd import synthetic as S
+from tests.gpu_helpers import dev, host
+from tests.test_oracle_formats import canonical_cb2, canonical_q2k
+
+pytestmark = pytest.mark.gpu
+
+
+def gpu_quant(fmt, w):
+    rows, cols = w.shape
+    out = torch.zeros(D.packed_bytes(fmt, rows, cols), dtype=torch.uint8, device="cuda")
+    D.quantize(fmt, dev(w), rows, cols, out)
+    torch.cuda.synchronize()
+    return host(out)
+
+
+def gpu_dequant(fmt, packed, rows, cols):
+    out = torch.empty((rows, cols), dtype=torch.float32, device="cuda")
+    D.dequantize(fmt, dev(packed), rows, cols, out)
+    torch.cuda.synchronize()
+    return host(out)
+
+
+def test_grid_matches_oracle():
+    assert np.array_equal(D.grid_levels(), O.grid_levels())
+
+
+@pytest.mark.parametrize("rows,cols,scale", [(1, 256, 0.02), (37, 512, 0.02), (64, 4096, 0.02), (5, 768, 30.0)])
+def test_quantize_byte_exact(rows, cols, scale):
+    w = (np.random.default_rng(rows * cols).standard_normal((rows, cols)) * scale).astype(np.float32)
+    assert np.array_equal(gpu_quant(D.FMT_CB2, w), O.cb2_quantize(w))
+    assert np.array_equal(gpu_quant(D.FMT_Q2K, w), O.q2k_quantize(w))
+
+
+def test_quantize_edge_blocks_byte_exact():
+    x = np.zeros((6, 256), dtype=np.float32)
+    x[1, 17] = 0.5                       # single spike
+    x[2, :] = 1e-9                       # d underflows
+    x[3, 5], x[3, 6] = 3e38, -3e38       # d clamps at 65504
+    x[4, :] = -0.01                      # all negative
+    x[5, ::2] = 0.03                     # sub-blocks with exact ties
+    x[5, 1::2] = -0.03
+    assert np.array_equal(gpu_quant(D.FMT_CB2, x), O.cb2_quantize(x))
+    assert np.array_equal(gpu_quant(D.FMT_Q2K, x), O.q2k_quantize(x))
+
+
+def test_quantize_canonical_round_trip():
+    rng = np.random.default_rng(9)
+    cb = canonical_cb2(rng, 32)
+    w = O.cb2_dequantize(cb, 32, 256)
+    assert np.array_equal(gpu_quant(D.FMT_CB2, w), cb)
+    qk = canonical_q2k(rng, 32)
+    w = O.q2k_dequantize(qk, 32, 256)
+    assert np.array_equal(gpu_quant(D.FMT_Q2K, w), qk)
+
+
+def test_dequantize_bit_exact():
+    rng = np.random.default_rng(10)
+    w = (rng.standard_normal((48, 1024)) * 0.02).astype(np.float32)
+    for fmt, quant, deq in ((D.FMT_CB2, O.cb2_quantize, O.cb2_dequantize), (D.FMT_Q2K, O.q2k_quantize, O.q2k_dequantize)):
+        p = quant(w)
+        got = gpu_dequant(fmt, p, 48, 1024)
+        assert np.array_equal(got.view(np.uint32), deq(p, 48, 1024).view(np.uint32))
+
+
+def test_dequantize_random_codes_bit_exact():
+    """Arbitrary code bytes (every index, sign code and scale) with finite scales."""
+    rng = np.random.default_rng(11)
+    rows, cols = 16, 512
+    n = rows * cols // 256
+    codes = rng.integers(0, 256, n * 64, dtype=np.uint8)
+    d = (np.abs(rng.standard_normal(n)) * 1e-3).astype(np.float16).view(np.uint16)
+    cb = np.concatenate([codes, d.view(np.uint8)])
+    assert np.array_equal(gpu_dequant(D.FMT_CB2, cb, rows, cols).view(np.uint32),
+                          O.cb2_dequantize(cb, rows, cols).view(np.uint32))
+    sub = rng.integers(0, 256, n * 16, dtype=np.uint8)
+    sup = (np.abs(rng.standard_normal(2 * n)) * 1e-3).astype(np.float16).view(np.uint16)
+    qk = np.concatenate([codes, sub, sup.view(np.uint8)])
+    assert np.array_equal(gpu_dequant(D.FMT_Q2K, qk, rows, cols).view(np.uint32),
+                          O.q2k_dequantize(qk, rows, cols).view(np.uint32))
+
+
+def test_full_size_expert_quantize_byte_exact():
+    """One routed expert at the DeepSeek V4 Flash shape (f 2048, d 4096)."""
+    cfg = S.CONFIGS["decode1"]
+    g, u, dn = S.gen_expert(cfg, 7)
+    assert np.array_equal(gpu_quant(D.FMT_CB2, g), O.cb2_quantize(g))
+    assert np.array_equal(gpu_quant(D.FMT_Q2K, dn), O.q2k_quantize(dn))
+
+
+def test_empty_matrix_is_a_no_op():
+    D.quantize(D.FMT_CB2, 0, 0, 256, 0)
+    D.dequantize(D.FMT_Q2K, 0, 0, 512, 0)

@@ -1,0 +1,157 @@
+"""GPU parity of routing and of the full layer against the oracle, at the
+tiny configuration (all experts oracle-quantized) and at the full DeepSeek V4
+Flash shapes (device-quantized experts whose bytes are checked against the
+oracle's for every expert the oracle uses).
+
+Bars: expert indices, counts, offsets and permutation bit-exact; gate weights
+within 1e-5 (fp32 softmax of fp32-accumulated logits); layer outputs within
+2e-3 per token row, max |y - ref| / max |ref| (fp32 accumulation with binary16
+activations; the expected error is ~1e-4)."""
+import numpy as np
+import pytest
+
+from bit_quantized_routed_router_amd import ds4moe as D
+from bit_quantized_routed_router_amd import synthetic as S
+from tests.gpu_helpers import SeededLayer, check_routing, rel_err_rows
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-3
+
+
+def oracle_ref(L: SeededLayer, x, tokens=None):
+    r = L.oracle.forward(x, L.cfg.x_dtype, tokens=tokens)
+    return dict(idx=r["idx"], w=r["w"], counts=r["counts"], offsets=r["offsets"], perm=r["perm"], y=r["y64"],
+                tokens=r["tokens"])
+
+
+def check_used_experts_bytes(L: SeededLayer, idx):
+    for e in np.unique(idx):
+        for got, ref in zip(L.device_expert_bytes(int(e)), L.oracle_expert(int(e))):
+            assert np.array_equal(got, ref), f"device packing of expert {e} differs from the oracle's"
+
+
+# ------------------------------------------------------------------ tiny
+@pytest.fixture(scope="module")
+def tiny():
+    print("[setup] tiny layer (oracle-packed)", flush=True)
+    return SeededLayer(S.CONFIGS["tiny"], device_quantize=False)
+
+
+def test_tiny_route(tiny):
+    x = tiny.x()
+    ref = oracle_ref(tiny, x)
+    got = tiny.route(x)
+    check_routing(got, ref, tiny.cfg.k)
+
+
+@pytest.mark.parametrize("mode", [D.MODE_DECODE, D.MODE_PREFILL])
+def test_tiny_forward(tiny, mode):
+    x = tiny.x()
+    ref = oracle_ref(tiny, x)
+    got = tiny.forward(x, mode)
+    check_routing(got, ref, tiny.cfg.k)
+    err = rel_err_rows(got["y"], ref["y"])
+    print(f"tiny mode={mode} rel err {err:.3e}")
+    assert err <= TOL
+
+
+@pytest.mark.parametrize("T", [1, 3, 16, 17, 40, 64])
+def test_tiny_decode_token_counts(tiny, T):
+    """Ragged decode batches, including more than one 16-token group."""
+    x = tiny.x(T=T, variant=100 + T)
+    ref = oracle_ref(tiny, x)
+    got = tiny.forward(x, D.MODE_DECODE)
+    assert np.array_equal(got["idx"], ref["idx"])
+    assert rel_err_rows(got["y"], ref["y"]) <= TOL
+
+
+@pytest.mark.parametrize("T", [1, 15, 33, 200])
+def test_tiny_prefill_token_counts(tiny, T):
+    x = tiny.x(T=T, variant=200 + T)
+    ref = oracle_ref(tiny, x)
+    got = tiny.forward(x, D.MODE_PREFILL)
+    check_routing(got, ref, tiny.cfg.k)
+    assert rel_err_rows(got["y"], ref["y"]) <= TOL
+
+
+@pytest.mark.parametrize("T", [20, 200])
+def test_tiny_route_many_tokens(tiny, T):
+    x = tiny.x(T=T, variant=300 + T)
+    check_routing(tiny.route(x), oracle_ref(tiny, x), tiny.cfg.k)
+
+
+def test_tiny_decode_equals_prefill_routing(tiny):
+    x = tiny.x()
+    a = tiny.forward(x, D.MODE_DECODE)
+    b = tiny.forward(x, D.MODE_PREFILL)
+    assert np.array_equal(a["idx"], b["idx"])
+    assert rel_err_rows(a["y"], b["y"].astype(np.float64)) <= TOL
+
+
+def test_tiny_repeatable(tiny):
+    x = tiny.x()
+    a = tiny.forward(x, D.MODE_DECODE)
+    b = tiny.forward(x, D.MODE_DECODE)
+    assert np.array_equal(a["y"], b["y"])
+    a = tiny.forward(x, D.MODE_PREFILL)
+    b = tiny.forward(x, D.MODE_PREFILL)
+    assert np.array_equal(a["y"], b["y"])
+
+
+# ------------------------------------------------------------------ full size
+@pytest.fixture(scope="module")
+def decode1():
+    print("[setup] decode1 layer (device-packed, 256 experts)", flush=True)
+    return SeededLayer(S.CONFIGS["decode1"], device_quantize=True)
+
+
+def test_decode1_forward(decode1):
+    x = decode1.x()
+    ref = oracle_ref(decode1, x)
+    check_used_experts_bytes(decode1, ref["idx"])
+    got = decode1.forward(x, D.MODE_DECODE)
+    check_routing(got, ref, decode1.cfg.k)
+    err = rel_err_rows(got["y"], ref["y"])
+    print(f"decode1 rel err {err:.3e}")
+    assert err <= TOL
+
+
+def test_decode1_prefill_entry_point(decode1):
+    x = decode1.x()
+    ref = oracle_ref(decode1, x)
+    got = decode1.forward(x, D.MODE_PREFILL)
+    check_routing(got, ref, decode1.cfg.k)
+    assert rel_err_rows(got["y"], ref["y"]) <= TOL
+
+
+def test_decode16_forward():
+    print("[setup] decode16 layer (device-packed, hot-pool bias)", flush=True)
+    L = SeededLayer(S.CONFIGS["decode16"], device_quantize=True)
+    x = L.x()
+    ref = oracle_ref(L, x)
+    assert 58 <= len(np.unique(ref["idx"])) <= 62
+    check_used_experts_bytes(L, ref["idx"])
+    got = L.forward(x, D.MODE_DECODE)
+    check_routing(got, ref, L.cfg.k)
+    err = rel_err_rows(got["y"], ref["y"])
+    print(f"decode16 rel err {err:.3e}")
+    assert err <= TOL
+    r = L.route(x)
+    check_routing(r, ref, L.cfg.k)
+
+
+def test_prefill_2048_sampled():
+    """2048-token prefill: routing for all tokens bit-exact, outputs of a
+    seeded sample of tokens against the oracle."""
+    print("[setup] prefill layer (device-packed, Zipf bias)", flush=True)
+    L = SeededLayer(S.CONFIGS["prefill"], device_quantize=True)
+    x = L.x()
+    sample = np.sort(np.random.default_rng(42).choice(L.cfg.T, 24, replace=False))
+    sample = np.unique(np.concatenate([sample, [0, L.cfg.T - 1]]))
+    ref = oracle_ref(L, x, tokens=sample)
+    got = L.forward(x, D.MODE_PREFILL)
+    check_routing(got, ref, L.cfg.k)
+    check_used_experts_bytes(L, ref["idx"][sample])
+    err = rel_err_rows(got["y"][sample], ref["y"])
+    print(f"prefill sampled rel err {err:.3e}")
+    assert err <= TOL

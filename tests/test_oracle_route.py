@@ -73,3 +73,23 @@ def test_permute_brute_force(T, E, k):
 def test_topk_gap_helper():
     logits = np.array([[3.0, 1.0, 2.0, 2.5]])
     assert np.allclose(O.topk_gap(logits, 2), [0.5])
+
+
+def test_configs_carry_the_selected_seeds():
+    """synthetic.CONFIGS holds the variants find_seeds.py selected."""
+    import json
+    import os
+    sel = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "seeds.json")))
+    for name in ("decode1", "decode16", "prefill"):
+        c = S.CONFIGS[name]
+        assert c.router_variant == sel[name]["router_variant"]
+        assert c.x_variant == sel[name]["x_variant"]
+    assert S.CONFIGS["prefill"].zipf_beta == sel["prefill"]["zipf_beta"]
+
+
+@pytest.mark.slow
+def test_decode1_gap_rule_holds():
+    cfg = S.CONFIGS["decode1"]
+    X = O.x_to_f64(S.gen_x(cfg), cfg.x_dtype)
+    L = O.router_logits(X, S.gen_router(cfg), S.gen_bias(cfg))
+    assert O.topk_gap(L, cfg.k).min() > 1e-4
