@@ -170,7 +170,9 @@ def bench_decode(args):
     # distinct experts per step (1 token: k distinct) -> algorithmic bytes
     nb = decode_bytes(cfg, cfg.k, T=1)
     dom = "k_gateup_decode"
-    ms_dom, cnt_dom = kern.get(dom, (float("nan"), 0))
+    hits = [v for k2, v in kern.items() if k2 == dom or k2.startswith(dom + "<")]
+    ms_dom = sum(v[0] for v in hits) if hits else float("nan")
+    cnt_dom = sum(v[1] for v in hits)
     dur_us = ms_dom / max(cnt_dom, 1) * 1e3
     achieved = nb[dom] / (dur_us * 1e-6) / 1e9
     res = dict(ms_per_step=graph_ms, eager_ms_per_step=eager_ms, kernels={k: dict(mean_us=v[0] / max(v[1], 1) * 1e3,
