@@ -38,11 +38,18 @@ WsLayout ws_layout(const ds4moe_layer& L, int64_t T, int mode) {
   y.tok_slot = take(dmax * kDecodeGroup * 4);
   y.tiles = take(((S + 15) / 16 + E) * 2 * 4);
   y.ntiles = take(4);
+  const int64_t Tdec = std::min<int64_t>(Tg, kDecodeGroup);
+  y.plog = take((d / 256) * Tdec * E * 4);
+  y.ctrl = take((size_t)ctrl_ints(L) * 4);
   if (mode != DS4MOE_MODE_ROUTE) {  // expert buffers (not needed for routing alone)
     y.hs16 = take(Tg * fs * 2);
     y.hw16 = take(S * f * 2);
     y.hsum = take(S * (f / 16) * 4);
     if (mode == DS4MOE_MODE_PREFILL) y.yp = take(S * d * 4);
+    if (mode == DS4MOE_MODE_DECODE) {
+      y.sh_part = take((fs / 16) * kShChunks * 2 * 16 * Tdec * 4);
+      y.dn_part = take((d / 16) * (kDnShChunks + dmax) * 16 * Tdec * 4);
+    }
   }
   y.total = o;
   return y;

@@ -20,10 +20,19 @@ struct WsLayout {
   size_t ndist, distinct, tok_slot;  // decode: distinct experts and their token slots
   size_t hs16, hw16, hsum, yp;        // activations between the kernels
   size_t tiles, ntiles;               // prefill: (expert, token group) work list
+  size_t plog;                        // decode: partial router logits [d/256][Tg][E]
+  size_t ctrl;                        // decode: flags and counters, cleared by the first kernel of a call
+  size_t sh_part, dn_part;            // decode: per-chunk / per-source partial tiles
   size_t total;
 };
 
 WsLayout ws_layout(const ds4moe_layer& L, int64_t T, int mode);
+
+// Decode control words: [0] routing ready, then one counter per shared-expert
+// gate/up tile (fs/16), then one per output tile of the down product (d/16).
+inline int ctrl_ints(const ds4moe_layer& L) { return 1 + L.d_ff_shared / 16 + L.d_model / 16; }
+constexpr int kShChunks = 4;  // K chunks of a shared-expert gate/up tile (decode)
+constexpr int kDnShChunks = 4;  // K chunks of a shared-expert down tile (decode)
 
 // Everything a forward launch needs, resolved on the host.
 struct Fwd {

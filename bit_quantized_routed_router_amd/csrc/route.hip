@@ -11,8 +11,9 @@
 
 #include "common.h"
 #include "internal.h"
-#include "trace.h"
+#include "routefin.h"
 #include "tiles.h"
+#include "trace.h"
 
 namespace ds4 {
 
@@ -76,170 +77,75 @@ __global__ __launch_bounds__(NW * 64) void k_router_logits(const uint16_t* __res
   }
 }
 
-// ---------------------------------------------------------------- top-k
-// One wave selects the k largest of E logits (lane owns e = lane + 64 i),
-// leaving the chosen indices/values in LDS (sel_e, sel_v, round order).
-__device__ inline void wave_topk(const float* __restrict__ l, int E, int k, int lane, int* sel_e, float* sel_v) {
-  float v[kMaxExperts / 64];
-  uint32_t taken = 0;
-  const int per = (E + 63) / 64;
+// Decode router: block = 16 experts x one K chunk of CK = 256 inputs (4 waves,
+// two K-steps each); writes partial logits plog[kc][t][e].  Activations are
+// read in their input type and converted in registers; the blocks of expert
+// tile 0 also store the binary16 copy (hi, and lo for fp32 input) that the
+// expert kernels read.  Block (0, 0) clears the down kernel's tile counters.
+template <bool LO>
+__global__ __launch_bounds__(256) void k_router_partial(const uint16_t* __restrict__ wr, int E, int d,
+                                                        const void* __restrict__ x, int T,
+                                                        float* __restrict__ plog, _Float16* __restrict__ xh,
+                                                        _Float16* __restrict__ xl, int32_t* __restrict__ zero_ctr,
+                                                        int nzero) {
+  __shared__ float red[4 * 64 * 4];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c = lane & 15, q = lane >> 4;
+  const int e0 = blockIdx.x * 16, kc = blockIdx.y;
+  if (blockIdx.x == 0 && kc == 0)
+    for (int i = threadIdx.x; i < nzero; i += blockDim.x) zero_ctr[i] = 0;
+  const int arow = min(e0 + c, E - 1);
+  const uint16_t* rp = wr + (int64_t)arow * d;
+  float4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int i = 0; i < kMaxExperts / 64; ++i) {
-    const int e = lane + 64 * i;
-    v[i] = (i < per && e < E) ? l[e] : -__builtin_inff();
-  }
-  for (int j = 0; j < k; ++j) {
-    float bv = -__builtin_inff();
-    int be = 0x7FFFFFFF;
+  for (int h = 0; h < 2; ++h) {
+    const int ks = kc * 8 + wave * 2 + h;
+    const int k0 = ks * 32 + 8 * q;
+    half8_t a = *(const half8_t*)(rp + k0);
+    half8_t bh = zero_half8(), bl = zero_half8();
+    if (c < T) {
+      float v[8];
+      if (!LO) {
+        u32x4_t u = *(const u32x4_t*)((const uint16_t*)x + (int64_t)c * d + k0);
 #pragma unroll
-    for (int i = 0; i < kMaxExperts / 64; ++i) {
-      const int e = lane + 64 * i;
-      // strict '>' keeps the lower index among equal logits (e grows with i)
-      if (i < per && e < E && !((taken >> i) & 1u) && (v[i] > bv || be == 0x7FFFFFFF)) {
-        bv = v[i];
-        be = e;
+        for (int p = 0; p < 4; ++p) {
+          v[2 * p] = __builtin_bit_cast(float, u[p] << 16);
+          v[2 * p + 1] = __builtin_bit_cast(float, u[p] & 0xFFFF0000u);
+        }
+      } else {
+        const float4* src = (const float4*)((const float*)x + (int64_t)c * d + k0);
+        float4 a0 = src[0], a1 = src[1];
+        v[0] = a0.x; v[1] = a0.y; v[2] = a0.z; v[3] = a0.w;
+        v[4] = a1.x; v[5] = a1.y; v[6] = a1.z; v[7] = a1.w;
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        bh[e] = (_Float16)v[e];
+        bl[e] = (_Float16)(v[e] - (float)bh[e]);
+      }
+      if (blockIdx.x == 0) {
+        *(half8_t*)(xh + (int64_t)c * d + k0) = bh;
+        if (LO) *(half8_t*)(xl + (int64_t)c * d + k0) = bl;
       }
     }
+    acc = mfma16x16x32(a, bh, acc);
+    if (LO) acc = mfma16x16x32(a, bl, acc);
+  }
+  acc = block_reduce_waves<4>(acc, red, wave, lane);
+  if (wave == 0 && c < T) {
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      float ov = __shfl_xor(bv, o);
-      int oe = __shfl_xor(be, o);
-      if (ov > bv || (ov == bv && oe < be)) {
-        bv = ov;
-        be = oe;
-      }
-    }
-    if ((be & 63) == lane) taken |= 1u << (be >> 6);
-    if (lane == 0) {
-      sel_e[j] = be;
-      sel_v[j] = bv;
+    for (int r = 0; r < 4; ++r) {
+      const int e = e0 + 4 * q + r;
+      if (e < E) plog[((int64_t)kc * T + c) * E + e] = acc[r];
     }
   }
 }
 
-// Lane 0: sort the k selected experts by index and compute their softmax.
-__device__ inline void finish_token(int* sel_e, float* sel_v, int k, int64_t t, int32_t* idx, float* w,
-                                    int32_t* idx_out, float* w_out) {
-  const float lmax = sel_v[0];
-  for (int a = 1; a < k; ++a) {  // insertion sort by expert index
-    int e = sel_e[a];
-    float v = sel_v[a];
-    int b = a - 1;
-    while (b >= 0 && sel_e[b] > e) {
-      sel_e[b + 1] = sel_e[b];
-      sel_v[b + 1] = sel_v[b];
-      --b;
-    }
-    sel_e[b + 1] = e;
-    sel_v[b + 1] = v;
-  }
-  float den = 0.0f;
-  for (int j = 0; j < k; ++j) den += expf(sel_v[j] - lmax);
-  for (int j = 0; j < k; ++j) {
-    const float wj = expf(sel_v[j] - lmax) / den;
-    idx[t * k + j] = sel_e[j];
-    w[t * k + j] = wj;
-    if (idx_out) idx_out[t * k + j] = sel_e[j];
-    if (w_out) w_out[t * k + j] = wj;
-  }
-}
-
-// Block-wide exclusive scan of one int per thread (256 threads); returns the
-// thread's exclusive prefix and writes the block total to *total.
-__device__ inline int block_excl_scan(int v, int* tmp, int* total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int inc = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    int u = __shfl_up(inc, o);
-    if (lane >= o) inc += u;
-  }
-  if (lane == 63) tmp[wave] = inc;
-  __syncthreads();
-  int pre = 0, tot = 0;
-  for (int w = 0; w < (int)(blockDim.x >> 6); ++w) {
-    if (w < wave) pre += tmp[w];
-    tot += tmp[w];
-  }
-  __syncthreads();
-  *total = tot;
-  return pre + inc - v;
-}
-
-// ---------------------------------------------------------------- decode: one block does it all
-// T <= 16 tokens.  Produces idx/w, counts, offsets, perm, inv and the
-// distinct-expert table: distinct[i] (ascending expert), tok_slot[i*16 + t]
-// = slot of token t in expert distinct[i], or -1.
-__global__ __launch_bounds__(256) void k_route_finish_decode(
-    const float* __restrict__ logits, int E, int k, int T, int32_t* __restrict__ idx, float* __restrict__ w,
-    int32_t* idx_out, float* w_out, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
-    int32_t* __restrict__ perm, int32_t* __restrict__ inv, int32_t* counts_out, int32_t* offsets_out,
-    int32_t* perm_out, int32_t* __restrict__ ndist, int32_t* __restrict__ distinct, int32_t* __restrict__ tok_slot) {
-  __shared__ int s_sel_e[4][kMaxTopK];
-  __shared__ float s_sel_v[4][kMaxTopK];
-  __shared__ int s_idx[kDecodeGroup * kMaxTopK];
-  __shared__ int s_cnt[kMaxExperts];
-  __shared__ int s_off[kMaxExperts];
-  __shared__ int s_dpos[kMaxExperts];
-  __shared__ int s_tmp[8];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int e = threadIdx.x; e < E; e += blockDim.x) s_cnt[e] = 0;
-  for (int t = wave; t < T; t += 4) {
-    wave_topk(logits + (int64_t)t * E, E, k, lane, s_sel_e[wave], s_sel_v[wave]);
-    if (lane == 0) {
-      finish_token(s_sel_e[wave], s_sel_v[wave], k, t, idx, w, idx_out, w_out);
-      for (int j = 0; j < k; ++j) s_idx[t * k + j] = s_sel_e[wave][j];
-    }
-  }
-  __syncthreads();
-  const int S = T * k;
-  for (int s = threadIdx.x; s < S; s += blockDim.x) atomicAdd(&s_cnt[s_idx[s]], 1);
-  __syncthreads();
-  // exclusive scans over experts: thread owns EPT consecutive experts
-  const int EPT = (E + 255) / 256;
-  int csum = 0, dsum = 0;
-  for (int i = 0; i < EPT; ++i) {
-    const int e = threadIdx.x * EPT + i;
-    if (e < E) {
-      csum += s_cnt[e];
-      dsum += s_cnt[e] > 0;
-    }
-  }
-  int ctot, dtot;
-  int cpre = block_excl_scan(csum, s_tmp, &ctot);
-  int dpre = block_excl_scan(dsum, s_tmp, &dtot);
-  for (int i = 0; i < EPT; ++i) {
-    const int e = threadIdx.x * EPT + i;
-    if (e < E) {
-      s_off[e] = cpre;
-      s_dpos[e] = s_cnt[e] > 0 ? dpre : -1;
-      counts[e] = s_cnt[e];
-      offsets[e] = cpre;
-      if (counts_out) counts_out[e] = s_cnt[e];
-      if (offsets_out) offsets_out[e] = cpre;
-      if (s_cnt[e] > 0) distinct[dpre] = e;
-      cpre += s_cnt[e];
-      dpre += s_cnt[e] > 0;
-    }
-  }
-  if (threadIdx.x == 0) {
-    offsets[E] = ctot;
-    if (offsets_out) offsets_out[E] = ctot;
-    *ndist = dtot;
-  }
-  for (int i = threadIdx.x; i < dtot * kDecodeGroup; i += blockDim.x) tok_slot[i] = -1;
-  __syncthreads();
-  for (int s = threadIdx.x; s < S; s += blockDim.x) {
-    const int e = s_idx[s], t = s / k;
-    int rank = 0;
-    for (int u = 0; u < t; ++u)
-      for (int j = 0; j < k; ++j) rank += s_idx[u * k + j] == e;
-    const int pos = s_off[e] + rank;
-    perm[pos] = s;
-    inv[s] = pos;
-    if (perm_out) perm_out[pos] = s;
-    tok_slot[s_dpos[e] * kDecodeGroup + t] = s;
-  }
+// ---------------------------------------------------------------- decode finish (routing only)
+__global__ __launch_bounds__(256) void k_route_finish_decode(const float* __restrict__ plog, int nparts,
+                                                             const float* __restrict__ bias, int E, int k, int T,
+                                                             RouteOut o) {
+  route_finish_block(plog, nparts, bias, E, k, T, o);
 }
 
 // ---------------------------------------------------------------- prefill: top-k per token
@@ -338,19 +244,26 @@ hipError_t launch_route(const Fwd& f, bool decode) {
   int32_t* perm = (int32_t*)(ws + y.perm);
   int32_t* inv = (int32_t*)(ws + y.inv);
 
-  const int64_t n8 = f.T * d / 8;
-  const int cblocks = (int)std::min<int64_t>((n8 + 255) / 256, 4096);
-  DS4_LAUNCH(k_convert_x, dim3(cblocks), dim3(256), 0, f.st, f.x, f.x_dtype, n8, xh, xl);
-  const dim3 lg((E + 15) / 16, (unsigned)((f.T + 15) / 16));
   if (decode) {
+    const int T = (int)f.T;
+    const int kr = d / QK;  // one partial per 256-input chunk
+    float* plog = (float*)(ws + y.plog);
+    const dim3 pg((E + 15) / 16, kr);
+    int32_t* ctrl = (int32_t*)(ws + y.ctrl);
+    const int nctrl = ctrl_ints(L);
     if (f.lo)
-      DS4_LAUNCH((k_router_logits<16, true>), lg, dim3(1024), 0, f.st, L.router_w, L.router_bias, E, d, xh, xl, f.T, logits);
+      DS4_LAUNCH(k_router_partial<true>, pg, dim3(256), 0, f.st, L.router_w, E, d, f.x, T, plog, xh, xl, ctrl, nctrl);
     else
-      DS4_LAUNCH((k_router_logits<16, false>), lg, dim3(1024), 0, f.st, L.router_w, L.router_bias, E, d, xh, xl, f.T, logits);
-    DS4_LAUNCH(k_route_finish_decode, dim3(1), dim3(256), 0, f.st, logits, E, k, (int)f.T, idx, w,
-                       f.idx_out, f.w_out, counts, offsets, perm, inv, f.counts_out, f.offsets_out, f.perm_out,
-                       (int32_t*)(ws + y.ndist), (int32_t*)(ws + y.distinct), (int32_t*)(ws + y.tok_slot));
+      DS4_LAUNCH(k_router_partial<false>, pg, dim3(256), 0, f.st, L.router_w, E, d, f.x, T, plog, xh, xl, ctrl, nctrl);
+    if (!f.y) {  // routing only: finish here; the forward pass finishes inside its gate/up kernel
+      DS4_LAUNCH(k_route_finish_decode, dim3(1), dim3(256), 0, f.st, plog, kr, L.router_bias, E, k, T,
+                 route_out(f));
+    }
   } else {
+    const int64_t n8 = f.T * d / 8;
+    const int cblocks = (int)std::min<int64_t>((n8 + 255) / 256, 4096);
+    DS4_LAUNCH(k_convert_x, dim3(cblocks), dim3(256), 0, f.st, f.x, f.x_dtype, n8, xh, xl);
+    const dim3 lg((E + 15) / 16, (unsigned)((f.T + 15) / 16));
     if (f.lo)
       DS4_LAUNCH((k_router_logits<4, true>), lg, dim3(256), 0, f.st, L.router_w, L.router_bias, E, d, xh, xl, f.T, logits);
     else

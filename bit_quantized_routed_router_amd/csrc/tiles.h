@@ -33,6 +33,7 @@ __device__ inline void f16_tile(const uint16_t* __restrict__ rowp0, const uint16
                                 const _Float16* bcol, const _Float16* bcol_lo, int ks0, int ks1, int lane,
                                 float4_t& acc0, float4_t& acc1) {
   const int ko = 8 * (lane >> 4);
+#pragma unroll 4
   for (int ks = ks0; ks < ks1; ++ks) {
     half8_t b = load_b(bcol, ks, lane);
     half8_t a0 = *(const half8_t*)(rowp0 + ks * 32 + ko);
