@@ -14,9 +14,9 @@ shared expert, bf16 activations -- in layer-tokens per second.
   * the K timed steps are captured once into a HIP graph and replayed (the
     launch sequence a decode loop would submit), bracketed by events on the
     capture stream; the eager (host-launched) rate is reported beside it;
-  * "roofline" covers the dominant kernel (k_gateup_decode): algorithmic
-    bytes per launch / its mean duration from HIP events around each launch
-    during an eager pass over the same steps;
+  * "roofline" covers the dominant decode kernel (the longest of the three
+    stages): algorithmic bytes per launch / its mean duration from HIP events
+    around each launch during an eager pass over the same steps;
   * "prefill" times ds4moe_forward_prefill on a 2048-token chunk with
     Zipf-like expert loads against the dense fp16 MFMA peak;
   * "cpu_baseline" times the CPU oracle on a bounded sample of decode tokens.
@@ -45,21 +45,20 @@ def log(*a):
 
 
 def decode_bytes(cfg, n_distinct, T=1):
-    """Algorithmic bytes of one decode step and of its kernels."""
+    """Algorithmic HBM bytes of one decode step and of each of its kernels:
+    every weight byte the step needs read once, activations read/written once.
+    stage 1: router + shared gate/up; stage 2: shared down + routed gate/up;
+    stage 3: routed down."""
     from bit_quantized_routed_router_amd import ds4moe as D
-    d, f, fs, E = cfg.d, cfg.f, cfg.fs, cfg.E
+    d, f, fs, E, k = cfg.d, cfg.f, cfg.fs, cfg.E, cfg.k
     cb = D.packed_bytes(D.FMT_CB2, f, d)
     qb = D.packed_bytes(D.FMT_Q2K, d, f)
     x_bytes = T * d * 2
-    router = E * d * 2
-    shared_gu = 2 * fs * d * 2
-    shared_dn = d * fs * 2
-    routed_gu = n_distinct * 2 * cb
-    routed_dn = n_distinct * qb
-    gateup = shared_gu + routed_gu + T * d * 2 + T * cfg.k * f * 2 + T * fs * 2
-    down = shared_dn + routed_dn + T * d * 4
-    total = router + shared_gu + shared_dn + routed_gu + routed_dn + x_bytes + T * d * 4
-    return dict(total=total, k_gateup_decode=gateup, k_down_decode=down)
+    s1 = E * d * 2 + 2 * fs * d * 2 + x_bytes + T * fs * 2
+    s2 = d * fs * 2 + n_distinct * 2 * cb + T * fs * 2 + T * k * f * 2 + T * d * 4
+    s3 = n_distinct * qb + T * k * f * 2 + T * d * 4 + T * d * 4
+    total = E * d * 2 + 3 * fs * d * 2 + n_distinct * (2 * cb + qb) + x_bytes + T * d * 4
+    return dict(total=total, k_dec_stage1=s1, k_dec_stage2=s2, k_dec_stage3=s3)
 
 
 def make_layer(cfg, copies=1, cfg_seed=None):
@@ -167,19 +166,26 @@ def bench_decode(args):
     if not torch.equal(y[args.warmup:], y_eager[args.warmup:]):
         raise RuntimeError("graph replay differs from the eager run")
 
-    # distinct experts per step (1 token: k distinct) -> algorithmic bytes
+    # distinct experts per step (1 token: k distinct) -> algorithmic bytes;
+    # the dominant kernel is the one with the largest share of the step time
     nb = decode_bytes(cfg, cfg.k, T=1)
-    dom = "k_gateup_decode"
-    hits = [v for k2, v in kern.items() if k2 == dom or k2.startswith(dom + "<")]
-    ms_dom = sum(v[0] for v in hits) if hits else float("nan")
-    cnt_dom = sum(v[1] for v in hits)
-    dur_us = ms_dom / max(cnt_dom, 1) * 1e3
-    achieved = nb[dom] / (dur_us * 1e-6) / 1e9
+    per = {}
+    for name in ("k_dec_stage1", "k_dec_stage2", "k_dec_stage3"):
+        hits = [v for k2, v in kern.items() if k2 == name or k2.startswith(name + "<")]
+        ms = sum(v[0] for v in hits)
+        cnt = sum(v[1] for v in hits)
+        if cnt:
+            us = ms / cnt * 1e3
+            per[name] = dict(mean_us=us, bytes_per_launch=nb[name], gbs=nb[name] / (us * 1e-6) / 1e9)
+    if not per:
+        raise RuntimeError(f"no decode kernel in the trace: {sorted(kern)}")
+    dom = max(per, key=lambda n: per[n]["mean_us"])
+    achieved = per[dom]["gbs"]
     res = dict(ms_per_step=graph_ms, eager_ms_per_step=eager_ms, kernels={k: dict(mean_us=v[0] / max(v[1], 1) * 1e3,
-               launches=v[1]) for k, v in kern.items()},
+               launches=v[1]) for k, v in kern.items()}, decode_kernels=per,
                roofline=dict(bound="hbm", kernel=dom, achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
                              frac=achieved / HBM_PEAK_GBS, traffic=None, bytes_per_launch=nb[dom],
-                             mean_launch_us=dur_us),
+                             mean_launch_us=per[dom]["mean_us"]),
                layer_bytes=nb["total"], layer_gbs=nb["total"] / (graph_ms * 1e-3) / 1e9)
     res["layer_hbm_frac"] = res["layer_gbs"] / HBM_PEAK_GBS
     del layers, g

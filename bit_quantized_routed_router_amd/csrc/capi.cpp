@@ -7,6 +7,7 @@
 
 #include "common.h"
 #include "internal.h"
+#include "trace.h"
 
 namespace ds4 {
 
@@ -23,6 +24,9 @@ WsLayout ws_layout(const ds4moe_layer& L, int64_t T, int mode) {
   const int64_t d = L.d_model, E = L.n_experts, k = L.top_k, f = L.d_ff, fs = L.d_ff_shared;
   const int64_t Tg = mode == DS4MOE_MODE_DECODE ? std::min<int64_t>(T, kDecodeGroup) : T;
   const int64_t S = Tg * k;
+  // first and of fixed size, so every mode and layer shape finds its counters
+  // at the same place in a shared workspace
+  y.ctrl = take((size_t)kCtrlInts * 4);
   y.x_hi = take(Tg * d * 2);
   y.x_lo = take(Tg * d * 2);
   y.logits = take(Tg * E * 4);
@@ -39,16 +43,15 @@ WsLayout ws_layout(const ds4moe_layer& L, int64_t T, int mode) {
   y.tiles = take(((S + 15) / 16 + E) * 2 * 4);
   y.ntiles = take(4);
   const int64_t Tdec = std::min<int64_t>(Tg, kDecodeGroup);
-  y.plog = take((d / 256) * Tdec * E * 4);
-  y.ctrl = take((size_t)ctrl_ints(L) * 4);
+  y.plog = take((d / 256) * Tdec * E * 4);  // one partial per 256 (routing only) or 512 inputs (forward)
   if (mode != DS4MOE_MODE_ROUTE) {  // expert buffers (not needed for routing alone)
     y.hs16 = take(Tg * fs * 2);
     y.hw16 = take(S * f * 2);
     y.hsum = take(S * (f / 16) * 4);
     if (mode == DS4MOE_MODE_PREFILL) y.yp = take(S * d * 4);
     if (mode == DS4MOE_MODE_DECODE) {
-      y.sh_part = take((fs / 16) * kShChunks * 2 * 16 * Tdec * 4);
-      y.dn_part = take((d / 16) * (kDnShChunks + dmax) * 16 * Tdec * 4);
+      y.gu_part = take((fs / 16) * 4 * 16 * Tdec * 4);
+      y.ys = take(Tdec * d * 4);
     }
   }
   y.total = o;
@@ -101,6 +104,14 @@ static Fwd make_fwd(const ds4moe_layer* L, const void* x, int x_dtype, int64_t T
 
 static int hip_status(hipError_t e) { return e == hipSuccess ? DS4MOE_OK : DS4MOE_EHIP; }
 
+__global__ __launch_bounds__(256) void k_zero_bytes(uint8_t* __restrict__ p, size_t n) {
+  const size_t n16 = n / 16;
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride)
+    ((u32x4_t*)p)[i] = u32x4_t{0u, 0u, 0u, 0u};
+  if (blockIdx.x == 0 && threadIdx.x < n % 16) p[n16 * 16 + threadIdx.x] = 0;
+}
+
 }  // namespace ds4
 
 using namespace ds4;
@@ -150,6 +161,16 @@ size_t ds4moe_workspace_bytes(const ds4moe_layer* L, int64_t T, int mode) {
   return ws_layout(*L, T, mode).total;
 }
 
+int ds4moe_workspace_init(void* ws, size_t ws_bytes, void* stream) {
+  if (!ws) return DS4MOE_EINVAL;
+  if ((uintptr_t)ws & 255) return DS4MOE_EALIGN;
+  if (ws_bytes == 0) return DS4MOE_OK;
+  const size_t blocks = std::min<size_t>((ws_bytes / 16 + 255) / 256 + 1, 4096);
+  hipStream_t st = (hipStream_t)stream;
+  DS4_LAUNCH(k_zero_bytes, dim3((unsigned)blocks), dim3(256), 0, st, (uint8_t*)ws, ws_bytes);
+  return hip_status(hipGetLastError());
+}
+
 int ds4moe_route(const ds4moe_layer* L, const void* x, int x_dtype, int64_t T, int32_t* topk_idx, float* topk_w,
                  int32_t* counts, int32_t* offsets, int32_t* perm, void* ws, size_t ws_bytes, void* stream) {
   int rc = check_layer(L);
@@ -182,9 +203,7 @@ int ds4moe_forward_decode(const ds4moe_layer* L, const void* x, int x_dtype, int
     Fwd f = make_fwd(L, (const char*)x + t0 * d * xes, x_dtype, tg, y + t0 * d,
                      topk_idx_out ? topk_idx_out + t0 * k : nullptr, topk_w_out ? topk_w_out + t0 * k : nullptr, ws,
                      DS4MOE_MODE_DECODE, stream);
-    hipError_t e = launch_route(f, true);
-    if (e == hipSuccess) e = launch_decode_experts(f);
-    if (e != hipSuccess) return DS4MOE_EHIP;
+    if (launch_decode(f) != hipSuccess) return DS4MOE_EHIP;
   }
   return DS4MOE_OK;
 }

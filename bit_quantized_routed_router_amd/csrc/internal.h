@@ -5,7 +5,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
-#include "../../include/ds4moe.h"
+#include "ds4moe.h"
 
 namespace ds4 {
 
@@ -21,18 +21,20 @@ struct WsLayout {
   size_t hs16, hw16, hsum, yp;        // activations between the kernels
   size_t tiles, ntiles;               // prefill: (expert, token group) work list
   size_t plog;                        // decode: partial router logits [d/256][Tg][E]
-  size_t ctrl;                        // decode: flags and counters, cleared by the first kernel of a call
-  size_t sh_part, dn_part;            // decode: per-chunk / per-source partial tiles
+  size_t ctrl;                        // decode: arrival counters (see ctrl_ints)
+  size_t gu_part, ys;                 // decode: shared-expert gate/up half-K partial tiles, shared-expert output
   size_t total;
 };
 
 WsLayout ws_layout(const ds4moe_layer& L, int64_t T, int mode);
 
-// Decode control words: [0] routing ready, then one counter per shared-expert
-// gate/up tile (fs/16), then one per output tile of the down product (d/16).
-inline int ctrl_ints(const ds4moe_layer& L) { return 1 + L.d_ff_shared / 16 + L.d_model / 16; }
-constexpr int kShChunks = 4;  // K chunks of a shared-expert gate/up tile (decode)
-constexpr int kDnShChunks = 4;  // K chunks of a shared-expert down tile (decode)
+// Decode arrival counters at workspace offset 0: [0] router blocks, then one
+// per 16-row tile of the shared expert's gate/up.  Each counter is reset by
+// the block that sees the last arrival, and the last kernel of a call clears
+// them all, so they are zero whenever no call is running; a new workspace
+// must start zeroed.
+constexpr int kCtrlInts = 1 + kMaxDim / 16;
+inline int ctrl_ints(const ds4moe_layer& L) { return 1 + L.d_ff_shared / 16; }
 
 // Everything a forward launch needs, resolved on the host.
 struct Fwd {
@@ -60,7 +62,7 @@ hipError_t launch_dequant_q2k(const void* packed, int64_t rows, int64_t cols, fl
 // routing: x conversion + logits + top-k + grouping.  decode == true builds
 // the distinct-expert tables of a <= 16-token group.
 hipError_t launch_route(const Fwd& f, bool decode);
-hipError_t launch_decode_experts(const Fwd& f);
+hipError_t launch_decode(const Fwd& f);  // full layer for one group of <= 16 tokens
 hipError_t launch_prefill_experts(const Fwd& f);
 
 }  // namespace ds4

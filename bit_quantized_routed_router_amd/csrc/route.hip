@@ -145,7 +145,8 @@ __global__ __launch_bounds__(256) void k_router_partial(const uint16_t* __restri
 __global__ __launch_bounds__(256) void k_route_finish_decode(const float* __restrict__ plog, int nparts,
                                                              const float* __restrict__ bias, int E, int k, int T,
                                                              RouteOut o) {
-  route_finish_block(plog, nparts, bias, E, k, T, o);
+  __shared__ RouteLds lds;
+  route_finish_block(lds, plog, nparts, bias, E, k, T, o);
 }
 
 // ---------------------------------------------------------------- prefill: top-k per token
@@ -155,10 +156,21 @@ __global__ __launch_bounds__(256) void k_topk_rows(const float* __restrict__ log
   __shared__ int s_sel_e[4][kMaxTopK];
   __shared__ float s_sel_v[4][kMaxTopK];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t t = (int64_t)blockIdx.x * 4 + wave;
-  if (t >= T) return;
-  wave_topk(logits + t * E, E, k, lane, s_sel_e[wave], s_sel_v[wave]);
-  if (lane == 0) finish_token(s_sel_e[wave], s_sel_v[wave], k, t, idx, w, idx_out, w_out);
+  const int64_t t0 = (int64_t)blockIdx.x * 4;
+  if (t0 + wave < T) wave_select(logits + (t0 + wave) * E, E, k, lane, s_sel_e[wave], s_sel_v[wave]);
+  __syncthreads();
+  for (int i = threadIdx.x; i < 4 * k; i += blockDim.x) {
+    const int tw = i / k, j = i % k;
+    const int64_t t = t0 + tw;
+    if (t < T) {
+      const int e = s_sel_e[tw][j];
+      const float wj = gate_weight(s_sel_v[tw], k, j);
+      idx[t * k + j] = e;
+      w[t * k + j] = wj;
+      if (idx_out) idx_out[t * k + j] = e;
+      if (w_out) w_out[t * k + j] = wj;
+    }
+  }
 }
 
 // prefill grouping, pass 1: counts[e] (one block per expert)
@@ -255,10 +267,7 @@ hipError_t launch_route(const Fwd& f, bool decode) {
       DS4_LAUNCH(k_router_partial<true>, pg, dim3(256), 0, f.st, L.router_w, E, d, f.x, T, plog, xh, xl, ctrl, nctrl);
     else
       DS4_LAUNCH(k_router_partial<false>, pg, dim3(256), 0, f.st, L.router_w, E, d, f.x, T, plog, xh, xl, ctrl, nctrl);
-    if (!f.y) {  // routing only: finish here; the forward pass finishes inside its gate/up kernel
-      DS4_LAUNCH(k_route_finish_decode, dim3(1), dim3(256), 0, f.st, plog, kr, L.router_bias, E, k, T,
-                 route_out(f));
-    }
+    DS4_LAUNCH(k_route_finish_decode, dim3(1), dim3(256), 0, f.st, plog, kr, L.router_bias, E, k, T, route_out(f));
   } else {
     const int64_t n8 = f.T * d / 8;
     const int cblocks = (int)std::min<int64_t>((n8 + 255) / 256, 4096);

@@ -10,72 +10,81 @@
 
 namespace ds4 {
 
+// Order-preserving map of a float to a u32 key: a > b  <=>  key(a) > key(b)
+// for non-NaN values, and a == b  <=>  key(a) == key(b) (-0 is keyed as +0).
+__device__ inline uint32_t order_key(float v) {
+  uint32_t u = __builtin_bit_cast(uint32_t, v);
+  u = u == 0x80000000u ? 0u : u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
 // One wave selects the k largest of E logits l[0..E) (lane owns
-// e = lane + 64 i) and leaves the chosen indices/values in sel_e/sel_v in
-// selection order.
-__device__ inline void wave_topk(const float* __restrict__ l, int E, int k, int lane, int* sel_e, float* sel_v) {
-  float v[kMaxExperts / 64];
-  uint32_t taken = 0;
-  const int per = (E + 63) / 64;
+// e = lane + 64 i, i < PER, PER * 64 >= E), equal logits going to the lower
+// expert index, and writes the chosen experts and logits to sel_e/sel_v in
+// ascending expert order.  The k-th largest key is found bit by bit from the
+// top: a candidate threshold is kept when at least k keys reach it.  Counting
+// uses only ballots and popcounts, so no data crosses lanes, and every step
+// is straight-line code.  Slots past E get key 0, which no candidate (>= 1)
+// admits; k <= E guarantees k real keys.
+template <int PER>
+__device__ inline void wave_select_n(const float* l, int E, int k, int lane, int* sel_e, float* sel_v) {
+  float v[PER];
+  uint32_t key[PER];
 #pragma unroll
-  for (int i = 0; i < kMaxExperts / 64; ++i) {
+  for (int i = 0; i < PER; ++i) {
     const int e = lane + 64 * i;
-    v[i] = (i < per && e < E) ? l[e] : -__builtin_inff();
+    v[i] = l[e < E ? e : E - 1];
   }
-  for (int j = 0; j < k; ++j) {
-    float bv = -__builtin_inff();
-    int be = 0x7FFFFFFF;
 #pragma unroll
-    for (int i = 0; i < kMaxExperts / 64; ++i) {
-      const int e = lane + 64 * i;
-      // strict '>' keeps the lower index among equal logits (e grows with i)
-      if (i < per && e < E && !((taken >> i) & 1u) && (v[i] > bv || be == 0x7FFFFFFF)) {
-        bv = v[i];
-        be = e;
-      }
-    }
+  for (int i = 0; i < PER; ++i) key[i] = lane + 64 * i < E ? order_key(v[i]) : 0u;
+  uint32_t thr = 0;
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float ov = __shfl_xor(bv, o);
-      const int oe = __shfl_xor(be, o);
-      if (ov > bv || (ov == bv && oe < be)) {
-        bv = ov;
-        be = oe;
-      }
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = thr | (1u << bit);
+    int cnt = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) cnt += __popcll(__ballot(key[i] >= cand));
+    thr = cnt >= k ? cand : thr;
+  }
+  int gt = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) gt += __popcll(__ballot(key[i] > thr));
+  const int need_eq = k - gt;  // keys equal to the threshold still to take, lowest index first
+  const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;  // lanes under this one
+  int eq_before = 0, pos0 = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const bool eq = key[i] == thr;
+    const uint64_t eqm = __ballot(eq);
+    const bool sel = key[i] > thr || (eq && eq_before + __popcll(eqm & below) < need_eq);
+    eq_before += __popcll(eqm);
+    const uint64_t sm = __ballot(sel);
+    if (sel) {
+      const int pos = pos0 + __popcll(sm & below);
+      sel_e[pos] = lane + 64 * i;
+      sel_v[pos] = v[i];
     }
-    if ((be & 63) == lane) taken |= 1u << (be >> 6);
-    if (lane == 0) {
-      sel_e[j] = be;
-      sel_v[j] = bv;
-    }
+    pos0 += __popcll(sm);
   }
 }
 
-// Lane 0: sort the k selected experts by index and compute their softmax.
-__device__ inline void finish_token(int* sel_e, float* sel_v, int k, int64_t t, int32_t* idx, float* w,
-                                    int32_t* idx_out, float* w_out) {
-  const float lmax = sel_v[0];
-  for (int a = 1; a < k; ++a) {  // insertion sort by expert index
-    const int e = sel_e[a];
-    const float v = sel_v[a];
-    int b = a - 1;
-    while (b >= 0 && sel_e[b] > e) {
-      sel_e[b + 1] = sel_e[b];
-      sel_v[b + 1] = sel_v[b];
-      --b;
-    }
-    sel_e[b + 1] = e;
-    sel_v[b + 1] = v;
-  }
+__device__ inline void wave_select(const float* l, int E, int k, int lane, int* sel_e, float* sel_v) {
+  if (E <= 256)
+    wave_select_n<4>(l, E, k, lane, sel_e, sel_v);
+  else if (E <= 512)
+    wave_select_n<8>(l, E, k, lane, sel_e, sel_v);
+  else
+    wave_select_n<16>(l, E, k, lane, sel_e, sel_v);
+}
+
+// Gate weight of selected slot j: softmax over the k selected logits,
+// shifted by their maximum, with the denominator summed in slot order.
+__device__ inline float gate_weight(const float* sel_v, int k, int j) {
+  float vmax = sel_v[0];
+  for (int a = 1; a < k; ++a) vmax = fmaxf(vmax, sel_v[a]);
   float den = 0.0f;
-  for (int j = 0; j < k; ++j) den += expf(sel_v[j] - lmax);
-  for (int j = 0; j < k; ++j) {
-    const float wj = expf(sel_v[j] - lmax) / den;
-    idx[t * k + j] = sel_e[j];
-    w[t * k + j] = wj;
-    if (idx_out) idx_out[t * k + j] = sel_e[j];
-    if (w_out) w_out[t * k + j] = wj;
-  }
+  for (int a = 0; a < k; ++a) den += expf(sel_v[a] - vmax);
+  return expf(sel_v[j] - vmax) / den;
 }
 
 // Block-wide exclusive scan of one int per thread (blockDim a multiple of
@@ -110,80 +119,98 @@ struct RouteOut {
   int32_t *ndist, *distinct, *tok_slot;  // distinct experts, slot of token t in distinct[i] at [i*16 + t]
 };
 
-// Run by a whole block (any multiple of 64 threads up to 1024): logits =
-// sum of nparts partial rows plog[p][t][e] (+ bias), top-k and softmax per
-// token, then counts, offsets, perm (slots t*k + j by expert, then token),
-// inv, and the distinct-expert table.
-__device__ inline void route_finish_block(const float* __restrict__ plog, int nparts, const float* __restrict__ bias,
-                                          int E, int k, int T, const RouteOut& o) {
-  __shared__ int s_sel_e[16][kMaxTopK];
-  __shared__ float s_sel_v[16][kMaxTopK];
-  __shared__ int s_idx[kDecodeGroup * kMaxTopK];
-  __shared__ int s_cnt[kMaxExperts];
-  __shared__ int s_off[kMaxExperts];
-  __shared__ int s_dpos[kMaxExperts];
-  __shared__ int s_tmp[16];
+// Run by a whole block (any multiple of 64 threads up to 1024), T <= 16
+// (so S = T * k <= 256):
+// logits = sum of nparts partial rows plog[p][t][e] (+ bias), top-k and
+// gate weights per token, then counts, offsets, perm (slots t*k + j by
+// expert, then token), inv, and the distinct-expert table.  COH: the
+// partials were written by other blocks of the running kernel (read them
+// with coherent loads).
+// LDS of route_finish_block (a struct so kernels can overlay it with the
+// LDS of their other block roles).
+struct RouteLds {
+  float logit[4096];
+  int sel_e[kDecodeGroup][kMaxTopK];
+  float sel_v[kDecodeGroup][kMaxTopK];
+  uint32_t tokm[kMaxExperts];  // bit t: token t chose expert e
+  int off[kMaxExperts];
+  int dpos[kMaxExperts];
+  int ndist;
+};
+
+template <bool COH = false>
+__device__ inline void route_finish_block(RouteLds& R, const float* __restrict__ plog, int nparts,
+                                          const float* __restrict__ bias, int E, int k, int T, const RouteOut& o) {
+  float* s_logit = R.logit;
+  auto& s_sel_e = R.sel_e;
+  auto& s_sel_v = R.sel_v;
+  uint32_t* s_tokm = R.tokm;
+  int* s_off = R.off;
+  int* s_dpos = R.dpos;
+  int& s_ndist = R.ndist;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nwaves = blockDim.x >> 6, nthr = blockDim.x;
-  for (int e = threadIdx.x; e < E; e += nthr) s_cnt[e] = 0;
+  for (int e = threadIdx.x; e < E; e += nthr) s_tokm[e] = 0u;
+  float* logits = T * E <= 4096 ? s_logit : o.logits;
   for (int i = threadIdx.x; i < T * E; i += nthr) {
     const int e = i % E;
     float a = 0.0f;
 #pragma unroll 8
-    for (int p = 0; p < nparts; ++p) a += plog[(int64_t)p * T * E + i];
-    o.logits[i] = bias ? a + bias[e] : a;
+    for (int p = 0; p < nparts; ++p) {
+      const float* src = plog + (int64_t)p * T * E + i;
+      a += COH ? __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : *src;
+    }
+    logits[i] = bias ? a + bias[e] : a;
   }
   __syncthreads();
-  for (int t = wave; t < T; t += nwaves) {
-    wave_topk(o.logits + (int64_t)t * E, E, k, lane, s_sel_e[wave], s_sel_v[wave]);
-    if (lane == 0) {
-      finish_token(s_sel_e[wave], s_sel_v[wave], k, t, o.idx, o.w, o.idx_out, o.w_out);
-      for (int j = 0; j < k; ++j) s_idx[t * k + j] = s_sel_e[wave][j];
-    }
-  }
+  for (int t = wave; t < T; t += nwaves) wave_select(logits + (int64_t)t * E, E, k, lane, s_sel_e[t], s_sel_v[t]);
   __syncthreads();
   const int S = T * k;
-  for (int s = threadIdx.x; s < S; s += nthr) atomicAdd(&s_cnt[s_idx[s]], 1);
+  for (int s = threadIdx.x; s < S; s += nthr) {
+    const int t = s / k, j = s % k;
+    const int e = s_sel_e[t][j];
+    const float wj = gate_weight(s_sel_v[t], k, j);
+    o.idx[s] = e;
+    o.w[s] = wj;
+    if (o.idx_out) o.idx_out[s] = e;
+    if (o.w_out) o.w_out[s] = wj;
+    atomicOr(&s_tokm[e], 1u << t);
+  }
   __syncthreads();
-  const int EPT = (E + nthr - 1) / nthr;  // consecutive experts per thread
-  int csum = 0, dsum = 0;
-  for (int i = 0; i < EPT; ++i) {
-    const int e = threadIdx.x * EPT + i;
-    if (e < E) {
-      csum += s_cnt[e];
-      dsum += s_cnt[e] > 0;
+  // per expert: count = tokens that chose it; offset = selected slots of
+  // lower experts; distinct position = distinct experts below it (a slot
+  // stands for its expert's first token).  O(S) per expert, no scan.
+  for (int e = threadIdx.x; e <= E; e += nthr) {
+    int off = 0, dpos = 0;
+    for (int s = 0; s < S; ++s) {
+      const int es = s_sel_e[s / k][s % k];
+      const int ts = s / k;
+      off += es < e;
+      dpos += es < e && ts == __ffs(s_tokm[es]) - 1;
     }
-  }
-  int ctot, dtot;
-  int cpre = block_excl_scan(csum, s_tmp, &ctot);
-  int dpre = block_excl_scan(dsum, s_tmp, &dtot);
-  for (int i = 0; i < EPT; ++i) {
-    const int e = threadIdx.x * EPT + i;
-    if (e < E) {
-      s_off[e] = cpre;
-      s_dpos[e] = s_cnt[e] > 0 ? dpre : -1;
-      o.counts[e] = s_cnt[e];
-      o.offsets[e] = cpre;
-      if (o.counts_out) o.counts_out[e] = s_cnt[e];
-      if (o.offsets_out) o.offsets_out[e] = cpre;
-      if (s_cnt[e] > 0) o.distinct[dpre] = e;
-      cpre += s_cnt[e];
-      dpre += s_cnt[e] > 0;
+    if (e == E) {
+      o.offsets[E] = S;
+      if (o.offsets_out) o.offsets_out[E] = S;
+      *o.ndist = dpos;
+      s_ndist = dpos;
+      continue;
     }
+    const int c = __popc(s_tokm[e]);
+    s_off[e] = off;
+    s_dpos[e] = dpos;
+    o.counts[e] = c;
+    o.offsets[e] = off;
+    if (o.counts_out) o.counts_out[e] = c;
+    if (o.offsets_out) o.offsets_out[e] = off;
+    if (c > 0) o.distinct[dpos] = e;
   }
-  if (threadIdx.x == 0) {
-    o.offsets[E] = ctot;
-    if (o.offsets_out) o.offsets_out[E] = ctot;
-    *o.ndist = dtot;
-  }
-  for (int i = threadIdx.x; i < dtot * kDecodeGroup; i += nthr) o.tok_slot[i] = -1;
+  __syncthreads();
+  for (int i = threadIdx.x; i < s_ndist * kDecodeGroup; i += nthr) o.tok_slot[i] = -1;
   __syncthreads();
   for (int s = threadIdx.x; s < S; s += nthr) {
-    const int e = s_idx[s], t = s / k;
-    int rank = 0;
-    for (int u = 0; u < t; ++u)
-      for (int j = 0; j < k; ++j) rank += s_idx[u * k + j] == e;
-    const int pos = s_off[e] + rank;
+    const int t = s / k;
+    const int e = s_sel_e[t][s % k];
+    const int pos = s_off[e] + __popc(s_tokm[e] & ((1u << t) - 1u));  // earlier tokens of expert e
     o.perm[pos] = s;
     o.inv[s] = pos;
     if (o.perm_out) o.perm_out[pos] = s;

@@ -58,6 +58,8 @@ def lib() -> ctypes.CDLL:
         L.ds4moe_dequantize.argtypes = [I32, P, I64, I64, P, P]
         L.ds4moe_workspace_bytes.restype = SZ
         L.ds4moe_workspace_bytes.argtypes = [LP, I64, I32]
+        L.ds4moe_workspace_init.restype = I32
+        L.ds4moe_workspace_init.argtypes = [P, SZ, P]
         L.ds4moe_route.restype = I32
         L.ds4moe_route.argtypes = [LP, P, I32, I64, P, P, P, P, P, P, SZ, P]
         L.ds4moe_forward_decode.restype = I32
@@ -77,6 +79,7 @@ def lib() -> ctypes.CDLL:
 
 
 EXPORTS = ["ds4moe_packed_bytes", "ds4moe_quantize", "ds4moe_dequantize", "ds4moe_workspace_bytes",
+           "ds4moe_workspace_init",
            "ds4moe_route", "ds4moe_forward_decode", "ds4moe_forward_prefill", "ds4moe_strerror",
            "ds4moe_grid_levels", "ds4moe_trace_enable", "ds4moe_trace_read"]
 
@@ -120,6 +123,11 @@ def dequantize(fmt: int, packed, rows: int, cols: int, w, stream=None) -> None:
 
 def workspace_bytes(desc: LayerDesc, T: int, mode: int) -> int:
     return int(lib().ds4moe_workspace_bytes(ctypes.byref(desc), T, mode))
+
+
+def workspace_init(ws, nbytes: int, stream=None) -> None:
+    """Zero a new workspace (required once before its first forward call)."""
+    _check(lib().ds4moe_workspace_init(_ptr(ws), int(nbytes), _stream(stream)), "ds4moe_workspace_init")
 
 
 def route(desc, x, x_dtype, T, topk_idx, topk_w, counts, offsets, perm, ws, ws_bytes, stream=None) -> None:
@@ -187,4 +195,6 @@ class Layer:
         n = workspace_bytes(self.desc, T, mode)
         if n == 0:
             raise Ds4moeError(ESHAPE, "ds4moe_workspace_bytes")
-        return torch.empty(n + 256, dtype=torch.uint8, device="cuda"), n
+        ws = torch.empty(n + 256, dtype=torch.uint8, device="cuda")
+        workspace_init(ws, n)
+        return ws, n

@@ -25,7 +25,8 @@
  * the stream has passed the call.  The library allocates no device memory:
  * the caller provides a workspace of ds4moe_workspace_bytes() bytes (256-byte
  * aligned) for each call; calls that share a workspace must be ordered on one
- * stream.  The codebook grid is a compile-time table; the only mutable
+ * stream.  A workspace must be all zero before its first forward call
+ * (ds4moe_workspace_init); every call leaves it ready for the next one.  The codebook grid is a compile-time table; the only mutable
  * global state is the opt-in kernel timer (ds4moe_trace_enable).
  *
  * ---------------------------------------------------------------- formats
@@ -127,6 +128,15 @@ int ds4moe_dequantize(int fmt, const void *packed, int64_t rows, int64_t cols, f
  * ds4moe_forward_prefill, DS4MOE_MODE_ROUTE for ds4moe_route.  0 on invalid
  * input. */
 size_t ds4moe_workspace_bytes(const ds4moe_layer *L, int64_t T, int mode);
+
+/* Zero ws_bytes bytes of a new workspace with a kernel on `stream` (no memset
+ * node, so the call may be captured in a HIP graph).  The decode kernels hand
+ * partial results between blocks through arrival counters kept in the
+ * workspace; each call returns them to zero, so this is needed once per
+ * allocation.  A forward call on a workspace that was never zeroed may return
+ * wrong outputs; it still reads and writes only inside its buffers.
+ * ws: 256-byte aligned device pointer. */
+int ds4moe_workspace_init(void *ws, size_t ws_bytes, void *stream);
 
 /* Router + top-k + gate weights + token grouping for T tokens.
  * x: [T, d] fp32 or bf16 (x_dtype).  Outputs: topk_idx [T, k] int32 (ascending

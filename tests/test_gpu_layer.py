@@ -176,3 +176,41 @@ def test_decode1_alternating_calls_are_bitwise_stable(decode1):
     for k in range(2):
         rows = outs[k][[i for i in range(0, 40, 2)]]
         assert torch.equal(rows, rows[0:1].expand_as(rows))
+
+
+def test_workspace_init_zeroes_exactly_its_range():
+    import torch
+    n = 1_000_003
+    buf = torch.full((n + 512,), 0xAB, dtype=torch.uint8, device="cuda")
+    D.workspace_init(buf, n)
+    torch.cuda.synchronize()
+    h = buf.cpu().numpy()
+    assert not h[:n].any()
+    assert (h[n:] == 0xAB).all()
+
+
+def test_tiny_workspace_shared_by_prefill_and_decode(tiny):
+    """One buffer, zeroed once, serves a prefill call and then decode calls:
+    the decode outputs equal those on a fresh workspace bit for bit and match
+    the oracle."""
+    import torch
+    from tests.gpu_helpers import dev, host
+    c = tiny.cfg
+    xp = tiny.x()
+    Tp, Td = xp.shape[0], 5
+    desc = tiny.layer.desc
+    n = max(D.workspace_bytes(desc, Tp, D.MODE_PREFILL), D.workspace_bytes(desc, Td, D.MODE_DECODE))
+    ws = torch.empty(n + 256, dtype=torch.uint8, device="cuda")
+    D.workspace_init(ws, n)
+    yp = torch.empty((Tp, c.d), dtype=torch.float32, device="cuda")
+    D.forward_prefill(desc, tiny.x_dev(xp), tiny.x_dtype(), Tp, yp, None, None, None, ws, n)
+    xd = tiny.x_dev(xp[:Td])
+    ys = [torch.empty((Td, c.d), dtype=torch.float32, device="cuda") for _ in range(2)]
+    for y in ys:
+        D.forward_decode(desc, xd, tiny.x_dtype(), Td, y, None, None, ws, n)
+    fresh = tiny.forward(xp[:Td], D.MODE_DECODE)["y"]
+    torch.cuda.synchronize()
+    for y in ys:
+        assert np.array_equal(host(y), fresh)
+    ref = oracle_ref(tiny, xp[:Td])
+    assert rel_err_rows(fresh, ref["y"]) <= TOL
