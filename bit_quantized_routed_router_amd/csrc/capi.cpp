@@ -43,7 +43,7 @@ WsLayout ws_layout(const ds4moe_layer& L, int64_t T, int mode) {
   y.tiles = take(((S + 15) / 16 + E) * 2 * 4);
   y.ntiles = take(4);
   const int64_t Tdec = std::min<int64_t>(Tg, kDecodeGroup);
-  y.plog = take((d / 256) * Tdec * E * 4);  // one partial per 256 (routing only) or 512 inputs (forward)
+  y.plog = take((d / 128) * Tdec * E * 4);  // one partial per 256 (routing only) or 128 inputs (forward)
   if (mode != DS4MOE_MODE_ROUTE) {  // expert buffers (not needed for routing alone)
     y.hs16 = take(Tg * fs * 2);
     y.hw16 = take(S * f * 2);
@@ -52,6 +52,7 @@ WsLayout ws_layout(const ds4moe_layer& L, int64_t T, int mode) {
     if (mode == DS4MOE_MODE_DECODE) {
       y.gu_part = take((fs / 16) * 4 * 16 * Tdec * 4);
       y.ys = take(Tdec * d * 4);
+      y.y_part = take((d / 16) * kDownParts * 16 * Tdec * 4);
     }
   }
   y.total = o;

@@ -212,6 +212,34 @@ __device__ inline half8_t q2k_frag(uint32_t u, int hi, uint32_t s) {
   return as_half8(r);
 }
 
+// (1024 + q_a, 1024 + q_b) binary16 pairs of the 8 codes packed in v (code
+// 2p at bits 4p, code 2p+1 at bits 16 + 4p): one shift and one three-input
+// bit operation, (x & 0x00030003) | 0x64006400, per pair.
+__device__ inline void q2k_pairs(uint32_t v, uint32_t (&pr)[4]) {
+#pragma unroll
+  for (int p = 0; p < 4; ++p) pr[p] = __builtin_amdgcn_bitop3_b32(v >> (4 * p), 0x00030003u, 0x64006400u, 0xEA);
+}
+
+// Both A fragments of one Q2K sub-block (its u32 of 16 codes): binary16
+// s * q for codes 0..7 (lo) and 8..15 (hi), exact; one scale conversion.
+__device__ inline void q2k_subblock(uint32_t u, uint32_t s, half8_t& lo, half8_t& hi) {
+  const _Float16 S = (_Float16)(uint16_t)s;
+  const half2_t S2 = {S, S};
+  const half2_t C2 = S2 * (half2_t){(_Float16)-1024.0f, (_Float16)-1024.0f};
+  const uint32_t h16 = u >> 16;
+  uint32_t pl[4], ph[4];
+  q2k_pairs((u & 0xFFFFu) | (u << 14), pl);
+  q2k_pairs(h16 | (h16 << 14), ph);
+  u32x4_t a, b;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    a[p] = as_u32(__builtin_elementwise_fma(as_half2(pl[p]), S2, C2));
+    b[p] = as_u32(__builtin_elementwise_fma(as_half2(ph[p]), S2, C2));
+  }
+  lo = as_half8(a);
+  hi = as_half8(b);
+}
+
 // binary16 (1024 + n) trick for a byte's high nibble, pairs of bytes.
 __device__ inline uint32_t nib_hi_pair_f16(uint32_t w, int byte0) {
   uint32_t a = (w >> (8 * byte0 + 4)) & 0xFu;

@@ -1,27 +1,27 @@
 // Batched decode (T <= 16 tokens per group): the whole layer in three
-// streaming kernels whose 16 MFMA columns are the group's tokens.
+// streaming kernels whose 16 MFMA columns are the group's tokens.  The
+// routed experts' dequantization is arithmetic-bound while the F16 shared
+// expert is memory-bound, so each stage pairs one with the other:
 //
-//   k_dec_stage1  router partial logits per input chunk, and the shared
-//                 expert's gate and up products as half-K partial tiles;
-//                 neither depends on routing.  The last router block to
-//                 arrive finishes routing (sum of partials, top-k, gate
-//                 weights, grouping); the last of the four blocks of a shared
-//                 tile forms h = silu(g) * u.  x is read in its input type and
-//                 converted in registers (the chunk owners of expert tile 0
-//                 keep the binary16 copy for stage 2).
-//   k_dec_stage2  the shared expert's down product, and for every distinct
+//   k_dec_stage1  router partial logits per input chunk (the last router
+//                 block to arrive finishes routing: top-k, gate weights,
+//                 grouping) and the shared expert's gate product as half-K
+//                 partial tiles.  x is read in its input type; the router
+//                 chunk owners keep the binary16 copy for stage 2.
+//   k_dec_stage2  the shared expert's up product (the last of a tile's two
+//                 blocks forms h = silu(g) * u), and for every distinct
 //                 selected expert its gate/up tiles: w * silu(G x) * (U x) as
-//                 binary16 plus fp32 sums over each 16 rows (one Q2K
-//                 sub-block of the down input).
-//   k_dec_stage3  one block per 16 output rows runs every distinct expert's
-//                 down product for those rows, adds the shared expert's
-//                 output, and writes y; waves take (expert, super-block)
-//                 units round-robin and their partials are added in a fixed
-//                 order.  It also clears stage 1's arrival counters.
+//                 binary16 plus the sums over each 16 rows (one Q2K
+//                 sub-block of the down input) as binary16 hi/lo.
+//   k_dec_stage3  per 16 output rows, a few blocks each take a share of the
+//                 routed super-blocks and of the shared expert's down input;
+//                 their partial tiles are added in a fixed order by the block
+//                 that arrives last, which writes y.  It also clears the
+//                 earlier stages' arrival counters.
 // Each distinct expert is read once per call however many tokens chose it,
-// and results do not depend on block scheduling.  Inside stage 1, blocks hand
-// partials to the last arriver with device-coherent (sc1) stores and loads
-// around an atomic counter, which needs no L2 write-back.
+// and results do not depend on block scheduling.  Blocks hand partials to
+// the last arriver with device-coherent (sc1) stores and loads around an
+// atomic counter, which needs no L2 write-back.
 //
 // Operands.  Packed weights: every lane owns a contiguous 16-byte piece of
 // its row's super-block and feeds those weights to consecutive MFMA steps
@@ -45,14 +45,9 @@ namespace ds4 {
 
 __constant__ GridTables c_dec_tables = make_grid_tables();
 
-constexpr int kW = 4;           // waves per block, stages 1 and 2
-constexpr int kW3 = 8;          // waves per block, stage 3
+constexpr int kW = 4;           // waves per block
 constexpr int kStageHalves = 4096;        // binary16 activations a stage-1/2 block may stage (per hi/lo part)
-constexpr size_t kStage3Bytes = 36 * 1024;  // stage 3 LDS for staged activations
-constexpr int kUnitsAhead = 8;  // stage 3 units whose weight loads a wave keeps in flight
-
-// inputs per router partial: 512, or 256 when d is an odd multiple of 256
-__host__ __device__ inline int router_chunk(int d) { return d % 512 == 0 ? 512 : 256; }
+constexpr size_t kStage3Bytes = 32 * 1024;  // stage 3 LDS for staged activations and sums
 
 __device__ inline int cb2_boff(int q, int s) { return 32 * (2 * q + (s >> 2)) + 8 * (s & 3); }
 __device__ inline int q2k_boff(int q, int s) { return 16 * (4 * q + (s >> 1)) + 8 * (s & 1); }
@@ -200,29 +195,58 @@ struct XStage {  // activations x[T][k0 .. k0+K) in the input type -> binary16 h
 // ============================================================== stage 1
 struct Stage1Lds {
   union {
-    RouteLds route;
-    struct {
+    RouteLds route;  // router blocks
+    struct {         // shared-gate blocks
       _Float16 bh[kStageHalves + 16 * 8];
       _Float16 bl[kStageHalves + 16 * 8];
-      float4_t red[kW][64];
     } sh;
   };
+  float4_t red[kW][64];
   int last;
 };
 
-// blocks [0, rblocks): router (expert tile, input chunk), chunk-major;
-// then 4 blocks per shared 16-row tile: (gate|up) x (K half).
+constexpr int kRouterWaitPolls = 0;  // bound on a shared-gate block's wait for the router blocks (0: no wait)
+
+// inputs per router block: 512, or 256 when d is an odd multiple of 256
+__host__ __device__ inline int router_chunk(int d) { return d % 512 == 0 ? 512 : 256; }
+
+// F16 rows (the lane's A row) x K-steps [ks0, ks1) of one staged or global
+// activation set, accumulated into acc.  a[]: the first kBatch steps,
+// loaded by the caller; later batches load here.
+// TRANS: the weights are the MFMA's B operand, so a lane's four outputs are
+// tokens 4q..4q+3 of its own row (otherwise rows 4q..4q+3 of its column).
+template <bool LO, bool BL, int kBatch, typename GetB, bool TRANS = false>
+__device__ inline void f16_steps(const uint16_t* __restrict__ rowp, int ks0, int ks1, int q, half8_t (&a)[kBatch],
+                                 GetB getb, float4_t& acc) {
+  for (int ks = ks0; ks < ks1; ks += kBatch) {
+    if (ks != ks0) {
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) a[j] = *(const half8_t*)(rowp + max(min(ks + j, ks1 - 1), 0) * 32 + 8 * q);
+    }
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {  // steps past the range multiply a zero A fragment
+      const int ksj = max(min(ks + j, ks1 - 1), 0);
+      const half8_t aj = ks + j < ks1 ? a[j] : zero_half8();
+      half8_t bh, bl;
+      getb(ksj * 32 + 8 * q, bh, bl);
+      acc = TRANS ? mfma16x16x32(bh, aj, acc) : mfma16x16x32(aj, bh, acc);
+      if (LO) acc = TRANS ? mfma16x16x32(bl, aj, acc) : mfma16x16x32(aj, bl, acc);
+    }
+  }
+}
+
+// blocks [0, rblocks): router (expert tile, input chunk), chunk-major; then
+// two blocks per shared 16-row tile: gate product over one K half each.
 template <bool LO, bool BL>
-__global__ __launch_bounds__(kW * 64) __attribute__((amdgpu_waves_per_eu(4))) void k_dec_stage1(ds4moe_layer L, int T, const void* __restrict__ x,
+__global__ __launch_bounds__(kW * 64) void k_dec_stage1(ds4moe_layer L, int T, const void* __restrict__ x,
                                                         int rblocks, float* __restrict__ plog, RouteOut ro,
                                                         _Float16* __restrict__ xh, _Float16* __restrict__ xl,
-                                                        float* __restrict__ gu_part, _Float16* __restrict__ hs16,
-                                                        int32_t* __restrict__ ctrl) {
+                                                        float* __restrict__ gu_part, int32_t* __restrict__ ctrl) {
   __shared__ Stage1Lds lds;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = lane & 15, q = lane >> 4;
   const int tc = min(c, T - 1);  // token feeding MFMA column c
-  const int d = L.d_model, E = L.n_experts, fs = L.d_ff_shared;
+  const int d = L.d_model, E = L.n_experts;
   float4_t acc = {0.f, 0.f, 0.f, 0.f};
   if ((int)blockIdx.x < rblocks) {  // ---------------- router partial logits
     const int ntile = (E + 15) / 16;
@@ -242,7 +266,7 @@ __global__ __launch_bounds__(kW * 64) __attribute__((amdgpu_waves_per_eu(4))) vo
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
       if (h < spw) {
-        if (et == 0 && c < T) {
+        if (et == 0 && c < T) {  // binary16 copy of x for stage 2
           const int k0 = (kc * (ck / 32) + wave * spw + h) * 32 + 8 * q;
           *(half8_t*)(xh + (int64_t)c * d + k0) = bh[h];
           if (LO) *(half8_t*)(xl + (int64_t)c * d + k0) = bl[h];
@@ -251,7 +275,7 @@ __global__ __launch_bounds__(kW * 64) __attribute__((amdgpu_waves_per_eu(4))) vo
         if (LO) acc = mfma16x16x32(a[h], bl[h], acc);
       }
     }
-    acc = reduce_waves<kW>(acc, lds.sh.red, wave, lane);
+    acc = reduce_waves<kW>(acc, lds.red, wave, lane);
     if (wave == 0) {
       if (c < T) {
 #pragma unroll
@@ -263,74 +287,53 @@ __global__ __launch_bounds__(kW * 64) __attribute__((amdgpu_waves_per_eu(4))) vo
       wait_stores();
     }
     __syncthreads();
-    if (threadIdx.x == 0) lds.last = atomicAdd(&ctrl[0], 1) == rblocks - 1;
+    if (threadIdx.x == 0) lds.last = atomicAdd(&ctrl[0], 1) == rblocks - 1;  // cleared by stage 3
     __syncthreads();
-    if (!lds.last) return;
-    route_finish_block<true>(lds.route, plog, d / ck, L.router_bias, E, L.top_k, T, ro);
-    if (threadIdx.x == 0) ctrl[0] = 0;
+    if (lds.last) route_finish_block<true>(lds.route, plog, d / ck, L.router_bias, E, L.top_k, T, ro);
     return;
   }
-  // ---------------- shared expert: (tile, gate|up, K half)
+  // ---------------- shared expert gate: (tile, K half)
+  // Let the router stream go first: the gate blocks start loading once every
+  // router block has arrived.  The wait is bounded and only orders traffic;
+  // results do not depend on it.
+  if (threadIdx.x == 0) {
+    for (int it = 0; it < kRouterWaitPolls && ld_acq_int(&ctrl[0]) < rblocks; ++it) __builtin_amdgcn_s_sleep(16);
+  }
+  __syncthreads();
   const int sb = blockIdx.x - rblocks;
-  const int tile = sb >> 2, part = sb & 3, mat = part >> 1, half = part & 1;
-  const uint16_t* rp = (mat ? L.sh_up : L.sh_gate) + (int64_t)(tile * 16 + c) * d;
-  const int nkh = d / 64;  // K-steps per half
+  const int tile = sb >> 1, half = sb & 1;
+  const uint16_t* rp = L.sh_gate + (int64_t)(tile * 16 + c) * d + half * (d / 2);
   int ks0, ks1;
-  split_range(nkh, kW, wave, ks0, ks1);
-  const int kb = half * (d / 2);  // first input of this half
-  const int st = stage_stride(d / 2);
+  split_range(d / 64, kW, wave, ks0, ks1);
+  const int kb = half * (d / 2), st = stage_stride(d / 2);
   constexpr int kBatch = 16;
   XStage<LO> xs;
   if (BL) xs.load(x, d, T, kb, d / 2);  // one piece per thread: T * d / 2 <= 8 * blockDim
   pin();
-  for (int ks = ks0; ks < ks1 || ks == ks0; ks += kBatch) {  // every wave runs the first batch (staging barrier)
-    half8_t a[kBatch];
+  half8_t a[kBatch];
 #pragma unroll
-    for (int j = 0; j < kBatch; ++j) a[j] = *(const half8_t*)(rp + kb + max(min(ks + j, ks1 - 1), 0) * 32 + 8 * q);
-    pin();
-    if (BL && ks == ks0) {
-      xs.store(lds.sh.bh, lds.sh.bl, T, d / 2);
-      __syncthreads();
-    }
-#pragma unroll
-    for (int j = 0; j < kBatch; ++j) {  // steps past the range multiply a zero A fragment
-      const int ksj = max(min(ks + j, ks1 - 1), 0);
-      const half8_t aj = ks + j < ks1 ? a[j] : zero_half8();
-      const int kk = ksj * 32 + 8 * q;  // within the half
-      half8_t bh, bl;
-      if (BL) {
-        bh = *(const half8_t*)(lds.sh.bh + tc * st + kk);
-        if (LO) bl = *(const half8_t*)(lds.sh.bl + tc * st + kk);
-      } else {
-        load_x8<LO>(x, d, tc, kb + kk, bh, bl);
-      }
-      acc = mfma16x16x32(aj, bh, acc);
-      if (LO) acc = mfma16x16x32(aj, bl, acc);
-    }
+  for (int j = 0; j < kBatch; ++j) a[j] = *(const half8_t*)(rp + max(min(ks0 + j, ks1 - 1), 0) * 32 + 8 * q);
+  pin();
+  if (BL) {
+    xs.store(lds.sh.bh, lds.sh.bl, T, d / 2);
+    __syncthreads();
   }
-  acc = reduce_waves<kW>(acc, lds.sh.red, wave, lane);
-  float* tp = gu_part + (size_t)tile * 4 * 16 * T;  // [part][row][t]
-  if (wave == 0) {
-    if (c < T) {
+  f16_steps<LO, BL, kBatch>(rp, ks0, ks1, q, a,
+                            [&](int kk, half8_t& bh, half8_t& bl) {
+                              if (BL) {
+                                bh = *(const half8_t*)(lds.sh.bh + tc * st + kk);
+                                if (LO) bl = *(const half8_t*)(lds.sh.bl + tc * st + kk);
+                              } else {
+                                load_x8<LO>(x, d, tc, kb + kk, bh, bl);
+                              }
+                            },
+                            acc);
+  acc = reduce_waves<kW>(acc, lds.red, wave, lane);
+  float* tp = gu_part + (size_t)tile * 4 * 16 * T;  // [part][row][t]; parts 0, 1: gate halves
+  if (wave == 0 && c < T) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) st_coh(&tp[((size_t)part * 16 + 4 * q + r) * T + c], acc[r]);
-    }
-    wait_stores();
+    for (int r = 0; r < 4; ++r) tp[((size_t)half * 16 + 4 * q + r) * T + c] = acc[r];
   }
-  __syncthreads();
-  if (threadIdx.x == 0) lds.last = atomicAdd(&ctrl[1 + tile], 1) == 3;
-  __syncthreads();
-  if (!lds.last || wave != 0) return;
-  if (c < T) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = 4 * q + r;
-      const float g = ld_coh(&tp[((size_t)0 * 16 + row) * T + c]) + ld_coh(&tp[((size_t)1 * 16 + row) * T + c]);
-      const float u = ld_coh(&tp[((size_t)2 * 16 + row) * T + c]) + ld_coh(&tp[((size_t)3 * 16 + row) * T + c]);
-      hs16[(int64_t)c * fs + tile * 16 + row] = (_Float16)(silu(g) * u);
-    }
-  }
-  if (lane == 0) ctrl[1 + tile] = 0;
 }
 
 // ============================================================== stage 2
@@ -341,58 +344,80 @@ struct Stage2Lds {
   _Float16 bl[kStageHalves + 16 * 8];
   float4_t red[kW][64];
   float4_t red2[kW][64];
+  int last;
 };
 
 constexpr int kSb2 = 4;  // CB2 super-blocks a wave loads at once
 
+// blocks [0, 2 nsh): shared expert up, (tile, K half); the second of a
+// tile's blocks to arrive forms h = silu(g) * u.  Then the routed gate/up
+// tiles: (distinct expert, 16-row tile).
 template <bool LO, bool BL>
-__global__ __launch_bounds__(kW * 64) __attribute__((amdgpu_waves_per_eu(4))) void k_dec_stage2(ds4moe_layer L, int T, RouteOut ro,
-                                                        const _Float16* __restrict__ xh,
-                                                        const _Float16* __restrict__ xl,
-                                                        const _Float16* __restrict__ hs16, float* __restrict__ ys,
-                                                        _Float16* __restrict__ hw16, float* __restrict__ hsum) {
+__global__ __launch_bounds__(kW * 64) __attribute__((amdgpu_waves_per_eu(4))) void k_dec_stage2(
+    ds4moe_layer L, int T, RouteOut ro, const _Float16* __restrict__ xh, const _Float16* __restrict__ xl,
+    float* __restrict__ gu_part, _Float16* __restrict__ hs16, _Float16* __restrict__ hw16,
+    _Float16* __restrict__ hsum, int32_t* __restrict__ ctrl) {
   __shared__ Stage2Lds lds;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = lane & 15, q = lane >> 4;
   const int tc = min(c, T - 1);
   const int d = L.d_model, f = L.d_ff, fs = L.d_ff_shared, k = L.top_k;
-  const int nr = f / 16, nb = d / QK, ndt = d / 16;
+  const int nr = f / 16, nb = d / QK, nsh = fs / 16;
   float4_t ag = {0.f, 0.f, 0.f, 0.f}, au = ag;
-  if ((int)blockIdx.x < ndt) {  // ---------------- shared expert down, 16 output rows
-    const int row0 = blockIdx.x * 16;
+  if ((int)blockIdx.x < 2 * nsh) {  // ---------------- shared expert up, (tile, K half)
+    const int tile = blockIdx.x >> 1, half = blockIdx.x & 1;
+    const uint16_t* rp = L.sh_up + (int64_t)(tile * 16 + c) * d + half * (d / 2);
     int ks0, ks1;
-    split_range(fs / 32, kW, wave, ks0, ks1);
-    const uint16_t* rp = L.sh_down + (int64_t)(row0 + c) * fs;
-    const int st = stage_stride(fs);
-    F16Stage<2> hs;  // T * fs <= 4096 halves: 512 pieces over 256 threads
-    if (BL) hs.load(hs16, fs, T, fs);
-    pin();
-    constexpr int kBatch = 16;
-    for (int ks = ks0; ks < ks1 || ks == ks0; ks += kBatch) {
-      half8_t a[kBatch];
+    split_range(d / 64, kW, wave, ks0, ks1);
+    const int kb = half * (d / 2), st = stage_stride(d / 2);
+    if (BL) dma_rows(xh + kb, d, T, d / 2, lds.bh, st, wave, kW, lane);
+    if (BL && LO) dma_rows(xl + kb, d, T, d / 2, lds.bl, st, wave, kW, lane);
+    constexpr int kBatch = BL ? 16 : 8;  // global activations take registers too
+    half8_t a[kBatch];
 #pragma unroll
-      for (int j = 0; j < kBatch; ++j) a[j] = *(const half8_t*)(rp + max(min(ks + j, ks1 - 1), 0) * 32 + 8 * q);
-      pin();
-      if (BL && ks == ks0) {
-        hs.store(lds.bh, T, fs);
-        __syncthreads();
+    for (int j = 0; j < kBatch; ++j) a[j] = *(const half8_t*)(rp + max(min(ks0 + j, ks1 - 1), 0) * 32 + 8 * q);
+    if (BL) {
+      wait_all();
+      __syncthreads();
+    }
+    f16_steps<LO, BL, kBatch>(rp, ks0, ks1, q, a,
+                              [&](int kk, half8_t& bh, half8_t& bl) {
+                                if (BL) {
+                                  bh = *(const half8_t*)(lds.bh + tc * st + kk);
+                                  if (LO) bl = *(const half8_t*)(lds.bl + tc * st + kk);
+                                } else {
+                                  bh = *(const half8_t*)(xh + (int64_t)tc * d + kb + kk);
+                                  if (LO) bl = *(const half8_t*)(xl + (int64_t)tc * d + kb + kk);
+                                }
+                              },
+                              ag);
+    ag = reduce_waves<kW>(ag, lds.red, wave, lane);
+    float* tp = gu_part + (size_t)tile * 4 * 16 * T;  // parts 2, 3: up halves
+    if (wave == 0) {
+      if (c < T) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) st_coh(&tp[((size_t)(2 + half) * 16 + 4 * q + r) * T + c], ag[r]);
       }
+      wait_stores();
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) lds.last = atomicAdd(&ctrl[1 + tile], 1) == 1;
+    __syncthreads();
+    if (!lds.last || wave != 0) return;
+    if (c < T) {
 #pragma unroll
-      for (int j = 0; j < kBatch; ++j) {  // steps past the range multiply a zero A fragment
-        const int ksj = max(min(ks + j, ks1 - 1), 0);
-        const half8_t aj = ks + j < ks1 ? a[j] : zero_half8();
-        const int kk = ksj * 32 + 8 * q;
-        const half8_t b = BL ? *(const half8_t*)(lds.bh + tc * st + kk)
-                             : *(const half8_t*)(hs16 + (int64_t)tc * fs + kk);
-        ag = mfma16x16x32(aj, b, ag);
+      for (int r = 0; r < 4; ++r) {
+        const int row = 4 * q + r;
+        const float g = tp[((size_t)0 * 16 + row) * T + c] + tp[((size_t)1 * 16 + row) * T + c];  // stage 1
+        const float u = ld_coh(&tp[((size_t)2 * 16 + row) * T + c]) + ld_coh(&tp[((size_t)3 * 16 + row) * T + c]);
+        hs16[(int64_t)c * fs + tile * 16 + row] = (_Float16)(silu(g) * u);
       }
     }
-    ag = reduce_waves<kW>(ag, lds.red, wave, lane);
-    if (wave == 0 && c < T) *(float4_t*)(ys + (int64_t)c * d + row0 + 4 * q) = ag;
+    if (lane == 0) ctrl[1 + tile] = 0;
     return;
   }
   // ---------------- routed gate/up: distinct expert i, 16-row tile
-  const int rel = blockIdx.x - ndt;
+  const int rel = blockIdx.x - 2 * nsh;
   const int i = rel / nr, tile = rel % nr;
   const int row0 = tile * 16;
   // phase 1: copies into LDS (activations, grid tables), independent of routing
@@ -407,8 +432,8 @@ __global__ __launch_bounds__(kW * 64) __attribute__((amdgpu_waves_per_eu(4))) vo
   wait_all();
   if (i >= nd) return;  // whole block; no copy is in flight
   __syncthreads();
-  if (slot >= T * k) slot = -1;
-  const int tb = slot >= 0 ? slot / k : 0;  // token feeding column c (any token when c has none)
+  // Transposed products: x (token c') is the MFMA's A operand, the weights
+  // its B operand, so lane (c, q) ends with tokens 4q..4q+3 of row row0 + c.
   const size_t mb = (size_t)f * nb;  // blocks per matrix
   const uint8_t* gc = (const uint8_t*)L.gate + (size_t)e * mb * 66;
   const uint8_t* uc = (const uint8_t*)L.up + (size_t)e * mb * 66;
@@ -418,6 +443,8 @@ __global__ __launch_bounds__(kW * 64) __attribute__((amdgpu_waves_per_eu(4))) vo
   const uint8_t* urow = uc + (size_t)(row0 + c) * nb * 64 + 16 * q;
   int sb0, sb1;
   split_range(nb, kW, wave, sb0, sb1);
+  // d of kSb2 consecutive super-blocks in one load per matrix when aligned
+  const bool dvec = nb % kSb2 == 0;
   for (int b0 = sb0; b0 < sb1; b0 += kSb2) {
     // phase 3: weight loads, consumed as they arrive
     u32x4_t cg[kSb2], cu[kSb2];
@@ -427,44 +454,52 @@ __global__ __launch_bounds__(kW * 64) __attribute__((amdgpu_waves_per_eu(4))) vo
       const int b = min(b0 + j, sb1 - 1);
       cg[j] = __builtin_nontemporal_load((const u32x4_t*)(grow + b * 64));
       cu[j] = __builtin_nontemporal_load((const u32x4_t*)(urow + b * 64));
-      dg[j] = h2f(gd[b]);
-      du[j] = h2f(ud[b]);
     }
+    if (dvec && b0 + kSb2 <= sb1) {
+      const u32x2_t g4 = *(const u32x2_t*)(gd + b0), u4 = *(const u32x2_t*)(ud + b0);
+#pragma unroll
+      for (int j = 0; j < kSb2; ++j) {
+        dg[j] = h2f((uint16_t)((j < 2 ? g4.x : g4.y) >> (16 * (j & 1))));
+        du[j] = h2f((uint16_t)((j < 2 ? u4.x : u4.y) >> (16 * (j & 1))));
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < kSb2; ++j) {
+        const int b = min(b0 + j, sb1 - 1);
+        dg[j] = h2f(gd[b]);
+        du[j] = h2f(ud[b]);
+      }
+    }
+    pin();
 #pragma unroll
     for (int j = 0; j < kSb2; ++j) {  // super-blocks past the range get a zero scale
-      {
-        const int kb = min(b0 + j, sb1 - 1) * QK;
-        if (b0 + j >= sb1) {
-          dg[j] = 0.0f;
-          du[j] = 0.0f;
-        }
-        float4_t pg = {0.f, 0.f, 0.f, 0.f}, pu = pg;
+      const int kb = min(b0 + j, sb1 - 1) * QK;
+      const float sg = b0 + j < sb1 ? dg[j] : 0.0f, su = b0 + j < sb1 ? du[j] : 0.0f;
+      float4_t pg = {0.f, 0.f, 0.f, 0.f}, pu = pg;
 #pragma unroll
-        for (int s = 0; s < 8; ++s) {
-          const int kk = kb + cb2_boff(q, s);
-          half8_t bh, bl;
-          if (BL) {
-            bh = *(const half8_t*)(lds.bh + tb * st + kk);
-            if (LO) bl = *(const half8_t*)(lds.bl + tb * st + kk);
-          } else {
-            bh = *(const half8_t*)(xh + (int64_t)tb * d + kk);
-            if (LO) bl = *(const half8_t*)(xl + (int64_t)tb * d + kk);
-          }
-          const half8_t a0 = cb2_frag((s & 4) ? cg[j].z : cg[j].x, (s & 4) ? cg[j].w : cg[j].y, s & 3, lds.mag, lds.sgn);
-          const half8_t a1 = cb2_frag((s & 4) ? cu[j].z : cu[j].x, (s & 4) ? cu[j].w : cu[j].y, s & 3, lds.mag, lds.sgn);
-          pg = mfma16x16x32(a0, bh, pg);
-          pu = mfma16x16x32(a1, bh, pu);
-          if (LO) {
-            pg = mfma16x16x32(a0, bl, pg);
-            pu = mfma16x16x32(a1, bl, pu);
-          }
+      for (int s2 = 0; s2 < 8; ++s2) {
+        const int kk = kb + cb2_boff(q, s2);
+        half8_t bh, bl;
+        if (BL) {
+          bh = *(const half8_t*)(lds.bh + tc * st + kk);
+          if (LO) bl = *(const half8_t*)(lds.bl + tc * st + kk);
+        } else {
+          bh = *(const half8_t*)(xh + (int64_t)tc * d + kk);
+          if (LO) bl = *(const half8_t*)(xl + (int64_t)tc * d + kk);
         }
-        // d of output row 4q + r is the A-row value of lane 4q + r
+        const half8_t a0 = cb2_frag((s2 & 4) ? cg[j].z : cg[j].x, (s2 & 4) ? cg[j].w : cg[j].y, s2 & 3, lds.mag, lds.sgn);
+        const half8_t a1 = cb2_frag((s2 & 4) ? cu[j].z : cu[j].x, (s2 & 4) ? cu[j].w : cu[j].y, s2 & 3, lds.mag, lds.sgn);
+        pg = mfma16x16x32(bh, a0, pg);
+        pu = mfma16x16x32(bh, a1, pu);
+        if (LO) {
+          pg = mfma16x16x32(bl, a0, pg);
+          pu = mfma16x16x32(bl, a1, pu);
+        }
+      }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          ag[r] += __shfl(dg[j], 4 * q + r) * pg[r];
-          au[r] += __shfl(du[j], 4 * q + r) * pu[r];
-        }
+      for (int r = 0; r < 4; ++r) {  // the lane's own row: its own d
+        ag[r] += sg * pg[r];
+        au[r] += su * pu[r];
       }
     }
   }
@@ -479,64 +514,86 @@ __global__ __launch_bounds__(kW * 64) __attribute__((amdgpu_waves_per_eu(4))) vo
     ag += lds.red[w][lane];
     au += lds.red2[w][lane];
   }
-  float psum = 0.0f;
-  if (slot >= 0) {
-    const float wt = ro.w[slot];
-    _Float16 hv[4];
+  // tokens 4q..4q+3: their slots for this expert; h = w * silu(g) * u as
+  // binary16 into hw16[slot][row], and the 16-row sums into hsum
+  const int4 sl4 = *(const int4*)(ro.tok_slot + i * kDecodeGroup + 4 * q);
+  const int slots[4] = {sl4.x, sl4.y, sl4.z, sl4.w};
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      hv[r] = (_Float16)(wt * (silu(ag[r]) * au[r]));
-      psum += (float)hv[r];
+  for (int r = 0; r < 4; ++r) {
+    const int slot = slots[r];
+    const bool has = 4 * q + r < T && slot >= 0 && slot < T * k;
+    float hv = 0.0f;
+    if (has) {
+      const _Float16 h16 = (_Float16)(ro.w[slot] * (silu(ag[r]) * au[r]));
+      hw16[(int64_t)slot * f + row0 + c] = h16;
+      hv = (float)h16;
     }
-    u32x2_t pk;
-    pk.x = (uint32_t)__builtin_bit_cast(uint16_t, hv[0]) | ((uint32_t)__builtin_bit_cast(uint16_t, hv[1]) << 16);
-    pk.y = (uint32_t)__builtin_bit_cast(uint16_t, hv[2]) | ((uint32_t)__builtin_bit_cast(uint16_t, hv[3]) << 16);
-    *(u32x2_t*)(hw16 + (int64_t)slot * f + row0 + 4 * q) = pk;
+    // sum over the 16 rows (lanes 16q..16q+15): quad, half-row and row mirrors
+    hv += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, hv), 0xB1, 0xF, 0xF, true));
+    hv += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, hv), 0x4E, 0xF, 0xF, true));
+    hv += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, hv), 0x141, 0xF, 0xF, true));
+    hv += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, hv), 0x140, 0xF, 0xF, true));
+    if (has && c == 0) {  // binary16 hi and lo planes of the sum (the Q2K min term's A operand)
+      const _Float16 hi = (_Float16)hv;
+      hsum[(int64_t)slot * (f / 16) + tile] = hi;
+      hsum[(int64_t)(T * k + slot) * (f / 16) + tile] = (_Float16)(hv - (float)hi);
+    }
   }
-  psum += __shfl_xor(psum, 16);
-  psum += __shfl_xor(psum, 32);
-  if (slot >= 0 && q == 0) hsum[(int64_t)slot * (f / 16) + tile] = psum;
 }
 
 // ============================================================== stage 3
-// Weight operands of one (expert, super-block) Q2K unit for lane (c, q).
+// Weight operands of one (expert, super-block) Q2K unit for lane (c, q):
+// its row is row0 + c.
 struct Q2kW {
-  u32x4_t codes;    // sub-blocks 4q..4q+3 of the lane's row
-  uint32_t sc4;     // their scale/min bytes
-  u32x2_t mins;     // scale/min bytes 8(q&1)..+7 (min MFMA operand; used by lanes q < 2)
-  uint32_t sup[4];  // (d, dmin) of the lane's four output rows
+  u32x4_t codes;  // sub-blocks 4q..4q+3 of the lane's row
+  uint32_t sc4;   // their scale/min bytes
+  u32x2_t mins;   // scale/min bytes 8(q&1)..+7 (min MFMA operand; used by lanes q < 2)
+  uint32_t sup;   // (d, dmin) of the lane's row
 };
 
-__device__ inline void q2k_wload(Q2kW& U, const uint8_t* base, size_t mb, int nb, int row0, int b, int c, int q) {
-  const uint8_t* rc = base + (size_t)(row0 + c) * nb * 64 + b * 64;
-  const uint8_t* rs = base + mb * 64 + (size_t)(row0 + c) * nb * 16 + b * 16;
-  const uint16_t* sup = (const uint16_t*)(base + mb * 80);
-  U.codes = __builtin_nontemporal_load((const u32x4_t*)(rc + 16 * q));
-  U.sc4 = *(const uint32_t*)(rs + 4 * q);
-  U.mins = *(const u32x2_t*)(rs + 8 * (q & 1));
-#pragma unroll
-  for (int r = 0; r < 4; ++r) U.sup[r] = *(const uint32_t*)(sup + ((size_t)(row0 + 4 * q + r) * nb + b) * 2);
+// Per-lane byte offsets of a Q2K unit's operands within one expert's packed
+// matrix, for super-block 0 (add b * 64, b * 16, b * 4 for super-block b).
+struct Q2kOff {
+  uint32_t codes, sc, mins, sup;
+};
+
+__device__ inline Q2kOff q2k_offsets(size_t mb, int nb, int row0, int c, int q) {
+  Q2kOff o;
+  o.codes = (uint32_t)((size_t)(row0 + c) * nb * 64 + 16 * q);
+  o.sc = (uint32_t)(mb * 64 + (size_t)(row0 + c) * nb * 16 + 4 * q);
+  o.mins = (uint32_t)(mb * 64 + (size_t)(row0 + c) * nb * 16 + 8 * (q & 1));
+  o.sup = (uint32_t)(mb * 80 + (size_t)(row0 + c) * nb * 4);
+  return o;
 }
 
-// bcol: activation column of the unit's super-block (LDS or global);
-// cs: its 16 sub-block sums.  valid: the column has a slot for this expert.
-__device__ inline void q2k_unit(const Q2kW& U, const _Float16* bcol, const float* cs, bool valid, int q,
-                                float4_t& acc) {
+// base: the expert's packed down matrix (wave-uniform); b: super-block (wave-uniform).
+__device__ inline void q2k_wload(Q2kW& U, const uint8_t* base, const Q2kOff& o, int b) {
+  U.codes = __builtin_nontemporal_load((const u32x4_t*)(base + o.codes + b * 64));
+  U.sc4 = *(const uint32_t*)(base + o.sc + b * 16);
+  U.mins = *(const u32x2_t*)(base + o.mins + b * 16);
+  U.sup = *(const uint32_t*)(base + o.sup + b * 4);
+}
+
+// One unit, transposed: the activations are the MFMA's A operand (row c' =
+// token c'), the weights its B operand, so lane (c, q) ends with tokens
+// 4q..4q+3 of row row0 + c.  bcol: the activation row of the lane's token at
+// the unit's super-block (LDS or global); csh/csl: binary16 hi/lo of its 16
+// sub-block sums.  vmask: bit r set when token 4q + r has a slot for this
+// expert.
+__device__ inline void q2k_unit(const Q2kW& U, const _Float16* bcol, const _Float16* csh, const _Float16* csl,
+                                uint32_t vmask, int q, float4_t& acc) {
   half8_t b[8];
 #pragma unroll
   for (int s = 0; s < 8; ++s) b[s] = *(const half8_t*)(bcol + q2k_boff(q, s));
-  half8_t bh, bl;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const float v = cs[8 * (q & 1) + e];
-    bh[e] = (_Float16)v;
-    bl[e] = (_Float16)(v - (float)bh[e]);
-  }
+  const half8_t bh = *(const half8_t*)(csh + 8 * (q & 1));
+  const half8_t bl = *(const half8_t*)(csl + 8 * (q & 1));
   float4_t p = {0.f, 0.f, 0.f, 0.f}, pm = p;
 #pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    const half8_t a = q2k_frag(U.codes[s >> 1], s & 1, (U.sc4 >> (8 * (s >> 1))) & 15u);
-    p = mfma16x16x32(a, b[s], p);
+  for (int j = 0; j < 4; ++j) {  // sub-block 4q + j: two MFMA steps share its scale
+    half8_t alo, ahi;
+    q2k_subblock(U.codes[j], (U.sc4 >> (8 * j)) & 15u, alo, ahi);
+    p = mfma16x16x32(b[2 * j], alo, p);
+    p = mfma16x16x32(b[2 * j + 1], ahi, p);
   }
   // min term: K-slots 0..15 are the 16 sub-blocks (lane groups q >= 2 add zeros)
   u32x4_t t;
@@ -545,97 +602,156 @@ __device__ inline void q2k_unit(const Q2kW& U, const _Float16* bcol, const float
   t.z = nib_hi_pair_f16(U.mins.y, 0);
   t.w = nib_hi_pair_f16(U.mins.y, 2);
   const half8_t am = q < 2 ? as_half8(t) : zero_half8();
-  pm = mfma16x16x32(am, bh, pm);
-  pm = mfma16x16x32(am, bl, pm);
+  pm = mfma16x16x32(bh, am, pm);
+  pm = mfma16x16x32(bl, am, pm);
+  const float dd = h2f((uint16_t)(U.sup & 0xFFFFu)), dm = h2f((uint16_t)(U.sup >> 16));
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const float v = h2f((uint16_t)(U.sup[r] & 0xFFFFu)) * p[r] - h2f((uint16_t)(U.sup[r] >> 16)) * pm[r];
-    acc[r] += valid ? v : 0.0f;
-  }
+  for (int r = 0; r < 4; ++r) acc[r] += ((vmask >> r) & 1u) ? dd * p[r] - dm * pm[r] : 0.0f;
 }
 
+constexpr int kUnits3 = 4;  // units whose weight loads a wave keeps in flight
+
+// Block (tile, part): output rows tile*16.., super-blocks of part `part`
+// (split_range over nparts), every distinct expert.  Partial tiles are
+// added in part order by the block that arrives last.
 template <bool BL>
-__global__ __launch_bounds__(kW3 * 64) void k_dec_stage3(ds4moe_layer L, int T, const int32_t* __restrict__ ndist,
-                                                         const int32_t* __restrict__ distinct,
-                                                         const int32_t* __restrict__ tok_slot,
-                                                         const _Float16* __restrict__ hw16,
-                                                         const float* __restrict__ hsum,
-                                                         const float* __restrict__ ys, int32_t* __restrict__ ctrl,
-                                                         int nctrl, int maxd, float* __restrict__ y) {
+__global__ __launch_bounds__(kW * 64) __attribute__((amdgpu_waves_per_eu(4))) void k_dec_stage3(
+    ds4moe_layer L, int T, int nparts, const int32_t* __restrict__ ndist, const int32_t* __restrict__ distinct,
+    const int32_t* __restrict__ tok_slot, const _Float16* __restrict__ hw16, const _Float16* __restrict__ hsum,
+    const _Float16* __restrict__ hs16, float* __restrict__ y_part, int32_t* __restrict__ ctrl, int nctrl1, int maxd,
+    float* __restrict__ y) {
   extern __shared__ __align__(16) unsigned char s_dyn[];  // staged activations when BL
-  __shared__ float4_t s_red[kW3][64];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __shared__ float4_t s_red[kW][64];
+  __shared__ int s_last;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = lane & 15, q = lane >> 4;
-  const int d = L.d_model, f = L.d_ff, k = L.top_k;
-  const int row0 = blockIdx.x * 16;
-  const int nb = f / QK;
+  const int tc = min(c, T - 1);
+  const int d = L.d_model, f = L.d_ff, fs = L.d_ff_shared, k = L.top_k;
+  const int tile = blockIdx.x / nparts, part = blockIdx.x % nparts;
+  const int row0 = tile * 16;
+  const int nb = f / QK, fs16 = f / 16;
   const size_t mb = (size_t)d * nb;
   const int S = T * k;
+  int sb0, sb1;
+  split_range(nb, nparts, part, sb0, sb1);
+  const int nbp = sb1 - sb0;  // routed super-blocks of this part
+  const int kcs = fs / nparts, k0s = part * kcs;  // shared down inputs of this part
   const uint8_t* down = (const uint8_t*)L.down;
-  _Float16* s_h = (_Float16*)s_dyn;                   // [S][f]
-  float* s_cs = (float*)(s_dyn + (size_t)S * f * 2);  // [S][f/16]
-  float4_t acc = {0.f, 0.f, 0.f, 0.f};
-  const int maxunits = maxd * nb;
+  // staged: routed activations [S][nbp * 256], their sums [2][S][nbp * 16],
+  // shared activations [T][kcs + 8]
+  _Float16* s_h = (_Float16*)s_dyn;
+  _Float16* s_cs = s_h + (size_t)S * nbp * QK;
+  _Float16* s_hs = s_cs + (size_t)2 * S * nbp * 16;
+  const int sts = stage_stride(kcs);
   if (blockIdx.x == 0)
-    for (int i = threadIdx.x; i < nctrl; i += blockDim.x) ctrl[i] = 0;
+    for (int i = threadIdx.x; i < nctrl1; i += blockDim.x) ctrl[i] = 0;
   // copies of the activations into LDS, then the routing tables; waiting for
   // the tables also completes the copies, and one barrier publishes them
   if (BL) {
-    dma_pieces(hw16, S * f / 8, s_h, wave, kW3, lane);
-    dma_pieces(hsum, S * (f / 16) / 4, s_cs, wave, kW3, lane);
+    if (nbp > 0) {
+      dma_rows(hw16 + sb0 * QK, f, S, nbp * QK, s_h, nbp * QK, wave, kW, lane);
+      dma_rows(hsum + sb0 * 16, fs16, 2 * S, nbp * 16, s_cs, nbp * 16, wave, kW, lane);
+    }
+    dma_rows(hs16 + k0s, fs, T, kcs, s_hs, sts, wave, kW, lane);
   }
-  const int nunits = min(*ndist, maxd) * nb;
-  // Units: u = (expert slot u / nb, super-block u % nb); wave w takes
-  // u = w, w + kW3, ... in batches of kUnitsAhead whose weight loads are all
-  // issued before the batch's first MFMA.
-  int ej[kUnitsAhead], sj[kUnitsAhead];
+  const int nd = min(*ndist, maxd);
+  const int maxunits = maxd * nbp, nunits = nd * nbp;
+  // units u = (expert slot u / nbp, super-block sb0 + u % nbp); wave w takes
+  // u = w, w + kW, ... in batches of kUnits3
+  int ej[kUnits3], sj[kUnits3];
 #pragma unroll
-  for (int j = 0; j < kUnitsAhead; ++j) {
-    const int i = min((wave + j * kW3) / nb, maxd - 1);
+  for (int j = 0; j < kUnits3; ++j) {
+    const int i = nbp > 0 ? min((wave + j * kW) / nbp, maxd - 1) : 0;
     ej[j] = distinct[i];
     sj[j] = tok_slot[i * kDecodeGroup + c];
   }
   wait_all();
   __syncthreads();
-  for (int u0 = wave; u0 < maxunits; u0 += kW3 * kUnitsAhead) {
+  float4_t acc = {0.f, 0.f, 0.f, 0.f};
+  // shared expert down over this part's inputs (F16 rows row0..+15)
+  {
+    const uint16_t* rp = L.sh_down + (int64_t)(row0 + c) * fs + k0s;
+    int ks0, ks1;
+    split_range(kcs / 32, kW, wave, ks0, ks1);
+    constexpr int kBatch = 4;
+    half8_t a[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) a[j] = *(const half8_t*)(rp + max(min(ks0 + j, ks1 - 1), 0) * 32 + 8 * q);
+    auto getb = [&](int kk, half8_t& bh, half8_t&) {
+      bh = BL ? *(const half8_t*)(s_hs + tc * sts + kk) : *(const half8_t*)(hs16 + (int64_t)tc * fs + k0s + kk);
+    };
+    f16_steps<false, BL, kBatch, decltype(getb), true>(rp, ks0, ks1, q, a, getb, acc);
+  }
+  const Q2kOff off = q2k_offsets(mb, nb, row0, c, q);
+  for (int u0 = wave; u0 < maxunits; u0 += kW * kUnits3) {
     if (u0 != wave) {  // routing tables of later batches
 #pragma unroll
-      for (int j = 0; j < kUnitsAhead; ++j) {
-        const int i = min((u0 + j * kW3) / nb, maxd - 1);
+      for (int j = 0; j < kUnits3; ++j) {
+        const int i = min((u0 + j * kW) / nbp, maxd - 1);
         ej[j] = distinct[i];
         sj[j] = tok_slot[i * kDecodeGroup + c];
       }
     }
-    Q2kW W[kUnitsAhead];
+    Q2kW W[kUnits3];
 #pragma unroll
-    for (int j = 0; j < kUnitsAhead; ++j) {
-      const int u = min(u0 + j * kW3, maxunits - 1);
-      q2k_wload(W[j], down + (size_t)clamp_index(ej[j], L.n_experts) * mb * 84, mb, nb, row0, u % nb, c, q);
+    for (int j = 0; j < kUnits3; ++j) {
+      const int u = min(u0 + j * kW, maxunits - 1);
+      const int e = __builtin_amdgcn_readfirstlane(clamp_index(ej[j], L.n_experts));  // the same in every lane
+      q2k_wload(W[j], down + (size_t)e * mb * 84, off, sb0 + u % nbp);
     }
-    // units past the end and columns without a slot add nothing
+    pin();
+    // units past the end and tokens without a slot add nothing
 #pragma unroll
-    for (int j = 0; j < kUnitsAhead; ++j) {
-      const int u = u0 + j * kW3;
-      const int slot = sj[j];
-      const bool valid = u < nunits && slot >= 0 && slot < S;
-      const int row = valid ? slot : 0;
-      const int b = min(u, maxunits - 1) % nb;
+    for (int j = 0; j < kUnits3; ++j) {
+      const int u = u0 + j * kW;
+      const int slot = sj[j];  // slot of token c for this unit's expert
+      const bool has = u < nunits && slot >= 0 && slot < S;
+      const uint32_t vmask = (uint32_t)(__ballot(has) >> (4 * q)) & 15u;  // tokens 4q..4q+3
+      const int row = has ? slot : 0;
+      const int bl = min(u, maxunits - 1) % nbp;  // super-block within the part
       if (BL)
-        q2k_unit(W[j], s_h + (size_t)row * f + b * QK, s_cs + (size_t)row * (f / 16) + b * 16, valid, q, acc);
+        q2k_unit(W[j], s_h + (size_t)row * nbp * QK + bl * QK, s_cs + (size_t)row * nbp * 16 + bl * 16,
+                 s_cs + (size_t)(S + row) * nbp * 16 + bl * 16, vmask, q, acc);
       else
-        q2k_unit(W[j], hw16 + (size_t)row * f + b * QK, hsum + (size_t)row * (f / 16) + b * 16, valid, q, acc);
+        q2k_unit(W[j], hw16 + (size_t)row * f + (sb0 + bl) * QK, hsum + (size_t)row * fs16 + (sb0 + bl) * 16,
+                 hsum + (size_t)(S + row) * fs16 + (sb0 + bl) * 16, vmask, q, acc);
     }
   }
-  acc = reduce_waves<kW3>(acc, s_red, wave, lane);
-  if (wave == 0 && c < T) {
-    const float4_t s = *(const float4_t*)(ys + (int64_t)c * d + row0 + 4 * q);
-    *(float4_t*)(y + (int64_t)c * d + row0 + 4 * q) = acc + s;
+  acc = reduce_waves<kW>(acc, s_red, wave, lane);  // lane (c, q): tokens 4q + r of row row0 + c
+  if (nparts == 1) {
+    if (wave == 0) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (4 * q + r < T) y[(int64_t)(4 * q + r) * d + row0 + c] = acc[r];
+    }
+    return;
   }
+  float* tp = y_part + (size_t)tile * nparts * 16 * T;  // [part][row][t]
+  if (wave == 0) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (4 * q + r < T) st_coh(&tp[((size_t)part * 16 + c) * T + 4 * q + r], acc[r]);
+    wait_stores();
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) s_last = atomicAdd(&ctrl[kCtrlDown + tile], 1) == nparts - 1;
+  __syncthreads();
+  if (!s_last || wave != 0) return;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int t = 4 * q + r;
+    if (t < T) {
+      float sum = 0.0f;
+      for (int pp = 0; pp < nparts; ++pp) sum += ld_coh(&tp[((size_t)pp * 16 + c) * T + t]);
+      y[(int64_t)t * d + row0 + c] = sum;
+    }
+  }
+  if (lane == 0) ctrl[kCtrlDown + tile] = 0;
 }
 
 // ============================================================== launcher
 template <bool LO, bool BL>
-static void launch_stages12(const Fwd& f, int rblocks, int nsh, int ndt, int maxd, int nr, const RouteOut& ro) {
+static void launch_stages12(const Fwd& f, int rblocks, int nsh, int maxd, int nr, const RouteOut& ro) {
   const ds4moe_layer& L = f.L;
   const WsLayout& y = f.lay;
   char* ws = f.ws;
@@ -645,14 +761,14 @@ static void launch_stages12(const Fwd& f, int rblocks, int nsh, int ndt, int max
   auto plog = (float*)(ws + y.plog);
   auto ctrl = (int32_t*)(ws + y.ctrl);
   auto gu = (float*)(ws + y.gu_part);
-  auto ys = (float*)(ws + y.ys);
   auto hs16 = (_Float16*)(ws + y.hs16);
   auto hw16 = (_Float16*)(ws + y.hw16);
-  auto hsum = (float*)(ws + y.hsum);
+  auto hsum = (_Float16*)(ws + y.hsum);
   const dim3 blk(kW * 64);
-  DS4_LAUNCH((k_dec_stage1<LO, BL>), dim3(rblocks + 4 * nsh), blk, 0, f.st, L, T, f.x, rblocks, plog, ro, xh, xl, gu,
-             hs16, ctrl);
-  DS4_LAUNCH((k_dec_stage2<LO, BL>), dim3(ndt + maxd * nr), blk, 0, f.st, L, T, ro, xh, xl, hs16, ys, hw16, hsum);
+  DS4_LAUNCH((k_dec_stage1<LO, BL>), dim3(rblocks + 2 * nsh), blk, 0, f.st, L, T, f.x, rblocks, plog, ro, xh, xl, gu,
+             ctrl);
+  DS4_LAUNCH((k_dec_stage2<LO, BL>), dim3(2 * nsh + maxd * nr), blk, 0, f.st, L, T, ro, xh, xl, gu, hs16, hw16, hsum,
+             ctrl);
 }
 
 hipError_t launch_decode(const Fwd& f) {
@@ -660,35 +776,40 @@ hipError_t launch_decode(const Fwd& f) {
   const WsLayout& y = f.lay;
   char* ws = f.ws;
   const int T = (int)f.T;
-  const int d = L.d_model, E = L.n_experts;
-  const int kr = d / router_chunk(d);
-  const int rblocks = ((E + 15) / 16) * kr;
-  const int nsh = L.d_ff_shared / 16, nr = L.d_ff / 16, ndt = d / 16;
+  const int d = L.d_model, E = L.n_experts, fs = L.d_ff_shared;
+  const int rblocks = ((E + 15) / 16) * (d / router_chunk(d));
+  const int nsh = fs / 16, nr = L.d_ff / 16, ndt = d / 16;
   const int maxd = std::min(E, T * L.top_k);
   const RouteOut ro = route_out(f);
-  // stage the activations in LDS when every staged row set fits:
-  // x halves (stage 1), hs16 and x (stage 2)
-  const bool bl = (int64_t)T * std::max(d, L.d_ff_shared) <= kStageHalves;
+  // stage the activations in LDS when every staged row set fits: the x
+  // halves (stages 1 and 2) and x (stage 2 routed)
+  const bool bl = (int64_t)T * d <= kStageHalves;
   if (f.lo) {
-    if (bl) launch_stages12<true, true>(f, rblocks, nsh, ndt, maxd, nr, ro);
-    else launch_stages12<true, false>(f, rblocks, nsh, ndt, maxd, nr, ro);
+    if (bl) launch_stages12<true, true>(f, rblocks, nsh, maxd, nr, ro);
+    else launch_stages12<true, false>(f, rblocks, nsh, maxd, nr, ro);
   } else {
-    if (bl) launch_stages12<false, true>(f, rblocks, nsh, ndt, maxd, nr, ro);
-    else launch_stages12<false, false>(f, rblocks, nsh, ndt, maxd, nr, ro);
+    if (bl) launch_stages12<false, true>(f, rblocks, nsh, maxd, nr, ro);
+    else launch_stages12<false, false>(f, rblocks, nsh, maxd, nr, ro);
   }
   auto ctrl = (int32_t*)(ws + y.ctrl);
-  auto ys = (float*)(ws + y.ys);
+  auto hs16 = (_Float16*)(ws + y.hs16);
   auto hw16 = (_Float16*)(ws + y.hw16);
-  auto hsum = (float*)(ws + y.hsum);
+  auto hsum = (_Float16*)(ws + y.hsum);  // hi plane [S][f/16], then lo plane
+  auto y_part = (float*)(ws + y.y_part);
   const int S = T * L.top_k;
-  const size_t stage_bytes = (size_t)S * L.d_ff * 2 + (size_t)S * (L.d_ff / 16) * 4;
-  const dim3 blk3(kW3 * 64);
+  const int nb = L.d_ff / QK;
+  const int nparts = std::min(kDownParts, nb);
+  const int nbp_max = (nb + nparts - 1) / nparts;
+  // stage 3 stages each part's routed activations and sums, and its share of h
+  const size_t stage_bytes = (size_t)S * nbp_max * QK * 2 + (size_t)2 * S * nbp_max * 16 * 2 +
+                             (size_t)T * stage_stride(fs / nparts) * 2;
+  const dim3 blk3(kW * 64);
   if (stage_bytes <= kStage3Bytes)
-    DS4_LAUNCH(k_dec_stage3<true>, dim3(ndt), blk3, stage_bytes, f.st, L, T, ro.ndist, ro.distinct, ro.tok_slot,
-               hw16, hsum, ys, ctrl, ctrl_ints(L), maxd, f.y);
+    DS4_LAUNCH(k_dec_stage3<true>, dim3(ndt * nparts), blk3, stage_bytes, f.st, L, T, nparts, ro.ndist, ro.distinct,
+               ro.tok_slot, hw16, hsum, hs16, y_part, ctrl, ctrl_ints(L), maxd, f.y);
   else
-    DS4_LAUNCH(k_dec_stage3<false>, dim3(ndt), blk3, 0, f.st, L, T, ro.ndist, ro.distinct, ro.tok_slot, hw16,
-               hsum, ys, ctrl, ctrl_ints(L), maxd, f.y);
+    DS4_LAUNCH(k_dec_stage3<false>, dim3(ndt * nparts), blk3, 0, f.st, L, T, nparts, ro.ndist, ro.distinct,
+               ro.tok_slot, hw16, hsum, hs16, y_part, ctrl, ctrl_ints(L), maxd, f.y);
   return hipGetLastError();
 }
 

@@ -83,8 +83,8 @@ __device__ inline float gate_weight(const float* sel_v, int k, int j) {
   float vmax = sel_v[0];
   for (int a = 1; a < k; ++a) vmax = fmaxf(vmax, sel_v[a]);
   float den = 0.0f;
-  for (int a = 0; a < k; ++a) den += expf(sel_v[a] - vmax);
-  return expf(sel_v[j] - vmax) / den;
+  for (int a = 0; a < k; ++a) den += __expf(sel_v[a] - vmax);
+  return __expf(sel_v[j] - vmax) / den;
 }
 
 // Block-wide exclusive scan of one int per thread (blockDim a multiple of
@@ -119,43 +119,132 @@ struct RouteOut {
   int32_t *ndist, *distinct, *tok_slot;  // distinct experts, slot of token t in distinct[i] at [i*16 + t]
 };
 
-// Run by a whole block (any multiple of 64 threads up to 1024), T <= 16
-// (so S = T * k <= 256):
-// logits = sum of nparts partial rows plog[p][t][e] (+ bias), top-k and
-// gate weights per token, then counts, offsets, perm (slots t*k + j by
-// expert, then token), inv, and the distinct-expert table.  COH: the
-// partials were written by other blocks of the running kernel (read them
-// with coherent loads).
-// LDS of route_finish_block (a struct so kernels can overlay it with the
+// LDS of route_finish_block (a struct so kernels can place it beside the
 // LDS of their other block roles).
 struct RouteLds {
-  float logit[4096];
-  int sel_e[kDecodeGroup][kMaxTopK];
-  float sel_v[kDecodeGroup][kMaxTopK];
-  uint32_t tokm[kMaxExperts];  // bit t: token t chose expert e
-  int off[kMaxExperts];
-  int dpos[kMaxExperts];
-  int ndist;
+  float logit[1024];                    // logits when T * E <= 1024 (else the workspace copy)
+  int sel_e[kDecodeGroup][kMaxTopK];    // per token: chosen experts, ascending
+  float sel_v[kDecodeGroup][kMaxTopK];  // their logits
+  int fe[kDecodeGroup * kMaxTopK];      // expert of slot s = t * k + j
+  uint32_t tokm[kMaxExperts];           // bit t: token t chose expert e
+  uint32_t selm[kMaxExperts / 32];      // bit e: some token chose expert e
+  int selpre[kMaxExperts / 32 + 1];     // chosen experts below word w of selm
+  int dist[kDecodeGroup * kMaxTopK];    // distinct experts, ascending
+  int wsel[16];                         // one token: chosen experts per wave
 };
 
+// Number of experts below e that some token chose (e's distinct position).
+__device__ inline int distinct_below(const RouteLds& R, int e) {
+  return R.selpre[e >> 5] + __popc(R.selm[e >> 5] & ((1u << (e & 31)) - 1u));
+}
+
+// One key per lane: flags the k largest valid keys, equal keys going to the
+// lower lane; every valid lane is flagged when fewer than k are valid.  The
+// k-th largest key is found bit by bit with ballots (valid order keys are
+// never 0).
+__device__ inline bool wave_top_flags(uint32_t key, bool valid, int k, int lane) {
+  key = valid ? key : 0u;
+  uint32_t thr = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = thr | (1u << bit);
+    thr = __popcll(__ballot(key >= cand)) >= k ? cand : thr;
+  }
+  const int need_eq = k - __popcll(__ballot(key > thr));
+  const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;
+  const bool eq = valid && key == thr;
+  return key > thr || (eq && __popcll(__ballot(eq) & below) < need_eq);
+}
+
+// One token (T = 1, E <= 64 * waves, waves * k <= 64): each wave flags the k
+// largest logits of its 64 experts, wave 0 then flags the k largest of those
+// candidates.  Lane order is expert order at both levels, so ties go to the
+// lower expert index and the winners, compacted by ballot, come out in
+// ascending expert order.  With one token, slot j holds the j-th chosen
+// expert, so perm and inv are the identity.  logits are filled and the block
+// has passed a barrier.
+__device__ inline void route_finish_one(RouteLds& R, const float* logits, int E, int k, const RouteOut& o) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
+  const int e = threadIdx.x;
+  const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;
+  int* cand_e = R.fe;              // [nwaves][k] candidates, ascending within a wave
+  int* cand_n = R.wsel;            // candidates per wave
+  {
+    const bool f = wave_top_flags(e < E ? order_key(logits[e]) : 0u, e < E, k, lane);
+    const uint64_t fm = __ballot(f);
+    if (f) cand_e[wave * k + __popcll(fm & below)] = e;
+    if (lane == 0) cand_n[wave] = __popcll(fm);
+  }
+  __syncthreads();
+  if (wave == 0) {
+    const int w = lane / k, j = lane - w * k;
+    const bool valid = w < nwaves && j < cand_n[w];
+    const int ce = valid ? cand_e[lane] : 0;
+    const float cv = valid ? logits[ce] : 0.0f;
+    const bool f = wave_top_flags(order_key(cv), valid, k, lane);
+    const uint64_t fm = __ballot(f);
+    if (f) {
+      const int pos = __popcll(fm & below);
+      R.sel_e[0][pos] = ce;
+      R.sel_v[0][pos] = cv;
+      atomicOr(&R.selm[ce >> 5], 1u << (ce & 31));
+    }
+    __builtin_amdgcn_wave_barrier();
+    if (lane < k) {
+      const int ej = R.sel_e[0][lane];
+      float vmax = R.sel_v[0][0];
+      for (int a = 1; a < k; ++a) vmax = fmaxf(vmax, R.sel_v[0][a]);
+      float den = 0.0f;  // summed in slot order, as in gate_weight
+      for (int a = 0; a < k; ++a) den += __expf(R.sel_v[0][a] - vmax);
+      const float wj = __expf(R.sel_v[0][lane] - vmax) / den;
+      o.idx[lane] = ej;
+      o.w[lane] = wj;
+      if (o.idx_out) o.idx_out[lane] = ej;
+      if (o.w_out) o.w_out[lane] = wj;
+      o.perm[lane] = lane;
+      o.inv[lane] = lane;
+      if (o.perm_out) o.perm_out[lane] = lane;
+      o.distinct[lane] = ej;
+    }
+    if (lane == 0) {
+      o.offsets[E] = k;
+      if (o.offsets_out) o.offsets_out[E] = k;
+      *o.ndist = k;
+    }
+  }
+  __syncthreads();
+  if (e < E) {  // counts and offsets from the chosen-expert bitmask
+    const uint32_t wd = R.selm[e >> 5];
+    const int c = (wd >> (e & 31)) & 1u;
+    int off = __popc(wd & ((1u << (e & 31)) - 1u));
+    for (int w = 0; w < (e >> 5); ++w) off += __popc(R.selm[w]);
+    o.counts[e] = c;
+    o.offsets[e] = off;
+    if (o.counts_out) o.counts_out[e] = c;
+    if (o.offsets_out) o.offsets_out[e] = off;
+  }
+  for (int i = threadIdx.x; i < k * kDecodeGroup; i += blockDim.x)
+    o.tok_slot[i] = (i % kDecodeGroup) == 0 ? i / kDecodeGroup : -1;
+}
+
+// Run by a whole block (any multiple of 64 threads up to 1024), T <= 16
+// (so S = T * k <= 256): logits = sum of nparts partial rows plog[p][t][e]
+// (+ bias), top-k and gate weights per token, then counts, offsets, perm
+// (slots t*k + j by expert, then token), inv, and the distinct-expert table.
+// COH: the partials were written by other blocks of the running kernel (read
+// them with coherent loads).
 template <bool COH = false>
 __device__ inline void route_finish_block(RouteLds& R, const float* __restrict__ plog, int nparts,
                                           const float* __restrict__ bias, int E, int k, int T, const RouteOut& o) {
-  float* s_logit = R.logit;
-  auto& s_sel_e = R.sel_e;
-  auto& s_sel_v = R.sel_v;
-  uint32_t* s_tokm = R.tokm;
-  int* s_off = R.off;
-  int* s_dpos = R.dpos;
-  int& s_ndist = R.ndist;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nwaves = blockDim.x >> 6, nthr = blockDim.x;
-  for (int e = threadIdx.x; e < E; e += nthr) s_tokm[e] = 0u;
-  float* logits = T * E <= 4096 ? s_logit : o.logits;
+  const int S = T * k;
+  for (int e = threadIdx.x; e < E; e += nthr) R.tokm[e] = 0u;
+  for (int w = threadIdx.x; w < (E + 31) / 32; w += nthr) R.selm[w] = 0u;
+  float* logits = T * E <= 1024 ? R.logit : o.logits;
   for (int i = threadIdx.x; i < T * E; i += nthr) {
     const int e = i % E;
     float a = 0.0f;
-#pragma unroll 8
+#pragma unroll 32
     for (int p = 0; p < nparts; ++p) {
       const float* src = plog + (int64_t)p * T * E + i;
       a += COH ? __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : *src;
@@ -163,58 +252,79 @@ __device__ inline void route_finish_block(RouteLds& R, const float* __restrict__
     logits[i] = bias ? a + bias[e] : a;
   }
   __syncthreads();
-  for (int t = wave; t < T; t += nwaves) wave_select(logits + (int64_t)t * E, E, k, lane, s_sel_e[t], s_sel_v[t]);
+  if (T == 1 && E <= 64 * nwaves && nwaves * k <= 64) {
+    route_finish_one(R, logits, E, k, o);
+    return;
+  }
+  for (int t = wave; t < T; t += nwaves) wave_select(logits + (int64_t)t * E, E, k, lane, R.sel_e[t], R.sel_v[t]);
   __syncthreads();
-  const int S = T * k;
+  // per slot: gate weight, and the expert/token bitmaps
   for (int s = threadIdx.x; s < S; s += nthr) {
-    const int t = s / k, j = s % k;
-    const int e = s_sel_e[t][j];
-    const float wj = gate_weight(s_sel_v[t], k, j);
+    const int t = s / k, j = s - t * k;
+    const int e = R.sel_e[t][j];
+    const float wj = gate_weight(R.sel_v[t], k, j);
     o.idx[s] = e;
     o.w[s] = wj;
     if (o.idx_out) o.idx_out[s] = e;
     if (o.w_out) o.w_out[s] = wj;
-    atomicOr(&s_tokm[e], 1u << t);
+    R.fe[s] = e;
+    atomicOr(&R.tokm[e], 1u << t);
+    atomicOr(&R.selm[e >> 5], 1u << (e & 31));
   }
   __syncthreads();
-  // per expert: count = tokens that chose it; offset = selected slots of
-  // lower experts; distinct position = distinct experts below it (a slot
-  // stands for its expert's first token).  O(S) per expert, no scan.
-  for (int e = threadIdx.x; e <= E; e += nthr) {
-    int off = 0, dpos = 0;
-    for (int s = 0; s < S; ++s) {
-      const int es = s_sel_e[s / k][s % k];
-      const int ts = s / k;
-      off += es < e;
-      dpos += es < e && ts == __ffs(s_tokm[es]) - 1;
+  if (threadIdx.x == 0) {  // prefix counts of chosen experts per 32-expert word
+    int n = 0;
+    for (int w = 0; w <= (E + 31) / 32; ++w) {
+      R.selpre[w] = n;
+      if (w < (E + 31) / 32) n += __popc(R.selm[w]);
     }
+  }
+  __syncthreads();
+  // per expert: count, offset (selected slots of lower experts), distinct table
+  for (int e = threadIdx.x; e <= E; e += nthr) {
+    int off = 0;
+    for (int s = 0; s < S; ++s) off += R.fe[s] < e;
     if (e == E) {
       o.offsets[E] = S;
       if (o.offsets_out) o.offsets_out[E] = S;
-      *o.ndist = dpos;
-      s_ndist = dpos;
+      *o.ndist = R.selpre[(E + 31) / 32];
       continue;
     }
-    const int c = __popc(s_tokm[e]);
-    s_off[e] = off;
-    s_dpos[e] = dpos;
+    const int c = __popc(R.tokm[e]);
     o.counts[e] = c;
     o.offsets[e] = off;
     if (o.counts_out) o.counts_out[e] = c;
     if (o.offsets_out) o.offsets_out[e] = off;
-    if (c > 0) o.distinct[dpos] = e;
+    if (c > 0) {
+      const int dp = distinct_below(R, e);
+      o.distinct[dp] = e;
+      R.dist[dp] = e;
+    }
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < s_ndist * kDecodeGroup; i += nthr) o.tok_slot[i] = -1;
-  __syncthreads();
+  // per slot: position in the expert-major order
   for (int s = threadIdx.x; s < S; s += nthr) {
     const int t = s / k;
-    const int e = s_sel_e[t][s % k];
-    const int pos = s_off[e] + __popc(s_tokm[e] & ((1u << t) - 1u));  // earlier tokens of expert e
+    const int e = R.fe[s];
+    int off = 0;
+    for (int s2 = 0; s2 < S; ++s2) off += R.fe[s2] < e;
+    const int pos = off + __popc(R.tokm[e] & ((1u << t) - 1u));  // earlier tokens of expert e
     o.perm[pos] = s;
     o.inv[s] = pos;
     if (o.perm_out) o.perm_out[pos] = s;
-    o.tok_slot[s_dpos[e] * kDecodeGroup + t] = s;
+  }
+  // per (distinct expert, token): its slot, or -1
+  const int nd = R.selpre[(E + 31) / 32];
+  for (int i = threadIdx.x; i < nd * kDecodeGroup; i += nthr) {
+    const int di = i / kDecodeGroup, t = i % kDecodeGroup;
+    const int e = R.dist[di];
+    int slot = -1;
+    if (t < T && ((R.tokm[e] >> t) & 1u)) {
+      int j = 0;
+      while (R.sel_e[t][j] != e) ++j;  // e is among token t's k experts
+      slot = t * k + j;
+    }
+    o.tok_slot[i] = slot;
   }
 }
 

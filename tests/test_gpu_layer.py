@@ -116,6 +116,15 @@ def test_decode1_forward(decode1):
     assert err <= TOL
 
 
+def test_decode1_route_one_token(decode1):
+    """Routing alone for one token at E = 256 (the routing block's width):
+    indices, weights, counts, offsets (including offsets[E]) and perm."""
+    x = decode1.x()
+    ref = oracle_ref(decode1, x)
+    got = decode1.route(x)
+    check_routing(got, ref, decode1.cfg.k)
+
+
 def test_decode1_prefill_entry_point(decode1):
     x = decode1.x()
     ref = oracle_ref(decode1, x)
