@@ -39,6 +39,26 @@ MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA, vendor peak
 
 METRIC = "routed-MoE layer decode tok/s + % HBM peak; 2048-tok prefill tok/s + % MFMA"
 
+# HBM bytes per launch of the decode kernels, from two rocprofv3 counter
+# passes (FETCH_SIZE, WRITE_SIZE) scaled by the same counters on a 256 MiB
+# device copy; valid for the kernel sources with this hash only (see
+# profiles/decode1_hbm_traffic.md for the commands and the raw counts).
+TRAFFIC_SOURCE_HASH = "56008426c763f62d"
+TRAFFIC_BYTES = {"k_dec_stage1": 19.16e6, "k_dec_stage2": 44.05e6, "k_dec_stage3": 46.56e6}
+
+
+def kernel_source_hash():
+    """sha256 over the library's kernel sources (name + bytes, sorted)."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "bit_quantized_routed_router_amd", "csrc", "*"))):
+        if f.endswith((".hip", ".h", ".cpp")):
+            h.update(os.path.basename(f).encode())
+            with open(f, "rb") as fh:
+                h.update(fh.read())
+    return h.hexdigest()[:16]
+
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
@@ -184,8 +204,11 @@ def bench_decode(args):
     res = dict(ms_per_step=graph_ms, eager_ms_per_step=eager_ms, kernels={k: dict(mean_us=v[0] / max(v[1], 1) * 1e3,
                launches=v[1]) for k, v in kern.items()}, decode_kernels=per,
                roofline=dict(bound="hbm", kernel=dom, achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
-                             frac=achieved / HBM_PEAK_GBS, traffic=None, bytes_per_launch=nb[dom],
-                             mean_launch_us=per[dom]["mean_us"]),
+                             frac=achieved / HBM_PEAK_GBS,
+                             traffic=(TRAFFIC_BYTES[dom] if kernel_source_hash() == TRAFFIC_SOURCE_HASH
+                                      else None),
+                             traffic_unit="HBM bytes per launch",
+                             bytes_per_launch=nb[dom], mean_launch_us=per[dom]["mean_us"]),
                layer_bytes=nb["total"], layer_gbs=nb["total"] / (graph_ms * 1e-3) / 1e9)
     res["layer_hbm_frac"] = res["layer_gbs"] / HBM_PEAK_GBS
     del layers, g
