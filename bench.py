@@ -340,7 +340,9 @@ def main():
                       "frac": dec["layer_hbm_frac"]},
         "eager_ms_per_step": dec["eager_ms_per_step"],
         "kernels_us": {k: round(v["mean_us"], 2) for k, v in dec["kernels"].items()},
-        "prefill": None if pre is None else {k: pre[k] for k in ("workload", "tok_s", "ms", "tflops", "mfma_frac")},
+        "prefill": None if pre is None else dict(
+            {k: pre[k] for k in ("workload", "tok_s", "ms", "tflops", "mfma_frac")},
+            kernels_us={k: round(v["mean_us"], 2) for k, v in pre["kernels"].items()}),
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -40,7 +40,7 @@ WsLayout ws_layout(const ds4moe_layer& L, int64_t T, int mode) {
   y.ndist = take(4);
   y.distinct = take(E * 4);
   y.tok_slot = take(dmax * kDecodeGroup * 4);
-  y.tiles = take(((S + 15) / 16 + E) * 2 * 4);
+  y.tiles = take(((S + kPrefillTile - 1) / kPrefillTile + E) * 2 * 4);
   y.ntiles = take(4);
   const int64_t Tdec = std::min<int64_t>(Tg, kDecodeGroup);
   y.plog = take((d / 128) * Tdec * E * 4);  // one partial per 256 (routing only) or 128 inputs (forward)
@@ -214,7 +214,9 @@ int ds4moe_forward_prefill(const ds4moe_layer* L, const void* x, int x_dtype, in
                            void* stream) {
   int rc = check_layer(L);
   if (rc) return rc;
-  if (T > 65535 * 16 / 2 || (T * L->top_k + 15) / 16 + L->n_experts > 65535) return DS4MOE_ESHAPE;
+  if (T > 65535 * 16 / 2) return DS4MOE_ESHAPE;  // 16-token groups along a grid's y dimension
+  // the grouped products address activations and h with 32-bit byte offsets
+  if (T * L->d_model >= (int64_t)1 << 31 || T * L->top_k * L->d_ff >= (int64_t)1 << 31) return DS4MOE_ESHAPE;
   if ((rc = check_io(x, x_dtype, T, ws, ws_bytes, ws_layout(*L, T, DS4MOE_MODE_PREFILL).total))) return rc;
   if (!y) return DS4MOE_EINVAL;
   if (!al16(y)) return DS4MOE_EALIGN;

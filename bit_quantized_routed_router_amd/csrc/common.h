@@ -254,6 +254,11 @@ __device__ inline half8_t zero_half8() {
   return as_half8(z);
 }
 
+// Keeps the scheduler from moving instructions across it: load phases are
+// issued in program order, so a wait for an early phase never waits for the
+// weight stream behind it (loads retire in issue order).
+__device__ inline void pin() { __builtin_amdgcn_sched_barrier(0); }
+
 __device__ inline float silu(float g) { return g / (1.0f + __expf(-g)); }
 
 }  // namespace ds4

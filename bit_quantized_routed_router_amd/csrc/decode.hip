@@ -91,11 +91,6 @@ __device__ inline float4_t reduce_waves(float4_t v, float4_t (*red)[64], int wav
 // of consecutive tokens across LDS banks.
 __host__ __device__ inline int stage_stride(int K) { return K + 8; }
 
-// Keeps the scheduler from moving instructions across it: the load phases
-// below are issued in program order, so a wait for an early phase never
-// waits for the weight stream behind it (loads retire in issue order).
-__device__ inline void pin() { __builtin_amdgcn_sched_barrier(0); }
-
 // LDS staging of a small row set in two steps: load() issues up to M
 // 16-byte pieces per thread into registers, store() writes them to LDS
 // later.  The callers' launch conditions keep the row set within M pieces

@@ -13,6 +13,7 @@ constexpr int kDecodeGroup = 16;  // tokens per decode group (one MFMA column ti
 constexpr int kMaxDim = 16384;
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 16;
+constexpr int kPrefillTile = 128;  // slots per prefill work tile (one expert)
 
 // Byte offsets of the workspace regions (each 256-byte aligned).
 struct WsLayout {

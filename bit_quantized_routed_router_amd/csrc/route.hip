@@ -186,7 +186,8 @@ __global__ __launch_bounds__(256) void k_count_experts(const int32_t* __restrict
 }
 
 // prefill grouping, pass 2: offsets, perm, inv, and the GEMM work list of
-// (expert, group of 16 tokens) tiles (one block per expert).
+// (expert, run of up to kPrefillTile of its slots) tiles (one block per
+// expert).
 __global__ __launch_bounds__(256) void k_scatter_experts(const int32_t* __restrict__ idx, int64_t T, int k, int E,
                                                          const int32_t* __restrict__ counts,
                                                          int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
@@ -199,7 +200,7 @@ __global__ __launch_bounds__(256) void k_scatter_experts(const int32_t* __restri
   for (int u = threadIdx.x; u < E; u += blockDim.x) {
     if (u < e) {
       a += counts[u];
-      b += (counts[u] + 15) / 16;
+      b += (counts[u] + kPrefillTile - 1) / kPrefillTile;
     }
   }
   int off, tstart;
@@ -213,10 +214,10 @@ __global__ __launch_bounds__(256) void k_scatter_experts(const int32_t* __restri
     if (e == E - 1) {
       offsets[E] = off + cnt;
       if (offsets_out) offsets_out[E] = off + cnt;
-      *ntiles = tstart + (cnt + 15) / 16;
+      *ntiles = tstart + (cnt + kPrefillTile - 1) / kPrefillTile;
     }
   }
-  for (int g = threadIdx.x; g < (cnt + 15) / 16; g += blockDim.x) {
+  for (int g = threadIdx.x; g < (cnt + kPrefillTile - 1) / kPrefillTile; g += blockDim.x) {
     tiles[2 * (tstart + g)] = e;
     tiles[2 * (tstart + g) + 1] = g;
   }

@@ -155,8 +155,12 @@ int ds4moe_forward_decode(const ds4moe_layer *L, const void *x, int x_dtype, int
                           int32_t *topk_idx_out, float *topk_w_out, void *ws, size_t ws_bytes,
                           void *stream);
 
-/* Full layer for any T >= 1 (prefill chunk; grouped GEMMs).  Same outputs
- * as ds4moe_forward_decode plus the optional permutation perm_out [T*k]. */
+/* Full layer for 1 <= T <= 524280 tokens (prefill chunk; grouped GEMMs),
+ * with T * d_model < 2^31 and T * k * d_ff < 2^31 (DS4MOE_ESHAPE otherwise).
+ * Same outputs as ds4moe_forward_decode plus the optional permutation
+ * perm_out [T*k].  The routed products round each dequantized weight to
+ * binary16 (block scales folded in), so weights must stay within binary16
+ * range; the decode entry point applies the block scales in fp32. */
 int ds4moe_forward_prefill(const ds4moe_layer *L, const void *x, int x_dtype, int64_t T, float *y,
                            int32_t *topk_idx_out, float *topk_w_out, int32_t *perm_out, void *ws,
                            size_t ws_bytes, void *stream);
