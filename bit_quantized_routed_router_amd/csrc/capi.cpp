@@ -41,7 +41,8 @@ WsLayout ws_layout(const ds4moe_layer& L, int64_t T, int mode) {
   y.distinct = take(E * 4);
   y.tok_slot = take(dmax * kDecodeGroup * 4);
   y.tiles = take(((S + kPrefillTile - 1) / kPrefillTile + E) * 2 * 4);
-  y.ntiles = take(4);
+  y.stiles = take(E * 2 * 4);
+  y.ntiles = take(2 * 4);
   const int64_t Tdec = std::min<int64_t>(Tg, kDecodeGroup);
   y.plog = take((d / 128) * Tdec * E * 4);  // one partial per 256 (routing only) or 128 inputs (forward)
   if (mode != DS4MOE_MODE_ROUTE) {  // expert buffers (not needed for routing alone)

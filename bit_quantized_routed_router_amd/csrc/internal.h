@@ -14,13 +14,21 @@ constexpr int kMaxDim = 16384;
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 16;
 constexpr int kPrefillTile = 128;  // slots per prefill work tile (one expert)
+constexpr int kSmallTile = 32;     // tiles of at most this many slots go to the small-tile list
+// Prefill work tiles of an expert with n slots: runs of kPrefillTile; the
+// remainder is a small tile when it holds at most kSmallTile slots.
+__host__ __device__ inline int big_tiles(int n) { return n / kPrefillTile + (n % kPrefillTile > kSmallTile ? 1 : 0); }
+__host__ __device__ inline int small_tiles(int n) {
+  const int r = n % kPrefillTile;
+  return r > 0 && r <= kSmallTile ? 1 : 0;
+}
 
 // Byte offsets of the workspace regions (each 256-byte aligned).
 struct WsLayout {
   size_t x_hi, x_lo, logits, topk_idx, topk_w, counts, offsets, perm, inv;
   size_t ndist, distinct, tok_slot;  // decode: distinct experts and their token slots
   size_t hs16, hw16, hsum, yp;        // activations between the kernels
-  size_t tiles, ntiles;               // prefill: (expert, token group) work list
+  size_t tiles, stiles, ntiles;       // prefill: (expert, run) work lists of large and small tiles, their counts
   size_t plog;                        // decode: partial router logits [d/128][Tg][E]
   size_t ctrl;                        // decode: arrival counters (see ctrl_ints)
   size_t gu_part, ys;                 // decode: shared-expert gate/up half-K partial tiles, shared-expert output

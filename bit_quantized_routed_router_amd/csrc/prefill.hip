@@ -2,16 +2,16 @@
 // run of up to 128 of its slots) tiles built by the grouping kernels, plus
 // the dense shared expert.
 //
-//   k_shared_gateup_prefill   hs16[t]  = silu(Wsg x_t) * (Wsu x_t)        (binary16)
-//   k_pf_gateup               hw16[p]  = w_s * silu(G_e x_t) * (U_e x_t)  (binary16)
-//   k_pf_down                 yp[s]    = D_e hw16[p]                       (fp32)
-//   k_shared_down_prefill     y[t]     = Wsd hs16[t]                       (fp32)
-//   k_combine                 y[t]    += sum_j yp[t*k + j], j ascending
+//   k_pf_gateup<DENSE>   hs16[t] = silu(Wsg x_t) * (Wsu x_t)          (binary16)
+//   k_pf_gateup          hw16[p] = w_s * silu(G_e x_t) * (U_e x_t)    (binary16)
+//   k_pf_down            yp[s]   = D_e hw16[p]                         (fp32)
+//   k_pf_down<DENSE>     y[t]    = Wsd hs16[t]                         (fp32)
+//   k_combine            y[t]   += sum_j yp[t*k + j], j ascending
 // Slots s = t*k + j sit at position p of the expert-sorted list (perm[p] = s).
 // The combine order is fixed, so results are deterministic.
 //
-// Routed products (grouped GEMM).  A block takes one work tile and a slice
-// of output rows.  Each of its four waves owns four 16-row weight fragments
+// Grouped GEMM.  A block takes one work tile (a routed expert's run of up to
+// 128 slots, or 128 tokens of the shared expert) and a slice of output rows.  Each of its four waves owns four 16-row weight fragments
 // and all of the tile's slots (up to eight 16-slot fragments), so a weight is
 // decoded once per tile and a staged activation fragment feeds four MFMAs
 // (v_mfma_f32_16x16x32_f16 with the slots as A rows and the weights as B
@@ -22,55 +22,43 @@
 // K-steps are permuted so that a lane's weight codes for the whole chunk are
 // one 8-byte piece of its row (CB2: one sub-block; Q2K: two sub-blocks): at
 // step j lane group q covers inputs 32q + 8j .. +7 of the chunk, and the
-// activation fragments are read at the same offsets.  Weights are decoded to
-// binary16 with the block scales folded in (one rounding of d*(2s+1) and one
-// of the product, CB2; d*s*q - dmin*m rounded once, Q2K); the fp32 MFMA
-// accumulates.  Work items are laid out so that each XCD takes a contiguous
+// activation fragments are read at the same offsets.  Routed weights are
+// decoded to binary16 with the block scales folded in (CB2: d*(2s+1) rounded
+// to binary16, then its product with sign*m; Q2K: d*s and dmin*m rounded to
+// binary16, then q*(d*s) - dmin*m rounded once); F16 weights are used as
+// stored.  The MFMA accumulates in fp32.  Work items are laid out so that each XCD takes a contiguous
 // range (blocks are dealt to the 8 XCDs round-robin): the row slices of one
 // tile and the tiles of one expert share that XCD's L2.
 #include <algorithm>
 
 #include "common.h"
 #include "internal.h"
-#include "trace.h"
 #include "tiles.h"
+#include "trace.h"
 
 namespace ds4 {
 
 __constant__ GridTables c_pre_tables = make_grid_tables();
 
-constexpr int kPW = 4;  // waves per block, splitting K
 
-template <bool LO>
-__global__ __launch_bounds__(kPW * 64) void k_shared_gateup_prefill(ds4moe_layer L, int64_t T,
-                                                                    const _Float16* __restrict__ xh,
-                                                                    const _Float16* __restrict__ xl,
-                                                                    _Float16* __restrict__ hs16) {
-  __shared__ float s_red[kPW * 64 * 4];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int c = lane & 15, q = lane >> 4;
-  const int d = L.d_model, fs = L.d_ff_shared;
-  const int row0 = blockIdx.x * 16;
-  const int64_t t = (int64_t)blockIdx.y * 16 + c;
-  const _Float16* bh = t < T ? xh + t * d : nullptr;
-  const _Float16* bl = (LO && t < T) ? xl + t * d : nullptr;
-  int ks0, ks1;
-  split_range(d / 32, kPW, wave, ks0, ks1);
-  float4_t ag = {0.f, 0.f, 0.f, 0.f}, au = ag;
-  const int64_t ar = (int64_t)(row0 + c) * d;
-  f16_tile<true, LO>(L.sh_gate + ar, L.sh_up + ar, bh, bl, ks0, ks1, lane, ag, au);
-  ag = block_reduce_waves<kPW>(ag, s_red, wave, lane);
-  au = block_reduce_waves<kPW>(au, s_red, wave, lane);
-  if (wave == 0 && t < T) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) hs16[t * fs + row0 + 4 * q + r] = (_Float16)(silu(ag[r]) * au[r]);
-  }
-}
 
 constexpr int kTT = kPrefillTile;  // slots per work tile (128)
 constexpr int kKC = 128;           // inputs per staged activation chunk
 constexpr int kGW = 4;             // waves per block
-constexpr int kChunk = kTT * kKC;  // halves per staged chunk (32 KB)
+constexpr int kChunk = kTT * kKC;  // halves per staged chunk of 128 rows (32 KB)
+// Halves of a block's activation ring: 64 KB for tiles of up to 128 slots,
+// 32 KB for small tiles (<= 32 slots).
+constexpr int ring_halves(bool small) { return small ? kChunk : 2 * kChunk; }
+
+// Ring slots of a tile: as many as the activation ring holds (R * 16 NF
+// rows of 128 inputs) and the 6-bit load counter can track (R - 1 batches of
+// `loads` vector-memory instructions in flight, <= 63), at most 6.
+// Small tiles have little work per chunk, so they need the deepest prefetch.
+constexpr int ring_depth(int nf, int loads, bool lo, int ring, int rmax = 6) {
+  int r = lo ? 2 : rmax;
+  while (r > 2 && (r * nf * 16 * kKC > ring || (r - 1) * loads > 63)) --r;
+  return r;
+}
 
 // Work item of this block: blocks b < count are spread so that XCD x = b % 8
 // runs items [start_x, start_x + quota_x) in order; blocks >= count exit.
@@ -90,17 +78,64 @@ __device__ inline void vm_wait() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-// One 128-input chunk of the tile's 128 activation rows into a swizzled LDS
-// buffer: wave instruction m moves rows 4g .. 4g+3 (g = wave + 4m), lane l
+// Workgroup barrier for the chunk loop.  __syncthreads() carries a release
+// fence, and the compiler meets it by waiting for every outstanding load --
+// LDS-bound copies count as LDS stores -- which would drain the whole
+// prefetch ring.  Here the loop orders memory itself: a wave has waited for
+// its own copies into the slot it is about to read before this barrier, and
+// its reads of a slot have returned (lgkmcnt) before the barrier after which
+// that slot is refilled.  The memory clobber keeps the compiler from moving
+// LDS accesses across it.
+__device__ inline void ring_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// The chunk loop of a tile with R chunks in flight and one barrier per
+// chunk.  issue(ch, u) starts loading chunk ch into ring slot u (B
+// vector-memory instructions per lane); compute(u) consumes slot u.  At each
+// step the wave waits for its copies of the chunk it is about to use, the
+// barrier makes everyone's copies visible and shows that all waves are done
+// with the previous chunk, whose slot is then refilled with the chunk R - 1
+// ahead before computing.  Every step issues a batch -- past the last chunk
+// it repeats the last one (cache hits, never read) -- so the loop has one
+// shape and the compiler's own waits for the weight registers stay partial.
+// Passes of R chunks run unrolled (static slot indices); steps past the last
+// chunk keep the waits and issues and skip the compute.  The final wait
+// drains every load before the block's LDS can be reused.
+template <int R, int B, typename Issue, typename Compute>
+__device__ __attribute__((always_inline)) inline void ring_loop(int nch, Issue issue, Compute compute) {
+  static_assert(R >= 2 && (R - 1) * B <= 63, "ring depth");
+#pragma unroll
+  for (int u = 0; u < R - 1; ++u) issue(min(u, nch - 1), u);
+  auto step = [&](int ch, int u) {
+    pin();
+    vm_wait<(R - 2) * B>();
+    ring_barrier();
+    pin();
+    issue(min(ch + R - 1, nch - 1), (u + R - 1) % R);
+    pin();
+    if (ch < nch) compute(u);
+  };
+  for (int ch0 = 0; ch0 < nch; ch0 += R) {
+#pragma unroll
+    for (int u = 0; u < R; ++u) step(ch0 + u, u);
+  }
+  vm_wait<0>();
+}
+
+// Copy instructions per wave and chunk for 16 NF rows (4 NF groups of 4 rows)
+// over NW waves; every wave issues the same number.
+constexpr int dma_per_wave(int nf, int nw) { return (4 * nf + nw - 1) / nw; }
+
+// One 128-input chunk of the tile's first 16 NF activation rows into a
+// swizzled LDS buffer: wave instruction m moves rows 4g .. 4g+3 (g = wave + NW m), lane l
 // writing physical piece l & 15 of row 4g + l/16, which holds logical piece
 // (l & 15) ^ (row & 15).  row_of(r): element offset of tile row r from src
 // (src is the same for the whole block, offsets fit 32 bits).
-template <bool LO, typename RowOf>
+template <bool LO, int NF, int NW, typename RowOf>
 __device__ inline void stage_rows(const _Float16* __restrict__ src, const _Float16* __restrict__ src_lo, RowOf row_of,
                                   int ch, _Float16* dh, _Float16* dl, int wave, int lane) {
 #pragma unroll
-  for (int m = 0; m < 8; ++m) {
-    const int g = wave + kGW * m;
+  for (int m = 0; m < dma_per_wave(NF, NW); ++m) {  // 4 NF groups of 4 rows dealt to NW waves
+    const int g = min(wave + NW * m, 4 * NF - 1);   // a spare slot repeats the last group (same bytes)
     const int r = 4 * g + (lane >> 4);
     const int u = (lane & 15) ^ (r & 15);
     const uint32_t off = 2u * ((uint32_t)row_of(r) + (uint32_t)(ch * kKC + 8 * u));
@@ -123,13 +158,15 @@ __device__ inline half8_t slot_frag(const _Float16* buf, int i, int c, int q, in
 }
 
 // CB2 group j of a sub-block (index word idxw, aux word aux) as binary16
-// sign * m * D, with D = binary16(d * (2s+1)) in both halves of D2.
+// sign * m * D, with D = binary16(d * (2s+1)) in both halves of D2.  mag/sgn
+// point at this lane's copy of the tables, whose entries are TC copies apart.
+template <int TC>
 __device__ inline half8_t cb2_frag_scaled(uint32_t idxw, uint32_t aux, int j, const uint32_t* mag,
                                           const uint32_t* sgn, half2_t D2) {
   const uint32_t idx = (idxw >> (8 * j)) & 0xFFu;
   const uint32_t code = (aux >> (7 * j)) & 0x7Fu;
-  const u32x4_t m = *(const u32x4_t*)(mag + 4 * idx);
-  const u32x4_t s = *(const u32x4_t*)(sgn + 4 * code);
+  const u32x4_t m = *(const u32x4_t*)(mag + 4 * TC * idx);
+  const u32x4_t s = *(const u32x4_t*)(sgn + 4 * TC * code);
   u32x4_t r;
   r.x = as_u32(as_half2(m.x ^ s.x) * D2);
   r.y = as_u32(as_half2(m.y ^ s.y) * D2);
@@ -144,40 +181,71 @@ __device__ inline half2_t h2splat(float v) {
   return (half2_t){h, h};
 }
 
-template <bool LO>
+// Codebook tables in LDS: TC interleaved copies of each 16-byte entry, lane l
+// reading copy l % TC.  A 16-byte read serves 8 lanes per LDS cycle, so with
+// TC = 8 those lanes always hit 8 different 16-byte bank groups whatever
+// entries they look up (one copy, random indices: about 2-way conflicts).
+template <int TC>
+struct CbTables {
+  uint32_t mag[256 * TC * 4];
+  uint32_t sgn[128 * TC * 4];
+  __device__ inline void stage(const GridTables& t) {
+    for (int i = threadIdx.x; i < 256 * TC * 4; i += blockDim.x) mag[i] = t.mag[i / (TC * 4)][i % 4];
+    for (int i = threadIdx.x; i < 128 * TC * 4; i += blockDim.x) sgn[i] = t.sgn[i / (TC * 4)][i % 4];
+  }
+};
+
+template <bool LO, int TC, int RING>
 struct GuLds {
-  _Float16 xh[2][kChunk];
-  _Float16 xl[LO ? 2 : 1][LO ? kChunk : 8];
-  uint32_t mag[256 * 4];
-  uint32_t sgn[128 * 4];
+  _Float16 xh[RING];
+  _Float16 xl[LO ? RING : 8];
+  CbTables<TC> tab;
   int tok[kTT];
   float w[kTT];
 };
 
-// Gate/up of one work tile for a 128-row slice of h, NF slot fragments.
-template <bool LO, int NF>
-__device__ __attribute__((always_inline)) inline void gateup_tile(const ds4moe_layer& L, GuLds<LO>& s,
+// Weights of one 128-input chunk for a lane's four fragments.  CB2: the lane's sub-block (8 bytes) and its block's d; F16:
+// the lane's 4 x 8 binary16 values (inputs 32q .. 32q+31 of the chunk).
+template <bool F16>
+struct GuW {
+  u32x2_t cw[4];
+  uint32_t dv[4];
+  u32x4_t wv[F16 ? 4 : 1][F16 ? 4 : 1];
+  static constexpr int kLoads = F16 ? 16 : 8;
+};
+
+// Gate/up of one work tile (up to 128 slots) for a 128-row slice of h, NF
+// slot fragments.  DENSE: the shared expert (F16 weights, weight 1, rows are
+// tokens); otherwise routed expert e (CB2 weights, routing weights s.w).
+template <bool LO, bool DENSE, int NW, int TC, int RING, int NF>
+__device__ __attribute__((always_inline)) inline void gateup_tile(const ds4moe_layer& L, GuLds<LO, TC, RING>& s,
                                                                   const _Float16* __restrict__ xh,
                                                                   const _Float16* __restrict__ xl, int e, int rt,
-                                                                  int pos0, int n, _Float16* __restrict__ hw16) {
+                                                                  int pos0, int n, _Float16* __restrict__ hout) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, c = lane & 15, q = lane >> 4;
-  const int d = L.d_model, fd = L.d_ff, nb = d / QK, nch = d / kKC;
+  const int d = L.d_model, fd = DENSE ? L.d_ff_shared : L.d_ff, nb = d / QK, nch = d / kKC;
   const size_t mb = (size_t)fd * nb;
-  const uint8_t* gb = (const uint8_t*)L.gate + (size_t)e * mb * 66;
-  const uint8_t* ub = (const uint8_t*)L.up + (size_t)e * mb * 66;
-  const int hr0 = rt * 128 + 32 * wave;
-  // fragment f: rows hr0 + 16 (f & 1) + c of gate (f < 2) or up (f >= 2)
+  const uint8_t* gb = DENSE ? (const uint8_t*)L.sh_gate : (const uint8_t*)L.gate + (size_t)e * mb * 66;
+  const uint8_t* ub = DENSE ? (const uint8_t*)L.sh_up : (const uint8_t*)L.up + (size_t)e * mb * 66;
   const uint8_t* gd = gb + mb * 64;
   const uint8_t* ud = ub + mb * 64;
-  uint32_t rowblk[2];
+  const int hr0 = rt * 32 * NW + 32 * wave;
+  // fragment f: rows hr0 + 16 (f & 1) + c of gate (f < 2) or up (f >= 2)
+  uint32_t rowu[2];
 #pragma unroll
-  for (int h = 0; h < 2; ++h) rowblk[h] = (uint32_t)((hr0 + 16 * h + c) * nb);
-  auto load_w = [&](int ch, u32x2_t (&cw)[4], uint32_t (&dv)[4]) {
+  for (int h = 0; h < 2; ++h) rowu[h] = (uint32_t)((hr0 + 16 * h + c) * (DENSE ? d : nb));
+  auto load_w = [&](int ch, GuW<DENSE>& W) {
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
-      const uint32_t blk = rowblk[f & 1] + (uint32_t)(ch >> 1);
-      cw[f] = ld_at<u32x2_t>(f < 2 ? gb : ub, blk * 64u + (uint32_t)(32 * (ch & 1) + 8 * q));
-      dv[f] = ld_at<uint16_t>(f < 2 ? gd : ud, blk * 2u);
+      if constexpr (DENSE) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          W.wv[f][j] = ld_at<u32x4_t>(f < 2 ? gb : ub, 2u * (rowu[f & 1] + (uint32_t)(ch * kKC + 32 * q + 8 * j)));
+      } else {
+        const uint32_t blk = rowu[f & 1] + (uint32_t)(ch >> 1);
+        W.cw[f] = ld_at<u32x2_t>(f < 2 ? gb : ub, blk * 64u + (uint32_t)(32 * (ch & 1) + 8 * q));
+        W.dv[f] = ld_at<uint16_t>(f < 2 ? gd : ud, blk * 2u);
+      }
     }
   };
   auto rows = [&](int r) { return s.tok[r] * d; };
@@ -187,33 +255,34 @@ __device__ __attribute__((always_inline)) inline void gateup_tile(const ds4moe_l
 #pragma unroll
     for (int i = 0; i < NF; ++i) acc[f][i] = (float4_t){0.f, 0.f, 0.f, 0.f};
 
-  constexpr int kBatch = 8 * (LO ? 2 : 1) + 8;  // vector-memory instructions per chunk and lane
-  u32x2_t cw[4], cwn[4];
-  uint32_t dv[4], dvn[4];
-  stage_rows<LO>(xh, xl, rows, 0, s.xh[0], s.xl[0], wave, lane);
-  load_w(0, cw, dv);
-  for (int ch = 0; ch < nch; ++ch) {
-    const int buf = ch & 1;
-    if (ch + 1 < nch) {
-      pin();
-      stage_rows<LO>(xh, xl, rows, ch + 1, s.xh[buf ^ 1], s.xl[LO ? buf ^ 1 : 0], wave, lane);
-      load_w(ch + 1, cwn, dvn);
-      pin();
-      vm_wait<kBatch>();
-    } else {
-      vm_wait<0>();
-    }
-    __syncthreads();
+  constexpr int kBatch = dma_per_wave(NF, NW) * (LO ? 2 : 1) + GuW<DENSE>::kLoads;  // per chunk and lane
+  constexpr int R = ring_depth(NF, kBatch, LO, RING);
+  constexpr int kSlot = NF * 16 * kKC;  // halves per ring slot
+  static_assert(R * kSlot <= RING, "ring slots exceed the staging buffer");
+  GuW<DENSE> W[R];
+  auto issue = [&](int ch, int u) {
+    stage_rows<LO, NF, NW>(xh, xl, rows, ch, s.xh + u * kSlot, s.xl + (LO ? u * kSlot : 0), wave, lane);
+    load_w(ch, W[u]);
+  };
+  const uint32_t* tmag = s.tab.mag + 4 * (lane % TC);
+  const uint32_t* tsgn = s.tab.sgn + 4 * (lane % TC);
+  auto compute = [&](int u) {
     half2_t D2[4];
+    if constexpr (!DENSE) {
 #pragma unroll
-    for (int f = 0; f < 4; ++f) D2[f] = h2splat(f16f(dv[f]) * (float)(2 * (cw[f].y >> 28) + 1));
-    const _Float16* bh = s.xh[buf];
-    const _Float16* bl = s.xl[LO ? buf : 0];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
+      for (int f = 0; f < 4; ++f) D2[f] = h2splat(f16f(W[u].dv[f]) * (float)(2 * (W[u].cw[f].y >> 28) + 1));
+    }
+    const _Float16* bh = s.xh + u * kSlot;
+    const _Float16* bl = s.xl + (LO ? u * kSlot : 0);
+    auto step = [&](int j) {
       half8_t wf[4];
 #pragma unroll
-      for (int f = 0; f < 4; ++f) wf[f] = cb2_frag_scaled(cw[f].x, cw[f].y, j, s.mag, s.sgn, D2[f]);
+      for (int f = 0; f < 4; ++f) {
+        if constexpr (DENSE)
+          wf[f] = as_half8(W[u].wv[f][j]);
+        else
+          wf[f] = cb2_frag_scaled<TC>(W[u].cw[f].x, W[u].cw[f].y, j, tmag, tsgn, D2[f]);
+      }
 #pragma unroll
       for (int i = 0; i < NF; ++i) {
         const half8_t a = slot_frag(bh, i, c, q, j);
@@ -225,93 +294,153 @@ __device__ __attribute__((always_inline)) inline void gateup_tile(const ds4moe_l
           for (int f = 0; f < 4; ++f) acc[f][i] = mfma16x16x32(al, wf[f], acc[f][i]);
         }
       }
-    }
-    __syncthreads();
-    if (ch + 1 < nch) {
+    };
 #pragma unroll
-      for (int f = 0; f < 4; ++f) {
-        cw[f] = cwn[f];
-        dv[f] = dvn[f];
-      }
-    }
-  }
+    for (int j = 0; j < 4; ++j) step(j);
+  };
+  ring_loop<R, kBatch>(nch, issue, compute);
 #pragma unroll
   for (int i = 0; i < NF; ++i) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int t = 16 * i + 4 * q + r;
       if (t < n) {
-        const float wt = s.w[t];
+        const float wt = DENSE ? 1.0f : s.w[t];
 #pragma unroll
         for (int h = 0; h < 2; ++h)
-          hw16[(int64_t)(pos0 + t) * fd + hr0 + 16 * h + c] =
+          hout[(int64_t)(pos0 + t) * fd + hr0 + 16 * h + c] =
               (_Float16)(wt * (silu(acc[h][i][r]) * acc[h + 2][i][r]));
       }
     }
   }
 }
 
-template <bool LO>
-__global__ __launch_bounds__(kGW * 64) __attribute__((amdgpu_waves_per_eu(2))) void k_pf_gateup(
-    ds4moe_layer L, const _Float16* __restrict__ xh, const _Float16* __restrict__ xl,
-    const int32_t* __restrict__ tiles, const int32_t* __restrict__ ntiles, const int32_t* __restrict__ counts,
-    const int32_t* __restrict__ offsets, const int32_t* __restrict__ perm, const float* __restrict__ topk_w,
-    _Float16* __restrict__ hw16) {
-  __shared__ GuLds<LO> s;
-  const int rowtiles = L.d_ff / 128;
+// Routed: item -> (work tile, row slice).  Dense: item -> (128 tokens, row
+// slice).  Returns false for blocks without work.
+template <bool DENSE, bool SMALL>
+__device__ inline bool tile_of(int rowtiles, int64_t T, const int32_t* big, const int32_t* small,
+                               const int32_t* ntiles, const int32_t* counts, const int32_t* offsets, int& e, int& rt,
+                               int& pos0, int& n) {
+  const int32_t* tiles = SMALL ? small : big;
+  const int ntile = DENSE ? (int)((T + kTT - 1) / kTT) : ntiles[SMALL ? 1 : 0];
   int item;
-  if (!xcd_item(*ntiles * rowtiles, item)) return;
-  const int tile = item / rowtiles, rt = item - tile * rowtiles;
-  const int e = tiles[2 * tile], g = tiles[2 * tile + 1];
-  const int pos0 = offsets[e] + kTT * g;
-  const int n = min(kTT, counts[e] - kTT * g);
-  stage_grid_tables(s.mag, s.sgn, c_pre_tables);
-  if ((int)threadIdx.x < kTT) {
-    const int slot = perm[pos0 + min((int)threadIdx.x, n - 1)];
-    s.tok[threadIdx.x] = slot / L.top_k;
-    s.w[threadIdx.x] = topk_w[slot];
+  if (!xcd_item(ntile * rowtiles, item)) return false;
+  const int tile = item / rowtiles;
+  rt = item - tile * rowtiles;
+  if (DENSE) {
+    e = -1;
+    pos0 = tile * kTT;
+    n = (int)min((int64_t)kTT, T - pos0);
+  } else {
+    e = tiles[2 * tile];
+    const int g = tiles[2 * tile + 1];
+    pos0 = offsets[e] + kTT * g;
+    n = min(kTT, counts[e] - kTT * g);
   }
-  __syncthreads();
-  switch ((n + 15) >> 4) {
-    case 1: gateup_tile<LO, 1>(L, s, xh, xl, e, rt, pos0, n, hw16); break;
-    case 2: gateup_tile<LO, 2>(L, s, xh, xl, e, rt, pos0, n, hw16); break;
-    case 3: gateup_tile<LO, 3>(L, s, xh, xl, e, rt, pos0, n, hw16); break;
-    case 4: gateup_tile<LO, 4>(L, s, xh, xl, e, rt, pos0, n, hw16); break;
-    case 5: gateup_tile<LO, 5>(L, s, xh, xl, e, rt, pos0, n, hw16); break;
-    case 6: gateup_tile<LO, 6>(L, s, xh, xl, e, rt, pos0, n, hw16); break;
-    case 7: gateup_tile<LO, 7>(L, s, xh, xl, e, rt, pos0, n, hw16); break;
-    default: gateup_tile<LO, 8>(L, s, xh, xl, e, rt, pos0, n, hw16); break;
-  }
+  return true;
 }
 
+// Slot fragments of a tile with n slots: small-tile kernels see 1-2, large
+// ones 3-8, the shared expert's any.
+#define DS4_NF_SWITCH(n, SMALL, DENSE, CALL)                  \
+  switch (((n) + 15) >> 4) {                                  \
+    case 1: if constexpr (SMALL || DENSE) CALL(1); break;     \
+    case 2: if constexpr (SMALL || DENSE) CALL(2); break;     \
+    case 3: if constexpr (!SMALL) CALL(3); break;             \
+    case 4: if constexpr (!SMALL) CALL(4); break;             \
+    case 5: if constexpr (!SMALL) CALL(5); break;             \
+    case 6: if constexpr (!SMALL) CALL(6); break;             \
+    case 7: if constexpr (!SMALL) CALL(7); break;             \
+    default: if constexpr (!SMALL) CALL(8); break;            \
+  }
+
+// Routed gate/up (CB2) over the work list into hw16, or (DENSE) the shared
+// expert's gate/up (F16) over all T tokens into hs16.
+// Waves per gate/up block (each owns 32 rows of h) and codebook table copies.
+template <bool LO, bool DENSE>
+constexpr int gu_waves() { return 4; }
+template <bool LO, bool DENSE>
+constexpr int gu_copies() { return 1; }
+
+// SMALL: the small-tile list (at most 32 slots per tile, a smaller ring).
+template <bool LO, bool DENSE, bool SMALL>
+__global__ __launch_bounds__((gu_waves<LO, DENSE>() * 64))
+__attribute__((amdgpu_waves_per_eu(DENSE || LO ? 1 : 2))) void k_pf_gateup(
+    ds4moe_layer L, int64_t T, const _Float16* __restrict__ xh, const _Float16* __restrict__ xl,
+    const int32_t* __restrict__ tiles, const int32_t* __restrict__ stiles, const int32_t* __restrict__ ntiles,
+    const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets, const int32_t* __restrict__ perm,
+    const float* __restrict__ topk_w, _Float16* __restrict__ hout) {
+  constexpr int NW = gu_waves<LO, DENSE>(), TC = gu_copies<LO, DENSE>(), RING = ring_halves(SMALL);
+  __shared__ GuLds<LO, TC, RING> s;
+  int e, rt, pos0, n;
+  if (!tile_of<DENSE, SMALL>((DENSE ? L.d_ff_shared : L.d_ff) / (32 * NW), T, tiles, stiles, ntiles, counts, offsets,
+                             e, rt, pos0, n))
+    return;
+  if (!DENSE) s.tab.stage(c_pre_tables);
+  if ((int)threadIdx.x < kTT) {
+    const int r = min((int)threadIdx.x, n - 1);
+    if (DENSE) {
+      s.tok[threadIdx.x] = pos0 + r;
+    } else {
+      const int slot = perm[pos0 + r];
+      s.tok[threadIdx.x] = slot / L.top_k;
+      s.w[threadIdx.x] = topk_w[slot];
+    }
+  }
+  __syncthreads();
+#define DS4_GU(NF) gateup_tile<LO, DENSE, NW, TC, RING, NF>(L, s, xh, xl, e, rt, pos0, n, hout)
+  DS4_NF_SWITCH(n, SMALL, DENSE, DS4_GU)
+#undef DS4_GU
+}
+
+template <int RING>
 struct DnLds {
-  _Float16 xh[2][kChunk];
+  _Float16 xh[RING];
   int slot[kTT];
 };
 
-// Down product of one work tile for a 256-row slice of the output.
-template <int NF>
-__device__ __attribute__((always_inline)) inline void down_tile(const ds4moe_layer& L, DnLds& s,
-                                                                const _Float16* __restrict__ hw16, int e, int rt,
-                                                                int pos0, int n, float* __restrict__ yp) {
+// Down weights of one chunk.  Q2K: the lane's two sub-blocks of codes, the
+// aligned word holding their two scale bytes, the block's d/dmin; F16: 4 x 8
+// binary16 values per fragment.
+template <bool F16>
+struct DnW {
+  u32x2_t cw[4];
+  uint32_t sc[4], dd[4];
+  u32x4_t wv[F16 ? 4 : 1][F16 ? 4 : 1];
+  static constexpr int kLoads = F16 ? 16 : 12;
+};
+
+// Down product of one work tile for a 256-row slice of the output.  Routed
+// (Q2K): yp[slot] = D_e h.  DENSE (shared, F16): y[t] = Wsd hs16[t].
+template <bool DENSE, int RING, int NF>
+__device__ __attribute__((always_inline)) inline void down_tile(const ds4moe_layer& L, DnLds<RING>& s,
+                                                                const _Float16* __restrict__ hin, int e, int rt,
+                                                                int pos0, int n, float* __restrict__ yp,
+                                                                float* __restrict__ y) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, c = lane & 15, q = lane >> 4;
-  const int d = L.d_model, fd = L.d_ff, nb = fd / QK, nch = fd / kKC;
+  const int d = L.d_model, fd = DENSE ? L.d_ff_shared : L.d_ff, nb = fd / QK, nch = fd / kKC;
   const size_t mb = (size_t)d * nb;
-  const uint8_t* base = (const uint8_t*)L.down + (size_t)e * mb * 84;
+  const uint8_t* base = DENSE ? (const uint8_t*)L.sh_down : (const uint8_t*)L.down + (size_t)e * mb * 84;
   const uint8_t* sub = base + mb * 64;
   const uint8_t* sup = base + mb * 80;
   const int r0 = rt * 256 + 64 * wave;
-  const uint32_t blk0 = (uint32_t)((r0 + c) * nb);  // fragment f: + 16 f nb
-  auto load_w = [&](int ch, u32x2_t (&cw)[4], uint32_t (&sc)[4], uint32_t (&dd)[4]) {
+  const uint32_t row0 = (uint32_t)((r0 + c) * (DENSE ? fd : nb));  // fragment f: + 16 f (fd or nb)
+  auto load_w = [&](int ch, DnW<DENSE>& W) {
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
-      const uint32_t blk = blk0 + (uint32_t)(16 * f * nb + (ch >> 1));
-      cw[f] = ld_at<u32x2_t>(base, blk * 64u + (uint32_t)(32 * (ch & 1) + 8 * q));
-      sc[f] = ld_at<uint16_t>(sub, blk * 16u + (uint32_t)(8 * (ch & 1) + 2 * q));
-      dd[f] = ld_at<uint32_t>(sup, blk * 4u);
+      if constexpr (DENSE) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          W.wv[f][j] = ld_at<u32x4_t>(base, 2u * (row0 + (uint32_t)(16 * f * fd + ch * kKC + 32 * q + 8 * j)));
+      } else {
+        const uint32_t blk = row0 + (uint32_t)(16 * f * nb + (ch >> 1));
+        W.cw[f] = ld_at<u32x2_t>(base, blk * 64u + (uint32_t)(32 * (ch & 1) + 8 * q));
+        W.sc[f] = ld_at<uint32_t>(sub, blk * 16u + (uint32_t)(8 * (ch & 1) + 4 * (q >> 1)));
+        W.dd[f] = ld_at<uint32_t>(sup, blk * 4u);
+      }
     }
   };
-  const _Float16* hbase = hw16 + (int64_t)pos0 * fd;
+  const _Float16* hbase = hin + (int64_t)pos0 * fd;
   auto rows = [&](int r) { return min(r, n - 1) * fd; };
   float4_t acc[4][NF];
 #pragma unroll
@@ -319,48 +448,46 @@ __device__ __attribute__((always_inline)) inline void down_tile(const ds4moe_lay
 #pragma unroll
     for (int i = 0; i < NF; ++i) acc[f][i] = (float4_t){0.f, 0.f, 0.f, 0.f};
 
-  constexpr int kBatch = 8 + 12;
-  u32x2_t cw[4], cwn[4];
-  uint32_t sc[4], scn[4], dd[4], ddn[4];
-  stage_rows<false>(hbase, nullptr, rows, 0, s.xh[0], nullptr, wave, lane);
-  load_w(0, cw, sc, dd);
+  constexpr int kBatch = dma_per_wave(NF, kGW) + DnW<DENSE>::kLoads;
+  constexpr int R = ring_depth(NF, kBatch, false, RING, RING < 2 * kChunk ? 3 : 6);  // small: register budget
+  constexpr int kSlot = NF * 16 * kKC;
+  static_assert(R * kSlot <= RING, "ring slots exceed the staging buffer");
+  DnW<DENSE> W[R];
+  auto issue = [&](int ch, int u) {
+    stage_rows<false, NF, kGW>(hbase, nullptr, rows, ch, s.xh + u * kSlot, nullptr, wave, lane);
+    load_w(ch, W[u]);
+  };
   const half2_t k1024 = {(_Float16)-1024.0f, (_Float16)-1024.0f};
-  for (int ch = 0; ch < nch; ++ch) {
-    const int buf = ch & 1;
-    if (ch + 1 < nch) {
-      pin();
-      stage_rows<false>(hbase, nullptr, rows, ch + 1, s.xh[buf ^ 1], nullptr, wave, lane);
-      load_w(ch + 1, cwn, scn, ddn);
-      pin();
-      vm_wait<kBatch>();
-    } else {
-      vm_wait<0>();
-    }
-    __syncthreads();
-    const _Float16* bh = s.xh[buf];
+  auto compute = [&](int u) {
+    const _Float16* bh = s.xh + u * kSlot;
+    auto half_chunk = [&](int h) {  // Q2K: sub-block 2q + h of the chunk feeds steps 2h, 2h+1
+      half2_t A2[4], nB2[4];         // binary16 d * s and -(dmin * m) of the sub-block
+      if constexpr (!DENSE) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {  // sub-block 2q + h of the chunk: steps 2h, 2h+1
-      half2_t A2[4], nB2[4];  // binary16 d * s and -(dmin * m) of the sub-block
-#pragma unroll
-      for (int f = 0; f < 4; ++f) {
-        const uint32_t sm = (sc[f] >> (8 * h)) & 0xFFu;
-        A2[f] = h2splat(f16f(dd[f]) * (float)(sm & 15u));
-        nB2[f] = h2splat(-f16f(dd[f] >> 16) * (float)(sm >> 4));
+        for (int f = 0; f < 4; ++f) {
+          const uint32_t sm = (W[u].sc[f] >> (16 * (q & 1) + 8 * h)) & 0xFFu;
+          A2[f] = h2splat(f16f(W[u].dd[f]) * (float)(sm & 15u));
+          nB2[f] = h2splat(-f16f(W[u].dd[f] >> 16) * (float)(sm >> 4));
+        }
       }
 #pragma unroll
-      for (int jj = 0; jj < 2; ++jj) {  // codes 8jj .. 8jj+7 of the sub-block
+      for (int jj = 0; jj < 2; ++jj) {  // Q2K: codes 8jj .. 8jj+7 of the sub-block
         const int j = 2 * h + jj;
         half8_t wf[4];
 #pragma unroll
         for (int f = 0; f < 4; ++f) {
-          const uint32_t fld = (cw[f][h] >> (16 * jj)) & 0xFFFFu;
-          uint32_t pr[4];
-          q2k_pairs(fld | (fld << 14), pr);
-          u32x4_t a;
+          if constexpr (DENSE) {
+            wf[f] = as_half8(W[u].wv[f][j]);
+          } else {
+            const uint32_t fld = ((h ? W[u].cw[f].y : W[u].cw[f].x) >> (16 * jj)) & 0xFFFFu;
+            uint32_t pr[4];
+            q2k_pairs(fld | (fld << 14), pr);
+            u32x4_t a;
 #pragma unroll
-          for (int p = 0; p < 4; ++p)
-            a[p] = as_u32(__builtin_elementwise_fma(as_half2(pr[p]) + k1024, A2[f], nB2[f]));
-          wf[f] = as_half8(a);
+            for (int p = 0; p < 4; ++p)
+              a[p] = as_u32(__builtin_elementwise_fma(as_half2(pr[p]) + k1024, A2[f], nB2[f]));
+            wf[f] = as_half8(a);
+          }
         }
 #pragma unroll
         for (int i = 0; i < NF; ++i) {
@@ -369,79 +496,51 @@ __device__ __attribute__((always_inline)) inline void down_tile(const ds4moe_lay
           for (int f = 0; f < 4; ++f) acc[f][i] = mfma16x16x32(a, wf[f], acc[f][i]);
         }
       }
-    }
-    __syncthreads();
-    if (ch + 1 < nch) {
+    };
 #pragma unroll
-      for (int f = 0; f < 4; ++f) {
-        cw[f] = cwn[f];
-        sc[f] = scn[f];
-        dd[f] = ddn[f];
-      }
-    }
-  }
+    for (int h = 0; h < 2; ++h) half_chunk(h);
+  };
+  ring_loop<R, kBatch>(nch, issue, compute);
 #pragma unroll
   for (int i = 0; i < NF; ++i) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int t = 16 * i + 4 * q + r;
       if (t < n) {
-        const int64_t row = (int64_t)s.slot[t] * d;
+        if constexpr (DENSE) {
 #pragma unroll
-        for (int f = 0; f < 4; ++f) yp[row + r0 + 16 * f + c] = acc[f][i][r];
+          for (int f = 0; f < 4; ++f) y[(int64_t)(pos0 + t) * d + r0 + 16 * f + c] = acc[f][i][r];
+        } else {
+          const int64_t row = (int64_t)s.slot[t] * d;
+#pragma unroll
+          for (int f = 0; f < 4; ++f) yp[row + r0 + 16 * f + c] = acc[f][i][r];
+        }
       }
     }
   }
 }
 
-__global__ __launch_bounds__(kGW * 64) __attribute__((amdgpu_waves_per_eu(2))) void k_pf_down(
-    ds4moe_layer L, const int32_t* __restrict__ tiles, const int32_t* __restrict__ ntiles,
-    const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets, const int32_t* __restrict__ perm,
-    const _Float16* __restrict__ hw16, float* __restrict__ yp) {
-  __shared__ DnLds s;
-  const int rowtiles = L.d_model / 256;
-  int item;
-  if (!xcd_item(*ntiles * rowtiles, item)) return;
-  const int tile = item / rowtiles, rt = item - tile * rowtiles;
-  const int e = tiles[2 * tile], g = tiles[2 * tile + 1];
-  const int pos0 = offsets[e] + kTT * g;
-  const int n = min(kTT, counts[e] - kTT * g);
-  if ((int)threadIdx.x < kTT) s.slot[threadIdx.x] = perm[pos0 + min((int)threadIdx.x, n - 1)];
+// Routed down (Q2K) over the work list into yp, or (DENSE) the shared
+// expert's down (F16) over all T tokens into y.
+template <bool DENSE, bool SMALL>
+__global__ __launch_bounds__(kGW * 64)
+__attribute__((amdgpu_waves_per_eu(DENSE ? 1 : 2))) void k_pf_down(
+    ds4moe_layer L, int64_t T, const int32_t* __restrict__ tiles, const int32_t* __restrict__ stiles,
+    const int32_t* __restrict__ ntiles, const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ perm, const _Float16* __restrict__ hin, float* __restrict__ yp,
+    float* __restrict__ y) {
+  constexpr int RING = ring_halves(SMALL);
+  __shared__ DnLds<RING> s;
+  int e, rt, pos0, n;
+  if (!tile_of<DENSE, SMALL>(L.d_model / 256, T, tiles, stiles, ntiles, counts, offsets, e, rt, pos0, n)) return;
+  if (!DENSE && (int)threadIdx.x < kTT) s.slot[threadIdx.x] = perm[pos0 + min((int)threadIdx.x, n - 1)];
   __syncthreads();
-  switch ((n + 15) >> 4) {
-    case 1: down_tile<1>(L, s, hw16, e, rt, pos0, n, yp); break;
-    case 2: down_tile<2>(L, s, hw16, e, rt, pos0, n, yp); break;
-    case 3: down_tile<3>(L, s, hw16, e, rt, pos0, n, yp); break;
-    case 4: down_tile<4>(L, s, hw16, e, rt, pos0, n, yp); break;
-    case 5: down_tile<5>(L, s, hw16, e, rt, pos0, n, yp); break;
-    case 6: down_tile<6>(L, s, hw16, e, rt, pos0, n, yp); break;
-    case 7: down_tile<7>(L, s, hw16, e, rt, pos0, n, yp); break;
-    default: down_tile<8>(L, s, hw16, e, rt, pos0, n, yp); break;
-  }
+#define DS4_DN(NF) down_tile<DENSE, RING, NF>(L, s, hin, e, rt, pos0, n, yp, y)
+  DS4_NF_SWITCH(n, SMALL, DENSE, DS4_DN)
+#undef DS4_DN
 }
 
-__global__ __launch_bounds__(kPW * 64) void k_shared_down_prefill(ds4moe_layer L, int64_t T,
-                                                                  const _Float16* __restrict__ hs16,
-                                                                  float* __restrict__ y) {
-  __shared__ float s_red[kPW * 64 * 4];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int c = lane & 15, q = lane >> 4;
-  const int d = L.d_model, fs = L.d_ff_shared;
-  const int row0 = blockIdx.x * 16;
-  const int64_t t = (int64_t)blockIdx.y * 16 + c;
-  const _Float16* bcol = t < T ? hs16 + t * fs : nullptr;
-  int ks0, ks1;
-  split_range(fs / 32, kPW, wave, ks0, ks1);
-  float4_t acc = {0.f, 0.f, 0.f, 0.f}, unused = acc;
-  f16_tile<false, false>(L.sh_down + (int64_t)(row0 + c) * fs, nullptr, bcol, nullptr, ks0, ks1, lane, acc, unused);
-  acc = block_reduce_waves<kPW>(acc, s_red, wave, lane);
-  if (wave == 0 && t < T) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) y[t * d + row0 + 4 * q + r] = acc[r];
-  }
-}
-
-// y[t][i] += sum_j yp[t*k + j][i], four columns per lane.
+// y[t][i] += sum_j yp[t*k + j][i] in ascending j, four columns per lane.
 __global__ __launch_bounds__(256) void k_combine(int64_t T, int d, int k, const float* __restrict__ yp,
                                                  float* __restrict__ y) {
   const int64_t n4 = T * d / 4;
@@ -467,10 +566,12 @@ hipError_t launch_prefill_experts(const Fwd& f) {
   const int64_t T = f.T;
   const int d = L.d_model, E = L.n_experts, k = L.top_k;
   const int64_t S = T * k;
-  const int64_t maxtiles = (S + kTT - 1) / kTT + E;  // >= sum_e ceil(n_e / kTT)
+  const int64_t maxtiles = (S + kTT - 1) / kTT + E;  // >= the large-tile count; the small list holds <= E
+  const int64_t ttiles = (T + kTT - 1) / kTT;
   auto xh = (const _Float16*)(ws + y.x_hi);
   auto xl = f.lo ? (const _Float16*)(ws + y.x_lo) : nullptr;
   auto tiles = (const int32_t*)(ws + y.tiles);
+  auto stiles = (const int32_t*)(ws + y.stiles);
   auto ntiles = (const int32_t*)(ws + y.ntiles);
   auto counts = (const int32_t*)(ws + y.counts);
   auto offsets = (const int32_t*)(ws + y.offsets);
@@ -479,18 +580,30 @@ hipError_t launch_prefill_experts(const Fwd& f) {
   auto hs16 = (_Float16*)(ws + y.hs16);
   auto hw16 = (_Float16*)(ws + y.hw16);
   auto yp = (float*)(ws + y.yp);
-  const unsigned tg = (unsigned)((T + 15) / 16);
-  const dim3 blk(kPW * 64), gblk(kGW * 64);
-  const dim3 ggu((unsigned)(maxtiles * (L.d_ff / 128))), gdn((unsigned)(maxtiles * (d / 256)));
+  const dim3 blk(kGW * 64);
+  const int gr = L.d_ff / (32 * gu_waves<false, false>());  // gate/up row slices
+  const dim3 gsh((unsigned)(ttiles * (L.d_ff_shared / 128))), gsd((unsigned)(ttiles * (d / 256)));
+  const dim3 ggu((unsigned)(maxtiles * gr)), ggs((unsigned)(E * gr));
+  const dim3 gdn((unsigned)(maxtiles * (d / 256))), gds((unsigned)(E * (d / 256)));
+#define DS4_GU_LAUNCH(LO, DENSE, SMALL, grid, out)                                                                  \
+  DS4_LAUNCH((k_pf_gateup<LO, DENSE, SMALL>), grid, blk, 0, f.st, L, T, xh, xl, tiles, stiles, ntiles, counts, \
+             offsets, perm, w, out)
   if (f.lo) {
-    DS4_LAUNCH(k_shared_gateup_prefill<true>, dim3(L.d_ff_shared / 16, tg), blk, 0, f.st, L, T, xh, xl, hs16);
-    DS4_LAUNCH(k_pf_gateup<true>, ggu, gblk, 0, f.st, L, xh, xl, tiles, ntiles, counts, offsets, perm, w, hw16);
+    DS4_GU_LAUNCH(true, true, false, gsh, hs16);
+    DS4_GU_LAUNCH(true, false, false, ggu, hw16);
+    DS4_GU_LAUNCH(true, false, true, ggs, hw16);
   } else {
-    DS4_LAUNCH(k_shared_gateup_prefill<false>, dim3(L.d_ff_shared / 16, tg), blk, 0, f.st, L, T, xh, xl, hs16);
-    DS4_LAUNCH(k_pf_gateup<false>, ggu, gblk, 0, f.st, L, xh, xl, tiles, ntiles, counts, offsets, perm, w, hw16);
+    DS4_GU_LAUNCH(false, true, false, gsh, hs16);
+    DS4_GU_LAUNCH(false, false, false, ggu, hw16);
+    DS4_GU_LAUNCH(false, false, true, ggs, hw16);
   }
-  DS4_LAUNCH(k_pf_down, gdn, gblk, 0, f.st, L, tiles, ntiles, counts, offsets, perm, hw16, yp);
-  DS4_LAUNCH(k_shared_down_prefill, dim3(d / 16, tg), blk, 0, f.st, L, T, hs16, f.y);
+#undef DS4_GU_LAUNCH
+  DS4_LAUNCH((k_pf_down<false, false>), gdn, blk, 0, f.st, L, T, tiles, stiles, ntiles, counts, offsets, perm, hw16,
+             yp, f.y);
+  DS4_LAUNCH((k_pf_down<false, true>), gds, blk, 0, f.st, L, T, tiles, stiles, ntiles, counts, offsets, perm, hw16,
+             yp, f.y);
+  DS4_LAUNCH((k_pf_down<true, false>), gsd, blk, 0, f.st, L, T, tiles, stiles, ntiles, counts, offsets, perm, hs16,
+             yp, f.y);
   const int64_t n4 = T * d / 4;
   const int cb = (int)std::min<int64_t>((n4 + 255) / 256, 8192);
   DS4_LAUNCH(k_combine, dim3(cb), dim3(256), 0, f.st, T, d, k, yp, f.y);

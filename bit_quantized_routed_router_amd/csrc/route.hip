@@ -185,27 +185,32 @@ __global__ __launch_bounds__(256) void k_count_experts(const int32_t* __restrict
   if (threadIdx.x == 0) counts[e] = tot;
 }
 
-// prefill grouping, pass 2: offsets, perm, inv, and the GEMM work list of
-// (expert, run of up to kPrefillTile of its slots) tiles (one block per
-// expert).
+// prefill grouping, pass 2: offsets, perm, inv, and the GEMM work lists of
+// (expert, run of its slots) tiles (one block per expert): runs of
+// kPrefillTile slots go to `tiles`, an expert's remainder of at most
+// kSmallTile slots to `stiles` (ntiles[0], ntiles[1]: their lengths).  A
+// tile (e, g) covers positions offsets[e] + kPrefillTile g onward.
 __global__ __launch_bounds__(256) void k_scatter_experts(const int32_t* __restrict__ idx, int64_t T, int k, int E,
                                                          const int32_t* __restrict__ counts,
                                                          int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
                                                          int32_t* __restrict__ inv, int32_t* counts_out,
                                                          int32_t* offsets_out, int32_t* perm_out,
-                                                         int32_t* __restrict__ tiles, int32_t* __restrict__ ntiles) {
+                                                         int32_t* __restrict__ tiles, int32_t* __restrict__ stiles,
+                                                         int32_t* __restrict__ ntiles) {
   __shared__ int s_tmp[8];
   const int e = blockIdx.x;
-  int a = 0, b = 0;
+  int a = 0, b = 0, c = 0;
   for (int u = threadIdx.x; u < E; u += blockDim.x) {
     if (u < e) {
       a += counts[u];
-      b += (counts[u] + kPrefillTile - 1) / kPrefillTile;
+      b += big_tiles(counts[u]);
+      c += small_tiles(counts[u]);
     }
   }
-  int off, tstart;
+  int off, tstart, sstart;
   block_excl_scan(a, s_tmp, &off);
   block_excl_scan(b, s_tmp, &tstart);
+  block_excl_scan(c, s_tmp, &sstart);
   const int cnt = counts[e];
   if (threadIdx.x == 0) {
     offsets[e] = off;
@@ -214,10 +219,15 @@ __global__ __launch_bounds__(256) void k_scatter_experts(const int32_t* __restri
     if (e == E - 1) {
       offsets[E] = off + cnt;
       if (offsets_out) offsets_out[E] = off + cnt;
-      *ntiles = tstart + (cnt + kPrefillTile - 1) / kPrefillTile;
+      ntiles[0] = tstart + big_tiles(cnt);
+      ntiles[1] = sstart + small_tiles(cnt);
+    }
+    if (small_tiles(cnt)) {
+      stiles[2 * sstart] = e;
+      stiles[2 * sstart + 1] = cnt / kPrefillTile;
     }
   }
-  for (int g = threadIdx.x; g < (cnt + kPrefillTile - 1) / kPrefillTile; g += blockDim.x) {
+  for (int g = threadIdx.x; g < big_tiles(cnt); g += blockDim.x) {
     tiles[2 * (tstart + g)] = e;
     tiles[2 * (tstart + g) + 1] = g;
   }
@@ -282,7 +292,8 @@ hipError_t launch_route(const Fwd& f, bool decode) {
                        f.idx_out, f.w_out);
     DS4_LAUNCH(k_count_experts, dim3(E), dim3(256), 0, f.st, idx, f.T * k, counts);
     DS4_LAUNCH(k_scatter_experts, dim3(E), dim3(256), 0, f.st, idx, f.T, k, E, counts, offsets, perm, inv,
-                       f.counts_out, f.offsets_out, f.perm_out, (int32_t*)(ws + y.tiles), (int32_t*)(ws + y.ntiles));
+                       f.counts_out, f.offsets_out, f.perm_out, (int32_t*)(ws + y.tiles), (int32_t*)(ws + y.stiles),
+                       (int32_t*)(ws + y.ntiles));
   }
   return hipGetLastError();
 }
