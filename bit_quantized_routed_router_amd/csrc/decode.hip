@@ -200,7 +200,12 @@ struct Stage1Lds {
   int last;
 };
 
-constexpr int kRouterWaitPolls = 0;  // bound on a shared-gate block's wait for the router blocks (0: no wait)
+// Sleeps (of s_sleep 16, about 0.4 us each) a shared-expert block of stage 1
+// takes before it starts streaming, so the router's 2 MB go first and the
+// routing finish overlaps the shared expert instead of following it.  Waiting
+// on the router's arrival counter instead would have hundreds of blocks poll
+// one L2 line that the router blocks must update.
+constexpr int kSharedStartSleeps = 3;
 
 // inputs per router block: 512, or 256 when d is an odd multiple of 256
 __host__ __device__ inline int router_chunk(int d) { return d % 512 == 0 ? 512 : 256; }
@@ -231,12 +236,14 @@ __device__ inline void f16_steps(const uint16_t* __restrict__ rowp, int ks0, int
 }
 
 // blocks [0, rblocks): router (expert tile, input chunk), chunk-major; then
-// two blocks per shared 16-row tile: gate product over one K half each.
+// four blocks per shared 16-row tile: the gate and up products over one K
+// half each.
 template <bool LO, bool BL>
 __global__ __launch_bounds__(kW * 64) void k_dec_stage1(ds4moe_layer L, int T, const void* __restrict__ x,
                                                         int rblocks, float* __restrict__ plog, RouteOut ro,
                                                         _Float16* __restrict__ xh, _Float16* __restrict__ xl,
-                                                        float* __restrict__ gu_part, int32_t* __restrict__ ctrl) {
+                                                        float* __restrict__ gu_part, _Float16* __restrict__ hs16,
+                                                        int32_t* __restrict__ ctrl) {
   __shared__ Stage1Lds lds;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = lane & 15, q = lane >> 4;
@@ -287,17 +294,16 @@ __global__ __launch_bounds__(kW * 64) void k_dec_stage1(ds4moe_layer L, int T, c
     if (lds.last) route_finish_block<true>(lds.route, plog, d / ck, L.router_bias, E, L.top_k, T, ro);
     return;
   }
-  // ---------------- shared expert gate: (tile, K half)
-  // Let the router stream go first: the gate blocks start loading once every
-  // router block has arrived.  The wait is bounded and only orders traffic;
-  // results do not depend on it.
-  if (threadIdx.x == 0) {
-    for (int it = 0; it < kRouterWaitPolls && ld_acq_int(&ctrl[0]) < rblocks; ++it) __builtin_amdgcn_s_sleep(16);
-  }
-  __syncthreads();
+  // ---------------- shared expert gate and up: (tile, part), parts 0, 1 the
+  // gate's K halves and 2, 3 the up's; the last of a tile's four blocks to
+  // arrive forms h = silu(g) * u.
+  // Let the router stream go first (only orders traffic; results do not
+  // depend on it).
+  for (int it = 0; it < kSharedStartSleeps; ++it) __builtin_amdgcn_s_sleep(16);
   const int sb = blockIdx.x - rblocks;
-  const int tile = sb >> 1, half = sb & 1;
-  const uint16_t* rp = L.sh_gate + (int64_t)(tile * 16 + c) * d + half * (d / 2);
+  const int tile = sb >> 2, part = sb & 3, half = part & 1;
+  const int fs = L.d_ff_shared;
+  const uint16_t* rp = (part < 2 ? L.sh_gate : L.sh_up) + (int64_t)(tile * 16 + c) * d + half * (d / 2);
   int ks0, ks1;
   split_range(d / 64, kW, wave, ks0, ks1);
   const int kb = half * (d / 2), st = stage_stride(d / 2);
@@ -324,11 +330,29 @@ __global__ __launch_bounds__(kW * 64) void k_dec_stage1(ds4moe_layer L, int T, c
                             },
                             acc);
   acc = reduce_waves<kW>(acc, lds.red, wave, lane);
-  float* tp = gu_part + (size_t)tile * 4 * 16 * T;  // [part][row][t]; parts 0, 1: gate halves
-  if (wave == 0 && c < T) {
+  float* tp = gu_part + (size_t)tile * 4 * 16 * T;  // [part][row][t]
+  if (wave == 0) {
+    if (c < T) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) tp[((size_t)half * 16 + 4 * q + r) * T + c] = acc[r];
+      for (int r = 0; r < 4; ++r) st_coh(&tp[((size_t)part * 16 + 4 * q + r) * T + c], acc[r]);
+    }
+    wait_stores();
   }
+  __syncthreads();
+  if (threadIdx.x == 0) lds.last = atomicAdd(&ctrl[1 + tile], 1) == 3;
+  __syncthreads();
+  if (!lds.last || wave != 0) return;
+  if (c < T) {
+    float pv[4][4];  // [part][r]: every coherent load in flight before the first use
+#pragma unroll
+    for (int pt = 0; pt < 4; ++pt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) pv[pt][r] = ld_coh(&tp[((size_t)pt * 16 + 4 * q + r) * T + c]);
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      hs16[(int64_t)c * fs + tile * 16 + 4 * q + r] = (_Float16)(silu(pv[0][r] + pv[1][r]) * (pv[2][r] + pv[3][r]));
+  }
+  if (lane == 0) ctrl[1 + tile] = 0;
 }
 
 // ============================================================== stage 2
@@ -344,75 +368,52 @@ struct Stage2Lds {
 
 constexpr int kSb2 = 4;  // CB2 super-blocks a wave loads at once
 
-// blocks [0, 2 nsh): shared expert up, (tile, K half); the second of a
-// tile's blocks to arrive forms h = silu(g) * u.  Then the routed gate/up
-// tiles: (distinct expert, 16-row tile).
+// blocks [0, d/16): shared expert down, ys = Wsd h for 16 output rows (the
+// memory stream); then the routed gate/up tiles: (distinct expert, 16-row
+// tile), whose codebook decoding is the arithmetic.
 template <bool LO, bool BL>
 __global__ __launch_bounds__(kW * 64) __attribute__((amdgpu_waves_per_eu(4))) void k_dec_stage2(
     ds4moe_layer L, int T, RouteOut ro, const _Float16* __restrict__ xh, const _Float16* __restrict__ xl,
-    float* __restrict__ gu_part, _Float16* __restrict__ hs16, _Float16* __restrict__ hw16,
-    _Float16* __restrict__ hsum, int32_t* __restrict__ ctrl) {
+    const _Float16* __restrict__ hs16, float* __restrict__ ys, _Float16* __restrict__ hw16,
+    _Float16* __restrict__ hsum) {
   __shared__ Stage2Lds lds;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = lane & 15, q = lane >> 4;
   const int tc = min(c, T - 1);
   const int d = L.d_model, f = L.d_ff, fs = L.d_ff_shared, k = L.top_k;
-  const int nr = f / 16, nb = d / QK, nsh = fs / 16;
+  const int nr = f / 16, nb = d / QK, ndt = d / 16;
   float4_t ag = {0.f, 0.f, 0.f, 0.f}, au = ag;
-  if ((int)blockIdx.x < 2 * nsh) {  // ---------------- shared expert up, (tile, K half)
-    const int tile = blockIdx.x >> 1, half = blockIdx.x & 1;
-    const uint16_t* rp = L.sh_up + (int64_t)(tile * 16 + c) * d + half * (d / 2);
+  if ((int)blockIdx.x < ndt) {  // ---------------- shared expert down: 16 output rows into ys
+    const int tile = blockIdx.x;
+    const uint16_t* rp = L.sh_down + (int64_t)(tile * 16 + c) * fs;
     int ks0, ks1;
-    split_range(d / 64, kW, wave, ks0, ks1);
-    const int kb = half * (d / 2), st = stage_stride(d / 2);
-    if (BL) dma_rows(xh + kb, d, T, d / 2, lds.bh, st, wave, kW, lane);
-    if (BL && LO) dma_rows(xl + kb, d, T, d / 2, lds.bl, st, wave, kW, lane);
-    constexpr int kBatch = BL ? 16 : 8;  // global activations take registers too
+    split_range(fs / 32, kW, wave, ks0, ks1);
+    const int st = stage_stride(fs);
+    const bool bls = T * fs <= kStageHalves;  // h of the group fits the stage
+    if (bls) dma_rows(hs16, fs, T, fs, lds.bh, st, wave, kW, lane);
+    constexpr int kBatch = 16;
     half8_t a[kBatch];
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) a[j] = *(const half8_t*)(rp + max(min(ks0 + j, ks1 - 1), 0) * 32 + 8 * q);
-    if (BL) {
+    if (bls) {
       wait_all();
       __syncthreads();
     }
-    f16_steps<LO, BL, kBatch>(rp, ks0, ks1, q, a,
-                              [&](int kk, half8_t& bh, half8_t& bl) {
-                                if (BL) {
-                                  bh = *(const half8_t*)(lds.bh + tc * st + kk);
-                                  if (LO) bl = *(const half8_t*)(lds.bl + tc * st + kk);
-                                } else {
-                                  bh = *(const half8_t*)(xh + (int64_t)tc * d + kb + kk);
-                                  if (LO) bl = *(const half8_t*)(xl + (int64_t)tc * d + kb + kk);
-                                }
-                              },
-                              ag);
+    f16_steps<false, BL, kBatch>(rp, ks0, ks1, q, a,
+                                 [&](int kk, half8_t& bh, half8_t&) {
+                                   bh = bls ? *(const half8_t*)(lds.bh + tc * st + kk)
+                                            : *(const half8_t*)(hs16 + (int64_t)tc * fs + kk);
+                                 },
+                                 ag);
     ag = reduce_waves<kW>(ag, lds.red, wave, lane);
-    float* tp = gu_part + (size_t)tile * 4 * 16 * T;  // parts 2, 3: up halves
-    if (wave == 0) {
-      if (c < T) {
+    if (wave == 0 && c < T) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) st_coh(&tp[((size_t)(2 + half) * 16 + 4 * q + r) * T + c], ag[r]);
-      }
-      wait_stores();
+      for (int r = 0; r < 4; ++r) ys[(int64_t)c * d + tile * 16 + 4 * q + r] = ag[r];
     }
-    __syncthreads();
-    if (threadIdx.x == 0) lds.last = atomicAdd(&ctrl[1 + tile], 1) == 1;
-    __syncthreads();
-    if (!lds.last || wave != 0) return;
-    if (c < T) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = 4 * q + r;
-        const float g = tp[((size_t)0 * 16 + row) * T + c] + tp[((size_t)1 * 16 + row) * T + c];  // stage 1
-        const float u = ld_coh(&tp[((size_t)2 * 16 + row) * T + c]) + ld_coh(&tp[((size_t)3 * 16 + row) * T + c]);
-        hs16[(int64_t)c * fs + tile * 16 + row] = (_Float16)(silu(g) * u);
-      }
-    }
-    if (lane == 0) ctrl[1 + tile] = 0;
     return;
   }
   // ---------------- routed gate/up: distinct expert i, 16-row tile
-  const int rel = blockIdx.x - 2 * nsh;
+  const int rel = blockIdx.x - ndt;
   const int i = rel / nr, tile = rel % nr;
   const int row0 = tile * 16;
   // phase 1: copies into LDS (activations, grid tables), independent of routing
@@ -607,13 +608,13 @@ __device__ inline void q2k_unit(const Q2kW& U, const _Float16* bcol, const _Floa
 constexpr int kUnits3 = 4;  // units whose weight loads a wave keeps in flight
 
 // Block (tile, part): output rows tile*16.., super-blocks of part `part`
-// (split_range over nparts), every distinct expert.  Partial tiles are
-// added in part order by the block that arrives last.
+// (split_range over nparts), every distinct expert.  The block that arrives
+// last writes y = ys + the partial tiles in part order.
 template <bool BL>
 __global__ __launch_bounds__(kW * 64) __attribute__((amdgpu_waves_per_eu(4))) void k_dec_stage3(
     ds4moe_layer L, int T, int nparts, const int32_t* __restrict__ ndist, const int32_t* __restrict__ distinct,
     const int32_t* __restrict__ tok_slot, const _Float16* __restrict__ hw16, const _Float16* __restrict__ hsum,
-    const _Float16* __restrict__ hs16, float* __restrict__ y_part, int32_t* __restrict__ ctrl, int nctrl1, int maxd,
+    const float* __restrict__ ys, float* __restrict__ y_part, int32_t* __restrict__ ctrl, int nctrl1, int maxd,
     float* __restrict__ y) {
   extern __shared__ __align__(16) unsigned char s_dyn[];  // staged activations when BL
   __shared__ float4_t s_red[kW][64];
@@ -621,7 +622,7 @@ __global__ __launch_bounds__(kW * 64) __attribute__((amdgpu_waves_per_eu(4))) vo
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = lane & 15, q = lane >> 4;
   const int tc = min(c, T - 1);
-  const int d = L.d_model, f = L.d_ff, fs = L.d_ff_shared, k = L.top_k;
+  const int d = L.d_model, f = L.d_ff, k = L.top_k;
   const int tile = blockIdx.x / nparts, part = blockIdx.x % nparts;
   const int row0 = tile * 16;
   const int nb = f / QK, fs16 = f / 16;
@@ -630,24 +631,17 @@ __global__ __launch_bounds__(kW * 64) __attribute__((amdgpu_waves_per_eu(4))) vo
   int sb0, sb1;
   split_range(nb, nparts, part, sb0, sb1);
   const int nbp = sb1 - sb0;  // routed super-blocks of this part
-  const int kcs = fs / nparts, k0s = part * kcs;  // shared down inputs of this part
   const uint8_t* down = (const uint8_t*)L.down;
-  // staged: routed activations [S][nbp * 256], their sums [2][S][nbp * 16],
-  // shared activations [T][kcs + 8]
+  // staged: routed activations [S][nbp * 256], their sums [2][S][nbp * 16]
   _Float16* s_h = (_Float16*)s_dyn;
   _Float16* s_cs = s_h + (size_t)S * nbp * QK;
-  _Float16* s_hs = s_cs + (size_t)2 * S * nbp * 16;
-  const int sts = stage_stride(kcs);
   if (blockIdx.x == 0)
     for (int i = threadIdx.x; i < nctrl1; i += blockDim.x) ctrl[i] = 0;
   // copies of the activations into LDS, then the routing tables; waiting for
   // the tables also completes the copies, and one barrier publishes them
-  if (BL) {
-    if (nbp > 0) {
-      dma_rows(hw16 + sb0 * QK, f, S, nbp * QK, s_h, nbp * QK, wave, kW, lane);
-      dma_rows(hsum + sb0 * 16, fs16, 2 * S, nbp * 16, s_cs, nbp * 16, wave, kW, lane);
-    }
-    dma_rows(hs16 + k0s, fs, T, kcs, s_hs, sts, wave, kW, lane);
+  if (BL && nbp > 0) {
+    dma_rows(hw16 + sb0 * QK, f, S, nbp * QK, s_h, nbp * QK, wave, kW, lane);
+    dma_rows(hsum + sb0 * 16, fs16, 2 * S, nbp * 16, s_cs, nbp * 16, wave, kW, lane);
   }
   const int nd = min(*ndist, maxd);
   const int maxunits = maxd * nbp, nunits = nd * nbp;
@@ -663,20 +657,6 @@ __global__ __launch_bounds__(kW * 64) __attribute__((amdgpu_waves_per_eu(4))) vo
   wait_all();
   __syncthreads();
   float4_t acc = {0.f, 0.f, 0.f, 0.f};
-  // shared expert down over this part's inputs (F16 rows row0..+15)
-  {
-    const uint16_t* rp = L.sh_down + (int64_t)(row0 + c) * fs + k0s;
-    int ks0, ks1;
-    split_range(kcs / 32, kW, wave, ks0, ks1);
-    constexpr int kBatch = 4;
-    half8_t a[kBatch];
-#pragma unroll
-    for (int j = 0; j < kBatch; ++j) a[j] = *(const half8_t*)(rp + max(min(ks0 + j, ks1 - 1), 0) * 32 + 8 * q);
-    auto getb = [&](int kk, half8_t& bh, half8_t&) {
-      bh = BL ? *(const half8_t*)(s_hs + tc * sts + kk) : *(const half8_t*)(hs16 + (int64_t)tc * fs + k0s + kk);
-    };
-    f16_steps<false, BL, kBatch, decltype(getb), true>(rp, ks0, ks1, q, a, getb, acc);
-  }
   const Q2kOff off = q2k_offsets(mb, nb, row0, c, q);
   for (int u0 = wave; u0 < maxunits; u0 += kW * kUnits3) {
     if (u0 != wave) {  // routing tables of later batches
@@ -716,8 +696,10 @@ __global__ __launch_bounds__(kW * 64) __attribute__((amdgpu_waves_per_eu(4))) vo
   if (nparts == 1) {
     if (wave == 0) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if (4 * q + r < T) y[(int64_t)(4 * q + r) * d + row0 + c] = acc[r];
+      for (int r = 0; r < 4; ++r) {
+        const int64_t o = (int64_t)(4 * q + r) * d + row0 + c;
+        if (4 * q + r < T) y[o] = ys[o] + acc[r];
+      }
     }
     return;
   }
@@ -736,7 +718,7 @@ __global__ __launch_bounds__(kW * 64) __attribute__((amdgpu_waves_per_eu(4))) vo
   for (int r = 0; r < 4; ++r) {
     const int t = 4 * q + r;
     if (t < T) {
-      float sum = 0.0f;
+      float sum = ys[(int64_t)t * d + row0 + c];
       for (int pp = 0; pp < nparts; ++pp) sum += ld_coh(&tp[((size_t)pp * 16 + c) * T + t]);
       y[(int64_t)t * d + row0 + c] = sum;
     }
@@ -759,11 +741,12 @@ static void launch_stages12(const Fwd& f, int rblocks, int nsh, int maxd, int nr
   auto hs16 = (_Float16*)(ws + y.hs16);
   auto hw16 = (_Float16*)(ws + y.hw16);
   auto hsum = (_Float16*)(ws + y.hsum);
+  auto ys = (float*)(ws + y.ys);
+  const int ndt = L.d_model / 16;
   const dim3 blk(kW * 64);
-  DS4_LAUNCH((k_dec_stage1<LO, BL>), dim3(rblocks + 2 * nsh), blk, 0, f.st, L, T, f.x, rblocks, plog, ro, xh, xl, gu,
-             ctrl);
-  DS4_LAUNCH((k_dec_stage2<LO, BL>), dim3(2 * nsh + maxd * nr), blk, 0, f.st, L, T, ro, xh, xl, gu, hs16, hw16, hsum,
-             ctrl);
+  DS4_LAUNCH((k_dec_stage1<LO, BL>), dim3(rblocks + 4 * nsh), blk, 0, f.st, L, T, f.x, rblocks, plog, ro, xh, xl, gu,
+             hs16, ctrl);
+  DS4_LAUNCH((k_dec_stage2<LO, BL>), dim3(ndt + maxd * nr), blk, 0, f.st, L, T, ro, xh, xl, hs16, ys, hw16, hsum);
 }
 
 hipError_t launch_decode(const Fwd& f) {
@@ -787,7 +770,7 @@ hipError_t launch_decode(const Fwd& f) {
     else launch_stages12<false, false>(f, rblocks, nsh, maxd, nr, ro);
   }
   auto ctrl = (int32_t*)(ws + y.ctrl);
-  auto hs16 = (_Float16*)(ws + y.hs16);
+  auto ys = (const float*)(ws + y.ys);
   auto hw16 = (_Float16*)(ws + y.hw16);
   auto hsum = (_Float16*)(ws + y.hsum);  // hi plane [S][f/16], then lo plane
   auto y_part = (float*)(ws + y.y_part);
@@ -795,16 +778,15 @@ hipError_t launch_decode(const Fwd& f) {
   const int nb = L.d_ff / QK;
   const int nparts = std::min(kDownParts, nb);
   const int nbp_max = (nb + nparts - 1) / nparts;
-  // stage 3 stages each part's routed activations and sums, and its share of h
-  const size_t stage_bytes = (size_t)S * nbp_max * QK * 2 + (size_t)2 * S * nbp_max * 16 * 2 +
-                             (size_t)T * stage_stride(fs / nparts) * 2;
+  // stage 3 stages each part's routed activations and their sums
+  const size_t stage_bytes = (size_t)S * nbp_max * QK * 2 + (size_t)2 * S * nbp_max * 16 * 2;
   const dim3 blk3(kW * 64);
   if (stage_bytes <= kStage3Bytes)
     DS4_LAUNCH(k_dec_stage3<true>, dim3(ndt * nparts), blk3, stage_bytes, f.st, L, T, nparts, ro.ndist, ro.distinct,
-               ro.tok_slot, hw16, hsum, hs16, y_part, ctrl, ctrl_ints(L), maxd, f.y);
+               ro.tok_slot, hw16, hsum, ys, y_part, ctrl, ctrl_ints(L), maxd, f.y);
   else
     DS4_LAUNCH(k_dec_stage3<false>, dim3(ndt * nparts), blk3, 0, f.st, L, T, nparts, ro.ndist, ro.distinct,
-               ro.tok_slot, hw16, hsum, hs16, y_part, ctrl, ctrl_ints(L), maxd, f.y);
+               ro.tok_slot, hw16, hsum, ys, y_part, ctrl, ctrl_ints(L), maxd, f.y);
   return hipGetLastError();
 }
 
