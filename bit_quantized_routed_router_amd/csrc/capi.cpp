@@ -53,7 +53,6 @@ WsLayout ws_layout(const ds4moe_layer& L, int64_t T, int mode) {
     if (mode == DS4MOE_MODE_DECODE) {
       y.gu_part = take((fs / 16) * 4 * 16 * Tdec * 4);
       y.ys = take(Tdec * d * 4);
-      y.y_part = take((d / 16) * kDownParts * 16 * Tdec * 4);
     }
   }
   y.total = o;

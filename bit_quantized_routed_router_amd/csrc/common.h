@@ -259,6 +259,25 @@ __device__ inline half8_t zero_half8() {
 // weight stream behind it (loads retire in issue order).
 __device__ inline void pin() { __builtin_amdgcn_sched_barrier(0); }
 
+// Load of a wave-uniform address through the scalar unit (constant address
+// space): it is counted apart from vector loads, so waiting for it does not
+// wait for the wave's vector loads or copies into LDS.  Only for data that no
+// block of the running kernel writes.
+__device__ inline int ld_uniform(const int32_t* p) { return *(const __attribute__((address_space(4))) int32_t*)p; }
+
 __device__ inline float silu(float g) { return g / (1.0f + __expf(-g)); }
+
+// Work item of this block: blocks b < count are spread so that XCD x = b % 8
+// (blocks are dealt to the 8 XCDs round-robin) runs the contiguous items
+// [start_x, start_x + quota_x) in order, so neighbouring items share an L2;
+// blocks >= count get none.
+__device__ inline bool xcd_item(int count, int& item) {
+  const int b = blockIdx.x;
+  if (b >= count) return false;
+  const int x = b & 7, i = b >> 3;
+  const int base = count >> 3, rem = count & 7;
+  item = x * base + min(x, rem) + i;
+  return true;
+}
 
 }  // namespace ds4

@@ -1,27 +1,26 @@
 // Batched decode (T <= 16 tokens per group): the whole layer in three
-// streaming kernels whose 16 MFMA columns are the group's tokens.  The
-// routed experts' dequantization is arithmetic-bound while the F16 shared
-// expert is memory-bound, so each stage pairs one with the other:
+// streaming kernels whose 16 MFMA columns are the group's tokens.  Routing
+// gates the routed experts, so the F16 shared expert (independent of it)
+// fills the first two stages beside the routing chain:
 //
 //   k_dec_stage1  router partial logits per input chunk (the last router
 //                 block to arrive finishes routing: top-k, gate weights,
-//                 grouping) and the shared expert's gate product as half-K
-//                 partial tiles.  x is read in its input type; the router
-//                 chunk owners keep the binary16 copy for stage 2.
-//   k_dec_stage2  the shared expert's up product (the last of a tile's two
-//                 blocks forms h = silu(g) * u), and for every distinct
-//                 selected expert its gate/up tiles: w * silu(G x) * (U x) as
-//                 binary16 plus the sums over each 16 rows (one Q2K
+//                 grouping) and the shared expert's gate and up products,
+//                 four blocks per 16 rows (gate or up, half of K each); the
+//                 last of the four forms h = silu(g) * u as binary16.  x is
+//                 read in its input type; the router chunk owners keep the
+//                 binary16 copy for stage 2.
+//   k_dec_stage2  the shared expert's down product ys (fp32), and for every
+//                 distinct selected expert its gate/up tiles: w * silu(G x) *
+//                 (U x) as binary16 plus the sums over each 16 rows (one Q2K
 //                 sub-block of the down input) as binary16 hi/lo.
-//   k_dec_stage3  per 16 output rows, a few blocks each take a share of the
-//                 routed super-blocks and of the shared expert's down input;
-//                 their partial tiles are added in a fixed order by the block
-//                 that arrives last, which writes y.  It also clears the
-//                 earlier stages' arrival counters.
+//   k_dec_stage3  one block per 16 output rows over every distinct expert's
+//                 down super-blocks; it writes y = ys + the routed terms and
+//                 clears the earlier stages' arrival counters.
 // Each distinct expert is read once per call however many tokens chose it,
-// and results do not depend on block scheduling.  Blocks hand partials to
-// the last arriver with device-coherent (sc1) stores and loads around an
-// atomic counter, which needs no L2 write-back.
+// and results do not depend on block scheduling.  Blocks hand stage-1
+// partials to the last arriver with device-coherent (sc1) stores and loads
+// around an atomic counter, which needs no L2 write-back.
 //
 // Operands.  Packed weights: every lane owns a contiguous 16-byte piece of
 // its row's super-block and feeds those weights to consecutive MFMA steps
@@ -368,11 +367,37 @@ struct Stage2Lds {
 
 constexpr int kSb2 = 4;  // CB2 super-blocks a wave loads at once
 
+// One CB2 group's codebook entries, read ahead of their use: magnitudes and
+// sign masks of the 8 weights (binary16 bit patterns).
+struct Cb2Raw {
+  u32x4_t m, s;
+};
+struct Cb2Step {  // one sub-block step of a routed gate/up wave
+  Cb2Raw g, u;
+  half8_t bh, bl;
+};
+__device__ inline void cb2_lookup(Cb2Raw& R, uint32_t idxw, uint32_t aux, int q, const uint32_t* mag,
+                                  const uint32_t* sgn) {
+  R.m = *(const u32x4_t*)(mag + 4 * ((idxw >> (8 * q)) & 0xFFu));
+  R.s = *(const u32x4_t*)(sgn + 4 * ((aux >> (7 * q)) & 0x7Fu));
+}
+// sign * (2s+1) * m as binary16 (exact integers <= 155), s from aux bits 28..31
+__device__ inline half8_t cb2_apply(const Cb2Raw& R, uint32_t aux) {
+  const _Float16 S = (_Float16)(float)(2 * (aux >> 28) + 1);
+  const half2_t S2 = {S, S};
+  u32x4_t r;
+  r.x = as_u32(as_half2(R.m.x ^ R.s.x) * S2);
+  r.y = as_u32(as_half2(R.m.y ^ R.s.y) * S2);
+  r.z = as_u32(as_half2(R.m.z ^ R.s.z) * S2);
+  r.w = as_u32(as_half2(R.m.w ^ R.s.w) * S2);
+  return as_half8(r);
+}
+
 // blocks [0, d/16): shared expert down, ys = Wsd h for 16 output rows (the
 // memory stream); then the routed gate/up tiles: (distinct expert, 16-row
 // tile), whose codebook decoding is the arithmetic.
 template <bool LO, bool BL>
-__global__ __launch_bounds__(kW * 64) __attribute__((amdgpu_waves_per_eu(4))) void k_dec_stage2(
+__global__ __launch_bounds__(kW * 64) __attribute__((amdgpu_waves_per_eu(LO ? 2 : 4))) void k_dec_stage2(
     ds4moe_layer L, int T, RouteOut ro, const _Float16* __restrict__ xh, const _Float16* __restrict__ xl,
     const _Float16* __restrict__ hs16, float* __restrict__ ys, _Float16* __restrict__ hw16,
     _Float16* __restrict__ hsum) {
@@ -421,13 +446,14 @@ __global__ __launch_bounds__(kW * 64) __attribute__((amdgpu_waves_per_eu(4))) vo
   if (BL) dma_rows(xh, d, T, d, lds.bh, st, wave, kW, lane);
   if (BL && LO) dma_rows(xl, d, T, d, lds.bl, st, wave, kW, lane);
   dma_pieces(&c_dec_tables.mag[0][0], 384, lds.mag, wave, kW, lane);  // mag (256 pieces), then sgn
-  // phase 2: routing tables; waiting for them also completes the copies
-  const int nd = *ro.ndist;
-  const int e = clamp_index(ro.distinct[i], L.n_experts);
-  int slot = ro.tok_slot[i * kDecodeGroup + c];
-  wait_all();
-  if (i >= nd) return;  // whole block; no copy is in flight
-  __syncthreads();
+  // phase 2: routing tables by scalar loads, which do not wait for the
+  // copies: the first weight batch goes out while they are in flight
+  const int nd = ld_uniform(ro.ndist);
+  if (i >= nd) {  // whole block
+    wait_all();   // no copy into LDS left in flight
+    return;
+  }
+  const int e = clamp_index(ld_uniform(ro.distinct + i), L.n_experts);
   // Transposed products: x (token c') is the MFMA's A operand, the weights
   // its B operand, so lane (c, q) ends with tokens 4q..4q+3 of row row0 + c.
   const size_t mb = (size_t)f * nb;  // blocks per matrix
@@ -441,13 +467,15 @@ __global__ __launch_bounds__(kW * 64) __attribute__((amdgpu_waves_per_eu(4))) vo
   split_range(nb, kW, wave, sb0, sb1);
   // d of kSb2 consecutive super-blocks in one load per matrix when aligned
   const bool dvec = nb % kSb2 == 0;
-  for (int b0 = sb0; b0 < sb1; b0 += kSb2) {
-    // phase 3: weight loads, consumed as they arrive
-    u32x4_t cg[kSb2], cu[kSb2];
-    float dg[kSb2], du[kSb2];
+  u32x4_t cg[kSb2], cu[kSb2];
+  float dg[kSb2], du[kSb2];
+  // phase 3: weight loads of kSb2 super-blocks from b0, consumed as they
+  // arrive (indices clamped into [0, nb): a wave with an empty range loads
+  // a valid block it never uses)
+  auto load_batch = [&](int b0) {
 #pragma unroll
     for (int j = 0; j < kSb2; ++j) {
-      const int b = min(b0 + j, sb1 - 1);
+      const int b = max(min(b0 + j, sb1 - 1), 0);
       cg[j] = __builtin_nontemporal_load((const u32x4_t*)(grow + b * 64));
       cu[j] = __builtin_nontemporal_load((const u32x4_t*)(urow + b * 64));
     }
@@ -461,41 +489,60 @@ __global__ __launch_bounds__(kW * 64) __attribute__((amdgpu_waves_per_eu(4))) vo
     } else {
 #pragma unroll
       for (int j = 0; j < kSb2; ++j) {
-        const int b = min(b0 + j, sb1 - 1);
+        const int b = max(min(b0 + j, sb1 - 1), 0);
         dg[j] = h2f(gd[b]);
         du[j] = h2f(ud[b]);
       }
     }
+  };
+  load_batch(sb0);
+  wait_all();  // the copies (and the first batch)
+  __syncthreads();
+  for (int b0 = sb0; b0 < sb1; b0 += kSb2) {
+    if (b0 != sb0) load_batch(b0);
     pin();
-#pragma unroll
-    for (int j = 0; j < kSb2; ++j) {  // super-blocks past the range get a zero scale
-      const int kb = min(b0 + j, sb1 - 1) * QK;
-      const float sg = b0 + j < sb1 ? dg[j] : 0.0f, su = b0 + j < sb1 ? du[j] : 0.0f;
-      float4_t pg = {0.f, 0.f, 0.f, 0.f}, pu = pg;
-#pragma unroll
-      for (int s2 = 0; s2 < 8; ++s2) {
-        const int kk = kb + cb2_boff(q, s2);
-        half8_t bh, bl;
-        if (BL) {
-          bh = *(const half8_t*)(lds.bh + tc * st + kk);
-          if (LO) bl = *(const half8_t*)(lds.bl + tc * st + kk);
-        } else {
-          bh = *(const half8_t*)(xh + (int64_t)tc * d + kk);
-          if (LO) bl = *(const half8_t*)(xl + (int64_t)tc * d + kk);
-        }
-        const half8_t a0 = cb2_frag((s2 & 4) ? cg[j].z : cg[j].x, (s2 & 4) ? cg[j].w : cg[j].y, s2 & 3, lds.mag, lds.sgn);
-        const half8_t a1 = cb2_frag((s2 & 4) ? cu[j].z : cu[j].x, (s2 & 4) ? cu[j].w : cu[j].y, s2 & 3, lds.mag, lds.sgn);
-        pg = mfma16x16x32(bh, a0, pg);
-        pu = mfma16x16x32(bh, a1, pu);
-        if (LO) {
-          pg = mfma16x16x32(bl, a0, pg);
-          pu = mfma16x16x32(bl, a1, pu);
-        }
+    // 8 steps per super-block (one per sub-block); each step's LDS reads
+    // (activations, codebook magnitudes and signs) are issued one step ahead
+    Cb2Step F[2];
+    auto fetch = [&](Cb2Step& G, int t) {
+      const int j = t >> 3, s2 = t & 7;
+      const int kk = min(b0 + j, sb1 - 1) * QK + cb2_boff(q, s2);
+      if (BL) {
+        G.bh = *(const half8_t*)(lds.bh + tc * st + kk);
+        if (LO) G.bl = *(const half8_t*)(lds.bl + tc * st + kk);
+      } else {
+        G.bh = *(const half8_t*)(xh + (int64_t)tc * d + kk);
+        if (LO) G.bl = *(const half8_t*)(xl + (int64_t)tc * d + kk);
       }
+      cb2_lookup(G.g, (s2 & 4) ? cg[j].z : cg[j].x, (s2 & 4) ? cg[j].w : cg[j].y, s2 & 3, lds.mag, lds.sgn);
+      cb2_lookup(G.u, (s2 & 4) ? cu[j].z : cu[j].x, (s2 & 4) ? cu[j].w : cu[j].y, s2 & 3, lds.mag, lds.sgn);
+    };
+    float4_t pg = {0.f, 0.f, 0.f, 0.f}, pu = pg;
+    fetch(F[0], 0);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {  // the lane's own row: its own d
-        ag[r] += sg * pg[r];
-        au[r] += su * pu[r];
+    for (int t = 0; t < 8 * kSb2; ++t) {
+      if (t + 1 < 8 * kSb2) fetch(F[(t + 1) & 1], t + 1);
+      pin();
+      const Cb2Step& G = F[t & 1];
+      const int j = t >> 3, s2 = t & 7;
+      const half8_t a0 = cb2_apply(G.g, (s2 & 4) ? cg[j].w : cg[j].y);
+      const half8_t a1 = cb2_apply(G.u, (s2 & 4) ? cu[j].w : cu[j].y);
+      pg = mfma16x16x32(G.bh, a0, pg);
+      pu = mfma16x16x32(G.bh, a1, pu);
+      if (LO) {
+        pg = mfma16x16x32(G.bl, a0, pg);
+        pu = mfma16x16x32(G.bl, a1, pu);
+      }
+      pin();
+      if (s2 == 7) {  // super-blocks past the range get a zero scale
+        const float sg = b0 + j < sb1 ? dg[j] : 0.0f, su = b0 + j < sb1 ? du[j] : 0.0f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {  // the lane's own row: its own d
+          ag[r] += sg * pg[r];
+          au[r] += su * pu[r];
+        }
+        pg = float4_t{0.f, 0.f, 0.f, 0.f};
+        pu = pg;
       }
     }
   }
@@ -570,26 +617,33 @@ __device__ inline void q2k_wload(Q2kW& U, const uint8_t* base, const Q2kOff& o, 
   U.sup = *(const uint32_t*)(base + o.sup + b * 4);
 }
 
+// Activation operands of one unit for lane (c, q): its token's binary16 h at
+// the lane's K offsets and the hi/lo sums of the 16 sub-blocks.
+struct Q2kA {
+  half8_t b[8], bh, bl;
+};
+
+// bcol: the activation row of the lane's token at the unit's super-block
+// (LDS or global); csh/csl: binary16 hi/lo of its 16 sub-block sums.
+__device__ inline void q2k_act(Q2kA& A, const _Float16* bcol, const _Float16* csh, const _Float16* csl, int q) {
+#pragma unroll
+  for (int s = 0; s < 8; ++s) A.b[s] = *(const half8_t*)(bcol + q2k_boff(q, s));
+  A.bh = *(const half8_t*)(csh + 8 * (q & 1));
+  A.bl = *(const half8_t*)(csl + 8 * (q & 1));
+}
+
 // One unit, transposed: the activations are the MFMA's A operand (row c' =
 // token c'), the weights its B operand, so lane (c, q) ends with tokens
-// 4q..4q+3 of row row0 + c.  bcol: the activation row of the lane's token at
-// the unit's super-block (LDS or global); csh/csl: binary16 hi/lo of its 16
-// sub-block sums.  vmask: bit r set when token 4q + r has a slot for this
-// expert.
-__device__ inline void q2k_unit(const Q2kW& U, const _Float16* bcol, const _Float16* csh, const _Float16* csl,
-                                uint32_t vmask, int q, float4_t& acc) {
-  half8_t b[8];
-#pragma unroll
-  for (int s = 0; s < 8; ++s) b[s] = *(const half8_t*)(bcol + q2k_boff(q, s));
-  const half8_t bh = *(const half8_t*)(csh + 8 * (q & 1));
-  const half8_t bl = *(const half8_t*)(csl + 8 * (q & 1));
+// 4q..4q+3 of row row0 + c.  vmask: bit r set when token 4q + r has a slot
+// for this expert.
+__device__ inline void q2k_unit(const Q2kW& U, const Q2kA& A, uint32_t vmask, int q, float4_t& acc) {
   float4_t p = {0.f, 0.f, 0.f, 0.f}, pm = p;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {  // sub-block 4q + j: two MFMA steps share its scale
     half8_t alo, ahi;
     q2k_subblock(U.codes[j], (U.sc4 >> (8 * j)) & 15u, alo, ahi);
-    p = mfma16x16x32(b[2 * j], alo, p);
-    p = mfma16x16x32(b[2 * j + 1], ahi, p);
+    p = mfma16x16x32(A.b[2 * j], alo, p);
+    p = mfma16x16x32(A.b[2 * j + 1], ahi, p);
   }
   // min term: K-slots 0..15 are the 16 sub-blocks (lane groups q >= 2 add zeros)
   u32x4_t t;
@@ -598,132 +652,133 @@ __device__ inline void q2k_unit(const Q2kW& U, const _Float16* bcol, const _Floa
   t.z = nib_hi_pair_f16(U.mins.y, 0);
   t.w = nib_hi_pair_f16(U.mins.y, 2);
   const half8_t am = q < 2 ? as_half8(t) : zero_half8();
-  pm = mfma16x16x32(bh, am, pm);
-  pm = mfma16x16x32(bl, am, pm);
+  pm = mfma16x16x32(A.bh, am, pm);
+  pm = mfma16x16x32(A.bl, am, pm);
   const float dd = h2f((uint16_t)(U.sup & 0xFFFFu)), dm = h2f((uint16_t)(U.sup >> 16));
 #pragma unroll
   for (int r = 0; r < 4; ++r) acc[r] += ((vmask >> r) & 1u) ? dd * p[r] - dm * pm[r] : 0.0f;
 }
 
-constexpr int kUnits3 = 4;  // units whose weight loads a wave keeps in flight
+constexpr int kW3 = 16;     // waves per stage-3 block: 4 per SIMD, few units each
+constexpr int kUnits3 = 3;  // units whose weight loads a wave keeps in flight
 
-// Block (tile, part): output rows tile*16.., super-blocks of part `part`
-// (split_range over nparts), every distinct expert.  The block that arrives
-// last writes y = ys + the partial tiles in part order.
+// Block `tile`: output rows tile*16 .. tile*16+15 over every (distinct
+// expert, super-block) unit, so the whole sum stays in the block and it
+// writes y = ys + the routed terms itself.
 template <bool BL>
-__global__ __launch_bounds__(kW * 64) __attribute__((amdgpu_waves_per_eu(4))) void k_dec_stage3(
-    ds4moe_layer L, int T, int nparts, const int32_t* __restrict__ ndist, const int32_t* __restrict__ distinct,
+__global__ __launch_bounds__(kW3 * 64) __attribute__((amdgpu_waves_per_eu(4))) void k_dec_stage3(
+    ds4moe_layer L, int T, const int32_t* __restrict__ ndist, const int32_t* __restrict__ distinct,
     const int32_t* __restrict__ tok_slot, const _Float16* __restrict__ hw16, const _Float16* __restrict__ hsum,
-    const float* __restrict__ ys, float* __restrict__ y_part, int32_t* __restrict__ ctrl, int nctrl1, int maxd,
-    float* __restrict__ y) {
+    const float* __restrict__ ys, int32_t* __restrict__ ctrl, int nctrl1, int maxd, float* __restrict__ y) {
   extern __shared__ __align__(16) unsigned char s_dyn[];  // staged activations when BL
-  __shared__ float4_t s_red[kW][64];
-  __shared__ int s_last;
+  __shared__ float4_t s_red[kW3][64];
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = lane & 15, q = lane >> 4;
-  const int tc = min(c, T - 1);
   const int d = L.d_model, f = L.d_ff, k = L.top_k;
-  const int tile = blockIdx.x / nparts, part = blockIdx.x % nparts;
-  const int row0 = tile * 16;
+  const int tile = blockIdx.x, row0 = tile * 16;
   const int nb = f / QK, fs16 = f / 16;
   const size_t mb = (size_t)d * nb;
   const int S = T * k;
-  int sb0, sb1;
-  split_range(nb, nparts, part, sb0, sb1);
-  const int nbp = sb1 - sb0;  // routed super-blocks of this part
   const uint8_t* down = (const uint8_t*)L.down;
-  // staged: routed activations [S][nbp * 256], their sums [2][S][nbp * 16]
+  // staged: routed activations [S][f], their sums [2][S][f / 16]
   _Float16* s_h = (_Float16*)s_dyn;
-  _Float16* s_cs = s_h + (size_t)S * nbp * QK;
+  _Float16* s_cs = s_h + (size_t)S * f;
   if (blockIdx.x == 0)
     for (int i = threadIdx.x; i < nctrl1; i += blockDim.x) ctrl[i] = 0;
-  // copies of the activations into LDS, then the routing tables; waiting for
-  // the tables also completes the copies, and one barrier publishes them
-  if (BL && nbp > 0) {
-    dma_rows(hw16 + sb0 * QK, f, S, nbp * QK, s_h, nbp * QK, wave, kW, lane);
-    dma_rows(hsum + sb0 * 16, fs16, 2 * S, nbp * 16, s_cs, nbp * 16, wave, kW, lane);
+  // copies of the activations into LDS; one barrier publishes them
+  if (BL) {
+    dma_rows(hw16, f, S, f, s_h, f, wave, kW3, lane);
+    dma_rows(hsum, fs16, 2 * S, fs16, s_cs, fs16, wave, kW3, lane);
   }
-  const int nd = min(*ndist, maxd);
-  const int maxunits = maxd * nbp, nunits = nd * nbp;
-  // units u = (expert slot u / nbp, super-block sb0 + u % nbp); wave w takes
-  // u = w, w + kW, ... in batches of kUnits3
-  int ej[kUnits3], sj[kUnits3];
-#pragma unroll
-  for (int j = 0; j < kUnits3; ++j) {
-    const int i = nbp > 0 ? min((wave + j * kW) / nbp, maxd - 1) : 0;
-    ej[j] = distinct[i];
-    sj[j] = tok_slot[i * kDecodeGroup + c];
-  }
-  wait_all();
-  __syncthreads();
-  float4_t acc = {0.f, 0.f, 0.f, 0.f};
+  // routing tables: expert ids by scalar loads, which do not wait for the
+  // copies, so the first weight batch goes out while they are in flight
+  const int nd = min(ld_uniform(ndist), maxd);
+  const int maxunits = maxd * nb, nunits = nd * nb;
+  // units u = (expert slot u / nb, super-block u % nb); wave w takes
+  // u = w, w + kW3, ... in batches of kUnits3
+  int sj[kUnits3], bsb[kUnits3];  // per unit: slot of token c, super-block
+  Q2kW W[kUnits3];
   const Q2kOff off = q2k_offsets(mb, nb, row0, c, q);
-  for (int u0 = wave; u0 < maxunits; u0 += kW * kUnits3) {
-    if (u0 != wave) {  // routing tables of later batches
-#pragma unroll
-      for (int j = 0; j < kUnits3; ++j) {
-        const int i = min((u0 + j * kW) / nbp, maxd - 1);
-        ej[j] = distinct[i];
-        sj[j] = tok_slot[i * kDecodeGroup + c];
-      }
+  // unit u -> (expert slot u / nb, super-block u % nb), stepped by kW3
+  // without a division per unit
+  const int di = kW3 / nb, db = kW3 % nb;
+  auto unit_at = [&](int u, int& i, int& b) {  // u clamped into [0, maxunits)
+    i = u / nb;
+    b = u - i * nb;
+  };
+  auto step_unit = [&](int& i, int& b) {
+    i += di;
+    b += db;
+    if (b >= nb) {
+      b -= nb;
+      ++i;
     }
-    Q2kW W[kUnits3];
+  };
+  auto load_batch = [&](int u0) {
+    int ij[kUnits3], bj[kUnits3], ej[kUnits3];
+    unit_at(u0, ij[0], bj[0]);
+#pragma unroll
+    for (int j = 1; j < kUnits3; ++j) {
+      ij[j] = ij[j - 1];
+      bj[j] = bj[j - 1];
+      step_unit(ij[j], bj[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < kUnits3; ++j) {  // units past the end repeat the last one
+      if (ij[j] >= maxd) {
+        ij[j] = maxd - 1;
+        bj[j] = nb - 1;
+      }
+      ej[j] = ld_uniform(distinct + ij[j]);  // all expert ids in flight before the first address needs one
+    }
+    pin();
 #pragma unroll
     for (int j = 0; j < kUnits3; ++j) {
-      const int u = min(u0 + j * kW, maxunits - 1);
-      const int e = __builtin_amdgcn_readfirstlane(clamp_index(ej[j], L.n_experts));  // the same in every lane
-      q2k_wload(W[j], down + (size_t)e * mb * 84, off, sb0 + u % nbp);
+      q2k_wload(W[j], down + (size_t)clamp_index(ej[j], L.n_experts) * mb * 84, off, bj[j]);
+      sj[j] = tok_slot[ij[j] * kDecodeGroup + c];
+      bsb[j] = bj[j];
     }
+  };
+  load_batch(wave);
+  float ysv[4];  // the shared expert's output for this lane's tokens (read early)
+#pragma unroll
+  for (int r = 0; r < 4; ++r) ysv[r] = ys[(int64_t)min(4 * q + r, T - 1) * d + row0 + c];
+#pragma unroll
+  for (int j = 0; j < kUnits3; ++j) asm volatile("" ::"v"(sj[j]));  // keeps these loads ahead of the barrier
+#pragma unroll
+  for (int r = 0; r < 4; ++r) asm volatile("" ::"v"(ysv[r]));
+  asm volatile("" ::"s"(nd));
+  wait_all();  // the copies (and the first batch)
+  __syncthreads();
+  float4_t acc = {0.f, 0.f, 0.f, 0.f};
+  for (int u0 = wave; u0 < maxunits; u0 += kW3 * kUnits3) {
+    if (u0 != wave) load_batch(u0);
     pin();
     // units past the end and tokens without a slot add nothing
 #pragma unroll
     for (int j = 0; j < kUnits3; ++j) {
-      const int u = u0 + j * kW;
+      const int u = u0 + j * kW3;
       const int slot = sj[j];  // slot of token c for this unit's expert
       const bool has = u < nunits && slot >= 0 && slot < S;
       const uint32_t vmask = (uint32_t)(__ballot(has) >> (4 * q)) & 15u;  // tokens 4q..4q+3
       const int row = has ? slot : 0;
-      const int bl = min(u, maxunits - 1) % nbp;  // super-block within the part
+      const int b = bsb[j];  // super-block
+      Q2kA A;
       if (BL)
-        q2k_unit(W[j], s_h + (size_t)row * nbp * QK + bl * QK, s_cs + (size_t)row * nbp * 16 + bl * 16,
-                 s_cs + (size_t)(S + row) * nbp * 16 + bl * 16, vmask, q, acc);
+        q2k_act(A, s_h + (size_t)row * f + b * QK, s_cs + (size_t)row * fs16 + b * 16,
+                s_cs + (size_t)(S + row) * fs16 + b * 16, q);
       else
-        q2k_unit(W[j], hw16 + (size_t)row * f + (sb0 + bl) * QK, hsum + (size_t)row * fs16 + (sb0 + bl) * 16,
-                 hsum + (size_t)(S + row) * fs16 + (sb0 + bl) * 16, vmask, q, acc);
+        q2k_act(A, hw16 + (size_t)row * f + b * QK, hsum + (size_t)row * fs16 + b * 16,
+                hsum + (size_t)(S + row) * fs16 + b * 16, q);
+      q2k_unit(W[j], A, vmask, q, acc);
     }
   }
-  acc = reduce_waves<kW>(acc, s_red, wave, lane);  // lane (c, q): tokens 4q + r of row row0 + c
-  if (nparts == 1) {
-    if (wave == 0) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int64_t o = (int64_t)(4 * q + r) * d + row0 + c;
-        if (4 * q + r < T) y[o] = ys[o] + acc[r];
-      }
-    }
-    return;
-  }
-  float* tp = y_part + (size_t)tile * nparts * 16 * T;  // [part][row][t]
+  acc = reduce_waves<kW3>(acc, s_red, wave, lane);  // lane (c, q): tokens 4q + r of row row0 + c
   if (wave == 0) {
 #pragma unroll
     for (int r = 0; r < 4; ++r)
-      if (4 * q + r < T) st_coh(&tp[((size_t)part * 16 + c) * T + 4 * q + r], acc[r]);
-    wait_stores();
+      if (4 * q + r < T) y[(int64_t)(4 * q + r) * d + row0 + c] = ysv[r] + acc[r];
   }
-  __syncthreads();
-  if (threadIdx.x == 0) s_last = atomicAdd(&ctrl[kCtrlDown + tile], 1) == nparts - 1;
-  __syncthreads();
-  if (!s_last || wave != 0) return;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int t = 4 * q + r;
-    if (t < T) {
-      float sum = ys[(int64_t)t * d + row0 + c];
-      for (int pp = 0; pp < nparts; ++pp) sum += ld_coh(&tp[((size_t)pp * 16 + c) * T + t]);
-      y[(int64_t)t * d + row0 + c] = sum;
-    }
-  }
-  if (lane == 0) ctrl[kCtrlDown + tile] = 0;
 }
 
 // ============================================================== launcher
@@ -773,20 +828,16 @@ hipError_t launch_decode(const Fwd& f) {
   auto ys = (const float*)(ws + y.ys);
   auto hw16 = (_Float16*)(ws + y.hw16);
   auto hsum = (_Float16*)(ws + y.hsum);  // hi plane [S][f/16], then lo plane
-  auto y_part = (float*)(ws + y.y_part);
   const int S = T * L.top_k;
-  const int nb = L.d_ff / QK;
-  const int nparts = std::min(kDownParts, nb);
-  const int nbp_max = (nb + nparts - 1) / nparts;
-  // stage 3 stages each part's routed activations and their sums
-  const size_t stage_bytes = (size_t)S * nbp_max * QK * 2 + (size_t)2 * S * nbp_max * 16 * 2;
-  const dim3 blk3(kW * 64);
+  // stage 3 stages the routed activations and their sums
+  const size_t stage_bytes = (size_t)S * L.d_ff * 2 + (size_t)2 * S * (L.d_ff / 16) * 2;
+  const dim3 blk3(kW3 * 64);
   if (stage_bytes <= kStage3Bytes)
-    DS4_LAUNCH(k_dec_stage3<true>, dim3(ndt * nparts), blk3, stage_bytes, f.st, L, T, nparts, ro.ndist, ro.distinct,
-               ro.tok_slot, hw16, hsum, ys, y_part, ctrl, ctrl_ints(L), maxd, f.y);
+    DS4_LAUNCH(k_dec_stage3<true>, dim3(ndt), blk3, stage_bytes, f.st, L, T, ro.ndist, ro.distinct, ro.tok_slot, hw16,
+               hsum, ys, ctrl, ctrl_ints(L), maxd, f.y);
   else
-    DS4_LAUNCH(k_dec_stage3<false>, dim3(ndt * nparts), blk3, 0, f.st, L, T, nparts, ro.ndist, ro.distinct,
-               ro.tok_slot, hw16, hsum, ys, y_part, ctrl, ctrl_ints(L), maxd, f.y);
+    DS4_LAUNCH(k_dec_stage3<false>, dim3(ndt), blk3, 0, f.st, L, T, ro.ndist, ro.distinct, ro.tok_slot, hw16, hsum,
+               ys, ctrl, ctrl_ints(L), maxd, f.y);
   return hipGetLastError();
 }
 

@@ -32,22 +32,18 @@ struct WsLayout {
   size_t plog;                        // decode: partial router logits [d/128][Tg][E]
   size_t ctrl;                        // decode: arrival counters (see ctrl_ints)
   size_t gu_part, ys;                 // decode: shared-expert gate/up half-K partial tiles, shared-expert output
-  size_t y_part;                      // decode: stage-3 partial output tiles [d/16][parts][16][Tg]
   size_t total;
 };
 
 WsLayout ws_layout(const ds4moe_layer& L, int64_t T, int mode);
 
 // Decode arrival counters at workspace offset 0: [0] router blocks, then one
-// per 16-row tile of the shared expert's gate/up (stage 1), and from
-// kCtrlDown one per 16-row output tile (stage 3).  Each counter is reset by
-// the block that sees the last arrival, and stage 3 also clears stage 1's, so
-// they are zero whenever no call is running; a new workspace must start
-// zeroed.
-constexpr int kCtrlDown = 1 + kMaxDim / 16;
-constexpr int kCtrlInts = kCtrlDown + kMaxDim / 16;
+// per 16-row tile of the shared expert's gate/up (stage 1).  Each counter is
+// reset by the block that sees the last arrival, and stage 3 clears them all
+// again, so they are zero whenever no call is running; a new workspace must
+// start zeroed.
+constexpr int kCtrlInts = 1 + kMaxDim / 16;
 inline int ctrl_ints(const ds4moe_layer& L) { return 1 + L.d_ff_shared / 16; }  // stage-1 counters
-constexpr int kDownParts = 4;  // stage 3 blocks per 16-row output tile (at most)
 
 // Everything a forward launch needs, resolved on the host.
 struct Fwd {

@@ -60,17 +60,6 @@ constexpr int ring_depth(int nf, int loads, bool lo, int ring, int rmax = 6) {
   return r;
 }
 
-// Work item of this block: blocks b < count are spread so that XCD x = b % 8
-// runs items [start_x, start_x + quota_x) in order; blocks >= count exit.
-__device__ inline bool xcd_item(int count, int& item) {
-  const int b = blockIdx.x;
-  if (b >= count) return false;
-  const int x = b & 7, i = b >> 3;
-  const int base = count >> 3, rem = count & 7;
-  item = x * base + min(x, rem) + i;
-  return true;
-}
-
 // Waits until at most N vector-memory operations of this wave are in flight.
 template <int N>
 __device__ inline void vm_wait() {
