@@ -39,12 +39,13 @@ MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA, vendor peak
 
 METRIC = "routed-MoE layer decode tok/s + % HBM peak; 2048-tok prefill tok/s + % MFMA"
 
-# HBM bytes per launch of the decode kernels, from two rocprofv3 counter
-# passes (FETCH_SIZE, WRITE_SIZE) scaled by the same counters on a 256 MiB
-# device copy; valid for the kernel sources with this hash only (see
-# profiles/decode1_hbm_traffic.md for the commands and the raw counts).
-TRAFFIC_SOURCE_HASH = "56008426c763f62d"
-TRAFFIC_BYTES = {"k_dec_stage1": 19.16e6, "k_dec_stage2": 44.05e6, "k_dec_stage3": 46.56e6}
+# HBM bytes per launch of the decode kernels, from rocprofv3 counter passes:
+# the L2's read requests to memory by size (the terms of FETCH_SIZE, each
+# 128-byte request at 128 bytes) and WRITE_SIZE, both checked against a
+# 256 MiB device copy (factor 1.000); valid for the kernel sources with this
+# hash only (profiles/decode1_hbm_traffic.md holds the commands and counts).
+TRAFFIC_SOURCE_HASH = "4fd25b16c260ac8e"
+TRAFFIC_BYTES = {"k_dec_stage1": 36.04e6, "k_dec_stage2": 43.64e6, "k_dec_stage3": 16.86e6}
 
 
 def kernel_source_hash():
@@ -250,7 +251,7 @@ def bench_prefill(args):
     torch.cuda.empty_cache()
     return dict(workload=f"prefill T={T}, Zipf(1.1)-shaped expert loads", tok_s=T / (ms * 1e-3), ms=ms,
                 flop=flop, tflops=tflops, mfma_frac=tflops / MFMA_F16_PEAK_TFLOPS,
-                kernels={k: dict(mean_us=v[0] / max(v[1], 1) * 1e3, launches=v[1]) for k, v in kern.items()})
+                kernels={k: dict(mean_us=v[0] / v[1] * 1e3, launches=v[1]) for k, v in kern.items() if v[1] > 0})
 
 
 def bench_cpu_oracle(seconds: float):
