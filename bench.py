@@ -68,16 +68,16 @@ def log(*a):
 def decode_bytes(cfg, n_distinct, T=1):
     """Algorithmic HBM bytes of one decode step and of each of its kernels:
     every weight byte the step needs read once, activations read/written once.
-    stage 1: router + shared gate and up; stage 2: routed gate/up + shared
-    down; stage 3: routed down."""
+    stage 1: router + shared gate and up; stage 2: routed gate/up; stage 3:
+    routed down + shared down."""
     from bit_quantized_routed_router_amd import ds4moe as D
     d, f, fs, E, k = cfg.d, cfg.f, cfg.fs, cfg.E, cfg.k
     cb = D.packed_bytes(D.FMT_CB2, f, d)
     qb = D.packed_bytes(D.FMT_Q2K, d, f)
     x_bytes = T * d * 2
     s1 = E * d * 2 + 2 * fs * d * 2 + x_bytes + T * fs * 2
-    s2 = n_distinct * 2 * cb + d * fs * 2 + x_bytes + T * fs * 2 + T * k * f * 2 + T * d * 4
-    s3 = n_distinct * qb + T * k * f * 2 + 2 * T * d * 4
+    s2 = n_distinct * 2 * cb + x_bytes + T * k * f * 2
+    s3 = n_distinct * qb + d * fs * 2 + T * fs * 2 + T * k * f * 2 + T * d * 4
     total = E * d * 2 + 3 * fs * d * 2 + n_distinct * (2 * cb + qb) + x_bytes + T * d * 4
     return dict(total=total, k_dec_stage1=s1, k_dec_stage2=s2, k_dec_stage3=s3)
 

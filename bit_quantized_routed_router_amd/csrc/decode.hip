@@ -10,13 +10,15 @@
 //                 last of the four forms h = silu(g) * u as binary16.  x is
 //                 read in its input type; the router chunk owners keep the
 //                 binary16 copy for stage 2.
-//   k_dec_stage2  the shared expert's down product ys (fp32), and for every
-//                 distinct selected expert its gate/up tiles: w * silu(G x) *
-//                 (U x) as binary16 plus the sums over each 16 rows (one Q2K
-//                 sub-block of the down input) as binary16 hi/lo.
-//   k_dec_stage3  one block per 16 output rows over every distinct expert's
-//                 down super-blocks; it writes y = ys + the routed terms and
-//                 clears the earlier stages' arrival counters.
+//   k_dec_stage2  for every distinct selected expert its gate/up tiles:
+//                 w * silu(G x) * (U x) as binary16 plus the sums over each
+//                 16 rows (one Q2K sub-block of the down input) as binary16
+//                 hi/lo.
+//   k_dec_stage3  one block per 16 output rows: the shared expert's down
+//                 product for those rows (an F16 stream that overlaps the
+//                 routed decode arithmetic) and every distinct expert's down
+//                 super-blocks; it writes y = ys + the routed terms and clears
+//                 the earlier stages' arrival counters.
 // Each distinct expert is read once per call however many tokens chose it,
 // and results do not depend on block scheduling.  Blocks hand stage-1
 // partials to the last arriver with device-coherent (sc1) stores and loads
@@ -393,52 +395,21 @@ __device__ inline half8_t cb2_apply(const Cb2Raw& R, uint32_t aux) {
   return as_half8(r);
 }
 
-// blocks [0, d/16): shared expert down, ys = Wsd h for 16 output rows (the
-// memory stream); then the routed gate/up tiles: (distinct expert, 16-row
-// tile), whose codebook decoding is the arithmetic.
+// One block per (distinct expert, 16-row tile) of the routed gate/up
+// products, whose codebook decoding is the arithmetic.
 template <bool LO, bool BL>
 __global__ __launch_bounds__(kW * 64) __attribute__((amdgpu_waves_per_eu(LO ? 2 : 4))) void k_dec_stage2(
     ds4moe_layer L, int T, RouteOut ro, const _Float16* __restrict__ xh, const _Float16* __restrict__ xl,
-    const _Float16* __restrict__ hs16, float* __restrict__ ys, _Float16* __restrict__ hw16,
-    _Float16* __restrict__ hsum) {
+    _Float16* __restrict__ hw16, _Float16* __restrict__ hsum) {
   __shared__ Stage2Lds lds;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = lane & 15, q = lane >> 4;
   const int tc = min(c, T - 1);
-  const int d = L.d_model, f = L.d_ff, fs = L.d_ff_shared, k = L.top_k;
-  const int nr = f / 16, nb = d / QK, ndt = d / 16;
+  const int d = L.d_model, f = L.d_ff, k = L.top_k;
+  const int nr = f / 16, nb = d / QK;
   float4_t ag = {0.f, 0.f, 0.f, 0.f}, au = ag;
-  if ((int)blockIdx.x < ndt) {  // ---------------- shared expert down: 16 output rows into ys
-    const int tile = blockIdx.x;
-    const uint16_t* rp = L.sh_down + (int64_t)(tile * 16 + c) * fs;
-    int ks0, ks1;
-    split_range(fs / 32, kW, wave, ks0, ks1);
-    const int st = stage_stride(fs);
-    const bool bls = T * fs <= kStageHalves;  // h of the group fits the stage
-    if (bls) dma_rows(hs16, fs, T, fs, lds.bh, st, wave, kW, lane);
-    constexpr int kBatch = 16;
-    half8_t a[kBatch];
-#pragma unroll
-    for (int j = 0; j < kBatch; ++j) a[j] = *(const half8_t*)(rp + max(min(ks0 + j, ks1 - 1), 0) * 32 + 8 * q);
-    if (bls) {
-      wait_all();
-      __syncthreads();
-    }
-    f16_steps<false, BL, kBatch>(rp, ks0, ks1, q, a,
-                                 [&](int kk, half8_t& bh, half8_t&) {
-                                   bh = bls ? *(const half8_t*)(lds.bh + tc * st + kk)
-                                            : *(const half8_t*)(hs16 + (int64_t)tc * fs + kk);
-                                 },
-                                 ag);
-    ag = reduce_waves<kW>(ag, lds.red, wave, lane);
-    if (wave == 0 && c < T) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) ys[(int64_t)c * d + tile * 16 + 4 * q + r] = ag[r];
-    }
-    return;
-  }
   // ---------------- routed gate/up: distinct expert i, 16-row tile
-  const int rel = blockIdx.x - ndt;
+  const int rel = blockIdx.x;
   const int i = rel / nr, tile = rel % nr;
   const int row0 = tile * 16;
   // phase 1: copies into LDS (activations, grid tables), independent of routing
@@ -662,33 +633,40 @@ __device__ inline void q2k_unit(const Q2kW& U, const Q2kA& A, uint32_t vmask, in
 constexpr int kW3 = 16;     // waves per stage-3 block: 4 per SIMD, few units each
 constexpr int kUnits3 = 3;  // units whose weight loads a wave keeps in flight
 
-// Block `tile`: output rows tile*16 .. tile*16+15 over every (distinct
-// expert, super-block) unit, so the whole sum stays in the block and it
-// writes y = ys + the routed terms itself.
+// Block `tile`: output rows tile*16 .. tile*16+15 of the shared expert's
+// down product and of every (distinct expert, super-block) unit, so the
+// whole sum stays in the block and it writes y = ys + the routed terms
+// itself.  The routed weights are requested first: their decode is the
+// arithmetic, and the shared expert's F16 rows stream in behind them.
 template <bool BL>
 __global__ __launch_bounds__(kW3 * 64) __attribute__((amdgpu_waves_per_eu(4))) void k_dec_stage3(
     ds4moe_layer L, int T, const int32_t* __restrict__ ndist, const int32_t* __restrict__ distinct,
     const int32_t* __restrict__ tok_slot, const _Float16* __restrict__ hw16, const _Float16* __restrict__ hsum,
-    const float* __restrict__ ys, int32_t* __restrict__ ctrl, int nctrl1, int maxd, float* __restrict__ y) {
+    const _Float16* __restrict__ hs16, int32_t* __restrict__ ctrl, int nctrl1, int maxd, float* __restrict__ y) {
   extern __shared__ __align__(16) unsigned char s_dyn[];  // staged activations when BL
   __shared__ float4_t s_red[kW3][64];
+  __shared__ float4_t s_red2[kW3][64];
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = lane & 15, q = lane >> 4;
-  const int d = L.d_model, f = L.d_ff, k = L.top_k;
+  const int d = L.d_model, f = L.d_ff, k = L.top_k, fs = L.d_ff_shared;
   const int tile = blockIdx.x, row0 = tile * 16;
   const int nb = f / QK, fs16 = f / 16;
   const size_t mb = (size_t)d * nb;
   const int S = T * k;
+  const int tc = min(c, T - 1);  // token feeding MFMA row c of the shared product
   const uint8_t* down = (const uint8_t*)L.down;
-  // staged: routed activations [S][f], their sums [2][S][f / 16]
+  // staged: routed activations [S][f], their sums [2][S][f / 16], the
+  // shared expert's activations [T][fs]
   _Float16* s_h = (_Float16*)s_dyn;
   _Float16* s_cs = s_h + (size_t)S * f;
+  _Float16* s_hs = s_cs + (size_t)2 * S * fs16;
   if (blockIdx.x == 0)
     for (int i = threadIdx.x; i < nctrl1; i += blockDim.x) ctrl[i] = 0;
   // copies of the activations into LDS; one barrier publishes them
   if (BL) {
     dma_rows(hw16, f, S, f, s_h, f, wave, kW3, lane);
     dma_rows(hsum, fs16, 2 * S, fs16, s_cs, fs16, wave, kW3, lane);
+    dma_rows(hs16, fs, T, fs, s_hs, fs, wave, kW3, lane);
   }
   // routing tables: expert ids by scalar loads, which do not wait for the
   // copies, so the first weight batch goes out while they are in flight
@@ -740,16 +718,22 @@ __global__ __launch_bounds__(kW3 * 64) __attribute__((amdgpu_waves_per_eu(4))) v
     }
   };
   load_batch(wave);
-  float ysv[4];  // the shared expert's output for this lane's tokens (read early)
-#pragma unroll
-  for (int r = 0; r < 4; ++r) ysv[r] = ys[(int64_t)min(4 * q + r, T - 1) * d + row0 + c];
 #pragma unroll
   for (int j = 0; j < kUnits3; ++j) asm volatile("" ::"v"(sj[j]));  // keeps these loads ahead of the barrier
-#pragma unroll
-  for (int r = 0; r < 4; ++r) asm volatile("" ::"v"(ysv[r]));
   asm volatile("" ::"s"(nd));
   wait_all();  // the copies (and the first batch)
   __syncthreads();
+  // the shared expert's down rows (this wave's K-steps) stream in while the
+  // routed units compute: issued after the barrier, so no wait above
+  // includes them
+  const uint16_t* srow = L.sh_down + (int64_t)(row0 + c) * fs;
+  int sk0, sk1;
+  split_range(fs / 32, kW3, wave, sk0, sk1);
+  constexpr int kBatchS = 4;
+  half8_t sa[kBatchS];
+#pragma unroll
+  for (int j = 0; j < kBatchS; ++j) sa[j] = *(const half8_t*)(srow + max(min(sk0 + j, sk1 - 1), 0) * 32 + 8 * q);
+  pin();
   float4_t acc = {0.f, 0.f, 0.f, 0.f};
   for (int u0 = wave; u0 < maxunits; u0 += kW3 * kUnits3) {
     if (u0 != wave) load_batch(u0);
@@ -773,11 +757,28 @@ __global__ __launch_bounds__(kW3 * 64) __attribute__((amdgpu_waves_per_eu(4))) v
       q2k_unit(W[j], A, vmask, q, acc);
     }
   }
-  acc = reduce_waves<kW3>(acc, s_red, wave, lane);  // lane (c, q): tokens 4q + r of row row0 + c
+  // shared expert, transposed like the routed units: lane (c, q) ends with
+  // tokens 4q..4q+3 of row row0 + c
+  float4_t accs = {0.f, 0.f, 0.f, 0.f};
+  {
+    auto getb = [&](int kk, half8_t& bh, half8_t&) {
+      bh = BL ? *(const half8_t*)(s_hs + tc * fs + kk) : *(const half8_t*)(hs16 + (int64_t)tc * fs + kk);
+    };
+    f16_steps<false, BL, kBatchS, decltype(getb), true>(srow, sk0, sk1, q, sa, getb, accs);
+  }
+  s_red[wave][lane] = acc;  // lane (c, q): tokens 4q + r of row row0 + c
+  s_red2[wave][lane] = accs;
+  __syncthreads();
   if (wave == 0) {
+    float4_t ar = s_red[0][lane], as = s_red2[0][lane];
+#pragma unroll
+    for (int w = 1; w < kW3; ++w) {
+      ar += s_red[w][lane];
+      as += s_red2[w][lane];
+    }
 #pragma unroll
     for (int r = 0; r < 4; ++r)
-      if (4 * q + r < T) y[(int64_t)(4 * q + r) * d + row0 + c] = ysv[r] + acc[r];
+      if (4 * q + r < T) y[(int64_t)(4 * q + r) * d + row0 + c] = as[r] + ar[r];
   }
 }
 
@@ -796,12 +797,10 @@ static void launch_stages12(const Fwd& f, int rblocks, int nsh, int maxd, int nr
   auto hs16 = (_Float16*)(ws + y.hs16);
   auto hw16 = (_Float16*)(ws + y.hw16);
   auto hsum = (_Float16*)(ws + y.hsum);
-  auto ys = (float*)(ws + y.ys);
-  const int ndt = L.d_model / 16;
   const dim3 blk(kW * 64);
   DS4_LAUNCH((k_dec_stage1<LO, BL>), dim3(rblocks + 4 * nsh), blk, 0, f.st, L, T, f.x, rblocks, plog, ro, xh, xl, gu,
              hs16, ctrl);
-  DS4_LAUNCH((k_dec_stage2<LO, BL>), dim3(ndt + maxd * nr), blk, 0, f.st, L, T, ro, xh, xl, hs16, ys, hw16, hsum);
+  DS4_LAUNCH((k_dec_stage2<LO, BL>), dim3(maxd * nr), blk, 0, f.st, L, T, ro, xh, xl, hw16, hsum);
 }
 
 hipError_t launch_decode(const Fwd& f) {
@@ -825,19 +824,21 @@ hipError_t launch_decode(const Fwd& f) {
     else launch_stages12<false, false>(f, rblocks, nsh, maxd, nr, ro);
   }
   auto ctrl = (int32_t*)(ws + y.ctrl);
-  auto ys = (const float*)(ws + y.ys);
+  auto hs16 = (const _Float16*)(ws + y.hs16);
   auto hw16 = (_Float16*)(ws + y.hw16);
   auto hsum = (_Float16*)(ws + y.hsum);  // hi plane [S][f/16], then lo plane
   const int S = T * L.top_k;
-  // stage 3 stages the routed activations and their sums
-  const size_t stage_bytes = (size_t)S * L.d_ff * 2 + (size_t)2 * S * (L.d_ff / 16) * 2;
+  // stage 3 stages the routed activations, their sums and the shared
+  // expert's activations
+  const size_t stage_bytes =
+      (size_t)S * L.d_ff * 2 + (size_t)2 * S * (L.d_ff / 16) * 2 + (size_t)T * L.d_ff_shared * 2;
   const dim3 blk3(kW3 * 64);
   if (stage_bytes <= kStage3Bytes)
     DS4_LAUNCH(k_dec_stage3<true>, dim3(ndt), blk3, stage_bytes, f.st, L, T, ro.ndist, ro.distinct, ro.tok_slot, hw16,
-               hsum, ys, ctrl, ctrl_ints(L), maxd, f.y);
+               hsum, hs16, ctrl, ctrl_ints(L), maxd, f.y);
   else
     DS4_LAUNCH(k_dec_stage3<false>, dim3(ndt), blk3, 0, f.st, L, T, ro.ndist, ro.distinct, ro.tok_slot, hw16, hsum,
-               ys, ctrl, ctrl_ints(L), maxd, f.y);
+               hs16, ctrl, ctrl_ints(L), maxd, f.y);
   return hipGetLastError();
 }
 
