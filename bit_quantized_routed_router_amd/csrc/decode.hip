@@ -146,67 +146,13 @@ __device__ inline void dma_pieces(const void* src, int n, void* dst, int wave, i
 
 __device__ inline void wait_all() { __builtin_amdgcn_s_waitcnt(0); }
 
-template <bool LO>
-struct XStage {  // activations x[T][k0 .. k0+K) in the input type -> binary16 hi/lo LDS rows, one piece per thread
-  u32x4_t u;
-  float4 a, b;
-  __device__ inline void load(const void* x, int d, int T, int k0, int K) {
-    const int n8 = K / 8;
-    const int i = min((int)threadIdx.x, T * n8 - 1);
-    const int64_t off = (int64_t)(i / n8) * d + k0 + 8 * (i % n8);
-    if (!LO) {
-      u = *(const u32x4_t*)((const uint16_t*)x + off);
-    } else {
-      const float4* src = (const float4*)((const float*)x + off);
-      a = src[0];
-      b = src[1];
-    }
-  }
-  __device__ inline void store(_Float16* sh, _Float16* sl, int T, int K) const {
-    const int n8 = K / 8, st = stage_stride(K);
-    const int i = threadIdx.x;
-    if (i >= T * n8) return;
-    float v[8];
-    if (!LO) {
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        v[2 * p] = __builtin_bit_cast(float, u[p] << 16);
-        v[2 * p + 1] = __builtin_bit_cast(float, u[p] & 0xFFFF0000u);
-      }
-    } else {
-      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-      v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-    }
-    half8_t h, l;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      h[e] = (_Float16)v[e];
-      l[e] = (_Float16)(v[e] - (float)h[e]);
-    }
-    *(half8_t*)(sh + (i / n8) * st + 8 * (i % n8)) = h;
-    if (LO) *(half8_t*)(sl + (i / n8) * st + 8 * (i % n8)) = l;
-  }
-};
-
 // ============================================================== stage 1
 struct Stage1Lds {
-  union {
-    RouteLds route;  // router blocks
-    struct {         // shared-gate blocks
-      _Float16 bh[kStageHalves + 16 * 8];
-      _Float16 bl[kStageHalves + 16 * 8];
-    } sh;
-  };
+  RouteLds route;
   float4_t red[kW][64];
   int last;
 };
 
-// Sleeps (of s_sleep 16, about 0.4 us each) a shared-expert block of stage 1
-// takes before it starts streaming, so the router's 2 MB go first and the
-// routing finish overlaps the shared expert instead of following it.  Waiting
-// on the router's arrival counter instead would have hundreds of blocks poll
-// one L2 line that the router blocks must update.
-constexpr int kSharedStartSleeps = 3;
 
 // inputs per router block: 512, or 256 when d is an odd multiple of 256
 __host__ __device__ inline int router_chunk(int d) { return d % 512 == 0 ? 512 : 256; }
@@ -236,14 +182,12 @@ __device__ inline void f16_steps(const uint16_t* __restrict__ rowp, int ks0, int
   }
 }
 
-// blocks [0, rblocks): router (expert tile, input chunk), chunk-major; then
-// four blocks per shared 16-row tile: the gate and up products over one K
-// half each.
-template <bool LO, bool BL>
+// One block per (expert tile, input chunk) of the router, chunk-major; the
+// last block to arrive finishes routing.
+template <bool LO>
 __global__ __launch_bounds__(kW * 64) void k_dec_stage1(ds4moe_layer L, int T, const void* __restrict__ x,
                                                         int rblocks, float* __restrict__ plog, RouteOut ro,
                                                         _Float16* __restrict__ xh, _Float16* __restrict__ xl,
-                                                        float* __restrict__ gu_part, _Float16* __restrict__ hs16,
                                                         int32_t* __restrict__ ctrl) {
   __shared__ Stage1Lds lds;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -251,7 +195,7 @@ __global__ __launch_bounds__(kW * 64) void k_dec_stage1(ds4moe_layer L, int T, c
   const int tc = min(c, T - 1);  // token feeding MFMA column c
   const int d = L.d_model, E = L.n_experts;
   float4_t acc = {0.f, 0.f, 0.f, 0.f};
-  if ((int)blockIdx.x < rblocks) {  // ---------------- router partial logits
+  {  // ---------------- router partial logits
     const int ntile = (E + 15) / 16;
     const int et = blockIdx.x % ntile, kc = blockIdx.x / ntile;
     const int e0 = et * 16;
@@ -293,45 +237,52 @@ __global__ __launch_bounds__(kW * 64) void k_dec_stage1(ds4moe_layer L, int T, c
     if (threadIdx.x == 0) lds.last = atomicAdd(&ctrl[0], 1) == rblocks - 1;  // cleared by stage 3
     __syncthreads();
     if (lds.last) route_finish_block<true>(lds.route, plog, d / ck, L.router_bias, E, L.top_k, T, ro);
-    return;
   }
-  // ---------------- shared expert gate and up: (tile, part), parts 0, 1 the
-  // gate's K halves and 2, 3 the up's; the last of a tile's four blocks to
-  // arrive forms h = silu(g) * u.
-  // Let the router stream go first (only orders traffic; results do not
-  // depend on it).
-  for (int it = 0; it < kSharedStartSleeps; ++it) __builtin_amdgcn_s_sleep(16);
-  const int sb = blockIdx.x - rblocks;
-  const int tile = sb >> 2, part = sb & 3, half = part & 1;
-  const int fs = L.d_ff_shared;
-  const uint16_t* rp = (part < 2 ? L.sh_gate : L.sh_up) + (int64_t)(tile * 16 + c) * d + half * (d / 2);
+}
+
+// Shared expert gate and up, block sb = (tile, part): part 0 is the gate,
+// part 1 the up product of 16 rows over the whole input; the second of a
+// tile's two blocks to arrive forms h = silu(g) * u as binary16.  x comes as
+// the binary16 hi/lo copy (xh, xl) that the router blocks wrote; bhs/bls:
+// LDS staging of it when BL, red: the wave reduction, last: one LDS int.
+template <bool LO, bool BL>
+__device__ inline void shared_gateup_block(const ds4moe_layer& L, int T, const _Float16* __restrict__ xh,
+                                           const _Float16* __restrict__ xl, int sb, float* __restrict__ gu_part,
+                                           _Float16* __restrict__ hs16, int32_t* __restrict__ ctrl, _Float16* bhs,
+                                           _Float16* bls, float4_t (*red)[64], int& last) {
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c = lane & 15, q = lane >> 4;
+  const int tc = min(c, T - 1);  // token feeding MFMA column c
+  const int d = L.d_model, fs = L.d_ff_shared;
+  float4_t acc = {0.f, 0.f, 0.f, 0.f};
+  const int tile = sb >> 1, part = sb & 1;
+  const uint16_t* rp = (part == 0 ? L.sh_gate : L.sh_up) + (int64_t)(tile * 16 + c) * d;
   int ks0, ks1;
-  split_range(d / 64, kW, wave, ks0, ks1);
-  const int kb = half * (d / 2), st = stage_stride(d / 2);
+  split_range(d / 32, kW, wave, ks0, ks1);
+  const int st = stage_stride(d);
+  if (BL) dma_rows(xh, d, T, d, bhs, st, wave, kW, lane);
+  if (BL && LO) dma_rows(xl, d, T, d, bls, st, wave, kW, lane);
   constexpr int kBatch = 16;
-  XStage<LO> xs;
-  if (BL) xs.load(x, d, T, kb, d / 2);  // one piece per thread: T * d / 2 <= 8 * blockDim
-  pin();
   half8_t a[kBatch];
 #pragma unroll
   for (int j = 0; j < kBatch; ++j) a[j] = *(const half8_t*)(rp + max(min(ks0 + j, ks1 - 1), 0) * 32 + 8 * q);
-  pin();
   if (BL) {
-    xs.store(lds.sh.bh, lds.sh.bl, T, d / 2);
+    wait_all();
     __syncthreads();
   }
   f16_steps<LO, BL, kBatch>(rp, ks0, ks1, q, a,
                             [&](int kk, half8_t& bh, half8_t& bl) {
                               if (BL) {
-                                bh = *(const half8_t*)(lds.sh.bh + tc * st + kk);
-                                if (LO) bl = *(const half8_t*)(lds.sh.bl + tc * st + kk);
+                                bh = *(const half8_t*)(bhs + tc * st + kk);
+                                if (LO) bl = *(const half8_t*)(bls + tc * st + kk);
                               } else {
-                                load_x8<LO>(x, d, tc, kb + kk, bh, bl);
+                                bh = *(const half8_t*)(xh + (int64_t)tc * d + kk);
+                                if (LO) bl = *(const half8_t*)(xl + (int64_t)tc * d + kk);
                               }
                             },
                             acc);
-  acc = reduce_waves<kW>(acc, lds.red, wave, lane);
-  float* tp = gu_part + (size_t)tile * 4 * 16 * T;  // [part][row][t]
+  acc = reduce_waves<kW>(acc, red, wave, lane);
+  float* tp = gu_part + (size_t)tile * 2 * 16 * T;  // [part][row][t]
   if (wave == 0) {
     if (c < T) {
 #pragma unroll
@@ -340,18 +291,17 @@ __global__ __launch_bounds__(kW * 64) void k_dec_stage1(ds4moe_layer L, int T, c
     wait_stores();
   }
   __syncthreads();
-  if (threadIdx.x == 0) lds.last = atomicAdd(&ctrl[1 + tile], 1) == 3;
+  if (threadIdx.x == 0) last = atomicAdd(&ctrl[1 + tile], 1) == 1;
   __syncthreads();
-  if (!lds.last || wave != 0) return;
+  if (!last || wave != 0) return;
   if (c < T) {
-    float pv[4][4];  // [part][r]: every coherent load in flight before the first use
+    float pv[2][4];  // [part][r]: every coherent load in flight before the first use
 #pragma unroll
-    for (int pt = 0; pt < 4; ++pt)
+    for (int pt = 0; pt < 2; ++pt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) pv[pt][r] = ld_coh(&tp[((size_t)pt * 16 + 4 * q + r) * T + c]);
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-      hs16[(int64_t)c * fs + tile * 16 + 4 * q + r] = (_Float16)(silu(pv[0][r] + pv[1][r]) * (pv[2][r] + pv[3][r]));
+    for (int r = 0; r < 4; ++r) hs16[(int64_t)c * fs + tile * 16 + 4 * q + r] = (_Float16)(silu(pv[0][r]) * pv[1][r]);
   }
   if (lane == 0) ctrl[1 + tile] = 0;
 }
@@ -395,13 +345,21 @@ __device__ inline half8_t cb2_apply(const Cb2Raw& R, uint32_t aux) {
   return as_half8(r);
 }
 
-// One block per (distinct expert, 16-row tile) of the routed gate/up
-// products, whose codebook decoding is the arithmetic.
+// Blocks [0, maxd * f/16): one per (distinct expert, 16-row tile) of the
+// routed gate/up products, whose codebook decoding is the arithmetic; then
+// two per 16-row tile of the shared expert (gate, up), an F16 stream
+// dispatched behind the routed blocks.
 template <bool LO, bool BL>
 __global__ __launch_bounds__(kW * 64) __attribute__((amdgpu_waves_per_eu(LO ? 2 : 4))) void k_dec_stage2(
-    ds4moe_layer L, int T, RouteOut ro, const _Float16* __restrict__ xh, const _Float16* __restrict__ xl,
-    _Float16* __restrict__ hw16, _Float16* __restrict__ hsum) {
+    ds4moe_layer L, int T, RouteOut ro, const _Float16* __restrict__ xh,
+    const _Float16* __restrict__ xl, _Float16* __restrict__ hw16, _Float16* __restrict__ hsum, int rtiles,
+    float* __restrict__ gu_part, _Float16* __restrict__ hs16, int32_t* __restrict__ ctrl) {
   __shared__ Stage2Lds lds;
+  if ((int)blockIdx.x >= rtiles) {
+    shared_gateup_block<LO, BL>(L, T, xh, xl, blockIdx.x - rtiles, gu_part, hs16, ctrl, lds.bh, lds.bl, lds.red,
+                                lds.last);
+    return;
+  }
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = lane & 15, q = lane >> 4;
   const int tc = min(c, T - 1);
@@ -798,9 +756,9 @@ static void launch_stages12(const Fwd& f, int rblocks, int nsh, int maxd, int nr
   auto hw16 = (_Float16*)(ws + y.hw16);
   auto hsum = (_Float16*)(ws + y.hsum);
   const dim3 blk(kW * 64);
-  DS4_LAUNCH((k_dec_stage1<LO, BL>), dim3(rblocks + 4 * nsh), blk, 0, f.st, L, T, f.x, rblocks, plog, ro, xh, xl, gu,
-             hs16, ctrl);
-  DS4_LAUNCH((k_dec_stage2<LO, BL>), dim3(maxd * nr), blk, 0, f.st, L, T, ro, xh, xl, hw16, hsum);
+  DS4_LAUNCH((k_dec_stage1<LO>), dim3(rblocks), blk, 0, f.st, L, T, f.x, rblocks, plog, ro, xh, xl, ctrl);
+  DS4_LAUNCH((k_dec_stage2<LO, BL>), dim3(maxd * nr + 2 * nsh), blk, 0, f.st, L, T, ro, xh, xl, hw16, hsum,
+             maxd * nr, gu, hs16, ctrl);
 }
 
 hipError_t launch_decode(const Fwd& f) {

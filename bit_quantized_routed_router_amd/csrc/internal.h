@@ -31,7 +31,7 @@ struct WsLayout {
   size_t tiles, stiles, ntiles;       // prefill: (expert, run) work lists of large and small tiles, their counts
   size_t plog;                        // decode: partial router logits [d/128][Tg][E]
   size_t ctrl;                        // decode: arrival counters (see ctrl_ints)
-  size_t gu_part, ys;                 // decode: shared-expert gate/up half-K partial tiles, shared-expert output
+  size_t gu_part;                     // decode: shared-expert gate and up tiles handed to the tile's last block
   size_t total;
 };
 
@@ -43,7 +43,7 @@ WsLayout ws_layout(const ds4moe_layer& L, int64_t T, int mode);
 // again, so they are zero whenever no call is running; a new workspace must
 // start zeroed.
 constexpr int kCtrlInts = 1 + kMaxDim / 16;
-inline int ctrl_ints(const ds4moe_layer& L) { return 1 + L.d_ff_shared / 16; }  // stage-1 counters
+inline int ctrl_ints(const ds4moe_layer& L) { return 1 + L.d_ff_shared / 16; }  // router + shared tiles
 
 // Everything a forward launch needs, resolved on the host.
 struct Fwd {

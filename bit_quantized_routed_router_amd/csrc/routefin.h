@@ -244,10 +244,21 @@ __device__ inline void route_finish_block(RouteLds& R, const float* __restrict__
   for (int i = threadIdx.x; i < T * E; i += nthr) {
     const int e = i % E;
     float a = 0.0f;
-#pragma unroll 32
-    for (int p = 0; p < nparts; ++p) {
-      const float* src = plog + (int64_t)p * T * E + i;
-      a += COH ? __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : *src;
+    // 16 partials at a time, all loads in flight before the first add (a
+    // loop that waits for each load would pay one memory round trip per
+    // partial); summed in ascending p
+    for (int p0 = 0; p0 < nparts; p0 += 16) {
+      float v[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        if (p0 + j < nparts) {
+          const float* src = plog + (int64_t)(p0 + j) * T * E + i;
+          v[j] = COH ? __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : *src;
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        if (p0 + j < nparts) a += v[j];
     }
     logits[i] = bias ? a + bias[e] : a;
   }
