@@ -49,6 +49,7 @@ __constant__ GridTables c_dec_tables = make_grid_tables();
 constexpr int kW = 4;           // waves per block
 constexpr int kStageHalves = 4096;        // binary16 activations a stage-1/2 block may stage (per hi/lo part)
 constexpr size_t kStage3Bytes = 32 * 1024;  // stage 3 LDS for staged activations and sums
+constexpr size_t kStage3OneBytes = 40 * 1024;  // the same for the one-token form
 
 __device__ inline int cb2_boff(int q, int s) { return 32 * (2 * q + (s >> 2)) + 8 * (s & 3); }
 __device__ inline int q2k_boff(int q, int s) { return 16 * (4 * q + (s >> 1)) + 8 * (s & 1); }
@@ -740,6 +741,192 @@ __global__ __launch_bounds__(kW3 * 64) __attribute__((amdgpu_waves_per_eu(4))) v
   }
 }
 
+// ============================================================== stage 3, one token
+// With one token the MFMA's 16 token columns would carry one useful column,
+// so the routed down product runs on v_dot2_f32_f16 instead, each lane
+// over its own row.  Codes become binary16 without a per-weight rescale: a
+// three-input bit operation puts the two codes of a pair (codes i and i + 8
+// of a sub-block, the same bits of its two 16-bit halves) into the low
+// mantissa bits under an exponent that gives them unit weight, so each half
+// reads base + q exactly, base being 64, 16 or 4 for mantissa bit 4, 6 or 8.
+// The dot product of a sub-block's 8 pairs with (h_i, h_{i+8}) is then
+// sum_k q_k h_k + OFF, OFF = sum_k base_k h_k, and the sub-block adds
+// d s (dot - OFF) - dmin m HS with HS = sum_k h_k.  OFF and HS come from the
+// same binary16 h, once per block.
+//
+// Pair i of sub-block u32 u (codes at bits 2i and 2i + 16) is taken from
+// u << 4, u >> 2 or u >> 8, which moves it to mantissa bit 4, 6 or 8:
+//   pairs 0, 3, 6 -> bit 4 (base 64), 1, 4, 7 -> bit 6 (base 16), 2, 5 -> bit 8 (base 4).
+__host__ __device__ constexpr int q2k_pair_base(int i) { return i % 3 == 0 ? 64 : (i % 3 == 1 ? 16 : 4); }
+
+__device__ inline void q2k_pairs_unit_weight(uint32_t u, uint32_t (&w)[8]) {
+  const uint32_t a = u << 4, b = u >> 2, c = u >> 8;
+  // (x & mask) | magic: 0x5400 = 64, 0x4C00 = 16, 0x4400 = 4 (binary16)
+  w[0] = __builtin_amdgcn_bitop3_b32(a, 0x00300030u, 0x54005400u, 0xEA);
+  w[1] = __builtin_amdgcn_bitop3_b32(a, 0x00C000C0u, 0x4C004C00u, 0xEA);
+  w[2] = __builtin_amdgcn_bitop3_b32(a, 0x03000300u, 0x44004400u, 0xEA);
+  w[3] = __builtin_amdgcn_bitop3_b32(b, 0x00300030u, 0x54005400u, 0xEA);
+  w[4] = __builtin_amdgcn_bitop3_b32(b, 0x00C000C0u, 0x4C004C00u, 0xEA);
+  w[5] = __builtin_amdgcn_bitop3_b32(b, 0x03000300u, 0x44004400u, 0xEA);
+  w[6] = __builtin_amdgcn_bitop3_b32(c, 0x00300030u, 0x54005400u, 0xEA);
+  w[7] = __builtin_amdgcn_bitop3_b32(c, 0x00C000C0u, 0x4C004C00u, 0xEA);
+}
+
+__device__ inline float dot2(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2(as_half2(a), as_half2(b), c, false);
+}
+
+// Block `tile` (16 waves): output rows tile*16 .. +15 of token 0.  Lane
+// (c, q) works on row row0 + c, sub-blocks 4q .. 4q + 3 of each unit's
+// super-block.  LDS: h as pairs [S][f/16][8] (u32), OFF and HS [S][f/16]
+// (fp32), the shared expert's h [fs] (binary16).
+__global__ __launch_bounds__(kW3 * 64) __attribute__((amdgpu_waves_per_eu(4))) void k_dec_stage3_one(
+    ds4moe_layer L, const int32_t* __restrict__ ndist, const int32_t* __restrict__ distinct,
+    const int32_t* __restrict__ tok_slot, const _Float16* __restrict__ hw16, const _Float16* __restrict__ hs16,
+    int32_t* __restrict__ ctrl, int nctrl1, int maxd, float* __restrict__ y) {
+  extern __shared__ __align__(16) unsigned char s_dyn[];
+  __shared__ float s_row[kW3][16];
+  __shared__ float4_t s_red2[kW3][64];
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c = lane & 15, q = lane >> 4;
+  const int d = L.d_model, f = L.d_ff, k = L.top_k, fs = L.d_ff_shared;
+  const int tile = blockIdx.x, row0 = tile * 16;
+  const int nb = f / QK, nsb = f / 16;
+  const size_t mb = (size_t)d * nb;
+  const int S = k;  // one token: k slots
+  uint32_t* s_pair = (uint32_t*)s_dyn;                   // [S][nsb][8]
+  float* s_off = (float*)(s_pair + (size_t)S * nsb * 8);  // [S][nsb]
+  float* s_hs = s_off + (size_t)S * nsb;                  // [S][nsb]
+  _Float16* s_sh = (_Float16*)(s_hs + (size_t)S * nsb);   // [fs]
+  if (blockIdx.x == 0)
+    for (int i = threadIdx.x; i < nctrl1; i += blockDim.x) ctrl[i] = 0;
+  const uint8_t* down = (const uint8_t*)L.down;
+  const int nd = min(ld_uniform(ndist), maxd);
+  const int maxunits = maxd * nb, nunits = nd * nb;
+  // units u = (expert slot u / nb, super-block u % nb); wave w takes
+  // u = w, w + kW3, ... in batches of kUnits3
+  struct W1 {
+    u32x4_t codes;  // sub-blocks 4q .. 4q + 3 of the lane's row
+    uint32_t sc4;   // their scale/min bytes
+    uint32_t sup;   // (d, dmin) of the lane's row
+  };
+  W1 W[kUnits3];
+  int ib[kUnits3][2];  // per unit: slot of the token for its expert, super-block
+  const uint32_t o_codes = (uint32_t)((size_t)(row0 + c) * nb * 64 + 16 * q);
+  const uint32_t o_sc = (uint32_t)(mb * 64 + (size_t)(row0 + c) * nb * 16 + 4 * q);
+  const uint32_t o_sup = (uint32_t)(mb * 80 + (size_t)(row0 + c) * nb * 4);
+  auto load_batch = [&](int u0) {
+    int ej[kUnits3];
+#pragma unroll
+    for (int j = 0; j < kUnits3; ++j) {  // units past the end repeat the last one
+      const int u = min(u0 + j * kW3, maxunits - 1);
+      const int i = u / nb;  // distinct expert
+      ib[j][1] = u - i * nb;
+      ej[j] = ld_uniform(distinct + i);  // all ids and slots in flight before the first address needs one
+      ib[j][0] = clamp_index(ld_uniform(tok_slot + i * kDecodeGroup), S);
+    }
+    pin();
+#pragma unroll
+    for (int j = 0; j < kUnits3; ++j) {
+      const uint8_t* base = down + (size_t)clamp_index(ej[j], L.n_experts) * mb * 84;
+      const int b = ib[j][1];
+      W[j].codes = __builtin_nontemporal_load((const u32x4_t*)(base + o_codes + b * 64));
+      W[j].sc4 = *(const uint32_t*)(base + o_sc + b * 16);
+      W[j].sup = *(const uint32_t*)(base + o_sup + b * 4);
+    }
+  };
+  load_batch(wave);
+  // staging: the routed h as pairs with their OFF and HS sums, one
+  // (slot, sub-block) per thread; the shared expert's h by copy
+  dma_rows(hs16, fs, 1, fs, s_sh, fs, wave, kW3, lane);
+  for (int t = threadIdx.x; t < S * nsb; t += blockDim.x) {
+    const u32x4_t lo = *(const u32x4_t*)(hw16 + (size_t)t * 16), hi = *(const u32x4_t*)(hw16 + (size_t)t * 16 + 8);
+    const half8_t hl = as_half8(lo), hh = as_half8(hi);
+    float off = 0.0f, hs = 0.0f;
+    u32x4_t p0, p1;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const half2_t pr = {hl[i], hh[i]};
+      if (i < 4) p0[i] = as_u32(pr); else p1[i - 4] = as_u32(pr);
+      off += (float)q2k_pair_base(i) * ((float)hl[i] + (float)hh[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) hs += (float)hl[i];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) hs += (float)hh[i];
+    *(u32x4_t*)(s_pair + (size_t)t * 8) = p0;
+    *(u32x4_t*)(s_pair + (size_t)t * 8 + 4) = p1;
+    s_off[t] = off;
+    s_hs[t] = hs;
+  }
+#pragma unroll
+  for (int j = 0; j < kUnits3; ++j) asm volatile("" ::"v"(W[j].sup));  // keeps these loads ahead of the barrier
+  wait_all();
+  __syncthreads();
+  // the shared expert's down rows stream in while the routed units compute
+  const uint16_t* srow = L.sh_down + (int64_t)(row0 + c) * fs;
+  int sk0, sk1;
+  split_range(fs / 32, kW3, wave, sk0, sk1);
+  constexpr int kBatchS = 4;
+  half8_t sa[kBatchS];
+#pragma unroll
+  for (int j = 0; j < kBatchS; ++j) sa[j] = *(const half8_t*)(srow + max(min(sk0 + j, sk1 - 1), 0) * 32 + 8 * q);
+  pin();
+  float yr = 0.0f;  // row row0 + c, this lane's sub-blocks
+  for (int u0 = wave; u0 < maxunits; u0 += kW3 * kUnits3) {
+    if (u0 != wave) load_batch(u0);
+    pin();
+#pragma unroll
+    for (int j = 0; j < kUnits3; ++j) {
+      if (u0 + j * kW3 >= nunits) continue;  // wave-uniform
+      const int sbase = ib[j][0] * nsb + ib[j][1] * 16 + 4 * q;  // (slot, first sub-block) of the lane
+      const float4_t off4 = *(const float4_t*)(s_off + sbase), hs4 = *(const float4_t*)(s_hs + sbase);
+      float as = 0.0f, am = 0.0f;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const u32x4_t h0 = *(const u32x4_t*)(s_pair + (size_t)(sbase + jj) * 8);
+        const u32x4_t h1 = *(const u32x4_t*)(s_pair + (size_t)(sbase + jj) * 8 + 4);
+        uint32_t w[8];
+        q2k_pairs_unit_weight(W[j].codes[jj], w);
+        float acc = dot2(w[0], h0.x, 0.0f);
+        acc = dot2(w[1], h0.y, acc);
+        acc = dot2(w[2], h0.z, acc);
+        acc = dot2(w[3], h0.w, acc);
+        acc = dot2(w[4], h1.x, acc);
+        acc = dot2(w[5], h1.y, acc);
+        acc = dot2(w[6], h1.z, acc);
+        acc = dot2(w[7], h1.w, acc);
+        const uint32_t sm = (W[j].sc4 >> (8 * jj)) & 0xFFu;
+        as += (float)(sm & 15u) * (acc - off4[jj]);
+        am += (float)(sm >> 4) * hs4[jj];
+      }
+      const float dd = h2f((uint16_t)(W[j].sup & 0xFFFFu)), dm = h2f((uint16_t)(W[j].sup >> 16));
+      yr += dd * as - dm * am;
+    }
+  }
+  // shared expert, transposed MFMA: lane (c, 0) ends with token 0 of row c
+  float4_t accs = {0.f, 0.f, 0.f, 0.f};
+  {
+    auto getb = [&](int kk, half8_t& bh, half8_t&) { bh = *(const half8_t*)(s_sh + kk); };
+    f16_steps<false, true, kBatchS, decltype(getb), true>(srow, sk0, sk1, q, sa, getb, accs);
+  }
+  // row sums over the four lane groups, then over the waves
+  yr += __shfl_xor(yr, 16);
+  yr += __shfl_xor(yr, 32);
+  if (q == 0) s_row[wave][c] = yr;
+  s_red2[wave][lane] = accs;
+  __syncthreads();
+  if (wave == 0 && q == 0) {
+    float ar = s_row[0][c], as = s_red2[0][lane][0];
+#pragma unroll
+    for (int w = 1; w < kW3; ++w) {
+      ar += s_row[w][c];
+      as += s_red2[w][lane][0];
+    }
+    y[row0 + c] = as + ar;
+  }
+}
+
 // ============================================================== launcher
 template <bool LO, bool BL>
 static void launch_stages12(const Fwd& f, int rblocks, int nsh, int maxd, int nr, const RouteOut& ro) {
@@ -791,6 +978,14 @@ hipError_t launch_decode(const Fwd& f) {
   const size_t stage_bytes =
       (size_t)S * L.d_ff * 2 + (size_t)2 * S * (L.d_ff / 16) * 2 + (size_t)T * L.d_ff_shared * 2;
   const dim3 blk3(kW3 * 64);
+  // one token: the dot-product form (pairs, OFF and HS sums, shared h)
+  const size_t one_bytes = (size_t)L.top_k * L.d_ff * 2 + (size_t)2 * L.top_k * (L.d_ff / 16) * 4 +
+                           (size_t)L.d_ff_shared * 2;
+  if (T == 1 && one_bytes <= kStage3OneBytes) {
+    DS4_LAUNCH(k_dec_stage3_one, dim3(ndt), blk3, one_bytes, f.st, L, ro.ndist, ro.distinct, ro.tok_slot, hw16,
+               hs16, ctrl, ctrl_ints(L), maxd, f.y);
+    return hipGetLastError();
+  }
   if (stage_bytes <= kStage3Bytes)
     DS4_LAUNCH(k_dec_stage3<true>, dim3(ndt), blk3, stage_bytes, f.st, L, T, ro.ndist, ro.distinct, ro.tok_slot, hw16,
                hsum, hs16, ctrl, ctrl_ints(L), maxd, f.y);
