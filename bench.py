@@ -44,8 +44,8 @@ METRIC = "routed-MoE layer decode tok/s + % HBM peak; 2048-tok prefill tok/s + %
 # 128-byte request at 128 bytes) and WRITE_SIZE, both checked against a
 # 256 MiB device copy (factor 1.000); valid for the kernel sources with this
 # hash only (profiles/decode1_hbm_traffic.md holds the commands and counts).
-TRAFFIC_SOURCE_HASH = "4fd25b16c260ac8e"
-TRAFFIC_BYTES = {"k_dec_stage1": 36.04e6, "k_dec_stage2": 43.64e6, "k_dec_stage3": 16.86e6}
+TRAFFIC_SOURCE_HASH = "97c7c1589ee82fd7"
+TRAFFIC_BYTES = {"k_dec_stage1": 2.26e6, "k_dec_stage2": 60.21e6, "k_dec_stage3": 33.61e6}
 
 
 def kernel_source_hash():
@@ -68,15 +68,15 @@ def log(*a):
 def decode_bytes(cfg, n_distinct, T=1):
     """Algorithmic HBM bytes of one decode step and of each of its kernels:
     every weight byte the step needs read once, activations read/written once.
-    stage 1: router + shared gate and up; stage 2: routed gate/up; stage 3:
+    stage 1: router; stage 2: routed gate/up + shared gate and up; stage 3:
     routed down + shared down."""
     from bit_quantized_routed_router_amd import ds4moe as D
     d, f, fs, E, k = cfg.d, cfg.f, cfg.fs, cfg.E, cfg.k
     cb = D.packed_bytes(D.FMT_CB2, f, d)
     qb = D.packed_bytes(D.FMT_Q2K, d, f)
     x_bytes = T * d * 2
-    s1 = E * d * 2 + 2 * fs * d * 2 + x_bytes + T * fs * 2
-    s2 = n_distinct * 2 * cb + x_bytes + T * k * f * 2
+    s1 = E * d * 2 + x_bytes
+    s2 = n_distinct * 2 * cb + 2 * fs * d * 2 + T * d * 2 + T * k * f * 2 + T * fs * 2
     s3 = n_distinct * qb + d * fs * 2 + T * fs * 2 + T * k * f * 2 + T * d * 4
     total = E * d * 2 + 3 * fs * d * 2 + n_distinct * (2 * cb + qb) + x_bytes + T * d * 4
     return dict(total=total, k_dec_stage1=s1, k_dec_stage2=s2, k_dec_stage3=s3)
@@ -192,7 +192,9 @@ def bench_decode(args):
     nb = decode_bytes(cfg, cfg.k, T=1)
     per = {}
     for name in ("k_dec_stage1", "k_dec_stage2", "k_dec_stage3"):
-        hits = [v for k2, v in kern.items() if k2 == name or k2.startswith(name + "<")]
+        # a stage's kernel is named for it, with template arguments or a
+        # variant suffix (k_dec_stage3_one: the one-token form)
+        hits = [v for k2, v in kern.items() if k2.split("<")[0] in (name, name + "_one")]
         ms = sum(v[0] for v in hits)
         cnt = sum(v[1] for v in hits)
         if cnt:
