@@ -44,20 +44,27 @@ METRIC = "routed-MoE layer decode tok/s + % HBM peak; 2048-tok prefill tok/s + %
 # 128-byte request at 128 bytes) and WRITE_SIZE, both checked against a
 # 256 MiB device copy (factor 1.000); valid for the kernel sources with this
 # hash only (profiles/decode1_hbm_traffic.md holds the commands and counts).
-TRAFFIC_SOURCE_HASH = "97c7c1589ee82fd7"
+TRAFFIC_SOURCE_HASH = "3fd64b5d605c414b"
 TRAFFIC_BYTES = {"k_dec_stage1": 2.26e6, "k_dec_stage2": 60.21e6, "k_dec_stage3": 33.61e6}
 
 
-def kernel_source_hash():
-    """sha256 over the library's kernel sources (name + bytes, sorted)."""
+def kernel_source_hash(csrc=None):
+    """sha256 over the library's sources (name + code, sorted by name), with
+    comments and whitespace removed, so that only a change to the code itself
+    invalidates counters taken earlier."""
     import glob
     import hashlib
+    import re
+    csrc = csrc or os.path.join(ROOT, "bit_quantized_routed_router_amd", "csrc")
     h = hashlib.sha256()
-    for f in sorted(glob.glob(os.path.join(ROOT, "bit_quantized_routed_router_amd", "csrc", "*"))):
+    for f in sorted(glob.glob(os.path.join(csrc, "*"))):
         if f.endswith((".hip", ".h", ".cpp")):
+            with open(f, encoding="utf-8") as fh:
+                code = fh.read()
+            code = re.sub(r"/\*.*?\*/", " ", code, flags=re.S)
+            code = re.sub(r"//[^\n]*", " ", code)
             h.update(os.path.basename(f).encode())
-            with open(f, "rb") as fh:
-                h.update(fh.read())
+            h.update(" ".join(code.split()).encode())
     return h.hexdigest()[:16]
 
 

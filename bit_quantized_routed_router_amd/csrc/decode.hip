@@ -1,28 +1,29 @@
 // Batched decode (T <= 16 tokens per group): the whole layer in three
 // streaming kernels whose 16 MFMA columns are the group's tokens.  Routing
-// gates the routed experts, so the F16 shared expert (independent of it)
-// fills the first two stages beside the routing chain:
+// gates the routed experts; the F16 shared expert (independent of it)
+// streams beside the routed work of stages 2 and 3:
 //
-//   k_dec_stage1  router partial logits per input chunk (the last router
-//                 block to arrive finishes routing: top-k, gate weights,
-//                 grouping) and the shared expert's gate and up products,
-//                 four blocks per 16 rows (gate or up, half of K each); the
-//                 last of the four forms h = silu(g) * u as binary16.  x is
-//                 read in its input type; the router chunk owners keep the
-//                 binary16 copy for stage 2.
+//   k_dec_stage1  router partial logits per input chunk; the last router
+//                 block to arrive finishes routing (top-k, gate weights,
+//                 grouping).  x is read in its input type; the router chunk
+//                 owners keep the binary16 copy for stage 2.
 //   k_dec_stage2  for every distinct selected expert its gate/up tiles:
 //                 w * silu(G x) * (U x) as binary16 plus the sums over each
 //                 16 rows (one Q2K sub-block of the down input) as binary16
-//                 hi/lo.
+//                 hi/lo; behind them the shared expert's gate and up, two
+//                 blocks per 16 rows, the second of which forms
+//                 h = silu(g) * u as binary16.
 //   k_dec_stage3  one block per 16 output rows: the shared expert's down
 //                 product for those rows (an F16 stream that overlaps the
 //                 routed decode arithmetic) and every distinct expert's down
 //                 super-blocks; it writes y = ys + the routed terms and clears
-//                 the earlier stages' arrival counters.
+//                 the earlier stages' arrival counters.  One token takes the
+//                 dot-product form k_dec_stage3_one.
 // Each distinct expert is read once per call however many tokens chose it,
-// and results do not depend on block scheduling.  Blocks hand stage-1
-// partials to the last arriver with device-coherent (sc1) stores and loads
-// around an atomic counter, which needs no L2 write-back.
+// and results do not depend on block scheduling.  Blocks hand partials to
+// the last arriver (router logits, shared gate/up tiles) with
+// device-coherent (sc1) stores and loads around an atomic counter, which
+// needs no L2 write-back.
 //
 // Operands.  Packed weights: every lane owns a contiguous 16-byte piece of
 // its row's super-block and feeds those weights to consecutive MFMA steps

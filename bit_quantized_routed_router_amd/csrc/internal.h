@@ -37,8 +37,8 @@ struct WsLayout {
 
 WsLayout ws_layout(const ds4moe_layer& L, int64_t T, int mode);
 
-// Decode arrival counters at workspace offset 0: [0] router blocks, then one
-// per 16-row tile of the shared expert's gate/up (stage 1).  Each counter is
+// Decode arrival counters at workspace offset 0: [0] router blocks (stage 1),
+// then one per 16-row tile of the shared expert's gate/up (stage 2).  Each counter is
 // reset by the block that sees the last arrival, and stage 3 clears them all
 // again, so they are zero whenever no call is running; a new workspace must
 // start zeroed.
