@@ -19,6 +19,7 @@ shared expert, bf16 activations -- in layer-tokens per second.
     around each launch during an eager pass over the same steps;
   * "prefill" times ds4moe_forward_prefill on a 2048-token chunk with
     Zipf-like expert loads against the dense fp16 MFMA peak;
+  * "decode16" times the 16-token batched decode (about 60 distinct experts);
   * "cpu_baseline" times the CPU oracle on a bounded sample of decode tokens.
 """
 from __future__ import annotations
@@ -226,6 +227,59 @@ def bench_decode(args):
     return res
 
 
+def bench_decode16(copies=4, steps=64, warmup=8):
+    """Side report: the 16-token batched decode (hot-pool router bias, about 60
+    distinct experts per step), K graph-replayed steps over `copies` layer
+    copies with fresh tokens per step.  Whole-layer HBM fraction from the
+    algorithmic bytes of the experts each step actually selected."""
+    import torch
+    from bit_quantized_routed_router_amd import ds4moe as D
+    from bit_quantized_routed_router_amd import synthetic as S
+
+    cfg = S.CONFIGS["decode16"]
+    T = cfg.T
+    layers = make_layer(cfg, copies=copies)
+    nsteps = warmup + steps
+    xs = np.stack([S.gen_x(cfg, variant=2000 + n) for n in range(nsteps)])
+    x = torch.from_numpy(xs.view(np.int16)).cuda()
+    y = torch.empty((nsteps, T, cfg.d), dtype=torch.float32, device="cuda")
+    idx = torch.empty((nsteps, T, cfg.k), dtype=torch.int32, device="cuda")
+    w = torch.empty((nsteps, T, cfg.k), dtype=torch.float32, device="cuda")
+    ws, wsn = layers[0].workspace(T, D.MODE_DECODE)
+
+    def step(n, stream):
+        L = layers[n % len(layers)]
+        D.forward_decode(L.desc, x[n], D.DT_BF16, T, y[n], idx[n], w[n], ws, wsn, stream=stream)
+
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        for n in range(warmup):
+            step(n, s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for n in range(warmup, nsteps):
+            step(n, torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    g.replay()  # first replay, untimed
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    with torch.cuda.stream(s):
+        g.replay()
+    e1.record(s)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    sel = idx[warmup:].cpu().numpy()
+    distinct = [len(np.unique(sel[n])) for n in range(steps)]
+    nbytes = float(np.mean([decode_bytes(cfg, nd, T=T)["total"] for nd in distinct]))
+    del layers, g
+    torch.cuda.empty_cache()
+    return dict(workload=f"decode16: T={T}, hot-pool router bias, {copies} layer copies round-robin, graph replay",
+                tok_s=T / (ms * 1e-3), us_per_step=ms * 1e3, distinct_mean=float(np.mean(distinct)),
+                bytes_per_step=nbytes, hbm_frac=nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS)
+
+
 def bench_prefill(args):
     import torch
     from bit_quantized_routed_router_amd import ds4moe as D
@@ -306,6 +360,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=16)
     ap.add_argument("--copies", type=int, default=8)
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-decode16", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     args = ap.parse_args()
@@ -320,6 +375,10 @@ def main():
 
     dec = bench_decode(args)
     log(f"[bench] decode: graph {dec['ms_per_step'] * 1e3:.1f} us/step, eager {dec['eager_ms_per_step'] * 1e3:.1f} us/step")
+    d16 = None if args.no_decode16 else bench_decode16()
+    if d16:
+        log(f"[bench] decode16: {d16['us_per_step']:.1f} us/step, {d16['tok_s']:.0f} tok/s, "
+            f"{d16['distinct_mean']:.1f} distinct experts, {100 * d16['hbm_frac']:.1f} % of HBM peak")
     pre = None if args.no_prefill else bench_prefill(args)
     if pre:
         log(f"[bench] prefill: {pre['ms']:.3f} ms, {pre['tok_s']:.0f} tok/s, {pre['tflops']:.1f} TFLOP/s")
@@ -350,6 +409,7 @@ def main():
                       "frac": dec["layer_hbm_frac"]},
         "eager_ms_per_step": dec["eager_ms_per_step"],
         "kernels_us": {k: round(v["mean_us"], 2) for k, v in dec["kernels"].items()},
+        "decode16": d16,
         "prefill": None if pre is None else dict(
             {k: pre[k] for k in ("workload", "tok_s", "ms", "tflops", "mfma_frac")},
             kernels_us={k: round(v["mean_us"], 2) for k, v in pre["kernels"].items()}),
