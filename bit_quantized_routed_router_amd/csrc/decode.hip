@@ -309,11 +309,21 @@ __device__ inline void shared_gateup_block(const ds4moe_layer& L, int T, const _
 }
 
 // ============================================================== stage 2
+// Activation rows of one super-block per wave when the group's x is not
+// staged whole: 16 token rows of 256 inputs, 8 halves of padding per row.
+constexpr int kSbRow = QK + 8;
+constexpr int kSbRows = kDecodeGroup * kSbRow;
+
+// BL: the group's whole x staged once per block (bh, bl); otherwise each
+// wave stages the super-block it is about to decode (xw, xwl).
+template <bool LO, bool BL>
 struct Stage2Lds {
   uint32_t mag[256 * 4];
   uint32_t sgn[128 * 4];
-  _Float16 bh[kStageHalves + 16 * 8];
-  _Float16 bl[kStageHalves + 16 * 8];
+  _Float16 bh[BL ? kStageHalves + 16 * 8 : 8];
+  _Float16 bl[BL ? kStageHalves + 16 * 8 : 8];
+  _Float16 xw[BL ? 8 : kW * kSbRows];
+  _Float16 xwl[BL || !LO ? 8 : kW * kSbRows];
   float4_t red[kW][64];
   float4_t red2[kW][64];
   int last;
@@ -351,12 +361,16 @@ __device__ inline half8_t cb2_apply(const Cb2Raw& R, uint32_t aux) {
 // routed gate/up products, whose codebook decoding is the arithmetic; then
 // two per 16-row tile of the shared expert (gate, up), an F16 stream
 // dispatched behind the routed blocks.
+// Waves per SIMD that stage 2's LDS allows: 4 blocks per CU with x staged
+// whole, 3 with the per-wave super-block buffers, fewer with fp32 input.
+constexpr int stage2_waves(bool lo, bool bl) { return bl ? (lo ? 2 : 4) : (lo ? 1 : 3); }
+
 template <bool LO, bool BL>
-__global__ __launch_bounds__(kW * 64) __attribute__((amdgpu_waves_per_eu(LO ? 2 : 4))) void k_dec_stage2(
+__global__ __launch_bounds__(kW * 64) __attribute__((amdgpu_waves_per_eu(stage2_waves(LO, BL)))) void k_dec_stage2(
     ds4moe_layer L, int T, RouteOut ro, const _Float16* __restrict__ xh,
     const _Float16* __restrict__ xl, _Float16* __restrict__ hw16, _Float16* __restrict__ hsum, int rtiles,
     float* __restrict__ gu_part, _Float16* __restrict__ hs16, int32_t* __restrict__ ctrl) {
-  __shared__ Stage2Lds lds;
+  __shared__ Stage2Lds<LO, BL> lds;
   if ((int)blockIdx.x >= rtiles) {
     shared_gateup_block<LO, BL>(L, T, xh, xl, blockIdx.x - rtiles, gu_part, hs16, ctrl, lds.bh, lds.bl, lds.red,
                                 lds.last);
@@ -429,7 +443,57 @@ __global__ __launch_bounds__(kW * 64) __attribute__((amdgpu_waves_per_eu(LO ? 2 
   load_batch(sb0);
   wait_all();  // the copies (and the first batch)
   __syncthreads();
-  for (int b0 = sb0; b0 < sb1; b0 += kSb2) {
+  if constexpr (!BL) {
+    // Each wave stages the activations of the super-block it decodes next
+    // (16 token rows x 256 inputs) and waits for its own copies; the
+    // buffer is its own, so no block barrier is needed.  Rows at or beyond
+    // T are never read (the MFMA rows of those tokens repeat token T - 1).
+    _Float16* xw = lds.xw + wave * kSbRows;
+    _Float16* xwl = LO ? lds.xwl + wave * kSbRows : nullptr;
+    for (int b0 = sb0; b0 < sb1; b0 += kSb2) {
+      if (b0 != sb0) load_batch(b0);
+#pragma unroll
+      for (int j = 0; j < kSb2; ++j) {
+        if (b0 + j >= sb1) break;  // wave-uniform
+        pin();
+        dma_rows(xh + (int64_t)(b0 + j) * QK, d, T, QK, xw, kSbRow, 0, 1, lane);
+        if (LO) dma_rows(xl + (int64_t)(b0 + j) * QK, d, T, QK, xwl, kSbRow, 0, 1, lane);
+        wait_all();
+        pin();
+        Cb2Step F[2];
+        auto fetch = [&](Cb2Step& G, int s2) {
+          const int kk = cb2_boff(q, s2);
+          G.bh = *(const half8_t*)(xw + tc * kSbRow + kk);
+          if (LO) G.bl = *(const half8_t*)(xwl + tc * kSbRow + kk);
+          cb2_lookup(G.g, (s2 & 4) ? cg[j].z : cg[j].x, (s2 & 4) ? cg[j].w : cg[j].y, s2 & 3, lds.mag, lds.sgn);
+          cb2_lookup(G.u, (s2 & 4) ? cu[j].z : cu[j].x, (s2 & 4) ? cu[j].w : cu[j].y, s2 & 3, lds.mag, lds.sgn);
+        };
+        float4_t pg = {0.f, 0.f, 0.f, 0.f}, pu = pg;
+        fetch(F[0], 0);
+#pragma unroll
+        for (int s2 = 0; s2 < 8; ++s2) {
+          if (s2 + 1 < 8) fetch(F[(s2 + 1) & 1], s2 + 1);
+          pin();
+          const Cb2Step& G = F[s2 & 1];
+          const half8_t a0 = cb2_apply(G.g, (s2 & 4) ? cg[j].w : cg[j].y);
+          const half8_t a1 = cb2_apply(G.u, (s2 & 4) ? cu[j].w : cu[j].y);
+          pg = mfma16x16x32(G.bh, a0, pg);
+          pu = mfma16x16x32(G.bh, a1, pu);
+          if (LO) {
+            pg = mfma16x16x32(G.bl, a0, pg);
+            pu = mfma16x16x32(G.bl, a1, pu);
+          }
+          pin();
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {  // the lane's own row: its own d
+          ag[r] += dg[j] * pg[r];
+          au[r] += du[j] * pu[r];
+        }
+      }
+    }
+  }
+  for (int b0 = sb0; BL && b0 < sb1; b0 += kSb2) {
     if (b0 != sb0) load_batch(b0);
     pin();
     // 8 steps per super-block (one per sub-block); each step's LDS reads
