@@ -694,8 +694,8 @@ __global__ __launch_bounds__(kW3 * 64) __attribute__((amdgpu_waves_per_eu(4))) v
   }
   // routing tables: expert ids by scalar loads, which do not wait for the
   // copies, so the first weight batch goes out while they are in flight
-  const int nd = min(ld_uniform(ndist), maxd);
-  const int maxunits = maxd * nb, nunits = nd * nb;
+  const int nd = max(1, min(ld_uniform(ndist), maxd));  // a call selects at least one expert
+  const int nunits = nd * nb;  // only the selected experts' units: their weights alone are read
   // units u = (expert slot u / nb, super-block u % nb); wave w takes
   // u = w, w + kW3, ... in batches of kUnits3
   int sj[kUnits3], bsb[kUnits3];  // per unit: slot of token c, super-block
@@ -704,7 +704,7 @@ __global__ __launch_bounds__(kW3 * 64) __attribute__((amdgpu_waves_per_eu(4))) v
   // unit u -> (expert slot u / nb, super-block u % nb), stepped by kW3
   // without a division per unit
   const int di = kW3 / nb, db = kW3 % nb;
-  auto unit_at = [&](int u, int& i, int& b) {  // u clamped into [0, maxunits)
+  auto unit_at = [&](int u, int& i, int& b) {
     i = u / nb;
     b = u - i * nb;
   };
@@ -727,8 +727,8 @@ __global__ __launch_bounds__(kW3 * 64) __attribute__((amdgpu_waves_per_eu(4))) v
     }
 #pragma unroll
     for (int j = 0; j < kUnits3; ++j) {  // units past the end repeat the last one
-      if (ij[j] >= maxd) {
-        ij[j] = maxd - 1;
+      if (ij[j] >= nd) {
+        ij[j] = nd - 1;
         bj[j] = nb - 1;
       }
       ej[j] = ld_uniform(distinct + ij[j]);  // all expert ids in flight before the first address needs one
@@ -759,7 +759,7 @@ __global__ __launch_bounds__(kW3 * 64) __attribute__((amdgpu_waves_per_eu(4))) v
   for (int j = 0; j < kBatchS; ++j) sa[j] = *(const half8_t*)(srow + max(min(sk0 + j, sk1 - 1), 0) * 32 + 8 * q);
   pin();
   float4_t acc = {0.f, 0.f, 0.f, 0.f};
-  for (int u0 = wave; u0 < maxunits; u0 += kW3 * kUnits3) {
+  for (int u0 = wave; u0 < nunits; u0 += kW3 * kUnits3) {
     if (u0 != wave) load_batch(u0);
     pin();
     // units past the end and tokens without a slot add nothing
