@@ -184,30 +184,39 @@ struct CbTables {
   }
 };
 
-template <bool LO, int TC, int RING>
+// CB2 block scales staged per block: the first NBS blocks of each of the
+// block's 128 gate and 128 up rows.  The scale plane of a row spans its whole
+// K range, so read per chunk its cache lines stay live for the block's whole
+// life and are evicted and fetched again; staged once, each is read once.
+template <bool LO, int TC, int RING, int NBS>
 struct GuLds {
   _Float16 xh[RING];
   _Float16 xl[LO ? RING : 8];
   CbTables<TC> tab;
   int tok[kTT];
   float w[kTT];
+  uint16_t dsc[NBS ? 2 * 128 * NBS : 2];
 };
+template <bool DENSE>
+constexpr int gu_nbs() { return DENSE ? 0 : 16; }
 
 // Weights of one 128-input chunk for a lane's four fragments.  CB2: the lane's sub-block (8 bytes) and its block's d; F16:
-// the lane's 4 x 8 binary16 values (inputs 32q .. 32q+31 of the chunk).
+// the lane's 4 x 8 binary16 values (inputs 32q .. 32q+31 of the chunk).  kLoads counts the vector-memory loads of a
+// chunk when every scale comes from LDS; kMaxLoads when they are all read from memory (blocks past the staged ones).
 template <bool F16>
 struct GuW {
   u32x2_t cw[4];
   uint32_t dv[4];
   u32x4_t wv[F16 ? 4 : 1][F16 ? 4 : 1];
-  static constexpr int kLoads = F16 ? 16 : 8;
+  static constexpr int kLoads = F16 ? 16 : 4;
+  static constexpr int kMaxLoads = F16 ? 16 : 8;
 };
 
 // Gate/up of one work tile (up to 128 slots) for a 128-row slice of h, NF
 // slot fragments.  DENSE: the shared expert (F16 weights, weight 1, rows are
 // tokens); otherwise routed expert e (CB2 weights, routing weights s.w).
-template <bool LO, bool DENSE, int NW, int TC, int RING, int NF>
-__device__ __attribute__((always_inline)) inline void gateup_tile(const ds4moe_layer& L, GuLds<LO, TC, RING>& s,
+template <bool LO, bool DENSE, int NW, int TC, int RING, int NF, int NBS>
+__device__ __attribute__((always_inline)) inline void gateup_tile(const ds4moe_layer& L, GuLds<LO, TC, RING, NBS>& s,
                                                                   const _Float16* __restrict__ xh,
                                                                   const _Float16* __restrict__ xl, int e, int rt,
                                                                   int pos0, int n, _Float16* __restrict__ hout) {
@@ -233,7 +242,10 @@ __device__ __attribute__((always_inline)) inline void gateup_tile(const ds4moe_l
       } else {
         const uint32_t blk = rowu[f & 1] + (uint32_t)(ch >> 1);
         W.cw[f] = ld_at<u32x2_t>(f < 2 ? gb : ub, blk * 64u + (uint32_t)(32 * (ch & 1) + 8 * q));
-        W.dv[f] = ld_at<uint16_t>(f < 2 ? gd : ud, blk * 2u);
+        if (NBS > 0 && (ch >> 1) < NBS)
+          W.dv[f] = s.dsc[((f >> 1) * 128 + 32 * wave + 16 * (f & 1) + c) * NBS + (ch >> 1)];
+        else
+          W.dv[f] = ld_at<uint16_t>(f < 2 ? gd : ud, blk * 2u);
       }
     }
   };
@@ -244,8 +256,10 @@ __device__ __attribute__((always_inline)) inline void gateup_tile(const ds4moe_l
 #pragma unroll
     for (int i = 0; i < NF; ++i) acc[f][i] = (float4_t){0.f, 0.f, 0.f, 0.f};
 
-  constexpr int kBatch = dma_per_wave(NF, NW) * (LO ? 2 : 1) + GuW<DENSE>::kLoads;  // per chunk and lane
-  constexpr int R = ring_depth(NF, kBatch, LO, RING);
+  // Loads per chunk and lane.  The ring depth keeps the largest count within the load counter; the waits use the
+  // smallest, which is exact when every scale is staged and waits longer than needed otherwise.
+  constexpr int kBatch = dma_per_wave(NF, NW) * (LO ? 2 : 1) + GuW<DENSE>::kLoads;
+  constexpr int R = ring_depth(NF, dma_per_wave(NF, NW) * (LO ? 2 : 1) + GuW<DENSE>::kMaxLoads, LO, RING);
   constexpr int kSlot = NF * 16 * kKC;  // halves per ring slot
   static_assert(R * kSlot <= RING, "ring slots exceed the staging buffer");
   GuW<DENSE> W[R];
@@ -360,12 +374,25 @@ __attribute__((amdgpu_waves_per_eu(DENSE || LO ? 1 : 2))) void k_pf_gateup(
     const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets, const int32_t* __restrict__ perm,
     const float* __restrict__ topk_w, _Float16* __restrict__ hout) {
   constexpr int NW = gu_waves<LO, DENSE>(), TC = gu_copies<LO, DENSE>(), RING = ring_halves(SMALL);
-  __shared__ GuLds<LO, TC, RING> s;
+  constexpr int NBS = gu_nbs<DENSE>();
+  static_assert(NW == 4, "the staged scales cover 4 waves x 32 rows");
+  __shared__ GuLds<LO, TC, RING, NBS> s;
   int e, rt, pos0, n;
   if (!tile_of<DENSE, SMALL>((DENSE ? L.d_ff_shared : L.d_ff) / (32 * NW), T, tiles, stiles, ntiles, counts, offsets,
                              e, rt, pos0, n))
     return;
-  if (!DENSE) s.tab.stage(c_pre_tables);
+  if constexpr (!DENSE) {
+    s.tab.stage(c_pre_tables);
+    // scales of rows rt*128 .. +127 of gate (g = 0) and up (g = 1), blocks 0 .. ns-1
+    const int nb = L.d_model / QK, ns = min(nb, NBS);
+    const size_t mb = (size_t)L.d_ff * nb;
+    const uint16_t* gd = (const uint16_t*)((const uint8_t*)L.gate + (size_t)e * mb * 66 + mb * 64);
+    const uint16_t* ud = (const uint16_t*)((const uint8_t*)L.up + (size_t)e * mb * 66 + mb * 64);
+    for (int i = threadIdx.x; i < 2 * 128 * ns; i += blockDim.x) {
+      const int g = i / (128 * ns), r = (i / ns) % 128, b = i % ns;
+      s.dsc[(g * 128 + r) * NBS + b] = (g ? ud : gd)[(size_t)(rt * 128 + r) * nb + b];
+    }
+  }
   if ((int)threadIdx.x < kTT) {
     const int r = min((int)threadIdx.x, n - 1);
     if (DENSE) {
@@ -377,32 +404,42 @@ __attribute__((amdgpu_waves_per_eu(DENSE || LO ? 1 : 2))) void k_pf_gateup(
     }
   }
   __syncthreads();
-#define DS4_GU(NF) gateup_tile<LO, DENSE, NW, TC, RING, NF>(L, s, xh, xl, e, rt, pos0, n, hout)
+#define DS4_GU(NF) gateup_tile<LO, DENSE, NW, TC, RING, NF, NBS>(L, s, xh, xl, e, rt, pos0, n, hout)
   DS4_NF_SWITCH(n, SMALL, DENSE, DS4_GU)
 #undef DS4_GU
 }
 
-template <int RING>
+// Q2K scales staged per block (NBS > 0): sub-block bytes (16 per block) and
+// d/dmin (4 bytes per block) of the first NBS blocks of the block's 256 rows,
+// rows padded by one word so that 16 rows read at once hit distinct banks.
+template <int RING, int NBS>
 struct DnLds {
   _Float16 xh[RING];
   int slot[kTT];
+  uint32_t sc[NBS ? 256 * (4 * NBS + 1) : 1];
+  uint32_t dd[NBS ? 256 * (NBS + 1) : 1];
 };
+// Staged Q2K blocks: small tiles only (the large-tile ring leaves no room).
+template <bool DENSE, bool SMALL>
+constexpr int dn_nbs() { return !DENSE && SMALL ? 8 : 0; }
 
 // Down weights of one chunk.  Q2K: the lane's two sub-blocks of codes, the
 // aligned word holding their two scale bytes, the block's d/dmin; F16: 4 x 8
-// binary16 values per fragment.
-template <bool F16>
+// binary16 values per fragment.  kLoads / kMaxLoads: vector-memory loads of a
+// chunk with the scales staged in LDS / read from memory.
+template <bool F16, bool STAGED>
 struct DnW {
   u32x2_t cw[4];
   uint32_t sc[4], dd[4];
   u32x4_t wv[F16 ? 4 : 1][F16 ? 4 : 1];
-  static constexpr int kLoads = F16 ? 16 : 12;
+  static constexpr int kMaxLoads = F16 ? 16 : 12;
+  static constexpr int kLoads = F16 ? 16 : STAGED ? 4 : 12;
 };
 
 // Down product of one work tile for a 256-row slice of the output.  Routed
 // (Q2K): yp[slot] = D_e h.  DENSE (shared, F16): y[t] = Wsd hs16[t].
-template <bool DENSE, int RING, int NF>
-__device__ __attribute__((always_inline)) inline void down_tile(const ds4moe_layer& L, DnLds<RING>& s,
+template <bool DENSE, int RING, int NF, int NBS>
+__device__ __attribute__((always_inline)) inline void down_tile(const ds4moe_layer& L, DnLds<RING, NBS>& s,
                                                                 const _Float16* __restrict__ hin, int e, int rt,
                                                                 int pos0, int n, float* __restrict__ yp,
                                                                 float* __restrict__ y) {
@@ -414,7 +451,8 @@ __device__ __attribute__((always_inline)) inline void down_tile(const ds4moe_lay
   const uint8_t* sup = base + mb * 80;
   const int r0 = rt * 256 + 64 * wave;
   const uint32_t row0 = (uint32_t)((r0 + c) * (DENSE ? fd : nb));  // fragment f: + 16 f (fd or nb)
-  auto load_w = [&](int ch, DnW<DENSE>& W) {
+  using WT = DnW<DENSE, (NBS > 0)>;
+  auto load_w = [&](int ch, WT& W) {
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
       if constexpr (DENSE) {
@@ -424,8 +462,14 @@ __device__ __attribute__((always_inline)) inline void down_tile(const ds4moe_lay
       } else {
         const uint32_t blk = row0 + (uint32_t)(16 * f * nb + (ch >> 1));
         W.cw[f] = ld_at<u32x2_t>(base, blk * 64u + (uint32_t)(32 * (ch & 1) + 8 * q));
-        W.sc[f] = ld_at<uint32_t>(sub, blk * 16u + (uint32_t)(8 * (ch & 1) + 4 * (q >> 1)));
-        W.dd[f] = ld_at<uint32_t>(sup, blk * 4u);
+        if (NBS > 0 && (ch >> 1) < NBS) {
+          const int lr = 64 * wave + 16 * f + c;
+          W.sc[f] = s.sc[lr * (4 * NBS + 1) + 4 * (ch >> 1) + 2 * (ch & 1) + (q >> 1)];
+          W.dd[f] = s.dd[lr * (NBS + 1) + (ch >> 1)];
+        } else {
+          W.sc[f] = ld_at<uint32_t>(sub, blk * 16u + (uint32_t)(8 * (ch & 1) + 4 * (q >> 1)));
+          W.dd[f] = ld_at<uint32_t>(sup, blk * 4u);
+        }
       }
     }
   };
@@ -437,11 +481,13 @@ __device__ __attribute__((always_inline)) inline void down_tile(const ds4moe_lay
 #pragma unroll
     for (int i = 0; i < NF; ++i) acc[f][i] = (float4_t){0.f, 0.f, 0.f, 0.f};
 
-  constexpr int kBatch = dma_per_wave(NF, kGW) + DnW<DENSE>::kLoads;
-  constexpr int R = ring_depth(NF, kBatch, false, RING, RING < 2 * kChunk ? 3 : 6);  // small: register budget
+  // As in gate/up: the depth bounds the largest load count, the waits use the smallest.
+  constexpr int kBatch = dma_per_wave(NF, kGW) + WT::kLoads;
+  constexpr int R = ring_depth(NF, dma_per_wave(NF, kGW) + WT::kMaxLoads, false, RING,
+                               RING < 2 * kChunk ? 3 : 6);  // small: register budget
   constexpr int kSlot = NF * 16 * kKC;
   static_assert(R * kSlot <= RING, "ring slots exceed the staging buffer");
-  DnW<DENSE> W[R];
+  WT W[R];
   auto issue = [&](int ch, int u) {
     stage_rows<false, NF, kGW>(hbase, nullptr, rows, ch, s.xh + u * kSlot, nullptr, wave, lane);
     load_w(ch, W[u]);
@@ -519,12 +565,29 @@ __attribute__((amdgpu_waves_per_eu(DENSE ? 1 : 2))) void k_pf_down(
     const int32_t* __restrict__ perm, const _Float16* __restrict__ hin, float* __restrict__ yp,
     float* __restrict__ y) {
   constexpr int RING = ring_halves(SMALL);
-  __shared__ DnLds<RING> s;
+  constexpr int NBS = dn_nbs<DENSE, SMALL>();
+  __shared__ DnLds<RING, NBS> s;
   int e, rt, pos0, n;
   if (!tile_of<DENSE, SMALL>(L.d_model / 256, T, tiles, stiles, ntiles, counts, offsets, e, rt, pos0, n)) return;
   if (!DENSE && (int)threadIdx.x < kTT) s.slot[threadIdx.x] = perm[pos0 + min((int)threadIdx.x, n - 1)];
+  if constexpr (NBS > 0) {
+    // scales of rows rt*256 .. +255, blocks 0 .. ns-1
+    const int nb = L.d_ff / QK, ns = min(nb, NBS);
+    const size_t mb = (size_t)L.d_model * nb;
+    const uint8_t* base = (const uint8_t*)L.down + (size_t)e * mb * 84;
+    const uint32_t* sub = (const uint32_t*)(base + mb * 64);
+    const uint32_t* sup = (const uint32_t*)(base + mb * 80);
+    for (int i = threadIdx.x; i < 256 * 4 * ns; i += blockDim.x) {
+      const int r = i / (4 * ns), wd = i % (4 * ns);  // word wd of the row's first ns blocks
+      s.sc[r * (4 * NBS + 1) + wd] = sub[(size_t)(rt * 256 + r) * nb * 4 + wd];
+    }
+    for (int i = threadIdx.x; i < 256 * ns; i += blockDim.x) {
+      const int r = i / ns, b = i % ns;
+      s.dd[r * (NBS + 1) + b] = sup[(size_t)(rt * 256 + r) * nb + b];
+    }
+  }
   __syncthreads();
-#define DS4_DN(NF) down_tile<DENSE, RING, NF>(L, s, hin, e, rt, pos0, n, yp, y)
+#define DS4_DN(NF) down_tile<DENSE, RING, NF, NBS>(L, s, hin, e, rt, pos0, n, yp, y)
   DS4_NF_SWITCH(n, SMALL, DENSE, DS4_DN)
 #undef DS4_DN
 }
