@@ -409,37 +409,43 @@ __attribute__((amdgpu_waves_per_eu(DENSE || LO ? 1 : 2))) void k_pf_gateup(
 #undef DS4_GU
 }
 
-// Q2K scales staged per block (NBS > 0): sub-block bytes (16 per block) and
-// d/dmin (4 bytes per block) of the first NBS blocks of the block's 256 rows,
-// rows padded by one word so that 16 rows read at once hit distinct banks.
-template <int RING, int NBS>
+// Q2K scales staged per block: d/dmin (4 bytes per block) of the first NBS
+// blocks and, with SC, the sub-block bytes (16 per block) too, for the
+// block's 256 rows; rows padded by one word so that 16 rows read at once hit
+// distinct banks.
+template <int RING, int NBS, bool SC>
 struct DnLds {
   _Float16 xh[RING];
   int slot[kTT];
-  uint32_t sc[NBS ? 256 * (4 * NBS + 1) : 1];
+  uint32_t sc[SC ? 256 * (4 * NBS + 1) : 1];
   uint32_t dd[NBS ? 256 * (NBS + 1) : 1];
 };
-// Staged Q2K blocks: small tiles only (the large-tile ring leaves no room).
-template <bool DENSE, bool SMALL>
-constexpr int dn_nbs() { return !DENSE && SMALL ? 8 : 0; }
+// Staged Q2K blocks.  Small tiles: d/dmin and the sub-block bytes of the
+// first 8 blocks, later blocks read from memory in the loop.  Large tiles
+// (the ring leaves room for d/dmin only): d/dmin when the whole row fits
+// (d_ff <= 2048, DDS), with no in-loop fallback, which would not fit the
+// register budget.
+template <bool DENSE, bool SMALL, bool DDS>
+constexpr int dn_nbs() { return DENSE || (!SMALL && !DDS) ? 0 : 8; }
+constexpr int kDnStagedMax = 8;
 
 // Down weights of one chunk.  Q2K: the lane's two sub-blocks of codes, the
 // aligned word holding their two scale bytes, the block's d/dmin; F16: 4 x 8
 // binary16 values per fragment.  kLoads / kMaxLoads: vector-memory loads of a
 // chunk with the scales staged in LDS / read from memory.
-template <bool F16, bool STAGED>
+template <bool F16, bool SC, bool DD>
 struct DnW {
   u32x2_t cw[4];
   uint32_t sc[4], dd[4];
   u32x4_t wv[F16 ? 4 : 1][F16 ? 4 : 1];
   static constexpr int kMaxLoads = F16 ? 16 : 12;
-  static constexpr int kLoads = F16 ? 16 : STAGED ? 4 : 12;
+  static constexpr int kLoads = F16 ? 16 : 4 + (SC ? 0 : 4) + (DD ? 0 : 4);
 };
 
 // Down product of one work tile for a 256-row slice of the output.  Routed
 // (Q2K): yp[slot] = D_e h.  DENSE (shared, F16): y[t] = Wsd hs16[t].
-template <bool DENSE, int RING, int NF, int NBS>
-__device__ __attribute__((always_inline)) inline void down_tile(const ds4moe_layer& L, DnLds<RING, NBS>& s,
+template <bool DENSE, int RING, int NF, int NBS, bool SC, bool FULL>
+__device__ __attribute__((always_inline)) inline void down_tile(const ds4moe_layer& L, DnLds<RING, NBS, SC>& s,
                                                                 const _Float16* __restrict__ hin, int e, int rt,
                                                                 int pos0, int n, float* __restrict__ yp,
                                                                 float* __restrict__ y) {
@@ -451,7 +457,7 @@ __device__ __attribute__((always_inline)) inline void down_tile(const ds4moe_lay
   const uint8_t* sup = base + mb * 80;
   const int r0 = rt * 256 + 64 * wave;
   const uint32_t row0 = (uint32_t)((r0 + c) * (DENSE ? fd : nb));  // fragment f: + 16 f (fd or nb)
-  using WT = DnW<DENSE, (NBS > 0)>;
+  using WT = DnW<DENSE, SC, (NBS > 0)>;
   auto load_w = [&](int ch, WT& W) {
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
@@ -462,14 +468,15 @@ __device__ __attribute__((always_inline)) inline void down_tile(const ds4moe_lay
       } else {
         const uint32_t blk = row0 + (uint32_t)(16 * f * nb + (ch >> 1));
         W.cw[f] = ld_at<u32x2_t>(base, blk * 64u + (uint32_t)(32 * (ch & 1) + 8 * q));
-        if (NBS > 0 && (ch >> 1) < NBS) {
-          const int lr = 64 * wave + 16 * f + c;
+        const int lr = 64 * wave + 16 * f + c;
+        if (SC && (ch >> 1) < NBS)
           W.sc[f] = s.sc[lr * (4 * NBS + 1) + 4 * (ch >> 1) + 2 * (ch & 1) + (q >> 1)];
-          W.dd[f] = s.dd[lr * (NBS + 1) + (ch >> 1)];
-        } else {
+        else
           W.sc[f] = ld_at<uint32_t>(sub, blk * 16u + (uint32_t)(8 * (ch & 1) + 4 * (q >> 1)));
+        if (NBS > 0 && (FULL || (ch >> 1) < NBS))
+          W.dd[f] = s.dd[lr * (NBS + 1) + (ch >> 1)];
+        else
           W.dd[f] = ld_at<uint32_t>(sup, blk * 4u);
-        }
       }
     }
   };
@@ -557,7 +564,7 @@ __device__ __attribute__((always_inline)) inline void down_tile(const ds4moe_lay
 
 // Routed down (Q2K) over the work list into yp, or (DENSE) the shared
 // expert's down (F16) over all T tokens into y.
-template <bool DENSE, bool SMALL>
+template <bool DENSE, bool SMALL, bool DDS>
 __global__ __launch_bounds__(kGW * 64)
 __attribute__((amdgpu_waves_per_eu(DENSE ? 1 : 2))) void k_pf_down(
     ds4moe_layer L, int64_t T, const int32_t* __restrict__ tiles, const int32_t* __restrict__ stiles,
@@ -565,8 +572,10 @@ __attribute__((amdgpu_waves_per_eu(DENSE ? 1 : 2))) void k_pf_down(
     const int32_t* __restrict__ perm, const _Float16* __restrict__ hin, float* __restrict__ yp,
     float* __restrict__ y) {
   constexpr int RING = ring_halves(SMALL);
-  constexpr int NBS = dn_nbs<DENSE, SMALL>();
-  __shared__ DnLds<RING, NBS> s;
+  constexpr int NBS = dn_nbs<DENSE, SMALL, DDS>();
+  constexpr bool SC = !DENSE && SMALL;
+  static_assert(!DDS || (!DENSE && !SMALL), "DDS: large routed tiles");
+  __shared__ DnLds<RING, NBS, SC> s;
   int e, rt, pos0, n;
   if (!tile_of<DENSE, SMALL>(L.d_model / 256, T, tiles, stiles, ntiles, counts, offsets, e, rt, pos0, n)) return;
   if (!DENSE && (int)threadIdx.x < kTT) s.slot[threadIdx.x] = perm[pos0 + min((int)threadIdx.x, n - 1)];
@@ -577,9 +586,11 @@ __attribute__((amdgpu_waves_per_eu(DENSE ? 1 : 2))) void k_pf_down(
     const uint8_t* base = (const uint8_t*)L.down + (size_t)e * mb * 84;
     const uint32_t* sub = (const uint32_t*)(base + mb * 64);
     const uint32_t* sup = (const uint32_t*)(base + mb * 80);
-    for (int i = threadIdx.x; i < 256 * 4 * ns; i += blockDim.x) {
-      const int r = i / (4 * ns), wd = i % (4 * ns);  // word wd of the row's first ns blocks
-      s.sc[r * (4 * NBS + 1) + wd] = sub[(size_t)(rt * 256 + r) * nb * 4 + wd];
+    if constexpr (SC) {
+      for (int i = threadIdx.x; i < 256 * 4 * ns; i += blockDim.x) {
+        const int r = i / (4 * ns), wd = i % (4 * ns);  // word wd of the row's first ns blocks
+        s.sc[r * (4 * NBS + 1) + wd] = sub[(size_t)(rt * 256 + r) * nb * 4 + wd];
+      }
     }
     for (int i = threadIdx.x; i < 256 * ns; i += blockDim.x) {
       const int r = i / ns, b = i % ns;
@@ -587,7 +598,7 @@ __attribute__((amdgpu_waves_per_eu(DENSE ? 1 : 2))) void k_pf_down(
     }
   }
   __syncthreads();
-#define DS4_DN(NF) down_tile<DENSE, RING, NF, NBS>(L, s, hin, e, rt, pos0, n, yp, y)
+#define DS4_DN(NF) down_tile<DENSE, RING, NF, NBS, SC, DDS>(L, s, hin, e, rt, pos0, n, yp, y)
   DS4_NF_SWITCH(n, SMALL, DENSE, DS4_DN)
 #undef DS4_DN
 }
@@ -650,12 +661,16 @@ hipError_t launch_prefill_experts(const Fwd& f) {
     DS4_GU_LAUNCH(false, false, true, ggs, hw16);
   }
 #undef DS4_GU_LAUNCH
-  DS4_LAUNCH((k_pf_down<false, false>), gdn, blk, 0, f.st, L, T, tiles, stiles, ntiles, counts, offsets, perm, hw16,
-             yp, f.y);
-  DS4_LAUNCH((k_pf_down<false, true>), gds, blk, 0, f.st, L, T, tiles, stiles, ntiles, counts, offsets, perm, hw16,
-             yp, f.y);
-  DS4_LAUNCH((k_pf_down<true, false>), gsd, blk, 0, f.st, L, T, tiles, stiles, ntiles, counts, offsets, perm, hs16,
-             yp, f.y);
+  if (L.d_ff / QK <= kDnStagedMax)
+    DS4_LAUNCH((k_pf_down<false, false, true>), gdn, blk, 0, f.st, L, T, tiles, stiles, ntiles, counts, offsets, perm,
+               hw16, yp, f.y);
+  else
+    DS4_LAUNCH((k_pf_down<false, false, false>), gdn, blk, 0, f.st, L, T, tiles, stiles, ntiles, counts, offsets, perm,
+               hw16, yp, f.y);
+  DS4_LAUNCH((k_pf_down<false, true, false>), gds, blk, 0, f.st, L, T, tiles, stiles, ntiles, counts, offsets, perm,
+             hw16, yp, f.y);
+  DS4_LAUNCH((k_pf_down<true, false, false>), gsd, blk, 0, f.st, L, T, tiles, stiles, ntiles, counts, offsets, perm,
+             hs16, yp, f.y);
   const int64_t n4 = T * d / 4;
   const int cb = (int)std::min<int64_t>((n4 + 255) / 256, 8192);
   DS4_LAUNCH(k_combine, dim3(cb), dim3(256), 0, f.st, T, d, k, yp, f.y);
