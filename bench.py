@@ -20,6 +20,8 @@ shared expert, bf16 activations -- in layer-tokens per second.
   * "prefill" times ds4moe_forward_prefill on a 2048-token chunk with
     Zipf-like expert loads against the dense fp16 MFMA peak;
   * "decode16" times the 16-token batched decode (about 60 distinct experts);
+  * "decode_small" times speculative-verify shapes, T = 2, 4, 8 tokens per
+    call at the decode1 layer shape;
   * "cpu_baseline" times the CPU oracle on a bounded sample of decode tokens.
 """
 from __future__ import annotations
@@ -227,20 +229,17 @@ def bench_decode(args):
     return res
 
 
-def bench_decode16(copies=4, steps=64, warmup=8):
-    """Side report: the 16-token batched decode (hot-pool router bias, about 60
-    distinct experts per step), K graph-replayed steps over `copies` layer
-    copies with fresh tokens per step.  Whole-layer HBM fraction from the
+def decode_batch(cfg, layers, T, steps, warmup, xvar0):
+    """K graph-replayed T-token decode steps over the given layer copies (round
+    robin) with fresh tokens per step.  Returns us/step, tok/s, the mean
+    distinct-expert count and the whole-layer HBM fraction from the
     algorithmic bytes of the experts each step actually selected."""
     import torch
     from bit_quantized_routed_router_amd import ds4moe as D
     from bit_quantized_routed_router_amd import synthetic as S
 
-    cfg = S.CONFIGS["decode16"]
-    T = cfg.T
-    layers = make_layer(cfg, copies=copies)
     nsteps = warmup + steps
-    xs = np.stack([S.gen_x(cfg, variant=2000 + n) for n in range(nsteps)])
+    xs = np.stack([S.gen_x(cfg, variant=xvar0 + n, T=T) for n in range(nsteps)])
     x = torch.from_numpy(xs.view(np.int16)).cuda()
     y = torch.empty((nsteps, T, cfg.d), dtype=torch.float32, device="cuda")
     idx = torch.empty((nsteps, T, cfg.k), dtype=torch.int32, device="cuda")
@@ -273,11 +272,43 @@ def bench_decode16(copies=4, steps=64, warmup=8):
     sel = idx[warmup:].cpu().numpy()
     distinct = [len(np.unique(sel[n])) for n in range(steps)]
     nbytes = float(np.mean([decode_bytes(cfg, nd, T=T)["total"] for nd in distinct]))
-    del layers, g
-    torch.cuda.empty_cache()
-    return dict(workload=f"decode16: T={T}, hot-pool router bias, {copies} layer copies round-robin, graph replay",
-                tok_s=T / (ms * 1e-3), us_per_step=ms * 1e3, distinct_mean=float(np.mean(distinct)),
+    del g
+    return dict(tok_s=T / (ms * 1e-3), us_per_step=ms * 1e3, distinct_mean=float(np.mean(distinct)),
                 bytes_per_step=nbytes, hbm_frac=nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS)
+
+
+def bench_decode16(copies=4, steps=64, warmup=8):
+    """Side report: the 16-token batched decode (hot-pool router bias, about 60
+    distinct experts per step)."""
+    import torch
+    from bit_quantized_routed_router_amd import synthetic as S
+
+    cfg = S.CONFIGS["decode16"]
+    layers = make_layer(cfg, copies=copies)
+    r = decode_batch(cfg, layers, cfg.T, steps, warmup, 2000)
+    del layers
+    torch.cuda.empty_cache()
+    return dict(workload=f"decode16: T={cfg.T}, hot-pool router bias, {copies} layer copies round-robin, "
+                         "graph replay", **r)
+
+
+def bench_decode_small(copies=4, steps=64, warmup=8, Ts=(2, 4, 8)):
+    """Side report: speculative-verify and small-batch shapes, T = 2, 4, 8
+    tokens per decode call at the decode1 layer shape (no router bias, so the
+    T * 6 slots mostly select distinct experts)."""
+    import torch
+    from bit_quantized_routed_router_amd import synthetic as S
+
+    cfg = S.CONFIGS["decode1"]
+    layers = make_layer(cfg, copies=copies)
+    out = {}
+    for T in Ts:
+        r = decode_batch(cfg, layers, T, steps, warmup, 3000 + 100 * T)
+        out[f"T{T}"] = r
+    del layers
+    torch.cuda.empty_cache()
+    return dict(workload=f"decode at T = {', '.join(map(str, Ts))}: decode1 layer shape, {copies} layer copies "
+                         "round-robin, graph replay", **out)
 
 
 def bench_prefill(args):
@@ -361,6 +392,7 @@ def main():
     ap.add_argument("--copies", type=int, default=8)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-decode16", action="store_true")
+    ap.add_argument("--no-decode-small", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     args = ap.parse_args()
@@ -376,6 +408,12 @@ def main():
     dec = bench_decode(args)
     log(f"[bench] decode: graph {dec['ms_per_step'] * 1e3:.1f} us/step, eager {dec['eager_ms_per_step'] * 1e3:.1f} us/step")
     d16 = None if args.no_decode16 else bench_decode16()
+    dsm = None if args.no_decode_small else bench_decode_small()
+    if dsm:
+        for key, r in dsm.items():
+            if key.startswith("T"):
+                log(f"[bench] decode {key}: {r['us_per_step']:.1f} us/step, {r['tok_s']:.0f} tok/s, "
+                    f"{r['distinct_mean']:.1f} distinct experts, {100 * r['hbm_frac']:.1f} % of HBM peak")
     if d16:
         log(f"[bench] decode16: {d16['us_per_step']:.1f} us/step, {d16['tok_s']:.0f} tok/s, "
             f"{d16['distinct_mean']:.1f} distinct experts, {100 * d16['hbm_frac']:.1f} % of HBM peak")
@@ -410,6 +448,7 @@ def main():
         "eager_ms_per_step": dec["eager_ms_per_step"],
         "kernels_us": {k: round(v["mean_us"], 2) for k, v in dec["kernels"].items()},
         "decode16": d16,
+        "decode_small": dsm,
         "prefill": None if pre is None else dict(
             {k: pre[k] for k in ("workload", "tok_s", "ms", "tflops", "mfma_frac")},
             kernels_us={k: round(v["mean_us"], 2) for k, v in pre["kernels"].items()}),

@@ -10,6 +10,7 @@ activations; the expected error is ~1e-4)."""
 import numpy as np
 import pytest
 
+from oracle import oracle as O
 from bit_quantized_routed_router_amd import ds4moe as D
 from bit_quantized_routed_router_amd import synthetic as S
 from tests.gpu_helpers import SeededLayer, check_routing, rel_err_rows
@@ -131,6 +132,28 @@ def test_decode1_prefill_entry_point(decode1):
     got = decode1.forward(x, D.MODE_PREFILL)
     check_routing(got, ref, decode1.cfg.k)
     assert rel_err_rows(got["y"], ref["y"]) <= TOL
+
+
+@pytest.mark.parametrize("T", [2, 4, 8])
+def test_decode1_small_batch(decode1, T):
+    """Speculative-verify shapes: T = 2, 4 and 8 tokens per decode call at
+    the full layer shape (T * 6 slots over mostly distinct experts).  The input
+    variant is the first whose fp64 gap between the 6th and 7th logit exceeds
+    1e-4 for every token, so that the expert sets are unique against the
+    GPU's fp32 accumulation."""
+    for v in range(400 + 64 * T, 464 + 64 * T):
+        x = decode1.x(T=T, variant=v)
+        if O.topk_gap(decode1.oracle.route(x, decode1.cfg.x_dtype)["logits"], decode1.cfg.k).min() > 1e-4:
+            break
+    else:
+        raise AssertionError("no input variant with a clear top-k gap")
+    ref = oracle_ref(decode1, x)
+    check_used_experts_bytes(decode1, ref["idx"])
+    got = decode1.forward(x, D.MODE_DECODE)
+    check_routing(got, ref, decode1.cfg.k)
+    err = rel_err_rows(got["y"], ref["y"])
+    print(f"decode T={T} rel err {err:.3e}")
+    assert err <= TOL
 
 
 def test_decode16_forward():
