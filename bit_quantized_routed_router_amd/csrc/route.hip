@@ -179,7 +179,16 @@ __global__ __launch_bounds__(256) void k_count_experts(const int32_t* __restrict
   __shared__ int s_tmp[8];
   const int e = blockIdx.x;
   int c = 0;
-  for (int64_t s = threadIdx.x; s < S; s += blockDim.x) c += idx[s] == e;
+  // 16-byte loads (idx sits in the 256-byte aligned workspace), four in
+  // flight per thread, so the loop does not wait on each load in turn
+  const int64_t S4 = S / 4;
+  const int4* v = (const int4*)idx;
+#pragma unroll 4
+  for (int64_t i = threadIdx.x; i < S4; i += blockDim.x) {
+    const int4 a = v[i];
+    c += (a.x == e) + (a.y == e) + (a.z == e) + (a.w == e);
+  }
+  for (int64_t s = 4 * S4 + threadIdx.x; s < S; s += blockDim.x) c += idx[s] == e;
   int tot;
   block_excl_scan(c, s_tmp, &tot);
   if (threadIdx.x == 0) counts[e] = tot;
