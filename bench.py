@@ -47,8 +47,8 @@ METRIC = "routed-MoE layer decode tok/s + % HBM peak; 2048-tok prefill tok/s + %
 # 128-byte request at 128 bytes) and WRITE_SIZE, both checked against a
 # 256 MiB device copy (factor 1.000); valid for the kernel sources with this
 # hash only (profiles/decode1_hbm_traffic.md holds the commands and counts).
-TRAFFIC_SOURCE_HASH = "55c00dc0fd9e2d07"
-TRAFFIC_BYTES = {"k_dec_stage1": 2.26e6, "k_dec_stage2": 60.16e6, "k_dec_stage3": 33.61e6}
+TRAFFIC_SOURCE_HASH = "1f8fcca8b8ca99ea"
+TRAFFIC_BYTES = {"k_dec_stage1": 2.26e6, "k_dec_stage2": 60.06e6, "k_dec_stage3": 33.61e6}
 
 
 def kernel_source_hash(csrc=None):
@@ -397,7 +397,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures the layer on one GPU only; this build has no multi-GPU path "
+        print("bench.py measures the layer on one GPU only; the library has no multi-GPU path "
               "(run with --gpus 1).", file=sys.stderr)
         sys.exit(2)
     import torch

@@ -235,7 +235,7 @@ const char* ds4moe_strerror(int status) {
     case DS4MOE_EALIGN: return "misaligned pointer (16 bytes for tensors, 256 for the workspace)";
     case DS4MOE_EWORKSPACE: return "workspace smaller than ds4moe_workspace_bytes()";
     case DS4MOE_EHIP: return "HIP runtime error at launch";
-    case DS4MOE_EUNSUPPORTED: return "not supported by this build";
+    case DS4MOE_EUNSUPPORTED: return "not supported by this library";
     default: return "unknown status";
   }
 }

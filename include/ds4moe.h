@@ -79,7 +79,7 @@ enum {
   DS4MOE_EALIGN = -3,       /* pointer not aligned as required */
   DS4MOE_EWORKSPACE = -4,   /* workspace smaller than ds4moe_workspace_bytes() */
   DS4MOE_EHIP = -5,         /* the HIP runtime reported an error at launch */
-  DS4MOE_EUNSUPPORTED = -6  /* valid but not supported by this build */
+  DS4MOE_EUNSUPPORTED = -6  /* valid but not supported by this library */
 };
 
 enum { DS4MOE_FMT_F16 = 0, DS4MOE_FMT_CB2 = 1, DS4MOE_FMT_Q2K = 2 };
@@ -89,7 +89,7 @@ enum { DS4MOE_MODE_DECODE = 0, DS4MOE_MODE_PREFILL = 1, DS4MOE_MODE_ROUTE = 2 };
 /* Largest T accepted by ds4moe_forward_decode (tokens beyond 16 are run as
  * consecutive groups of 16). */
 #define DS4MOE_DECODE_MAX_T 64
-/* Limits of this build: d_model, d_ff, d_ff_shared <= 16384; E <= 1024;
+/* Limits of this library: d_model, d_ff, d_ff_shared <= 16384; E <= 1024;
  * k <= 16. */
 
 /* Layer descriptor.  Plain data: read during the call, not retained.
