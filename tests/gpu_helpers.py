@@ -43,11 +43,14 @@ def rel_err_rows(y: np.ndarray, ref: np.ndarray) -> float:
 class SeededLayer:
     """A synthetic layer (config cfg) held both on the device and for the oracle."""
 
-    def __init__(self, cfg: S.Config, device_quantize: bool, cfg_seed: int | None = None, chunk: int = 16):
+    def __init__(self, cfg: S.Config, device_quantize: bool, cfg_seed: int | None = None, chunk: int = 16,
+                 router: np.ndarray | None = None):
+        """router: binary16 bits [E, d] to use instead of the seeded draw
+        (edge-case tests build routers with repeated rows)."""
         self.cfg = cfg
         self.seed = cfg.seed if cfg_seed is None else cfg_seed
         c = cfg
-        self.router = S.gen_router(cfg, cfg_seed=cfg_seed)
+        self.router = S.gen_router(cfg, cfg_seed=cfg_seed) if router is None else np.ascontiguousarray(router)
         self.bias = S.gen_bias(cfg)
         self.sh = S.gen_shared(cfg, cfg_seed=cfg_seed)
         cb = D.packed_bytes(D.FMT_CB2, c.f, c.d)
@@ -138,11 +141,24 @@ class SeededLayer:
         return out
 
 
+TAU = 1e-4  # top-k gap that input seeds must clear (fp64 logits)
+
+
 def check_routing(got: dict, ref: dict, k: int, w_tol: float = 1e-5):
-    """Indices, counts, offsets and permutation bit-exact; weights within w_tol."""
+    """Indices, counts, offsets and permutation bit-exact; weights within
+    w_tol.  With the oracle's logits in ref: the GPU's selected logits, seen
+    through its weights (log(w_j / w_0) = l_j - l_0 under the softmax), agree
+    with the oracle's differences within TAU / 2."""
     assert np.array_equal(got["idx"], ref["idx"]), "top-k indices differ"
     assert np.abs(got["w"] - ref["w"]).max() <= w_tol
     assert np.abs(got["w"].sum(axis=1) - 1.0).max() <= 1e-5
+    if "logits" in ref:
+        lsel = np.take_along_axis(ref["logits"], ref["idx"].astype(np.int64), axis=1)
+        w = got["w"].astype(np.float64)
+        ok = w.min(axis=1) > 1e-30  # log of an underflowed weight says nothing
+        dl_gpu = np.log(w[ok]) - np.log(w[ok][:, :1])
+        dl_ref = lsel[ok] - lsel[ok][:, :1]
+        assert np.abs(dl_gpu - dl_ref).max() <= TAU / 2, "selected logit differences off by more than tau/2"
     if "counts" in got:
         assert np.array_equal(got["counts"], ref["counts"])
         assert np.array_equal(got["offsets"], ref["offsets"])

@@ -22,7 +22,7 @@ TOL = 2e-3
 def oracle_ref(L: SeededLayer, x, tokens=None):
     r = L.oracle.forward(x, L.cfg.x_dtype, tokens=tokens)
     return dict(idx=r["idx"], w=r["w"], counts=r["counts"], offsets=r["offsets"], perm=r["perm"], y=r["y64"],
-                tokens=r["tokens"])
+                tokens=r["tokens"], logits=r["logits"])
 
 
 def check_used_experts_bytes(L: SeededLayer, idx):
@@ -172,18 +172,51 @@ def test_decode16_forward():
     check_routing(r, ref, L.cfg.k)
 
 
+def slot_tile_kinds(counts, offsets, inv, idx, k):
+    """Tile kind of every slot t*k + j in the prefill work lists: 'full' (a
+    run of 128 slots), 'rem' (an expert's remainder of 33..127 slots, a large
+    tile) or 'small' (a remainder of at most 32 slots, the small-tile list)."""
+    kinds = np.empty(inv.shape[0], dtype=object)
+    for s in range(inv.shape[0]):
+        e = int(idx[s // k, s % k])
+        n = int(counts[e])
+        local = int(inv[s]) - int(offsets[e])
+        if local < (n // 128) * 128:
+            kinds[s] = "full"
+        else:
+            kinds[s] = "rem" if n % 128 > 32 else "small"
+    return kinds
+
+
 def test_prefill_2048_sampled():
     """2048-token prefill: routing for all tokens bit-exact, outputs of a
-    seeded sample of tokens against the oracle."""
+    sample of tokens against the oracle.  The sample is drawn so that it
+    holds slots in all three tile kinds of the grouped products (full
+    128-slot tiles, large remainder tiles, small tiles)."""
     print("[setup] prefill layer (device-packed, Zipf bias)", flush=True)
     L = SeededLayer(S.CONFIGS["prefill"], device_quantize=True)
     x = L.x()
-    sample = np.sort(np.random.default_rng(42).choice(L.cfg.T, 24, replace=False))
-    sample = np.unique(np.concatenate([sample, [0, L.cfg.T - 1]]))
+    k, T = L.cfg.k, L.cfg.T
+    r = L.oracle.route(x, L.cfg.x_dtype)
+    kinds = slot_tile_kinds(r["counts"], r["offsets"], r["inv"], r["idx"], k).reshape(T, k)
+    g = np.random.default_rng(42)
+    sample = [0, T - 1]
+    for kind in ("full", "rem", "small"):
+        has = np.flatnonzero((kinds == kind).any(axis=1))
+        assert len(has) >= 8, f"fewer than 8 tokens with a slot in a {kind} tile"
+        sample += list(g.choice(has, 8, replace=False))
+    sample = np.unique(np.array(sample))
+    covered = {kd: int((kinds[sample] == kd).sum()) for kd in ("full", "rem", "small")}
+    print(f"prefill sample: {len(sample)} tokens, slots per tile kind {covered}")
+    assert min(covered.values()) >= 8
     ref = oracle_ref(L, x, tokens=sample)
     got = L.forward(x, D.MODE_PREFILL)
-    check_routing(got, ref, L.cfg.k)
+    check_routing(got, ref, k)
     check_used_experts_bytes(L, ref["idx"][sample])
+    for kd in ("full", "rem", "small"):
+        toks = np.flatnonzero((kinds[sample] == kd).any(axis=1))
+        e = rel_err_rows(got["y"][sample[toks]], ref["y"][toks])
+        print(f"prefill sampled ({kd}-tile tokens) rel err {e:.3e}")
     err = rel_err_rows(got["y"][sample], ref["y"])
     print(f"prefill sampled rel err {err:.3e}")
     assert err <= TOL

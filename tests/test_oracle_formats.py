@@ -57,6 +57,69 @@ def test_splitmix64_published_first_output():
     assert O.splitmix64_sequence(0, 1)[0] == 0xE220A8397B1DCDAF
 
 
+_M64 = (1 << 64) - 1
+
+
+def _splitmix64_py(state: int, n: int) -> list[int]:
+    """splitmix64 written out from its published definition (Steele, Lea and
+    Flood, OOPSLA 2014): add the golden-ratio increment, then two
+    xor-shift-multiply rounds and a final xor-shift."""
+    out = []
+    for _ in range(n):
+        state = (state + 0x9E3779B97F4A7C15) & _M64
+        z = state
+        z = ((z ^ (z >> 30)) * 0xBF58476D1CE4E5B9) & _M64
+        z = ((z ^ (z >> 27)) * 0x94D049BB133111EB) & _M64
+        out.append(z ^ (z >> 31))
+    return out
+
+
+def _grid_fixture():
+    return json.load(open(os.path.join(GOLDEN, "grid_rule.json")))
+
+
+def test_splitmix64_published_vectors_both_implementations():
+    pub = _grid_fixture()["splitmix64_published"]
+    five = [int(v) for v in pub["state1234567_first5"]]
+    assert _splitmix64_py(1234567, 5) == five
+    assert O.splitmix64_sequence(1234567, 5) == five
+    assert _splitmix64_py(0, 1)[0] == int(pub["state0_first"], 16)
+    seed = int(_grid_fixture()["seed"], 16)
+    assert O.splitmix64_sequence(seed, 3000) == _splitmix64_py(seed, 3000)
+
+
+def test_grid_entry0_hand_worked():
+    fx = _grid_fixture()
+    e0 = fx["entry0"]
+    draws = _splitmix64_py(int(fx["seed"], 16), 8)
+    assert [hex(v) for v in draws] == e0["draws"]
+    assert [v >> 32 for v in draws] == e0["upper32"]
+    # remainder mod 3 by the decimal digit sum, as worked in the fixture
+    assert [sum(map(int, str(u))) % 3 for u in e0["upper32"]] == e0["levels"]
+    assert list(O.grid_levels()[0]) == e0["levels"]
+
+
+def test_grid_rebuilt_from_written_rule():
+    """The whole grid rebuilt in Python from the written rule (level =
+    (draw >> 32) % 3 in coordinate order; a repeated entry is discarded and
+    drawn again in full) with the independent generator above; the rule's
+    redraw branch is taken at the fixture's entries."""
+    fx = _grid_fixture()
+    seed = int(fx["seed"], 16)
+    stream = iter(_splitmix64_py(seed, 256 * 8 * 4))
+    grid, redraws = [], []
+    for i in range(256):
+        while True:
+            e = tuple((next(stream) >> 32) % 3 for _ in range(8))
+            if e in grid:
+                redraws.append(dict(entry=i, rejected=list(e), equals_entry=grid.index(e)))
+                continue
+            grid.append(e)
+            break
+    assert redraws == fx["redraws"]
+    assert np.array_equal(np.array(grid, dtype=np.uint8), O.grid_levels())
+
+
 def test_grid_shape_distinct_and_balanced():
     lv = O.grid_levels()
     assert lv.shape == (256, 8)
