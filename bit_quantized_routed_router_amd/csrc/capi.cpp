@@ -4,6 +4,7 @@
 
 #include <algorithm>
 #include <cstring>
+#include <mutex>
 
 #include "common.h"
 #include "internal.h"
@@ -112,6 +113,40 @@ __global__ __launch_bounds__(256) void k_zero_bytes(uint8_t* __restrict__ p, siz
   if (blockIdx.x == 0 && threadIdx.x < n % 16) p[n16 * 16 + threadIdx.x] = 0;
 }
 
+// ---------------------------------------------------------------- static scratch
+// Device memory of ds4moe_forward_decode_static: a fixed array in place of
+// the caller's workspace.  Host code never uses the array's name as an
+// address (on the host it is only a stand-in for the symbol); it takes each
+// device's copy from hipGetSymbolAddress once, with that device current.
+static __device__ __align__(256) unsigned char scratch[DS4MOE_STATIC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+struct StaticScratch {
+  std::mutex mu;
+  void* ptr[kMaxDevices] = {};
+};
+static StaticScratch g_static;
+
+// This device's scratch address; on the first call for a device, looks it up
+// and clears the whole array with a kernel on `st` (the arrival counters the
+// decode kernels keep at its start must be zero before the first call; each
+// call returns them to zero).
+static int static_scratch(hipStream_t st, void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return DS4MOE_EHIP;
+  std::lock_guard<std::mutex> lk(g_static.mu);
+  if (!g_static.ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return DS4MOE_EHIP;
+    const size_t n = DS4MOE_STATIC_SCRATCH_BYTES;
+    DS4_LAUNCH(k_zero_bytes, dim3(1024), dim3(256), 0, st, (uint8_t*)p, n);
+    if (hipGetLastError() != hipSuccess) return DS4MOE_EHIP;
+    g_static.ptr[dev] = p;
+  }
+  *out = g_static.ptr[dev];
+  return DS4MOE_OK;
+}
+
 }  // namespace ds4
 
 using namespace ds4;
@@ -206,6 +241,21 @@ int ds4moe_forward_decode(const ds4moe_layer* L, const void* x, int x_dtype, int
     if (launch_decode(f) != hipSuccess) return DS4MOE_EHIP;
   }
   return DS4MOE_OK;
+}
+
+int ds4moe_forward_decode_static(const ds4moe_layer* L, const void* x, int x_dtype, int64_t T, float* y,
+                                 int32_t* topk_idx_out, float* topk_w_out, void* stream) {
+  int rc = check_layer(L);
+  if (rc) return rc;
+  if (!x || !y) return DS4MOE_EINVAL;
+  if (x_dtype != DS4MOE_DT_F32 && x_dtype != DS4MOE_DT_BF16) return DS4MOE_EINVAL;
+  if (T < 1 || T > DS4MOE_DECODE_MAX_T) return DS4MOE_ESHAPE;
+  const size_t need = ws_layout(*L, T, DS4MOE_MODE_DECODE).total;
+  if (need > DS4MOE_STATIC_SCRATCH_BYTES) return DS4MOE_EWORKSPACE;
+  if (!al16(x) || !al16(y) || !opt_al4(topk_idx_out) || !opt_al4(topk_w_out)) return DS4MOE_EALIGN;
+  void* ws = nullptr;
+  if ((rc = static_scratch((hipStream_t)stream, &ws))) return rc;
+  return ds4moe_forward_decode(L, x, x_dtype, T, y, topk_idx_out, topk_w_out, ws, need, stream);
 }
 
 int ds4moe_forward_prefill(const ds4moe_layer* L, const void* x, int x_dtype, int64_t T, float* y,

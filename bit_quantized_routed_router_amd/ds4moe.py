@@ -64,6 +64,8 @@ def lib() -> ctypes.CDLL:
         L.ds4moe_route.argtypes = [LP, P, I32, I64, P, P, P, P, P, P, SZ, P]
         L.ds4moe_forward_decode.restype = I32
         L.ds4moe_forward_decode.argtypes = [LP, P, I32, I64, P, P, P, P, SZ, P]
+        L.ds4moe_forward_decode_static.restype = I32
+        L.ds4moe_forward_decode_static.argtypes = [LP, P, I32, I64, P, P, P, P]
         L.ds4moe_forward_prefill.restype = I32
         L.ds4moe_forward_prefill.argtypes = [LP, P, I32, I64, P, P, P, P, P, SZ, P]
         L.ds4moe_strerror.restype = ctypes.c_char_p
@@ -80,7 +82,7 @@ def lib() -> ctypes.CDLL:
 
 EXPORTS = ["ds4moe_packed_bytes", "ds4moe_quantize", "ds4moe_dequantize", "ds4moe_workspace_bytes",
            "ds4moe_workspace_init",
-           "ds4moe_route", "ds4moe_forward_decode", "ds4moe_forward_prefill", "ds4moe_strerror",
+           "ds4moe_route", "ds4moe_forward_decode", "ds4moe_forward_decode_static", "ds4moe_forward_prefill", "ds4moe_strerror",
            "ds4moe_grid_levels", "ds4moe_trace_enable", "ds4moe_trace_read"]
 
 
@@ -138,6 +140,15 @@ def route(desc, x, x_dtype, T, topk_idx, topk_w, counts, offsets, perm, ws, ws_b
 def forward_decode(desc, x, x_dtype, T, y, topk_idx_out, topk_w_out, ws, ws_bytes, stream=None) -> None:
     _check(lib().ds4moe_forward_decode(ctypes.byref(desc), _ptr(x), x_dtype, T, _ptr(y), _ptr(topk_idx_out),
                                        _ptr(topk_w_out), _ptr(ws), ws_bytes, _stream(stream)), "ds4moe_forward_decode")
+
+
+STATIC_SCRATCH_BYTES = 4 << 20
+
+
+def forward_decode_static(desc, x, x_dtype, T, y, topk_idx_out, topk_w_out, stream=None) -> None:
+    """forward_decode on the library's own device array (no workspace)."""
+    _check(lib().ds4moe_forward_decode_static(ctypes.byref(desc), _ptr(x), x_dtype, T, _ptr(y), _ptr(topk_idx_out),
+                                              _ptr(topk_w_out), _stream(stream)), "ds4moe_forward_decode_static")
 
 
 def forward_prefill(desc, x, x_dtype, T, y, topk_idx_out, topk_w_out, perm_out, ws, ws_bytes, stream=None) -> None:

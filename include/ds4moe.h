@@ -155,6 +155,26 @@ int ds4moe_forward_decode(const ds4moe_layer *L, const void *x, int x_dtype, int
                           int32_t *topk_idx_out, float *topk_w_out, void *ws, size_t ws_bytes,
                           void *stream);
 
+/* Bytes of the device array that ds4moe_forward_decode_static uses as its
+ * workspace (one copy per GPU, held until the process ends). */
+#define DS4MOE_STATIC_SCRATCH_BYTES ((size_t)4 << 20)
+
+/* ds4moe_forward_decode without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments and results as
+ * ds4moe_forward_decode (bit for bit: the same kernels run), with the
+ * library's own device array of DS4MOE_STATIC_SCRATCH_BYTES as workspace.
+ * Allocates nothing: on its first call on a device it looks up that device's
+ * copy of the array and clears it with a kernel on `stream`.  Returns
+ * DS4MOE_EWORKSPACE, with nothing launched, when the call's workspace
+ * (ds4moe_workspace_bytes(L, T, DS4MOE_MODE_DECODE)) exceeds the array
+ * (DeepSeek V4 Flash's shape needs 1.6 MB at any T).  All calls on one GPU
+ * share its array: calls that may overlap (on different streams or host
+ * threads without ordering between them) race and give wrong outputs; calls
+ * ordered on one stream are safe. */
+int ds4moe_forward_decode_static(const ds4moe_layer *L, const void *x, int x_dtype, int64_t T, float *y,
+                                 int32_t *topk_idx_out, float *topk_w_out, void *stream);
+
 /* Full layer for 1 <= T <= 524280 tokens (prefill chunk; grouped GEMMs),
  * with T * d_model < 2^31 and T * k * d_ff < 2^31 (DS4MOE_ESHAPE otherwise).
  * Same outputs as ds4moe_forward_decode plus the optional permutation

@@ -90,6 +90,34 @@ def test_forward_argument_errors():
     assert lib.ds4moe_route(ctypes.byref(L), A, D.DT_BF16, 4, A + 2, A, None, None, None, A, 1 << 40, None) == D.EALIGN
 
 
+def test_static_decode_argument_errors():
+    """The workspace-free decode rejects bad arguments, and shapes whose
+    workspace exceeds its device array, before any HIP call."""
+    lib = D.lib()
+
+    def call(L, x=A, dt=D.DT_BF16, T=1, y=A):
+        return lib.ds4moe_forward_decode_static(ctypes.byref(L) if L is not None else None, x, dt, T, y, None,
+                                                None, None)
+
+    big = desc(d=16384, E=1024, k=16, f=16384, fs=16384)
+    assert D.workspace_bytes(big, 16, D.MODE_DECODE) > D.STATIC_SCRATCH_BYTES
+    assert call(big, T=16) == D.EWORKSPACE
+    assert D.workspace_bytes(desc(), 64, D.MODE_DECODE) <= D.STATIC_SCRATCH_BYTES
+    assert call(None) == D.EINVAL
+    assert call(desc(d=4000)) == D.ESHAPE
+    assert call(desc(), T=0) == D.ESHAPE
+    assert call(desc(), T=65) == D.ESHAPE
+    assert call(desc(), dt=3) == D.EINVAL
+    assert call(desc(), y=None) == D.EINVAL
+    assert call(desc(), x=A + 2) == D.EALIGN
+
+
+def test_header_static_scratch_size_matches_binding():
+    src = open(HEADER).read()
+    m = re.search(r"#define DS4MOE_STATIC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", src)
+    assert m and int(m.group(1)) << int(m.group(2)) == D.STATIC_SCRATCH_BYTES
+
+
 def test_codec_argument_errors():
     lib = D.lib()
     assert lib.ds4moe_quantize(7, A, 4, 256, A, None) == D.EINVAL
