@@ -13,16 +13,21 @@ shared expert, bf16 activations -- in layer-tokens per second.
     cannot serve the shared/router weights from one step to the next;
   * the K timed steps are captured once into a HIP graph and replayed (the
     launch sequence a decode loop would submit), bracketed by events on the
-    capture stream; the eager (host-launched) rate is reported beside it;
+    capture stream; the headline is the median of --repeats replays after an
+    untimed first one; the eager (host-launched) median is reported beside it;
   * "roofline" covers the dominant decode kernel (the longest of the three
-    stages): algorithmic bytes per launch / its mean duration from HIP events
-    around each launch during an eager pass over the same steps;
+    stages): algorithmic bytes per launch / its mean duration from the
+    start/stop events the library attaches to each kernel dispatch
+    (hipExtLaunchKernel) during an eager pass over the same steps;
+  * "measured_peaks" gives a device copy rate and a library fp16 GEMM rate
+    on the same GPU beside the vendor peaks;
   * "prefill" times ds4moe_forward_prefill on a 2048-token chunk with
     Zipf-like expert loads against the dense fp16 MFMA peak;
   * "decode16" times the 16-token batched decode (about 60 distinct experts);
   * "decode_small" times speculative-verify shapes, T = 2, 4, 8 tokens per
     call at the decode1 layer shape;
-  * "cpu_baseline" times the CPU oracle on a bounded sample of decode tokens.
+  * "cpu_baseline" times the CPU oracle on a bounded sample of decode tokens,
+    on all host threads and on one.
 """
 from __future__ import annotations
 
@@ -38,6 +43,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, vendor peak
+WEIGHT_SIGMA = 0.02
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA, vendor peak
 
 METRIC = "routed-MoE layer decode tok/s + % HBM peak; 2048-tok prefill tok/s + % MFMA"
@@ -155,45 +161,50 @@ def bench_decode(args):
             step(n, s)
     torch.cuda.synchronize()
 
-    # eager pass over the timed steps (host-launched)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    with torch.cuda.stream(s):
-        e0.record(s)
+    def timed(run):
+        """ms of one pass over the K timed steps, events on the launch stream,
+        synchronized before and after."""
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(s):
+            e0.record(s)
+            run()
+            e1.record(s)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+
+    def eager():
         for n in range(args.warmup, nsteps):
             step(n, s)
-        e1.record(s)
-    torch.cuda.synchronize()
-    eager_ms = e0.elapsed_time(e1) / args.steps
+
+    # eager passes over the timed steps (host-launched)
+    eager_runs = [timed(eager) / args.steps for _ in range(args.repeats)]
+    eager_ms = float(np.median(eager_runs))
     y_eager = y.clone()
 
-    # traced eager pass: per-kernel durations from events around each launch
+    # traced eager pass: per-kernel durations from the start/stop events the
+    # library attaches to each kernel's dispatch (hipExtLaunchKernel)
     D.trace_read(reset=True)
     D.trace_enable(True)
-    with torch.cuda.stream(s):
-        for n in range(args.warmup, nsteps):
-            step(n, s)
+    eager()
     torch.cuda.synchronize()
     D.trace_enable(False)
     kern = D.trace_read(reset=True)
 
-    # graph: the timed steps captured once, replayed
+    # graph: the timed steps captured once, replayed; the first replay is
+    # untimed and checked against the eager results, then the median of
+    # `repeats` timed replays
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=s):
         for n in range(args.warmup, nsteps):
             step(n, torch.cuda.current_stream())
     torch.cuda.synchronize()
-    g.replay()  # first replay (not timed), checked against the eager results
+    g.replay()
     torch.cuda.synchronize()
     if not torch.equal(y[args.warmup:], y_eager[args.warmup:]):
         raise RuntimeError("graph replay differs from the eager run")
-    torch.cuda.synchronize()
-    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    g0.record(s)
-    with torch.cuda.stream(s):
-        g.replay()
-    g1.record(s)
-    torch.cuda.synchronize()
-    graph_ms = g0.elapsed_time(g1) / args.steps
+    graph_runs = [timed(g.replay) / args.steps for _ in range(args.repeats)]
+    graph_ms = float(np.median(graph_runs))
     if not torch.equal(y[args.warmup:], y_eager[args.warmup:]):
         raise RuntimeError("graph replay differs from the eager run")
 
@@ -214,10 +225,13 @@ def bench_decode(args):
         raise RuntimeError(f"no decode kernel in the trace: {sorted(kern)}")
     dom = max(per, key=lambda n: per[n]["mean_us"])
     achieved = per[dom]["gbs"]
-    res = dict(ms_per_step=graph_ms, eager_ms_per_step=eager_ms, kernels={k: dict(mean_us=v[0] / max(v[1], 1) * 1e3,
+    res = dict(ms_per_step=graph_ms, eager_ms_per_step=eager_ms, graph_runs_ms=graph_runs, eager_runs_ms=eager_runs,
+               kernels={k: dict(mean_us=v[0] / max(v[1], 1) * 1e3,
                launches=v[1]) for k, v in kern.items()}, decode_kernels=per,
                roofline=dict(bound="hbm", kernel=dom, achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
                              frac=achieved / HBM_PEAK_GBS,
+                             timing="mean kernel duration over the K timed steps of one eager pass, from start/stop "
+                                    "HIP events attached to each dispatch by hipExtLaunchKernel on the launch stream",
                              traffic=(TRAFFIC_BYTES[dom] if kernel_source_hash() == TRAFFIC_SOURCE_HASH
                                       else None),
                              traffic_unit="HBM bytes per launch",
@@ -325,14 +339,15 @@ def bench_prefill(args):
     for _ in range(2):
         D.forward_prefill(L.desc, x, D.DT_BF16, T, y, None, None, None, ws, wsn)
     torch.cuda.synchronize()
-    reps = 5
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(reps):
+    runs = []
+    for _ in range(args.repeats):  # median of `repeats` calls, each bracketed by events
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
         D.forward_prefill(L.desc, x, D.DT_BF16, T, y, None, None, None, ws, wsn)
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / reps
+        e1.record()
+        torch.cuda.synchronize()
+        runs.append(e0.elapsed_time(e1))
+    ms = float(np.median(runs))
     D.trace_read(reset=True)
     D.trace_enable(True)
     D.forward_prefill(L.desc, x, D.DT_BF16, T, y, None, None, None, ws, wsn)
@@ -343,9 +358,157 @@ def bench_prefill(args):
     tflops = flop / (ms * 1e-3) / 1e12
     del L
     torch.cuda.empty_cache()
-    return dict(workload=f"prefill T={T}, Zipf(1.1)-shaped expert loads", tok_s=T / (ms * 1e-3), ms=ms,
+    return dict(workload=f"prefill T={T}, Zipf(1.1)-shaped expert loads", tok_s=T / (ms * 1e-3), ms=ms, runs_ms=runs,
                 flop=flop, tflops=tflops, mfma_frac=tflops / MFMA_F16_PEAK_TFLOPS,
                 kernels={k: dict(mean_us=v[0] / v[1] * 1e3, launches=v[1]) for k, v in kern.items() if v[1] > 0})
+
+
+def bench_stack43(nlayers=43, tokens=256, warmup=16, repeats=3):
+    """The 43-layer stack of decode1-shaped layers, every layer's packed
+    experts resident in HBM at once (about 80 GB), one token at a time
+    through all layers (T = 1 per call).
+
+    Weights: layer l draws its fp32 weights N(0, 0.02) on the device from
+    torch's generator seeded 1000 + l and packs them with ds4moe_quantize
+    (untimed); router and shared expert are drawn likewise and rounded to
+    binary16.  Inputs: each (layer, token) gets its own pre-drawn bf16
+    N(0, 1) row (teacher forcing, as in the stack's parity test), so the
+    timed region holds library calls only; the residual and normalisation
+    between layers are outside the layer and not timed."""
+    import torch
+    from bit_quantized_routed_router_amd import ds4moe as D
+    from bit_quantized_routed_router_amd import synthetic as S
+
+    c = S.CONFIGS["stack43"]
+    cb = D.packed_bytes(D.FMT_CB2, c.f, c.d)
+    qb = D.packed_bytes(D.FMT_Q2K, c.d, c.f)
+    t0 = time.time()
+    layers, resident = [], 0
+    gen = torch.Generator(device="cuda")
+    for l in range(nlayers):
+        gen.manual_seed(1000 + l)
+        packed = []
+        for fmt, rows, cols, nb in ((D.FMT_CB2, c.f, c.d, cb), (D.FMT_CB2, c.f, c.d, cb), (D.FMT_Q2K, c.d, c.f, qb)):
+            w = torch.randn((c.E, rows * cols), generator=gen, device="cuda", dtype=torch.float32).mul_(WEIGHT_SIGMA)
+            buf = torch.empty(c.E * nb, dtype=torch.uint8, device="cuda")
+            for e in range(c.E):
+                D.quantize(fmt, w[e], rows, cols, buf[e * nb:(e + 1) * nb])
+            del w
+            packed.append(buf)
+        f16 = [torch.randn(n, generator=gen, device="cuda").mul_(WEIGHT_SIGMA).half()
+               for n in (c.E * c.d, c.fs * c.d, c.fs * c.d, c.d * c.fs)]
+        layers.append(D.Layer(c.d, c.E, c.k, c.f, c.fs, f16[0], None, f16[1], f16[2], f16[3], *packed))
+        resident += sum(t.numel() * t.element_size() for t in packed + f16)
+        if l % 8 == 7:
+            torch.cuda.synchronize()
+            log(f"[bench] stack43: {l + 1} layers packed, {time.time() - t0:.1f}s")
+    torch.cuda.synchronize()
+    pack_s = time.time() - t0
+    nsteps = warmup + tokens
+    gen.manual_seed(5000)
+    x = torch.randn((nlayers, nsteps, c.d), generator=gen, device="cuda").to(torch.bfloat16)
+    y = torch.empty((nlayers, nsteps, c.d), dtype=torch.float32, device="cuda")
+    idx = torch.empty((nlayers, nsteps, c.k), dtype=torch.int32, device="cuda")
+    ws, wsn = layers[0].workspace(1, D.MODE_DECODE)
+    s = torch.cuda.Stream()
+
+    def run(n0, n1, stream):
+        for n in range(n0, n1):
+            for l in range(nlayers):
+                D.forward_decode(layers[l].desc, x[l, n], D.DT_BF16, 1, y[l, n], idx[l, n], None, ws, wsn,
+                                 stream=stream)
+
+    def timed(fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(s):
+            e0.record(s)
+            fn()
+            e1.record(s)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+
+    with torch.cuda.stream(s):
+        run(0, warmup, s)
+    eager_runs = [timed(lambda: run(warmup, nsteps, s)) for _ in range(repeats)]
+    y_eager = y.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        run(warmup, nsteps, torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    if not torch.equal(y, y_eager):
+        raise RuntimeError("stack43: graph replay differs from the eager run")
+    graph_runs = [timed(g.replay) for _ in range(repeats)]
+    ms = float(np.median(graph_runs)) / tokens
+    eager_ms = float(np.median(eager_runs)) / tokens
+    sel = idx[:, warmup:].cpu().numpy()
+    distinct = float(np.mean([len(np.unique(sel[l, n])) for l in range(nlayers) for n in range(tokens)]))
+    per_token = nlayers * decode_bytes(c, c.k, T=1)["total"]
+    del g, layers, x, y, y_eager
+    torch.cuda.empty_cache()
+    return dict(workload=f"stack43: {nlayers} decode1-shaped layers resident, {tokens} tokens x {nlayers} layers, "
+                         "T=1 per call, teacher-forced seeded inputs, graph replay (median of "
+                         f"{repeats})",
+                tok_s=1.0 / (ms * 1e-3), us_per_token=ms * 1e3, eager_us_per_token=eager_ms * 1e3,
+                bytes_per_token=per_token, hbm_frac=per_token / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                resident_bytes=resident, distinct_per_layer=distinct, pack_s=pack_s)
+
+
+def measure_copy_gbs(nbytes=1 << 30, reps=5):
+    """Device-to-device copy rate of a plain torch copy (bytes read + written
+    per second), median of reps: the HBM figure measured beside the vendor
+    peak."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    ms = float(np.median(ts))
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2 * nbytes / (ms * 1e-3) / 1e9
+
+
+def measure_gemm_tflops(n=8192, reps=5):
+    """fp16 GEMM (n x n x n) through torch's library matmul, median of reps:
+    the dense-MFMA figure measured beside the vendor peak."""
+    import torch
+    a = torch.randn((n, n), dtype=torch.float16, device="cuda")
+    b = torch.randn((n, n), dtype=torch.float16, device="cuda")
+    c = a @ b
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        c = a @ b
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    ms = float(np.median(ts))
+    del a, b, c
+    torch.cuda.empty_cache()
+    return 2 * n ** 3 / (ms * 1e-3) / 1e12
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def bench_cpu_oracle(seconds: float):
@@ -371,17 +534,28 @@ def bench_cpu_oracle(seconds: float):
     for x in xs:  # pack the sample's experts (untimed)
         for e in np.unique(L.route(x, "bf16")["idx"]):
             L.expert(int(e))
-    done, t0 = 0, time.time()
-    while True:
-        for x in xs:
-            L.forward(x, "bf16")
-            done += 1
-        if time.time() - t0 >= seconds:
-            break
-    dt = time.time() - t0
-    threads = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
+
+    def rate(budget):
+        done, t0 = 0, time.time()
+        while True:
+            for x in xs:
+                L.forward(x, "bf16")
+                done += 1
+            if time.time() - t0 >= budget:
+                break
+        return done, time.time() - t0
+
+    threads = len(os.sched_getaffinity(0))
+    O.set_threads(threads)
+    done, dt = rate(seconds)
+    O.set_threads(1)
+    done1, dt1 = rate(seconds)
+    O.set_threads(threads)
     return dict(value=done / dt, unit="tok/s", cores=threads, kind="oracle",
-                sample=f"{done} decode1 tokens (T=1 layer calls over {ntok} distinct tokens), {dt:.1f}s, fp64")
+                value_1thread=done1 / dt1, cpu_model=cpu_model(),
+                sample=f"{done} decode1 tokens on {threads} threads in {dt:.1f}s and {done1} on 1 thread in "
+                       f"{dt1:.1f}s (T=1 layer calls over {ntok} distinct seeded tokens, experts packed beforehand), "
+                       "fp64")
 
 
 def main():
@@ -390,10 +564,13 @@ def main():
     ap.add_argument("--steps", type=int, default=256)
     ap.add_argument("--warmup", type=int, default=16)
     ap.add_argument("--copies", type=int, default=8)
+    ap.add_argument("--repeats", type=int, default=5, help="timed passes (eager) and graph replays; median reported")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-decode16", action="store_true")
     ap.add_argument("--no-decode-small", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-stack", action="store_true", help="skip the 43-layer stack leg (about 80 GB resident)")
+    ap.add_argument("--stack-tokens", type=int, default=256)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -420,6 +597,14 @@ def main():
     pre = None if args.no_prefill else bench_prefill(args)
     if pre:
         log(f"[bench] prefill: {pre['ms']:.3f} ms, {pre['tok_s']:.0f} tok/s, {pre['tflops']:.1f} TFLOP/s")
+    stk = None if args.no_stack else bench_stack43(tokens=args.stack_tokens)
+    if stk:
+        log(f"[bench] stack43: {stk['us_per_token']:.1f} us/token, {stk['tok_s']:.0f} tok/s, "
+            f"{100 * stk['hbm_frac']:.1f} % of HBM peak, {stk['resident_bytes'] / 1e9:.1f} GB resident "
+            f"(packed in {stk['pack_s']:.0f}s)")
+    copy_gbs = measure_copy_gbs()
+    gemm_tflops = measure_gemm_tflops()
+    log(f"[bench] measured: device copy {copy_gbs:.0f} GB/s, fp16 library GEMM {gemm_tflops:.0f} TFLOP/s")
     cpu = None if args.no_cpu_baseline else bench_cpu_oracle(args.cpu_seconds)
     ms = dec["ms_per_step"]
     out = {
@@ -442,7 +627,12 @@ def main():
             "global_batch": 1,
             "layer_copies": args.copies,
         },
-        "roofline": dec["roofline"],
+        "roofline": dict(dec["roofline"], measured_copy_gbs=copy_gbs,
+                         frac_of_measured_copy=dec["roofline"]["achieved"] / copy_gbs),
+        "measured_peaks": {"hbm_copy_gbs": copy_gbs, "fp16_gemm_tflops": gemm_tflops,
+                           "how": "median of 5: torch device copy of 1 GiB (read + write bytes); torch fp16 matmul "
+                                  "8192^3"},
+        "graph_runs_us": [round(v * 1e3, 2) for v in dec["graph_runs_ms"]],
         "layer_hbm": {"bytes_per_step": dec["layer_bytes"], "achieved_gbs": dec["layer_gbs"],
                       "frac": dec["layer_hbm_frac"]},
         "eager_ms_per_step": dec["eager_ms_per_step"],
@@ -450,8 +640,10 @@ def main():
         "decode16": d16,
         "decode_small": dsm,
         "prefill": None if pre is None else dict(
-            {k: pre[k] for k in ("workload", "tok_s", "ms", "tflops", "mfma_frac")},
+            {k: pre[k] for k in ("workload", "tok_s", "ms", "runs_ms", "tflops", "mfma_frac")},
+            frac_of_measured_gemm=pre["tflops"] / gemm_tflops,
             kernels_us={k: round(v["mean_us"], 2) for k, v in pre["kernels"].items()}),
+        "stack43": stk,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

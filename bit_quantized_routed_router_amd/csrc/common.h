@@ -174,44 +174,6 @@ __device__ inline half8_t as_half8(u32x4_t v) { return __builtin_bit_cast(half8_
 __device__ inline half2_t as_half2(uint32_t v) { return __builtin_bit_cast(half2_t, v); }
 __device__ inline uint32_t as_u32(half2_t v) { return __builtin_bit_cast(uint32_t, v); }
 
-// CB2 A fragment: the 8 weights of group q of one sub-block, as binary16
-// sign * (2s+1) * m (exact integers <= 155); the super-block's d is applied
-// to the fp32 product afterwards.  mag/sgn point at the LDS tables.
-__device__ inline half8_t cb2_frag(uint32_t idxw, uint32_t aux, int q, const uint32_t* mag,
-                                   const uint32_t* sgn) {
-  uint32_t idx = (idxw >> (8 * q)) & 0xFFu;
-  uint32_t code = (aux >> (7 * q)) & 0x7Fu;
-  _Float16 S = (_Float16)(float)(2 * (aux >> 28) + 1);
-  half2_t S2 = {S, S};
-  u32x4_t m = *(const u32x4_t*)(mag + 4 * idx);
-  u32x4_t s = *(const u32x4_t*)(sgn + 4 * code);
-  u32x4_t r;
-  r.x = as_u32(as_half2(m.x ^ s.x) * S2);
-  r.y = as_u32(as_half2(m.y ^ s.y) * S2);
-  r.z = as_u32(as_half2(m.z ^ s.z) * S2);
-  r.w = as_u32(as_half2(m.w ^ s.w) * S2);
-  return as_half8(r);
-}
-
-// Q2K A fragment: 8 consecutive codes (the low or high 16 bits of a
-// sub-block's u32) as binary16 s * q (exact integers <= 45).  The min term
-// and the super-block's d/dmin are applied afterwards.
-__device__ inline half8_t q2k_frag(uint32_t u, int hi, uint32_t s) {
-  uint32_t field = hi ? (u >> 16) : (u & 0xFFFFu);
-  uint32_t v = field | (field << 14);  // code 2p at bits 4p, code 2p+1 at bits 16+4p
-  _Float16 S = (_Float16)(float)s;
-  _Float16 C = (_Float16)(-1024.0f * (float)s);
-  half2_t S2 = {S, S}, C2 = {C, C};
-  u32x4_t r;
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    uint32_t pair = ((v >> (4 * p)) & 0x00030003u) | 0x64006400u;  // (1024 + q_a, 1024 + q_b)
-    half2_t t = __builtin_elementwise_fma(as_half2(pair), S2, C2);   // single rounding: exact
-    r[p] = as_u32(t);
-  }
-  return as_half8(r);
-}
-
 // (1024 + q_a, 1024 + q_b) binary16 pairs of the 8 codes packed in v (code
 // 2p at bits 4p, code 2p+1 at bits 16 + 4p): one shift and one three-input
 // bit operation, (x & 0x00030003) | 0x64006400, per pair.

@@ -1,4 +1,5 @@
-// Per-kernel timing with HIP events (see trace.h).  The only mutable global
+// Per-kernel timing with HIP events attached to each kernel's dispatch (see
+// trace.h).  The only mutable global
 // state of the library; it is touched only while tracing is enabled.
 #include "trace.h"
 
@@ -59,17 +60,21 @@ std::string clean(const char* raw) {
 TraceScope::TraceScope(const char* name, hipStream_t s) : st(s) {
   if (!g_on.load(std::memory_order_relaxed)) return;
   std::lock_guard<std::mutex> lk(g_mu);
-  Pending p{name_id(clean(name).c_str()), get_event(), get_event()};
-  if (!p.a || !p.b) return;
-  (void)hipEventRecord(p.a, st);
-  g_pending.push_back(p);
-  slot = (int)g_pending.size() - 1;
+  a = get_event();
+  b = get_event();
+  if (!a || !b) {
+    if (a) g_free.push_back(a);
+    if (b) g_free.push_back(b);
+    a = b = nullptr;
+    return;
+  }
+  id = name_id(clean(name).c_str());
 }
 
 TraceScope::~TraceScope() {
-  if (slot < 0) return;
+  if (id < 0) return;
   std::lock_guard<std::mutex> lk(g_mu);
-  (void)hipEventRecord(g_pending[slot].b, st);
+  g_pending.push_back(Pending{id, a, b});
 }
 
 }  // namespace ds4
@@ -85,16 +90,24 @@ int ds4moe_trace_enable(int on) {
 
 int ds4moe_trace_read(char* names, size_t names_cap, double* ms, long long* counts, int cap, int reset) {
   std::lock_guard<std::mutex> lk(g_mu);
-  for (const Pending& p : g_pending) {
+  // entries are taken off the list as they are counted, so an error midway
+  // leaves only the uncounted ones pending
+  size_t done = 0;
+  int rc = DS4MOE_OK;
+  for (; done < g_pending.size(); ++done) {
+    const Pending& p = g_pending[done];
     float t = 0.0f;
-    if (hipEventSynchronize(p.b) != hipSuccess || hipEventElapsedTime(&t, p.a, p.b) != hipSuccess)
-      return DS4MOE_EHIP;
+    if (hipEventSynchronize(p.b) != hipSuccess || hipEventElapsedTime(&t, p.a, p.b) != hipSuccess) {
+      rc = DS4MOE_EHIP;
+      break;
+    }
     g_ms[p.id] += t;
     g_count[p.id] += 1;
     g_free.push_back(p.a);
     g_free.push_back(p.b);
   }
-  g_pending.clear();
+  g_pending.erase(g_pending.begin(), g_pending.begin() + (std::ptrdiff_t)done);
+  if (rc != DS4MOE_OK) return rc;
   const int n = (int)g_names.size();
   std::string joined;
   for (int i = 0; i < n && i < cap; ++i) {

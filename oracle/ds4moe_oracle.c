@@ -25,6 +25,7 @@
  * depend on the thread count.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -594,4 +595,19 @@ void orc_swiglu(const double *g, const double *u, int64_t n, double *h)
 {
     for (int64_t i = 0; i < n; i++)
         h[i] = g[i] / (1.0 + exp(-g[i])) * u[i];
+}
+
+/* ------------------------------------------------------------------------- */
+/* Threads of the parallel loops (independent output rows only, so results   */
+/* do not depend on the count).                                              */
+/* ------------------------------------------------------------------------- */
+
+void orc_set_threads(int n)
+{
+    omp_set_num_threads(n > 0 ? n : 1);
+}
+
+int orc_max_threads(void)
+{
+    return omp_get_max_threads();
 }

@@ -69,6 +69,8 @@ def lib():
         L.orc_topk.argtypes = [P, I64, I64, ctypes.c_int, P, P]
         L.orc_permute.argtypes = [P, I64, ctypes.c_int, I64, P, P, P, P]
         L.orc_swiglu.argtypes = [P, P, I64, P]
+        L.orc_set_threads.argtypes = [ctypes.c_int]
+        L.orc_max_threads.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -76,6 +78,15 @@ def lib():
 def _p(a: np.ndarray):
     assert a.flags["C_CONTIGUOUS"]
     return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def set_threads(n: int) -> None:
+    """Threads of the oracle's parallel loops from the calling thread on."""
+    lib().orc_set_threads(int(n))
+
+
+def max_threads() -> int:
+    return int(lib().orc_max_threads())
 
 
 # ---------------------------------------------------------------- scalars

@@ -264,6 +264,39 @@ def test_cb2_group_search_equals_brute_force():
                 assert scores[idx, code] == scores.min(), (trial, j, g)
 
 
+def test_cb2_group_choice_is_fp64_sse_optimal_within_score_resolution():
+    """Independent of the integer score: the fp64 squared error of the chosen
+    (entry, sign code) against x, sum_k (x_k - sign_k a m_k)^2, is within the
+    score's rounding of the fp64 optimum over all 256 x 128 choices.  The
+    score is 4096 SSE / a^2 minus a constant, with x/a rounded to 1/4096:
+    rounding moves each cross term 2 R_k m_k by at most m_k <= 5, so eight
+    coordinates move a score by at most 40 units, i.e. 40 a^2 / 4096 of SSE,
+    and the chosen pair can trail the optimum by twice that."""
+    lv = O.grid_levels()
+    m = 2.0 * lv.astype(np.float64) + 1.0  # [256, 8]
+    pats = np.array([[(c >> k) & 1 for k in range(7)] + [bin(c).count("1") & 1] for c in range(128)])
+    sgn = np.where(pats == 1, -1.0, 1.0)  # [128, 8]
+    rng = np.random.default_rng(31)
+    worst = 0.0
+    for trial in range(10):
+        x = (rng.standard_normal(256) * 0.02).astype(np.float32)
+        packed = O.cb2_quantize(x[None, :])
+        codes, dpl = O.cb2_planes(packed, 1, 256)
+        d = float(np.array([dpl[0]], dtype=np.uint16).view(np.float16)[0])
+        for j in range(8):
+            aux = int.from_bytes(codes[8 * j + 4: 8 * j + 8].tobytes(), "little")
+            a = d * (2 * (aux >> 28) + 1)
+            for g in range(4):
+                xg = x[32 * j + 8 * g: 32 * j + 8 * g + 8].astype(np.float64)
+                vals = a * m[:, None, :] * sgn[None, :, :]  # [256, 128, 8]
+                sse = ((xg[None, None, :] - vals) ** 2).sum(-1)
+                got = sse[int(codes[8 * j + g]), (aux >> (7 * g)) & 0x7F]
+                slack = (got - sse.min()) / (a * a / 4096.0)
+                worst = max(worst, slack)
+                assert slack <= 80.0, (trial, j, g, slack)
+    print(f"largest gap to the fp64 optimum: {worst:.2f} / 4096 a^2")
+
+
 # ----------------------------------------------------------------- Q2K
 def _q2k_from_fixture(b):
     codes = np.zeros(64, dtype=np.uint8)
@@ -419,3 +452,13 @@ def test_quantizer_is_deterministic_and_thread_independent(monkeypatch):
     c2, d2 = O.cb2_planes(a2, 7, 512)
     assert np.array_equal(ca[: 7 * 2 * 64], c2) and np.array_equal(da[:14], d2)
     assert np.array_equal(a, O.cb2_quantize(x)) and np.array_equal(b, O.q2k_quantize(x))
+    n = O.max_threads()
+    try:
+        O.set_threads(1)
+        assert np.array_equal(a, O.cb2_quantize(x)) and np.array_equal(b, O.q2k_quantize(x))
+        Xa = rng.standard_normal((5, 512))
+        y1 = O.cb2_matmul(a, 40, 512, Xa)
+        O.set_threads(max(n, 3))
+        assert np.array_equal(y1, O.cb2_matmul(a, 40, 512, Xa))
+    finally:
+        O.set_threads(n)
