@@ -454,6 +454,95 @@ void orc_q2k_quantize(const float *w, int64_t rows, int64_t cols, uint8_t *codes
 }
 
 /* ------------------------------------------------------------------------- */
+/* MXFP4: the public OCP Microscaling (MX) format with FP4 E2M1 elements, one  */
+/* E8M0 scale per block of 32 elements.  It is DeepSeek's native format for    */
+/* the routed experts (TopDigg "DwarfStar (ds4) Deep Dive", 5.2, download     */
+/* options; diego-rodriguez.work guide, 4, model files).                      */
+/*   E2M1: sign bit, 2 exponent bits (bias 1), 1 mantissa bit; exponent 0 is  */
+/*         subnormal (0 and 0.5).  Values 0, 0.5, 1, 1.5, 2, 3, 4, 6.         */
+/*   E8M0: 8 exponent bits, bias 127, value 2^(E - 127); 0xFF is NaN.         */
+/* [rows, cols], two planes: codes rows*cols/2 bytes (element k of a row at   */
+/* byte k/2, even k in the low nibble), then scales rows*cols/32 bytes.       */
+/* Weight = e2m1(code) * 2^(scale - 127), exact in binary32 (rounded only     */
+/* where it leaves binary32's range, scale codes >= 253).                     */
+/* ------------------------------------------------------------------------- */
+
+double orc_e2m1_value(int code)
+{
+    int s = (code >> 3) & 1, e = (code >> 1) & 3, m = code & 1;
+    double mag = e == 0 ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+    return s ? -mag : mag;
+}
+
+double orc_e8m0_value(int code)
+{
+    return code == 255 ? NAN : ldexp(1.0, code - 127);
+}
+
+void orc_mx4_dequantize(const uint8_t *codes, const uint8_t *scales, int64_t rows, int64_t cols, float *out)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; r++)
+        for (int64_t k = 0; k < cols; k++) {
+            int byte = codes[(r * cols + k) / 2];
+            int c = (k & 1) ? byte >> 4 : byte & 15;
+            double v = orc_e2m1_value(c) * orc_e8m0_value(scales[(r * cols + k) / 32]);
+            out[r * cols + k] = (float)v;
+        }
+}
+
+/*
+ * MXFP4 quantizer, the OCP MX conversion of a block of 32:
+ *  1. amax = max |x|; a block of zeros gets scale code 0 and zero elements;
+ *  2. shared exponent = floor(log2(amax)) - 2 (2 = the largest E2M1
+ *     exponent), stored biased by 127 and clamped to 0..254;
+ *  3. each x / 2^shared is rounded to the nearest E2M1 value, ties to the
+ *     even code, values beyond 6 to 6 (saturation: 6 is the nearest);
+ *     the sign bit is set for negative x with a non-zero magnitude.
+ * Inputs must be finite.
+ */
+static void mx4_quantize_block(const float *x, uint8_t *codes, uint8_t *scale)
+{
+    double amax = 0.0;
+    for (int i = 0; i < 32; i++) {
+        double a = fabs((double)x[i]);
+        if (a > amax)
+            amax = a;
+    }
+    memset(codes, 0, 16);
+    *scale = 0;
+    if (amax == 0.0)
+        return;
+    int ex;
+    frexp(amax, &ex); /* amax = m * 2^ex, m in [0.5, 1): floor(log2 amax) = ex - 1 */
+    int sc = (ex - 1) - 2 + 127;
+    sc = sc < 0 ? 0 : (sc > 254 ? 254 : sc);
+    *scale = (uint8_t)sc;
+    for (int i = 0; i < 32; i++) {
+        double r = ldexp(fabs((double)x[i]), 127 - sc); /* exact */
+        int best = 0;
+        double bd = r;
+        for (int c = 1; c < 8; c++) {
+            double dd = fabs(r - orc_e2m1_value(c));
+            if (dd < bd || (dd == bd && (c & 1) == 0)) {
+                bd = dd;
+                best = c;
+            }
+        }
+        int code = best | ((x[i] < 0.0f && best != 0) ? 8 : 0);
+        codes[i / 2] |= (uint8_t)((i & 1) ? code << 4 : code);
+    }
+}
+
+void orc_mx4_quantize(const float *w, int64_t rows, int64_t cols, uint8_t *codes, uint8_t *scales)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; r++)
+        for (int64_t b = 0; b < cols / 32; b++)
+            mx4_quantize_block(w + r * cols + b * 32, codes + (r * cols + b * 32) / 2, scales + (r * cols) / 32 + b);
+}
+
+/* ------------------------------------------------------------------------- */
 /* Products with fp64 accumulation (sequential over K).                       */
 /* Y[n][rows] = W[rows][cols] . X[n][cols], W given packed or as F16.         */
 /* ------------------------------------------------------------------------- */
@@ -485,6 +574,23 @@ void orc_q2k_matmul(const uint8_t *codes, const uint8_t *sub, const uint16_t *su
     for (int64_t r = 0; r < rows; r++) {
         float *wrow = (float *)malloc(sizeof(float) * (size_t)cols);
         orc_q2k_dequantize(codes + r * nb * 64, sub + r * nb * 16, sup + r * nb * 2, 1, cols, wrow);
+        for (int64_t t = 0; t < n; t++) {
+            double acc = 0.0;
+            for (int64_t i = 0; i < cols; i++)
+                acc += (double)wrow[i] * X[t * cols + i];
+            Y[t * rows + r] = acc;
+        }
+        free(wrow);
+    }
+}
+
+void orc_mx4_matmul(const uint8_t *codes, const uint8_t *scales, int64_t rows, int64_t cols, const double *X,
+                    int64_t n, double *Y)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; r++) {
+        float *wrow = (float *)malloc(sizeof(float) * (size_t)cols);
+        orc_mx4_dequantize(codes + r * cols / 2, scales + r * cols / 32, 1, cols, wrow);
         for (int64_t t = 0; t < n; t++) {
             double acc = 0.0;
             for (int64_t i = 0; i < cols; i++)

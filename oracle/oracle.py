@@ -69,6 +69,13 @@ def lib():
         L.orc_topk.argtypes = [P, I64, I64, ctypes.c_int, P, P]
         L.orc_permute.argtypes = [P, I64, ctypes.c_int, I64, P, P, P, P]
         L.orc_swiglu.argtypes = [P, P, I64, P]
+        L.orc_e2m1_value.restype = ctypes.c_double
+        L.orc_e2m1_value.argtypes = [ctypes.c_int]
+        L.orc_e8m0_value.restype = ctypes.c_double
+        L.orc_e8m0_value.argtypes = [ctypes.c_int]
+        L.orc_mx4_dequantize.argtypes = [P, P, I64, I64, P]
+        L.orc_mx4_quantize.argtypes = [P, I64, I64, P, P]
+        L.orc_mx4_matmul.argtypes = [P, P, I64, I64, P, I64, P]
         L.orc_set_threads.argtypes = [ctypes.c_int]
         L.orc_max_threads.restype = ctypes.c_int
         _lib = L
@@ -126,6 +133,10 @@ def q2k_bytes(rows: int, cols: int) -> int:
     return rows * (cols // QK) * 84
 
 
+def mx4_bytes(rows: int, cols: int) -> int:
+    return rows * cols // 2 + rows * cols // 32
+
+
 def cb2_planes(packed: np.ndarray, rows: int, cols: int):
     nb = cols // QK
     n = rows * nb
@@ -141,6 +152,11 @@ def q2k_planes(packed: np.ndarray, rows: int, cols: int):
     sub = packed[n * 64: n * 80]
     sup = packed[n * 80: n * 84].view(np.uint16)
     return codes, sub, sup
+
+
+def mx4_planes(packed: np.ndarray, rows: int, cols: int):
+    n = rows * cols
+    return packed[: n // 2], packed[n // 2: n // 2 + n // 32]
 
 
 def _check(rows, cols):
@@ -184,6 +200,32 @@ def q2k_dequantize(packed: np.ndarray, rows: int, cols: int) -> np.ndarray:
     return out
 
 
+def e2m1_value(code: int) -> float:
+    return lib().orc_e2m1_value(int(code))
+
+
+def e8m0_value(code: int) -> float:
+    return lib().orc_e8m0_value(int(code))
+
+
+def mx4_quantize(w: np.ndarray) -> np.ndarray:
+    rows, cols = w.shape
+    _check(rows, cols)
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    packed = np.zeros(mx4_bytes(rows, cols), dtype=np.uint8)
+    codes, sc = mx4_planes(packed, rows, cols)
+    lib().orc_mx4_quantize(_p(w), rows, cols, _p(codes), _p(sc))
+    return packed
+
+
+def mx4_dequantize(packed: np.ndarray, rows: int, cols: int) -> np.ndarray:
+    _check(rows, cols)
+    codes, sc = mx4_planes(np.ascontiguousarray(packed), rows, cols)
+    out = np.zeros((rows, cols), dtype=np.float32)
+    lib().orc_mx4_dequantize(_p(codes), _p(sc), rows, cols, _p(out))
+    return out
+
+
 # ---------------------------------------------------------------- products (fp64)
 def cb2_matmul(packed, rows, cols, X: np.ndarray) -> np.ndarray:
     X = np.ascontiguousarray(X, dtype=np.float64)
@@ -200,6 +242,15 @@ def q2k_matmul(packed, rows, cols, X: np.ndarray) -> np.ndarray:
     codes, sub, sup = q2k_planes(packed, rows, cols)
     Y = np.zeros((n, rows), dtype=np.float64)
     lib().orc_q2k_matmul(_p(codes), _p(sub), _p(sup), rows, cols, _p(X), n, _p(Y))
+    return Y
+
+
+def mx4_matmul(packed, rows, cols, X: np.ndarray) -> np.ndarray:
+    X = np.ascontiguousarray(X, dtype=np.float64)
+    n = X.shape[0]
+    codes, sc = mx4_planes(packed, rows, cols)
+    Y = np.zeros((n, rows), dtype=np.float64)
+    lib().orc_mx4_matmul(_p(codes), _p(sc), rows, cols, _p(X), n, _p(Y))
     return Y
 
 
@@ -275,11 +326,13 @@ class Layer:
 
     experts: callable e -> (gate_packed, up_packed, down_packed), or a dict.
     Packed matrices follow the plane layout above; router and shared weights
-    are binary16 bit arrays.
+    are binary16 bit arrays.  expert_fmt: "cb2q2k" (CB2 gate/up, Q2K down)
+    or "mxfp4" (all three in MXFP4).
     """
 
-    def __init__(self, d, E, k, f, fs, router_bits, bias, sh_gate, sh_up, sh_down, experts):
+    def __init__(self, d, E, k, f, fs, router_bits, bias, sh_gate, sh_up, sh_down, experts, expert_fmt="cb2q2k"):
         self.d, self.E, self.k, self.f, self.fs = d, E, k, f, fs
+        self.expert_fmt = expert_fmt
         self.router_bits, self.bias = router_bits, bias
         self.sh_gate, self.sh_up, self.sh_down = sh_gate, sh_up, sh_down
         self._experts = experts
@@ -305,6 +358,10 @@ class Layer:
 
     def expert_out(self, e, Xe):
         gp, up, dp = self.expert(e)
+        if self.expert_fmt == "mxfp4":
+            g = mx4_matmul(gp, self.f, self.d, Xe)
+            u = mx4_matmul(up, self.f, self.d, Xe)
+            return mx4_matmul(dp, self.d, self.f, swiglu(g, u))
         g = cb2_matmul(gp, self.f, self.d, Xe)
         u = cb2_matmul(up, self.f, self.d, Xe)
         return q2k_matmul(dp, self.d, self.f, swiglu(g, u))
