@@ -26,6 +26,10 @@ shared expert, bf16 activations -- in layer-tokens per second.
   * "decode16" times the 16-token batched decode (about 60 distinct experts);
   * "decode_small" times speculative-verify shapes, T = 2, 4, 8 tokens per
     call at the decode1 layer shape;
+  * "mxfp4" times the decode1 shape and the 2048-token prefill with MXFP4
+    routed experts;
+  * "stack43" times 43 decode1-shaped layers resident at once, one token at a
+    time through all of them;
   * "cpu_baseline" times the CPU oracle on a bounded sample of decode tokens,
     on all host threads and on one.
 """
@@ -81,15 +85,15 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def decode_bytes(cfg, n_distinct, T=1):
+def decode_bytes(cfg, n_distinct, T=1, mx=False):
     """Algorithmic HBM bytes of one decode step and of each of its kernels:
     every weight byte the step needs read once, activations read/written once.
     stage 1: router; stage 2: routed gate/up + shared gate and up; stage 3:
     routed down + shared down."""
     from bit_quantized_routed_router_amd import ds4moe as D
     d, f, fs, E, k = cfg.d, cfg.f, cfg.fs, cfg.E, cfg.k
-    cb = D.packed_bytes(D.FMT_CB2, f, d)
-    qb = D.packed_bytes(D.FMT_Q2K, d, f)
+    cb = D.packed_bytes(D.FMT_MXFP4 if mx else D.FMT_CB2, f, d)
+    qb = D.packed_bytes(D.FMT_MXFP4 if mx else D.FMT_Q2K, d, f)
     x_bytes = T * d * 2
     s1 = E * d * 2 + x_bytes
     s2 = n_distinct * 2 * cb + 2 * fs * d * 2 + T * d * 2 + T * k * f * 2 + T * fs * 2
@@ -98,7 +102,7 @@ def decode_bytes(cfg, n_distinct, T=1):
     return dict(total=total, k_dec_stage1=s1, k_dec_stage2=s2, k_dec_stage3=s3)
 
 
-def make_layer(cfg, copies=1, cfg_seed=None):
+def make_layer(cfg, copies=1, cfg_seed=None, mx=False):
     import torch
     from bit_quantized_routed_router_amd import ds4moe as D
     from bit_quantized_routed_router_amd import synthetic as S
@@ -110,8 +114,9 @@ def make_layer(cfg, copies=1, cfg_seed=None):
         return torch.from_numpy(a).cuda()
 
     c = cfg
-    cb = D.packed_bytes(D.FMT_CB2, c.f, c.d)
-    qb = D.packed_bytes(D.FMT_Q2K, c.d, c.f)
+    fgu, fdn = (D.FMT_MXFP4, D.FMT_MXFP4) if mx else (D.FMT_CB2, D.FMT_Q2K)
+    cb = D.packed_bytes(fgu, c.f, c.d)
+    qb = D.packed_bytes(fdn, c.d, c.f)
     gate = torch.empty(c.E * cb, dtype=torch.uint8, device="cuda")
     up = torch.empty(c.E * cb, dtype=torch.uint8, device="cuda")
     down = torch.empty(c.E * qb, dtype=torch.uint8, device="cuda")
@@ -119,19 +124,22 @@ def make_layer(cfg, copies=1, cfg_seed=None):
     for e0 in range(0, c.E, 16):
         es = list(range(e0, min(c.E, e0 + 16)))
         for e, (g, u, dn) in zip(es, S.gen_experts(c, es, threads=16, cfg_seed=cfg_seed)):
-            D.quantize(D.FMT_CB2, dev(g), c.f, c.d, gate[e * cb:(e + 1) * cb])
-            D.quantize(D.FMT_CB2, dev(u), c.f, c.d, up[e * cb:(e + 1) * cb])
-            D.quantize(D.FMT_Q2K, dev(dn), c.d, c.f, down[e * qb:(e + 1) * qb])
+            D.quantize(fgu, dev(g), c.f, c.d, gate[e * cb:(e + 1) * cb])
+            D.quantize(fgu, dev(u), c.f, c.d, up[e * cb:(e + 1) * cb])
+            D.quantize(fdn, dev(dn), c.d, c.f, down[e * qb:(e + 1) * qb])
         torch.cuda.synchronize()
-    log(f"[bench] {c.name}: generated and quantized {c.E} experts in {time.time() - t0:.1f}s")
+    log(f"[bench] {c.name}: generated and quantized {c.E} {'MXFP4' if mx else 'CB2/Q2K'} experts "
+        f"in {time.time() - t0:.1f}s")
+    efmt = D.EXPERTS_MXFP4 if mx else D.EXPERTS_CB2_Q2K
     router = dev(S.gen_router(c, cfg_seed=cfg_seed))
     bias = S.gen_bias(c)
     bias = None if bias is None else dev(bias)
     sh = [dev(a) for a in S.gen_shared(c, cfg_seed=cfg_seed)]
-    layers = [D.Layer(c.d, c.E, c.k, c.f, c.fs, router, bias, sh[0], sh[1], sh[2], gate, up, down)]
+    layers = [D.Layer(c.d, c.E, c.k, c.f, c.fs, router, bias, sh[0], sh[1], sh[2], gate, up, down, efmt)]
     for _ in range(1, copies):
         layers.append(D.Layer(c.d, c.E, c.k, c.f, c.fs, router.clone(), None if bias is None else bias.clone(),
-                              sh[0].clone(), sh[1].clone(), sh[2].clone(), gate.clone(), up.clone(), down.clone()))
+                              sh[0].clone(), sh[1].clone(), sh[2].clone(), gate.clone(), up.clone(), down.clone(),
+                              efmt))
     torch.cuda.synchronize()
     return layers
 
@@ -243,7 +251,7 @@ def bench_decode(args):
     return res
 
 
-def decode_batch(cfg, layers, T, steps, warmup, xvar0):
+def decode_batch(cfg, layers, T, steps, warmup, xvar0, mx=False):
     """K graph-replayed T-token decode steps over the given layer copies (round
     robin) with fresh tokens per step.  Returns us/step, tok/s, the mean
     distinct-expert count and the whole-layer HBM fraction from the
@@ -285,7 +293,7 @@ def decode_batch(cfg, layers, T, steps, warmup, xvar0):
     ms = e0.elapsed_time(e1) / steps
     sel = idx[warmup:].cpu().numpy()
     distinct = [len(np.unique(sel[n])) for n in range(steps)]
-    nbytes = float(np.mean([decode_bytes(cfg, nd, T=T)["total"] for nd in distinct]))
+    nbytes = float(np.mean([decode_bytes(cfg, nd, T=T, mx=mx)["total"] for nd in distinct]))
     del g
     return dict(tok_s=T / (ms * 1e-3), us_per_step=ms * 1e3, distinct_mean=float(np.mean(distinct)),
                 bytes_per_step=nbytes, hbm_frac=nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS)
@@ -325,13 +333,28 @@ def bench_decode_small(copies=4, steps=64, warmup=8, Ts=(2, 4, 8)):
                          "round-robin, graph replay", **out)
 
 
-def bench_prefill(args):
+def bench_mxfp4(steps=64, warmup=8, copies=4):
+    """Side report: a layer whose routed experts are MXFP4 (the model's native
+    expert format), decode at T = 1 over layer copies with graph replay."""
+    import torch
+    from bit_quantized_routed_router_amd import synthetic as S
+
+    cfg = S.CONFIGS["decode1"]
+    layers = make_layer(cfg, copies=copies, mx=True)
+    r = decode_batch(cfg, layers, 1, steps, warmup, 4000, mx=True)
+    del layers
+    torch.cuda.empty_cache()
+    return dict(workload=f"decode1 shape with MXFP4 routed experts (gate, up, down), T=1, {copies} layer copies "
+                         "round-robin, graph replay", **r)
+
+
+def bench_prefill(args, mx=False):
     import torch
     from bit_quantized_routed_router_amd import ds4moe as D
     from bit_quantized_routed_router_amd import synthetic as S
 
     cfg = S.CONFIGS["prefill"]
-    L = make_layer(cfg)[0]
+    L = make_layer(cfg, mx=mx)[0]
     x = torch.from_numpy(S.gen_x(cfg).view(np.int16)).cuda()
     T = cfg.T
     y = torch.empty((T, cfg.d), dtype=torch.float32, device="cuda")
@@ -358,7 +381,8 @@ def bench_prefill(args):
     tflops = flop / (ms * 1e-3) / 1e12
     del L
     torch.cuda.empty_cache()
-    return dict(workload=f"prefill T={T}, Zipf(1.1)-shaped expert loads", tok_s=T / (ms * 1e-3), ms=ms, runs_ms=runs,
+    return dict(workload=f"prefill T={T}, Zipf(1.1)-shaped expert loads" + (", MXFP4 routed experts" if mx else ""),
+                tok_s=T / (ms * 1e-3), ms=ms, runs_ms=runs,
                 flop=flop, tflops=tflops, mfma_frac=tflops / MFMA_F16_PEAK_TFLOPS,
                 kernels={k: dict(mean_us=v[0] / v[1] * 1e3, launches=v[1]) for k, v in kern.items() if v[1] > 0})
 
@@ -570,6 +594,7 @@ def main():
     ap.add_argument("--no-decode-small", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-stack", action="store_true", help="skip the 43-layer stack leg (about 80 GB resident)")
+    ap.add_argument("--no-mxfp4", action="store_true", help="skip the MXFP4-expert side reports")
     ap.add_argument("--stack-tokens", type=int, default=256)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     args = ap.parse_args()
@@ -597,6 +622,13 @@ def main():
     pre = None if args.no_prefill else bench_prefill(args)
     if pre:
         log(f"[bench] prefill: {pre['ms']:.3f} ms, {pre['tok_s']:.0f} tok/s, {pre['tflops']:.1f} TFLOP/s")
+    mxd = None if args.no_mxfp4 else bench_mxfp4()
+    if mxd:
+        log(f"[bench] mxfp4 decode: {mxd['us_per_step']:.1f} us/step, {mxd['tok_s']:.0f} tok/s, "
+            f"{100 * mxd['hbm_frac']:.1f} % of HBM peak")
+    mxp = None if args.no_mxfp4 or args.no_prefill else bench_prefill(args, mx=True)
+    if mxp:
+        log(f"[bench] mxfp4 prefill: {mxp['ms']:.3f} ms, {mxp['tok_s']:.0f} tok/s, {mxp['tflops']:.1f} TFLOP/s")
     stk = None if args.no_stack else bench_stack43(tokens=args.stack_tokens)
     if stk:
         log(f"[bench] stack43: {stk['us_per_token']:.1f} us/token, {stk['tok_s']:.0f} tok/s, "
@@ -644,6 +676,10 @@ def main():
             frac_of_measured_gemm=pre["tflops"] / gemm_tflops,
             kernels_us={k: round(v["mean_us"], 2) for k, v in pre["kernels"].items()}),
         "stack43": stk,
+        "mxfp4": None if mxd is None else dict(
+            decode=mxd, prefill=None if mxp is None else dict(
+                {k: mxp[k] for k in ("workload", "tok_s", "ms", "tflops", "mfma_frac")},
+                kernels_us={k: round(v["mean_us"], 2) for k, v in mxp["kernels"].items()})),
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

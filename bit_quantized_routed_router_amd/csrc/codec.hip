@@ -1,4 +1,4 @@
-// CB2 / Q2K encoders and decoders (byte layouts in include/ds4moe.h).
+// CB2 / Q2K / MXFP4 encoders and decoders (byte layouts in include/ds4moe.h).
 //
 // The pages name the formats only (DS4 (DwarfStar 4) wiki note, "Key
 // Techniques": IQ2_XXS for gate/up, Q2_K for down); the quantizer steps are
@@ -258,6 +258,100 @@ __global__ __launch_bounds__(256) void k_dequant_q2k(const uint8_t* __restrict__
 }
 
 // ---------------------------------------------------------------------------
+// MXFP4 (OCP MX: FP4 E2M1 elements, one E8M0 scale per 32), one lane per
+// block of 32.  Quantizer:
+//  1. amax = max |x|; zero blocks get scale 0 and zero codes;
+//  2. scale code = clamp(floor(log2 amax) - 2 + 127, 0, 254), floor(log2)
+//     read from amax's exponent bits (normal or subnormal);
+//  3. r = |x| * 2^(127 - code) (exact wherever it can change the code:
+//     results below 2^-126, the only ones rounded, all give code 0), then
+//     the nearest E2M1 magnitude, ties to the even code, beyond 6 to 6;
+//     the sign bit for negative x of non-zero magnitude.
+// ---------------------------------------------------------------------------
+__device__ inline int floor_log2_pos(float a) {  // a > 0, finite
+  const uint32_t u = __builtin_bit_cast(uint32_t, a);
+  const int e = (int)(u >> 23);
+  if (e > 0) return e - 127;
+  return (31 - __builtin_clz(u & 0x7FFFFFu)) - 149;  // subnormal: mantissa * 2^-149
+}
+__device__ inline float pow2f(int k) {  // 2^k for -149 <= k <= 127, exact
+  return k >= -126 ? __builtin_bit_cast(float, (uint32_t)(k + 127) << 23)
+                   : __builtin_bit_cast(float, 1u << (k + 149));
+}
+// nearest E2M1 magnitude code of r >= 0, ties to the even code, saturating
+__device__ inline uint32_t e2m1_code(float r) {
+  if (r <= 0.25f) return 0;
+  if (r < 0.75f) return 1;
+  if (r <= 1.25f) return 2;
+  if (r < 1.75f) return 3;
+  if (r <= 2.5f) return 4;
+  if (r < 3.5f) return 5;
+  if (r <= 5.0f) return 6;
+  return 7;
+}
+// E2M1 magnitude of a 3-bit code: exponent 0 subnormal (0, 0.5), else
+// (1 + m/2) * 2^(e - 1)
+__device__ inline float e2m1_mag(uint32_t c) {
+  const uint32_t e = (c >> 1) & 3u, m = c & 1u;
+  return e == 0 ? 0.5f * (float)m : (1.0f + 0.5f * (float)m) * pow2f((int)e - 1);
+}
+
+__global__ __launch_bounds__(256) void k_quant_mx4(const float* __restrict__ w, int64_t nblk,
+                                                   uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+  const int64_t blk = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (blk >= nblk) return;
+  float v[32];
+  const float4* src = (const float4*)(w + blk * 32);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float4 a = src[i];
+    v[4 * i] = a.x;
+    v[4 * i + 1] = a.y;
+    v[4 * i + 2] = a.z;
+    v[4 * i + 3] = a.w;
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  uint32_t out[4] = {0u, 0u, 0u, 0u};
+  int sc = 0;
+  if (amax > 0.0f) {
+    sc = min(max(floor_log2_pos(amax) - 2 + 127, 0), 254);
+    const float inv = pow2f(127 - sc);
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const uint32_t m = e2m1_code(__fmul_rn(fabsf(v[i]), inv));
+      const uint32_t c = m | ((v[i] < 0.0f && m != 0u) ? 8u : 0u);
+      out[i >> 3] |= c << (4 * (i & 7));
+    }
+  }
+  *(u32x4_t*)(codes + blk * 16) = u32x4_t{out[0], out[1], out[2], out[3]};
+  scales[blk] = (uint8_t)sc;
+}
+
+__global__ __launch_bounds__(256) void k_dequant_mx4(const uint8_t* __restrict__ codes,
+                                                     const uint8_t* __restrict__ scales, int64_t nblk,
+                                                     float* __restrict__ out) {
+  const int64_t blk = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (blk >= nblk) return;
+  const u32x4_t cw = *(const u32x4_t*)(codes + blk * 16);
+  const int sc = scales[blk];
+  const float x = sc == 255 ? __builtin_nanf("") : pow2f(sc - 127);
+  float4* dst = (float4*)(out + blk * 32);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    float r[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t c = (cw[i >> 1] >> (4 * (4 * (i & 1) + j))) & 15u;
+      const float m = __fmul_rn(e2m1_mag(c & 7u), x);
+      r[j] = (c & 8u) ? -m : m;
+    }
+    dst[i] = make_float4(r[0], r[1], r[2], r[3]);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
 hipError_t launch_quant_cb2(const float* w, int64_t rows, int64_t cols, void* packed, hipStream_t st) {
@@ -299,6 +393,24 @@ hipError_t launch_dequant_q2k(const void* packed, int64_t rows, int64_t cols, fl
   const int64_t ns = nblk * 16;
   if (ns == 0) return hipSuccess;
   DS4_LAUNCH(k_dequant_q2k, dim3((unsigned)((ns + 255) / 256)), dim3(256), 0, st, codes, sub, sup, ns, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_mx4(const float* w, int64_t rows, int64_t cols, void* packed, hipStream_t st) {
+  const int64_t nblk = rows * (cols / 32);
+  uint8_t* codes = (uint8_t*)packed;
+  uint8_t* scales = codes + nblk * 16;
+  if (nblk == 0) return hipSuccess;
+  DS4_LAUNCH(k_quant_mx4, dim3((unsigned)((nblk + 255) / 256)), dim3(256), 0, st, w, nblk, codes, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant_mx4(const void* packed, int64_t rows, int64_t cols, float* out, hipStream_t st) {
+  const int64_t nblk = rows * (cols / 32);
+  const uint8_t* codes = (const uint8_t*)packed;
+  const uint8_t* scales = codes + nblk * 16;
+  if (nblk == 0) return hipSuccess;
+  DS4_LAUNCH(k_dequant_mx4, dim3((unsigned)((nblk + 255) / 256)), dim3(256), 0, st, codes, scales, nblk, out);
   return hipGetLastError();
 }
 

@@ -211,6 +211,22 @@ __device__ inline uint32_t nib_hi_pair_f16(uint32_t w, int byte0) {
   return as_u32(t - off);
 }
 
+// MXFP4 fragment: the 8 elements of one 32-bit code word (element 2i in the
+// low nibble of byte i) as binary16 with the block scale folded in, by the
+// FP4 conversion instruction; exact for scale codes 104..140 (every product
+// then lies on the binary16 grid).
+__device__ inline float e8m0_f32(uint32_t sc) {  // 2^(sc - 127); sc = 0 gives the subnormal 2^-127
+  return sc ? __builtin_bit_cast(float, sc << 23) : __builtin_bit_cast(float, 0x00400000u);
+}
+__device__ inline half8_t mx4_frag(uint32_t w, float scale) {
+  u32x4_t r;
+  r.x = as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, scale, 0));
+  r.y = as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, scale, 1));
+  r.z = as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, scale, 2));
+  r.w = as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, scale, 3));
+  return as_half8(r);
+}
+
 __device__ inline half8_t zero_half8() {
   u32x4_t z = {0u, 0u, 0u, 0u};
   return as_half8(z);

@@ -357,6 +357,20 @@ __device__ inline half8_t cb2_apply(const Cb2Raw& R, uint32_t aux) {
   return as_half8(r);
 }
 
+// Per lane and super-block b of an MXFP4 [rows, K] matrix: the lane's two
+// blocks 8b + 2q and 8b + 2q + 1 of its row (64 elements, the same K range
+// as a CB2 lane's two sub-blocks) and their two scale bytes.
+struct Mx4Sb {
+  u32x4_t c0, c1;
+  uint32_t sc;  // scale of block 2q in bits 0..7, of block 2q + 1 in bits 8..15
+};
+// step s2 (0..7) of super-block: block 2q + (s2 >> 2), code word s2 & 3
+__device__ inline half8_t mx4_step(const Mx4Sb& W, int s2) {
+  const u32x4_t& c = (s2 & 4) ? W.c1 : W.c0;
+  const uint32_t w = (s2 & 3) == 0 ? c.x : ((s2 & 3) == 1 ? c.y : ((s2 & 3) == 2 ? c.z : c.w));
+  return mx4_frag(w, e8m0_f32((W.sc >> ((s2 & 4) ? 8 : 0)) & 0xFFu));
+}
+
 // Blocks [0, maxd * f/16): one per (distinct expert, 16-row tile) of the
 // routed gate/up products, whose codebook decoding is the arithmetic; then
 // two per 16-row tile of the shared expert (gate, up), an F16 stream
@@ -366,6 +380,10 @@ __device__ inline half8_t cb2_apply(const Cb2Raw& R, uint32_t aux) {
 constexpr int stage2_waves(bool lo, bool bl) { return bl ? (lo ? 2 : 4) : (lo ? 1 : 3); }
 
 template <bool LO, bool BL>
+__device__ void routed_gateup_mx(const ds4moe_layer& L, int T, const RouteOut& ro, const _Float16* __restrict__ xh,
+                                 const _Float16* __restrict__ xl, _Float16* __restrict__ hw16, Stage2Lds<LO, BL>& lds);
+
+template <bool LO, bool BL, bool MX>
 __global__ __launch_bounds__(kW * 64) __attribute__((amdgpu_waves_per_eu(stage2_waves(LO, BL)))) void k_dec_stage2(
     ds4moe_layer L, int T, RouteOut ro, const _Float16* __restrict__ xh,
     const _Float16* __restrict__ xl, _Float16* __restrict__ hw16, _Float16* __restrict__ hsum, int rtiles,
@@ -374,6 +392,10 @@ __global__ __launch_bounds__(kW * 64) __attribute__((amdgpu_waves_per_eu(stage2_
   if ((int)blockIdx.x >= rtiles) {
     shared_gateup_block<LO, BL>(L, T, xh, xl, blockIdx.x - rtiles, gu_part, hs16, ctrl, lds.bh, lds.bl, lds.red,
                                 lds.last);
+    return;
+  }
+  if constexpr (MX) {
+    routed_gateup_mx<LO, BL>(L, T, ro, xh, xl, hw16, lds);
     return;
   }
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -579,6 +601,104 @@ __global__ __launch_bounds__(kW * 64) __attribute__((amdgpu_waves_per_eu(stage2_
   }
 }
 
+// Routed gate/up tile of an MXFP4 layer: as the CB2 tile, with the two code
+// blocks of each super-block turned into binary16 fragments by the FP4
+// conversion (block scales folded in, so no per-super-block scale after the
+// products).  Activations come from LDS when staged (BL), else from the
+// binary16 copy in memory.
+constexpr int kSbMx = 2;  // MXFP4 super-blocks a wave loads at once (32 bytes per matrix and lane each)
+
+template <bool LO, bool BL>
+__device__ void routed_gateup_mx(const ds4moe_layer& L, int T, const RouteOut& ro, const _Float16* __restrict__ xh,
+                                 const _Float16* __restrict__ xl, _Float16* __restrict__ hw16, Stage2Lds<LO, BL>& lds) {
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c = lane & 15, q = lane >> 4;
+  const int tc = min(c, T - 1);
+  const int d = L.d_model, f = L.d_ff, k = L.top_k;
+  const int nr = f / 16, nb = d / QK;
+  const int i = blockIdx.x / nr, tile = blockIdx.x % nr;
+  const int row0 = tile * 16;
+  const int st = stage_stride(d);
+  if (BL) dma_rows(xh, d, T, d, lds.bh, st, wave, kW, lane);
+  if (BL && LO) dma_rows(xl, d, T, d, lds.bl, st, wave, kW, lane);
+  const int nd = ld_uniform(ro.ndist);
+  if (i >= nd) {
+    wait_all();
+    return;
+  }
+  const int e = clamp_index(ld_uniform(ro.distinct + i), L.n_experts);
+  const size_t mbytes = (size_t)f * d * 17 / 32;  // one packed [f, d] matrix
+  const uint8_t* gm = (const uint8_t*)L.gate + (size_t)e * mbytes;
+  const uint8_t* um = (const uint8_t*)L.up + (size_t)e * mbytes;
+  const uint8_t* grow = gm + (size_t)(row0 + c) * (d / 2) + 32 * q;
+  const uint8_t* urow = um + (size_t)(row0 + c) * (d / 2) + 32 * q;
+  const uint8_t* gsc = gm + (size_t)f * d / 2 + (size_t)(row0 + c) * (d / 32) + 2 * q;
+  const uint8_t* usc = um + (size_t)f * d / 2 + (size_t)(row0 + c) * (d / 32) + 2 * q;
+  int sb0, sb1;
+  split_range(nb, kW, wave, sb0, sb1);
+  Mx4Sb wg[kSbMx], wu[kSbMx];
+  auto load_batch = [&](int b0) {
+#pragma unroll
+    for (int j = 0; j < kSbMx; ++j) {
+      const int b = max(min(b0 + j, sb1 - 1), 0);
+      wg[j].c0 = __builtin_nontemporal_load((const u32x4_t*)(grow + 128 * b));
+      wg[j].c1 = __builtin_nontemporal_load((const u32x4_t*)(grow + 128 * b + 16));
+      wu[j].c0 = __builtin_nontemporal_load((const u32x4_t*)(urow + 128 * b));
+      wu[j].c1 = __builtin_nontemporal_load((const u32x4_t*)(urow + 128 * b + 16));
+      wg[j].sc = *(const uint16_t*)(gsc + 8 * b);
+      wu[j].sc = *(const uint16_t*)(usc + 8 * b);
+    }
+  };
+  load_batch(sb0);
+  wait_all();  // the copies (and the first batch)
+  __syncthreads();
+  float4_t ag = {0.f, 0.f, 0.f, 0.f}, au = ag;
+  for (int b0 = sb0; b0 < sb1; b0 += kSbMx) {
+    if (b0 != sb0) load_batch(b0);
+    pin();
+#pragma unroll
+    for (int t = 0; t < 8 * kSbMx; ++t) {
+      const int j = t >> 3, s2 = t & 7;
+      if (b0 + j >= sb1) break;  // wave-uniform
+      const int kk = (b0 + j) * QK + cb2_boff(q, s2);
+      half8_t bh, bl;
+      if (BL) {
+        bh = *(const half8_t*)(lds.bh + tc * st + kk);
+        if (LO) bl = *(const half8_t*)(lds.bl + tc * st + kk);
+      } else {
+        bh = *(const half8_t*)(xh + (int64_t)tc * d + kk);
+        if (LO) bl = *(const half8_t*)(xl + (int64_t)tc * d + kk);
+      }
+      const half8_t a0 = mx4_step(wg[j], s2), a1 = mx4_step(wu[j], s2);
+      ag = mfma16x16x32(bh, a0, ag);
+      au = mfma16x16x32(bh, a1, au);
+      if (LO) {
+        ag = mfma16x16x32(bl, a0, ag);
+        au = mfma16x16x32(bl, a1, au);
+      }
+    }
+  }
+  lds.red[wave][lane] = ag;
+  lds.red2[wave][lane] = au;
+  __syncthreads();
+  if (wave != 0) return;
+  ag = lds.red[0][lane];
+  au = lds.red2[0][lane];
+#pragma unroll
+  for (int w = 1; w < kW; ++w) {
+    ag += lds.red[w][lane];
+    au += lds.red2[w][lane];
+  }
+  const int4 sl4 = *(const int4*)(ro.tok_slot + i * kDecodeGroup + 4 * q);
+  const int slots[4] = {sl4.x, sl4.y, sl4.z, sl4.w};
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int slot = slots[r];
+    if (4 * q + r < T && slot >= 0 && slot < T * k)
+      hw16[(int64_t)slot * f + row0 + c] = (_Float16)(ro.w[slot] * (silu(ag[r]) * au[r]));
+  }
+}
+
 // ============================================================== stage 3
 // Weight operands of one (expert, super-block) Q2K unit for lane (c, q):
 // its row is row0 + c.
@@ -662,7 +782,17 @@ constexpr int kUnits3 = 3;  // units whose weight loads a wave keeps in flight
 // whole sum stays in the block and it writes y = ys + the routed terms
 // itself.  The routed weights are requested first: their decode is the
 // arithmetic, and the shared expert's F16 rows stream in behind them.
-template <bool BL>
+// One MXFP4 down unit, transposed like q2k_unit: 8 steps over the lane's
+// two blocks (scales folded into the binary16 weights), no min term.
+__device__ inline void mx4_unit(const Mx4Sb& U, const Q2kA& A, uint32_t vmask, float4_t& acc) {
+  float4_t p = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s2 = 0; s2 < 8; ++s2) p = mfma16x16x32(A.b[s2], mx4_step(U, s2), p);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) acc[r] += ((vmask >> r) & 1u) ? p[r] : 0.0f;
+}
+
+template <bool BL, bool MX>
 __global__ __launch_bounds__(kW3 * 64) __attribute__((amdgpu_waves_per_eu(4))) void k_dec_stage3(
     ds4moe_layer L, int T, const int32_t* __restrict__ ndist, const int32_t* __restrict__ distinct,
     const int32_t* __restrict__ tok_slot, const _Float16* __restrict__ hw16, const _Float16* __restrict__ hsum,
@@ -689,7 +819,7 @@ __global__ __launch_bounds__(kW3 * 64) __attribute__((amdgpu_waves_per_eu(4))) v
   // copies of the activations into LDS; one barrier publishes them
   if (BL) {
     dma_rows(hw16, f, S, f, s_h, f, wave, kW3, lane);
-    dma_rows(hsum, fs16, 2 * S, fs16, s_cs, fs16, wave, kW3, lane);
+    if (!MX) dma_rows(hsum, fs16, 2 * S, fs16, s_cs, fs16, wave, kW3, lane);
     dma_rows(hs16, fs, T, fs, s_hs, fs, wave, kW3, lane);
   }
   // routing tables: expert ids by scalar loads, which do not wait for the
@@ -700,7 +830,11 @@ __global__ __launch_bounds__(kW3 * 64) __attribute__((amdgpu_waves_per_eu(4))) v
   // u = w, w + kW3, ... in batches of kUnits3
   int sj[kUnits3], bsb[kUnits3];  // per unit: slot of token c, super-block
   Q2kW W[kUnits3];
+  Mx4Sb WM[kUnits3];  // MXFP4: the lane's two blocks of the unit's super-block
   const Q2kOff off = q2k_offsets(mb, nb, row0, c, q);
+  const size_t mx_bytes = (size_t)d * f * 17 / 32;  // one packed MXFP4 [d, f] matrix
+  const uint32_t mx_codes = (uint32_t)((size_t)(row0 + c) * (f / 2) + 32 * q);
+  const uint32_t mx_sc = (uint32_t)((size_t)d * f / 2 + (size_t)(row0 + c) * (f / 32) + 2 * q);
   // unit u -> (expert slot u / nb, super-block u % nb), stepped by kW3
   // without a division per unit
   const int di = kW3 / nb, db = kW3 % nb;
@@ -736,7 +870,14 @@ __global__ __launch_bounds__(kW3 * 64) __attribute__((amdgpu_waves_per_eu(4))) v
     pin();
 #pragma unroll
     for (int j = 0; j < kUnits3; ++j) {
-      q2k_wload(W[j], down + (size_t)clamp_index(ej[j], L.n_experts) * mb * 84, off, bj[j]);
+      if constexpr (MX) {
+        const uint8_t* base = down + (size_t)clamp_index(ej[j], L.n_experts) * mx_bytes;
+        WM[j].c0 = __builtin_nontemporal_load((const u32x4_t*)(base + mx_codes + 128 * bj[j]));
+        WM[j].c1 = __builtin_nontemporal_load((const u32x4_t*)(base + mx_codes + 128 * bj[j] + 16));
+        WM[j].sc = *(const uint16_t*)(base + mx_sc + 8 * bj[j]);
+      } else {
+        q2k_wload(W[j], down + (size_t)clamp_index(ej[j], L.n_experts) * mb * 84, off, bj[j]);
+      }
       sj[j] = tok_slot[ij[j] * kDecodeGroup + c];
       bsb[j] = bj[j];
     }
@@ -772,13 +913,20 @@ __global__ __launch_bounds__(kW3 * 64) __attribute__((amdgpu_waves_per_eu(4))) v
       const int row = has ? slot : 0;
       const int b = bsb[j];  // super-block
       Q2kA A;
-      if (BL)
-        q2k_act(A, s_h + (size_t)row * f + b * QK, s_cs + (size_t)row * fs16 + b * 16,
-                s_cs + (size_t)(S + row) * fs16 + b * 16, q);
-      else
-        q2k_act(A, hw16 + (size_t)row * f + b * QK, hsum + (size_t)row * fs16 + b * 16,
-                hsum + (size_t)(S + row) * fs16 + b * 16, q);
-      q2k_unit(W[j], A, vmask, q, acc);
+      if constexpr (MX) {
+        const _Float16* bcol = (BL ? s_h : hw16) + (size_t)row * f + b * QK;
+#pragma unroll
+        for (int s2 = 0; s2 < 8; ++s2) A.b[s2] = *(const half8_t*)(bcol + q2k_boff(q, s2));
+        mx4_unit(WM[j], A, vmask, acc);
+      } else {
+        if (BL)
+          q2k_act(A, s_h + (size_t)row * f + b * QK, s_cs + (size_t)row * fs16 + b * 16,
+                  s_cs + (size_t)(S + row) * fs16 + b * 16, q);
+        else
+          q2k_act(A, hw16 + (size_t)row * f + b * QK, hsum + (size_t)row * fs16 + b * 16,
+                  hsum + (size_t)(S + row) * fs16 + b * 16, q);
+        q2k_unit(W[j], A, vmask, q, acc);
+      }
     }
   }
   // shared expert, transposed like the routed units: lane (c, q) ends with
@@ -993,7 +1141,7 @@ __global__ __launch_bounds__(kW3 * 64) __attribute__((amdgpu_waves_per_eu(4))) v
 }
 
 // ============================================================== launcher
-template <bool LO, bool BL>
+template <bool LO, bool BL, bool MX>
 static void launch_stages12(const Fwd& f, int rblocks, int nsh, int maxd, int nr, const RouteOut& ro) {
   const ds4moe_layer& L = f.L;
   const WsLayout& y = f.lay;
@@ -1009,7 +1157,7 @@ static void launch_stages12(const Fwd& f, int rblocks, int nsh, int maxd, int nr
   auto hsum = (_Float16*)(ws + y.hsum);
   const dim3 blk(kW * 64);
   DS4_LAUNCH((k_dec_stage1<LO>), dim3(rblocks), blk, 0, f.st, L, T, f.x, rblocks, plog, ro, xh, xl, ctrl);
-  DS4_LAUNCH((k_dec_stage2<LO, BL>), dim3(maxd * nr + 2 * nsh), blk, 0, f.st, L, T, ro, xh, xl, hw16, hsum,
+  DS4_LAUNCH((k_dec_stage2<LO, BL, MX>), dim3(maxd * nr + 2 * nsh), blk, 0, f.st, L, T, ro, xh, xl, hw16, hsum,
              maxd * nr, gu, hs16, ctrl);
 }
 
@@ -1026,13 +1174,18 @@ hipError_t launch_decode(const Fwd& f) {
   // stage the activations in LDS when every staged row set fits: the x
   // halves (stages 1 and 2) and x (stage 2 routed)
   const bool bl = (int64_t)T * d <= kStageHalves;
+  const bool mx = L.expert_fmt == DS4MOE_EXPERTS_MXFP4;
+#define DS4_S12(LO_, BL_)                                                   \
+  (mx ? launch_stages12<LO_, BL_, true>(f, rblocks, nsh, maxd, nr, ro)   \
+      : launch_stages12<LO_, BL_, false>(f, rblocks, nsh, maxd, nr, ro))
   if (f.lo) {
-    if (bl) launch_stages12<true, true>(f, rblocks, nsh, maxd, nr, ro);
-    else launch_stages12<true, false>(f, rblocks, nsh, maxd, nr, ro);
+    if (bl) DS4_S12(true, true);
+    else DS4_S12(true, false);
   } else {
-    if (bl) launch_stages12<false, true>(f, rblocks, nsh, maxd, nr, ro);
-    else launch_stages12<false, false>(f, rblocks, nsh, maxd, nr, ro);
+    if (bl) DS4_S12(false, true);
+    else DS4_S12(false, false);
   }
+#undef DS4_S12
   auto ctrl = (int32_t*)(ws + y.ctrl);
   auto hs16 = (const _Float16*)(ws + y.hs16);
   auto hw16 = (_Float16*)(ws + y.hw16);
@@ -1046,17 +1199,22 @@ hipError_t launch_decode(const Fwd& f) {
   // one token: the dot-product form (pairs, OFF and HS sums, shared h)
   const size_t one_bytes = (size_t)L.top_k * L.d_ff * 2 + (size_t)2 * L.top_k * (L.d_ff / 16) * 4 +
                            (size_t)L.d_ff_shared * 2;
-  if (T == 1 && one_bytes <= kStage3OneBytes) {
+  if (T == 1 && one_bytes <= kStage3OneBytes && !mx) {
     DS4_LAUNCH(k_dec_stage3_one, dim3(ndt), blk3, one_bytes, f.st, L, ro.ndist, ro.distinct, ro.tok_slot, hw16,
                hs16, ctrl, ctrl_ints(L), maxd, f.y);
     return hipGetLastError();
   }
-  if (stage_bytes <= kStage3Bytes)
-    DS4_LAUNCH(k_dec_stage3<true>, dim3(ndt), blk3, stage_bytes, f.st, L, T, ro.ndist, ro.distinct, ro.tok_slot, hw16,
-               hsum, hs16, ctrl, ctrl_ints(L), maxd, f.y);
-  else
-    DS4_LAUNCH(k_dec_stage3<false>, dim3(ndt), blk3, 0, f.st, L, T, ro.ndist, ro.distinct, ro.tok_slot, hw16, hsum,
-               hs16, ctrl, ctrl_ints(L), maxd, f.y);
+#define DS4_S3(BL_, MX_, BYTES)                                                                                  \
+  DS4_LAUNCH((k_dec_stage3<BL_, MX_>), dim3(ndt), blk3, BYTES, f.st, L, T, ro.ndist, ro.distinct, ro.tok_slot, hw16, \
+             hsum, hs16, ctrl, ctrl_ints(L), maxd, f.y)
+  if (stage_bytes <= kStage3Bytes) {
+    if (mx) DS4_S3(true, true, stage_bytes);
+    else DS4_S3(true, false, stage_bytes);
+  } else {
+    if (mx) DS4_S3(false, true, 0);
+    else DS4_S3(false, false, 0);
+  }
+#undef DS4_S3
   return hipGetLastError();
 }
 

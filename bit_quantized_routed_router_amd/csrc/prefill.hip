@@ -197,25 +197,29 @@ struct GuLds {
   float w[kTT];
   uint16_t dsc[NBS ? 2 * 128 * NBS : 2];
 };
-template <bool DENSE>
-constexpr int gu_nbs() { return DENSE ? 0 : 16; }
+template <bool DENSE, bool MX = false>
+constexpr int gu_nbs() { return DENSE || MX ? 0 : 16; }
 
 // Weights of one 128-input chunk for a lane's four fragments.  CB2: the lane's sub-block (8 bytes) and its block's d; F16:
 // the lane's 4 x 8 binary16 values (inputs 32q .. 32q+31 of the chunk).  kLoads counts the vector-memory loads of a
 // chunk when every scale comes from LDS; kMaxLoads when they are all read from memory (blocks past the staged ones).
-template <bool F16>
+// MXFP4: the lane's 32 inputs of the chunk are one MX block, 16 code bytes and
+// one scale byte per fragment.
+template <bool F16, bool MX = false>
 struct GuW {
-  u32x2_t cw[4];
+  u32x2_t cw[MX ? 1 : 4];
   uint32_t dv[4];
   u32x4_t wv[F16 ? 4 : 1][F16 ? 4 : 1];
-  static constexpr int kLoads = F16 ? 16 : 4;
+  u32x4_t mw[MX ? 4 : 1];
+  static constexpr int kLoads = F16 ? 16 : (MX ? 8 : 4);
   static constexpr int kMaxLoads = F16 ? 16 : 8;
 };
 
 // Gate/up of one work tile (up to 128 slots) for a 128-row slice of h, NF
 // slot fragments.  DENSE: the shared expert (F16 weights, weight 1, rows are
-// tokens); otherwise routed expert e (CB2 weights, routing weights s.w).
-template <bool LO, bool DENSE, int NW, int TC, int RING, int NF, int NBS>
+// tokens); otherwise routed expert e (CB2 weights, or MXFP4 with MX; routing
+// weights s.w).
+template <bool LO, bool DENSE, int NW, int TC, int RING, int NF, int NBS, bool MX = false>
 __device__ __attribute__((always_inline)) inline void gateup_tile(const ds4moe_layer& L, GuLds<LO, TC, RING, NBS>& s,
                                                                   const _Float16* __restrict__ xh,
                                                                   const _Float16* __restrict__ xl, int e, int rt,
@@ -223,19 +227,24 @@ __device__ __attribute__((always_inline)) inline void gateup_tile(const ds4moe_l
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, c = lane & 15, q = lane >> 4;
   const int d = L.d_model, fd = DENSE ? L.d_ff_shared : L.d_ff, nb = d / QK, nch = d / kKC;
   const size_t mb = (size_t)fd * nb;
-  const uint8_t* gb = DENSE ? (const uint8_t*)L.sh_gate : (const uint8_t*)L.gate + (size_t)e * mb * 66;
-  const uint8_t* ub = DENSE ? (const uint8_t*)L.sh_up : (const uint8_t*)L.up + (size_t)e * mb * 66;
-  const uint8_t* gd = gb + mb * 64;
-  const uint8_t* ud = ub + mb * 64;
+  const size_t mat_bytes = MX ? (size_t)fd * d * 17 / 32 : mb * 66;
+  const uint8_t* gb = DENSE ? (const uint8_t*)L.sh_gate : (const uint8_t*)L.gate + (size_t)e * mat_bytes;
+  const uint8_t* ub = DENSE ? (const uint8_t*)L.sh_up : (const uint8_t*)L.up + (size_t)e * mat_bytes;
+  const uint8_t* gd = gb + (MX ? (size_t)fd * d / 2 : mb * 64);  // CB2 d plane / MXFP4 scale plane
+  const uint8_t* ud = ub + (MX ? (size_t)fd * d / 2 : mb * 64);
   const int hr0 = rt * 32 * NW + 32 * wave;
   // fragment f: rows hr0 + 16 (f & 1) + c of gate (f < 2) or up (f >= 2)
   uint32_t rowu[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) rowu[h] = (uint32_t)((hr0 + 16 * h + c) * (DENSE ? d : nb));
-  auto load_w = [&](int ch, GuW<DENSE>& W) {
+  auto load_w = [&](int ch, GuW<DENSE, MX>& W) {
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
-      if constexpr (DENSE) {
+      if constexpr (MX) {  // row hr0 + 16 (f & 1) + c, block 4 ch + q
+        const uint32_t r = (uint32_t)(hr0 + 16 * (f & 1) + c), blk = (uint32_t)(4 * ch + q);
+        W.mw[f] = ld_at<u32x4_t>(f < 2 ? gb : ub, r * (uint32_t)(d / 2) + 16u * blk);
+        W.dv[f] = ld_at<uint8_t>(f < 2 ? gd : ud, r * (uint32_t)(d / 32) + blk);
+      } else if constexpr (DENSE) {
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           W.wv[f][j] = ld_at<u32x4_t>(f < 2 ? gb : ub, 2u * (rowu[f & 1] + (uint32_t)(ch * kKC + 32 * q + 8 * j)));
@@ -258,11 +267,11 @@ __device__ __attribute__((always_inline)) inline void gateup_tile(const ds4moe_l
 
   // Loads per chunk and lane.  The ring depth keeps the largest count within the load counter; the waits use the
   // smallest, which is exact when every scale is staged and waits longer than needed otherwise.
-  constexpr int kBatch = dma_per_wave(NF, NW) * (LO ? 2 : 1) + GuW<DENSE>::kLoads;
-  constexpr int R = ring_depth(NF, dma_per_wave(NF, NW) * (LO ? 2 : 1) + GuW<DENSE>::kMaxLoads, LO, RING);
+  constexpr int kBatch = dma_per_wave(NF, NW) * (LO ? 2 : 1) + GuW<DENSE, MX>::kLoads;
+  constexpr int R = ring_depth(NF, dma_per_wave(NF, NW) * (LO ? 2 : 1) + GuW<DENSE, MX>::kMaxLoads, LO, RING);
   constexpr int kSlot = NF * 16 * kKC;  // halves per ring slot
   static_assert(R * kSlot <= RING, "ring slots exceed the staging buffer");
-  GuW<DENSE> W[R];
+  GuW<DENSE, MX> W[R];
   auto issue = [&](int ch, int u) {
     stage_rows<LO, NF, NW>(xh, xl, rows, ch, s.xh + u * kSlot, s.xl + (LO ? u * kSlot : 0), wave, lane);
     load_w(ch, W[u]);
@@ -271,7 +280,11 @@ __device__ __attribute__((always_inline)) inline void gateup_tile(const ds4moe_l
   const uint32_t* tsgn = s.tab.sgn + 4 * (lane % TC);
   auto compute = [&](int u) {
     half2_t D2[4];
-    if constexpr (!DENSE) {
+    float XS[4];  // MXFP4 block scales
+    if constexpr (MX) {
+#pragma unroll
+      for (int f = 0; f < 4; ++f) XS[f] = e8m0_f32(W[u].dv[f] & 0xFFu);
+    } else if constexpr (!DENSE) {
 #pragma unroll
       for (int f = 0; f < 4; ++f) D2[f] = h2splat(f16f(W[u].dv[f]) * (float)(2 * (W[u].cw[f].y >> 28) + 1));
     }
@@ -281,7 +294,9 @@ __device__ __attribute__((always_inline)) inline void gateup_tile(const ds4moe_l
       half8_t wf[4];
 #pragma unroll
       for (int f = 0; f < 4; ++f) {
-        if constexpr (DENSE)
+        if constexpr (MX)
+          wf[f] = mx4_frag(W[u].mw[f][j], XS[f]);
+        else if constexpr (DENSE)
           wf[f] = as_half8(W[u].wv[f][j]);
         else
           wf[f] = cb2_frag_scaled<TC>(W[u].cw[f].x, W[u].cw[f].y, j, tmag, tsgn, D2[f]);
@@ -366,7 +381,8 @@ template <bool LO, bool DENSE>
 constexpr int gu_copies() { return 1; }
 
 // SMALL: the small-tile list (at most 32 slots per tile, a smaller ring).
-template <bool LO, bool DENSE, bool SMALL>
+// MX: the routed experts are MXFP4.
+template <bool LO, bool DENSE, bool SMALL, bool MX = false>
 __global__ __launch_bounds__((gu_waves<LO, DENSE>() * 64))
 __attribute__((amdgpu_waves_per_eu(DENSE || LO ? 1 : 2))) void k_pf_gateup(
     ds4moe_layer L, int64_t T, const _Float16* __restrict__ xh, const _Float16* __restrict__ xl,
@@ -374,14 +390,14 @@ __attribute__((amdgpu_waves_per_eu(DENSE || LO ? 1 : 2))) void k_pf_gateup(
     const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets, const int32_t* __restrict__ perm,
     const float* __restrict__ topk_w, _Float16* __restrict__ hout) {
   constexpr int NW = gu_waves<LO, DENSE>(), TC = gu_copies<LO, DENSE>(), RING = ring_halves(SMALL);
-  constexpr int NBS = gu_nbs<DENSE>();
+  constexpr int NBS = gu_nbs<DENSE, MX>();
   static_assert(NW == 4, "the staged scales cover 4 waves x 32 rows");
   __shared__ GuLds<LO, TC, RING, NBS> s;
   int e, rt, pos0, n;
   if (!tile_of<DENSE, SMALL>((DENSE ? L.d_ff_shared : L.d_ff) / (32 * NW), T, tiles, stiles, ntiles, counts, offsets,
                              e, rt, pos0, n))
     return;
-  if constexpr (!DENSE) {
+  if constexpr (!DENSE && !MX) {
     s.tab.stage(c_pre_tables);
     // scales of rows rt*128 .. +127 of gate (g = 0) and up (g = 1), blocks 0 .. ns-1
     const int nb = L.d_model / QK, ns = min(nb, NBS);
@@ -404,7 +420,7 @@ __attribute__((amdgpu_waves_per_eu(DENSE || LO ? 1 : 2))) void k_pf_gateup(
     }
   }
   __syncthreads();
-#define DS4_GU(NF) gateup_tile<LO, DENSE, NW, TC, RING, NF, NBS>(L, s, xh, xl, e, rt, pos0, n, hout)
+#define DS4_GU(NF) gateup_tile<LO, DENSE, NW, TC, RING, NF, NBS, MX>(L, s, xh, xl, e, rt, pos0, n, hout)
   DS4_NF_SWITCH(n, SMALL, DENSE, DS4_GU)
 #undef DS4_GU
 }
@@ -433,18 +449,20 @@ constexpr int kDnStagedMax = 8;
 // aligned word holding their two scale bytes, the block's d/dmin; F16: 4 x 8
 // binary16 values per fragment.  kLoads / kMaxLoads: vector-memory loads of a
 // chunk with the scales staged in LDS / read from memory.
-template <bool F16, bool SC, bool DD>
+template <bool F16, bool SC, bool DD, bool MX = false>
 struct DnW {
-  u32x2_t cw[4];
-  uint32_t sc[4], dd[4];
+  u32x2_t cw[MX ? 1 : 4];
+  uint32_t sc[4], dd[MX ? 1 : 4];
   u32x4_t wv[F16 ? 4 : 1][F16 ? 4 : 1];
-  static constexpr int kMaxLoads = F16 ? 16 : 12;
-  static constexpr int kLoads = F16 ? 16 : 4 + (SC ? 0 : 4) + (DD ? 0 : 4);
+  u32x4_t mw[MX ? 4 : 1];  // MXFP4: the lane's block of 32 (16 code bytes); its scale byte in sc
+  static constexpr int kMaxLoads = F16 ? 16 : (MX ? 8 : 12);
+  static constexpr int kLoads = F16 ? 16 : (MX ? 8 : 4 + (SC ? 0 : 4) + (DD ? 0 : 4));
 };
 
 // Down product of one work tile for a 256-row slice of the output.  Routed
-// (Q2K): yp[slot] = D_e h.  DENSE (shared, F16): y[t] = Wsd hs16[t].
-template <bool DENSE, int RING, int NF, int NBS, bool SC, bool FULL>
+// (Q2K, or MXFP4 with MX): yp[slot] = D_e h.  DENSE (shared, F16):
+// y[t] = Wsd hs16[t].
+template <bool DENSE, int RING, int NF, int NBS, bool SC, bool FULL, bool MX = false>
 __device__ __attribute__((always_inline)) inline void down_tile(const ds4moe_layer& L, DnLds<RING, NBS, SC>& s,
                                                                 const _Float16* __restrict__ hin, int e, int rt,
                                                                 int pos0, int n, float* __restrict__ yp,
@@ -452,16 +470,21 @@ __device__ __attribute__((always_inline)) inline void down_tile(const ds4moe_lay
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, c = lane & 15, q = lane >> 4;
   const int d = L.d_model, fd = DENSE ? L.d_ff_shared : L.d_ff, nb = fd / QK, nch = fd / kKC;
   const size_t mb = (size_t)d * nb;
-  const uint8_t* base = DENSE ? (const uint8_t*)L.sh_down : (const uint8_t*)L.down + (size_t)e * mb * 84;
-  const uint8_t* sub = base + mb * 64;
+  const size_t mat_bytes = MX ? (size_t)d * fd * 17 / 32 : mb * 84;
+  const uint8_t* base = DENSE ? (const uint8_t*)L.sh_down : (const uint8_t*)L.down + (size_t)e * mat_bytes;
+  const uint8_t* sub = base + (MX ? (size_t)d * fd / 2 : mb * 64);  // Q2K sub-scales / MXFP4 scale plane
   const uint8_t* sup = base + mb * 80;
   const int r0 = rt * 256 + 64 * wave;
   const uint32_t row0 = (uint32_t)((r0 + c) * (DENSE ? fd : nb));  // fragment f: + 16 f (fd or nb)
-  using WT = DnW<DENSE, SC, (NBS > 0)>;
+  using WT = DnW<DENSE, SC, (NBS > 0), MX>;
   auto load_w = [&](int ch, WT& W) {
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
-      if constexpr (DENSE) {
+      if constexpr (MX) {  // row r0 + 16 f + c, block 4 ch + q
+        const uint32_t r = (uint32_t)(r0 + 16 * f + c), blk = (uint32_t)(4 * ch + q);
+        W.mw[f] = ld_at<u32x4_t>(base, r * (uint32_t)(fd / 2) + 16u * blk);
+        W.sc[f] = ld_at<uint8_t>(sub, r * (uint32_t)(fd / 32) + blk);
+      } else if constexpr (DENSE) {
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           W.wv[f][j] = ld_at<u32x4_t>(base, 2u * (row0 + (uint32_t)(16 * f * fd + ch * kKC + 32 * q + 8 * j)));
@@ -502,6 +525,24 @@ __device__ __attribute__((always_inline)) inline void down_tile(const ds4moe_lay
   const half2_t k1024 = {(_Float16)-1024.0f, (_Float16)-1024.0f};
   auto compute = [&](int u) {
     const _Float16* bh = s.xh + u * kSlot;
+    if constexpr (MX) {
+      float XS[4];
+#pragma unroll
+      for (int f = 0; f < 4; ++f) XS[f] = e8m0_f32(W[u].sc[f] & 0xFFu);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {  // code word j: inputs 32q + 8j .. +7 of the chunk
+        half8_t wf[4];
+#pragma unroll
+        for (int f = 0; f < 4; ++f) wf[f] = mx4_frag(W[u].mw[f][j], XS[f]);
+#pragma unroll
+        for (int i = 0; i < NF; ++i) {
+          const half8_t a = slot_frag(bh, i, c, q, j);
+#pragma unroll
+          for (int f = 0; f < 4; ++f) acc[f][i] = mfma16x16x32(a, wf[f], acc[f][i]);
+        }
+      }
+      return;
+    }
     auto half_chunk = [&](int h) {  // Q2K: sub-block 2q + h of the chunk feeds steps 2h, 2h+1
       half2_t A2[4], nB2[4];         // binary16 d * s and -(dmin * m) of the sub-block
       if constexpr (!DENSE) {
@@ -562,9 +603,9 @@ __device__ __attribute__((always_inline)) inline void down_tile(const ds4moe_lay
   }
 }
 
-// Routed down (Q2K) over the work list into yp, or (DENSE) the shared
-// expert's down (F16) over all T tokens into y.
-template <bool DENSE, bool SMALL, bool DDS>
+// Routed down (Q2K, or MXFP4 with MX) over the work list into yp, or (DENSE)
+// the shared expert's down (F16) over all T tokens into y.
+template <bool DENSE, bool SMALL, bool DDS, bool MX = false>
 __global__ __launch_bounds__(kGW * 64)
 __attribute__((amdgpu_waves_per_eu(DENSE ? 1 : 2))) void k_pf_down(
     ds4moe_layer L, int64_t T, const int32_t* __restrict__ tiles, const int32_t* __restrict__ stiles,
@@ -572,8 +613,8 @@ __attribute__((amdgpu_waves_per_eu(DENSE ? 1 : 2))) void k_pf_down(
     const int32_t* __restrict__ perm, const _Float16* __restrict__ hin, float* __restrict__ yp,
     float* __restrict__ y) {
   constexpr int RING = ring_halves(SMALL);
-  constexpr int NBS = dn_nbs<DENSE, SMALL, DDS>();
-  constexpr bool SC = !DENSE && SMALL;
+  constexpr int NBS = MX ? 0 : dn_nbs<DENSE, SMALL, DDS>();
+  constexpr bool SC = !DENSE && SMALL && !MX;
   static_assert(!DDS || (!DENSE && !SMALL), "DDS: large routed tiles");
   __shared__ DnLds<RING, NBS, SC> s;
   int e, rt, pos0, n;
@@ -598,7 +639,7 @@ __attribute__((amdgpu_waves_per_eu(DENSE ? 1 : 2))) void k_pf_down(
     }
   }
   __syncthreads();
-#define DS4_DN(NF) down_tile<DENSE, RING, NF, NBS, SC, DDS>(L, s, hin, e, rt, pos0, n, yp, y)
+#define DS4_DN(NF) down_tile<DENSE, RING, NF, NBS, SC, DDS, MX>(L, s, hin, e, rt, pos0, n, yp, y)
   DS4_NF_SWITCH(n, SMALL, DENSE, DS4_DN)
 #undef DS4_DN
 }
@@ -648,27 +689,42 @@ hipError_t launch_prefill_experts(const Fwd& f) {
   const dim3 gsh((unsigned)(ttiles * (L.d_ff_shared / 128))), gsd((unsigned)(ttiles * (d / 256)));
   const dim3 ggu((unsigned)(maxtiles * gr)), ggs((unsigned)(E * gr));
   const dim3 gdn((unsigned)(maxtiles * (d / 256))), gds((unsigned)(E * (d / 256)));
-#define DS4_GU_LAUNCH(LO, DENSE, SMALL, grid, out)                                                                  \
-  DS4_LAUNCH((k_pf_gateup<LO, DENSE, SMALL>), grid, blk, 0, f.st, L, T, xh, xl, tiles, stiles, ntiles, counts, \
+  const bool mx = L.expert_fmt == DS4MOE_EXPERTS_MXFP4;
+#define DS4_GU_LAUNCH(LO, DENSE, SMALL, MX, grid, out)                                                                \
+  DS4_LAUNCH((k_pf_gateup<LO, DENSE, SMALL, MX>), grid, blk, 0, f.st, L, T, xh, xl, tiles, stiles, ntiles, counts, \
              offsets, perm, w, out)
   if (f.lo) {
-    DS4_GU_LAUNCH(true, true, false, gsh, hs16);
-    DS4_GU_LAUNCH(true, false, false, ggu, hw16);
-    DS4_GU_LAUNCH(true, false, true, ggs, hw16);
+    DS4_GU_LAUNCH(true, true, false, false, gsh, hs16);
+    if (mx) {
+      DS4_GU_LAUNCH(true, false, false, true, ggu, hw16);
+      DS4_GU_LAUNCH(true, false, true, true, ggs, hw16);
+    } else {
+      DS4_GU_LAUNCH(true, false, false, false, ggu, hw16);
+      DS4_GU_LAUNCH(true, false, true, false, ggs, hw16);
+    }
   } else {
-    DS4_GU_LAUNCH(false, true, false, gsh, hs16);
-    DS4_GU_LAUNCH(false, false, false, ggu, hw16);
-    DS4_GU_LAUNCH(false, false, true, ggs, hw16);
+    DS4_GU_LAUNCH(false, true, false, false, gsh, hs16);
+    if (mx) {
+      DS4_GU_LAUNCH(false, false, false, true, ggu, hw16);
+      DS4_GU_LAUNCH(false, false, true, true, ggs, hw16);
+    } else {
+      DS4_GU_LAUNCH(false, false, false, false, ggu, hw16);
+      DS4_GU_LAUNCH(false, false, true, false, ggs, hw16);
+    }
   }
 #undef DS4_GU_LAUNCH
-  if (L.d_ff / QK <= kDnStagedMax)
-    DS4_LAUNCH((k_pf_down<false, false, true>), gdn, blk, 0, f.st, L, T, tiles, stiles, ntiles, counts, offsets, perm,
-               hw16, yp, f.y);
-  else
-    DS4_LAUNCH((k_pf_down<false, false, false>), gdn, blk, 0, f.st, L, T, tiles, stiles, ntiles, counts, offsets, perm,
-               hw16, yp, f.y);
-  DS4_LAUNCH((k_pf_down<false, true, false>), gds, blk, 0, f.st, L, T, tiles, stiles, ntiles, counts, offsets, perm,
-             hw16, yp, f.y);
+#define DS4_DN_LAUNCH(DENSE, SMALL, DDS, MX, grid, hin)                                                          \
+  DS4_LAUNCH((k_pf_down<DENSE, SMALL, DDS, MX>), grid, blk, 0, f.st, L, T, tiles, stiles, ntiles, counts, offsets, \
+             perm, hin, yp, f.y)
+  if (mx) {
+    DS4_DN_LAUNCH(false, false, false, true, gdn, hw16);
+    DS4_DN_LAUNCH(false, true, false, true, gds, hw16);
+  } else {
+    if (L.d_ff / QK <= kDnStagedMax) DS4_DN_LAUNCH(false, false, true, false, gdn, hw16);
+    else DS4_DN_LAUNCH(false, false, false, false, gdn, hw16);
+    DS4_DN_LAUNCH(false, true, false, false, gds, hw16);
+  }
+#undef DS4_DN_LAUNCH
   DS4_LAUNCH((k_pf_down<true, false, false>), gsd, blk, 0, f.st, L, T, tiles, stiles, ntiles, counts, offsets, perm,
              hs16, yp, f.y);
   const int64_t n4 = T * d / 4;

@@ -15,7 +15,8 @@ import torch
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libds4moe.so")
 
 OK, EINVAL, ESHAPE, EALIGN, EWORKSPACE, EHIP, EUNSUPPORTED = 0, -1, -2, -3, -4, -5, -6
-FMT_F16, FMT_CB2, FMT_Q2K = 0, 1, 2
+FMT_F16, FMT_CB2, FMT_Q2K, FMT_MXFP4 = 0, 1, 2, 3
+EXPERTS_CB2_Q2K, EXPERTS_MXFP4 = 0, 1
 DT_F32, DT_BF16 = 0, 1
 MODE_DECODE, MODE_PREFILL, MODE_ROUTE = 0, 1, 2
 DECODE_MAX_T = 64
@@ -35,6 +36,7 @@ class LayerDesc(ctypes.Structure):
         ("router_w", ctypes.c_void_p), ("router_bias", ctypes.c_void_p),
         ("sh_gate", ctypes.c_void_p), ("sh_up", ctypes.c_void_p), ("sh_down", ctypes.c_void_p),
         ("gate", ctypes.c_void_p), ("up", ctypes.c_void_p), ("down", ctypes.c_void_p),
+        ("expert_fmt", ctypes.c_int32),
     ]
 
 
@@ -187,20 +189,23 @@ class Layer:
 
     router_w, sh_gate, sh_up, sh_down: binary16 bit patterns (int16/uint16 or
     float16 CUDA tensors); gate/up/down: uint8 CUDA tensors of E packed
-    matrices each; router_bias: float32 CUDA tensor or None.
+    matrices each; router_bias: float32 CUDA tensor or None; expert_fmt:
+    EXPERTS_CB2_Q2K or EXPERTS_MXFP4.
     """
 
-    def __init__(self, d, E, k, f, fs, router_w, router_bias, sh_gate, sh_up, sh_down, gate, up, down):
+    def __init__(self, d, E, k, f, fs, router_w, router_bias, sh_gate, sh_up, sh_down, gate, up, down,
+                 expert_fmt=EXPERTS_CB2_Q2K):
         self.tensors = dict(router_w=router_w, router_bias=router_bias, sh_gate=sh_gate, sh_up=sh_up,
                             sh_down=sh_down, gate=gate, up=up, down=down)
         self.d, self.E, self.k, self.f, self.fs = d, E, k, f, fs
+        self.expert_fmt = expert_fmt
         self.desc = LayerDesc(d, E, k, f, fs, _ptr(router_w), _ptr(router_bias), _ptr(sh_gate), _ptr(sh_up),
-                              _ptr(sh_down), _ptr(gate), _ptr(up), _ptr(down))
+                              _ptr(sh_down), _ptr(gate), _ptr(up), _ptr(down), expert_fmt)
 
     def with_experts(self, gate, up, down) -> "Layer":
         t = dict(self.tensors)
         return Layer(self.d, self.E, self.k, self.f, self.fs, t["router_w"], t["router_bias"], t["sh_gate"],
-                     t["sh_up"], t["sh_down"], gate, up, down)
+                     t["sh_up"], t["sh_down"], gate, up, down, self.expert_fmt)
 
     def workspace(self, T: int, mode: int):
         n = workspace_bytes(self.desc, T, mode)

@@ -60,6 +60,23 @@
  *   Weight K = 256b + 16j + i = (d * s_j) * q - dmin * m_j; both products
  *   are exact in binary32 and the difference is rounded once.
  *
+ * MXFP4 (4.25 bits per weight; 136 bytes per 256 weights): the OCP
+ * Microscaling format with FP4 E2M1 elements and one E8M0 scale per 32.
+ *   code plane   rows*cols/2 bytes: element K of row r at byte
+ *                (r*cols + K)/2, even K in the low nibble; nibble = sign bit
+ *                (bit 3), 2 exponent bits (bias 1), 1 mantissa bit, so
+ *                magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6.
+ *   scale plane  rows*cols/32 bytes at offset rows*cols/2: E8M0, value
+ *                2^(E - 127) (0xFF is NaN).
+ *   Weight = e2m1 * 2^(E - 127), exact in binary32.  The quantizer follows
+ *   the OCP MX conversion: shared exponent floor(log2 max|w|) - 2, elements
+ *   to the nearest E2M1 value (ties to the even code, saturating at 6); a
+ *   negative weight that rounds to zero is stored as +0.
+ *   The forward calls form each weight in binary16 with its block scale
+ *   folded in, which is exact for scale codes 104..140 (2^-23 .. 2^13);
+ *   other scales round (binary16) or overflow.  The quantizer gives codes in
+ *   that range for blocks whose largest |w| lies in [2^-21, 2^16).
+ *
  * F16 weights are plain row-major binary16 [rows, cols].
  */
 #ifndef DS4MOE_H
@@ -82,7 +99,12 @@ enum {
   DS4MOE_EUNSUPPORTED = -6  /* valid but not supported by this library */
 };
 
-enum { DS4MOE_FMT_F16 = 0, DS4MOE_FMT_CB2 = 1, DS4MOE_FMT_Q2K = 2 };
+enum { DS4MOE_FMT_F16 = 0, DS4MOE_FMT_CB2 = 1, DS4MOE_FMT_Q2K = 2, DS4MOE_FMT_MXFP4 = 3 };
+/* Formats of a layer's routed experts (ds4moe_layer.expert_fmt):
+ * CB2_Q2K: gate/up CB2, down Q2K (the pages' 2-bit recipe);
+ * MXFP4: gate, up and down all MXFP4 (the model's native expert format,
+ * TopDigg "DwarfStar (ds4) Deep Dive" 5.2, download options). */
+enum { DS4MOE_EXPERTS_CB2_Q2K = 0, DS4MOE_EXPERTS_MXFP4 = 1 };
 enum { DS4MOE_DT_F32 = 0, DS4MOE_DT_BF16 = 1 };
 enum { DS4MOE_MODE_DECODE = 0, DS4MOE_MODE_PREFILL = 1, DS4MOE_MODE_ROUTE = 2 };
 
@@ -105,19 +127,22 @@ typedef struct {
   const uint16_t *sh_gate;     /* F16 [fs, d] */
   const uint16_t *sh_up;       /* F16 [fs, d] */
   const uint16_t *sh_down;     /* F16 [d, fs] */
-  const void *gate;            /* CB2, E packed [f, d] matrices */
-  const void *up;              /* CB2, E packed [f, d] matrices */
-  const void *down;            /* Q2K, E packed [d, f] matrices */
+  const void *gate;            /* E packed [f, d] matrices (CB2, or MXFP4) */
+  const void *up;              /* E packed [f, d] matrices (CB2, or MXFP4) */
+  const void *down;            /* E packed [d, f] matrices (Q2K, or MXFP4) */
+  int32_t expert_fmt;          /* DS4MOE_EXPERTS_*; 0 (CB2/Q2K) when the struct is zero-initialised */
 } ds4moe_layer;
 
 /* Bytes of one packed [rows, cols] matrix (host function; 0 if cols % 256 != 0
- * or fmt is unknown).  F16: rows*cols*2. */
+ * or fmt is unknown).  F16: rows*cols*2; CB2 66, Q2K 84, MXFP4 136 bytes per
+ * 256 weights. */
 size_t ds4moe_packed_bytes(int fmt, int64_t rows, int64_t cols);
 
 /* Quantize fp32 [rows, cols] (row-major, finite values) into the packed
- * matrix `packed` (ds4moe_packed_bytes bytes).  fmt: DS4MOE_FMT_CB2 or
- * DS4MOE_FMT_Q2K.  Deterministic: the bytes equal those of the format's
- * reference quantizer (steps in the library's documentation). */
+ * matrix `packed` (ds4moe_packed_bytes bytes).  fmt: DS4MOE_FMT_CB2,
+ * DS4MOE_FMT_Q2K or DS4MOE_FMT_MXFP4.  Deterministic: the bytes equal those
+ * of the format's reference quantizer (steps in the library's
+ * documentation). */
 int ds4moe_quantize(int fmt, const float *w, int64_t rows, int64_t cols, void *packed, void *stream);
 
 /* Decode a packed matrix to fp32 [rows, cols] (bit-exact). */

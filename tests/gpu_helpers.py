@@ -44,18 +44,26 @@ class SeededLayer:
     """A synthetic layer (config cfg) held both on the device and for the oracle."""
 
     def __init__(self, cfg: S.Config, device_quantize: bool, cfg_seed: int | None = None, chunk: int = 16,
-                 router: np.ndarray | None = None):
+                 router: np.ndarray | None = None, expert_fmt: str = "cb2q2k"):
         """router: binary16 bits [E, d] to use instead of the seeded draw
-        (edge-case tests build routers with repeated rows)."""
+        (edge-case tests build routers with repeated rows); expert_fmt:
+        "cb2q2k" (CB2 gate/up, Q2K down) or "mxfp4" (all three MXFP4)."""
         self.cfg = cfg
         self.seed = cfg.seed if cfg_seed is None else cfg_seed
+        self.expert_fmt = expert_fmt
         c = cfg
         self.router = S.gen_router(cfg, cfg_seed=cfg_seed) if router is None else np.ascontiguousarray(router)
         self.bias = S.gen_bias(cfg)
         self.sh = S.gen_shared(cfg, cfg_seed=cfg_seed)
-        cb = D.packed_bytes(D.FMT_CB2, c.f, c.d)
-        qb = D.packed_bytes(D.FMT_Q2K, c.d, c.f)
-        assert cb == O.cb2_bytes(c.f, c.d) and qb == O.q2k_bytes(c.d, c.f)
+        mx = expert_fmt == "mxfp4"
+        self.fmt_gu = D.FMT_MXFP4 if mx else D.FMT_CB2
+        self.fmt_dn = D.FMT_MXFP4 if mx else D.FMT_Q2K
+        cb = D.packed_bytes(self.fmt_gu, c.f, c.d)
+        qb = D.packed_bytes(self.fmt_dn, c.d, c.f)
+        if mx:
+            assert cb == O.mx4_bytes(c.f, c.d) and qb == O.mx4_bytes(c.d, c.f)
+        else:
+            assert cb == O.cb2_bytes(c.f, c.d) and qb == O.q2k_bytes(c.d, c.f)
         self.cb, self.qb = cb, qb
         self.gate = torch.empty(c.E * cb, dtype=torch.uint8, device="cuda")
         self.up = torch.empty(c.E * cb, dtype=torch.uint8, device="cuda")
@@ -66,9 +74,9 @@ class SeededLayer:
                 es = list(range(e0, min(c.E, e0 + chunk)))
                 mats = S.gen_experts(cfg, es, threads=16, cfg_seed=cfg_seed)
                 for e, (g, u, dn) in zip(es, mats):
-                    D.quantize(D.FMT_CB2, dev(g), c.f, c.d, self.gate[e * cb:(e + 1) * cb])
-                    D.quantize(D.FMT_CB2, dev(u), c.f, c.d, self.up[e * cb:(e + 1) * cb])
-                    D.quantize(D.FMT_Q2K, dev(dn), c.d, c.f, self.down[e * qb:(e + 1) * qb])
+                    D.quantize(self.fmt_gu, dev(g), c.f, c.d, self.gate[e * cb:(e + 1) * cb])
+                    D.quantize(self.fmt_gu, dev(u), c.f, c.d, self.up[e * cb:(e + 1) * cb])
+                    D.quantize(self.fmt_dn, dev(dn), c.d, c.f, self.down[e * qb:(e + 1) * qb])
                 torch.cuda.synchronize()
         else:
             for e in range(c.E):
@@ -79,12 +87,15 @@ class SeededLayer:
                 self.down[e * qb:(e + 1) * qb] = dev(dp)
         self.layer = D.Layer(c.d, c.E, c.k, c.f, c.fs, dev(self.router),
                              None if self.bias is None else dev(self.bias),
-                             dev(self.sh[0]), dev(self.sh[1]), dev(self.sh[2]), self.gate, self.up, self.down)
+                             dev(self.sh[0]), dev(self.sh[1]), dev(self.sh[2]), self.gate, self.up, self.down,
+                             D.EXPERTS_MXFP4 if mx else D.EXPERTS_CB2_Q2K)
         self.oracle = O.Layer(c.d, c.E, c.k, c.f, c.fs, self.router, self.bias, self.sh[0], self.sh[1], self.sh[2],
-                              self.oracle_expert)
+                              self.oracle_expert, expert_fmt=expert_fmt)
 
     def _oracle_quantize(self, e):
         g, u, dn = S.gen_expert(self.cfg, e, cfg_seed=self.seed)
+        if self.expert_fmt == "mxfp4":
+            return O.mx4_quantize(g), O.mx4_quantize(u), O.mx4_quantize(dn)
         return O.cb2_quantize(g), O.cb2_quantize(u), O.q2k_quantize(dn)
 
     def oracle_expert(self, e):

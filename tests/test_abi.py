@@ -34,6 +34,7 @@ def test_packed_sizes():
     assert D.packed_bytes(D.FMT_CB2, 2048, 4096) == 2048 * 16 * 66 == 2162688
     assert D.packed_bytes(D.FMT_Q2K, 4096, 2048) == 4096 * 8 * 84 == 2752512
     assert D.packed_bytes(D.FMT_F16, 3, 5) == 30
+    assert D.packed_bytes(D.FMT_MXFP4, 2048, 4096) == 2048 * 4096 * 17 // 32 == 4456448
     assert D.packed_bytes(D.FMT_CB2, 4, 300) == 0
     assert D.packed_bytes(9, 4, 256) == 0
 
@@ -75,6 +76,9 @@ def test_forward_argument_errors():
     assert call_decode(desc(E=2000)) == D.ESHAPE
     assert call_decode(desc(gate=A + 4)) == D.EALIGN
     assert call_decode(desc(router_bias=A + 2)) == D.EALIGN
+    bad = desc()
+    bad.expert_fmt = 7
+    assert call_decode(bad) == D.EINVAL
     assert call_decode(L, T=0) == D.ESHAPE
     assert call_decode(L, T=65) == D.ESHAPE
     assert call_decode(L, dt=5) == D.EINVAL
@@ -123,6 +127,8 @@ def test_codec_argument_errors():
     assert lib.ds4moe_quantize(7, A, 4, 256, A, None) == D.EINVAL
     assert lib.ds4moe_quantize(D.FMT_F16, A, 4, 256, A, None) == D.EINVAL
     assert lib.ds4moe_quantize(D.FMT_CB2, A, 4, 300, A, None) == D.ESHAPE
+    assert lib.ds4moe_quantize(D.FMT_MXFP4, A, 4, 288, A, None) == D.ESHAPE
+    assert lib.ds4moe_quantize(D.FMT_MXFP4 + 1, A, 4, 256, A, None) == D.EINVAL
     assert lib.ds4moe_quantize(D.FMT_CB2, A, -1, 256, A, None) == D.EINVAL
     assert lib.ds4moe_quantize(D.FMT_CB2, None, 4, 256, A, None) == D.EINVAL
     assert lib.ds4moe_quantize(D.FMT_Q2K, A + 4, 4, 256, A, None) == D.EALIGN

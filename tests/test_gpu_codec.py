@@ -98,3 +98,50 @@ def test_full_size_expert_quantize_byte_exact():
 def test_empty_matrix_is_a_no_op():
     D.quantize(D.FMT_CB2, 0, 0, 256, 0)
     D.dequantize(D.FMT_Q2K, 0, 0, 512, 0)
+
+
+# ------------------------------------------------------------------ MXFP4
+def test_mx4_quantize_byte_exact():
+    rng = np.random.default_rng(21)
+    for rows, cols, scale in ((1, 256, 0.02), (37, 512, 0.02), (16, 4096, 1.0), (8, 768, 3e4)):
+        w = (rng.standard_normal((rows, cols)) * scale).astype(np.float32)
+        assert np.array_equal(gpu_quant(D.FMT_MXFP4, w), O.mx4_quantize(w)), (rows, cols, scale)
+
+
+def test_mx4_quantize_edge_blocks_byte_exact():
+    x = np.zeros((8, 256), dtype=np.float32)
+    x[1, 17] = 0.5                                    # single spike
+    x[2, :] = 1e-40                                   # subnormal inputs, scale clamps at 0
+    x[3, 5], x[3, 6] = 3e38, -3e38                    # the largest scales
+    x[4, :] = -0.01                                   # all negative
+    ties = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0, 7.99, -0.25, -5.0, 0.1], dtype=np.float32)
+    x[5, :12] = ties * 2.0 ** -6                      # every midpoint, and saturation
+    x[6, :12] = ties * 2.0 ** 10
+    x[7, ::3] = -1e-3                                 # negatives rounding to zero beside larger values
+    x[7, 1::3] = 0.7
+    assert np.array_equal(gpu_quant(D.FMT_MXFP4, x), O.mx4_quantize(x))
+
+
+def test_mx4_dequantize_random_codes_bit_exact():
+    """Every code byte with scale codes across the range (1 .. 252), and the
+    quantizer's own output."""
+    rng = np.random.default_rng(22)
+    rows, cols = 16, 512
+    n = rows * cols
+    codes = rng.integers(0, 256, n // 2, dtype=np.uint8)
+    codes[:256] = np.arange(256)
+    scales = rng.integers(1, 253, n // 32).astype(np.uint8)
+    p = np.concatenate([codes, scales])
+    assert np.array_equal(gpu_dequant(D.FMT_MXFP4, p, rows, cols).view(np.uint32),
+                          O.mx4_dequantize(p, rows, cols).view(np.uint32))
+    w = (rng.standard_normal((rows, cols)) * 0.02).astype(np.float32)
+    q = O.mx4_quantize(w)
+    assert np.array_equal(gpu_dequant(D.FMT_MXFP4, q, rows, cols).view(np.uint32),
+                          O.mx4_dequantize(q, rows, cols).view(np.uint32))
+
+
+def test_mx4_full_size_expert_quantize_byte_exact():
+    cfg = S.CONFIGS["decode1"]
+    g, u, dn = S.gen_expert(cfg, 7)
+    assert np.array_equal(gpu_quant(D.FMT_MXFP4, g), O.mx4_quantize(g))
+    assert np.array_equal(gpu_quant(D.FMT_MXFP4, dn), O.mx4_quantize(dn))
