@@ -454,6 +454,170 @@ void orc_q2k_quantize(const float *w, int64_t rows, int64_t cols, uint8_t *codes
 }
 
 /* ------------------------------------------------------------------------- */
+/* Q4K: the 4-bit super-block format (Q4_K class, 4.5 bits per weight) of the */
+/* Q4 layers of the q2-q4 mix (TopDigg "DwarfStar (ds4) Deep Dive", 5.2:      */
+/* the last six routed-expert layers at Q4; the wiki note's Comparison Notes  */
+/* name the Q4_K layouts).  Layout (this library's own):                      */
+/*   code plane     [rows][nb][128]: sub-block j (32 weights) at bytes        */
+/*                  16j..16j+15 of its block; LE u32 word k of a sub-block    */
+/*                  holds elements 8k..8k+7: element 8k+2p at bits 4p..4p+3,  */
+/*                  element 8k+2p+1 at bits 16+4p..19+4p (p = 0..3)           */
+/*   scale plane    [rows][nb][12]: LE u32 w0, w1, w2; nibble j of w0 is      */
+/*                  s_j & 15, nibble j of w1 is m_j & 15, bits 2j..2j+1 of w2 */
+/*                  are s_j >> 4 and bits 16+2j..17+2j are m_j >> 4 (6 bits) */
+/*   superscale     [rows][nb][2] binary16: d, then dmin                      */
+/* Weight K = 256 b + 32 j + i has value (d * s_j) * q - dmin * m_j: both     */
+/* products are exact in binary32, the difference is rounded once.           */
+/* ------------------------------------------------------------------------- */
+
+static int q4k_code(const uint8_t *blk, int i) /* element i (0..255) of a block's code plane */
+{
+    int j = i / 32, r = i % 32, k = r / 8, e = r % 8, p = e / 2;
+    const uint8_t *w = blk + 16 * j + 4 * k;
+    uint32_t u = (uint32_t)w[0] | (uint32_t)w[1] << 8 | (uint32_t)w[2] << 16 | (uint32_t)w[3] << 24;
+    int sh = (e & 1) ? 16 + 4 * p : 4 * p;
+    return (int)((u >> sh) & 15u);
+}
+
+static void q4k_scale_min(const uint8_t *sc, int j, int *s, int *m)
+{
+    uint32_t w[3];
+    for (int t = 0; t < 3; t++)
+        w[t] = (uint32_t)sc[4 * t] | (uint32_t)sc[4 * t + 1] << 8 | (uint32_t)sc[4 * t + 2] << 16 |
+               (uint32_t)sc[4 * t + 3] << 24;
+    *s = (int)(((w[0] >> (4 * j)) & 15u) | (((w[2] >> (2 * j)) & 3u) << 4));
+    *m = (int)(((w[1] >> (4 * j)) & 15u) | (((w[2] >> (16 + 2 * j)) & 3u) << 4));
+}
+
+void orc_q4k_dequantize(const uint8_t *codes, const uint8_t *scales, const uint16_t *sup, int64_t rows, int64_t cols,
+                        float *out)
+{
+    int64_t nb = cols / QK;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; r++)
+        for (int64_t b = 0; b < nb; b++) {
+            const uint8_t *blk = codes + (r * nb + b) * 128;
+            const uint8_t *sc = scales + (r * nb + b) * 12;
+            float d = orc_f16_to_f32(sup[(r * nb + b) * 2]), dmin = orc_f16_to_f32(sup[(r * nb + b) * 2 + 1]);
+            for (int i = 0; i < QK; i++) {
+                int s, m;
+                q4k_scale_min(sc, i / 32, &s, &m);
+                float t1 = d * (float)s;
+                t1 = t1 * (float)q4k_code(blk, i);
+                float t2 = dmin * (float)m;
+                out[r * cols + b * QK + i] = t1 - t2;
+            }
+        }
+}
+
+/*
+ * Q4K quantizer (this library's own deterministic steps, those of Q2K at
+ * 4-bit codes and 6-bit scales):
+ *  1. per sub-block j of 32: b_j = max(0, -min x), a_j = (max x + b_j) / 15
+ *  2. d = half(max_j a_j / 63), dmin = half(max_j b_j / 63), clamped to 65504
+ *  3. s_j = d > 0 ? clamp(rne(a_j / d), 0, 63) : 0; m_j likewise with dmin
+ *  4. q = argmin over 0..15 of |value(q) - x| using the decoder's own binary32
+ *     formula, ties to the lower q.
+ */
+static void q4k_quantize_block(const float *x, uint8_t *blk, uint8_t *sc, uint16_t *sup)
+{
+    float a[8], bb[8], amax = 0.0f, bmax = 0.0f;
+    for (int j = 0; j < 8; j++) {
+        float mx = x[32 * j], mn = x[32 * j];
+        for (int i = 1; i < 32; i++) {
+            float v = x[32 * j + i];
+            if (v > mx)
+                mx = v;
+            if (v < mn)
+                mn = v;
+        }
+        bb[j] = mn < 0.0f ? -mn : 0.0f;
+        a[j] = (mx + bb[j]) / 15.0f;
+        if (a[j] > amax)
+            amax = a[j];
+        if (bb[j] > bmax)
+            bmax = bb[j];
+    }
+    uint16_t dbits = f16_clamped(amax / 63.0f), mbits = f16_clamped(bmax / 63.0f);
+    float d = orc_f16_to_f32(dbits), dmin = orc_f16_to_f32(mbits);
+    sup[0] = dbits;
+    sup[1] = mbits;
+    uint32_t w[3] = {0u, 0u, 0u};
+    memset(blk, 0, 128);
+    for (int j = 0; j < 8; j++) {
+        int s = 0, m = 0;
+        if (d > 0.0f) {
+            float v = rintf(a[j] / d);
+            s = v < 0.0f ? 0 : (v > 63.0f ? 63 : (int)v);
+        }
+        if (dmin > 0.0f) {
+            float v = rintf(bb[j] / dmin);
+            m = v < 0.0f ? 0 : (v > 63.0f ? 63 : (int)v);
+        }
+        w[0] |= (uint32_t)(s & 15) << (4 * j);
+        w[1] |= (uint32_t)(m & 15) << (4 * j);
+        w[2] |= (uint32_t)(s >> 4) << (2 * j) | (uint32_t)(m >> 4) << (16 + 2 * j);
+        for (int i = 0; i < 32; i++) {
+            float xv = x[32 * j + i];
+            int bq = 0;
+            float berr = 0.0f;
+            for (int q = 0; q < 16; q++) {
+                float t1 = d * (float)s;
+                t1 = t1 * (float)q;
+                float err = fabsf((t1 - dmin * (float)m) - xv);
+                if (q == 0 || err < berr) {
+                    bq = q;
+                    berr = err;
+                }
+            }
+            int k = i / 8, e = i % 8, p = e / 2;
+            int sh = (e & 1) ? 16 + 4 * p : 4 * p;
+            uint8_t *wb = blk + 16 * j + 4 * k;
+            uint32_t u = (uint32_t)wb[0] | (uint32_t)wb[1] << 8 | (uint32_t)wb[2] << 16 | (uint32_t)wb[3] << 24;
+            u |= (uint32_t)bq << sh;
+            wb[0] = (uint8_t)u;
+            wb[1] = (uint8_t)(u >> 8);
+            wb[2] = (uint8_t)(u >> 16);
+            wb[3] = (uint8_t)(u >> 24);
+        }
+    }
+    for (int t = 0; t < 3; t++) {
+        sc[4 * t] = (uint8_t)w[t];
+        sc[4 * t + 1] = (uint8_t)(w[t] >> 8);
+        sc[4 * t + 2] = (uint8_t)(w[t] >> 16);
+        sc[4 * t + 3] = (uint8_t)(w[t] >> 24);
+    }
+}
+
+void orc_q4k_quantize(const float *w, int64_t rows, int64_t cols, uint8_t *codes, uint8_t *scales, uint16_t *sup)
+{
+    int64_t nb = cols / QK;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t r = 0; r < rows; r++)
+        for (int64_t b = 0; b < nb; b++)
+            q4k_quantize_block(w + r * cols + b * QK, codes + (r * nb + b) * 128, scales + (r * nb + b) * 12,
+                               sup + (r * nb + b) * 2);
+}
+
+void orc_q4k_matmul(const uint8_t *codes, const uint8_t *scales, const uint16_t *sup, int64_t rows, int64_t cols,
+                    const double *X, int64_t n, double *Y)
+{
+    int64_t nb = cols / QK;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; r++) {
+        float *wrow = (float *)malloc(sizeof(float) * (size_t)cols);
+        orc_q4k_dequantize(codes + r * nb * 128, scales + r * nb * 12, sup + r * nb * 2, 1, cols, wrow);
+        for (int64_t t = 0; t < n; t++) {
+            double acc = 0.0;
+            for (int64_t i = 0; i < cols; i++)
+                acc += (double)wrow[i] * X[t * cols + i];
+            Y[t * rows + r] = acc;
+        }
+        free(wrow);
+    }
+}
+
+/* ------------------------------------------------------------------------- */
 /* MXFP4: the public OCP Microscaling (MX) format with FP4 E2M1 elements, one  */
 /* E8M0 scale per block of 32 elements.  It is DeepSeek's native format for    */
 /* the routed experts (TopDigg "DwarfStar (ds4) Deep Dive", 5.2, download     */

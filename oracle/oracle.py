@@ -76,6 +76,9 @@ def lib():
         L.orc_mx4_dequantize.argtypes = [P, P, I64, I64, P]
         L.orc_mx4_quantize.argtypes = [P, I64, I64, P, P]
         L.orc_mx4_matmul.argtypes = [P, P, I64, I64, P, I64, P]
+        L.orc_q4k_dequantize.argtypes = [P, P, P, I64, I64, P]
+        L.orc_q4k_quantize.argtypes = [P, I64, I64, P, P, P]
+        L.orc_q4k_matmul.argtypes = [P, P, P, I64, I64, P, I64, P]
         L.orc_set_threads.argtypes = [ctypes.c_int]
         L.orc_max_threads.restype = ctypes.c_int
         _lib = L
@@ -131,6 +134,15 @@ def cb2_bytes(rows: int, cols: int) -> int:
 
 def q2k_bytes(rows: int, cols: int) -> int:
     return rows * (cols // QK) * 84
+
+
+def q4k_bytes(rows: int, cols: int) -> int:
+    return rows * (cols // QK) * 144
+
+
+def q4k_planes(packed: np.ndarray, rows: int, cols: int):
+    n = rows * (cols // QK)
+    return packed[: n * 128], packed[n * 128: n * 140], packed[n * 140: n * 144].view(np.uint16)
 
 
 def mx4_bytes(rows: int, cols: int) -> int:
@@ -208,6 +220,24 @@ def e8m0_value(code: int) -> float:
     return lib().orc_e8m0_value(int(code))
 
 
+def q4k_quantize(w: np.ndarray) -> np.ndarray:
+    rows, cols = w.shape
+    _check(rows, cols)
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    packed = np.zeros(q4k_bytes(rows, cols), dtype=np.uint8)
+    codes, sc, sup = q4k_planes(packed, rows, cols)
+    lib().orc_q4k_quantize(_p(w), rows, cols, _p(codes), _p(sc), _p(sup))
+    return packed
+
+
+def q4k_dequantize(packed: np.ndarray, rows: int, cols: int) -> np.ndarray:
+    _check(rows, cols)
+    codes, sc, sup = q4k_planes(np.ascontiguousarray(packed), rows, cols)
+    out = np.zeros((rows, cols), dtype=np.float32)
+    lib().orc_q4k_dequantize(_p(codes), _p(sc), _p(sup), rows, cols, _p(out))
+    return out
+
+
 def mx4_quantize(w: np.ndarray) -> np.ndarray:
     rows, cols = w.shape
     _check(rows, cols)
@@ -242,6 +272,15 @@ def q2k_matmul(packed, rows, cols, X: np.ndarray) -> np.ndarray:
     codes, sub, sup = q2k_planes(packed, rows, cols)
     Y = np.zeros((n, rows), dtype=np.float64)
     lib().orc_q2k_matmul(_p(codes), _p(sub), _p(sup), rows, cols, _p(X), n, _p(Y))
+    return Y
+
+
+def q4k_matmul(packed, rows, cols, X: np.ndarray) -> np.ndarray:
+    X = np.ascontiguousarray(X, dtype=np.float64)
+    n = X.shape[0]
+    codes, sc, sup = q4k_planes(packed, rows, cols)
+    Y = np.zeros((n, rows), dtype=np.float64)
+    lib().orc_q4k_matmul(_p(codes), _p(sc), _p(sup), rows, cols, _p(X), n, _p(Y))
     return Y
 
 
@@ -326,8 +365,8 @@ class Layer:
 
     experts: callable e -> (gate_packed, up_packed, down_packed), or a dict.
     Packed matrices follow the plane layout above; router and shared weights
-    are binary16 bit arrays.  expert_fmt: "cb2q2k" (CB2 gate/up, Q2K down)
-    or "mxfp4" (all three in MXFP4).
+    are binary16 bit arrays.  expert_fmt: "cb2q2k" (CB2 gate/up, Q2K down),
+    "mxfp4" (all three in MXFP4) or "q4k" (all three in Q4K).
     """
 
     def __init__(self, d, E, k, f, fs, router_bits, bias, sh_gate, sh_up, sh_down, experts, expert_fmt="cb2q2k"):
@@ -362,6 +401,10 @@ class Layer:
             g = mx4_matmul(gp, self.f, self.d, Xe)
             u = mx4_matmul(up, self.f, self.d, Xe)
             return mx4_matmul(dp, self.d, self.f, swiglu(g, u))
+        if self.expert_fmt == "q4k":
+            g = q4k_matmul(gp, self.f, self.d, Xe)
+            u = q4k_matmul(up, self.f, self.d, Xe)
+            return q4k_matmul(dp, self.d, self.f, swiglu(g, u))
         g = cb2_matmul(gp, self.f, self.d, Xe)
         u = cb2_matmul(up, self.f, self.d, Xe)
         return q2k_matmul(dp, self.d, self.f, swiglu(g, u))

@@ -133,3 +133,27 @@ def test_mxfp4_matmul_and_expert_chain_match_numpy():
     D = O.mx4_dequantize(packs[5][2], cfg.d, cfg.f).astype(np.float64)
     gx, ux = Xt @ G.T, Xt @ U.T
     assert np.allclose(L.expert_out(5, Xt), (gx * expit(gx) * ux) @ D.T, rtol=1e-11, atol=1e-12)
+
+
+def test_q4k_matmul_and_expert_chain_match_numpy():
+    """Q4K experts: the oracle's product and the layer's expert chain equal
+    numpy fp64 on the dequantized matrices."""
+    cfg = S.CONFIGS["tiny"]
+    rng = np.random.default_rng(3)
+    w = (rng.standard_normal((48, 512)) * 0.02).astype(np.float32)
+    X = rng.standard_normal((5, 512))
+    p = O.q4k_quantize(w)
+    ref = X @ O.q4k_dequantize(p, 48, 512).astype(np.float64).T
+    assert np.allclose(O.q4k_matmul(p, 48, 512, X), ref, rtol=1e-12, atol=1e-14)
+    packs = {}
+    for e in range(cfg.E):
+        g, u, dn = S.gen_expert(cfg, e)
+        packs[e] = (O.q4k_quantize(g), O.q4k_quantize(u), O.q4k_quantize(dn))
+    sg, su, sd = S.gen_shared(cfg)
+    L = O.Layer(cfg.d, cfg.E, cfg.k, cfg.f, cfg.fs, S.gen_router(cfg), None, sg, su, sd, packs, expert_fmt="q4k")
+    Xt = O.x_to_f64(S.gen_x(cfg), "f32")
+    G = O.q4k_dequantize(packs[9][0], cfg.f, cfg.d).astype(np.float64)
+    U = O.q4k_dequantize(packs[9][1], cfg.f, cfg.d).astype(np.float64)
+    D = O.q4k_dequantize(packs[9][2], cfg.d, cfg.f).astype(np.float64)
+    gx, ux = Xt @ G.T, Xt @ U.T
+    assert np.allclose(L.expert_out(9, Xt), (gx * expit(gx) * ux) @ D.T, rtol=1e-11, atol=1e-12)
