@@ -72,7 +72,9 @@ static int check_layer(const ds4moe_layer* L) {
       !al16(L->up) || !al16(L->down))
     return DS4MOE_EALIGN;
   if (L->router_bias && ((uintptr_t)L->router_bias & 3)) return DS4MOE_EALIGN;
-  if (L->expert_fmt != DS4MOE_EXPERTS_CB2_Q2K && L->expert_fmt != DS4MOE_EXPERTS_MXFP4) return DS4MOE_EINVAL;
+  if (L->expert_fmt != DS4MOE_EXPERTS_CB2_Q2K && L->expert_fmt != DS4MOE_EXPERTS_MXFP4 &&
+      L->expert_fmt != DS4MOE_EXPERTS_Q4K)
+    return DS4MOE_EINVAL;
   return DS4MOE_OK;
 }
 
@@ -162,10 +164,13 @@ size_t ds4moe_packed_bytes(int fmt, int64_t rows, int64_t cols) {
   if (fmt == DS4MOE_FMT_CB2) return nblk * 66;
   if (fmt == DS4MOE_FMT_Q2K) return nblk * 84;
   if (fmt == DS4MOE_FMT_MXFP4) return nblk * 136;
+  if (fmt == DS4MOE_FMT_Q4K) return nblk * 144;
   return 0;
 }
 
-static bool codec_fmt(int fmt) { return fmt == DS4MOE_FMT_CB2 || fmt == DS4MOE_FMT_Q2K || fmt == DS4MOE_FMT_MXFP4; }
+static bool codec_fmt(int fmt) {
+  return fmt == DS4MOE_FMT_CB2 || fmt == DS4MOE_FMT_Q2K || fmt == DS4MOE_FMT_MXFP4 || fmt == DS4MOE_FMT_Q4K;
+}
 
 int ds4moe_quantize(int fmt, const float* w, int64_t rows, int64_t cols, void* packed, void* stream) {
   if (!codec_fmt(fmt)) return DS4MOE_EINVAL;
@@ -177,6 +182,7 @@ int ds4moe_quantize(int fmt, const float* w, int64_t rows, int64_t cols, void* p
   hipStream_t st = (hipStream_t)stream;
   hipError_t e = fmt == DS4MOE_FMT_CB2   ? launch_quant_cb2(w, rows, cols, packed, st)
                  : fmt == DS4MOE_FMT_Q2K ? launch_quant_q2k(w, rows, cols, packed, st)
+                 : fmt == DS4MOE_FMT_Q4K ? launch_quant_q4k(w, rows, cols, packed, st)
                                          : launch_quant_mx4(w, rows, cols, packed, st);
   return hip_status(e);
 }
@@ -191,6 +197,7 @@ int ds4moe_dequantize(int fmt, const void* packed, int64_t rows, int64_t cols, f
   hipStream_t st = (hipStream_t)stream;
   hipError_t e = fmt == DS4MOE_FMT_CB2   ? launch_dequant_cb2(packed, rows, cols, w, st)
                  : fmt == DS4MOE_FMT_Q2K ? launch_dequant_q2k(packed, rows, cols, w, st)
+                 : fmt == DS4MOE_FMT_Q4K ? launch_dequant_q4k(packed, rows, cols, w, st)
                                          : launch_dequant_mx4(packed, rows, cols, w, st);
   return hip_status(e);
 }

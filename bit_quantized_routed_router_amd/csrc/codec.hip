@@ -1,4 +1,4 @@
-// CB2 / Q2K / MXFP4 encoders and decoders (byte layouts in include/ds4moe.h).
+// CB2 / Q2K / MXFP4 / Q4K encoders and decoders (byte layouts in include/ds4moe.h).
 //
 // The pages name the formats only (DS4 (DwarfStar 4) wiki note, "Key
 // Techniques": IQ2_XXS for gate/up, Q2_K for down); the quantizer steps are
@@ -352,6 +352,130 @@ __global__ __launch_bounds__(256) void k_dequant_mx4(const uint8_t* __restrict__
 }
 
 // ---------------------------------------------------------------------------
+// Q4K quantizer.  8 lanes per super-block, one lane per sub-block of 32: the
+// Q2K steps with 4-bit codes and 6-bit scales.
+//  1. b_j = max(0, -min x), a_j = (max x + b_j) / 15
+//  2. d = half(min(max a / 63, 65504)), dmin = half(min(max b / 63, 65504))
+//  3. s_j = d > 0 ? clamp(rne(a_j / d), 0, 63) : 0; m_j likewise with dmin
+//  4. q = argmin_q |((d*s)*q - dmin*m) - x|, lower q on ties.
+// Code word k of sub-block j: element 8k + 2p at bits 4p, 8k + 2p + 1 at
+// bits 16 + 4p; scale words: nibbles of s and m, then their high bits.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_quant_q4k(const float* __restrict__ w, int64_t nblk,
+                                                   uint8_t* __restrict__ codes, uint8_t* __restrict__ scl,
+                                                   uint16_t* __restrict__ sup) {
+  const int64_t blk = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 3;
+  const int j = threadIdx.x & 7;
+  const bool valid = blk < nblk;
+  float v[32];
+  if (valid) {
+    const float4* src = (const float4*)(w + blk * QK + 32 * j);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float4 t = src[i];
+      v[4 * i] = t.x; v[4 * i + 1] = t.y; v[4 * i + 2] = t.z; v[4 * i + 3] = t.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) v[i] = 0.0f;
+  }
+  float mx = v[0], mn = v[0];
+#pragma unroll
+  for (int i = 1; i < 32; ++i) {
+    mx = fmaxf(mx, v[i]);
+    mn = fminf(mn, v[i]);
+  }
+  const float b = mn < 0.0f ? -mn : 0.0f;
+  const float a = __fdiv_rn(__fadd_rn(mx, b), 15.0f);
+  float amax = a, bmax = b;
+#pragma unroll
+  for (int o = 1; o < 8; o <<= 1) {
+    amax = fmaxf(amax, __shfl_xor(amax, o, 8));
+    bmax = fmaxf(bmax, __shfl_xor(bmax, o, 8));
+  }
+  const uint32_t dbits = f32_to_f16_bits_rne(fminf(__fdiv_rn(amax, 63.0f), 65504.0f));
+  const uint32_t mbits = f32_to_f16_bits_rne(fminf(__fdiv_rn(bmax, 63.0f), 65504.0f));
+  const float d = f16_bits_to_f32(dbits), dmin = f16_bits_to_f32(mbits);
+  uint32_t s = 0, m = 0;
+  if (d > 0.0f) {
+    float t = __builtin_rintf(__fdiv_rn(a, d));
+    s = t < 0.0f ? 0u : (t > 63.0f ? 63u : (uint32_t)t);
+  }
+  if (dmin > 0.0f) {
+    float t = __builtin_rintf(__fdiv_rn(b, dmin));
+    m = t < 0.0f ? 0u : (t > 63.0f ? 63u : (uint32_t)t);
+  }
+  const float ds = __fmul_rn(d, (float)s);
+  const float dm = __fmul_rn(dmin, (float)m);
+  uint32_t cw[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    uint32_t bq = 0;
+    float berr = fabsf(__fsub_rn(__fsub_rn(0.0f, dm), v[i]));
+    for (int q = 1; q < 16; ++q) {
+      const float err = fabsf(__fsub_rn(__fsub_rn(__fmul_rn(ds, (float)q), dm), v[i]));
+      if (err < berr) {
+        berr = err;
+        bq = (uint32_t)q;
+      }
+    }
+    const int e = i & 7, p = e >> 1;
+    cw[i >> 3] |= bq << ((e & 1) ? 16 + 4 * p : 4 * p);
+  }
+  // scale words of the block: each lane's fields, OR-reduced over the 8 lanes
+  uint32_t w0 = (s & 15u) << (4 * j), w1 = (m & 15u) << (4 * j);
+  uint32_t w2 = ((s >> 4) << (2 * j)) | ((m >> 4) << (16 + 2 * j));
+#pragma unroll
+  for (int o = 1; o < 8; o <<= 1) {
+    w0 |= __shfl_xor(w0, o, 8);
+    w1 |= __shfl_xor(w1, o, 8);
+    w2 |= __shfl_xor(w2, o, 8);
+  }
+  if (valid) {
+    *(u32x4_t*)(codes + blk * 128 + 16 * j) = u32x4_t{cw[0], cw[1], cw[2], cw[3]};
+    if (j == 0) {
+      uint32_t* sw = (uint32_t*)(scl + blk * 12);
+      sw[0] = w0;
+      sw[1] = w1;
+      sw[2] = w2;
+      sup[2 * blk] = (uint16_t)dbits;
+      sup[2 * blk + 1] = (uint16_t)mbits;
+    }
+  }
+}
+
+// One lane per Q4K sub-block of 32.
+__global__ __launch_bounds__(256) void k_dequant_q4k(const uint8_t* __restrict__ codes,
+                                                     const uint8_t* __restrict__ scl,
+                                                     const uint16_t* __restrict__ sup, int64_t nsub,
+                                                     float* __restrict__ out) {
+  const int64_t si = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (si >= nsub) return;
+  const int64_t blk = si >> 3;
+  const int j = (int)(si & 7);
+  const u32x4_t cw = *(const u32x4_t*)(codes + blk * 128 + 16 * j);
+  const uint32_t* sw = (const uint32_t*)(scl + blk * 12);
+  const uint32_t s = ((sw[0] >> (4 * j)) & 15u) | (((sw[2] >> (2 * j)) & 3u) << 4);
+  const uint32_t m = ((sw[1] >> (4 * j)) & 15u) | (((sw[2] >> (16 + 2 * j)) & 3u) << 4);
+  const float d = f16_bits_to_f32(sup[2 * blk]), dmin = f16_bits_to_f32(sup[2 * blk + 1]);
+  const float ds = __fmul_rn(d, (float)s);
+  const float dm = __fmul_rn(dmin, (float)m);
+  float4* dst = (float4*)(out + si * 32);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    float r[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int p = e >> 1;
+      const uint32_t q = (cw[k] >> ((e & 1) ? 16 + 4 * p : 4 * p)) & 15u;
+      r[e] = __fsub_rn(__fmul_rn(ds, (float)q), dm);
+    }
+    dst[2 * k] = make_float4(r[0], r[1], r[2], r[3]);
+    dst[2 * k + 1] = make_float4(r[4], r[5], r[6], r[7]);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
 hipError_t launch_quant_cb2(const float* w, int64_t rows, int64_t cols, void* packed, hipStream_t st) {
@@ -393,6 +517,28 @@ hipError_t launch_dequant_q2k(const void* packed, int64_t rows, int64_t cols, fl
   const int64_t ns = nblk * 16;
   if (ns == 0) return hipSuccess;
   DS4_LAUNCH(k_dequant_q2k, dim3((unsigned)((ns + 255) / 256)), dim3(256), 0, st, codes, sub, sup, ns, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_q4k(const float* w, int64_t rows, int64_t cols, void* packed, hipStream_t st) {
+  const int64_t nblk = rows * (cols / QK);
+  uint8_t* codes = (uint8_t*)packed;
+  uint8_t* scl = codes + nblk * 128;
+  uint16_t* sup = (uint16_t*)(codes + nblk * 140);
+  const int64_t threads = nblk * 8;
+  if (threads == 0) return hipSuccess;
+  DS4_LAUNCH(k_quant_q4k, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, w, nblk, codes, scl, sup);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant_q4k(const void* packed, int64_t rows, int64_t cols, float* out, hipStream_t st) {
+  const int64_t nblk = rows * (cols / QK);
+  const uint8_t* codes = (const uint8_t*)packed;
+  const uint8_t* scl = codes + nblk * 128;
+  const uint16_t* sup = (const uint16_t*)(codes + nblk * 140);
+  const int64_t ns = nblk * 8;
+  if (ns == 0) return hipSuccess;
+  DS4_LAUNCH(k_dequant_q4k, dim3((unsigned)((ns + 255) / 256)), dim3(256), 0, st, codes, scl, sup, ns, out);
   return hipGetLastError();
 }
 

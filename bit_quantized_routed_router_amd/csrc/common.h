@@ -227,6 +227,33 @@ __device__ inline half8_t mx4_frag(uint32_t w, float scale) {
   return as_half8(r);
 }
 
+// Q4K fragment: the 8 codes of one 32-bit word (element 2p at bits 4p,
+// element 2p + 1 at bits 16 + 4p) as binary16 q * DS + NDM rounded once,
+// with DS = binary16(d * s) and NDM = -binary16(dmin * m) in both halves:
+// (x & 0x000F000F) | 0x64006400 reads 1024 + q in each half, exactly.
+__device__ inline half8_t q4k_frag(uint32_t w, half2_t DS, half2_t NDM) {
+  const half2_t k1024 = {(_Float16)-1024.0f, (_Float16)-1024.0f};
+  u32x4_t r;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const uint32_t t = __builtin_amdgcn_bitop3_b32(w >> (4 * p), 0x000F000Fu, 0x64006400u, 0xEA);
+    r[p] = as_u32(__builtin_elementwise_fma(as_half2(t) + k1024, DS, NDM));
+  }
+  return as_half8(r);
+}
+// DS and NDM of sub-block j of a Q4K super-block from its scale words
+// (w0: s nibbles, w1: m nibbles, w2: high bits) and its (d, dmin) word.
+__device__ inline void q4k_scales(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t sup, int j, half2_t& DS,
+                                  half2_t& NDM) {
+  const uint32_t s = ((w0 >> (4 * j)) & 15u) | (((w2 >> (2 * j)) & 3u) << 4);
+  const uint32_t m = ((w1 >> (4 * j)) & 15u) | (((w2 >> (16 + 2 * j)) & 3u) << 4);
+  const float d = (float)__builtin_bit_cast(_Float16, (uint16_t)(sup & 0xFFFFu));
+  const float dmin = (float)__builtin_bit_cast(_Float16, (uint16_t)(sup >> 16));
+  const _Float16 a = (_Float16)(d * (float)s), b = -(_Float16)(dmin * (float)m);
+  DS = (half2_t){a, a};
+  NDM = (half2_t){b, b};
+}
+
 __device__ inline half8_t zero_half8() {
   u32x4_t z = {0u, 0u, 0u, 0u};
   return as_half8(z);

@@ -370,6 +370,28 @@ __device__ inline half8_t mx4_step(const Mx4Sb& W, int s2) {
   const uint32_t w = (s2 & 3) == 0 ? c.x : ((s2 & 3) == 1 ? c.y : ((s2 & 3) == 2 ? c.z : c.w));
   return mx4_frag(w, e8m0_f32((W.sc >> ((s2 & 4) ? 8 : 0)) & 0xFFu));
 }
+// Per lane and super-block b of a Q4K [rows, K] matrix: the lane's two
+// sub-blocks 2q and 2q + 1 of its row (64 elements), the block's three
+// scale words and its (d, dmin) word.
+struct Q4kSb {
+  u32x4_t c0, c1;
+  uint32_t w0, w1, w2, sup;
+};
+// binary16 scales of the lane's two sub-blocks: [0] = 2q, [1] = 2q + 1
+struct Q4kS {
+  half2_t ds[2], nm[2];
+};
+__device__ inline Q4kS q4k_lane_scales(const Q4kSb& W, int q) {
+  Q4kS S;
+  q4k_scales(W.w0, W.w1, W.w2, W.sup, 2 * q, S.ds[0], S.nm[0]);
+  q4k_scales(W.w0, W.w1, W.w2, W.sup, 2 * q + 1, S.ds[1], S.nm[1]);
+  return S;
+}
+__device__ inline half8_t q4k_step(const Q4kSb& W, const Q4kS& S, int s2) {
+  const u32x4_t& c = (s2 & 4) ? W.c1 : W.c0;
+  const uint32_t w = (s2 & 3) == 0 ? c.x : ((s2 & 3) == 1 ? c.y : ((s2 & 3) == 2 ? c.z : c.w));
+  return q4k_frag(w, S.ds[s2 >> 2], S.nm[s2 >> 2]);
+}
 
 // Blocks [0, maxd * f/16): one per (distinct expert, 16-row tile) of the
 // routed gate/up products, whose codebook decoding is the arithmetic; then
@@ -379,11 +401,11 @@ __device__ inline half8_t mx4_step(const Mx4Sb& W, int s2) {
 // whole, 3 with the per-wave super-block buffers, fewer with fp32 input.
 constexpr int stage2_waves(bool lo, bool bl) { return bl ? (lo ? 2 : 4) : (lo ? 1 : 3); }
 
-template <bool LO, bool BL>
+template <bool LO, bool BL, bool Q4>
 __device__ void routed_gateup_mx(const ds4moe_layer& L, int T, const RouteOut& ro, const _Float16* __restrict__ xh,
                                  const _Float16* __restrict__ xl, _Float16* __restrict__ hw16, Stage2Lds<LO, BL>& lds);
 
-template <bool LO, bool BL, bool MX>
+template <bool LO, bool BL, bool MX, bool Q4 = false>
 __global__ __launch_bounds__(kW * 64) __attribute__((amdgpu_waves_per_eu(stage2_waves(LO, BL)))) void k_dec_stage2(
     ds4moe_layer L, int T, RouteOut ro, const _Float16* __restrict__ xh,
     const _Float16* __restrict__ xl, _Float16* __restrict__ hw16, _Float16* __restrict__ hsum, int rtiles,
@@ -394,8 +416,8 @@ __global__ __launch_bounds__(kW * 64) __attribute__((amdgpu_waves_per_eu(stage2_
                                 lds.last);
     return;
   }
-  if constexpr (MX) {
-    routed_gateup_mx<LO, BL>(L, T, ro, xh, xl, hw16, lds);
+  if constexpr (MX || Q4) {
+    routed_gateup_mx<LO, BL, Q4>(L, T, ro, xh, xl, hw16, lds);
     return;
   }
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -601,14 +623,16 @@ __global__ __launch_bounds__(kW * 64) __attribute__((amdgpu_waves_per_eu(stage2_
   }
 }
 
-// Routed gate/up tile of an MXFP4 layer: as the CB2 tile, with the two code
-// blocks of each super-block turned into binary16 fragments by the FP4
-// conversion (block scales folded in, so no per-super-block scale after the
-// products).  Activations come from LDS when staged (BL), else from the
+// Routed gate/up tile of an MXFP4 (Q4 false) or Q4K (Q4) layer: as the CB2
+// tile, with the lane's two 32-element blocks of each super-block turned
+// into binary16 fragments with their scales folded in (MXFP4 by the FP4
+// conversion, exact for the documented scale range; Q4K as q * binary16(d s)
+// - binary16(dmin m), rounded once), so no per-super-block scale after the
+// products.  Activations come from LDS when staged (BL), else from the
 // binary16 copy in memory.
-constexpr int kSbMx = 2;  // MXFP4 super-blocks a wave loads at once (32 bytes per matrix and lane each)
+constexpr int kSbMx = 2;  // super-blocks a wave loads at once (32 code bytes per matrix and lane each)
 
-template <bool LO, bool BL>
+template <bool LO, bool BL, bool Q4>
 __device__ void routed_gateup_mx(const ds4moe_layer& L, int T, const RouteOut& ro, const _Float16* __restrict__ xh,
                                  const _Float16* __restrict__ xl, _Float16* __restrict__ hw16, Stage2Lds<LO, BL>& lds) {
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -627,26 +651,46 @@ __device__ void routed_gateup_mx(const ds4moe_layer& L, int T, const RouteOut& r
     return;
   }
   const int e = clamp_index(ld_uniform(ro.distinct + i), L.n_experts);
-  const size_t mbytes = (size_t)f * d * 17 / 32;  // one packed [f, d] matrix
+  // one packed [f, d] matrix; a row's code bytes per super-block are 128 in both formats
+  const size_t mbytes = Q4 ? (size_t)f * nb * 144 : (size_t)f * d * 17 / 32;
   const uint8_t* gm = (const uint8_t*)L.gate + (size_t)e * mbytes;
   const uint8_t* um = (const uint8_t*)L.up + (size_t)e * mbytes;
   const uint8_t* grow = gm + (size_t)(row0 + c) * (d / 2) + 32 * q;
   const uint8_t* urow = um + (size_t)(row0 + c) * (d / 2) + 32 * q;
-  const uint8_t* gsc = gm + (size_t)f * d / 2 + (size_t)(row0 + c) * (d / 32) + 2 * q;
-  const uint8_t* usc = um + (size_t)f * d / 2 + (size_t)(row0 + c) * (d / 32) + 2 * q;
+  // MXFP4: the lane's two scale bytes; Q4K: the block's scale words, then (d, dmin)
+  const uint8_t* gsc = Q4 ? gm + (size_t)f * nb * 128 + (size_t)(row0 + c) * nb * 12
+                          : gm + (size_t)f * d / 2 + (size_t)(row0 + c) * (d / 32) + 2 * q;
+  const uint8_t* usc = Q4 ? um + (size_t)f * nb * 128 + (size_t)(row0 + c) * nb * 12
+                          : um + (size_t)f * d / 2 + (size_t)(row0 + c) * (d / 32) + 2 * q;
+  const uint8_t* gsp = gm + (size_t)f * nb * 140 + (size_t)(row0 + c) * nb * 4;  // Q4K only
+  const uint8_t* usp = um + (size_t)f * nb * 140 + (size_t)(row0 + c) * nb * 4;
   int sb0, sb1;
   split_range(nb, kW, wave, sb0, sb1);
   Mx4Sb wg[kSbMx], wu[kSbMx];
+  Q4kSb qg[kSbMx], qu[kSbMx];
   auto load_batch = [&](int b0) {
 #pragma unroll
     for (int j = 0; j < kSbMx; ++j) {
       const int b = max(min(b0 + j, sb1 - 1), 0);
-      wg[j].c0 = __builtin_nontemporal_load((const u32x4_t*)(grow + 128 * b));
-      wg[j].c1 = __builtin_nontemporal_load((const u32x4_t*)(grow + 128 * b + 16));
-      wu[j].c0 = __builtin_nontemporal_load((const u32x4_t*)(urow + 128 * b));
-      wu[j].c1 = __builtin_nontemporal_load((const u32x4_t*)(urow + 128 * b + 16));
-      wg[j].sc = *(const uint16_t*)(gsc + 8 * b);
-      wu[j].sc = *(const uint16_t*)(usc + 8 * b);
+      if constexpr (Q4) {
+        qg[j].c0 = __builtin_nontemporal_load((const u32x4_t*)(grow + 128 * b));
+        qg[j].c1 = __builtin_nontemporal_load((const u32x4_t*)(grow + 128 * b + 16));
+        qu[j].c0 = __builtin_nontemporal_load((const u32x4_t*)(urow + 128 * b));
+        qu[j].c1 = __builtin_nontemporal_load((const u32x4_t*)(urow + 128 * b + 16));
+        const uint32_t* gw = (const uint32_t*)(gsc + 12 * b);
+        const uint32_t* uw = (const uint32_t*)(usc + 12 * b);
+        qg[j].w0 = gw[0]; qg[j].w1 = gw[1]; qg[j].w2 = gw[2];
+        qu[j].w0 = uw[0]; qu[j].w1 = uw[1]; qu[j].w2 = uw[2];
+        qg[j].sup = *(const uint32_t*)(gsp + 4 * b);
+        qu[j].sup = *(const uint32_t*)(usp + 4 * b);
+      } else {
+        wg[j].c0 = __builtin_nontemporal_load((const u32x4_t*)(grow + 128 * b));
+        wg[j].c1 = __builtin_nontemporal_load((const u32x4_t*)(grow + 128 * b + 16));
+        wu[j].c0 = __builtin_nontemporal_load((const u32x4_t*)(urow + 128 * b));
+        wu[j].c1 = __builtin_nontemporal_load((const u32x4_t*)(urow + 128 * b + 16));
+        wg[j].sc = *(const uint16_t*)(gsc + 8 * b);
+        wu[j].sc = *(const uint16_t*)(usc + 8 * b);
+      }
     }
   };
   load_batch(sb0);
@@ -656,6 +700,14 @@ __device__ void routed_gateup_mx(const ds4moe_layer& L, int T, const RouteOut& r
   for (int b0 = sb0; b0 < sb1; b0 += kSbMx) {
     if (b0 != sb0) load_batch(b0);
     pin();
+    Q4kS sg[kSbMx], su[kSbMx];
+    if constexpr (Q4) {
+#pragma unroll
+      for (int j = 0; j < kSbMx; ++j) {
+        sg[j] = q4k_lane_scales(qg[j], q);
+        su[j] = q4k_lane_scales(qu[j], q);
+      }
+    }
 #pragma unroll
     for (int t = 0; t < 8 * kSbMx; ++t) {
       const int j = t >> 3, s2 = t & 7;
@@ -669,7 +721,8 @@ __device__ void routed_gateup_mx(const ds4moe_layer& L, int T, const RouteOut& r
         bh = *(const half8_t*)(xh + (int64_t)tc * d + kk);
         if (LO) bl = *(const half8_t*)(xl + (int64_t)tc * d + kk);
       }
-      const half8_t a0 = mx4_step(wg[j], s2), a1 = mx4_step(wu[j], s2);
+      const half8_t a0 = Q4 ? q4k_step(qg[j], sg[j], s2) : mx4_step(wg[j], s2);
+      const half8_t a1 = Q4 ? q4k_step(qu[j], su[j], s2) : mx4_step(wu[j], s2);
       ag = mfma16x16x32(bh, a0, ag);
       au = mfma16x16x32(bh, a1, au);
       if (LO) {
@@ -782,8 +835,8 @@ constexpr int kUnits3 = 3;  // units whose weight loads a wave keeps in flight
 // whole sum stays in the block and it writes y = ys + the routed terms
 // itself.  The routed weights are requested first: their decode is the
 // arithmetic, and the shared expert's F16 rows stream in behind them.
-// One MXFP4 down unit, transposed like q2k_unit: 8 steps over the lane's
-// two blocks (scales folded into the binary16 weights), no min term.
+// One MXFP4 or Q4K down unit, transposed like q2k_unit: 8 steps over the
+// lane's two 32-element blocks (scales folded into the binary16 weights).
 __device__ inline void mx4_unit(const Mx4Sb& U, const Q2kA& A, uint32_t vmask, float4_t& acc) {
   float4_t p = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -791,8 +844,16 @@ __device__ inline void mx4_unit(const Mx4Sb& U, const Q2kA& A, uint32_t vmask, f
 #pragma unroll
   for (int r = 0; r < 4; ++r) acc[r] += ((vmask >> r) & 1u) ? p[r] : 0.0f;
 }
+__device__ inline void q4k_unit(const Q4kSb& U, const Q2kA& A, uint32_t vmask, int q, float4_t& acc) {
+  const Q4kS S = q4k_lane_scales(U, q);
+  float4_t p = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s2 = 0; s2 < 8; ++s2) p = mfma16x16x32(A.b[s2], q4k_step(U, S, s2), p);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) acc[r] += ((vmask >> r) & 1u) ? p[r] : 0.0f;
+}
 
-template <bool BL, bool MX>
+template <bool BL, bool MX, bool Q4 = false>
 __global__ __launch_bounds__(kW3 * 64) __attribute__((amdgpu_waves_per_eu(4))) void k_dec_stage3(
     ds4moe_layer L, int T, const int32_t* __restrict__ ndist, const int32_t* __restrict__ distinct,
     const int32_t* __restrict__ tok_slot, const _Float16* __restrict__ hw16, const _Float16* __restrict__ hsum,
@@ -819,7 +880,7 @@ __global__ __launch_bounds__(kW3 * 64) __attribute__((amdgpu_waves_per_eu(4))) v
   // copies of the activations into LDS; one barrier publishes them
   if (BL) {
     dma_rows(hw16, f, S, f, s_h, f, wave, kW3, lane);
-    if (!MX) dma_rows(hsum, fs16, 2 * S, fs16, s_cs, fs16, wave, kW3, lane);
+    if (!MX && !Q4) dma_rows(hsum, fs16, 2 * S, fs16, s_cs, fs16, wave, kW3, lane);
     dma_rows(hs16, fs, T, fs, s_hs, fs, wave, kW3, lane);
   }
   // routing tables: expert ids by scalar loads, which do not wait for the
@@ -831,10 +892,13 @@ __global__ __launch_bounds__(kW3 * 64) __attribute__((amdgpu_waves_per_eu(4))) v
   int sj[kUnits3], bsb[kUnits3];  // per unit: slot of token c, super-block
   Q2kW W[kUnits3];
   Mx4Sb WM[kUnits3];  // MXFP4: the lane's two blocks of the unit's super-block
+  Q4kSb WQ[kUnits3];  // Q4K: the same, with the block's scale words
   const Q2kOff off = q2k_offsets(mb, nb, row0, c, q);
-  const size_t mx_bytes = (size_t)d * f * 17 / 32;  // one packed MXFP4 [d, f] matrix
+  const size_t mx_bytes = Q4 ? mb * 144 : (size_t)d * f * 17 / 32;  // one packed MXFP4 / Q4K [d, f] matrix
   const uint32_t mx_codes = (uint32_t)((size_t)(row0 + c) * (f / 2) + 32 * q);
   const uint32_t mx_sc = (uint32_t)((size_t)d * f / 2 + (size_t)(row0 + c) * (f / 32) + 2 * q);
+  const uint32_t q4_sc = (uint32_t)(mb * 128 + (size_t)(row0 + c) * nb * 12);
+  const uint32_t q4_sp = (uint32_t)(mb * 140 + (size_t)(row0 + c) * nb * 4);
   // unit u -> (expert slot u / nb, super-block u % nb), stepped by kW3
   // without a division per unit
   const int di = kW3 / nb, db = kW3 % nb;
@@ -870,7 +934,16 @@ __global__ __launch_bounds__(kW3 * 64) __attribute__((amdgpu_waves_per_eu(4))) v
     pin();
 #pragma unroll
     for (int j = 0; j < kUnits3; ++j) {
-      if constexpr (MX) {
+      if constexpr (Q4) {
+        const uint8_t* base = down + (size_t)clamp_index(ej[j], L.n_experts) * mx_bytes;
+        WQ[j].c0 = __builtin_nontemporal_load((const u32x4_t*)(base + mx_codes + 128 * bj[j]));
+        WQ[j].c1 = __builtin_nontemporal_load((const u32x4_t*)(base + mx_codes + 128 * bj[j] + 16));
+        const uint32_t* sw = (const uint32_t*)(base + q4_sc + 12 * bj[j]);
+        WQ[j].w0 = sw[0];
+        WQ[j].w1 = sw[1];
+        WQ[j].w2 = sw[2];
+        WQ[j].sup = *(const uint32_t*)(base + q4_sp + 4 * bj[j]);
+      } else if constexpr (MX) {
         const uint8_t* base = down + (size_t)clamp_index(ej[j], L.n_experts) * mx_bytes;
         WM[j].c0 = __builtin_nontemporal_load((const u32x4_t*)(base + mx_codes + 128 * bj[j]));
         WM[j].c1 = __builtin_nontemporal_load((const u32x4_t*)(base + mx_codes + 128 * bj[j] + 16));
@@ -913,11 +986,12 @@ __global__ __launch_bounds__(kW3 * 64) __attribute__((amdgpu_waves_per_eu(4))) v
       const int row = has ? slot : 0;
       const int b = bsb[j];  // super-block
       Q2kA A;
-      if constexpr (MX) {
+      if constexpr (MX || Q4) {
         const _Float16* bcol = (BL ? s_h : hw16) + (size_t)row * f + b * QK;
 #pragma unroll
         for (int s2 = 0; s2 < 8; ++s2) A.b[s2] = *(const half8_t*)(bcol + q2k_boff(q, s2));
-        mx4_unit(WM[j], A, vmask, acc);
+        if constexpr (Q4) q4k_unit(WQ[j], A, vmask, q, acc);
+        else mx4_unit(WM[j], A, vmask, acc);
       } else {
         if (BL)
           q2k_act(A, s_h + (size_t)row * f + b * QK, s_cs + (size_t)row * fs16 + b * 16,
@@ -1141,7 +1215,7 @@ __global__ __launch_bounds__(kW3 * 64) __attribute__((amdgpu_waves_per_eu(4))) v
 }
 
 // ============================================================== launcher
-template <bool LO, bool BL, bool MX>
+template <bool LO, bool BL, bool MX, bool Q4>
 static void launch_stages12(const Fwd& f, int rblocks, int nsh, int maxd, int nr, const RouteOut& ro) {
   const ds4moe_layer& L = f.L;
   const WsLayout& y = f.lay;
@@ -1157,7 +1231,7 @@ static void launch_stages12(const Fwd& f, int rblocks, int nsh, int maxd, int nr
   auto hsum = (_Float16*)(ws + y.hsum);
   const dim3 blk(kW * 64);
   DS4_LAUNCH((k_dec_stage1<LO>), dim3(rblocks), blk, 0, f.st, L, T, f.x, rblocks, plog, ro, xh, xl, ctrl);
-  DS4_LAUNCH((k_dec_stage2<LO, BL, MX>), dim3(maxd * nr + 2 * nsh), blk, 0, f.st, L, T, ro, xh, xl, hw16, hsum,
+  DS4_LAUNCH((k_dec_stage2<LO, BL, MX, Q4>), dim3(maxd * nr + 2 * nsh), blk, 0, f.st, L, T, ro, xh, xl, hw16, hsum,
              maxd * nr, gu, hs16, ctrl);
 }
 
@@ -1174,10 +1248,11 @@ hipError_t launch_decode(const Fwd& f) {
   // stage the activations in LDS when every staged row set fits: the x
   // halves (stages 1 and 2) and x (stage 2 routed)
   const bool bl = (int64_t)T * d <= kStageHalves;
-  const bool mx = L.expert_fmt == DS4MOE_EXPERTS_MXFP4;
-#define DS4_S12(LO_, BL_)                                                   \
-  (mx ? launch_stages12<LO_, BL_, true>(f, rblocks, nsh, maxd, nr, ro)   \
-      : launch_stages12<LO_, BL_, false>(f, rblocks, nsh, maxd, nr, ro))
+  const bool mx = L.expert_fmt == DS4MOE_EXPERTS_MXFP4, q4 = L.expert_fmt == DS4MOE_EXPERTS_Q4K;
+#define DS4_S12(LO_, BL_)                                                            \
+  (mx   ? launch_stages12<LO_, BL_, true, false>(f, rblocks, nsh, maxd, nr, ro)    \
+   : q4 ? launch_stages12<LO_, BL_, false, true>(f, rblocks, nsh, maxd, nr, ro)    \
+        : launch_stages12<LO_, BL_, false, false>(f, rblocks, nsh, maxd, nr, ro))
   if (f.lo) {
     if (bl) DS4_S12(true, true);
     else DS4_S12(true, false);
@@ -1199,20 +1274,22 @@ hipError_t launch_decode(const Fwd& f) {
   // one token: the dot-product form (pairs, OFF and HS sums, shared h)
   const size_t one_bytes = (size_t)L.top_k * L.d_ff * 2 + (size_t)2 * L.top_k * (L.d_ff / 16) * 4 +
                            (size_t)L.d_ff_shared * 2;
-  if (T == 1 && one_bytes <= kStage3OneBytes && !mx) {
+  if (T == 1 && one_bytes <= kStage3OneBytes && !mx && !q4) {
     DS4_LAUNCH(k_dec_stage3_one, dim3(ndt), blk3, one_bytes, f.st, L, ro.ndist, ro.distinct, ro.tok_slot, hw16,
                hs16, ctrl, ctrl_ints(L), maxd, f.y);
     return hipGetLastError();
   }
-#define DS4_S3(BL_, MX_, BYTES)                                                                                  \
-  DS4_LAUNCH((k_dec_stage3<BL_, MX_>), dim3(ndt), blk3, BYTES, f.st, L, T, ro.ndist, ro.distinct, ro.tok_slot, hw16, \
-             hsum, hs16, ctrl, ctrl_ints(L), maxd, f.y)
+#define DS4_S3(BL_, MX_, Q4_, BYTES)                                                                  \
+  DS4_LAUNCH((k_dec_stage3<BL_, MX_, Q4_>), dim3(ndt), blk3, BYTES, f.st, L, T, ro.ndist, ro.distinct, \
+             ro.tok_slot, hw16, hsum, hs16, ctrl, ctrl_ints(L), maxd, f.y)
   if (stage_bytes <= kStage3Bytes) {
-    if (mx) DS4_S3(true, true, stage_bytes);
-    else DS4_S3(true, false, stage_bytes);
+    if (mx) DS4_S3(true, true, false, stage_bytes);
+    else if (q4) DS4_S3(true, false, true, stage_bytes);
+    else DS4_S3(true, false, false, stage_bytes);
   } else {
-    if (mx) DS4_S3(false, true, 0);
-    else DS4_S3(false, false, 0);
+    if (mx) DS4_S3(false, true, false, 0);
+    else if (q4) DS4_S3(false, false, true, 0);
+    else DS4_S3(false, false, false, 0);
   }
 #undef DS4_S3
   return hipGetLastError();

@@ -69,6 +69,8 @@ hipError_t launch_dequant_cb2(const void* packed, int64_t rows, int64_t cols, fl
 hipError_t launch_dequant_q2k(const void* packed, int64_t rows, int64_t cols, float* out, hipStream_t st);
 hipError_t launch_quant_mx4(const float* w, int64_t rows, int64_t cols, void* packed, hipStream_t st);
 hipError_t launch_dequant_mx4(const void* packed, int64_t rows, int64_t cols, float* out, hipStream_t st);
+hipError_t launch_quant_q4k(const float* w, int64_t rows, int64_t cols, void* packed, hipStream_t st);
+hipError_t launch_dequant_q4k(const void* packed, int64_t rows, int64_t cols, float* out, hipStream_t st);
 
 // routing: x conversion + logits + top-k + grouping.  decode == true builds
 // the distinct-expert tables of a <= 16-token group.

@@ -197,29 +197,33 @@ struct GuLds {
   float w[kTT];
   uint16_t dsc[NBS ? 2 * 128 * NBS : 2];
 };
-template <bool DENSE, bool MX = false>
-constexpr int gu_nbs() { return DENSE || MX ? 0 : 16; }
+template <bool DENSE, bool MX = false, bool Q4 = false>
+constexpr int gu_nbs() { return DENSE || MX || Q4 ? 0 : 16; }
 
 // Weights of one 128-input chunk for a lane's four fragments.  CB2: the lane's sub-block (8 bytes) and its block's d; F16:
 // the lane's 4 x 8 binary16 values (inputs 32q .. 32q+31 of the chunk).  kLoads counts the vector-memory loads of a
 // chunk when every scale comes from LDS; kMaxLoads when they are all read from memory (blocks past the staged ones).
 // MXFP4: the lane's 32 inputs of the chunk are one MX block, 16 code bytes and
 // one scale byte per fragment.
-template <bool F16, bool MX = false>
+// Q4K (Q4): the lane's 32 inputs are one sub-block, 16 code bytes, plus its
+// super-block's three scale words and (d, dmin) word per fragment.
+template <bool F16, bool MX = false, bool Q4 = false>
 struct GuW {
-  u32x2_t cw[MX ? 1 : 4];
+  u32x2_t cw[MX || Q4 ? 1 : 4];
   uint32_t dv[4];
   u32x4_t wv[F16 ? 4 : 1][F16 ? 4 : 1];
-  u32x4_t mw[MX ? 4 : 1];
-  static constexpr int kLoads = F16 ? 16 : (MX ? 8 : 4);
-  static constexpr int kMaxLoads = F16 ? 16 : 8;
+  u32x4_t mw[MX || Q4 ? 4 : 1];
+  uint32_t qs[Q4 ? 4 : 1][Q4 ? 3 : 1];
+  int jq;  // Q4K: the lane's sub-block within its super-block (set at issue)
+  static constexpr int kLoads = F16 ? 16 : (Q4 ? 20 : (MX ? 8 : 4));
+  static constexpr int kMaxLoads = F16 ? 16 : (Q4 ? 20 : 8);
 };
 
 // Gate/up of one work tile (up to 128 slots) for a 128-row slice of h, NF
 // slot fragments.  DENSE: the shared expert (F16 weights, weight 1, rows are
 // tokens); otherwise routed expert e (CB2 weights, or MXFP4 with MX; routing
 // weights s.w).
-template <bool LO, bool DENSE, int NW, int TC, int RING, int NF, int NBS, bool MX = false>
+template <bool LO, bool DENSE, int NW, int TC, int RING, int NF, int NBS, bool MX = false, bool Q4 = false>
 __device__ __attribute__((always_inline)) inline void gateup_tile(const ds4moe_layer& L, GuLds<LO, TC, RING, NBS>& s,
                                                                   const _Float16* __restrict__ xh,
                                                                   const _Float16* __restrict__ xl, int e, int rt,
@@ -227,20 +231,30 @@ __device__ __attribute__((always_inline)) inline void gateup_tile(const ds4moe_l
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, c = lane & 15, q = lane >> 4;
   const int d = L.d_model, fd = DENSE ? L.d_ff_shared : L.d_ff, nb = d / QK, nch = d / kKC;
   const size_t mb = (size_t)fd * nb;
-  const size_t mat_bytes = MX ? (size_t)fd * d * 17 / 32 : mb * 66;
+  const size_t mat_bytes = Q4 ? mb * 144 : (MX ? (size_t)fd * d * 17 / 32 : mb * 66);
   const uint8_t* gb = DENSE ? (const uint8_t*)L.sh_gate : (const uint8_t*)L.gate + (size_t)e * mat_bytes;
   const uint8_t* ub = DENSE ? (const uint8_t*)L.sh_up : (const uint8_t*)L.up + (size_t)e * mat_bytes;
-  const uint8_t* gd = gb + (MX ? (size_t)fd * d / 2 : mb * 64);  // CB2 d plane / MXFP4 scale plane
-  const uint8_t* ud = ub + (MX ? (size_t)fd * d / 2 : mb * 64);
+  // CB2 d plane / MXFP4 scale plane / Q4K scale words
+  const uint8_t* gd = gb + (Q4 ? mb * 128 : (MX ? (size_t)fd * d / 2 : mb * 64));
+  const uint8_t* ud = ub + (Q4 ? mb * 128 : (MX ? (size_t)fd * d / 2 : mb * 64));
+  const uint8_t* gsp = gb + mb * 140;  // Q4K (d, dmin) words
+  const uint8_t* usp = ub + mb * 140;
   const int hr0 = rt * 32 * NW + 32 * wave;
   // fragment f: rows hr0 + 16 (f & 1) + c of gate (f < 2) or up (f >= 2)
   uint32_t rowu[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) rowu[h] = (uint32_t)((hr0 + 16 * h + c) * (DENSE ? d : nb));
-  auto load_w = [&](int ch, GuW<DENSE, MX>& W) {
+  auto load_w = [&](int ch, GuW<DENSE, MX, Q4>& W) {
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
-      if constexpr (MX) {  // row hr0 + 16 (f & 1) + c, block 4 ch + q
+      if constexpr (Q4) {  // row hr0 + 16 (f & 1) + c, sub-block 4 (ch & 1) + q of super-block ch / 2
+        const uint32_t r = (uint32_t)(hr0 + 16 * (f & 1) + c), blk = r * (uint32_t)nb + (uint32_t)(ch >> 1);
+        W.mw[f] = ld_at<u32x4_t>(f < 2 ? gb : ub, blk * 128u + 16u * (uint32_t)(4 * (ch & 1) + q));
+#pragma unroll
+        for (int t = 0; t < 3; ++t) W.qs[f][t] = ld_at<uint32_t>(f < 2 ? gd : ud, blk * 12u + 4u * t);
+        W.dv[f] = ld_at<uint32_t>(f < 2 ? gsp : usp, blk * 4u);
+        W.jq = 4 * (ch & 1) + q;
+      } else if constexpr (MX) {  // row hr0 + 16 (f & 1) + c, block 4 ch + q
         const uint32_t r = (uint32_t)(hr0 + 16 * (f & 1) + c), blk = (uint32_t)(4 * ch + q);
         W.mw[f] = ld_at<u32x4_t>(f < 2 ? gb : ub, r * (uint32_t)(d / 2) + 16u * blk);
         W.dv[f] = ld_at<uint8_t>(f < 2 ? gd : ud, r * (uint32_t)(d / 32) + blk);
@@ -267,11 +281,11 @@ __device__ __attribute__((always_inline)) inline void gateup_tile(const ds4moe_l
 
   // Loads per chunk and lane.  The ring depth keeps the largest count within the load counter; the waits use the
   // smallest, which is exact when every scale is staged and waits longer than needed otherwise.
-  constexpr int kBatch = dma_per_wave(NF, NW) * (LO ? 2 : 1) + GuW<DENSE, MX>::kLoads;
-  constexpr int R = ring_depth(NF, dma_per_wave(NF, NW) * (LO ? 2 : 1) + GuW<DENSE, MX>::kMaxLoads, LO, RING);
+  constexpr int kBatch = dma_per_wave(NF, NW) * (LO ? 2 : 1) + GuW<DENSE, MX, Q4>::kLoads;
+  constexpr int R = ring_depth(NF, dma_per_wave(NF, NW) * (LO ? 2 : 1) + GuW<DENSE, MX, Q4>::kMaxLoads, LO, RING);
   constexpr int kSlot = NF * 16 * kKC;  // halves per ring slot
   static_assert(R * kSlot <= RING, "ring slots exceed the staging buffer");
-  GuW<DENSE, MX> W[R];
+  GuW<DENSE, MX, Q4> W[R];
   auto issue = [&](int ch, int u) {
     stage_rows<LO, NF, NW>(xh, xl, rows, ch, s.xh + u * kSlot, s.xl + (LO ? u * kSlot : 0), wave, lane);
     load_w(ch, W[u]);
@@ -281,7 +295,12 @@ __device__ __attribute__((always_inline)) inline void gateup_tile(const ds4moe_l
   auto compute = [&](int u) {
     half2_t D2[4];
     float XS[4];  // MXFP4 block scales
-    if constexpr (MX) {
+    half2_t QD[4], QN[4];  // Q4K binary16 d*s and -dmin*m of the lane's sub-block
+    if constexpr (Q4) {
+#pragma unroll
+      for (int f = 0; f < 4; ++f)
+        q4k_scales(W[u].qs[f][0], W[u].qs[f][1], W[u].qs[f][2], W[u].dv[f], W[u].jq, QD[f], QN[f]);
+    } else if constexpr (MX) {
 #pragma unroll
       for (int f = 0; f < 4; ++f) XS[f] = e8m0_f32(W[u].dv[f] & 0xFFu);
     } else if constexpr (!DENSE) {
@@ -294,7 +313,9 @@ __device__ __attribute__((always_inline)) inline void gateup_tile(const ds4moe_l
       half8_t wf[4];
 #pragma unroll
       for (int f = 0; f < 4; ++f) {
-        if constexpr (MX)
+        if constexpr (Q4)
+          wf[f] = q4k_frag(W[u].mw[f][j], QD[f], QN[f]);
+        else if constexpr (MX)
           wf[f] = mx4_frag(W[u].mw[f][j], XS[f]);
         else if constexpr (DENSE)
           wf[f] = as_half8(W[u].wv[f][j]);
@@ -382,7 +403,7 @@ constexpr int gu_copies() { return 1; }
 
 // SMALL: the small-tile list (at most 32 slots per tile, a smaller ring).
 // MX: the routed experts are MXFP4.
-template <bool LO, bool DENSE, bool SMALL, bool MX = false>
+template <bool LO, bool DENSE, bool SMALL, bool MX = false, bool Q4 = false>
 __global__ __launch_bounds__((gu_waves<LO, DENSE>() * 64))
 __attribute__((amdgpu_waves_per_eu(DENSE || LO ? 1 : 2))) void k_pf_gateup(
     ds4moe_layer L, int64_t T, const _Float16* __restrict__ xh, const _Float16* __restrict__ xl,
@@ -390,14 +411,14 @@ __attribute__((amdgpu_waves_per_eu(DENSE || LO ? 1 : 2))) void k_pf_gateup(
     const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets, const int32_t* __restrict__ perm,
     const float* __restrict__ topk_w, _Float16* __restrict__ hout) {
   constexpr int NW = gu_waves<LO, DENSE>(), TC = gu_copies<LO, DENSE>(), RING = ring_halves(SMALL);
-  constexpr int NBS = gu_nbs<DENSE, MX>();
+  constexpr int NBS = gu_nbs<DENSE, MX, Q4>();
   static_assert(NW == 4, "the staged scales cover 4 waves x 32 rows");
   __shared__ GuLds<LO, TC, RING, NBS> s;
   int e, rt, pos0, n;
   if (!tile_of<DENSE, SMALL>((DENSE ? L.d_ff_shared : L.d_ff) / (32 * NW), T, tiles, stiles, ntiles, counts, offsets,
                              e, rt, pos0, n))
     return;
-  if constexpr (!DENSE && !MX) {
+  if constexpr (!DENSE && !MX && !Q4) {
     s.tab.stage(c_pre_tables);
     // scales of rows rt*128 .. +127 of gate (g = 0) and up (g = 1), blocks 0 .. ns-1
     const int nb = L.d_model / QK, ns = min(nb, NBS);
@@ -420,7 +441,7 @@ __attribute__((amdgpu_waves_per_eu(DENSE || LO ? 1 : 2))) void k_pf_gateup(
     }
   }
   __syncthreads();
-#define DS4_GU(NF) gateup_tile<LO, DENSE, NW, TC, RING, NF, NBS, MX>(L, s, xh, xl, e, rt, pos0, n, hout)
+#define DS4_GU(NF) gateup_tile<LO, DENSE, NW, TC, RING, NF, NBS, MX, Q4>(L, s, xh, xl, e, rt, pos0, n, hout)
   DS4_NF_SWITCH(n, SMALL, DENSE, DS4_GU)
 #undef DS4_GU
 }
@@ -449,20 +470,22 @@ constexpr int kDnStagedMax = 8;
 // aligned word holding their two scale bytes, the block's d/dmin; F16: 4 x 8
 // binary16 values per fragment.  kLoads / kMaxLoads: vector-memory loads of a
 // chunk with the scales staged in LDS / read from memory.
-template <bool F16, bool SC, bool DD, bool MX = false>
+template <bool F16, bool SC, bool DD, bool MX = false, bool Q4 = false>
 struct DnW {
-  u32x2_t cw[MX ? 1 : 4];
+  u32x2_t cw[MX || Q4 ? 1 : 4];
   uint32_t sc[4], dd[MX ? 1 : 4];
   u32x4_t wv[F16 ? 4 : 1][F16 ? 4 : 1];
-  u32x4_t mw[MX ? 4 : 1];  // MXFP4: the lane's block of 32 (16 code bytes); its scale byte in sc
-  static constexpr int kMaxLoads = F16 ? 16 : (MX ? 8 : 12);
-  static constexpr int kLoads = F16 ? 16 : (MX ? 8 : 4 + (SC ? 0 : 4) + (DD ? 0 : 4));
+  u32x4_t mw[MX || Q4 ? 4 : 1];  // MXFP4 / Q4K: the lane's 32 elements (16 code bytes); MXFP4's scale byte in sc
+  uint32_t qs[Q4 ? 4 : 1][Q4 ? 3 : 1];  // Q4K: scale words; (d, dmin) in dd
+  int jq;                                // Q4K: the lane's sub-block within its super-block
+  static constexpr int kMaxLoads = F16 ? 16 : (Q4 ? 20 : (MX ? 8 : 12));
+  static constexpr int kLoads = F16 ? 16 : (Q4 ? 20 : (MX ? 8 : 4 + (SC ? 0 : 4) + (DD ? 0 : 4)));
 };
 
 // Down product of one work tile for a 256-row slice of the output.  Routed
 // (Q2K, or MXFP4 with MX): yp[slot] = D_e h.  DENSE (shared, F16):
 // y[t] = Wsd hs16[t].
-template <bool DENSE, int RING, int NF, int NBS, bool SC, bool FULL, bool MX = false>
+template <bool DENSE, int RING, int NF, int NBS, bool SC, bool FULL, bool MX = false, bool Q4 = false>
 __device__ __attribute__((always_inline)) inline void down_tile(const ds4moe_layer& L, DnLds<RING, NBS, SC>& s,
                                                                 const _Float16* __restrict__ hin, int e, int rt,
                                                                 int pos0, int n, float* __restrict__ yp,
@@ -470,17 +493,25 @@ __device__ __attribute__((always_inline)) inline void down_tile(const ds4moe_lay
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, c = lane & 15, q = lane >> 4;
   const int d = L.d_model, fd = DENSE ? L.d_ff_shared : L.d_ff, nb = fd / QK, nch = fd / kKC;
   const size_t mb = (size_t)d * nb;
-  const size_t mat_bytes = MX ? (size_t)d * fd * 17 / 32 : mb * 84;
+  const size_t mat_bytes = Q4 ? mb * 144 : (MX ? (size_t)d * fd * 17 / 32 : mb * 84);
   const uint8_t* base = DENSE ? (const uint8_t*)L.sh_down : (const uint8_t*)L.down + (size_t)e * mat_bytes;
-  const uint8_t* sub = base + (MX ? (size_t)d * fd / 2 : mb * 64);  // Q2K sub-scales / MXFP4 scale plane
-  const uint8_t* sup = base + mb * 80;
+  // Q2K sub-scales / MXFP4 scale plane / Q4K scale words
+  const uint8_t* sub = base + (Q4 ? mb * 128 : (MX ? (size_t)d * fd / 2 : mb * 64));
+  const uint8_t* sup = base + (Q4 ? mb * 140 : mb * 80);
   const int r0 = rt * 256 + 64 * wave;
   const uint32_t row0 = (uint32_t)((r0 + c) * (DENSE ? fd : nb));  // fragment f: + 16 f (fd or nb)
-  using WT = DnW<DENSE, SC, (NBS > 0), MX>;
+  using WT = DnW<DENSE, SC, (NBS > 0), MX, Q4>;
   auto load_w = [&](int ch, WT& W) {
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
-      if constexpr (MX) {  // row r0 + 16 f + c, block 4 ch + q
+      if constexpr (Q4) {  // row r0 + 16 f + c, sub-block 4 (ch & 1) + q of super-block ch / 2
+        const uint32_t r = (uint32_t)(r0 + 16 * f + c), blk = r * (uint32_t)nb + (uint32_t)(ch >> 1);
+        W.mw[f] = ld_at<u32x4_t>(base, blk * 128u + 16u * (uint32_t)(4 * (ch & 1) + q));
+#pragma unroll
+        for (int t = 0; t < 3; ++t) W.qs[f][t] = ld_at<uint32_t>(sub, blk * 12u + 4u * t);
+        W.dd[f] = ld_at<uint32_t>(sup, blk * 4u);
+        W.jq = 4 * (ch & 1) + q;
+      } else if constexpr (MX) {  // row r0 + 16 f + c, block 4 ch + q
         const uint32_t r = (uint32_t)(r0 + 16 * f + c), blk = (uint32_t)(4 * ch + q);
         W.mw[f] = ld_at<u32x4_t>(base, r * (uint32_t)(fd / 2) + 16u * blk);
         W.sc[f] = ld_at<uint8_t>(sub, r * (uint32_t)(fd / 32) + blk);
@@ -525,15 +556,19 @@ __device__ __attribute__((always_inline)) inline void down_tile(const ds4moe_lay
   const half2_t k1024 = {(_Float16)-1024.0f, (_Float16)-1024.0f};
   auto compute = [&](int u) {
     const _Float16* bh = s.xh + u * kSlot;
-    if constexpr (MX) {
+    if constexpr (MX || Q4) {
       float XS[4];
+      half2_t QD[4], QN[4];
 #pragma unroll
-      for (int f = 0; f < 4; ++f) XS[f] = e8m0_f32(W[u].sc[f] & 0xFFu);
+      for (int f = 0; f < 4; ++f) {
+        if constexpr (Q4) q4k_scales(W[u].qs[f][0], W[u].qs[f][1], W[u].qs[f][2], W[u].dd[f], W[u].jq, QD[f], QN[f]);
+        else XS[f] = e8m0_f32(W[u].sc[f] & 0xFFu);
+      }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {  // code word j: inputs 32q + 8j .. +7 of the chunk
         half8_t wf[4];
 #pragma unroll
-        for (int f = 0; f < 4; ++f) wf[f] = mx4_frag(W[u].mw[f][j], XS[f]);
+        for (int f = 0; f < 4; ++f) wf[f] = Q4 ? q4k_frag(W[u].mw[f][j], QD[f], QN[f]) : mx4_frag(W[u].mw[f][j], XS[f]);
 #pragma unroll
         for (int i = 0; i < NF; ++i) {
           const half8_t a = slot_frag(bh, i, c, q, j);
@@ -605,7 +640,7 @@ __device__ __attribute__((always_inline)) inline void down_tile(const ds4moe_lay
 
 // Routed down (Q2K, or MXFP4 with MX) over the work list into yp, or (DENSE)
 // the shared expert's down (F16) over all T tokens into y.
-template <bool DENSE, bool SMALL, bool DDS, bool MX = false>
+template <bool DENSE, bool SMALL, bool DDS, bool MX = false, bool Q4 = false>
 __global__ __launch_bounds__(kGW * 64)
 __attribute__((amdgpu_waves_per_eu(DENSE ? 1 : 2))) void k_pf_down(
     ds4moe_layer L, int64_t T, const int32_t* __restrict__ tiles, const int32_t* __restrict__ stiles,
@@ -613,8 +648,8 @@ __attribute__((amdgpu_waves_per_eu(DENSE ? 1 : 2))) void k_pf_down(
     const int32_t* __restrict__ perm, const _Float16* __restrict__ hin, float* __restrict__ yp,
     float* __restrict__ y) {
   constexpr int RING = ring_halves(SMALL);
-  constexpr int NBS = MX ? 0 : dn_nbs<DENSE, SMALL, DDS>();
-  constexpr bool SC = !DENSE && SMALL && !MX;
+  constexpr int NBS = MX || Q4 ? 0 : dn_nbs<DENSE, SMALL, DDS>();
+  constexpr bool SC = !DENSE && SMALL && !MX && !Q4;
   static_assert(!DDS || (!DENSE && !SMALL), "DDS: large routed tiles");
   __shared__ DnLds<RING, NBS, SC> s;
   int e, rt, pos0, n;
@@ -639,7 +674,7 @@ __attribute__((amdgpu_waves_per_eu(DENSE ? 1 : 2))) void k_pf_down(
     }
   }
   __syncthreads();
-#define DS4_DN(NF) down_tile<DENSE, RING, NF, NBS, SC, DDS, MX>(L, s, hin, e, rt, pos0, n, yp, y)
+#define DS4_DN(NF) down_tile<DENSE, RING, NF, NBS, SC, DDS, MX, Q4>(L, s, hin, e, rt, pos0, n, yp, y)
   DS4_NF_SWITCH(n, SMALL, DENSE, DS4_DN)
 #undef DS4_DN
 }
@@ -689,40 +724,45 @@ hipError_t launch_prefill_experts(const Fwd& f) {
   const dim3 gsh((unsigned)(ttiles * (L.d_ff_shared / 128))), gsd((unsigned)(ttiles * (d / 256)));
   const dim3 ggu((unsigned)(maxtiles * gr)), ggs((unsigned)(E * gr));
   const dim3 gdn((unsigned)(maxtiles * (d / 256))), gds((unsigned)(E * (d / 256)));
-  const bool mx = L.expert_fmt == DS4MOE_EXPERTS_MXFP4;
-#define DS4_GU_LAUNCH(LO, DENSE, SMALL, MX, grid, out)                                                                \
-  DS4_LAUNCH((k_pf_gateup<LO, DENSE, SMALL, MX>), grid, blk, 0, f.st, L, T, xh, xl, tiles, stiles, ntiles, counts, \
-             offsets, perm, w, out)
+  const bool mx = L.expert_fmt == DS4MOE_EXPERTS_MXFP4, q4 = L.expert_fmt == DS4MOE_EXPERTS_Q4K;
+#define DS4_GU_LAUNCH(LO, DENSE, SMALL, MX, Q4, grid, out)                                                       \
+  DS4_LAUNCH((k_pf_gateup<LO, DENSE, SMALL, MX, Q4>), grid, blk, 0, f.st, L, T, xh, xl, tiles, stiles, ntiles, \
+             counts, offsets, perm, w, out)
+#define DS4_GU_ROUTED(LO)                                              \
+  do {                                                                 \
+    if (mx) {                                                          \
+      DS4_GU_LAUNCH(LO, false, false, true, false, ggu, hw16);         \
+      DS4_GU_LAUNCH(LO, false, true, true, false, ggs, hw16);          \
+    } else if (q4) {                                                   \
+      DS4_GU_LAUNCH(LO, false, false, false, true, ggu, hw16);         \
+      DS4_GU_LAUNCH(LO, false, true, false, true, ggs, hw16);          \
+    } else {                                                           \
+      DS4_GU_LAUNCH(LO, false, false, false, false, ggu, hw16);        \
+      DS4_GU_LAUNCH(LO, false, true, false, false, ggs, hw16);         \
+    }                                                                  \
+  } while (0)
   if (f.lo) {
-    DS4_GU_LAUNCH(true, true, false, false, gsh, hs16);
-    if (mx) {
-      DS4_GU_LAUNCH(true, false, false, true, ggu, hw16);
-      DS4_GU_LAUNCH(true, false, true, true, ggs, hw16);
-    } else {
-      DS4_GU_LAUNCH(true, false, false, false, ggu, hw16);
-      DS4_GU_LAUNCH(true, false, true, false, ggs, hw16);
-    }
+    DS4_GU_LAUNCH(true, true, false, false, false, gsh, hs16);
+    DS4_GU_ROUTED(true);
   } else {
-    DS4_GU_LAUNCH(false, true, false, false, gsh, hs16);
-    if (mx) {
-      DS4_GU_LAUNCH(false, false, false, true, ggu, hw16);
-      DS4_GU_LAUNCH(false, false, true, true, ggs, hw16);
-    } else {
-      DS4_GU_LAUNCH(false, false, false, false, ggu, hw16);
-      DS4_GU_LAUNCH(false, false, true, false, ggs, hw16);
-    }
+    DS4_GU_LAUNCH(false, true, false, false, false, gsh, hs16);
+    DS4_GU_ROUTED(false);
   }
+#undef DS4_GU_ROUTED
 #undef DS4_GU_LAUNCH
-#define DS4_DN_LAUNCH(DENSE, SMALL, DDS, MX, grid, hin)                                                          \
-  DS4_LAUNCH((k_pf_down<DENSE, SMALL, DDS, MX>), grid, blk, 0, f.st, L, T, tiles, stiles, ntiles, counts, offsets, \
+#define DS4_DN_LAUNCH(DENSE, SMALL, DDS, MX, Q4, grid, hin)                                                          \
+  DS4_LAUNCH((k_pf_down<DENSE, SMALL, DDS, MX, Q4>), grid, blk, 0, f.st, L, T, tiles, stiles, ntiles, counts, offsets, \
              perm, hin, yp, f.y)
   if (mx) {
-    DS4_DN_LAUNCH(false, false, false, true, gdn, hw16);
-    DS4_DN_LAUNCH(false, true, false, true, gds, hw16);
+    DS4_DN_LAUNCH(false, false, false, true, false, gdn, hw16);
+    DS4_DN_LAUNCH(false, true, false, true, false, gds, hw16);
+  } else if (q4) {
+    DS4_DN_LAUNCH(false, false, false, false, true, gdn, hw16);
+    DS4_DN_LAUNCH(false, true, false, false, true, gds, hw16);
   } else {
-    if (L.d_ff / QK <= kDnStagedMax) DS4_DN_LAUNCH(false, false, true, false, gdn, hw16);
-    else DS4_DN_LAUNCH(false, false, false, false, gdn, hw16);
-    DS4_DN_LAUNCH(false, true, false, false, gds, hw16);
+    if (L.d_ff / QK <= kDnStagedMax) DS4_DN_LAUNCH(false, false, true, false, false, gdn, hw16);
+    else DS4_DN_LAUNCH(false, false, false, false, false, gdn, hw16);
+    DS4_DN_LAUNCH(false, true, false, false, false, gds, hw16);
   }
 #undef DS4_DN_LAUNCH
   DS4_LAUNCH((k_pf_down<true, false, false>), gsd, blk, 0, f.st, L, T, tiles, stiles, ntiles, counts, offsets, perm,

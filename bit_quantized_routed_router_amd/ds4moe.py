@@ -15,8 +15,8 @@ import torch
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libds4moe.so")
 
 OK, EINVAL, ESHAPE, EALIGN, EWORKSPACE, EHIP, EUNSUPPORTED = 0, -1, -2, -3, -4, -5, -6
-FMT_F16, FMT_CB2, FMT_Q2K, FMT_MXFP4 = 0, 1, 2, 3
-EXPERTS_CB2_Q2K, EXPERTS_MXFP4 = 0, 1
+FMT_F16, FMT_CB2, FMT_Q2K, FMT_MXFP4, FMT_Q4K = 0, 1, 2, 3, 4
+EXPERTS_CB2_Q2K, EXPERTS_MXFP4, EXPERTS_Q4K = 0, 1, 2
 DT_F32, DT_BF16 = 0, 1
 MODE_DECODE, MODE_PREFILL, MODE_ROUTE = 0, 1, 2
 DECODE_MAX_T = 64
@@ -190,7 +190,7 @@ class Layer:
     router_w, sh_gate, sh_up, sh_down: binary16 bit patterns (int16/uint16 or
     float16 CUDA tensors); gate/up/down: uint8 CUDA tensors of E packed
     matrices each; router_bias: float32 CUDA tensor or None; expert_fmt:
-    EXPERTS_CB2_Q2K or EXPERTS_MXFP4.
+    EXPERTS_CB2_Q2K, EXPERTS_MXFP4 or EXPERTS_Q4K.
     """
 
     def __init__(self, d, E, k, f, fs, router_w, router_bias, sh_gate, sh_up, sh_down, gate, up, down,

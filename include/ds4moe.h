@@ -77,6 +77,24 @@
  *   other scales round (binary16) or overflow.  The quantizer gives codes in
  *   that range for blocks whose largest |w| lies in [2^-21, 2^16).
  *
+ * Q4K (4.5 bits per weight; 144 bytes per 256 weights), Q4_K class: 8
+ * sub-blocks of 32 per super-block, 4-bit codes, 6-bit scale and min per
+ * sub-block, binary16 d and dmin.
+ *   code plane      rows*nb*128 bytes: sub-block j at bytes 16j..16j+15 of
+ *                   its block; LE u32 word k of a sub-block holds elements
+ *                   8k..8k+7, element 8k+2p at bits 4p..4p+3 and element
+ *                   8k+2p+1 at bits 16+4p..19+4p (p = 0..3).
+ *   scale plane     rows*nb*12 bytes at offset rows*nb*128: LE u32 w0, w1,
+ *                   w2; nibble j of w0 = s_j & 15, nibble j of w1 = m_j & 15,
+ *                   bits 2j..2j+1 of w2 = s_j >> 4, bits 16+2j..17+2j of w2 =
+ *                   m_j >> 4.
+ *   superscale      rows*nb pairs (binary16 d, binary16 dmin) at offset
+ *                   rows*nb*140.
+ *   Weight K = 256b + 32j + i = (d * s_j) * q - dmin * m_j, exact products,
+ *   one rounding.  The forward calls round each weight to binary16 with
+ *   the scales folded in: q * binary16(d * s_j) - binary16(dmin * m_j),
+ *   rounded once, so weights must stay within binary16 range.
+ *
  * F16 weights are plain row-major binary16 [rows, cols].
  */
 #ifndef DS4MOE_H
@@ -99,12 +117,14 @@ enum {
   DS4MOE_EUNSUPPORTED = -6  /* valid but not supported by this library */
 };
 
-enum { DS4MOE_FMT_F16 = 0, DS4MOE_FMT_CB2 = 1, DS4MOE_FMT_Q2K = 2, DS4MOE_FMT_MXFP4 = 3 };
+enum { DS4MOE_FMT_F16 = 0, DS4MOE_FMT_CB2 = 1, DS4MOE_FMT_Q2K = 2, DS4MOE_FMT_MXFP4 = 3, DS4MOE_FMT_Q4K = 4 };
 /* Formats of a layer's routed experts (ds4moe_layer.expert_fmt):
  * CB2_Q2K: gate/up CB2, down Q2K (the pages' 2-bit recipe);
  * MXFP4: gate, up and down all MXFP4 (the model's native expert format,
- * TopDigg "DwarfStar (ds4) Deep Dive" 5.2, download options). */
-enum { DS4MOE_EXPERTS_CB2_Q2K = 0, DS4MOE_EXPERTS_MXFP4 = 1 };
+ * TopDigg "DwarfStar (ds4) Deep Dive" 5.2, download options);
+ * Q4K: gate, up and down all Q4K (the Q4 layers of the q2-q4 mix, same
+ * section: the last six routed-expert layers at Q4). */
+enum { DS4MOE_EXPERTS_CB2_Q2K = 0, DS4MOE_EXPERTS_MXFP4 = 1, DS4MOE_EXPERTS_Q4K = 2 };
 enum { DS4MOE_DT_F32 = 0, DS4MOE_DT_BF16 = 1 };
 enum { DS4MOE_MODE_DECODE = 0, DS4MOE_MODE_PREFILL = 1, DS4MOE_MODE_ROUTE = 2 };
 
@@ -127,20 +147,20 @@ typedef struct {
   const uint16_t *sh_gate;     /* F16 [fs, d] */
   const uint16_t *sh_up;       /* F16 [fs, d] */
   const uint16_t *sh_down;     /* F16 [d, fs] */
-  const void *gate;            /* E packed [f, d] matrices (CB2, or MXFP4) */
-  const void *up;              /* E packed [f, d] matrices (CB2, or MXFP4) */
-  const void *down;            /* E packed [d, f] matrices (Q2K, or MXFP4) */
+  const void *gate;            /* E packed [f, d] matrices (CB2, MXFP4 or Q4K) */
+  const void *up;              /* E packed [f, d] matrices (CB2, MXFP4 or Q4K) */
+  const void *down;            /* E packed [d, f] matrices (Q2K, MXFP4 or Q4K) */
   int32_t expert_fmt;          /* DS4MOE_EXPERTS_*; 0 (CB2/Q2K) when the struct is zero-initialised */
 } ds4moe_layer;
 
 /* Bytes of one packed [rows, cols] matrix (host function; 0 if cols % 256 != 0
- * or fmt is unknown).  F16: rows*cols*2; CB2 66, Q2K 84, MXFP4 136 bytes per
- * 256 weights. */
+ * or fmt is unknown).  F16: rows*cols*2; CB2 66, Q2K 84, MXFP4 136, Q4K 144
+ * bytes per 256 weights. */
 size_t ds4moe_packed_bytes(int fmt, int64_t rows, int64_t cols);
 
 /* Quantize fp32 [rows, cols] (row-major, finite values) into the packed
  * matrix `packed` (ds4moe_packed_bytes bytes).  fmt: DS4MOE_FMT_CB2,
- * DS4MOE_FMT_Q2K or DS4MOE_FMT_MXFP4.  Deterministic: the bytes equal those
+ * DS4MOE_FMT_Q2K, DS4MOE_FMT_MXFP4 or DS4MOE_FMT_Q4K.  Deterministic: the bytes equal those
  * of the format's reference quantizer (steps in the library's
  * documentation). */
 int ds4moe_quantize(int fmt, const float *w, int64_t rows, int64_t cols, void *packed, void *stream);

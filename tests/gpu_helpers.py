@@ -47,7 +47,8 @@ class SeededLayer:
                  router: np.ndarray | None = None, expert_fmt: str = "cb2q2k"):
         """router: binary16 bits [E, d] to use instead of the seeded draw
         (edge-case tests build routers with repeated rows); expert_fmt:
-        "cb2q2k" (CB2 gate/up, Q2K down) or "mxfp4" (all three MXFP4)."""
+        "cb2q2k" (CB2 gate/up, Q2K down), "mxfp4" or "q4k" (all three in
+        that format)."""
         self.cfg = cfg
         self.seed = cfg.seed if cfg_seed is None else cfg_seed
         self.expert_fmt = expert_fmt
@@ -55,15 +56,13 @@ class SeededLayer:
         self.router = S.gen_router(cfg, cfg_seed=cfg_seed) if router is None else np.ascontiguousarray(router)
         self.bias = S.gen_bias(cfg)
         self.sh = S.gen_shared(cfg, cfg_seed=cfg_seed)
-        mx = expert_fmt == "mxfp4"
-        self.fmt_gu = D.FMT_MXFP4 if mx else D.FMT_CB2
-        self.fmt_dn = D.FMT_MXFP4 if mx else D.FMT_Q2K
+        fmts = {"cb2q2k": (D.FMT_CB2, D.FMT_Q2K, D.EXPERTS_CB2_Q2K, O.cb2_bytes, O.q2k_bytes),
+                "mxfp4": (D.FMT_MXFP4, D.FMT_MXFP4, D.EXPERTS_MXFP4, O.mx4_bytes, O.mx4_bytes),
+                "q4k": (D.FMT_Q4K, D.FMT_Q4K, D.EXPERTS_Q4K, O.q4k_bytes, O.q4k_bytes)}
+        self.fmt_gu, self.fmt_dn, efmt, obytes_gu, obytes_dn = fmts[expert_fmt]
         cb = D.packed_bytes(self.fmt_gu, c.f, c.d)
         qb = D.packed_bytes(self.fmt_dn, c.d, c.f)
-        if mx:
-            assert cb == O.mx4_bytes(c.f, c.d) and qb == O.mx4_bytes(c.d, c.f)
-        else:
-            assert cb == O.cb2_bytes(c.f, c.d) and qb == O.q2k_bytes(c.d, c.f)
+        assert cb == obytes_gu(c.f, c.d) and qb == obytes_dn(c.d, c.f)
         self.cb, self.qb = cb, qb
         self.gate = torch.empty(c.E * cb, dtype=torch.uint8, device="cuda")
         self.up = torch.empty(c.E * cb, dtype=torch.uint8, device="cuda")
@@ -87,8 +86,7 @@ class SeededLayer:
                 self.down[e * qb:(e + 1) * qb] = dev(dp)
         self.layer = D.Layer(c.d, c.E, c.k, c.f, c.fs, dev(self.router),
                              None if self.bias is None else dev(self.bias),
-                             dev(self.sh[0]), dev(self.sh[1]), dev(self.sh[2]), self.gate, self.up, self.down,
-                             D.EXPERTS_MXFP4 if mx else D.EXPERTS_CB2_Q2K)
+                             dev(self.sh[0]), dev(self.sh[1]), dev(self.sh[2]), self.gate, self.up, self.down, efmt)
         self.oracle = O.Layer(c.d, c.E, c.k, c.f, c.fs, self.router, self.bias, self.sh[0], self.sh[1], self.sh[2],
                               self.oracle_expert, expert_fmt=expert_fmt)
 
@@ -96,6 +94,8 @@ class SeededLayer:
         g, u, dn = S.gen_expert(self.cfg, e, cfg_seed=self.seed)
         if self.expert_fmt == "mxfp4":
             return O.mx4_quantize(g), O.mx4_quantize(u), O.mx4_quantize(dn)
+        if self.expert_fmt == "q4k":
+            return O.q4k_quantize(g), O.q4k_quantize(u), O.q4k_quantize(dn)
         return O.cb2_quantize(g), O.cb2_quantize(u), O.q2k_quantize(dn)
 
     def oracle_expert(self, e):

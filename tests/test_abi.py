@@ -35,6 +35,7 @@ def test_packed_sizes():
     assert D.packed_bytes(D.FMT_Q2K, 4096, 2048) == 4096 * 8 * 84 == 2752512
     assert D.packed_bytes(D.FMT_F16, 3, 5) == 30
     assert D.packed_bytes(D.FMT_MXFP4, 2048, 4096) == 2048 * 4096 * 17 // 32 == 4456448
+    assert D.packed_bytes(D.FMT_Q4K, 2048, 4096) == 2048 * 16 * 144 == 4718592
     assert D.packed_bytes(D.FMT_CB2, 4, 300) == 0
     assert D.packed_bytes(9, 4, 256) == 0
 
@@ -128,7 +129,7 @@ def test_codec_argument_errors():
     assert lib.ds4moe_quantize(D.FMT_F16, A, 4, 256, A, None) == D.EINVAL
     assert lib.ds4moe_quantize(D.FMT_CB2, A, 4, 300, A, None) == D.ESHAPE
     assert lib.ds4moe_quantize(D.FMT_MXFP4, A, 4, 288, A, None) == D.ESHAPE
-    assert lib.ds4moe_quantize(D.FMT_MXFP4 + 1, A, 4, 256, A, None) == D.EINVAL
+    assert lib.ds4moe_quantize(D.FMT_Q4K + 1, A, 4, 256, A, None) == D.EINVAL
     assert lib.ds4moe_quantize(D.FMT_CB2, A, -1, 256, A, None) == D.EINVAL
     assert lib.ds4moe_quantize(D.FMT_CB2, None, 4, 256, A, None) == D.EINVAL
     assert lib.ds4moe_quantize(D.FMT_Q2K, A + 4, 4, 256, A, None) == D.EALIGN

@@ -145,3 +145,45 @@ def test_mx4_full_size_expert_quantize_byte_exact():
     g, u, dn = S.gen_expert(cfg, 7)
     assert np.array_equal(gpu_quant(D.FMT_MXFP4, g), O.mx4_quantize(g))
     assert np.array_equal(gpu_quant(D.FMT_MXFP4, dn), O.mx4_quantize(dn))
+
+
+# ------------------------------------------------------------------ Q4K
+def test_q4k_quantize_byte_exact():
+    rng = np.random.default_rng(31)
+    for rows, cols, scale in ((1, 256, 0.02), (37, 512, 0.02), (16, 4096, 1.0), (8, 768, 3e4)):
+        w = (rng.standard_normal((rows, cols)) * scale).astype(np.float32)
+        assert np.array_equal(gpu_quant(D.FMT_Q4K, w), O.q4k_quantize(w)), (rows, cols, scale)
+
+
+def test_q4k_quantize_edge_blocks_byte_exact():
+    from tests.test_oracle_q4k import canonical_q4k
+    x = np.zeros((6, 256), dtype=np.float32)
+    x[1, 17] = 0.5                       # single spike
+    x[2, :] = 1e-9                       # d underflows
+    x[3, 5], x[3, 6] = 3e38, -3e38       # d clamps at 65504
+    x[4, :] = -0.01                      # all negative
+    x[5, ::2] = 0.03                     # exact ties
+    x[5, 1::2] = -0.03
+    assert np.array_equal(gpu_quant(D.FMT_Q4K, x), O.q4k_quantize(x))
+    cq = canonical_q4k(np.random.default_rng(9), 16)
+    w = O.q4k_dequantize(cq, 16, 256)
+    assert np.array_equal(gpu_quant(D.FMT_Q4K, w), cq)
+
+
+def test_q4k_dequantize_random_codes_bit_exact():
+    rng = np.random.default_rng(32)
+    rows, cols = 16, 512
+    n = rows * cols // 256
+    codes = rng.integers(0, 256, n * 128, dtype=np.uint8)
+    scl = rng.integers(0, 256, n * 12, dtype=np.uint8)
+    sup = (np.abs(rng.standard_normal(2 * n)) * 1e-3).astype(np.float16).view(np.uint16)
+    p = np.concatenate([codes, scl, sup.view(np.uint8)])
+    assert np.array_equal(gpu_dequant(D.FMT_Q4K, p, rows, cols).view(np.uint32),
+                          O.q4k_dequantize(p, rows, cols).view(np.uint32))
+
+
+def test_q4k_full_size_expert_quantize_byte_exact():
+    cfg = S.CONFIGS["decode1"]
+    g, u, dn = S.gen_expert(cfg, 7)
+    assert np.array_equal(gpu_quant(D.FMT_Q4K, g), O.q4k_quantize(g))
+    assert np.array_equal(gpu_quant(D.FMT_Q4K, dn), O.q4k_quantize(dn))

@@ -1,10 +1,10 @@
-"""GPU parity of layers whose routed experts are MXFP4 (gate, up and down;
-the model's native expert format) against the oracle: the tiny
-configuration with oracle-packed experts, and the full DeepSeek V4 Flash
-shapes with device-packed experts whose bytes are checked against the
-oracle's.  Bars as for the CB2/Q2K layers: indices, counts, offsets and
-permutation bit-exact, weights within 1e-5, layer outputs within 2e-3 per
-token row."""
+"""GPU parity of layers whose routed experts are MXFP4 (the model's native
+expert format) or Q4K (the Q4 layers of the q2-q4 mix), gate, up and down
+alike, against the oracle: the tiny configuration with oracle-packed
+experts, and the full DeepSeek V4 Flash shapes with device-packed experts
+whose bytes are checked against the oracle's.  Bars as for the CB2/Q2K
+layers: indices, counts, offsets and permutation bit-exact, weights within
+1e-5, layer outputs within 2e-3 per token row."""
 import numpy as np
 import pytest
 
@@ -17,10 +17,13 @@ pytestmark = pytest.mark.gpu
 TOL = 2e-3
 
 
-@pytest.fixture(scope="module")
-def tiny_mx():
-    print("[setup] tiny MXFP4 layer (oracle-packed)", flush=True)
-    return SeededLayer(S.CONFIGS["tiny"], device_quantize=False, expert_fmt="mxfp4")
+FORMATS = ["mxfp4", "q4k"]
+
+
+@pytest.fixture(scope="module", params=FORMATS)
+def tiny_mx(request):
+    print(f"[setup] tiny {request.param} layer (oracle-packed)", flush=True)
+    return SeededLayer(S.CONFIGS["tiny"], device_quantize=False, expert_fmt=request.param)
 
 
 @pytest.mark.parametrize("T", [1, 3, 8, 16, 17, 40])
@@ -30,7 +33,7 @@ def test_tiny_mx_decode(tiny_mx, T):
     got = tiny_mx.forward(x, D.MODE_DECODE)
     check_routing(got, ref, tiny_mx.cfg.k)
     err = rel_err_rows(got["y"], ref["y"])
-    print(f"tiny mxfp4 decode T={T} rel err {err:.3e}")
+    print(f"tiny {tiny_mx.expert_fmt} decode T={T} rel err {err:.3e}")
     assert err <= TOL
 
 
@@ -41,14 +44,14 @@ def test_tiny_mx_prefill(tiny_mx, T):
     got = tiny_mx.forward(x, D.MODE_PREFILL)
     check_routing(got, ref, tiny_mx.cfg.k)
     err = rel_err_rows(got["y"], ref["y"])
-    print(f"tiny mxfp4 prefill T={T} rel err {err:.3e}")
+    print(f"tiny {tiny_mx.expert_fmt} prefill T={T} rel err {err:.3e}")
     assert err <= TOL
 
 
-@pytest.fixture(scope="module")
-def decode1_mx():
-    print("[setup] decode1 MXFP4 layer (device-packed, 256 experts)", flush=True)
-    return SeededLayer(S.CONFIGS["decode1"], device_quantize=True, expert_fmt="mxfp4")
+@pytest.fixture(scope="module", params=FORMATS)
+def decode1_mx(request):
+    print(f"[setup] decode1 {request.param} layer (device-packed, 256 experts)", flush=True)
+    return SeededLayer(S.CONFIGS["decode1"], device_quantize=True, expert_fmt=request.param)
 
 
 @pytest.mark.parametrize("T", [1, 4])
@@ -64,16 +67,17 @@ def test_decode1_mx(decode1_mx, T):
     got = L.forward(x, D.MODE_DECODE)
     check_routing(got, ref, L.cfg.k)
     err = rel_err_rows(got["y"], ref["y"])
-    print(f"decode1 mxfp4 T={T} rel err {err:.3e}")
+    print(f"decode1 {L.expert_fmt} T={T} rel err {err:.3e}")
     assert err <= TOL
 
 
-def test_prefill_2048_mx_sampled():
-    """2048-token prefill of an MXFP4 layer with the Zipf-shaped loads:
-    routing for every token exact, sampled outputs (slots in all three tile
-    kinds) against the oracle."""
-    print("[setup] prefill MXFP4 layer (device-packed, Zipf bias)", flush=True)
-    L = SeededLayer(S.CONFIGS["prefill"], device_quantize=True, expert_fmt="mxfp4")
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_prefill_2048_mx_sampled(fmt):
+    """2048-token prefill with the Zipf-shaped loads: routing for every token
+    exact, sampled outputs (slots in all three tile kinds) against the
+    oracle."""
+    print(f"[setup] prefill {fmt} layer (device-packed, Zipf bias)", flush=True)
+    L = SeededLayer(S.CONFIGS["prefill"], device_quantize=True, expert_fmt=fmt)
     x = L.x()
     k, T = L.cfg.k, L.cfg.T
     r = L.oracle.route(x, L.cfg.x_dtype)
@@ -89,5 +93,5 @@ def test_prefill_2048_mx_sampled():
     check_routing(got, ref, k)
     check_used_experts_bytes(L, ref["idx"][sample])
     err = rel_err_rows(got["y"][sample], ref["y"])
-    print(f"prefill mxfp4 sampled rel err {err:.3e}")
+    print(f"prefill {fmt} sampled rel err {err:.3e}")
     assert err <= TOL
