@@ -26,10 +26,11 @@ shared expert, bf16 activations -- in layer-tokens per second.
   * "decode16" times the 16-token batched decode (about 60 distinct experts);
   * "decode_small" times speculative-verify shapes, T = 2, 4, 8 tokens per
     call at the decode1 layer shape;
-  * "mxfp4" times the decode1 shape and the 2048-token prefill with MXFP4
-    routed experts;
+  * "mxfp4" and "q4k" time the decode1 shape and the 2048-token prefill with
+    MXFP4 and with Q4K routed experts;
   * "stack43" times 43 decode1-shaped layers resident at once, one token at a
-    time through all of them;
+    time through all of them, first all CB2/Q2K, then as the q2-q4 mix (the
+    last six layers' experts Q4K);
   * "cpu_baseline" times the CPU oracle on a bounded sample of decode tokens,
     on all host threads and on one.
 """
@@ -85,15 +86,25 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def decode_bytes(cfg, n_distinct, T=1, mx=False):
+def expert_formats(efmt):
+    """(gate/up format, down format, layer expert_fmt, label) of a routed-expert
+    recipe: "cb2q2k" (CB2 gate/up, Q2K down), "mxfp4" or "q4k" (all three)."""
+    from bit_quantized_routed_router_amd import ds4moe as D
+    return {"cb2q2k": (D.FMT_CB2, D.FMT_Q2K, D.EXPERTS_CB2_Q2K, "CB2/Q2K"),
+            "mxfp4": (D.FMT_MXFP4, D.FMT_MXFP4, D.EXPERTS_MXFP4, "MXFP4"),
+            "q4k": (D.FMT_Q4K, D.FMT_Q4K, D.EXPERTS_Q4K, "Q4K")}[efmt]
+
+
+def decode_bytes(cfg, n_distinct, T=1, efmt="cb2q2k"):
     """Algorithmic HBM bytes of one decode step and of each of its kernels:
     every weight byte the step needs read once, activations read/written once.
     stage 1: router; stage 2: routed gate/up + shared gate and up; stage 3:
     routed down + shared down."""
     from bit_quantized_routed_router_amd import ds4moe as D
     d, f, fs, E, k = cfg.d, cfg.f, cfg.fs, cfg.E, cfg.k
-    cb = D.packed_bytes(D.FMT_MXFP4 if mx else D.FMT_CB2, f, d)
-    qb = D.packed_bytes(D.FMT_MXFP4 if mx else D.FMT_Q2K, d, f)
+    fgu, fdn = expert_formats(efmt)[:2]
+    cb = D.packed_bytes(fgu, f, d)
+    qb = D.packed_bytes(fdn, d, f)
     x_bytes = T * d * 2
     s1 = E * d * 2 + x_bytes
     s2 = n_distinct * 2 * cb + 2 * fs * d * 2 + T * d * 2 + T * k * f * 2 + T * fs * 2
@@ -102,7 +113,7 @@ def decode_bytes(cfg, n_distinct, T=1, mx=False):
     return dict(total=total, k_dec_stage1=s1, k_dec_stage2=s2, k_dec_stage3=s3)
 
 
-def make_layer(cfg, copies=1, cfg_seed=None, mx=False):
+def make_layer(cfg, copies=1, cfg_seed=None, efmt="cb2q2k"):
     import torch
     from bit_quantized_routed_router_amd import ds4moe as D
     from bit_quantized_routed_router_amd import synthetic as S
@@ -114,7 +125,7 @@ def make_layer(cfg, copies=1, cfg_seed=None, mx=False):
         return torch.from_numpy(a).cuda()
 
     c = cfg
-    fgu, fdn = (D.FMT_MXFP4, D.FMT_MXFP4) if mx else (D.FMT_CB2, D.FMT_Q2K)
+    fgu, fdn, ecode, label = expert_formats(efmt)
     cb = D.packed_bytes(fgu, c.f, c.d)
     qb = D.packed_bytes(fdn, c.d, c.f)
     gate = torch.empty(c.E * cb, dtype=torch.uint8, device="cuda")
@@ -128,18 +139,16 @@ def make_layer(cfg, copies=1, cfg_seed=None, mx=False):
             D.quantize(fgu, dev(u), c.f, c.d, up[e * cb:(e + 1) * cb])
             D.quantize(fdn, dev(dn), c.d, c.f, down[e * qb:(e + 1) * qb])
         torch.cuda.synchronize()
-    log(f"[bench] {c.name}: generated and quantized {c.E} {'MXFP4' if mx else 'CB2/Q2K'} experts "
-        f"in {time.time() - t0:.1f}s")
-    efmt = D.EXPERTS_MXFP4 if mx else D.EXPERTS_CB2_Q2K
+    log(f"[bench] {c.name}: generated and quantized {c.E} {label} experts in {time.time() - t0:.1f}s")
     router = dev(S.gen_router(c, cfg_seed=cfg_seed))
     bias = S.gen_bias(c)
     bias = None if bias is None else dev(bias)
     sh = [dev(a) for a in S.gen_shared(c, cfg_seed=cfg_seed)]
-    layers = [D.Layer(c.d, c.E, c.k, c.f, c.fs, router, bias, sh[0], sh[1], sh[2], gate, up, down, efmt)]
+    layers = [D.Layer(c.d, c.E, c.k, c.f, c.fs, router, bias, sh[0], sh[1], sh[2], gate, up, down, ecode)]
     for _ in range(1, copies):
         layers.append(D.Layer(c.d, c.E, c.k, c.f, c.fs, router.clone(), None if bias is None else bias.clone(),
                               sh[0].clone(), sh[1].clone(), sh[2].clone(), gate.clone(), up.clone(), down.clone(),
-                              efmt))
+                              ecode))
     torch.cuda.synchronize()
     return layers
 
@@ -251,7 +260,7 @@ def bench_decode(args):
     return res
 
 
-def decode_batch(cfg, layers, T, steps, warmup, xvar0, mx=False):
+def decode_batch(cfg, layers, T, steps, warmup, xvar0, efmt="cb2q2k"):
     """K graph-replayed T-token decode steps over the given layer copies (round
     robin) with fresh tokens per step.  Returns us/step, tok/s, the mean
     distinct-expert count and the whole-layer HBM fraction from the
@@ -293,7 +302,7 @@ def decode_batch(cfg, layers, T, steps, warmup, xvar0, mx=False):
     ms = e0.elapsed_time(e1) / steps
     sel = idx[warmup:].cpu().numpy()
     distinct = [len(np.unique(sel[n])) for n in range(steps)]
-    nbytes = float(np.mean([decode_bytes(cfg, nd, T=T, mx=mx)["total"] for nd in distinct]))
+    nbytes = float(np.mean([decode_bytes(cfg, nd, T=T, efmt=efmt)["total"] for nd in distinct]))
     del g
     return dict(tok_s=T / (ms * 1e-3), us_per_step=ms * 1e3, distinct_mean=float(np.mean(distinct)),
                 bytes_per_step=nbytes, hbm_frac=nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS)
@@ -333,28 +342,29 @@ def bench_decode_small(copies=4, steps=64, warmup=8, Ts=(2, 4, 8)):
                          "round-robin, graph replay", **out)
 
 
-def bench_mxfp4(steps=64, warmup=8, copies=4):
+def bench_wide(efmt, steps=64, warmup=8, copies=4):
     """Side report: a layer whose routed experts are MXFP4 (the model's native
-    expert format), decode at T = 1 over layer copies with graph replay."""
+    expert format) or Q4K (the Q4 layers of the q2-q4 mix), decode at T = 1
+    over layer copies with graph replay."""
     import torch
     from bit_quantized_routed_router_amd import synthetic as S
 
     cfg = S.CONFIGS["decode1"]
-    layers = make_layer(cfg, copies=copies, mx=True)
-    r = decode_batch(cfg, layers, 1, steps, warmup, 4000, mx=True)
+    layers = make_layer(cfg, copies=copies, efmt=efmt)
+    r = decode_batch(cfg, layers, 1, steps, warmup, 4000, efmt=efmt)
     del layers
     torch.cuda.empty_cache()
-    return dict(workload=f"decode1 shape with MXFP4 routed experts (gate, up, down), T=1, {copies} layer copies "
-                         "round-robin, graph replay", **r)
+    return dict(workload=f"decode1 shape with {expert_formats(efmt)[3]} routed experts (gate, up, down), T=1, "
+                         f"{copies} layer copies round-robin, graph replay", **r)
 
 
-def bench_prefill(args, mx=False):
+def bench_prefill(args, efmt="cb2q2k"):
     import torch
     from bit_quantized_routed_router_amd import ds4moe as D
     from bit_quantized_routed_router_amd import synthetic as S
 
     cfg = S.CONFIGS["prefill"]
-    L = make_layer(cfg, mx=mx)[0]
+    L = make_layer(cfg, efmt=efmt)[0]
     x = torch.from_numpy(S.gen_x(cfg).view(np.int16)).cuda()
     T = cfg.T
     y = torch.empty((T, cfg.d), dtype=torch.float32, device="cuda")
@@ -381,16 +391,18 @@ def bench_prefill(args, mx=False):
     tflops = flop / (ms * 1e-3) / 1e12
     del L
     torch.cuda.empty_cache()
-    return dict(workload=f"prefill T={T}, Zipf(1.1)-shaped expert loads" + (", MXFP4 routed experts" if mx else ""),
+    return dict(workload=f"prefill T={T}, Zipf(1.1)-shaped expert loads, {expert_formats(efmt)[3]} routed experts",
                 tok_s=T / (ms * 1e-3), ms=ms, runs_ms=runs,
                 flop=flop, tflops=tflops, mfma_frac=tflops / MFMA_F16_PEAK_TFLOPS,
                 kernels={k: dict(mean_us=v[0] / v[1] * 1e3, launches=v[1]) for k, v in kern.items() if v[1] > 0})
 
 
-def bench_stack43(nlayers=43, tokens=256, warmup=16, repeats=3):
+def bench_stack43(nlayers=43, tokens=256, warmup=16, repeats=3, n_q4=6):
     """The 43-layer stack of decode1-shaped layers, every layer's packed
     experts resident in HBM at once (about 80 GB), one token at a time
-    through all layers (T = 1 per call).
+    through all layers (T = 1 per call).  Timed twice: all layers CB2/Q2K,
+    then as the q2-q4 mix, the last `n_q4` layers' experts re-packed as Q4K
+    from the same fp32 draws.
 
     Weights: layer l draws its fp32 weights N(0, 0.02) on the device from
     torch's generator seeded 1000 + l and packs them with ds4moe_quantize
@@ -404,15 +416,14 @@ def bench_stack43(nlayers=43, tokens=256, warmup=16, repeats=3):
     from bit_quantized_routed_router_amd import synthetic as S
 
     c = S.CONFIGS["stack43"]
-    cb = D.packed_bytes(D.FMT_CB2, c.f, c.d)
-    qb = D.packed_bytes(D.FMT_Q2K, c.d, c.f)
-    t0 = time.time()
-    layers, resident = [], 0
     gen = torch.Generator(device="cuda")
-    for l in range(nlayers):
+
+    def pack_layer(l, efmt):
+        fgu, fdn, ecode, _ = expert_formats(efmt)
         gen.manual_seed(1000 + l)
         packed = []
-        for fmt, rows, cols, nb in ((D.FMT_CB2, c.f, c.d, cb), (D.FMT_CB2, c.f, c.d, cb), (D.FMT_Q2K, c.d, c.f, qb)):
+        for fmt, rows, cols in ((fgu, c.f, c.d), (fgu, c.f, c.d), (fdn, c.d, c.f)):
+            nb = D.packed_bytes(fmt, rows, cols)
             w = torch.randn((c.E, rows * cols), generator=gen, device="cuda", dtype=torch.float32).mul_(WEIGHT_SIGMA)
             buf = torch.empty(c.E * nb, dtype=torch.uint8, device="cuda")
             for e in range(c.E):
@@ -421,8 +432,15 @@ def bench_stack43(nlayers=43, tokens=256, warmup=16, repeats=3):
             packed.append(buf)
         f16 = [torch.randn(n, generator=gen, device="cuda").mul_(WEIGHT_SIGMA).half()
                for n in (c.E * c.d, c.fs * c.d, c.fs * c.d, c.d * c.fs)]
-        layers.append(D.Layer(c.d, c.E, c.k, c.f, c.fs, f16[0], None, f16[1], f16[2], f16[3], *packed))
-        resident += sum(t.numel() * t.element_size() for t in packed + f16)
+        L = D.Layer(c.d, c.E, c.k, c.f, c.fs, f16[0], None, f16[1], f16[2], f16[3], *packed, ecode)
+        return L, sum(t.numel() * t.element_size() for t in packed + f16)
+
+    t0 = time.time()
+    layers, sizes, recipe = [], [], ["cb2q2k"] * nlayers
+    for l in range(nlayers):
+        L, nbytes = pack_layer(l, "cb2q2k")
+        layers.append(L)
+        sizes.append(nbytes)
         if l % 8 == 7:
             torch.cuda.synchronize()
             log(f"[bench] stack43: {l + 1} layers packed, {time.time() - t0:.1f}s")
@@ -452,32 +470,43 @@ def bench_stack43(nlayers=43, tokens=256, warmup=16, repeats=3):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1)
 
-    with torch.cuda.stream(s):
-        run(0, warmup, s)
-    eager_runs = [timed(lambda: run(warmup, nsteps, s)) for _ in range(repeats)]
-    y_eager = y.clone()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g, stream=s):
-        run(warmup, nsteps, torch.cuda.current_stream())
+    def measure(name):
+        with torch.cuda.stream(s):
+            run(0, warmup, s)
+        eager_runs = [timed(lambda: run(warmup, nsteps, s)) for _ in range(repeats)]
+        y_eager = y.clone()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            run(warmup, nsteps, torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        if not torch.equal(y, y_eager):
+            raise RuntimeError(f"stack43 {name}: graph replay differs from the eager run")
+        graph_runs = [timed(g.replay) for _ in range(repeats)]
+        del g, y_eager
+        ms = float(np.median(graph_runs)) / tokens
+        eager_ms = float(np.median(eager_runs)) / tokens
+        sel = idx[:, warmup:].cpu().numpy()
+        distinct = float(np.mean([len(np.unique(sel[l, n])) for l in range(nlayers) for n in range(tokens)]))
+        per_token = sum(decode_bytes(c, c.k, T=1, efmt=r)["total"] for r in recipe)
+        return dict(recipe=name, tok_s=1.0 / (ms * 1e-3), us_per_token=ms * 1e3, eager_us_per_token=eager_ms * 1e3,
+                    bytes_per_token=per_token, hbm_frac=per_token / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                    resident_bytes=sum(sizes), distinct_per_layer=distinct)
+
+    q2 = measure("q2 (all layers CB2/Q2K)")
+    for l in range(nlayers - n_q4, nlayers):  # the q2-q4 mix: the last layers' experts at Q4K
+        layers[l] = None
+        torch.cuda.empty_cache()
+        layers[l], sizes[l] = pack_layer(l, "q4k")
+        recipe[l] = "q4k"
     torch.cuda.synchronize()
-    g.replay()
-    torch.cuda.synchronize()
-    if not torch.equal(y, y_eager):
-        raise RuntimeError("stack43: graph replay differs from the eager run")
-    graph_runs = [timed(g.replay) for _ in range(repeats)]
-    ms = float(np.median(graph_runs)) / tokens
-    eager_ms = float(np.median(eager_runs)) / tokens
-    sel = idx[:, warmup:].cpu().numpy()
-    distinct = float(np.mean([len(np.unique(sel[l, n])) for l in range(nlayers) for n in range(tokens)]))
-    per_token = nlayers * decode_bytes(c, c.k, T=1)["total"]
-    del g, layers, x, y, y_eager
+    mix = measure(f"q2-q4 (last {n_q4} layers Q4K)")
+    del layers, x, y
     torch.cuda.empty_cache()
-    return dict(workload=f"stack43: {nlayers} decode1-shaped layers resident, {tokens} tokens x {nlayers} layers, "
-                         "T=1 per call, teacher-forced seeded inputs, graph replay (median of "
-                         f"{repeats})",
-                tok_s=1.0 / (ms * 1e-3), us_per_token=ms * 1e3, eager_us_per_token=eager_ms * 1e3,
-                bytes_per_token=per_token, hbm_frac=per_token / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                resident_bytes=resident, distinct_per_layer=distinct, pack_s=pack_s)
+    return dict(q2, workload=f"stack43: {nlayers} decode1-shaped layers resident, {tokens} tokens x {nlayers} "
+                             f"layers, T=1 per call, teacher-forced seeded inputs, graph replay (median of "
+                             f"{repeats})", pack_s=pack_s, q2q4=mix)
 
 
 def measure_copy_gbs(nbytes=1 << 30, reps=5):
@@ -594,7 +623,7 @@ def main():
     ap.add_argument("--no-decode-small", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-stack", action="store_true", help="skip the 43-layer stack leg (about 80 GB resident)")
-    ap.add_argument("--no-mxfp4", action="store_true", help="skip the MXFP4-expert side reports")
+    ap.add_argument("--no-wide", action="store_true", help="skip the MXFP4- and Q4K-expert side reports")
     ap.add_argument("--stack-tokens", type=int, default=256)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     args = ap.parse_args()
@@ -622,18 +651,22 @@ def main():
     pre = None if args.no_prefill else bench_prefill(args)
     if pre:
         log(f"[bench] prefill: {pre['ms']:.3f} ms, {pre['tok_s']:.0f} tok/s, {pre['tflops']:.1f} TFLOP/s")
-    mxd = None if args.no_mxfp4 else bench_mxfp4()
-    if mxd:
-        log(f"[bench] mxfp4 decode: {mxd['us_per_step']:.1f} us/step, {mxd['tok_s']:.0f} tok/s, "
-            f"{100 * mxd['hbm_frac']:.1f} % of HBM peak")
-    mxp = None if args.no_mxfp4 or args.no_prefill else bench_prefill(args, mx=True)
-    if mxp:
-        log(f"[bench] mxfp4 prefill: {mxp['ms']:.3f} ms, {mxp['tok_s']:.0f} tok/s, {mxp['tflops']:.1f} TFLOP/s")
+    wide = {}
+    for efmt in () if args.no_wide else ("mxfp4", "q4k"):
+        wd = bench_wide(efmt)
+        log(f"[bench] {efmt} decode: {wd['us_per_step']:.1f} us/step, {wd['tok_s']:.0f} tok/s, "
+            f"{100 * wd['hbm_frac']:.1f} % of HBM peak")
+        wp = None if args.no_prefill else bench_prefill(args, efmt=efmt)
+        if wp:
+            log(f"[bench] {efmt} prefill: {wp['ms']:.3f} ms, {wp['tok_s']:.0f} tok/s, {wp['tflops']:.1f} TFLOP/s")
+        wide[efmt] = dict(decode=wd, prefill=None if wp is None else dict(
+            {k: wp[k] for k in ("workload", "tok_s", "ms", "tflops", "mfma_frac")},
+            kernels_us={k: round(v["mean_us"], 2) for k, v in wp["kernels"].items()}))
     stk = None if args.no_stack else bench_stack43(tokens=args.stack_tokens)
     if stk:
-        log(f"[bench] stack43: {stk['us_per_token']:.1f} us/token, {stk['tok_s']:.0f} tok/s, "
-            f"{100 * stk['hbm_frac']:.1f} % of HBM peak, {stk['resident_bytes'] / 1e9:.1f} GB resident "
-            f"(packed in {stk['pack_s']:.0f}s)")
+        for r in (stk, stk["q2q4"]):
+            log(f"[bench] stack43 {r['recipe']}: {r['us_per_token']:.1f} us/token, {r['tok_s']:.0f} tok/s, "
+                f"{100 * r['hbm_frac']:.1f} % of HBM peak, {r['resident_bytes'] / 1e9:.1f} GB resident")
     copy_gbs = measure_copy_gbs()
     gemm_tflops = measure_gemm_tflops()
     log(f"[bench] measured: device copy {copy_gbs:.0f} GB/s, fp16 library GEMM {gemm_tflops:.0f} TFLOP/s")
@@ -676,10 +709,8 @@ def main():
             frac_of_measured_gemm=pre["tflops"] / gemm_tflops,
             kernels_us={k: round(v["mean_us"], 2) for k, v in pre["kernels"].items()}),
         "stack43": stk,
-        "mxfp4": None if mxd is None else dict(
-            decode=mxd, prefill=None if mxp is None else dict(
-                {k: mxp[k] for k in ("workload", "tok_s", "ms", "tflops", "mfma_frac")},
-                kernels_us={k: round(v["mean_us"], 2) for k, v in mxp["kernels"].items()})),
+        "mxfp4": wide.get("mxfp4"),
+        "q4k": wide.get("q4k"),
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
