@@ -15,6 +15,13 @@ Deep Dive", section 5.4):
   prefill   as decode1, T 2048, bias -1.1*beta*ln(rank) (Zipf-like loads)
   stack43   43 layers of the decode1 shape, per-layer seeds 1000 + layer
 
+Hyper-connection mixer inputs (the n = 4 streams of d around each layer, DS4
+(DwarfStar 4) wiki note, "Key Techniques"), gen_hc: streams X [T, 4, d] fp32
+N(0, 1) with stream i scaled by 2^(i - 1); projection phi [24, 4d] fp32
+N(0, 1/128^2), so each mixer logit has unit spread at d = 4096; bias [24]:
+pre/post N(0, 1), residual mixer 4 I + N(0, 0.5^2) (a near-identity mixer);
+alpha = (1, 1, 1).  Streams 10..13 of the layer seed.
+
 Every tensor comes from numpy PCG64(SeedSequence([cfg_seed, stream, variant])):
 stream 0 = x, 1 = router, 2/3/4 = shared gate/up/down, 5 = bias / pool,
 100 + 3*e + m = routed expert e, matrix m (0 gate, 1 up, 2 down).  Draws are
@@ -32,6 +39,10 @@ import numpy as np
 WEIGHT_SIGMA = 0.02
 
 STREAM_X, STREAM_ROUTER, STREAM_SH_GATE, STREAM_SH_UP, STREAM_SH_DOWN, STREAM_BIAS = 0, 1, 2, 3, 4, 5
+STREAM_HC_X, STREAM_HC_PHI, STREAM_HC_BIAS, STREAM_HC_Y = 10, 11, 12, 13
+HC_STREAMS = 4
+HC_SINKHORN_ITERS = 20
+HC_EPS = 1e-6
 
 
 def expert_stream(e: int, m: int) -> int:
@@ -185,3 +196,19 @@ def rank_frequency_slope(counts: np.ndarray) -> float:
 
 
 __all__ = [n for n in dir() if not n.startswith("_") and n not in ("annotations", "dataclasses", "math", "np")]
+
+
+def gen_hc(d: int, T: int, cfg_seed: int = 7, variant: int = 0):
+    """Hyper-connection mixer inputs: streams X [T, 4, d], projection phi
+    [24, 4d], bias [24], alpha (3,), sublayer output y [T, d]; float32."""
+    n = HC_STREAMS
+    no = 2 * n + n * n
+    X = normal_f32(rng(cfg_seed, STREAM_HC_X, variant), (T, n, d), 1.0)
+    X *= np.array([0.5, 1.0, 2.0, 4.0], dtype=np.float32)[None, :, None]
+    phi = normal_f32(rng(cfg_seed, STREAM_HC_PHI), (no, n * d), 1.0 / 128.0)
+    g = rng(cfg_seed, STREAM_HC_BIAS)
+    bias = normal_f32(g, (no,), 1.0)
+    bias[2 * n:] = normal_f32(g, (n * n,), 0.5) + 4.0 * np.eye(n, dtype=np.float32).ravel()
+    alpha = np.ones(3, dtype=np.float32)
+    y = normal_f32(rng(cfg_seed, STREAM_HC_Y, variant), (T, d), 1.0)
+    return X, phi, bias, alpha, y

@@ -868,6 +868,109 @@ void orc_swiglu(const double *g, const double *u, int64_t n, double *h)
 }
 
 /* ------------------------------------------------------------------------- */
+/* Hyper-connection mixer around the layer (DS4 (DwarfStar 4) wiki note, "Key */
+/* Techniques": activations travel as n = 4 streams of d = 4096, a learned    */
+/* mixer normalised by 20 Sinkhorn iterations reduces them to one row for the */
+/* sublayer and expands the sublayer's output back into n streams).          */
+/* Readings where the note is silent, after the manifold-constrained          */
+/* hyper-connection formulation that pairs a Sinkhorn-normalised residual     */
+/* mixer with per-stream reduce and expand weights:                           */
+/*   X [n][d] per token, flattened as k = i*d + c;                            */
+/*   x' = X / sqrt(mean_k X_k^2 + eps)      (RMS over all n*d values)          */
+/*   z_o = alpha_g * sum_k phi[o][k] x'_k + bias[o],  o < 2n + n*n, with      */
+/*         g = pre for o < n, post for n <= o < 2n, res otherwise             */
+/*   pre_i  = sigmoid(z_i)                  (reduce weights)                  */
+/*   post_i = 2 sigmoid(z_{n+i})            (expand weights)                  */
+/*   M = Sinkhorn(exp(Z)), Z[i][j] = z_{2n + n*i + j}; one iteration divides   */
+/*       every row by its sum, then every column by its sum                   */
+/*   reduce:  x_in[c]   = sum_i pre_i X[i][c]                                 */
+/*   expand:  X'[i][c]  = sum_j M[i][j] X[j][c] + post_i y[c]                 */
+/* ------------------------------------------------------------------------- */
+
+/* A[n][n] <- `iters` Sinkhorn iterations applied to exp(Z). */
+void orc_sinkhorn(const double *Z, int n, int iters, double *A)
+{
+    for (int q = 0; q < n * n; q++)
+        A[q] = exp(Z[q]);
+    for (int it = 0; it < iters; it++) {
+        for (int i = 0; i < n; i++) {
+            double s = 0.0;
+            for (int j = 0; j < n; j++)
+                s += A[i * n + j];
+            for (int j = 0; j < n; j++)
+                A[i * n + j] /= s;
+        }
+        for (int j = 0; j < n; j++) {
+            double s = 0.0;
+            for (int i = 0; i < n; i++)
+                s += A[i * n + j];
+            for (int i = 0; i < n; i++)
+                A[i * n + j] /= s;
+        }
+    }
+}
+
+/* X [T][n][d]; phi [2n+n*n][n*d]; bias [2n+n*n]; alpha {pre, post, res}.
+ * coef [T][2n+n*n] = pre (n), post (n), M (n*n, row-major); xin [T][d]. */
+void orc_hc_pre(const double *X, int64_t T, int n, int64_t d, const double *phi, const double *bias,
+                const double *alpha, double eps, int iters, double *coef, double *xin)
+{
+    const int no = 2 * n + n * n;
+    const int64_t nd = (int64_t)n * d;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; t++) {
+        const double *x = X + t * nd;
+        double ss = 0.0;
+        for (int64_t k = 0; k < nd; k++)
+            ss += x[k] * x[k];
+        const double r = sqrt(ss / (double)nd + eps);
+        double *xn = (double *)malloc(sizeof(double) * (size_t)nd);
+        for (int64_t k = 0; k < nd; k++)
+            xn[k] = x[k] / r;
+        double *z = (double *)malloc(sizeof(double) * (size_t)no);
+        for (int o = 0; o < no; o++) {
+            double acc = 0.0;
+            for (int64_t k = 0; k < nd; k++)
+                acc += phi[(int64_t)o * nd + k] * xn[k];
+            const double a = o < n ? alpha[0] : (o < 2 * n ? alpha[1] : alpha[2]);
+            z[o] = a * acc + bias[o];
+        }
+        double *cf = coef + t * no;
+        for (int i = 0; i < n; i++) {
+            cf[i] = 1.0 / (1.0 + exp(-z[i]));
+            cf[n + i] = 2.0 / (1.0 + exp(-z[n + i]));
+        }
+        orc_sinkhorn(z + 2 * n, n, iters, cf + 2 * n);
+        for (int64_t c = 0; c < d; c++) {
+            double acc = 0.0;
+            for (int i = 0; i < n; i++)
+                acc += cf[i] * x[(int64_t)i * d + c];
+            xin[t * d + c] = acc;
+        }
+        free(z);
+        free(xn);
+    }
+}
+
+/* Xout [T][n][d] = M X + post y, with coef as orc_hc_pre writes it. */
+void orc_hc_post(const double *X, const double *y, const double *coef, int64_t T, int n, int64_t d, double *Xout)
+{
+    const int no = 2 * n + n * n;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; t++) {
+        const double *cf = coef + t * no;
+        const double *M = cf + 2 * n;
+        for (int i = 0; i < n; i++)
+            for (int64_t c = 0; c < d; c++) {
+                double acc = 0.0;
+                for (int j = 0; j < n; j++)
+                    acc += M[i * n + j] * X[(t * n + j) * d + c];
+                Xout[(t * n + i) * d + c] = acc + cf[n + i] * y[t * d + c];
+            }
+    }
+}
+
+/* ------------------------------------------------------------------------- */
 /* Threads of the parallel loops (independent output rows only, so results   */
 /* do not depend on the count).                                              */
 /* ------------------------------------------------------------------------- */

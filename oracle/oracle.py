@@ -78,6 +78,9 @@ def lib():
         L.orc_mx4_matmul.argtypes = [P, P, I64, I64, P, I64, P]
         L.orc_q4k_dequantize.argtypes = [P, P, P, I64, I64, P]
         L.orc_q4k_quantize.argtypes = [P, I64, I64, P, P, P]
+        L.orc_sinkhorn.argtypes = [P, ctypes.c_int, ctypes.c_int, P]
+        L.orc_hc_pre.argtypes = [P, I64, ctypes.c_int, I64, P, P, P, ctypes.c_double, ctypes.c_int, P, P]
+        L.orc_hc_post.argtypes = [P, P, P, I64, ctypes.c_int, I64, P]
         L.orc_q4k_matmul.argtypes = [P, P, P, I64, I64, P, I64, P]
         L.orc_set_threads.argtypes = [ctypes.c_int]
         L.orc_max_threads.restype = ctypes.c_int
@@ -312,6 +315,46 @@ def swiglu(g: np.ndarray, u: np.ndarray) -> np.ndarray:
 
 
 # ---------------------------------------------------------------- routing
+# ---------------------------------------------------------------- HC mixer
+def sinkhorn(Z: np.ndarray, iters: int) -> np.ndarray:
+    """exp(Z) for an [n, n] Z after `iters` Sinkhorn iterations (rows, then
+    columns, each divided by its sum)."""
+    Z = np.ascontiguousarray(Z, dtype=np.float64)
+    n = Z.shape[0]
+    A = np.empty((n, n), dtype=np.float64)
+    lib().orc_sinkhorn(_p(Z), n, iters, _p(A))
+    return A
+
+
+def hc_pre(X: np.ndarray, phi: np.ndarray, bias: np.ndarray, alpha, eps: float, iters: int):
+    """Coefficients and reduced rows of the hyper-connection mixer.
+    X [T, n, d]; phi [2n + n*n, n*d]; bias [2n + n*n]; alpha (pre, post, res).
+    Returns coef [T, 2n + n*n] (pre, post, M row-major) and x_in [T, d]."""
+    X = np.ascontiguousarray(X, dtype=np.float64)
+    T, n, d = X.shape
+    no = 2 * n + n * n
+    phi = np.ascontiguousarray(phi, dtype=np.float64)
+    bias = np.ascontiguousarray(bias, dtype=np.float64)
+    assert phi.shape == (no, n * d) and bias.shape == (no,)
+    a = np.ascontiguousarray(alpha, dtype=np.float64)
+    coef = np.empty((T, no), dtype=np.float64)
+    xin = np.empty((T, d), dtype=np.float64)
+    lib().orc_hc_pre(_p(X), T, n, d, _p(phi), _p(bias), _p(a), float(eps), iters, _p(coef), _p(xin))
+    return coef, xin
+
+
+def hc_post(X: np.ndarray, y: np.ndarray, coef: np.ndarray) -> np.ndarray:
+    """Expanded streams X' [T, n, d] = M X + post y per token."""
+    X = np.ascontiguousarray(X, dtype=np.float64)
+    T, n, d = X.shape
+    y = np.ascontiguousarray(y, dtype=np.float64)
+    coef = np.ascontiguousarray(coef, dtype=np.float64)
+    assert y.shape == (T, d) and coef.shape == (T, 2 * n + n * n)
+    out = np.empty_like(X)
+    lib().orc_hc_post(_p(X), _p(y), _p(coef), T, n, d, _p(out))
+    return out
+
+
 def x_to_f64(x: np.ndarray, x_dtype: str) -> np.ndarray:
     """Activations to fp64, exactly: float32 values or bfloat16 bits."""
     if x_dtype == "f32":
