@@ -32,6 +32,7 @@ SOURCES = {
     "route.hip": [],
     "decode.hip": [],
     "prefill.hip": [],
+    "hc.hip": [],
     "capi.cpp": ["-x", "hip"],
     "trace.cpp": ["-x", "hip"],
 }

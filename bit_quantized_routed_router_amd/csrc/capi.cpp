@@ -1,5 +1,6 @@
 // C ABI of the ds4moe library: argument validation, workspace layout and
 // dispatch.  Nothing is enqueued unless every check passes.
+#include <cmath>
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -288,6 +289,47 @@ int ds4moe_forward_prefill(const ds4moe_layer* L, const void* x, int x_dtype, in
   hipError_t e = launch_route(f, false);
   if (e == hipSuccess) e = launch_prefill_experts(f);
   return hip_status(e);
+}
+
+// ---------------------------------------------------------------- hyper-connection mixer
+static int check_hc(const ds4moe_hc* H) {
+  if (!H || !H->phi || !H->bias) return DS4MOE_EINVAL;
+  if (H->n_streams < 1) return DS4MOE_EINVAL;
+  if (H->n_streams != 4) return DS4MOE_EUNSUPPORTED;
+  if (!dim_ok(H->d_model)) return DS4MOE_ESHAPE;
+  if (H->sinkhorn_iters < 1 || H->sinkhorn_iters > 64) return DS4MOE_EINVAL;
+  if (!(H->eps >= 0.0f) || !std::isfinite(H->eps) || !std::isfinite(H->alpha_pre) || !std::isfinite(H->alpha_post) ||
+      !std::isfinite(H->alpha_res))
+    return DS4MOE_EINVAL;
+  if (!al16(H->phi) || ((uintptr_t)H->bias & 3)) return DS4MOE_EALIGN;
+  return DS4MOE_OK;
+}
+
+size_t ds4moe_hc_workspace_bytes(const ds4moe_hc* H, int64_t T) {
+  if (check_hc(H) != DS4MOE_OK || T < 1 || T > kHcMaxT) return 0;
+  return hc_ws_bytes(H->d_model, T);
+}
+
+int ds4moe_hc_pre(const ds4moe_hc* H, const float* X, int64_t T, float* coef, float* x_out, uint16_t* x_bf16,
+                  void* ws, size_t ws_bytes, void* stream) {
+  const int st = check_hc(H);
+  if (st != DS4MOE_OK) return st;
+  if (!X || !coef || !ws) return DS4MOE_EINVAL;
+  if (T < 1 || T > kHcMaxT) return DS4MOE_ESHAPE;
+  if (!al16(X) || !al16(coef) || (x_out && !al16(x_out)) || ((uintptr_t)x_bf16 & 7) || ((uintptr_t)ws & 255))
+    return DS4MOE_EALIGN;
+  if (ws_bytes < hc_ws_bytes(H->d_model, T)) return DS4MOE_EWORKSPACE;
+  return hip_status(launch_hc_pre(*H, X, T, coef, x_out, x_bf16, ws, (hipStream_t)stream));
+}
+
+int ds4moe_hc_post(const ds4moe_hc* H, const float* X, const float* y, const float* coef, int64_t T, float* X_out,
+                   void* stream) {
+  const int st = check_hc(H);
+  if (st != DS4MOE_OK) return st;
+  if (!X || !y || !coef || !X_out) return DS4MOE_EINVAL;
+  if (T < 1 || T > kHcMaxT) return DS4MOE_ESHAPE;
+  if (!al16(X) || !al16(y) || !al16(coef) || !al16(X_out)) return DS4MOE_EALIGN;
+  return hip_status(launch_hc_post(*H, X, y, coef, T, X_out, (hipStream_t)stream));
 }
 
 const char* ds4moe_strerror(int status) {

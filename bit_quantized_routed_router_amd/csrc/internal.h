@@ -78,4 +78,12 @@ hipError_t launch_route(const Fwd& f, bool decode);
 hipError_t launch_decode(const Fwd& f);  // full layer for one group of <= 16 tokens
 hipError_t launch_prefill_experts(const Fwd& f);
 
+// hyper-connection mixer (ds4moe_hc); hc_ws_bytes: workspace of hc_pre
+constexpr int64_t kHcMaxT = 1 << 20;
+size_t hc_ws_bytes(int d, int64_t T);
+hipError_t launch_hc_pre(const ds4moe_hc& H, const float* X, int64_t T, float* coef, float* xout, uint16_t* xbf,
+                         void* ws, hipStream_t st);
+hipError_t launch_hc_post(const ds4moe_hc& H, const float* X, const float* y, const float* coef, int64_t T,
+                          float* Xo, hipStream_t st);
+
 }  // namespace ds4

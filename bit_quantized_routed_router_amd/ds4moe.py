@@ -40,6 +40,15 @@ class LayerDesc(ctypes.Structure):
     ]
 
 
+class HcDesc(ctypes.Structure):
+    """Mirror of ds4moe_hc."""
+    _fields_ = [
+        ("n_streams", ctypes.c_int32), ("d_model", ctypes.c_int32), ("sinkhorn_iters", ctypes.c_int32),
+        ("eps", ctypes.c_float), ("alpha_pre", ctypes.c_float), ("alpha_post", ctypes.c_float),
+        ("alpha_res", ctypes.c_float), ("phi", ctypes.c_void_p), ("bias", ctypes.c_void_p),
+    ]
+
+
 _lib = None
 
 
@@ -70,6 +79,13 @@ def lib() -> ctypes.CDLL:
         L.ds4moe_forward_decode_static.argtypes = [LP, P, I32, I64, P, P, P, P]
         L.ds4moe_forward_prefill.restype = I32
         L.ds4moe_forward_prefill.argtypes = [LP, P, I32, I64, P, P, P, P, P, SZ, P]
+        HP = ctypes.POINTER(HcDesc)
+        L.ds4moe_hc_workspace_bytes.restype = SZ
+        L.ds4moe_hc_workspace_bytes.argtypes = [HP, I64]
+        L.ds4moe_hc_pre.restype = I32
+        L.ds4moe_hc_pre.argtypes = [HP, P, I64, P, P, P, P, SZ, P]
+        L.ds4moe_hc_post.restype = I32
+        L.ds4moe_hc_post.argtypes = [HP, P, P, P, I64, P, P]
         L.ds4moe_strerror.restype = ctypes.c_char_p
         L.ds4moe_strerror.argtypes = [I32]
         L.ds4moe_trace_enable.restype = I32
@@ -85,7 +101,8 @@ def lib() -> ctypes.CDLL:
 EXPORTS = ["ds4moe_packed_bytes", "ds4moe_quantize", "ds4moe_dequantize", "ds4moe_workspace_bytes",
            "ds4moe_workspace_init",
            "ds4moe_route", "ds4moe_forward_decode", "ds4moe_forward_decode_static", "ds4moe_forward_prefill", "ds4moe_strerror",
-           "ds4moe_grid_levels", "ds4moe_trace_enable", "ds4moe_trace_read"]
+           "ds4moe_grid_levels", "ds4moe_trace_enable", "ds4moe_trace_read",
+           "ds4moe_hc_workspace_bytes", "ds4moe_hc_pre", "ds4moe_hc_post"]
 
 
 def strerror(status: int) -> str:
@@ -157,6 +174,38 @@ def forward_prefill(desc, x, x_dtype, T, y, topk_idx_out, topk_w_out, perm_out, 
     _check(lib().ds4moe_forward_prefill(ctypes.byref(desc), _ptr(x), x_dtype, T, _ptr(y), _ptr(topk_idx_out),
                                         _ptr(topk_w_out), _ptr(perm_out), _ptr(ws), ws_bytes, _stream(stream)),
            "ds4moe_forward_prefill")
+
+
+def hc_workspace_bytes(desc: HcDesc, T: int) -> int:
+    return int(lib().ds4moe_hc_workspace_bytes(ctypes.byref(desc), T))
+
+
+def hc_pre(desc, X, T, coef, x_out, x_bf16, ws, ws_bytes, stream=None) -> None:
+    _check(lib().ds4moe_hc_pre(ctypes.byref(desc), _ptr(X), T, _ptr(coef), _ptr(x_out), _ptr(x_bf16), _ptr(ws),
+                               ws_bytes, _stream(stream)), "ds4moe_hc_pre")
+
+
+def hc_post(desc, X, y, coef, T, X_out, stream=None) -> None:
+    _check(lib().ds4moe_hc_post(ctypes.byref(desc), _ptr(X), _ptr(y), _ptr(coef), T, _ptr(X_out), _stream(stream)),
+           "ds4moe_hc_post")
+
+
+class Hc:
+    """Device tensors of one hyper-connection mixer plus its ds4moe_hc
+    descriptor: phi float32 [2n + n*n, n*d], bias float32 [2n + n*n] (CUDA
+    tensors), alpha (pre, post, res)."""
+
+    def __init__(self, d, phi, bias, alpha, eps=1e-6, iters=20, n=4):
+        self.tensors = dict(phi=phi, bias=bias)
+        self.d, self.n = d, n
+        a = [float(v) for v in alpha]
+        self.desc = HcDesc(n, d, iters, float(eps), a[0], a[1], a[2], _ptr(phi), _ptr(bias))
+
+    def workspace(self, T: int):
+        n = hc_workspace_bytes(self.desc, T)
+        if n == 0:
+            raise Ds4moeError(ESHAPE, "ds4moe_hc_workspace_bytes")
+        return torch.empty(n, dtype=torch.uint8, device="cuda"), n
 
 
 def trace_enable(on: bool) -> None:

@@ -230,6 +230,60 @@ int ds4moe_forward_prefill(const ds4moe_layer *L, const void *x, int x_dtype, in
                            int32_t *topk_idx_out, float *topk_w_out, int32_t *perm_out, void *ws,
                            size_t ws_bytes, void *stream);
 
+/* ----------------------------------------------------------------------
+ * Hyper-connection mixer on either side of the layer (DS4 (DwarfStar 4)
+ * wiki note, "Key Techniques", hyper-connections with Sinkhorn
+ * normalization: the activations travel as n = 4 streams of d values; a
+ * learned mixer normalised by Sinkhorn iterations reduces them to the one
+ * row the sublayer consumes and expands its output back into n streams).
+ * The note gives no formulas; this library takes the manifold-constrained
+ * hyper-connection reading (per token t, streams X[n][d] flattened as
+ * k = i*d + c):
+ *   r      = sqrt(sum_k X_k^2 / (n d) + eps)
+ *   z_o    = alpha_g * (sum_k phi[o][k] X_k) / r + bias[o], o < 2n + n*n;
+ *            g = pre (o < n), post (o < 2n), res (otherwise)
+ *   pre_i  = 1 / (1 + e^-z_i),  post_i = 2 / (1 + e^-z_{n+i})
+ *   M      = sinkhorn_iters Sinkhorn iterations on exp(Z), Z[i][j] =
+ *            z_{2n+n*i+j}; one iteration divides every row by its sum, then
+ *            every column by its sum (the GPU subtracts each row's maximum
+ *            before exp, which the first row step cancels)
+ *   x_in   = sum_i pre_i X[i]                      (ds4moe_hc_pre)
+ *   X'[i]  = sum_j M[i][j] X[j] + post_i y          (ds4moe_hc_post)
+ * Everything is fp32 (binary32 inputs, fp32 accumulation).
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  int32_t n_streams;      /* n; this library runs n = 4 (else DS4MOE_EUNSUPPORTED) */
+  int32_t d_model;        /* d: multiple of 256, <= 16384 */
+  int32_t sinkhorn_iters; /* 1..64 (the note: 20) */
+  float eps;              /* RMS epsilon, finite, >= 0 */
+  float alpha_pre, alpha_post, alpha_res;
+  const float *phi;       /* fp32 [2n + n*n][n*d] row-major, 16-byte aligned */
+  const float *bias;      /* fp32 [2n + n*n], 4-byte aligned */
+} ds4moe_hc;
+
+/* Workspace bytes ds4moe_hc_pre needs for T tokens (0 on invalid input). */
+size_t ds4moe_hc_workspace_bytes(const ds4moe_hc *H, int64_t T);
+
+/* Coefficients and reduced rows of T tokens (1 <= T <= 1048576).
+ *   X      fp32 [T][n][d], 16-byte aligned (read only)
+ *   coef   fp32 [T][2n + n*n] out: pre (n), post (n), M row-major (n*n);
+ *          16-byte aligned
+ *   x_out  fp32 [T][d] out, or NULL; 16-byte aligned
+ *   x_bf16 bfloat16 bits [T][d] out (x_out rounded to nearest-even, the
+ *          layer's bf16 input), or NULL; 8-byte aligned
+ *   ws     device workspace of at least ds4moe_hc_workspace_bytes (no
+ *          state kept between calls; 256-byte aligned)
+ * Asynchronous on `stream`; nothing is enqueued on a non-zero return. */
+int ds4moe_hc_pre(const ds4moe_hc *H, const float *X, int64_t T, float *coef, float *x_out, uint16_t *x_bf16,
+                  void *ws, size_t ws_bytes, void *stream);
+
+/* Expanded streams X_out [T][n][d] = M X + post y per token, with coef as
+ * ds4moe_hc_pre wrote it and y fp32 [T][d] the sublayer's output (the
+ * layer's y).  X_out may equal X (in place); no other overlap.  All
+ * pointers 16-byte aligned.  Asynchronous on `stream`. */
+int ds4moe_hc_post(const ds4moe_hc *H, const float *X, const float *y, const float *coef, int64_t T,
+                   float *X_out, void *stream);
+
 /* Opt-in per-kernel timing (profiling aid).  While enabled, every kernel
  * the library launches is bracketed by two HIP events on its stream, which
  * adds a little launch overhead.  Thread-safe. */

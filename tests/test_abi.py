@@ -153,3 +153,59 @@ def test_binding_fails_loudly_without_library(monkeypatch):
     monkeypatch.setattr(D, "_LIB_PATH", "/nonexistent/libds4moe.so")
     with pytest.raises(RuntimeError):
         D.lib()
+
+
+def hc_desc(**kw):
+    v = dict(n_streams=4, d_model=4096, sinkhorn_iters=20, eps=1e-6, alpha_pre=1.0, alpha_post=1.0, alpha_res=1.0,
+             phi=A, bias=A)
+    v.update(kw)
+    return D.HcDesc(**v)
+
+
+def test_hc_workspace_sizes():
+    lib = D.lib()
+    # 16-token tiles, K-slices of 256 inputs (T <= 64) or 1024, 32 floats per (slice, token)
+    assert lib.ds4moe_hc_workspace_bytes(ctypes.byref(hc_desc()), 1) == 64 * 1 * 128
+    assert lib.ds4moe_hc_workspace_bytes(ctypes.byref(hc_desc()), 64) == 64 * 64 * 128
+    assert lib.ds4moe_hc_workspace_bytes(ctypes.byref(hc_desc()), 2048) == 16 * 2048 * 128
+    assert lib.ds4moe_hc_workspace_bytes(ctypes.byref(hc_desc()), 0) == 0
+    assert lib.ds4moe_hc_workspace_bytes(ctypes.byref(hc_desc()), (1 << 20) + 1) == 0
+    assert lib.ds4moe_hc_workspace_bytes(ctypes.byref(hc_desc(n_streams=2)), 1) == 0
+    assert lib.ds4moe_hc_workspace_bytes(None, 1) == 0
+
+
+def test_hc_argument_errors():
+    lib = D.lib()
+    big = 1 << 30
+    pre = lambda h, X=A, T=1, coef=A, xo=A, xb=A, ws=A, n=big: lib.ds4moe_hc_pre(  # noqa: E731
+        ctypes.byref(h), X, T, coef, xo, xb, ws, n, None)
+    post = lambda h, X=A, y=A, coef=A, T=1, Xo=A: lib.ds4moe_hc_post(ctypes.byref(h), X, y, coef, T, Xo, None)  # noqa: E731
+    h = hc_desc()
+    assert pre(hc_desc(phi=None)) == D.EINVAL
+    assert pre(hc_desc(bias=None)) == D.EINVAL
+    assert pre(hc_desc(n_streams=0)) == D.EINVAL
+    assert pre(hc_desc(n_streams=3)) == D.EUNSUPPORTED
+    assert pre(hc_desc(d_model=300)) == D.ESHAPE
+    assert pre(hc_desc(d_model=32768)) == D.ESHAPE
+    assert pre(hc_desc(sinkhorn_iters=0)) == D.EINVAL
+    assert pre(hc_desc(sinkhorn_iters=65)) == D.EINVAL
+    assert pre(hc_desc(eps=-1.0)) == D.EINVAL
+    assert pre(hc_desc(eps=float("nan"))) == D.EINVAL
+    assert pre(hc_desc(alpha_res=float("inf"))) == D.EINVAL
+    assert pre(hc_desc(phi=A + 4)) == D.EALIGN
+    assert pre(hc_desc(bias=A + 2)) == D.EALIGN
+    assert pre(h, X=None) == D.EINVAL
+    assert pre(h, coef=None) == D.EINVAL
+    assert pre(h, ws=None) == D.EINVAL
+    assert pre(h, T=0) == D.ESHAPE
+    assert pre(h, T=(1 << 20) + 1) == D.ESHAPE
+    assert pre(h, X=A + 4) == D.EALIGN
+    assert pre(h, xo=A + 8) == D.EALIGN
+    assert pre(h, xb=A + 4) == D.EALIGN
+    assert pre(h, ws=A + 16) == D.EALIGN
+    assert pre(h, n=64 * 128 - 1) == D.EWORKSPACE
+    assert post(hc_desc(n_streams=5)) == D.EUNSUPPORTED
+    assert post(h, y=None) == D.EINVAL
+    assert post(h, Xo=None) == D.EINVAL
+    assert post(h, T=0) == D.ESHAPE
+    assert post(h, coef=A + 4) == D.EALIGN
