@@ -28,6 +28,8 @@ shared expert, bf16 activations -- in layer-tokens per second.
     call at the decode1 layer shape;
   * "mxfp4" and "q4k" time the decode1 shape and the 2048-token prefill with
     MXFP4 and with Q4K routed experts;
+  * "hc" times the hyper-connection mixer (4 streams of 4096, 20 Sinkhorn
+    iterations) around the layer at T = 1 and T = 2048;
   * "stack43" times 43 decode1-shaped layers resident at once, one token at a
     time through all of them, first all CB2/Q2K, then as the q2-q4 mix (the
     last six layers' experts Q4K);
@@ -509,6 +511,151 @@ def bench_stack43(nlayers=43, tokens=256, warmup=16, repeats=3, n_q4=6):
                              f"{repeats})", pack_s=pack_s, q2q4=mix)
 
 
+def hc_bytes(d, T, n=4):
+    """Bytes each mixer kernel moves by design, and the step's algorithmic
+    bytes (streams read once): pre reads the projection and the streams,
+    writes the coefficients, the fp32 and the bf16 reduced rows; post reads
+    the streams, y and the coefficients and writes the streams."""
+    no, nd = 2 * n + n * n, n * d
+    ks = 1024 if T > 64 else 256
+    part = (nd // ks) * T * 32 * 4
+    x = T * nd * 4
+    outs = T * (no * 4 + d * 4 + d * 2)
+    if T <= 2:  # one launch: the partial kernel's last block also finishes the tokens
+        partial = no * nd * 4 + 2 * x + 2 * part + outs
+    else:
+        partial = no * nd * 4 + x + part
+    return dict(k_hc_partial=partial, k_hc_reduce=x + part + outs,
+                k_hc_post=2 * x + T * (d * 4 + no * 4),
+                pre_algorithmic=no * nd * 4 + x + outs, post_algorithmic=2 * x + T * (d * 4 + no * 4))
+
+
+def bench_hc(repeats=5, copies=192, steps=192):
+    """Side report: the hyper-connection mixer around the layer (4 streams of
+    4096, 20 Sinkhorn iterations).  Decode: T = 1, `copies` mixers (distinct
+    projections, 1.5 MB each, more than the 256 MB Infinity Cache holds)
+    round-robin with fresh streams per step, pre + post captured in one graph;
+    prefill: T = 2048, pre and post timed by events (median of `repeats`).
+    Per-kernel times come from the library's dispatch-attached events."""
+    import torch
+    from bit_quantized_routed_router_amd import ds4moe as D
+    from bit_quantized_routed_router_amd import synthetic as S
+
+    d = 4096
+    out = {}
+    # decode
+    X, phi, bias, alpha, y = S.gen_hc(d, steps)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(77)
+    phis = torch.randn((copies, 24, 4 * d), generator=gen, device="cuda").mul_(1.0 / 128.0)
+    bias_d = torch.from_numpy(bias).cuda()
+    mixers = [D.Hc(d, phis[i], bias_d, alpha, S.HC_EPS, S.HC_SINKHORN_ITERS) for i in range(copies)]
+    Xd = torch.from_numpy(X).cuda()
+    yd = torch.from_numpy(y).cuda()
+    Xo = torch.empty_like(Xd)
+    coef = torch.empty((steps, 24), dtype=torch.float32, device="cuda")
+    xo = torch.empty((steps, d), dtype=torch.float32, device="cuda")
+    xb = torch.empty((steps, d), dtype=torch.int16, device="cuda")
+    ws, wsn = mixers[0].workspace(1)
+
+    def step(i, stream):
+        H = mixers[i % copies].desc
+        D.hc_pre(H, Xd[i], 1, coef[i], xo[i], xb[i], ws, wsn, stream=stream)
+        D.hc_post(H, Xd[i], yd[i], coef[i], 1, Xo[i], stream=stream)
+
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        for i in range(steps):
+            step(i, s)
+    torch.cuda.synchronize()
+    D.trace_read(reset=True)
+    D.trace_enable(True)
+    with torch.cuda.stream(s):
+        for i in range(steps):
+            step(i, s)
+    torch.cuda.synchronize()
+    D.trace_enable(False)
+    kern = D.trace_read(reset=True)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for i in range(steps):
+            step(i, torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    runs = []
+    for _ in range(repeats):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        with torch.cuda.stream(s):
+            g.replay()
+        e1.record(s)
+        torch.cuda.synchronize()
+        runs.append(e0.elapsed_time(e1) / steps)
+    del g
+    b = hc_bytes(d, 1)
+    ku = {k: v[0] / v[1] * 1e3 for k, v in kern.items() if v[1] > 0}
+    out["decode"] = dict(workload=f"T=1, {copies} mixers round-robin, pre + post per step, graph replay (median of "
+                                  f"{repeats})", us_per_step=float(np.median(runs)) * 1e3,
+                         kernels_us={k: round(v, 2) for k, v in ku.items()},
+                         kernel_gbs={k: round(b[k.split("<")[0]] / (ku[k] * 1e-6) / 1e9, 1) for k in ku
+                                     if k.split("<")[0] in b})
+    del phis, mixers, Xd, yd, Xo, coef, xo, xb
+    torch.cuda.empty_cache()
+    # prefill
+    T = 2048
+    X, phi, bias, alpha, y = S.gen_hc(d, T)
+    H = D.Hc(d, torch.from_numpy(phi).cuda(), torch.from_numpy(bias).cuda(), alpha, S.HC_EPS, S.HC_SINKHORN_ITERS)
+    Xd = torch.from_numpy(X).cuda()
+    yd = torch.from_numpy(y).cuda()
+    Xo = torch.empty_like(Xd)
+    coef = torch.empty((T, 24), dtype=torch.float32, device="cuda")
+    xo = torch.empty((T, d), dtype=torch.float32, device="cuda")
+    xb = torch.empty((T, d), dtype=torch.int16, device="cuda")
+    ws, wsn = H.workspace(T)
+
+    def pre():
+        D.hc_pre(H.desc, Xd, T, coef, xo, xb, ws, wsn)
+
+    def post():
+        D.hc_post(H.desc, Xd, yd, coef, T, Xo)
+
+    res = {}
+    for name, fn in (("pre", pre), ("post", post)):
+        fn()
+        torch.cuda.synchronize()
+        r = []
+        for _ in range(repeats):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            r.append(e0.elapsed_time(e1))
+        res[name] = float(np.median(r))
+    D.trace_read(reset=True)
+    D.trace_enable(True)
+    pre()
+    post()
+    torch.cuda.synchronize()
+    D.trace_enable(False)
+    kern = D.trace_read(reset=True)
+    b = hc_bytes(d, T)
+    ku = {k: v[0] / v[1] * 1e3 for k, v in kern.items() if v[1] > 0}
+    out["prefill"] = dict(workload=f"T={T}, one mixer, pre and post timed by events (median of {repeats})",
+                          pre_us=res["pre"] * 1e3, post_us=res["post"] * 1e3,
+                          pre_hbm_frac=b["pre_algorithmic"] / (res["pre"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                          post_hbm_frac=b["post_algorithmic"] / (res["post"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                          kernels_us={k: round(v, 2) for k, v in ku.items()},
+                          kernel_gbs={k: round(b[k.split("<")[0]] / (ku[k] * 1e-6) / 1e9, 1) for k in ku
+                                      if k.split("<")[0] in b})
+    out["bytes_T1"] = hc_bytes(d, 1)
+    out["bytes_T2048"] = b
+    del Xd, yd, Xo, coef, xo, xb, H
+    torch.cuda.empty_cache()
+    return out
+
+
 def measure_copy_gbs(nbytes=1 << 30, reps=5):
     """Device-to-device copy rate of a plain torch copy (bytes read + written
     per second), median of reps: the HBM figure measured beside the vendor
@@ -624,6 +771,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-stack", action="store_true", help="skip the 43-layer stack leg (about 80 GB resident)")
     ap.add_argument("--no-wide", action="store_true", help="skip the MXFP4- and Q4K-expert side reports")
+    ap.add_argument("--no-hc", action="store_true", help="skip the hyper-connection mixer side report")
     ap.add_argument("--stack-tokens", type=int, default=256)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     args = ap.parse_args()
@@ -662,6 +810,12 @@ def main():
         wide[efmt] = dict(decode=wd, prefill=None if wp is None else dict(
             {k: wp[k] for k in ("workload", "tok_s", "ms", "tflops", "mfma_frac")},
             kernels_us={k: round(v["mean_us"], 2) for k, v in wp["kernels"].items()}))
+    hc = None if args.no_hc else bench_hc()
+    if hc:
+        log(f"[bench] hc decode: {hc['decode']['us_per_step']:.1f} us/step (pre + post), kernels "
+            f"{hc['decode']['kernels_us']}; prefill pre {hc['prefill']['pre_us']:.1f} us "
+            f"({100 * hc['prefill']['pre_hbm_frac']:.1f} % HBM), post {hc['prefill']['post_us']:.1f} us "
+            f"({100 * hc['prefill']['post_hbm_frac']:.1f} % HBM), kernels {hc['prefill']['kernel_gbs']} GB/s")
     stk = None if args.no_stack else bench_stack43(tokens=args.stack_tokens)
     if stk:
         for r in (stk, stk["q2q4"]):
@@ -711,6 +865,7 @@ def main():
         "stack43": stk,
         "mxfp4": wide.get("mxfp4"),
         "q4k": wide.get("q4k"),
+        "hc": hc,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

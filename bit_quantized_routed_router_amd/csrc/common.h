@@ -268,6 +268,24 @@ __device__ inline void pin() { __builtin_amdgcn_sched_barrier(0); }
 // space): it is counted apart from vector loads, so waiting for it does not
 // wait for the wave's vector loads or copies into LDS.  Only for data that no
 // block of the running kernel writes.
+// Coherent (device-scope) loads of data another block wrote in the same
+// kernel, after observing its release.
+__device__ inline int ld_acq_int(const int32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline float ld_coh(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline void fence_release() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
+__device__ inline void fence_acquire() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
+// Write-through (device-coherent) store for data handed to another block of
+// the same kernel; a writer waits for its coherent stores to complete
+// (wait_stores) before the counter that publishes them is incremented, so no
+// L2 write-back is needed.
+__device__ inline void st_coh(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline void wait_stores() { __builtin_amdgcn_s_waitcnt(0); }
 __device__ inline int ld_uniform(const int32_t* p) { return *(const __attribute__((address_space(4))) int32_t*)p; }
 
 __device__ inline float silu(float g) { return g / (1.0f + __expf(-g)); }

@@ -361,22 +361,5 @@ inline RouteOut route_out(const Fwd& f) {
   return o;
 }
 
-// Coherent (device-scope) loads of data another block wrote in the same
-// kernel, after observing its release.
-__device__ inline int ld_acq_int(const int32_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ inline float ld_coh(const float* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ inline void fence_release() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
-// Write-through (device-coherent) store for data handed to another block of
-// the same kernel; a writer waits for its coherent stores to complete
-// (wait_stores) before the counter that publishes them is incremented, so no
-// L2 write-back is needed.
-__device__ inline void st_coh(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ inline void wait_stores() { __builtin_amdgcn_s_waitcnt(0); }
 
 }  // namespace ds4

@@ -205,7 +205,9 @@ class Hc:
         n = hc_workspace_bytes(self.desc, T)
         if n == 0:
             raise Ds4moeError(ESHAPE, "ds4moe_hc_workspace_bytes")
-        return torch.empty(n, dtype=torch.uint8, device="cuda"), n
+        ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+        workspace_init(ws, n)
+        return ws, n
 
 
 def trace_enable(on: bool) -> None:

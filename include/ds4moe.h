@@ -271,8 +271,12 @@ size_t ds4moe_hc_workspace_bytes(const ds4moe_hc *H, int64_t T);
  *   x_out  fp32 [T][d] out, or NULL; 16-byte aligned
  *   x_bf16 bfloat16 bits [T][d] out (x_out rounded to nearest-even, the
  *          layer's bf16 input), or NULL; 8-byte aligned
- *   ws     device workspace of at least ds4moe_hc_workspace_bytes (no
- *          state kept between calls; 256-byte aligned)
+ *   ws     device workspace of at least ds4moe_hc_workspace_bytes,
+ *          256-byte aligned, zeroed once before its first use
+ *          (ds4moe_workspace_init); every call leaves its arrival counter
+ *          at zero again.  Calls that share a workspace must not overlap.
+ * For T <= 2 the whole step is one kernel launch (the last block to finish
+ * its partial projection completes the tokens), otherwise two.
  * Asynchronous on `stream`; nothing is enqueued on a non-zero return. */
 int ds4moe_hc_pre(const ds4moe_hc *H, const float *X, int64_t T, float *coef, float *x_out, uint16_t *x_bf16,
                   void *ws, size_t ws_bytes, void *stream);

@@ -164,10 +164,11 @@ def hc_desc(**kw):
 
 def test_hc_workspace_sizes():
     lib = D.lib()
-    # 16-token tiles, K-slices of 256 inputs (T <= 64) or 1024, 32 floats per (slice, token)
-    assert lib.ds4moe_hc_workspace_bytes(ctypes.byref(hc_desc()), 1) == 64 * 1 * 128
-    assert lib.ds4moe_hc_workspace_bytes(ctypes.byref(hc_desc()), 64) == 64 * 64 * 128
-    assert lib.ds4moe_hc_workspace_bytes(ctypes.byref(hc_desc()), 2048) == 16 * 2048 * 128
+    # K-slices of 256 inputs (T <= 64) or 1024, 32 floats per (slice, token), then a 256-byte counter
+    assert lib.ds4moe_hc_workspace_bytes(ctypes.byref(hc_desc()), 1) == 64 * 1 * 128 + 256
+    assert lib.ds4moe_hc_workspace_bytes(ctypes.byref(hc_desc()), 64) == 64 * 64 * 128 + 256
+    assert lib.ds4moe_hc_workspace_bytes(ctypes.byref(hc_desc()), 2048) == 16 * 2048 * 128 + 256
+    assert lib.ds4moe_hc_workspace_bytes(ctypes.byref(hc_desc(d_model=256)), 65) == 8448 + 256  # 65 * 128 rounded up
     assert lib.ds4moe_hc_workspace_bytes(ctypes.byref(hc_desc()), 0) == 0
     assert lib.ds4moe_hc_workspace_bytes(ctypes.byref(hc_desc()), (1 << 20) + 1) == 0
     assert lib.ds4moe_hc_workspace_bytes(ctypes.byref(hc_desc(n_streams=2)), 1) == 0
@@ -203,7 +204,7 @@ def test_hc_argument_errors():
     assert pre(h, xo=A + 8) == D.EALIGN
     assert pre(h, xb=A + 4) == D.EALIGN
     assert pre(h, ws=A + 16) == D.EALIGN
-    assert pre(h, n=64 * 128 - 1) == D.EWORKSPACE
+    assert pre(h, n=64 * 128 + 255) == D.EWORKSPACE
     assert post(hc_desc(n_streams=5)) == D.EUNSUPPORTED
     assert post(h, y=None) == D.EINVAL
     assert post(h, Xo=None) == D.EINVAL
