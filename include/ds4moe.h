@@ -26,8 +26,19 @@
  * the caller provides a workspace of ds4moe_workspace_bytes() bytes (256-byte
  * aligned) for each call; calls that share a workspace must be ordered on one
  * stream.  A workspace must be all zero before its first forward call
- * (ds4moe_workspace_init); every call leaves it ready for the next one.  The codebook grid is a compile-time table; the only mutable
- * global state is the opt-in kernel timer (ds4moe_trace_enable).
+ * (ds4moe_workspace_init); every call leaves it ready for the next one.
+ * The codebook grid is a compile-time table; the only mutable global state
+ * is the opt-in kernel timer (ds4moe_trace_enable).
+ *
+ * Numeric range.  The forward calls carry activations in binary16: x (bf16
+ * as one binary16 value, fp32 as a binary16 hi + lo pair) and the SwiGLU
+ * rows h = silu(gate x) * up x of the routed and the shared experts.  So
+ * |x| and every |h| must stay below 65504: larger values become infinities
+ * and the outputs non-finite (nothing checks this).  Below 2^-14 they keep
+ * less precision (binary16 subnormals) and below 2^-25 they become zero.
+ * Inputs that have been RMS-normalised, as the layer's
+ * input is in the model, keep x and h of order one.  Products accumulate
+ * in fp32 and y is fp32.
  *
  * ---------------------------------------------------------------- formats
  * A matrix W [rows, cols] is quantized along cols (the input dimension) in
@@ -162,7 +173,11 @@ size_t ds4moe_packed_bytes(int fmt, int64_t rows, int64_t cols);
  * matrix `packed` (ds4moe_packed_bytes bytes).  fmt: DS4MOE_FMT_CB2,
  * DS4MOE_FMT_Q2K, DS4MOE_FMT_MXFP4 or DS4MOE_FMT_Q4K.  Deterministic: the bytes equal those
  * of the format's reference quantizer (steps in the library's
- * documentation). */
+ * documentation).
+ * Passage: DS4 (DwarfStar 4) wiki note, "Key Techniques" (only the routed
+ * experts are quantized: gate/up IQ2_XXS, down Q2_K); TopDigg "DwarfStar
+ * (ds4) Deep Dive" 3.4 "Asymmetric Quantization"; 5.2 for the MXFP4 and
+ * Q4 expert downloads. */
 int ds4moe_quantize(int fmt, const float *w, int64_t rows, int64_t cols, void *packed, void *stream);
 
 /* Decode a packed matrix to fp32 [rows, cols] (bit-exact). */
@@ -184,6 +199,8 @@ size_t ds4moe_workspace_bytes(const ds4moe_layer *L, int64_t T, int mode);
 int ds4moe_workspace_init(void *ws, size_t ws_bytes, void *stream);
 
 /* Router + top-k + gate weights + token grouping for T tokens.
+ * Passage: DS4 (DwarfStar 4) wiki note, "Architecture" (256 routed experts,
+ * 6 active per token) and "Key Techniques" (the router stays F16).
  * x: [T, d] fp32 or bf16 (x_dtype).  Outputs: topk_idx [T, k] int32 (ascending
  * expert index per token), topk_w [T, k] fp32 (softmax of the selected
  * logits), counts [E], offsets [E+1] (exclusive scan of counts), perm [T*k]
@@ -195,7 +212,10 @@ int ds4moe_route(const ds4moe_layer *L, const void *x, int x_dtype, int64_t T, i
 
 /* Full layer for 1 <= T <= DS4MOE_DECODE_MAX_T tokens (batched decode).
  * y: [T, d] fp32.  topk_idx_out / topk_w_out: optional [T, k] copies of the
- * routing (NULL = not written). */
+ * routing (NULL = not written).
+ * Passage: DS4 (DwarfStar 4) wiki note, "Architecture" (6 routed + 1 shared
+ * expert per token); the batch bound covers TopDigg "DwarfStar (ds4) Deep
+ * Dive" 5.4's 16 batched sessions and its speculative-verify batches. */
 int ds4moe_forward_decode(const ds4moe_layer *L, const void *x, int x_dtype, int64_t T, float *y,
                           int32_t *topk_idx_out, float *topk_w_out, void *ws, size_t ws_bytes,
                           void *stream);
@@ -220,7 +240,9 @@ int ds4moe_forward_decode(const ds4moe_layer *L, const void *x, int x_dtype, int
 int ds4moe_forward_decode_static(const ds4moe_layer *L, const void *x, int x_dtype, int64_t T, float *y,
                                  int32_t *topk_idx_out, float *topk_w_out, void *stream);
 
-/* Full layer for 1 <= T <= 524280 tokens (prefill chunk; grouped GEMMs),
+/* Passage: DS4 (DwarfStar 4) wiki note, "Architecture" (prefill runs in
+ * chunks, 2048 tokens by default).
+ * Full layer for 1 <= T <= 524280 tokens (prefill chunk; grouped GEMMs),
  * with T * d_model < 2^31 and T * k * d_ff < 2^31 (DS4MOE_ESHAPE otherwise).
  * Same outputs as ds4moe_forward_decode plus the optional permutation
  * perm_out [T*k].  The routed products round each dequantized weight to

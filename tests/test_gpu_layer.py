@@ -56,6 +56,21 @@ def test_tiny_forward(tiny, mode):
     assert err <= TOL
 
 
+@pytest.mark.parametrize("mode", [D.MODE_DECODE, D.MODE_PREFILL])
+def test_tiny_large_activations_within_binary16(tiny, mode):
+    """x scaled by 64 (|x| in the hundreds, SwiGLU rows in the thousands):
+    still inside the binary16 range the boundary documents, so the layer
+    keeps its bar and stays finite."""
+    x = (tiny.x(variant=7) * np.float32(64.0)).astype(np.float32)
+    ref = oracle_ref(tiny, x)
+    got = tiny.forward(x, mode)
+    assert np.isfinite(got["y"]).all()
+    check_routing(got, ref, tiny.cfg.k)
+    err = rel_err_rows(got["y"], ref["y"])
+    print(f"tiny x*64 mode={mode} rel err {err:.3e}, max|x| {np.abs(x).max():.1f}, max|y| {np.abs(got['y']).max():.1f}")
+    assert err <= TOL
+
+
 @pytest.mark.parametrize("T", [1, 3, 16, 17, 40, 64])
 def test_tiny_decode_token_counts(tiny, T):
     """Ragged decode batches, including more than one 16-token group."""
