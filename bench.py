@@ -306,8 +306,18 @@ def decode_batch(cfg, layers, T, steps, warmup, xvar0, efmt="cb2q2k"):
     distinct = [len(np.unique(sel[n])) for n in range(steps)]
     nbytes = float(np.mean([decode_bytes(cfg, nd, T=T, efmt=efmt)["total"] for nd in distinct]))
     del g
+    # one eager pass with the library's dispatch-attached timer: per-kernel means
+    D.trace_read(reset=True)
+    D.trace_enable(True)
+    with torch.cuda.stream(s):
+        for n in range(warmup, nsteps):
+            step(n, s)
+    torch.cuda.synchronize()
+    D.trace_enable(False)
+    kern = D.trace_read(reset=True)
     return dict(tok_s=T / (ms * 1e-3), us_per_step=ms * 1e3, distinct_mean=float(np.mean(distinct)),
-                bytes_per_step=nbytes, hbm_frac=nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS)
+                bytes_per_step=nbytes, hbm_frac=nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                kernels_us={k: round(v[0] / v[1] * 1e3, 2) for k, v in kern.items() if v[1] > 0})
 
 
 def bench_decode16(copies=4, steps=64, warmup=8):
@@ -803,7 +813,7 @@ def main():
     for efmt in () if args.no_wide else ("mxfp4", "q4k"):
         wd = bench_wide(efmt)
         log(f"[bench] {efmt} decode: {wd['us_per_step']:.1f} us/step, {wd['tok_s']:.0f} tok/s, "
-            f"{100 * wd['hbm_frac']:.1f} % of HBM peak")
+            f"{100 * wd['hbm_frac']:.1f} % of HBM peak, kernels {wd['kernels_us']}")
         wp = None if args.no_prefill else bench_prefill(args, efmt=efmt)
         if wp:
             log(f"[bench] {efmt} prefill: {wp['ms']:.3f} ms, {wp['tok_s']:.0f} tok/s, {wp['tflops']:.1f} TFLOP/s")

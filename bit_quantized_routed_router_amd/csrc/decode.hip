@@ -630,11 +630,17 @@ __global__ __launch_bounds__(kW * 64) __attribute__((amdgpu_waves_per_eu(stage2_
 // - binary16(dmin m), rounded once), so no per-super-block scale after the
 // products.  Activations come from LDS when staged (BL), else from the
 // binary16 copy in memory.
-constexpr int kSbMx = 2;  // super-blocks a wave loads at once (32 code bytes per matrix and lane each)
+// super-blocks a wave loads at once (32 code bytes per matrix and lane each):
+// four for MXFP4; two for Q4K, whose three scale words and (d, dmin) per
+// super-block would not fit four blocks' worth in the 128 registers of a
+// 4-wave-per-SIMD kernel
+template <bool Q4>
+constexpr int sb_batch() { return Q4 ? 2 : 4; }
 
 template <bool LO, bool BL, bool Q4>
 __device__ void routed_gateup_mx(const ds4moe_layer& L, int T, const RouteOut& ro, const _Float16* __restrict__ xh,
                                  const _Float16* __restrict__ xl, _Float16* __restrict__ hw16, Stage2Lds<LO, BL>& lds) {
+  constexpr int kSbMx = sb_batch<Q4>();
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = lane & 15, q = lane >> 4;
   const int tc = min(c, T - 1);
@@ -700,34 +706,37 @@ __device__ void routed_gateup_mx(const ds4moe_layer& L, int T, const RouteOut& r
   for (int b0 = sb0; b0 < sb1; b0 += kSbMx) {
     if (b0 != sb0) load_batch(b0);
     pin();
-    Q4kS sg[kSbMx], su[kSbMx];
-    if constexpr (Q4) {
+    // nested constant-trip loops (fully unrolled, so the per-super-block
+    // registers are indexed statically); super-blocks past the range are
+    // skipped by a wave-uniform test
 #pragma unroll
-      for (int j = 0; j < kSbMx; ++j) {
-        sg[j] = q4k_lane_scales(qg[j], q);
-        su[j] = q4k_lane_scales(qu[j], q);
-      }
-    }
+    for (int j = 0; j < kSbMx; ++j) {
+      if (b0 + j < sb1) {
+        Q4kS sg, su;  // Q4K: this super-block's binary16 scales, formed just before use
+        if constexpr (Q4) {
+          sg = q4k_lane_scales(qg[j], q);
+          su = q4k_lane_scales(qu[j], q);
+        }
 #pragma unroll
-    for (int t = 0; t < 8 * kSbMx; ++t) {
-      const int j = t >> 3, s2 = t & 7;
-      if (b0 + j >= sb1) break;  // wave-uniform
-      const int kk = (b0 + j) * QK + cb2_boff(q, s2);
-      half8_t bh, bl;
-      if (BL) {
-        bh = *(const half8_t*)(lds.bh + tc * st + kk);
-        if (LO) bl = *(const half8_t*)(lds.bl + tc * st + kk);
-      } else {
-        bh = *(const half8_t*)(xh + (int64_t)tc * d + kk);
-        if (LO) bl = *(const half8_t*)(xl + (int64_t)tc * d + kk);
-      }
-      const half8_t a0 = Q4 ? q4k_step(qg[j], sg[j], s2) : mx4_step(wg[j], s2);
-      const half8_t a1 = Q4 ? q4k_step(qu[j], su[j], s2) : mx4_step(wu[j], s2);
-      ag = mfma16x16x32(bh, a0, ag);
-      au = mfma16x16x32(bh, a1, au);
-      if (LO) {
-        ag = mfma16x16x32(bl, a0, ag);
-        au = mfma16x16x32(bl, a1, au);
+        for (int s2 = 0; s2 < 8; ++s2) {
+          const int kk = (b0 + j) * QK + cb2_boff(q, s2);
+          half8_t bh, bl;
+          if (BL) {
+            bh = *(const half8_t*)(lds.bh + tc * st + kk);
+            if (LO) bl = *(const half8_t*)(lds.bl + tc * st + kk);
+          } else {
+            bh = *(const half8_t*)(xh + (int64_t)tc * d + kk);
+            if (LO) bl = *(const half8_t*)(xl + (int64_t)tc * d + kk);
+          }
+          const half8_t a0 = Q4 ? q4k_step(qg[j], sg, s2) : mx4_step(wg[j], s2);
+          const half8_t a1 = Q4 ? q4k_step(qu[j], su, s2) : mx4_step(wu[j], s2);
+          ag = mfma16x16x32(bh, a0, ag);
+          au = mfma16x16x32(bh, a1, au);
+          if (LO) {
+            ag = mfma16x16x32(bl, a0, ag);
+            au = mfma16x16x32(bl, a1, au);
+          }
+        }
       }
     }
   }
