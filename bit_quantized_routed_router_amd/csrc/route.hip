@@ -65,8 +65,8 @@ __global__ __launch_bounds__(NW * 64) void k_router_logits(const uint16_t* __res
   const int arow = min(e0 + (lane & 15), E - 1);
   int ks0, ks1;
   split_range(d / 32, NW, wave, ks0, ks1);
-  float4_t acc = {0.f, 0.f, 0.f, 0.f}, unused = acc;
-  f16_tile<false, LO>(wr + (int64_t)arow * d, nullptr, bh, bl, ks0, ks1, lane, acc, unused);
+  float4_t acc = {0.f, 0.f, 0.f, 0.f};
+  f16_tile<LO>(wr + (int64_t)arow * d, bh, bl, ks0, ks1, lane, acc);
   acc = block_reduce_waves<NW>(acc, red, wave, lane);
   if (wave == 0 && t < T) {
 #pragma unroll

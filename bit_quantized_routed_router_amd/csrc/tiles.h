@@ -22,27 +22,32 @@ __device__ inline half8_t load_b(const _Float16* col, int ks, int lane) {
 __device__ inline float h2f(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
 
 // ------------------------------------------------------------------ F16 rows
-// Two F16 matrices (e.g. gate and up) against the same columns.  W rows are
-// row-major with row length K; rowp* point at row (row0 + (lane & 15)).
-template <bool PAIR, bool LO>
-__device__ inline void f16_tile(const uint16_t* __restrict__ rowp0, const uint16_t* __restrict__ rowp1,
-                                const _Float16* bcol, const _Float16* bcol_lo, int ks0, int ks1, int lane,
-                                float4_t& acc0, float4_t& acc1) {
+// One F16 matrix (16 rows at rowp, lane row lane & 15) against 16 binary16
+// columns (bcol, and bcol_lo for the lo half of a split fp32 input; NULL
+// columns read as zero) over K-steps [ks0, ks1) of 32 inputs.  The loads of
+// a batch of K-steps go out together before its MFMAs (constant-trip inner
+// loops, so they unroll); the batch's tail past ks1 repeats the last step's
+// address and is not multiplied.
+template <bool LO>
+__device__ inline void f16_tile(const uint16_t* __restrict__ rowp, const _Float16* bcol, const _Float16* bcol_lo,
+                                int ks0, int ks1, int lane, float4_t& acc) {
+  constexpr int kB = LO ? 4 : 8;
   const int ko = 8 * (lane >> 4);
-#pragma unroll 4
-  for (int ks = ks0; ks < ks1; ++ks) {
-    half8_t b = load_b(bcol, ks, lane);
-    half8_t a0 = *(const half8_t*)(rowp0 + ks * 32 + ko);
-    acc0 = mfma16x16x32(a0, b, acc0);
-    half8_t a1;
-    if (PAIR) {
-      a1 = *(const half8_t*)(rowp1 + ks * 32 + ko);
-      acc1 = mfma16x16x32(a1, b, acc1);
+  for (int k0 = ks0; k0 < ks1; k0 += kB) {
+    half8_t a[kB], b[kB], bl[kB];
+#pragma unroll
+    for (int u = 0; u < kB; ++u) {
+      const int ks = min(k0 + u, ks1 - 1);
+      a[u] = *(const half8_t*)(rowp + ks * 32 + ko);
+      b[u] = load_b(bcol, ks, lane);
+      if (LO) bl[u] = load_b(bcol_lo, ks, lane);
     }
-    if (LO) {
-      half8_t bl = load_b(bcol_lo, ks, lane);
-      acc0 = mfma16x16x32(a0, bl, acc0);
-      if (PAIR) acc1 = mfma16x16x32(a1, bl, acc1);
+#pragma unroll
+    for (int u = 0; u < kB; ++u) {
+      if (k0 + u < ks1) {  // wave-uniform
+        acc = mfma16x16x32(a[u], b[u], acc);
+        if (LO) acc = mfma16x16x32(a[u], bl[u], acc);
+      }
     }
   }
 }
