@@ -213,10 +213,13 @@ struct GuW {
   uint32_t dv[4];
   u32x4_t wv[F16 ? 4 : 1][F16 ? 4 : 1];
   u32x4_t mw[MX || Q4 ? 4 : 1];
-  uint32_t qs[Q4 ? 4 : 1][Q4 ? 3 : 1];
+  u32x3_t qs[Q4 ? 4 : 1];  // Q4K: the super-block's three scale words (one 12-byte load)
   int jq;  // Q4K: the lane's sub-block within its super-block (set at issue)
-  static constexpr int kLoads = F16 ? 16 : (Q4 ? 20 : (MX ? 8 : 4));
-  static constexpr int kMaxLoads = F16 ? 16 : (Q4 ? 20 : 8);
+  static constexpr int kLoads = F16 ? 16 : (Q4 ? 12 : (MX ? 8 : 4));
+  static constexpr int kMaxLoads = F16 ? 16 : (Q4 ? 12 : 8);
+  // loads per chunk that size the ring: Q4K keeps the depth of 20 loads, which
+  // its registers allow (a deeper ring spills)
+  static constexpr int kRingLoads = Q4 ? 20 : kMaxLoads;
 };
 
 // Gate/up of one work tile (up to 128 slots) for a 128-row slice of h, NF
@@ -250,8 +253,7 @@ __device__ __attribute__((always_inline)) inline void gateup_tile(const ds4moe_l
       if constexpr (Q4) {  // row hr0 + 16 (f & 1) + c, sub-block 4 (ch & 1) + q of super-block ch / 2
         const uint32_t r = (uint32_t)(hr0 + 16 * (f & 1) + c), blk = r * (uint32_t)nb + (uint32_t)(ch >> 1);
         W.mw[f] = ld_at<u32x4_t>(f < 2 ? gb : ub, blk * 128u + 16u * (uint32_t)(4 * (ch & 1) + q));
-#pragma unroll
-        for (int t = 0; t < 3; ++t) W.qs[f][t] = ld_at<uint32_t>(f < 2 ? gd : ud, blk * 12u + 4u * t);
+        W.qs[f] = ld_at<u32x3_a4_t>(f < 2 ? gd : ud, blk * 12u);
         W.dv[f] = ld_at<uint32_t>(f < 2 ? gsp : usp, blk * 4u);
         W.jq = 4 * (ch & 1) + q;
       } else if constexpr (MX) {  // row hr0 + 16 (f & 1) + c, block 4 ch + q
@@ -282,7 +284,7 @@ __device__ __attribute__((always_inline)) inline void gateup_tile(const ds4moe_l
   // Loads per chunk and lane.  The ring depth keeps the largest count within the load counter; the waits use the
   // smallest, which is exact when every scale is staged and waits longer than needed otherwise.
   constexpr int kBatch = dma_per_wave(NF, NW) * (LO ? 2 : 1) + GuW<DENSE, MX, Q4>::kLoads;
-  constexpr int R = ring_depth(NF, dma_per_wave(NF, NW) * (LO ? 2 : 1) + GuW<DENSE, MX, Q4>::kMaxLoads, LO, RING);
+  constexpr int R = ring_depth(NF, dma_per_wave(NF, NW) * (LO ? 2 : 1) + GuW<DENSE, MX, Q4>::kRingLoads, LO, RING);
   constexpr int kSlot = NF * 16 * kKC;  // halves per ring slot
   static_assert(R * kSlot <= RING, "ring slots exceed the staging buffer");
   GuW<DENSE, MX, Q4> W[R];
@@ -476,10 +478,11 @@ struct DnW {
   uint32_t sc[4], dd[MX ? 1 : 4];
   u32x4_t wv[F16 ? 4 : 1][F16 ? 4 : 1];
   u32x4_t mw[MX || Q4 ? 4 : 1];  // MXFP4 / Q4K: the lane's 32 elements (16 code bytes); MXFP4's scale byte in sc
-  uint32_t qs[Q4 ? 4 : 1][Q4 ? 3 : 1];  // Q4K: scale words; (d, dmin) in dd
-  int jq;                                // Q4K: the lane's sub-block within its super-block
-  static constexpr int kMaxLoads = F16 ? 16 : (Q4 ? 20 : (MX ? 8 : 12));
-  static constexpr int kLoads = F16 ? 16 : (Q4 ? 20 : (MX ? 8 : 4 + (SC ? 0 : 4) + (DD ? 0 : 4)));
+  u32x3_t qs[Q4 ? 4 : 1];  // Q4K: scale words (one 12-byte load); (d, dmin) in dd
+  int jq;                   // Q4K: the lane's sub-block within its super-block
+  static constexpr int kMaxLoads = F16 ? 16 : (Q4 ? 12 : (MX ? 8 : 12));
+  static constexpr int kLoads = F16 ? 16 : (Q4 ? 12 : (MX ? 8 : 4 + (SC ? 0 : 4) + (DD ? 0 : 4)));
+  static constexpr int kRingLoads = Q4 ? 20 : kMaxLoads;  // as in GuW
 };
 
 // Down product of one work tile for a 256-row slice of the output.  Routed
@@ -507,8 +510,7 @@ __device__ __attribute__((always_inline)) inline void down_tile(const ds4moe_lay
       if constexpr (Q4) {  // row r0 + 16 f + c, sub-block 4 (ch & 1) + q of super-block ch / 2
         const uint32_t r = (uint32_t)(r0 + 16 * f + c), blk = r * (uint32_t)nb + (uint32_t)(ch >> 1);
         W.mw[f] = ld_at<u32x4_t>(base, blk * 128u + 16u * (uint32_t)(4 * (ch & 1) + q));
-#pragma unroll
-        for (int t = 0; t < 3; ++t) W.qs[f][t] = ld_at<uint32_t>(sub, blk * 12u + 4u * t);
+        W.qs[f] = ld_at<u32x3_a4_t>(sub, blk * 12u);
         W.dd[f] = ld_at<uint32_t>(sup, blk * 4u);
         W.jq = 4 * (ch & 1) + q;
       } else if constexpr (MX) {  // row r0 + 16 f + c, block 4 ch + q
@@ -544,7 +546,7 @@ __device__ __attribute__((always_inline)) inline void down_tile(const ds4moe_lay
 
   // As in gate/up: the depth bounds the largest load count, the waits use the smallest.
   constexpr int kBatch = dma_per_wave(NF, kGW) + WT::kLoads;
-  constexpr int R = ring_depth(NF, dma_per_wave(NF, kGW) + WT::kMaxLoads, false, RING,
+  constexpr int R = ring_depth(NF, dma_per_wave(NF, kGW) + WT::kRingLoads, false, RING,
                                RING < 2 * kChunk ? 3 : 6);  // small: register budget
   constexpr int kSlot = NF * 16 * kKC;
   static_assert(R * kSlot <= RING, "ring slots exceed the staging buffer");
