@@ -59,9 +59,9 @@ METRIC = "routed-MoE layer decode tok/s + % HBM peak; 2048-tok prefill tok/s + %
 # the L2's read requests to memory by size (the terms of FETCH_SIZE, each
 # 128-byte request at 128 bytes) and WRITE_SIZE, both checked against a
 # 256 MiB device copy (factor 1.000); valid for the kernel sources with this
-# hash only (profiles/decode1_hbm_traffic.md holds the commands and counts).
-TRAFFIC_SOURCE_HASH = "1f8fcca8b8ca99ea"
-TRAFFIC_BYTES = {"k_dec_stage1": 2.26e6, "k_dec_stage2": 60.06e6, "k_dec_stage3": 33.61e6}
+# hash only (profiles/decode_hbm_traffic.md holds the commands and counts).
+TRAFFIC_SOURCE_HASH = "91e26155d96a8c5c"
+TRAFFIC_BYTES = {"k_dec_stage1": 2.26e6, "k_dec_stage2": 60.18e6, "k_dec_stage3": 33.60e6}
 
 
 def kernel_source_hash(csrc=None):

@@ -683,10 +683,10 @@ __device__ void routed_gateup_mx(const ds4moe_layer& L, int T, const RouteOut& r
         qg[j].c1 = __builtin_nontemporal_load((const u32x4_t*)(grow + 128 * b + 16));
         qu[j].c0 = __builtin_nontemporal_load((const u32x4_t*)(urow + 128 * b));
         qu[j].c1 = __builtin_nontemporal_load((const u32x4_t*)(urow + 128 * b + 16));
-        const uint32_t* gw = (const uint32_t*)(gsc + 12 * b);
-        const uint32_t* uw = (const uint32_t*)(usc + 12 * b);
-        qg[j].w0 = gw[0]; qg[j].w1 = gw[1]; qg[j].w2 = gw[2];
-        qu[j].w0 = uw[0]; qu[j].w1 = uw[1]; qu[j].w2 = uw[2];
+        const u32x3_t gw = *(const u32x3_a4_t*)(gsc + 12 * b);  // one 12-byte load each
+        const u32x3_t uw = *(const u32x3_a4_t*)(usc + 12 * b);
+        qg[j].w0 = gw.x; qg[j].w1 = gw.y; qg[j].w2 = gw.z;
+        qu[j].w0 = uw.x; qu[j].w1 = uw.y; qu[j].w2 = uw.z;
         qg[j].sup = *(const uint32_t*)(gsp + 4 * b);
         qu[j].sup = *(const uint32_t*)(usp + 4 * b);
       } else {
@@ -947,10 +947,10 @@ __global__ __launch_bounds__(kW3 * 64) __attribute__((amdgpu_waves_per_eu(4))) v
         const uint8_t* base = down + (size_t)clamp_index(ej[j], L.n_experts) * mx_bytes;
         WQ[j].c0 = __builtin_nontemporal_load((const u32x4_t*)(base + mx_codes + 128 * bj[j]));
         WQ[j].c1 = __builtin_nontemporal_load((const u32x4_t*)(base + mx_codes + 128 * bj[j] + 16));
-        const uint32_t* sw = (const uint32_t*)(base + q4_sc + 12 * bj[j]);
-        WQ[j].w0 = sw[0];
-        WQ[j].w1 = sw[1];
-        WQ[j].w2 = sw[2];
+        const u32x3_t sw = *(const u32x3_a4_t*)(base + q4_sc + 12 * bj[j]);  // one 12-byte load
+        WQ[j].w0 = sw.x;
+        WQ[j].w1 = sw.y;
+        WQ[j].w2 = sw.z;
         WQ[j].sup = *(const uint32_t*)(base + q4_sp + 4 * bj[j]);
       } else if constexpr (MX) {
         const uint8_t* base = down + (size_t)clamp_index(ej[j], L.n_experts) * mx_bytes;
