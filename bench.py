@@ -381,7 +381,7 @@ def bench_prefill(args, efmt="cb2q2k"):
     T = cfg.T
     y = torch.empty((T, cfg.d), dtype=torch.float32, device="cuda")
     ws, wsn = L.workspace(T, D.MODE_PREFILL)
-    for _ in range(2):
+    for _ in range(5):  # warm-up: the first calls after packing run slower (clocks, caches)
         D.forward_prefill(L.desc, x, D.DT_BF16, T, y, None, None, None, ws, wsn)
     torch.cuda.synchronize()
     runs = []

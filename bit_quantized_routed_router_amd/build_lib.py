@@ -33,6 +33,7 @@ SOURCES = {
     "decode.hip": [],
     "prefill.hip": [],
     "hc.hip": [],
+    "dense.hip": [],
     "capi.cpp": ["-x", "hip"],
     "trace.cpp": ["-x", "hip"],
 }

@@ -77,6 +77,9 @@ hipError_t launch_dequant_q4k(const void* packed, int64_t rows, int64_t cols, fl
 hipError_t launch_route(const Fwd& f, bool decode);
 hipError_t launch_decode(const Fwd& f);  // full layer for one group of <= 16 tokens
 hipError_t launch_prefill_experts(const Fwd& f);
+// prefill shared expert: gate/up into hs16 (binary16), down into y (fp32)
+hipError_t launch_prefill_shared(const ds4moe_layer& L, int64_t T, bool lo, const _Float16* xh, const _Float16* xl,
+                                 _Float16* hs16, float* y, hipStream_t st);
 
 // hyper-connection mixer (ds4moe_hc); hc_ws_bytes: workspace of hc_pre
 constexpr int64_t kHcMaxT = 1 << 20;

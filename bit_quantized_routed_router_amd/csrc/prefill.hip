@@ -1,17 +1,15 @@
 // Prefill (any T): grouped expert products over the work list of (expert,
-// run of up to 128 of its slots) tiles built by the grouping kernels, plus
-// the dense shared expert.
+// run of up to 128 of its slots) tiles built by the grouping kernels; the
+// dense shared expert runs first (dense.hip: hs16 and y = Wsd hs16).
 //
-//   k_pf_gateup<DENSE>   hs16[t] = silu(Wsg x_t) * (Wsu x_t)          (binary16)
 //   k_pf_gateup          hw16[p] = w_s * silu(G_e x_t) * (U_e x_t)    (binary16)
 //   k_pf_down            yp[s]   = D_e hw16[p]                         (fp32)
-//   k_pf_down<DENSE>     y[t]    = Wsd hs16[t]                         (fp32)
 //   k_combine            y[t]   += sum_j yp[t*k + j], j ascending
 // Slots s = t*k + j sit at position p of the expert-sorted list (perm[p] = s).
 // The combine order is fixed, so results are deterministic.
 //
 // Grouped GEMM.  A block takes one work tile (a routed expert's run of up to
-// 128 slots, or 128 tokens of the shared expert) and a slice of output rows.  Each of its four waves owns four 16-row weight fragments
+// 128 slots) and a slice of output rows.  Each of its four waves owns four 16-row weight fragments
 // and all of the tile's slots (up to eight 16-slot fragments), so a weight is
 // decoded once per tile and a staged activation fragment feeds four MFMAs
 // (v_mfma_f32_16x16x32_f16 with the slots as A rows and the weights as B
@@ -32,6 +30,7 @@
 #include <algorithm>
 
 #include "common.h"
+#include "ring.h"
 #include "internal.h"
 #include "tiles.h"
 #include "trace.h"
@@ -58,56 +57,6 @@ constexpr int ring_depth(int nf, int loads, bool lo, int ring, int rmax = 6) {
   int r = lo ? 2 : rmax;
   while (r > 2 && (r * nf * 16 * kKC > ring || (r - 1) * loads > 63)) --r;
   return r;
-}
-
-// Waits until at most N vector-memory operations of this wave are in flight.
-template <int N>
-__device__ inline void vm_wait() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
-
-// Workgroup barrier for the chunk loop.  __syncthreads() carries a release
-// fence, and the compiler meets it by waiting for every outstanding load --
-// LDS-bound copies count as LDS stores -- which would drain the whole
-// prefetch ring.  Here the loop orders memory itself: a wave has waited for
-// its own copies into the slot it is about to read before this barrier, and
-// its reads of a slot have returned (lgkmcnt) before the barrier after which
-// that slot is refilled.  The memory clobber keeps the compiler from moving
-// LDS accesses across it.
-__device__ inline void ring_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-
-// The chunk loop of a tile with R chunks in flight and one barrier per
-// chunk.  issue(ch, u) starts loading chunk ch into ring slot u (B
-// vector-memory instructions per lane); compute(u) consumes slot u.  At each
-// step the wave waits for its copies of the chunk it is about to use, the
-// barrier makes everyone's copies visible and shows that all waves are done
-// with the previous chunk, whose slot is then refilled with the chunk R - 1
-// ahead before computing.  Every step issues a batch -- past the last chunk
-// it repeats the last one (cache hits, never read) -- so the loop has one
-// shape and the compiler's own waits for the weight registers stay partial.
-// Passes of R chunks run unrolled (static slot indices); steps past the last
-// chunk keep the waits and issues and skip the compute.  The final wait
-// drains every load before the block's LDS can be reused.
-template <int R, int B, typename Issue, typename Compute>
-__device__ __attribute__((always_inline)) inline void ring_loop(int nch, Issue issue, Compute compute) {
-  static_assert(R >= 2 && (R - 1) * B <= 63, "ring depth");
-#pragma unroll
-  for (int u = 0; u < R - 1; ++u) issue(min(u, nch - 1), u);
-  auto step = [&](int ch, int u) {
-    pin();
-    vm_wait<(R - 2) * B>();
-    ring_barrier();
-    pin();
-    issue(min(ch + R - 1, nch - 1), (u + R - 1) % R);
-    pin();
-    if (ch < nch) compute(u);
-  };
-  for (int ch0 = 0; ch0 < nch; ch0 += R) {
-#pragma unroll
-    for (int u = 0; u < R; ++u) step(ch0 + u, u);
-  }
-  vm_wait<0>();
 }
 
 // Copy instructions per wave and chunk for 16 NF rows (4 NF groups of 4 rows)
@@ -197,46 +146,44 @@ struct GuLds {
   float w[kTT];
   uint16_t dsc[NBS ? 2 * 128 * NBS : 2];
 };
-template <bool DENSE, bool MX = false, bool Q4 = false>
-constexpr int gu_nbs() { return DENSE || MX || Q4 ? 0 : 16; }
+template <bool MX = false, bool Q4 = false>
+constexpr int gu_nbs() { return MX || Q4 ? 0 : 16; }
 
-// Weights of one 128-input chunk for a lane's four fragments.  CB2: the lane's sub-block (8 bytes) and its block's d; F16:
-// the lane's 4 x 8 binary16 values (inputs 32q .. 32q+31 of the chunk).  kLoads counts the vector-memory loads of a
-// chunk when every scale comes from LDS; kMaxLoads when they are all read from memory (blocks past the staged ones).
+// Weights of one 128-input chunk for a lane's four fragments.  CB2: the lane's sub-block (8 bytes) and its block's d.
+// kLoads counts the vector-memory loads of a chunk when every scale comes from LDS; kMaxLoads when they are all read
+// from memory (blocks past the staged ones).
 // MXFP4: the lane's 32 inputs of the chunk are one MX block, 16 code bytes and
 // one scale byte per fragment.
 // Q4K (Q4): the lane's 32 inputs are one sub-block, 16 code bytes, plus its
 // super-block's three scale words and (d, dmin) word per fragment.
-template <bool F16, bool MX = false, bool Q4 = false>
+template <bool MX = false, bool Q4 = false>
 struct GuW {
   u32x2_t cw[MX || Q4 ? 1 : 4];
   uint32_t dv[4];
-  u32x4_t wv[F16 ? 4 : 1][F16 ? 4 : 1];
   u32x4_t mw[MX || Q4 ? 4 : 1];
   u32x3_t qs[Q4 ? 4 : 1];  // Q4K: the super-block's three scale words (one 12-byte load)
   int jq;  // Q4K: the lane's sub-block within its super-block (set at issue)
-  static constexpr int kLoads = F16 ? 16 : (Q4 ? 12 : (MX ? 8 : 4));
-  static constexpr int kMaxLoads = F16 ? 16 : (Q4 ? 12 : 8);
+  static constexpr int kLoads = Q4 ? 12 : (MX ? 8 : 4);
+  static constexpr int kMaxLoads = Q4 ? 12 : 8;
   // loads per chunk that size the ring: Q4K keeps the depth of 20 loads, which
   // its registers allow (a deeper ring spills)
   static constexpr int kRingLoads = Q4 ? 20 : kMaxLoads;
 };
 
 // Gate/up of one work tile (up to 128 slots) for a 128-row slice of h, NF
-// slot fragments.  DENSE: the shared expert (F16 weights, weight 1, rows are
-// tokens); otherwise routed expert e (CB2 weights, or MXFP4 with MX; routing
-// weights s.w).
-template <bool LO, bool DENSE, int NW, int TC, int RING, int NF, int NBS, bool MX = false, bool Q4 = false>
+// slot fragments, routed expert e (CB2 weights, or MXFP4 with MX, Q4K with
+// Q4; routing weights s.w).
+template <bool LO, int NW, int TC, int RING, int NF, int NBS, bool MX = false, bool Q4 = false>
 __device__ __attribute__((always_inline)) inline void gateup_tile(const ds4moe_layer& L, GuLds<LO, TC, RING, NBS>& s,
                                                                   const _Float16* __restrict__ xh,
                                                                   const _Float16* __restrict__ xl, int e, int rt,
                                                                   int pos0, int n, _Float16* __restrict__ hout) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, c = lane & 15, q = lane >> 4;
-  const int d = L.d_model, fd = DENSE ? L.d_ff_shared : L.d_ff, nb = d / QK, nch = d / kKC;
+  const int d = L.d_model, fd = L.d_ff, nb = d / QK, nch = d / kKC;
   const size_t mb = (size_t)fd * nb;
   const size_t mat_bytes = Q4 ? mb * 144 : (MX ? (size_t)fd * d * 17 / 32 : mb * 66);
-  const uint8_t* gb = DENSE ? (const uint8_t*)L.sh_gate : (const uint8_t*)L.gate + (size_t)e * mat_bytes;
-  const uint8_t* ub = DENSE ? (const uint8_t*)L.sh_up : (const uint8_t*)L.up + (size_t)e * mat_bytes;
+  const uint8_t* gb = (const uint8_t*)L.gate + (size_t)e * mat_bytes;
+  const uint8_t* ub = (const uint8_t*)L.up + (size_t)e * mat_bytes;
   // CB2 d plane / MXFP4 scale plane / Q4K scale words
   const uint8_t* gd = gb + (Q4 ? mb * 128 : (MX ? (size_t)fd * d / 2 : mb * 64));
   const uint8_t* ud = ub + (Q4 ? mb * 128 : (MX ? (size_t)fd * d / 2 : mb * 64));
@@ -246,8 +193,8 @@ __device__ __attribute__((always_inline)) inline void gateup_tile(const ds4moe_l
   // fragment f: rows hr0 + 16 (f & 1) + c of gate (f < 2) or up (f >= 2)
   uint32_t rowu[2];
 #pragma unroll
-  for (int h = 0; h < 2; ++h) rowu[h] = (uint32_t)((hr0 + 16 * h + c) * (DENSE ? d : nb));
-  auto load_w = [&](int ch, GuW<DENSE, MX, Q4>& W) {
+  for (int h = 0; h < 2; ++h) rowu[h] = (uint32_t)((hr0 + 16 * h + c) * nb);
+  auto load_w = [&](int ch, GuW<MX, Q4>& W) {
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
       if constexpr (Q4) {  // row hr0 + 16 (f & 1) + c, sub-block 4 (ch & 1) + q of super-block ch / 2
@@ -260,10 +207,6 @@ __device__ __attribute__((always_inline)) inline void gateup_tile(const ds4moe_l
         const uint32_t r = (uint32_t)(hr0 + 16 * (f & 1) + c), blk = (uint32_t)(4 * ch + q);
         W.mw[f] = ld_at<u32x4_t>(f < 2 ? gb : ub, r * (uint32_t)(d / 2) + 16u * blk);
         W.dv[f] = ld_at<uint8_t>(f < 2 ? gd : ud, r * (uint32_t)(d / 32) + blk);
-      } else if constexpr (DENSE) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          W.wv[f][j] = ld_at<u32x4_t>(f < 2 ? gb : ub, 2u * (rowu[f & 1] + (uint32_t)(ch * kKC + 32 * q + 8 * j)));
       } else {
         const uint32_t blk = rowu[f & 1] + (uint32_t)(ch >> 1);
         W.cw[f] = ld_at<u32x2_t>(f < 2 ? gb : ub, blk * 64u + (uint32_t)(32 * (ch & 1) + 8 * q));
@@ -283,11 +226,11 @@ __device__ __attribute__((always_inline)) inline void gateup_tile(const ds4moe_l
 
   // Loads per chunk and lane.  The ring depth keeps the largest count within the load counter; the waits use the
   // smallest, which is exact when every scale is staged and waits longer than needed otherwise.
-  constexpr int kBatch = dma_per_wave(NF, NW) * (LO ? 2 : 1) + GuW<DENSE, MX, Q4>::kLoads;
-  constexpr int R = ring_depth(NF, dma_per_wave(NF, NW) * (LO ? 2 : 1) + GuW<DENSE, MX, Q4>::kRingLoads, LO, RING);
+  constexpr int kBatch = dma_per_wave(NF, NW) * (LO ? 2 : 1) + GuW<MX, Q4>::kLoads;
+  constexpr int R = ring_depth(NF, dma_per_wave(NF, NW) * (LO ? 2 : 1) + GuW<MX, Q4>::kRingLoads, LO, RING);
   constexpr int kSlot = NF * 16 * kKC;  // halves per ring slot
   static_assert(R * kSlot <= RING, "ring slots exceed the staging buffer");
-  GuW<DENSE, MX, Q4> W[R];
+  GuW<MX, Q4> W[R];
   auto issue = [&](int ch, int u) {
     stage_rows<LO, NF, NW>(xh, xl, rows, ch, s.xh + u * kSlot, s.xl + (LO ? u * kSlot : 0), wave, lane);
     load_w(ch, W[u]);
@@ -305,7 +248,7 @@ __device__ __attribute__((always_inline)) inline void gateup_tile(const ds4moe_l
     } else if constexpr (MX) {
 #pragma unroll
       for (int f = 0; f < 4; ++f) XS[f] = e8m0_f32(W[u].dv[f] & 0xFFu);
-    } else if constexpr (!DENSE) {
+    } else {
 #pragma unroll
       for (int f = 0; f < 4; ++f) D2[f] = h2splat(f16f(W[u].dv[f]) * (float)(2 * (W[u].cw[f].y >> 28) + 1));
     }
@@ -319,8 +262,6 @@ __device__ __attribute__((always_inline)) inline void gateup_tile(const ds4moe_l
           wf[f] = q4k_frag(W[u].mw[f][j], QD[f], QN[f]);
         else if constexpr (MX)
           wf[f] = mx4_frag(W[u].mw[f][j], XS[f]);
-        else if constexpr (DENSE)
-          wf[f] = as_half8(W[u].wv[f][j]);
         else
           wf[f] = cb2_frag_scaled<TC>(W[u].cw[f].x, W[u].cw[f].y, j, tmag, tsgn, D2[f]);
       }
@@ -346,7 +287,7 @@ __device__ __attribute__((always_inline)) inline void gateup_tile(const ds4moe_l
     for (int r = 0; r < 4; ++r) {
       const int t = 16 * i + 4 * q + r;
       if (t < n) {
-        const float wt = DENSE ? 1.0f : s.w[t];
+        const float wt = s.w[t];
 #pragma unroll
         for (int h = 0; h < 2; ++h)
           hout[(int64_t)(pos0 + t) * fd + hr0 + 16 * h + c] =
@@ -356,71 +297,58 @@ __device__ __attribute__((always_inline)) inline void gateup_tile(const ds4moe_l
   }
 }
 
-// Routed: item -> (work tile, row slice).  Dense: item -> (128 tokens, row
-// slice).  Returns false for blocks without work.
-template <bool DENSE, bool SMALL>
-__device__ inline bool tile_of(int rowtiles, int64_t T, const int32_t* big, const int32_t* small,
-                               const int32_t* ntiles, const int32_t* counts, const int32_t* offsets, int& e, int& rt,
-                               int& pos0, int& n) {
+// Item -> (work tile, row slice); false for blocks without work.
+template <bool SMALL>
+__device__ inline bool tile_of(int rowtiles, const int32_t* big, const int32_t* small, const int32_t* ntiles,
+                               const int32_t* counts, const int32_t* offsets, int& e, int& rt, int& pos0, int& n) {
   const int32_t* tiles = SMALL ? small : big;
-  const int ntile = DENSE ? (int)((T + kTT - 1) / kTT) : ntiles[SMALL ? 1 : 0];
+  const int ntile = ntiles[SMALL ? 1 : 0];
   int item;
   if (!xcd_item(ntile * rowtiles, item)) return false;
   const int tile = item / rowtiles;
   rt = item - tile * rowtiles;
-  if (DENSE) {
-    e = -1;
-    pos0 = tile * kTT;
-    n = (int)min((int64_t)kTT, T - pos0);
-  } else {
-    e = tiles[2 * tile];
-    const int g = tiles[2 * tile + 1];
-    pos0 = offsets[e] + kTT * g;
-    n = min(kTT, counts[e] - kTT * g);
-  }
+  e = tiles[2 * tile];
+  const int g = tiles[2 * tile + 1];
+  pos0 = offsets[e] + kTT * g;
+  n = min(kTT, counts[e] - kTT * g);
   return true;
 }
 
 // Slot fragments of a tile with n slots: small-tile kernels see 1-2, large
-// ones 3-8, the shared expert's any.
-#define DS4_NF_SWITCH(n, SMALL, DENSE, CALL)                  \
-  switch (((n) + 15) >> 4) {                                  \
-    case 1: if constexpr (SMALL || DENSE) CALL(1); break;     \
-    case 2: if constexpr (SMALL || DENSE) CALL(2); break;     \
-    case 3: if constexpr (!SMALL) CALL(3); break;             \
-    case 4: if constexpr (!SMALL) CALL(4); break;             \
-    case 5: if constexpr (!SMALL) CALL(5); break;             \
-    case 6: if constexpr (!SMALL) CALL(6); break;             \
-    case 7: if constexpr (!SMALL) CALL(7); break;             \
-    default: if constexpr (!SMALL) CALL(8); break;            \
+// ones 3-8.
+#define DS4_NF_SWITCH(n, SMALL, CALL)                  \
+  switch (((n) + 15) >> 4) {                           \
+    case 1: if constexpr (SMALL) CALL(1); break;       \
+    case 2: if constexpr (SMALL) CALL(2); break;       \
+    case 3: if constexpr (!SMALL) CALL(3); break;      \
+    case 4: if constexpr (!SMALL) CALL(4); break;      \
+    case 5: if constexpr (!SMALL) CALL(5); break;      \
+    case 6: if constexpr (!SMALL) CALL(6); break;      \
+    case 7: if constexpr (!SMALL) CALL(7); break;      \
+    default: if constexpr (!SMALL) CALL(8); break;     \
   }
 
-// Routed gate/up (CB2) over the work list into hw16, or (DENSE) the shared
-// expert's gate/up (F16) over all T tokens into hs16.
+// Routed gate/up over the work list into hw16.
 // Waves per gate/up block (each owns 32 rows of h) and codebook table copies.
-template <bool LO, bool DENSE>
-constexpr int gu_waves() { return 4; }
-template <bool LO, bool DENSE>
-constexpr int gu_copies() { return 1; }
+constexpr int kGuWaves = 4;
+constexpr int kGuCopies = 1;
 
 // SMALL: the small-tile list (at most 32 slots per tile, a smaller ring).
-// MX: the routed experts are MXFP4.
-template <bool LO, bool DENSE, bool SMALL, bool MX = false, bool Q4 = false>
-__global__ __launch_bounds__((gu_waves<LO, DENSE>() * 64))
-__attribute__((amdgpu_waves_per_eu(DENSE || LO ? 1 : 2))) void k_pf_gateup(
-    ds4moe_layer L, int64_t T, const _Float16* __restrict__ xh, const _Float16* __restrict__ xl,
+// MX / Q4: the routed experts are MXFP4 / Q4K.
+template <bool LO, bool SMALL, bool MX = false, bool Q4 = false>
+__global__ __launch_bounds__((kGuWaves * 64))
+__attribute__((amdgpu_waves_per_eu(LO ? 1 : 2))) void k_pf_gateup(
+    ds4moe_layer L, const _Float16* __restrict__ xh, const _Float16* __restrict__ xl,
     const int32_t* __restrict__ tiles, const int32_t* __restrict__ stiles, const int32_t* __restrict__ ntiles,
     const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets, const int32_t* __restrict__ perm,
     const float* __restrict__ topk_w, _Float16* __restrict__ hout) {
-  constexpr int NW = gu_waves<LO, DENSE>(), TC = gu_copies<LO, DENSE>(), RING = ring_halves(SMALL);
-  constexpr int NBS = gu_nbs<DENSE, MX, Q4>();
+  constexpr int NW = kGuWaves, TC = kGuCopies, RING = ring_halves(SMALL);
+  constexpr int NBS = gu_nbs<MX, Q4>();
   static_assert(NW == 4, "the staged scales cover 4 waves x 32 rows");
   __shared__ GuLds<LO, TC, RING, NBS> s;
   int e, rt, pos0, n;
-  if (!tile_of<DENSE, SMALL>((DENSE ? L.d_ff_shared : L.d_ff) / (32 * NW), T, tiles, stiles, ntiles, counts, offsets,
-                             e, rt, pos0, n))
-    return;
-  if constexpr (!DENSE && !MX && !Q4) {
+  if (!tile_of<SMALL>(L.d_ff / (32 * NW), tiles, stiles, ntiles, counts, offsets, e, rt, pos0, n)) return;
+  if constexpr (!MX && !Q4) {
     s.tab.stage(c_pre_tables);
     // scales of rows rt*128 .. +127 of gate (g = 0) and up (g = 1), blocks 0 .. ns-1
     const int nb = L.d_model / QK, ns = min(nb, NBS);
@@ -434,17 +362,13 @@ __attribute__((amdgpu_waves_per_eu(DENSE || LO ? 1 : 2))) void k_pf_gateup(
   }
   if ((int)threadIdx.x < kTT) {
     const int r = min((int)threadIdx.x, n - 1);
-    if (DENSE) {
-      s.tok[threadIdx.x] = pos0 + r;
-    } else {
-      const int slot = perm[pos0 + r];
-      s.tok[threadIdx.x] = slot / L.top_k;
-      s.w[threadIdx.x] = topk_w[slot];
-    }
+    const int slot = perm[pos0 + r];
+    s.tok[threadIdx.x] = slot / L.top_k;
+    s.w[threadIdx.x] = topk_w[slot];
   }
   __syncthreads();
-#define DS4_GU(NF) gateup_tile<LO, DENSE, NW, TC, RING, NF, NBS, MX, Q4>(L, s, xh, xl, e, rt, pos0, n, hout)
-  DS4_NF_SWITCH(n, SMALL, DENSE, DS4_GU)
+#define DS4_GU(NF) gateup_tile<LO, NW, TC, RING, NF, NBS, MX, Q4>(L, s, xh, xl, e, rt, pos0, n, hout)
+  DS4_NF_SWITCH(n, SMALL, DS4_GU)
 #undef DS4_GU
 }
 
@@ -464,46 +388,43 @@ struct DnLds {
 // (the ring leaves room for d/dmin only): d/dmin when the whole row fits
 // (d_ff <= 2048, DDS), with no in-loop fallback, which would not fit the
 // register budget.
-template <bool DENSE, bool SMALL, bool DDS>
-constexpr int dn_nbs() { return DENSE || (!SMALL && !DDS) ? 0 : 8; }
+template <bool SMALL, bool DDS>
+constexpr int dn_nbs() { return !SMALL && !DDS ? 0 : 8; }
 constexpr int kDnStagedMax = 8;
 
 // Down weights of one chunk.  Q2K: the lane's two sub-blocks of codes, the
-// aligned word holding their two scale bytes, the block's d/dmin; F16: 4 x 8
-// binary16 values per fragment.  kLoads / kMaxLoads: vector-memory loads of a
-// chunk with the scales staged in LDS / read from memory.
-template <bool F16, bool SC, bool DD, bool MX = false, bool Q4 = false>
+// aligned word holding their two scale bytes, the block's d/dmin.  kLoads /
+// kMaxLoads: vector-memory loads of a chunk with the scales staged in LDS /
+// read from memory.
+template <bool SC, bool DD, bool MX = false, bool Q4 = false>
 struct DnW {
   u32x2_t cw[MX || Q4 ? 1 : 4];
   uint32_t sc[4], dd[MX ? 1 : 4];
-  u32x4_t wv[F16 ? 4 : 1][F16 ? 4 : 1];
   u32x4_t mw[MX || Q4 ? 4 : 1];  // MXFP4 / Q4K: the lane's 32 elements (16 code bytes); MXFP4's scale byte in sc
   u32x3_t qs[Q4 ? 4 : 1];  // Q4K: scale words (one 12-byte load); (d, dmin) in dd
   int jq;                   // Q4K: the lane's sub-block within its super-block
-  static constexpr int kMaxLoads = F16 ? 16 : (Q4 ? 12 : (MX ? 8 : 12));
-  static constexpr int kLoads = F16 ? 16 : (Q4 ? 12 : (MX ? 8 : 4 + (SC ? 0 : 4) + (DD ? 0 : 4)));
+  static constexpr int kMaxLoads = Q4 ? 12 : (MX ? 8 : 12);
+  static constexpr int kLoads = Q4 ? 12 : (MX ? 8 : 4 + (SC ? 0 : 4) + (DD ? 0 : 4));
   static constexpr int kRingLoads = Q4 ? 20 : kMaxLoads;  // as in GuW
 };
 
-// Down product of one work tile for a 256-row slice of the output.  Routed
-// (Q2K, or MXFP4 with MX): yp[slot] = D_e h.  DENSE (shared, F16):
-// y[t] = Wsd hs16[t].
-template <bool DENSE, int RING, int NF, int NBS, bool SC, bool FULL, bool MX = false, bool Q4 = false>
+// Down product of one work tile for a 256-row slice of the output (Q2K, or
+// MXFP4 with MX, Q4K with Q4): yp[slot] = D_e h.
+template <int RING, int NF, int NBS, bool SC, bool FULL, bool MX = false, bool Q4 = false>
 __device__ __attribute__((always_inline)) inline void down_tile(const ds4moe_layer& L, DnLds<RING, NBS, SC>& s,
                                                                 const _Float16* __restrict__ hin, int e, int rt,
-                                                                int pos0, int n, float* __restrict__ yp,
-                                                                float* __restrict__ y) {
+                                                                int pos0, int n, float* __restrict__ yp) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, c = lane & 15, q = lane >> 4;
-  const int d = L.d_model, fd = DENSE ? L.d_ff_shared : L.d_ff, nb = fd / QK, nch = fd / kKC;
+  const int d = L.d_model, fd = L.d_ff, nb = fd / QK, nch = fd / kKC;
   const size_t mb = (size_t)d * nb;
   const size_t mat_bytes = Q4 ? mb * 144 : (MX ? (size_t)d * fd * 17 / 32 : mb * 84);
-  const uint8_t* base = DENSE ? (const uint8_t*)L.sh_down : (const uint8_t*)L.down + (size_t)e * mat_bytes;
+  const uint8_t* base = (const uint8_t*)L.down + (size_t)e * mat_bytes;
   // Q2K sub-scales / MXFP4 scale plane / Q4K scale words
   const uint8_t* sub = base + (Q4 ? mb * 128 : (MX ? (size_t)d * fd / 2 : mb * 64));
   const uint8_t* sup = base + (Q4 ? mb * 140 : mb * 80);
   const int r0 = rt * 256 + 64 * wave;
-  const uint32_t row0 = (uint32_t)((r0 + c) * (DENSE ? fd : nb));  // fragment f: + 16 f (fd or nb)
-  using WT = DnW<DENSE, SC, (NBS > 0), MX, Q4>;
+  const uint32_t row0 = (uint32_t)((r0 + c) * nb);  // fragment f: + 16 f nb
+  using WT = DnW<SC, (NBS > 0), MX, Q4>;
   auto load_w = [&](int ch, WT& W) {
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
@@ -517,10 +438,6 @@ __device__ __attribute__((always_inline)) inline void down_tile(const ds4moe_lay
         const uint32_t r = (uint32_t)(r0 + 16 * f + c), blk = (uint32_t)(4 * ch + q);
         W.mw[f] = ld_at<u32x4_t>(base, r * (uint32_t)(fd / 2) + 16u * blk);
         W.sc[f] = ld_at<uint8_t>(sub, r * (uint32_t)(fd / 32) + blk);
-      } else if constexpr (DENSE) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          W.wv[f][j] = ld_at<u32x4_t>(base, 2u * (row0 + (uint32_t)(16 * f * fd + ch * kKC + 32 * q + 8 * j)));
       } else {
         const uint32_t blk = row0 + (uint32_t)(16 * f * nb + (ch >> 1));
         W.cw[f] = ld_at<u32x2_t>(base, blk * 64u + (uint32_t)(32 * (ch & 1) + 8 * q));
@@ -582,13 +499,11 @@ __device__ __attribute__((always_inline)) inline void down_tile(const ds4moe_lay
     }
     auto half_chunk = [&](int h) {  // Q2K: sub-block 2q + h of the chunk feeds steps 2h, 2h+1
       half2_t A2[4], nB2[4];         // binary16 d * s and -(dmin * m) of the sub-block
-      if constexpr (!DENSE) {
 #pragma unroll
-        for (int f = 0; f < 4; ++f) {
-          const uint32_t sm = (W[u].sc[f] >> (16 * (q & 1) + 8 * h)) & 0xFFu;
-          A2[f] = h2splat(f16f(W[u].dd[f]) * (float)(sm & 15u));
-          nB2[f] = h2splat(-f16f(W[u].dd[f] >> 16) * (float)(sm >> 4));
-        }
+      for (int f = 0; f < 4; ++f) {
+        const uint32_t sm = (W[u].sc[f] >> (16 * (q & 1) + 8 * h)) & 0xFFu;
+        A2[f] = h2splat(f16f(W[u].dd[f]) * (float)(sm & 15u));
+        nB2[f] = h2splat(-f16f(W[u].dd[f] >> 16) * (float)(sm >> 4));
       }
 #pragma unroll
       for (int jj = 0; jj < 2; ++jj) {  // Q2K: codes 8jj .. 8jj+7 of the sub-block
@@ -596,18 +511,14 @@ __device__ __attribute__((always_inline)) inline void down_tile(const ds4moe_lay
         half8_t wf[4];
 #pragma unroll
         for (int f = 0; f < 4; ++f) {
-          if constexpr (DENSE) {
-            wf[f] = as_half8(W[u].wv[f][j]);
-          } else {
-            const uint32_t fld = ((h ? W[u].cw[f].y : W[u].cw[f].x) >> (16 * jj)) & 0xFFFFu;
-            uint32_t pr[4];
-            q2k_pairs(fld | (fld << 14), pr);
-            u32x4_t a;
+          const uint32_t fld = ((h ? W[u].cw[f].y : W[u].cw[f].x) >> (16 * jj)) & 0xFFFFu;
+          uint32_t pr[4];
+          q2k_pairs(fld | (fld << 14), pr);
+          u32x4_t a;
 #pragma unroll
-            for (int p = 0; p < 4; ++p)
-              a[p] = as_u32(__builtin_elementwise_fma(as_half2(pr[p]) + k1024, A2[f], nB2[f]));
-            wf[f] = as_half8(a);
-          }
+          for (int p = 0; p < 4; ++p)
+            a[p] = as_u32(__builtin_elementwise_fma(as_half2(pr[p]) + k1024, A2[f], nB2[f]));
+          wf[f] = as_half8(a);
         }
 #pragma unroll
         for (int i = 0; i < NF; ++i) {
@@ -627,36 +538,29 @@ __device__ __attribute__((always_inline)) inline void down_tile(const ds4moe_lay
     for (int r = 0; r < 4; ++r) {
       const int t = 16 * i + 4 * q + r;
       if (t < n) {
-        if constexpr (DENSE) {
+        const int64_t row = (int64_t)s.slot[t] * d;
 #pragma unroll
-          for (int f = 0; f < 4; ++f) y[(int64_t)(pos0 + t) * d + r0 + 16 * f + c] = acc[f][i][r];
-        } else {
-          const int64_t row = (int64_t)s.slot[t] * d;
-#pragma unroll
-          for (int f = 0; f < 4; ++f) yp[row + r0 + 16 * f + c] = acc[f][i][r];
-        }
+        for (int f = 0; f < 4; ++f) yp[row + r0 + 16 * f + c] = acc[f][i][r];
       }
     }
   }
 }
 
-// Routed down (Q2K, or MXFP4 with MX) over the work list into yp, or (DENSE)
-// the shared expert's down (F16) over all T tokens into y.
-template <bool DENSE, bool SMALL, bool DDS, bool MX = false, bool Q4 = false>
+// Routed down (Q2K, or MXFP4 with MX, Q4K with Q4) over the work list into yp.
+template <bool SMALL, bool DDS, bool MX = false, bool Q4 = false>
 __global__ __launch_bounds__(kGW * 64)
-__attribute__((amdgpu_waves_per_eu(DENSE ? 1 : 2))) void k_pf_down(
-    ds4moe_layer L, int64_t T, const int32_t* __restrict__ tiles, const int32_t* __restrict__ stiles,
+__attribute__((amdgpu_waves_per_eu(2))) void k_pf_down(
+    ds4moe_layer L, const int32_t* __restrict__ tiles, const int32_t* __restrict__ stiles,
     const int32_t* __restrict__ ntiles, const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ perm, const _Float16* __restrict__ hin, float* __restrict__ yp,
-    float* __restrict__ y) {
+    const int32_t* __restrict__ perm, const _Float16* __restrict__ hin, float* __restrict__ yp) {
   constexpr int RING = ring_halves(SMALL);
-  constexpr int NBS = MX || Q4 ? 0 : dn_nbs<DENSE, SMALL, DDS>();
-  constexpr bool SC = !DENSE && SMALL && !MX && !Q4;
-  static_assert(!DDS || (!DENSE && !SMALL), "DDS: large routed tiles");
+  constexpr int NBS = MX || Q4 ? 0 : dn_nbs<SMALL, DDS>();
+  constexpr bool SC = SMALL && !MX && !Q4;
+  static_assert(!DDS || !SMALL, "DDS: large routed tiles");
   __shared__ DnLds<RING, NBS, SC> s;
   int e, rt, pos0, n;
-  if (!tile_of<DENSE, SMALL>(L.d_model / 256, T, tiles, stiles, ntiles, counts, offsets, e, rt, pos0, n)) return;
-  if (!DENSE && (int)threadIdx.x < kTT) s.slot[threadIdx.x] = perm[pos0 + min((int)threadIdx.x, n - 1)];
+  if (!tile_of<SMALL>(L.d_model / 256, tiles, stiles, ntiles, counts, offsets, e, rt, pos0, n)) return;
+  if ((int)threadIdx.x < kTT) s.slot[threadIdx.x] = perm[pos0 + min((int)threadIdx.x, n - 1)];
   if constexpr (NBS > 0) {
     // scales of rows rt*256 .. +255, blocks 0 .. ns-1
     const int nb = L.d_ff / QK, ns = min(nb, NBS);
@@ -676,8 +580,8 @@ __attribute__((amdgpu_waves_per_eu(DENSE ? 1 : 2))) void k_pf_down(
     }
   }
   __syncthreads();
-#define DS4_DN(NF) down_tile<DENSE, RING, NF, NBS, SC, DDS, MX, Q4>(L, s, hin, e, rt, pos0, n, yp, y)
-  DS4_NF_SWITCH(n, SMALL, DENSE, DS4_DN)
+#define DS4_DN(NF) down_tile<RING, NF, NBS, SC, DDS, MX, Q4>(L, s, hin, e, rt, pos0, n, yp)
+  DS4_NF_SWITCH(n, SMALL, DS4_DN)
 #undef DS4_DN
 }
 
@@ -708,7 +612,6 @@ hipError_t launch_prefill_experts(const Fwd& f) {
   const int d = L.d_model, E = L.n_experts, k = L.top_k;
   const int64_t S = T * k;
   const int64_t maxtiles = (S + kTT - 1) / kTT + E;  // >= the large-tile count; the small list holds <= E
-  const int64_t ttiles = (T + kTT - 1) / kTT;
   auto xh = (const _Float16*)(ws + y.x_hi);
   auto xl = f.lo ? (const _Float16*)(ws + y.x_lo) : nullptr;
   auto tiles = (const int32_t*)(ws + y.tiles);
@@ -722,53 +625,49 @@ hipError_t launch_prefill_experts(const Fwd& f) {
   auto hw16 = (_Float16*)(ws + y.hw16);
   auto yp = (float*)(ws + y.yp);
   const dim3 blk(kGW * 64);
-  const int gr = L.d_ff / (32 * gu_waves<false, false>());  // gate/up row slices
-  const dim3 gsh((unsigned)(ttiles * (L.d_ff_shared / 128))), gsd((unsigned)(ttiles * (d / 256)));
+  const int gr = L.d_ff / (32 * kGuWaves);  // gate/up row slices
   const dim3 ggu((unsigned)(maxtiles * gr)), ggs((unsigned)(E * gr));
   const dim3 gdn((unsigned)(maxtiles * (d / 256))), gds((unsigned)(E * (d / 256)));
   const bool mx = L.expert_fmt == DS4MOE_EXPERTS_MXFP4, q4 = L.expert_fmt == DS4MOE_EXPERTS_Q4K;
-#define DS4_GU_LAUNCH(LO, DENSE, SMALL, MX, Q4, grid, out)                                                       \
-  DS4_LAUNCH((k_pf_gateup<LO, DENSE, SMALL, MX, Q4>), grid, blk, 0, f.st, L, T, xh, xl, tiles, stiles, ntiles, \
-             counts, offsets, perm, w, out)
-#define DS4_GU_ROUTED(LO)                                              \
-  do {                                                                 \
-    if (mx) {                                                          \
-      DS4_GU_LAUNCH(LO, false, false, true, false, ggu, hw16);         \
-      DS4_GU_LAUNCH(LO, false, true, true, false, ggs, hw16);          \
-    } else if (q4) {                                                   \
-      DS4_GU_LAUNCH(LO, false, false, false, true, ggu, hw16);         \
-      DS4_GU_LAUNCH(LO, false, true, false, true, ggs, hw16);          \
-    } else {                                                           \
-      DS4_GU_LAUNCH(LO, false, false, false, false, ggu, hw16);        \
-      DS4_GU_LAUNCH(LO, false, true, false, false, ggs, hw16);         \
-    }                                                                  \
+#define DS4_GU_LAUNCH(LO, SMALL, MX, Q4, grid)                                                                   \
+  DS4_LAUNCH((k_pf_gateup<LO, SMALL, MX, Q4>), grid, blk, 0, f.st, L, xh, xl, tiles, stiles, ntiles, counts, offsets, \
+             perm, w, hw16)
+#define DS4_GU_ROUTED(LO)                                \
+  do {                                                   \
+    if (mx) {                                            \
+      DS4_GU_LAUNCH(LO, false, true, false, ggu);        \
+      DS4_GU_LAUNCH(LO, true, true, false, ggs);         \
+    } else if (q4) {                                     \
+      DS4_GU_LAUNCH(LO, false, false, true, ggu);        \
+      DS4_GU_LAUNCH(LO, true, false, true, ggs);         \
+    } else {                                             \
+      DS4_GU_LAUNCH(LO, false, false, false, ggu);       \
+      DS4_GU_LAUNCH(LO, true, false, false, ggs);        \
+    }                                                    \
   } while (0)
-  if (f.lo) {
-    DS4_GU_LAUNCH(true, true, false, false, false, gsh, hs16);
-    DS4_GU_ROUTED(true);
-  } else {
-    DS4_GU_LAUNCH(false, true, false, false, false, gsh, hs16);
-    DS4_GU_ROUTED(false);
-  }
+  // the shared expert first (dense GEMMs; its down product writes y, which
+  // the combine completes)
+  hipError_t e = launch_prefill_shared(L, T, f.lo, xh, xl, hs16, f.y, f.st);
+  if (e != hipSuccess) return e;
+  if (f.lo) DS4_GU_ROUTED(true);
+  else DS4_GU_ROUTED(false);
 #undef DS4_GU_ROUTED
 #undef DS4_GU_LAUNCH
-#define DS4_DN_LAUNCH(DENSE, SMALL, DDS, MX, Q4, grid, hin)                                                          \
-  DS4_LAUNCH((k_pf_down<DENSE, SMALL, DDS, MX, Q4>), grid, blk, 0, f.st, L, T, tiles, stiles, ntiles, counts, offsets, \
-             perm, hin, yp, f.y)
+#define DS4_DN_LAUNCH(SMALL, DDS, MX, Q4, grid)                                                                    \
+  DS4_LAUNCH((k_pf_down<SMALL, DDS, MX, Q4>), grid, blk, 0, f.st, L, tiles, stiles, ntiles, counts, offsets, perm, \
+             hw16, yp)
   if (mx) {
-    DS4_DN_LAUNCH(false, false, false, true, false, gdn, hw16);
-    DS4_DN_LAUNCH(false, true, false, true, false, gds, hw16);
+    DS4_DN_LAUNCH(false, false, true, false, gdn);
+    DS4_DN_LAUNCH(true, false, true, false, gds);
   } else if (q4) {
-    DS4_DN_LAUNCH(false, false, false, false, true, gdn, hw16);
-    DS4_DN_LAUNCH(false, true, false, false, true, gds, hw16);
+    DS4_DN_LAUNCH(false, false, false, true, gdn);
+    DS4_DN_LAUNCH(true, false, false, true, gds);
   } else {
-    if (L.d_ff / QK <= kDnStagedMax) DS4_DN_LAUNCH(false, false, true, false, false, gdn, hw16);
-    else DS4_DN_LAUNCH(false, false, false, false, false, gdn, hw16);
-    DS4_DN_LAUNCH(false, true, false, false, false, gds, hw16);
+    if (L.d_ff / QK <= kDnStagedMax) DS4_DN_LAUNCH(false, true, false, false, gdn);
+    else DS4_DN_LAUNCH(false, false, false, false, gdn);
+    DS4_DN_LAUNCH(true, false, false, false, gds);
   }
 #undef DS4_DN_LAUNCH
-  DS4_LAUNCH((k_pf_down<true, false, false>), gsd, blk, 0, f.st, L, T, tiles, stiles, ntiles, counts, offsets, perm,
-             hs16, yp, f.y);
   const int64_t n4 = T * d / 4;
   const int cb = (int)std::min<int64_t>((n4 + 255) / 256, 8192);
   DS4_LAUNCH(k_combine, dim3(cb), dim3(256), 0, f.st, T, d, k, yp, f.y);
