@@ -47,6 +47,10 @@ WsLayout ws_layout(const ds4moe_layer& L, int64_t T, int mode) {
   y.ntiles = take(2 * 4);
   const int64_t Tdec = std::min<int64_t>(Tg, kDecodeGroup);
   y.plog = take((d / 128) * Tdec * E * 4);  // one partial per 256 (routing only) or 128 inputs (forward)
+  if (mode != DS4MOE_MODE_DECODE) {
+    const int parts = router_splits(Tg, (int)E, (int)d);
+    y.rpart = take(parts > 1 ? (size_t)parts * Tg * E * 4 : 0);
+  }
   if (mode != DS4MOE_MODE_ROUTE) {  // expert buffers (not needed for routing alone)
     y.hs16 = take(Tg * fs * 2);
     y.hw16 = take(S * f * 2);

@@ -1,7 +1,11 @@
-// Dense fp16 GEMMs of the shared expert in prefill (the expert is F16 and
-// always on: DS4 (DwarfStar 4) wiki note, "Key Techniques"):
+// Dense fp16 GEMMs of prefill and routing: the shared expert (F16, always
+// on) and the F16 router (DS4 (DwarfStar 4) wiki note, "Key Techniques"):
 //   k_pf_shared_gateup   hs16[t][r] = silu(Wsg[r] . x[t]) * (Wsu[r] . x[t])   (binary16)
 //   k_pf_shared_down     y[t][o]    = Wsd[o] . hs16[t]                          (fp32)
+//   k_router_gemm        logits[t][e] = Wr[e] . x[t] + bias[e]                 (fp32)
+//                        (K split into parts when few tiles would fill the
+//                        chip: fp32 partials, then k_router_reduce adds them
+//                        in a fixed order)
 // C[t][n] = sum_k A[t][k] B[n][k] with A the token rows (binary16; an fp32
 // input as a hi + lo pair, both contracted) and B the weight rows.
 //
@@ -15,6 +19,8 @@
 // 8 lanes.  Blocks take (row tile, token tile) items, row tile major, dealt
 // so that each XCD runs a contiguous range: the blocks that share a weight
 // tile share an L2.
+#include <algorithm>
+
 #include "common.h"
 #include "internal.h"
 #include "ring.h"
@@ -117,6 +123,17 @@ __device__ inline bool item_of(int ntn, int ntt, int& nt, int& tt) {
 
 }  // namespace dense
 
+// K parts of the router GEMM: enough for about 256 blocks, each part a whole
+// number of 64-input chunks.
+int router_splits(int64_t T, int E, int d) {
+  // (callers may size a workspace before rejecting T or E: at least one tile)
+  const int64_t tiles =
+      std::max<int64_t>(1, ((T + dense::kBM - 1) / dense::kBM) * ((E + dense::kBN - 1) / dense::kBN));
+  int s = (int)std::max<int64_t>(1, std::min<int64_t>(256 / tiles, d / dense::kBK));
+  while (s > 1 && (d / dense::kBK) % s) --s;
+  return s;
+}
+
 // Shared gate/up: row tile nt = h-rows nt*128 .. +127 (B rows 0..127 its
 // gate rows, 128..255 its up rows); wave wn owns h-rows 32 wn .. +31 (row
 // fragments: gate 0/1, up 0/1).
@@ -189,6 +206,82 @@ __global__ __launch_bounds__(dense::kW * 64) __attribute__((amdgpu_waves_per_eu(
         for (int j = 0; j < 4; ++j) y[t * d + o0 + 64 * wn + 16 * j + c] = acc[i][j][r];
       }
     }
+}
+
+// Router: block (part p, expert tile nt, token tile tt) over inputs
+// [p d/P, (p+1) d/P); expert rows past E repeat the last one and are not
+// stored.  One part: logits + bias directly; more: partials part[p][t][e].
+template <bool LO>
+__global__ __launch_bounds__(dense::kW * 64) __attribute__((amdgpu_waves_per_eu(2))) void k_router_gemm(
+    const _Float16* __restrict__ xh, const _Float16* __restrict__ xl, int64_t T, int d, int E,
+    const uint16_t* __restrict__ wr, const float* __restrict__ bias, int ntt, int parts, float* __restrict__ part,
+    float* __restrict__ logits) {
+  using namespace dense;
+  __shared__ __align__(16) _Float16 s_ring[ring<LO>() * slot_halves<LO>()];
+  const int ntn = (E + kBN - 1) / kBN;
+  int item;
+  if (!xcd_item(parts * ntn * ntt, item)) return;
+  const int p = item / (ntn * ntt), nt = (item / ntt) % ntn, tt = item % ntt;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave >> 2, wn = wave & 3;
+  const int c = lane & 15, q = lane >> 4;
+  const int kc = d / parts, kb = p * kc;
+  const int64_t t0 = (int64_t)tt * kBM;
+  const int e0 = nt * kBN;
+  auto arow = [&](int r) { return (int64_t)min(t0 + r, T - 1) * d; };
+  auto brow = [&](int r) { return (const _Float16*)wr + (int64_t)min(e0 + r, E - 1) * d + kb; };
+  auto bfrag = [&](int j) { return 64 * wn + 16 * j; };
+  float4_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = float4_t{0.f, 0.f, 0.f, 0.f};
+  gemm<LO>(kc, xh + kb, LO ? xl + kb : nullptr, arow, brow, bfrag, s_ring, acc, wave, lane);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int64_t t = t0 + 64 * wm + 16 * i + 4 * q + r;
+      if (t >= T) continue;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int e = e0 + 64 * wn + 16 * j + c;
+        if (e >= E) continue;
+        if (parts == 1) logits[t * E + e] = acc[i][j][r] + (bias ? bias[e] : 0.0f);
+        else part[((int64_t)p * T + t) * E + e] = acc[i][j][r];
+      }
+    }
+}
+
+// logits[t][e] = sum_p part[p][t][e] (p ascending) + bias[e]
+__global__ __launch_bounds__(256) void k_router_reduce(const float* __restrict__ part, int parts, int64_t T, int E,
+                                                       const float* __restrict__ bias, float* __restrict__ logits) {
+  const int64_t n = T * E;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+    float v = part[i];
+    for (int p = 1; p < parts; ++p) v += part[(int64_t)p * n + i];
+    logits[i] = v + (bias ? bias[i % E] : 0.0f);
+  }
+}
+
+hipError_t launch_router_logits(const ds4moe_layer& L, int64_t T, bool lo, const _Float16* xh, const _Float16* xl,
+                                float* part, float* logits, hipStream_t st) {
+  using namespace dense;
+  const int d = L.d_model, E = L.n_experts;
+  const int ntt = (int)((T + kBM - 1) / kBM), ntn = (E + kBN - 1) / kBN;
+  const int parts = router_splits(T, E, d);
+  const dim3 grid((unsigned)(parts * ntn * ntt)), blk(kW * 64);
+  if (lo)
+    DS4_LAUNCH((k_router_gemm<true>), grid, blk, 0, st, xh, xl, T, d, E, (const uint16_t*)L.router_w, L.router_bias,
+               ntt, parts, part, logits);
+  else
+    DS4_LAUNCH((k_router_gemm<false>), grid, blk, 0, st, xh, xl, T, d, E, (const uint16_t*)L.router_w,
+               L.router_bias, ntt, parts, part, logits);
+  if (parts > 1) {
+    const int64_t n = T * E;
+    const int nb = (int)std::min<int64_t>((n + 255) / 256, 4096);
+    DS4_LAUNCH(k_router_reduce, dim3(nb), dim3(256), 0, st, part, parts, T, E, L.router_bias, logits);
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_prefill_shared(const ds4moe_layer& L, int64_t T, bool lo, const _Float16* xh, const _Float16* xl,

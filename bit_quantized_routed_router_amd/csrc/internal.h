@@ -30,6 +30,7 @@ struct WsLayout {
   size_t hs16, hw16, hsum, yp;        // activations between the kernels
   size_t tiles, stiles, ntiles;       // prefill: (expert, run) work lists of large and small tiles, their counts
   size_t plog;                        // decode: partial router logits [d/128][Tg][E]
+  size_t rpart;                       // prefill/route: router GEMM partials [parts][T][E] (parts > 1 only)
   size_t ctrl;                        // decode: arrival counters (see ctrl_ints)
   size_t gu_part;                     // decode: shared-expert gate and up tiles handed to the tile's last block
   size_t total;
@@ -77,6 +78,11 @@ hipError_t launch_dequant_q4k(const void* packed, int64_t rows, int64_t cols, fl
 hipError_t launch_route(const Fwd& f, bool decode);
 hipError_t launch_decode(const Fwd& f);  // full layer for one group of <= 16 tokens
 hipError_t launch_prefill_experts(const Fwd& f);
+// router logits [T][E] (+ bias) of binary16 activations; part: fp32
+// partials of router_splits(T, E, d) > 1 K parts ([parts][T][E])
+int router_splits(int64_t T, int E, int d);
+hipError_t launch_router_logits(const ds4moe_layer& L, int64_t T, bool lo, const _Float16* xh, const _Float16* xl,
+                                float* part, float* logits, hipStream_t st);
 // prefill shared expert: gate/up into hs16 (binary16), down into y (fp32)
 hipError_t launch_prefill_shared(const ds4moe_layer& L, int64_t T, bool lo, const _Float16* xh, const _Float16* xl,
                                  _Float16* hs16, float* y, hipStream_t st);

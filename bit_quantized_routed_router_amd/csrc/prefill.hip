@@ -32,7 +32,6 @@
 #include "common.h"
 #include "ring.h"
 #include "internal.h"
-#include "tiles.h"
 #include "trace.h"
 
 namespace ds4 {

@@ -48,35 +48,6 @@ __global__ __launch_bounds__(256) void k_convert_x(const void* __restrict__ x, i
   }
 }
 
-// ---------------------------------------------------------------- logits
-// Block: 16 experts x 16 tokens, NW waves splitting K.  logits [T, E] fp32.
-template <int NW, bool LO>
-__global__ __launch_bounds__(NW * 64) void k_router_logits(const uint16_t* __restrict__ wr,
-                                                           const float* __restrict__ bias, int E, int d,
-                                                           const _Float16* __restrict__ xh,
-                                                           const _Float16* __restrict__ xl, int64_t T,
-                                                           float* __restrict__ logits) {
-  __shared__ float red[NW * 64 * 4];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int e0 = blockIdx.x * 16;
-  const int64_t t = (int64_t)blockIdx.y * 16 + (lane & 15);
-  const _Float16* bh = t < T ? xh + t * d : nullptr;
-  const _Float16* bl = (LO && t < T) ? xl + t * d : nullptr;
-  const int arow = min(e0 + (lane & 15), E - 1);
-  int ks0, ks1;
-  split_range(d / 32, NW, wave, ks0, ks1);
-  float4_t acc = {0.f, 0.f, 0.f, 0.f};
-  f16_tile<LO>(wr + (int64_t)arow * d, bh, bl, ks0, ks1, lane, acc);
-  acc = block_reduce_waves<NW>(acc, red, wave, lane);
-  if (wave == 0 && t < T) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int e = e0 + 4 * (lane >> 4) + r;
-      if (e < E) logits[t * E + e] = acc[r] + (bias ? bias[e] : 0.0f);
-    }
-  }
-}
-
 // Decode router: block = 16 experts x one K chunk of CK = 256 inputs (4 waves,
 // two K-steps each); writes partial logits plog[kc][t][e].  Activations are
 // read in their input type and converted in registers; the blocks of expert
@@ -292,11 +263,8 @@ hipError_t launch_route(const Fwd& f, bool decode) {
     const int64_t n8 = f.T * d / 8;
     const int cblocks = (int)std::min<int64_t>((n8 + 255) / 256, 4096);
     DS4_LAUNCH(k_convert_x, dim3(cblocks), dim3(256), 0, f.st, f.x, f.x_dtype, n8, xh, xl);
-    const dim3 lg((E + 15) / 16, (unsigned)((f.T + 15) / 16));
-    if (f.lo)
-      DS4_LAUNCH((k_router_logits<4, true>), lg, dim3(256), 0, f.st, L.router_w, L.router_bias, E, d, xh, xl, f.T, logits);
-    else
-      DS4_LAUNCH((k_router_logits<4, false>), lg, dim3(256), 0, f.st, L.router_w, L.router_bias, E, d, xh, xl, f.T, logits);
+    const hipError_t e = launch_router_logits(L, f.T, f.lo, xh, xl, (float*)(ws + y.rpart), logits, f.st);
+    if (e != hipSuccess) return e;
     DS4_LAUNCH(k_topk_rows, dim3((unsigned)((f.T + 3) / 4)), dim3(256), 0, f.st, logits, E, k, f.T, idx, w,
                        f.idx_out, f.w_out);
     DS4_LAUNCH(k_count_experts, dim3(E), dim3(256), 0, f.st, idx, f.T * k, counts);
