@@ -73,11 +73,16 @@ inline constexpr GridLevels kGridLevels = make_grid_levels();
 //                7-bit sign code c; element 7's sign is the parity of c
 //   imag[e][k] : integer magnitudes for the quantizer's search
 //   isq[e]     : sum_k 4096 * m_ek^2
+//   mag8[e][w] : byte k of word w = high byte of binary16 m_{4w+k} (its low
+//                byte is zero for m in {1, 3, 5})
+//   sgn8[c][w] : byte k of word w = 0x80 if element 4w+k is negative
 struct GridTables {
   uint32_t mag[256][4];
   uint32_t sgn[128][4];
   int32_t imag[256][8];
   int32_t isq[256];
+  uint32_t mag8[256][2];
+  uint32_t sgn8[128][2];
 };
 
 constexpr uint32_t f16_of_small_odd(int m) {  // 1 -> 0x3C00, 3 -> 0x4200, 5 -> 0x4500
@@ -96,6 +101,7 @@ constexpr GridTables make_grid_tables() {
     t.isq[e] = sq;
     for (int p = 0; p < 4; ++p)
       t.mag[e][p] = f16_of_small_odd(t.imag[e][2 * p]) | (f16_of_small_odd(t.imag[e][2 * p + 1]) << 16);
+    for (int k = 0; k < 8; ++k) t.mag8[e][k >> 2] |= (f16_of_small_odd(t.imag[e][k]) >> 8) << (8 * (k & 3));
   }
   for (int c = 0; c < 128; ++c) {
     int par = 0;
@@ -105,6 +111,7 @@ constexpr GridTables make_grid_tables() {
       uint32_t n0 = (uint32_t)((c >> k0) & 1);
       uint32_t n1 = k1 < 7 ? (uint32_t)((c >> k1) & 1) : (uint32_t)par;
       t.sgn[c][p] = (n0 << 15) | (n1 << 31);
+      t.sgn8[c][p >> 1] |= ((n0 << 7) | (n1 << 15)) << (16 * (p & 1));
     }
   }
   return t;

@@ -49,38 +49,42 @@ constexpr int kChunk = kTT * kKC;  // halves per staged chunk of 128 rows (32 KB
 constexpr int ring_halves(bool small) { return small ? kChunk : 2 * kChunk; }
 
 // Ring slots of a tile: as many as the activation ring holds (R * 16 NF
-// rows of 128 inputs) and the 6-bit load counter can track (R - 1 batches of
+// rows of KC inputs) and the 6-bit load counter can track (R - 1 batches of
 // `loads` vector-memory instructions in flight, <= 63), at most 6.
 // Small tiles have little work per chunk, so they need the deepest prefetch.
-constexpr int ring_depth(int nf, int loads, bool lo, int ring, int rmax = 6) {
+constexpr int ring_depth(int nf, int loads, bool lo, int ring, int rmax = 6, int kc = kKC) {
   int r = lo ? 2 : rmax;
-  while (r > 2 && (r * nf * 16 * kKC > ring || (r - 1) * loads > 63)) --r;
+  while (r > 2 && (r * nf * 16 * kc > ring || (r - 1) * loads > 63)) --r;
   return r;
 }
 
-// Copy instructions per wave and chunk for 16 NF rows (4 NF groups of 4 rows)
-// over NW waves; every wave issues the same number.
-constexpr int dma_per_wave(int nf, int nw) { return (4 * nf + nw - 1) / nw; }
+// Copy instructions per wave and chunk for 16 NF rows of KC inputs (one
+// instruction moves 1 KB: 512 / KC rows) over NW waves; every wave issues the
+// same number.
+constexpr int dma_groups(int nf, int kc = kKC) { return nf * 16 * kc / 512; }
+constexpr int dma_per_wave(int nf, int nw, int kc = kKC) { return (dma_groups(nf, kc) + nw - 1) / nw; }
 
-// One 128-input chunk of the tile's first 16 NF activation rows into a
-// swizzled LDS buffer: wave instruction m moves rows 4g .. 4g+3 (g = wave + NW m), lane l
-// writing physical piece l & 15 of row 4g + l/16, which holds logical piece
-// (l & 15) ^ (row & 15).  row_of(r): element offset of tile row r from src
-// (src is the same for the whole block, offsets fit 32 bits).
-template <bool LO, int NF, int NW, typename RowOf>
+// One KC-input chunk of the tile's first 16 NF activation rows into a
+// swizzled LDS buffer: wave instruction m moves the P = 512 / KC rows of
+// group g = wave + NW m, lane l writing physical piece l % (KC / 8) of row
+// P g + l / (KC / 8), which holds logical piece (l % (KC / 8)) ^ (row & 15).
+// row_of(r): element offset of tile row r from src (src is the same for the
+// whole block, offsets fit 32 bits).
+template <bool LO, int NF, int NW, int KC = kKC, typename RowOf>
 __device__ inline void stage_rows(const _Float16* __restrict__ src, const _Float16* __restrict__ src_lo, RowOf row_of,
                                   int ch, _Float16* dh, _Float16* dl, int wave, int lane) {
+  constexpr int kPieces = KC / 8, kRowsPer = 64 / kPieces;
 #pragma unroll
-  for (int m = 0; m < dma_per_wave(NF, NW); ++m) {  // 4 NF groups of 4 rows dealt to NW waves
-    const int g = min(wave + NW * m, 4 * NF - 1);   // a spare slot repeats the last group (same bytes)
-    const int r = 4 * g + (lane >> 4);
-    const int u = (lane & 15) ^ (r & 15);
-    const uint32_t off = 2u * ((uint32_t)row_of(r) + (uint32_t)(ch * kKC + 8 * u));
+  for (int m = 0; m < dma_per_wave(NF, NW, KC); ++m) {  // groups dealt to NW waves
+    const int g = min(wave + NW * m, dma_groups(NF, KC) - 1);  // a spare slot repeats the last group (same bytes)
+    const int r = kRowsPer * g + lane / kPieces;
+    const int u = (lane % kPieces) ^ (r & 15);
+    const uint32_t off = 2u * ((uint32_t)row_of(r) + (uint32_t)(ch * KC + 8 * u));
     __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)((const char*)src + off),
-                                     (__attribute__((address_space(3))) void*)(dh + g * 4 * kKC), 16, 0, 0);
+                                     (__attribute__((address_space(3))) void*)(dh + g * kRowsPer * KC), 16, 0, 0);
     if (LO)
       __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)((const char*)src_lo + off),
-                                       (__attribute__((address_space(3))) void*)(dl + g * 4 * kKC), 16, 0, 0);
+                                       (__attribute__((address_space(3))) void*)(dl + g * kRowsPer * KC), 16, 0, 0);
   }
 }
 
@@ -89,26 +93,33 @@ __device__ inline T ld_at(const void* base, uint32_t byte_off) {
   return *(const T*)((const char*)base + byte_off);
 }
 
-// A fragment of slot fragment i at step j: row 16i + c, inputs 32q + 8j .. +7.
+// A fragment of slot fragment i at step j: row 16i + c, inputs (KC / 4) q + 8j .. +7.
+template <int KC = kKC>
 __device__ inline half8_t slot_frag(const _Float16* buf, int i, int c, int q, int j) {
-  return *(const half8_t*)(buf + (16 * i + c) * kKC + 8 * ((4 * q + j) ^ c));
+  return *(const half8_t*)(buf + (16 * i + c) * KC + 8 * (((KC / 32) * q + j) ^ c));
 }
 
 // CB2 group j of a sub-block (index word idxw, aux word aux) as binary16
-// sign * m * D, with D = binary16(d * (2s+1)) in both halves of D2.  mag/sgn
-// point at this lane's copy of the tables, whose entries are TC copies apart.
+// sign * m * D, with D = binary16(d * (2s+1)) in both halves of D2.  The
+// tables hold one byte per element (the high byte of binary16 sign * m, whose
+// low byte is zero), 8 bytes an entry: the sign bytes are XORed in, then a
+// byte permute widens two elements to a binary16 pair (low bytes zero) for
+// the scale multiply.  mag/sgn point at this lane's copy of the tables, whose
+// entries are TC copies apart.
 template <int TC>
 __device__ inline half8_t cb2_frag_scaled(uint32_t idxw, uint32_t aux, int j, const uint32_t* mag,
                                           const uint32_t* sgn, half2_t D2) {
   const uint32_t idx = (idxw >> (8 * j)) & 0xFFu;
   const uint32_t code = (aux >> (7 * j)) & 0x7Fu;
-  const u32x4_t m = *(const u32x4_t*)(mag + 4 * TC * idx);
-  const u32x4_t s = *(const u32x4_t*)(sgn + 4 * TC * code);
+  const u32x2_t m = *(const u32x2_t*)(mag + 2 * TC * idx);
+  const u32x2_t s = *(const u32x2_t*)(sgn + 2 * TC * code);
+  const uint32_t b0 = m.x ^ s.x, b1 = m.y ^ s.y;
+  // byte k of b -> high byte of a half: selector 0x0C yields a zero byte
   u32x4_t r;
-  r.x = as_u32(as_half2(m.x ^ s.x) * D2);
-  r.y = as_u32(as_half2(m.y ^ s.y) * D2);
-  r.z = as_u32(as_half2(m.z ^ s.z) * D2);
-  r.w = as_u32(as_half2(m.w ^ s.w) * D2);
+  r.x = as_u32(as_half2(__builtin_amdgcn_perm(0u, b0, 0x010C000Cu)) * D2);
+  r.y = as_u32(as_half2(__builtin_amdgcn_perm(0u, b0, 0x030C020Cu)) * D2);
+  r.z = as_u32(as_half2(__builtin_amdgcn_perm(0u, b1, 0x010C000Cu)) * D2);
+  r.w = as_u32(as_half2(__builtin_amdgcn_perm(0u, b1, 0x030C020Cu)) * D2);
   return as_half8(r);
 }
 
@@ -118,17 +129,15 @@ __device__ inline half2_t h2splat(float v) {
   return (half2_t){h, h};
 }
 
-// Codebook tables in LDS: TC interleaved copies of each 16-byte entry, lane l
-// reading copy l % TC.  A 16-byte read serves 8 lanes per LDS cycle, so with
-// TC = 8 those lanes always hit 8 different 16-byte bank groups whatever
-// entries they look up (one copy, random indices: about 2-way conflicts).
+// Codebook tables in LDS (byte forms, 8 bytes an entry): TC interleaved
+// copies of each entry, lane l reading copy l % TC.
 template <int TC>
 struct CbTables {
-  uint32_t mag[256 * TC * 4];
-  uint32_t sgn[128 * TC * 4];
+  uint32_t mag[256 * TC * 2];
+  uint32_t sgn[128 * TC * 2];
   __device__ inline void stage(const GridTables& t) {
-    for (int i = threadIdx.x; i < 256 * TC * 4; i += blockDim.x) mag[i] = t.mag[i / (TC * 4)][i % 4];
-    for (int i = threadIdx.x; i < 128 * TC * 4; i += blockDim.x) sgn[i] = t.sgn[i / (TC * 4)][i % 4];
+    for (int i = threadIdx.x; i < 256 * TC * 2; i += blockDim.x) mag[i] = t.mag8[i / (TC * 2)][i % 2];
+    for (int i = threadIdx.x; i < 128 * TC * 2; i += blockDim.x) sgn[i] = t.sgn8[i / (TC * 2)][i % 2];
   }
 };
 
@@ -148,18 +157,19 @@ struct GuLds {
 template <bool MX = false, bool Q4 = false>
 constexpr int gu_nbs() { return MX || Q4 ? 0 : 16; }
 
-// Weights of one 128-input chunk for a lane's four fragments.  CB2: the lane's sub-block (8 bytes) and its block's d.
+// Weights of one 128-input chunk for a lane's four fragments.  CB2: the lane's sub-block (8 bytes) and its block's d;
+// with WIDE, chunks of 256 inputs (one block per row): the lane's two sub-blocks (16 bytes, in mw).
 // kLoads counts the vector-memory loads of a chunk when every scale comes from LDS; kMaxLoads when they are all read
 // from memory (blocks past the staged ones).
 // MXFP4: the lane's 32 inputs of the chunk are one MX block, 16 code bytes and
 // one scale byte per fragment.
 // Q4K (Q4): the lane's 32 inputs are one sub-block, 16 code bytes, plus its
 // super-block's three scale words and (d, dmin) word per fragment.
-template <bool MX = false, bool Q4 = false>
+template <bool MX = false, bool Q4 = false, bool WIDE = false>
 struct GuW {
-  u32x2_t cw[MX || Q4 ? 1 : 4];
+  u32x2_t cw[MX || Q4 || WIDE ? 1 : 4];
   uint32_t dv[4];
-  u32x4_t mw[MX || Q4 ? 4 : 1];
+  u32x4_t mw[MX || Q4 || WIDE ? 4 : 1];
   u32x3_t qs[Q4 ? 4 : 1];  // Q4K: the super-block's three scale words (one 12-byte load)
   int jq;  // Q4K: the lane's sub-block within its super-block (set at issue)
   static constexpr int kLoads = Q4 ? 12 : (MX ? 8 : 4);
@@ -171,14 +181,17 @@ struct GuW {
 
 // Gate/up of one work tile (up to 128 slots) for a 128-row slice of h, NF
 // slot fragments, routed expert e (CB2 weights, or MXFP4 with MX, Q4K with
-// Q4; routing weights s.w).
-template <bool LO, int NW, int TC, int RING, int NF, int NBS, bool MX = false, bool Q4 = false>
+// Q4; routing weights s.w), in chunks of KC inputs (CB2: 128 or 256).
+template <bool LO, int NW, int TC, int RING, int NF, int NBS, bool MX = false, bool Q4 = false, int KC = kKC>
 __device__ __attribute__((always_inline)) inline void gateup_tile(const ds4moe_layer& L, GuLds<LO, TC, RING, NBS>& s,
                                                                   const _Float16* __restrict__ xh,
                                                                   const _Float16* __restrict__ xl, int e, int rt,
                                                                   int pos0, int n, _Float16* __restrict__ hout) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, c = lane & 15, q = lane >> 4;
-  const int d = L.d_model, fd = L.d_ff, nb = d / QK, nch = d / kKC;
+  constexpr bool WIDE = KC == 2 * kKC;  // CB2, one block per row and chunk
+  static_assert(KC == kKC || (WIDE && !MX && !Q4), "256-input chunks: CB2 only");
+  using WT = GuW<MX, Q4, WIDE>;
+  const int d = L.d_model, fd = L.d_ff, nb = d / QK, nch = d / KC;
   const size_t mb = (size_t)fd * nb;
   const size_t mat_bytes = Q4 ? mb * 144 : (MX ? (size_t)fd * d * 17 / 32 : mb * 66);
   const uint8_t* gb = (const uint8_t*)L.gate + (size_t)e * mat_bytes;
@@ -193,10 +206,17 @@ __device__ __attribute__((always_inline)) inline void gateup_tile(const ds4moe_l
   uint32_t rowu[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) rowu[h] = (uint32_t)((hr0 + 16 * h + c) * nb);
-  auto load_w = [&](int ch, GuW<MX, Q4>& W) {
+  auto load_w = [&](int ch, WT& W) {
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
-      if constexpr (Q4) {  // row hr0 + 16 (f & 1) + c, sub-block 4 (ch & 1) + q of super-block ch / 2
+      if constexpr (WIDE) {  // block ch of the row: sub-blocks 2q, 2q + 1
+        const uint32_t blk = rowu[f & 1] + (uint32_t)ch;
+        W.mw[f] = ld_at<u32x4_t>(f < 2 ? gb : ub, blk * 64u + 16u * (uint32_t)q);
+        if (NBS > 0 && ch < NBS)
+          W.dv[f] = s.dsc[((f >> 1) * 128 + 32 * wave + 16 * (f & 1) + c) * NBS + ch];
+        else
+          W.dv[f] = ld_at<uint16_t>(f < 2 ? gd : ud, blk * 2u);
+      } else if constexpr (Q4) {  // row hr0 + 16 (f & 1) + c, sub-block 4 (ch & 1) + q of super-block ch / 2
         const uint32_t r = (uint32_t)(hr0 + 16 * (f & 1) + c), blk = r * (uint32_t)nb + (uint32_t)(ch >> 1);
         W.mw[f] = ld_at<u32x4_t>(f < 2 ? gb : ub, blk * 128u + 16u * (uint32_t)(4 * (ch & 1) + q));
         W.qs[f] = ld_at<u32x3_a4_t>(f < 2 ? gd : ud, blk * 12u);
@@ -225,17 +245,18 @@ __device__ __attribute__((always_inline)) inline void gateup_tile(const ds4moe_l
 
   // Loads per chunk and lane.  The ring depth keeps the largest count within the load counter; the waits use the
   // smallest, which is exact when every scale is staged and waits longer than needed otherwise.
-  constexpr int kBatch = dma_per_wave(NF, NW) * (LO ? 2 : 1) + GuW<MX, Q4>::kLoads;
-  constexpr int R = ring_depth(NF, dma_per_wave(NF, NW) * (LO ? 2 : 1) + GuW<MX, Q4>::kRingLoads, LO, RING);
-  constexpr int kSlot = NF * 16 * kKC;  // halves per ring slot
+  constexpr int kDma = dma_per_wave(NF, NW, KC) * (LO ? 2 : 1);
+  constexpr int kBatch = kDma + WT::kLoads;
+  constexpr int R = ring_depth(NF, kDma + WT::kRingLoads, LO, RING, 6, KC);
+  constexpr int kSlot = NF * 16 * KC;  // halves per ring slot
   static_assert(R * kSlot <= RING, "ring slots exceed the staging buffer");
-  GuW<MX, Q4> W[R];
+  WT W[R];
   auto issue = [&](int ch, int u) {
-    stage_rows<LO, NF, NW>(xh, xl, rows, ch, s.xh + u * kSlot, s.xl + (LO ? u * kSlot : 0), wave, lane);
+    stage_rows<LO, NF, NW, KC>(xh, xl, rows, ch, s.xh + u * kSlot, s.xl + (LO ? u * kSlot : 0), wave, lane);
     load_w(ch, W[u]);
   };
-  const uint32_t* tmag = s.tab.mag + 4 * (lane % TC);
-  const uint32_t* tsgn = s.tab.sgn + 4 * (lane % TC);
+  const uint32_t* tmag = s.tab.mag + 2 * (lane % TC);
+  const uint32_t* tsgn = s.tab.sgn + 2 * (lane % TC);
   auto compute = [&](int u) {
     half2_t D2[4];
     float XS[4];  // MXFP4 block scales
@@ -247,17 +268,21 @@ __device__ __attribute__((always_inline)) inline void gateup_tile(const ds4moe_l
     } else if constexpr (MX) {
 #pragma unroll
       for (int f = 0; f < 4; ++f) XS[f] = e8m0_f32(W[u].dv[f] & 0xFFu);
-    } else {
+    } else if constexpr (!WIDE) {
 #pragma unroll
       for (int f = 0; f < 4; ++f) D2[f] = h2splat(f16f(W[u].dv[f]) * (float)(2 * (W[u].cw[f].y >> 28) + 1));
     }
     const _Float16* bh = s.xh + u * kSlot;
     const _Float16* bl = s.xl + (LO ? u * kSlot : 0);
+    // step j: lane group q covers inputs (KC / 4) q + 8j .. +7 of the chunk
     auto step = [&](int j) {
       half8_t wf[4];
 #pragma unroll
       for (int f = 0; f < 4; ++f) {
-        if constexpr (Q4)
+        if constexpr (WIDE)  // sub-block 2q + j / 4: words (x, y) or (z, w)
+          wf[f] = cb2_frag_scaled<TC>(j < 4 ? W[u].mw[f].x : W[u].mw[f].z, j < 4 ? W[u].mw[f].y : W[u].mw[f].w,
+                                      j & 3, tmag, tsgn, D2[f]);
+        else if constexpr (Q4)
           wf[f] = q4k_frag(W[u].mw[f][j], QD[f], QN[f]);
         else if constexpr (MX)
           wf[f] = mx4_frag(W[u].mw[f][j], XS[f]);
@@ -266,18 +291,29 @@ __device__ __attribute__((always_inline)) inline void gateup_tile(const ds4moe_l
       }
 #pragma unroll
       for (int i = 0; i < NF; ++i) {
-        const half8_t a = slot_frag(bh, i, c, q, j);
+        const half8_t a = slot_frag<KC>(bh, i, c, q, j);
 #pragma unroll
         for (int f = 0; f < 4; ++f) acc[f][i] = mfma16x16x32(a, wf[f], acc[f][i]);
         if (LO) {
-          const half8_t al = slot_frag(bl, i, c, q, j);
+          const half8_t al = slot_frag<KC>(bl, i, c, q, j);
 #pragma unroll
           for (int f = 0; f < 4; ++f) acc[f][i] = mfma16x16x32(al, wf[f], acc[f][i]);
         }
       }
     };
+    if constexpr (WIDE) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) step(j);
+      for (int h = 0; h < 2; ++h) {  // sub-block 2q + h: its scale, then its four steps
+#pragma unroll
+        for (int f = 0; f < 4; ++f)
+          D2[f] = h2splat(f16f(W[u].dv[f]) * (float)(2 * ((h ? W[u].mw[f].w : W[u].mw[f].y) >> 28) + 1));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) step(4 * h + j);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) step(j);
+    }
   };
   ring_loop<R, kBatch>(nch, issue, compute);
 #pragma unroll
@@ -342,6 +378,9 @@ __attribute__((amdgpu_waves_per_eu(LO ? 1 : 2))) void k_pf_gateup(
     const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets, const int32_t* __restrict__ perm,
     const float* __restrict__ topk_w, _Float16* __restrict__ hout) {
   constexpr int NW = kGuWaves, TC = kGuCopies, RING = ring_halves(SMALL);
+  // small CB2 tiles: 256-input chunks, so that a lane's codes of a row are one
+  // 16-byte load (a wave instruction reads 16 rows x 64 bytes)
+  constexpr int kGuKC = SMALL && !MX && !Q4 ? 2 * kKC : kKC;
   constexpr int NBS = gu_nbs<MX, Q4>();
   static_assert(NW == 4, "the staged scales cover 4 waves x 32 rows");
   __shared__ GuLds<LO, TC, RING, NBS> s;
@@ -366,7 +405,7 @@ __attribute__((amdgpu_waves_per_eu(LO ? 1 : 2))) void k_pf_gateup(
     s.w[threadIdx.x] = topk_w[slot];
   }
   __syncthreads();
-#define DS4_GU(NF) gateup_tile<LO, NW, TC, RING, NF, NBS, MX, Q4>(L, s, xh, xl, e, rt, pos0, n, hout)
+#define DS4_GU(NF) gateup_tile<LO, NW, TC, RING, NF, NBS, MX, Q4, kGuKC>(L, s, xh, xl, e, rt, pos0, n, hout)
   DS4_NF_SWITCH(n, SMALL, DS4_GU)
 #undef DS4_GU
 }
@@ -394,12 +433,14 @@ constexpr int kDnStagedMax = 8;
 // Down weights of one chunk.  Q2K: the lane's two sub-blocks of codes, the
 // aligned word holding their two scale bytes, the block's d/dmin.  kLoads /
 // kMaxLoads: vector-memory loads of a chunk with the scales staged in LDS /
-// read from memory.
-template <bool SC, bool DD, bool MX = false, bool Q4 = false>
+// read from memory.  WIDE (Q2K, 256-input chunks, one block per row): the
+// lane's four sub-blocks of codes (16 bytes, in mw) and the word of their
+// four scale bytes.
+template <bool SC, bool DD, bool MX = false, bool Q4 = false, bool WIDE = false>
 struct DnW {
-  u32x2_t cw[MX || Q4 ? 1 : 4];
+  u32x2_t cw[MX || Q4 || WIDE ? 1 : 4];
   uint32_t sc[4], dd[MX ? 1 : 4];
-  u32x4_t mw[MX || Q4 ? 4 : 1];  // MXFP4 / Q4K: the lane's 32 elements (16 code bytes); MXFP4's scale byte in sc
+  u32x4_t mw[MX || Q4 || WIDE ? 4 : 1];  // MXFP4 / Q4K: the lane's 32 elements (16 code bytes); MXFP4's scale byte in sc
   u32x3_t qs[Q4 ? 4 : 1];  // Q4K: scale words (one 12-byte load); (d, dmin) in dd
   int jq;                   // Q4K: the lane's sub-block within its super-block
   static constexpr int kMaxLoads = Q4 ? 12 : (MX ? 8 : 12);
@@ -408,13 +449,16 @@ struct DnW {
 };
 
 // Down product of one work tile for a 256-row slice of the output (Q2K, or
-// MXFP4 with MX, Q4K with Q4): yp[slot] = D_e h.
-template <int RING, int NF, int NBS, bool SC, bool FULL, bool MX = false, bool Q4 = false>
+// MXFP4 with MX, Q4K with Q4): yp[slot] = D_e h, in chunks of KC inputs
+// (Q2K: 128 or 256).
+template <int RING, int NF, int NBS, bool SC, bool FULL, bool MX = false, bool Q4 = false, int KC = kKC>
 __device__ __attribute__((always_inline)) inline void down_tile(const ds4moe_layer& L, DnLds<RING, NBS, SC>& s,
                                                                 const _Float16* __restrict__ hin, int e, int rt,
                                                                 int pos0, int n, float* __restrict__ yp) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, c = lane & 15, q = lane >> 4;
-  const int d = L.d_model, fd = L.d_ff, nb = fd / QK, nch = fd / kKC;
+  constexpr bool WIDE = KC == 2 * kKC;
+  static_assert(KC == kKC || (WIDE && !MX && !Q4), "256-input chunks: Q2K only");
+  const int d = L.d_model, fd = L.d_ff, nb = fd / QK, nch = fd / KC;
   const size_t mb = (size_t)d * nb;
   const size_t mat_bytes = Q4 ? mb * 144 : (MX ? (size_t)d * fd * 17 / 32 : mb * 84);
   const uint8_t* base = (const uint8_t*)L.down + (size_t)e * mat_bytes;
@@ -423,11 +467,23 @@ __device__ __attribute__((always_inline)) inline void down_tile(const ds4moe_lay
   const uint8_t* sup = base + (Q4 ? mb * 140 : mb * 80);
   const int r0 = rt * 256 + 64 * wave;
   const uint32_t row0 = (uint32_t)((r0 + c) * nb);  // fragment f: + 16 f nb
-  using WT = DnW<SC, (NBS > 0), MX, Q4>;
+  using WT = DnW<SC, (NBS > 0), MX, Q4, WIDE>;
   auto load_w = [&](int ch, WT& W) {
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
-      if constexpr (Q4) {  // row r0 + 16 f + c, sub-block 4 (ch & 1) + q of super-block ch / 2
+      if constexpr (WIDE) {  // block ch of row r0 + 16 f + c: sub-blocks 4q .. 4q + 3
+        const uint32_t blk = row0 + (uint32_t)(16 * f * nb + ch);
+        W.mw[f] = ld_at<u32x4_t>(base, blk * 64u + 16u * (uint32_t)q);
+        const int lr = 64 * wave + 16 * f + c;
+        if (SC && ch < NBS)
+          W.sc[f] = s.sc[lr * (4 * NBS + 1) + 4 * ch + q];
+        else
+          W.sc[f] = ld_at<uint32_t>(sub, blk * 16u + 4u * (uint32_t)q);
+        if (NBS > 0 && (FULL || ch < NBS))
+          W.dd[f] = s.dd[lr * (NBS + 1) + ch];
+        else
+          W.dd[f] = ld_at<uint32_t>(sup, blk * 4u);
+      } else if constexpr (Q4) {  // row r0 + 16 f + c, sub-block 4 (ch & 1) + q of super-block ch / 2
         const uint32_t r = (uint32_t)(r0 + 16 * f + c), blk = r * (uint32_t)nb + (uint32_t)(ch >> 1);
         W.mw[f] = ld_at<u32x4_t>(base, blk * 128u + 16u * (uint32_t)(4 * (ch & 1) + q));
         W.qs[f] = ld_at<u32x3_a4_t>(sub, blk * 12u);
@@ -461,14 +517,15 @@ __device__ __attribute__((always_inline)) inline void down_tile(const ds4moe_lay
     for (int i = 0; i < NF; ++i) acc[f][i] = (float4_t){0.f, 0.f, 0.f, 0.f};
 
   // As in gate/up: the depth bounds the largest load count, the waits use the smallest.
-  constexpr int kBatch = dma_per_wave(NF, kGW) + WT::kLoads;
-  constexpr int R = ring_depth(NF, dma_per_wave(NF, kGW) + WT::kRingLoads, false, RING,
-                               RING < 2 * kChunk ? 3 : 6);  // small: register budget
-  constexpr int kSlot = NF * 16 * kKC;
+  constexpr int kDma = dma_per_wave(NF, kGW, KC);
+  constexpr int kBatch = kDma + WT::kLoads;
+  constexpr int R = ring_depth(NF, kDma + WT::kRingLoads, false, RING,
+                               RING < 2 * kChunk ? 3 : 6, KC);  // small: register budget
+  constexpr int kSlot = NF * 16 * KC;
   static_assert(R * kSlot <= RING, "ring slots exceed the staging buffer");
   WT W[R];
   auto issue = [&](int ch, int u) {
-    stage_rows<false, NF, kGW>(hbase, nullptr, rows, ch, s.xh + u * kSlot, nullptr, wave, lane);
+    stage_rows<false, NF, kGW, KC>(hbase, nullptr, rows, ch, s.xh + u * kSlot, nullptr, wave, lane);
     load_w(ch, W[u]);
   };
   const half2_t k1024 = {(_Float16)-1024.0f, (_Float16)-1024.0f};
@@ -496,11 +553,13 @@ __device__ __attribute__((always_inline)) inline void down_tile(const ds4moe_lay
       }
       return;
     }
-    auto half_chunk = [&](int h) {  // Q2K: sub-block 2q + h of the chunk feeds steps 2h, 2h+1
+    // Q2K: sub-block h of the lane's chunk piece (2q + h, or 4q + h with WIDE)
+    // feeds steps 2h, 2h+1
+    auto half_chunk = [&](int h) {
       half2_t A2[4], nB2[4];         // binary16 d * s and -(dmin * m) of the sub-block
 #pragma unroll
       for (int f = 0; f < 4; ++f) {
-        const uint32_t sm = (W[u].sc[f] >> (16 * (q & 1) + 8 * h)) & 0xFFu;
+        const uint32_t sm = (W[u].sc[f] >> (WIDE ? 8 * h : 16 * (q & 1) + 8 * h)) & 0xFFu;
         A2[f] = h2splat(f16f(W[u].dd[f]) * (float)(sm & 15u));
         nB2[f] = h2splat(-f16f(W[u].dd[f] >> 16) * (float)(sm >> 4));
       }
@@ -510,7 +569,10 @@ __device__ __attribute__((always_inline)) inline void down_tile(const ds4moe_lay
         half8_t wf[4];
 #pragma unroll
         for (int f = 0; f < 4; ++f) {
-          const uint32_t fld = ((h ? W[u].cw[f].y : W[u].cw[f].x) >> (16 * jj)) & 0xFFFFu;
+          uint32_t word;
+          if constexpr (WIDE) word = W[u].mw[f][h];
+          else word = h ? W[u].cw[f].y : W[u].cw[f].x;
+          const uint32_t fld = (word >> (16 * jj)) & 0xFFFFu;
           uint32_t pr[4];
           q2k_pairs(fld | (fld << 14), pr);
           u32x4_t a;
@@ -521,14 +583,14 @@ __device__ __attribute__((always_inline)) inline void down_tile(const ds4moe_lay
         }
 #pragma unroll
         for (int i = 0; i < NF; ++i) {
-          const half8_t a = slot_frag(bh, i, c, q, j);
+          const half8_t a = slot_frag<KC>(bh, i, c, q, j);
 #pragma unroll
           for (int f = 0; f < 4; ++f) acc[f][i] = mfma16x16x32(a, wf[f], acc[f][i]);
         }
       }
     };
 #pragma unroll
-    for (int h = 0; h < 2; ++h) half_chunk(h);
+    for (int h = 0; h < (WIDE ? 4 : 2); ++h) half_chunk(h);
   };
   ring_loop<R, kBatch>(nch, issue, compute);
 #pragma unroll
@@ -556,6 +618,8 @@ __attribute__((amdgpu_waves_per_eu(2))) void k_pf_down(
   constexpr int NBS = MX || Q4 ? 0 : dn_nbs<SMALL, DDS>();
   constexpr bool SC = SMALL && !MX && !Q4;
   static_assert(!DDS || !SMALL, "DDS: large routed tiles");
+  // small Q2K tiles: 256-input chunks (a lane's codes of a row in one 16-byte load)
+  constexpr int kDnKC = SMALL && !MX && !Q4 ? 2 * kKC : kKC;
   __shared__ DnLds<RING, NBS, SC> s;
   int e, rt, pos0, n;
   if (!tile_of<SMALL>(L.d_model / 256, tiles, stiles, ntiles, counts, offsets, e, rt, pos0, n)) return;
@@ -579,7 +643,7 @@ __attribute__((amdgpu_waves_per_eu(2))) void k_pf_down(
     }
   }
   __syncthreads();
-#define DS4_DN(NF) down_tile<RING, NF, NBS, SC, DDS, MX, Q4>(L, s, hin, e, rt, pos0, n, yp)
+#define DS4_DN(NF) down_tile<RING, NF, NBS, SC, DDS, MX, Q4, kDnKC>(L, s, hin, e, rt, pos0, n, yp)
   DS4_NF_SWITCH(n, SMALL, DS4_DN)
 #undef DS4_DN
 }
