@@ -181,8 +181,13 @@ struct GuW {
 
 // Gate/up of one work tile (up to 128 slots) for a 128-row slice of h, NF
 // slot fragments, routed expert e (CB2 weights, or MXFP4 with MX, Q4K with
-// Q4; routing weights s.w), in chunks of KC inputs (CB2: 128 or 256).
-template <bool LO, int NW, int TC, int RING, int NF, int NBS, bool MX = false, bool Q4 = false, int KC = kKC>
+// Q4; routing weights s.w), in chunks of KC inputs (CB2: 128 or 256).  FS:
+// every block's scale is staged (d_model <= 256 NBS), so the scale reads are
+// LDS reads only; otherwise blocks past the staged ones read theirs from
+// memory (the compiler then forms one flat load over both address spaces,
+// which the LDS waits of the compute also wait for).
+template <bool LO, int NW, int TC, int RING, int NF, int NBS, bool MX = false, bool Q4 = false, int KC = kKC,
+          bool FS = false>
 __device__ __attribute__((always_inline)) inline void gateup_tile(const ds4moe_layer& L, GuLds<LO, TC, RING, NBS>& s,
                                                                   const _Float16* __restrict__ xh,
                                                                   const _Float16* __restrict__ xl, int e, int rt,
@@ -212,7 +217,7 @@ __device__ __attribute__((always_inline)) inline void gateup_tile(const ds4moe_l
       if constexpr (WIDE) {  // block ch of the row: sub-blocks 2q, 2q + 1
         const uint32_t blk = rowu[f & 1] + (uint32_t)ch;
         W.mw[f] = ld_at<u32x4_t>(f < 2 ? gb : ub, blk * 64u + 16u * (uint32_t)q);
-        if (NBS > 0 && ch < NBS)
+        if (NBS > 0 && (FS || ch < NBS))
           W.dv[f] = s.dsc[((f >> 1) * 128 + 32 * wave + 16 * (f & 1) + c) * NBS + ch];
         else
           W.dv[f] = ld_at<uint16_t>(f < 2 ? gd : ud, blk * 2u);
@@ -229,7 +234,7 @@ __device__ __attribute__((always_inline)) inline void gateup_tile(const ds4moe_l
       } else {
         const uint32_t blk = rowu[f & 1] + (uint32_t)(ch >> 1);
         W.cw[f] = ld_at<u32x2_t>(f < 2 ? gb : ub, blk * 64u + (uint32_t)(32 * (ch & 1) + 8 * q));
-        if (NBS > 0 && (ch >> 1) < NBS)
+        if (NBS > 0 && (FS || (ch >> 1) < NBS))
           W.dv[f] = s.dsc[((f >> 1) * 128 + 32 * wave + 16 * (f & 1) + c) * NBS + (ch >> 1)];
         else
           W.dv[f] = ld_at<uint16_t>(f < 2 ? gd : ud, blk * 2u);
@@ -370,7 +375,7 @@ constexpr int kGuCopies = 1;
 
 // SMALL: the small-tile list (at most 32 slots per tile, a smaller ring).
 // MX / Q4: the routed experts are MXFP4 / Q4K.
-template <bool LO, bool SMALL, bool MX = false, bool Q4 = false>
+template <bool LO, bool SMALL, bool MX = false, bool Q4 = false, bool FS = false>
 __global__ __launch_bounds__((kGuWaves * 64))
 __attribute__((amdgpu_waves_per_eu(LO ? 1 : 2))) void k_pf_gateup(
     ds4moe_layer L, const _Float16* __restrict__ xh, const _Float16* __restrict__ xl,
@@ -405,7 +410,7 @@ __attribute__((amdgpu_waves_per_eu(LO ? 1 : 2))) void k_pf_gateup(
     s.w[threadIdx.x] = topk_w[slot];
   }
   __syncthreads();
-#define DS4_GU(NF) gateup_tile<LO, NW, TC, RING, NF, NBS, MX, Q4, kGuKC>(L, s, xh, xl, e, rt, pos0, n, hout)
+#define DS4_GU(NF) gateup_tile<LO, NW, TC, RING, NF, NBS, MX, Q4, kGuKC, FS>(L, s, xh, xl, e, rt, pos0, n, hout)
   DS4_NF_SWITCH(n, SMALL, DS4_GU)
 #undef DS4_GU
 }
@@ -422,7 +427,8 @@ struct DnLds {
   uint32_t dd[NBS ? 256 * (NBS + 1) : 1];
 };
 // Staged Q2K blocks.  Small tiles: d/dmin and the sub-block bytes of the
-// first 8 blocks, later blocks read from memory in the loop.  Large tiles
+// first 8 blocks, later blocks read from memory in the loop (DDS: every
+// block staged, d_ff <= 2048, so the scale reads are LDS reads only).  Large tiles
 // (the ring leaves room for d/dmin only): d/dmin when the whole row fits
 // (d_ff <= 2048, DDS), with no in-loop fallback, which would not fit the
 // register budget.
@@ -475,7 +481,7 @@ __device__ __attribute__((always_inline)) inline void down_tile(const ds4moe_lay
         const uint32_t blk = row0 + (uint32_t)(16 * f * nb + ch);
         W.mw[f] = ld_at<u32x4_t>(base, blk * 64u + 16u * (uint32_t)q);
         const int lr = 64 * wave + 16 * f + c;
-        if (SC && ch < NBS)
+        if (SC && (FULL || ch < NBS))
           W.sc[f] = s.sc[lr * (4 * NBS + 1) + 4 * ch + q];
         else
           W.sc[f] = ld_at<uint32_t>(sub, blk * 16u + 4u * (uint32_t)q);
@@ -497,7 +503,7 @@ __device__ __attribute__((always_inline)) inline void down_tile(const ds4moe_lay
         const uint32_t blk = row0 + (uint32_t)(16 * f * nb + (ch >> 1));
         W.cw[f] = ld_at<u32x2_t>(base, blk * 64u + (uint32_t)(32 * (ch & 1) + 8 * q));
         const int lr = 64 * wave + 16 * f + c;
-        if (SC && (ch >> 1) < NBS)
+        if (SC && (FULL || (ch >> 1) < NBS))
           W.sc[f] = s.sc[lr * (4 * NBS + 1) + 4 * (ch >> 1) + 2 * (ch & 1) + (q >> 1)];
         else
           W.sc[f] = ld_at<uint32_t>(sub, blk * 16u + (uint32_t)(8 * (ch & 1) + 4 * (q >> 1)));
@@ -617,7 +623,6 @@ __attribute__((amdgpu_waves_per_eu(2))) void k_pf_down(
   constexpr int RING = ring_halves(SMALL);
   constexpr int NBS = MX || Q4 ? 0 : dn_nbs<SMALL, DDS>();
   constexpr bool SC = SMALL && !MX && !Q4;
-  static_assert(!DDS || !SMALL, "DDS: large routed tiles");
   // small Q2K tiles: 256-input chunks (a lane's codes of a row in one 16-byte load)
   constexpr int kDnKC = SMALL && !MX && !Q4 ? 2 * kKC : kKC;
   __shared__ DnLds<RING, NBS, SC> s;
@@ -692,9 +697,11 @@ hipError_t launch_prefill_experts(const Fwd& f) {
   const dim3 ggu((unsigned)(maxtiles * gr)), ggs((unsigned)(E * gr));
   const dim3 gdn((unsigned)(maxtiles * (d / 256))), gds((unsigned)(E * (d / 256)));
   const bool mx = L.expert_fmt == DS4MOE_EXPERTS_MXFP4, q4 = L.expert_fmt == DS4MOE_EXPERTS_Q4K;
-#define DS4_GU_LAUNCH(LO, SMALL, MX, Q4, grid)                                                                   \
-  DS4_LAUNCH((k_pf_gateup<LO, SMALL, MX, Q4>), grid, blk, 0, f.st, L, xh, xl, tiles, stiles, ntiles, counts, offsets, \
-             perm, w, hw16)
+  // every scale block staged in LDS (CB2 gate/up: d_model; Q2K down: d_ff)
+  const bool fsg = L.d_model / QK <= gu_nbs(), fsd = L.d_ff / QK <= kDnStagedMax;
+#define DS4_GU_LAUNCH(LO, SMALL, MX, Q4, grid, ...)                                                              \
+  DS4_LAUNCH((k_pf_gateup<LO, SMALL, MX, Q4, ##__VA_ARGS__>), grid, blk, 0, f.st, L, xh, xl, tiles, stiles, ntiles, \
+             counts, offsets, perm, w, hw16)
 #define DS4_GU_ROUTED(LO)                                \
   do {                                                   \
     if (mx) {                                            \
@@ -703,6 +710,9 @@ hipError_t launch_prefill_experts(const Fwd& f) {
     } else if (q4) {                                     \
       DS4_GU_LAUNCH(LO, false, false, true, ggu);        \
       DS4_GU_LAUNCH(LO, true, false, true, ggs);         \
+    } else if (fsg) {                                    \
+      DS4_GU_LAUNCH(LO, false, false, false, ggu, true); \
+      DS4_GU_LAUNCH(LO, true, false, false, ggs, true);  \
     } else {                                             \
       DS4_GU_LAUNCH(LO, false, false, false, ggu);       \
       DS4_GU_LAUNCH(LO, true, false, false, ggs);        \
@@ -726,9 +736,13 @@ hipError_t launch_prefill_experts(const Fwd& f) {
     DS4_DN_LAUNCH(false, false, false, true, gdn);
     DS4_DN_LAUNCH(true, false, false, true, gds);
   } else {
-    if (L.d_ff / QK <= kDnStagedMax) DS4_DN_LAUNCH(false, true, false, false, gdn);
-    else DS4_DN_LAUNCH(false, false, false, false, gdn);
-    DS4_DN_LAUNCH(true, false, false, false, gds);
+    if (fsd) {
+      DS4_DN_LAUNCH(false, true, false, false, gdn);
+      DS4_DN_LAUNCH(true, true, false, false, gds);
+    } else {
+      DS4_DN_LAUNCH(false, false, false, false, gdn);
+      DS4_DN_LAUNCH(true, false, false, false, gds);
+    }
   }
 #undef DS4_DN_LAUNCH
   const int64_t n4 = T * d / 4;
