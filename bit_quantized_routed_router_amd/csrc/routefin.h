@@ -240,7 +240,12 @@ __device__ inline void route_finish_block(RouteLds& R, const float* __restrict__
   const int S = T * k;
   for (int e = threadIdx.x; e < E; e += nthr) R.tokm[e] = 0u;
   for (int w = threadIdx.x; w < (E + 31) / 32; w += nthr) R.selm[w] = 0u;
-  float* logits = T * E <= 1024 ? R.logit : o.logits;
+  // logits in LDS when they fit, else in memory.  The stores and the
+  // one-token finish name the array itself: through a pointer that may be
+  // either, the compiler emits flat accesses, slower than LDS ones on this
+  // latency-bound chain.
+  const bool in_lds = T * E <= 1024;
+  float* logits = in_lds ? R.logit : o.logits;
   for (int i = threadIdx.x; i < T * E; i += nthr) {
     const int e = i % E;
     float a = 0.0f;
@@ -260,11 +265,13 @@ __device__ inline void route_finish_block(RouteLds& R, const float* __restrict__
       for (int j = 0; j < 16; ++j)
         if (p0 + j < nparts) a += v[j];
     }
-    logits[i] = bias ? a + bias[e] : a;
+    const float lg = bias ? a + bias[e] : a;
+    if (in_lds) R.logit[i] = lg;
+    else o.logits[i] = lg;
   }
   __syncthreads();
-  if (T == 1 && E <= 64 * nwaves && nwaves * k <= 64) {
-    route_finish_one(R, logits, E, k, o);
+  if (T == 1 && in_lds && E <= 64 * nwaves && nwaves * k <= 64) {
+    route_finish_one(R, R.logit, E, k, o);
     return;
   }
   for (int t = wave; t < T; t += nwaves) wave_select(logits + (int64_t)t * E, E, k, lane, R.sel_e[t], R.sel_v[t]);
