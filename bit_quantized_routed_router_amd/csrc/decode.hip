@@ -36,6 +36,7 @@
 // global memory.  Every wave issues the weight loads of its share before its
 // first MFMA.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 #include "internal.h"
@@ -149,8 +150,9 @@ __device__ inline void dma_pieces(const void* src, int n, void* dst, int wave, i
 __device__ inline void wait_all() { __builtin_amdgcn_s_waitcnt(0); }
 
 // ============================================================== stage 1
+template <bool GRP>
 struct Stage1Lds {
-  RouteLds route;
+  std::conditional_t<GRP, RouteLdsGroup, RouteLdsOne> route;
   float4_t red[kW][64];
   int last;
 };
@@ -185,13 +187,15 @@ __device__ inline void f16_steps(const uint16_t* __restrict__ rowp, int ks0, int
 }
 
 // One block per (expert tile, input chunk) of the router, chunk-major; the
-// last block to arrive finishes routing.
-template <bool LO>
+// last block to arrive finishes routing.  GRP: a group of tokens (T >= 2),
+// whose finish keeps 4096 logits in LDS and sums four logits' partials at a
+// time; one token keeps the smaller footprint.
+template <bool LO, bool GRP>
 __global__ __launch_bounds__(kW * 64) void k_dec_stage1(ds4moe_layer L, int T, const void* __restrict__ x,
                                                         int rblocks, float* __restrict__ plog, RouteOut ro,
                                                         _Float16* __restrict__ xh, _Float16* __restrict__ xl,
                                                         int32_t* __restrict__ ctrl) {
-  __shared__ Stage1Lds lds;
+  __shared__ Stage1Lds<GRP> lds;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = lane & 15, q = lane >> 4;
   const int tc = min(c, T - 1);  // token feeding MFMA column c
@@ -238,7 +242,7 @@ __global__ __launch_bounds__(kW * 64) void k_dec_stage1(ds4moe_layer L, int T, c
     __syncthreads();
     if (threadIdx.x == 0) lds.last = atomicAdd(&ctrl[0], 1) == rblocks - 1;  // cleared by stage 3
     __syncthreads();
-    if (lds.last) route_finish_block<true>(lds.route, plog, d / ck, L.router_bias, E, L.top_k, T, ro);
+    if (lds.last) route_finish_block<true, GRP ? 4 : 1>(lds.route, plog, d / ck, L.router_bias, E, L.top_k, T, ro);
   }
 }
 
@@ -1239,7 +1243,10 @@ static void launch_stages12(const Fwd& f, int rblocks, int nsh, int maxd, int nr
   auto hw16 = (_Float16*)(ws + y.hw16);
   auto hsum = (_Float16*)(ws + y.hsum);
   const dim3 blk(kW * 64);
-  DS4_LAUNCH((k_dec_stage1<LO>), dim3(rblocks), blk, 0, f.st, L, T, f.x, rblocks, plog, ro, xh, xl, ctrl);
+  if (T > 1)
+    DS4_LAUNCH((k_dec_stage1<LO, true>), dim3(rblocks), blk, 0, f.st, L, T, f.x, rblocks, plog, ro, xh, xl, ctrl);
+  else
+    DS4_LAUNCH((k_dec_stage1<LO, false>), dim3(rblocks), blk, 0, f.st, L, T, f.x, rblocks, plog, ro, xh, xl, ctrl);
   DS4_LAUNCH((k_dec_stage2<LO, BL, MX, Q4>), dim3(maxd * nr + 2 * nsh), blk, 0, f.st, L, T, ro, xh, xl, hw16, hsum,
              maxd * nr, gu, hs16, ctrl);
 }

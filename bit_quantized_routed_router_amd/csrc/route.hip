@@ -116,7 +116,7 @@ __global__ __launch_bounds__(256) void k_router_partial(const uint16_t* __restri
 __global__ __launch_bounds__(256) void k_route_finish_decode(const float* __restrict__ plog, int nparts,
                                                              const float* __restrict__ bias, int E, int k, int T,
                                                              RouteOut o) {
-  __shared__ RouteLds lds;
+  __shared__ RouteLdsGroup lds;
   route_finish_block(lds, plog, nparts, bias, E, k, T, o);
 }
 

@@ -121,8 +121,12 @@ struct RouteOut {
 
 // LDS of route_finish_block (a struct so kernels can place it beside the
 // LDS of their other block roles).
-struct RouteLds {
-  float logit[1024];                    // logits when T * E <= 1024 (else the workspace copy)
+// LDS of the routing finish, NL logits kept in LDS: 1024 for one token (a
+// small footprint for the launch the single-token step waits on), 4096 for a
+// group (16 tokens of 256 experts).
+template <int NL>
+struct RouteLdsN {
+  float logit[NL];                      // logits when T * E <= NL (else the workspace copy)
   int sel_e[kDecodeGroup][kMaxTopK];    // per token: chosen experts, ascending
   float sel_v[kDecodeGroup][kMaxTopK];  // their logits
   int fe[kDecodeGroup * kMaxTopK];      // expert of slot s = t * k + j
@@ -131,10 +135,15 @@ struct RouteLds {
   int selpre[kMaxExperts / 32 + 1];     // chosen experts below word w of selm
   int dist[kDecodeGroup * kMaxTopK];    // distinct experts, ascending
   int wsel[16];                         // one token: chosen experts per wave
+  int off[kMaxExperts];                 // per expert: slots of lower experts
+  int scan[16];                         // block scan: one total per wave
 };
+using RouteLdsOne = RouteLdsN<1024>;
+using RouteLdsGroup = RouteLdsN<4096>;
 
 // Number of experts below e that some token chose (e's distinct position).
-__device__ inline int distinct_below(const RouteLds& R, int e) {
+template <typename RL>
+__device__ inline int distinct_below(const RL& R, int e) {
   return R.selpre[e >> 5] + __popc(R.selm[e >> 5] & ((1u << (e & 31)) - 1u));
 }
 
@@ -162,7 +171,8 @@ __device__ inline bool wave_top_flags(uint32_t key, bool valid, int k, int lane)
 // ascending expert order.  With one token, slot j holds the j-th chosen
 // expert, so perm and inv are the identity.  logits are filled and the block
 // has passed a barrier.
-__device__ inline void route_finish_one(RouteLds& R, const float* logits, int E, int k, const RouteOut& o) {
+template <typename RL>
+__device__ inline void route_finish_one(RL& R, const float* logits, int E, int k, const RouteOut& o) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
   const int e = threadIdx.x;
   const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;
@@ -232,8 +242,10 @@ __device__ inline void route_finish_one(RouteLds& R, const float* logits, int E,
 // (slots t*k + j by expert, then token), inv, and the distinct-expert table.
 // COH: the partials were written by other blocks of the running kernel (read
 // them with coherent loads).
-template <bool COH = false>
-__device__ inline void route_finish_block(RouteLds& R, const float* __restrict__ plog, int nparts,
+// KLF: logits a thread sums at a time (1 keeps the one-token finish's
+// register footprint).
+template <bool COH = false, int KLF = 4, typename RL>
+__device__ inline void route_finish_block(RL& R, const float* __restrict__ plog, int nparts,
                                           const float* __restrict__ bias, int E, int k, int T, const RouteOut& o) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nwaves = blockDim.x >> 6, nthr = blockDim.x;
@@ -244,30 +256,46 @@ __device__ inline void route_finish_block(RouteLds& R, const float* __restrict__
   // one-token finish name the array itself: through a pointer that may be
   // either, the compiler emits flat accesses, slower than LDS ones on this
   // latency-bound chain.
-  const bool in_lds = T * E <= 1024;
+  const bool in_lds = T * E <= (int)(sizeof(R.logit) / sizeof(float));
   float* logits = in_lds ? R.logit : o.logits;
-  for (int i = threadIdx.x; i < T * E; i += nthr) {
-    const int e = i % E;
-    float a = 0.0f;
-    // 16 partials at a time, all loads in flight before the first add (a
-    // loop that waits for each load would pay one memory round trip per
-    // partial); summed in ascending p
-    for (int p0 = 0; p0 < nparts; p0 += 16) {
-      float v[16];
+  // kLf logits per thread at a time, 16 partials each, all loads in flight
+  // before the first add (a loop that waits for each load, or for each
+  // logit's loads, would pay one memory round trip per partial or per
+  // logit); each logit summed in ascending p
+  constexpr int kLf = KLF;
+  const int n = T * E;
+  for (int i0 = threadIdx.x; i0 < n; i0 += kLf * nthr) {
+    float a[kLf];
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        if (p0 + j < nparts) {
-          const float* src = plog + (int64_t)(p0 + j) * T * E + i;
-          v[j] = COH ? __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : *src;
+    for (int u = 0; u < kLf; ++u) a[u] = 0.0f;
+    for (int p0 = 0; p0 < nparts; p0 += 16) {
+      float v[kLf][16];
+#pragma unroll
+      for (int u = 0; u < kLf; ++u) {
+        const int i = i0 + u * nthr;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          if (i < n && p0 + j < nparts) {
+            const float* src = plog + (int64_t)(p0 + j) * n + i;
+            v[u][j] = COH ? __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : *src;
+          }
         }
       }
 #pragma unroll
-      for (int j = 0; j < 16; ++j)
-        if (p0 + j < nparts) a += v[j];
+      for (int u = 0; u < kLf; ++u)
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          if (i0 + u * nthr < n && p0 + j < nparts) a[u] += v[u][j];
     }
-    const float lg = bias ? a + bias[e] : a;
-    if (in_lds) R.logit[i] = lg;
-    else o.logits[i] = lg;
+#pragma unroll
+    for (int u = 0; u < kLf; ++u) {
+      const int i = i0 + u * nthr;
+      if (i < n) {
+        const float lg = bias ? a[u] + bias[i % E] : a[u];
+        if (in_lds) R.logit[i] = lg;
+        else o.logits[i] = lg;
+      }
+    }
   }
   __syncthreads();
   if (T == 1 && in_lds && E <= 64 * nwaves && nwaves * k <= 64) {
@@ -298,35 +326,40 @@ __device__ inline void route_finish_block(RouteLds& R, const float* __restrict__
     }
   }
   __syncthreads();
-  // per expert: count, offset (selected slots of lower experts), distinct table
-  for (int e = threadIdx.x; e <= E; e += nthr) {
-    int off = 0;
-    for (int s = 0; s < S; ++s) off += R.fe[s] < e;
-    if (e == E) {
-      o.offsets[E] = S;
-      if (o.offsets_out) o.offsets_out[E] = S;
-      *o.ndist = R.selpre[(E + 31) / 32];
-      continue;
+  // per expert: count, offset (the selected slots of lower experts: an
+  // exclusive scan of the counts, in chunks of the block's threads), and the
+  // distinct table
+  int base = 0;
+  for (int e0 = 0; e0 < E; e0 += nthr) {  // uniform trip count: every thread scans
+    const int e = e0 + (int)threadIdx.x;
+    const int c = e < E ? __popc(R.tokm[e]) : 0;
+    int tot;
+    const int off = base + block_excl_scan(c, R.scan, &tot);
+    base += tot;
+    if (e < E) {
+      R.off[e] = off;
+      o.counts[e] = c;
+      o.offsets[e] = off;
+      if (o.counts_out) o.counts_out[e] = c;
+      if (o.offsets_out) o.offsets_out[e] = off;
+      if (c > 0) {
+        const int dp = distinct_below(R, e);
+        o.distinct[dp] = e;
+        R.dist[dp] = e;
+      }
     }
-    const int c = __popc(R.tokm[e]);
-    o.counts[e] = c;
-    o.offsets[e] = off;
-    if (o.counts_out) o.counts_out[e] = c;
-    if (o.offsets_out) o.offsets_out[e] = off;
-    if (c > 0) {
-      const int dp = distinct_below(R, e);
-      o.distinct[dp] = e;
-      R.dist[dp] = e;
-    }
+  }
+  if (threadIdx.x == 0) {
+    o.offsets[E] = S;
+    if (o.offsets_out) o.offsets_out[E] = S;
+    *o.ndist = R.selpre[(E + 31) / 32];
   }
   __syncthreads();
   // per slot: position in the expert-major order
   for (int s = threadIdx.x; s < S; s += nthr) {
     const int t = s / k;
     const int e = R.fe[s];
-    int off = 0;
-    for (int s2 = 0; s2 < S; ++s2) off += R.fe[s2] < e;
-    const int pos = off + __popc(R.tokm[e] & ((1u << t) - 1u));  // earlier tokens of expert e
+    const int pos = R.off[e] + __popc(R.tokm[e] & ((1u << t) - 1u));  // earlier tokens of expert e
     o.perm[pos] = s;
     o.inv[s] = pos;
     if (o.perm_out) o.perm_out[pos] = s;
