@@ -188,8 +188,8 @@ __device__ inline void f16_steps(const uint16_t* __restrict__ rowp, int ks0, int
 
 // One block per (expert tile, input chunk) of the router, chunk-major; the
 // last block to arrive finishes routing.  GRP: a group of tokens (T >= 2),
-// whose finish keeps 4096 logits in LDS and sums four logits' partials at a
-// time; one token keeps the smaller footprint.
+// whose finish keeps 4096 logits in LDS and sums eight logits' partials at
+// a time; one token keeps the smaller footprint.
 template <bool LO, bool GRP>
 __global__ __launch_bounds__(kW * 64) void k_dec_stage1(ds4moe_layer L, int T, const void* __restrict__ x,
                                                         int rblocks, float* __restrict__ plog, RouteOut ro,
@@ -242,7 +242,7 @@ __global__ __launch_bounds__(kW * 64) void k_dec_stage1(ds4moe_layer L, int T, c
     __syncthreads();
     if (threadIdx.x == 0) lds.last = atomicAdd(&ctrl[0], 1) == rblocks - 1;  // cleared by stage 3
     __syncthreads();
-    if (lds.last) route_finish_block<true, GRP ? 4 : 1>(lds.route, plog, d / ck, L.router_bias, E, L.top_k, T, ro);
+    if (lds.last) route_finish_block<true, GRP ? 8 : 1>(lds.route, plog, d / ck, L.router_bias, E, L.top_k, T, ro);
   }
 }
 

@@ -26,55 +26,74 @@ __device__ inline uint32_t order_key(float v) {
 // uses only ballots and popcounts, so no data crosses lanes, and every step
 // is straight-line code.  Slots past E get key 0, which no candidate (>= 1)
 // admits; k <= E guarantees k real keys.
-template <int PER>
-__device__ inline void wave_select_n(const float* l, int E, int k, int lane, int* sel_e, float* sel_v) {
-  float v[PER];
-  uint32_t key[PER];
+// NT tokens at once (logits lp(t); outputs ep(t), vp(t)): the tokens'
+// selections are independent, so their ballot and popcount chains overlap.
+template <int PER, int NT, typename LP, typename EP, typename VP>
+__device__ inline void wave_select_n(LP lp, EP ep, VP vp, int E, int k, int lane) {
+  float v[NT][PER];
+  uint32_t key[NT][PER];
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int e = lane + 64 * i;
-    v[i] = l[e < E ? e : E - 1];
-  }
+  for (int t = 0; t < NT; ++t)
 #pragma unroll
-  for (int i = 0; i < PER; ++i) key[i] = lane + 64 * i < E ? order_key(v[i]) : 0u;
-  uint32_t thr = 0;
+    for (int i = 0; i < PER; ++i) {
+      const int e = lane + 64 * i;
+      v[t][i] = lp(t)[e < E ? e : E - 1];
+    }
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int i = 0; i < PER; ++i) key[t][i] = lane + 64 * i < E ? order_key(v[t][i]) : 0u;
+  uint32_t thr[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) thr[t] = 0;
 #pragma unroll
   for (int bit = 31; bit >= 0; --bit) {
-    const uint32_t cand = thr | (1u << bit);
-    int cnt = 0;
 #pragma unroll
-    for (int i = 0; i < PER; ++i) cnt += __popcll(__ballot(key[i] >= cand));
-    thr = cnt >= k ? cand : thr;
-  }
-  int gt = 0;
+    for (int t = 0; t < NT; ++t) {
+      const uint32_t cand = thr[t] | (1u << bit);
+      int cnt = 0;
 #pragma unroll
-  for (int i = 0; i < PER; ++i) gt += __popcll(__ballot(key[i] > thr));
-  const int need_eq = k - gt;  // keys equal to the threshold still to take, lowest index first
-  const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;  // lanes under this one
-  int eq_before = 0, pos0 = 0;
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const bool eq = key[i] == thr;
-    const uint64_t eqm = __ballot(eq);
-    const bool sel = key[i] > thr || (eq && eq_before + __popcll(eqm & below) < need_eq);
-    eq_before += __popcll(eqm);
-    const uint64_t sm = __ballot(sel);
-    if (sel) {
-      const int pos = pos0 + __popcll(sm & below);
-      sel_e[pos] = lane + 64 * i;
-      sel_v[pos] = v[i];
+      for (int i = 0; i < PER; ++i) cnt += __popcll(__ballot(key[t][i] >= cand));
+      thr[t] = cnt >= k ? cand : thr[t];
     }
-    pos0 += __popcll(sm);
+  }
+  const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;  // lanes under this one
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    int gt = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) gt += __popcll(__ballot(key[t][i] > thr[t]));
+    const int need_eq = k - gt;  // keys equal to the threshold still to take, lowest index first
+    int eq_before = 0, pos0 = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const bool eq = key[t][i] == thr[t];
+      const uint64_t eqm = __ballot(eq);
+      const bool sel = key[t][i] > thr[t] || (eq && eq_before + __popcll(eqm & below) < need_eq);
+      eq_before += __popcll(eqm);
+      const uint64_t sm = __ballot(sel);
+      if (sel) {
+        const int pos = pos0 + __popcll(sm & below);
+        ep(t)[pos] = lane + 64 * i;
+        vp(t)[pos] = v[t][i];
+      }
+      pos0 += __popcll(sm);
+    }
   }
 }
 
-__device__ inline void wave_select(const float* l, int E, int k, int lane, int* sel_e, float* sel_v) {
+template <int NT, typename LP, typename EP, typename VP>
+__device__ inline void wave_select_t(LP lp, EP ep, VP vp, int E, int k, int lane) {
   if (E <= 256)
-    wave_select_n<4>(l, E, k, lane, sel_e, sel_v);
+    wave_select_n<4, NT>(lp, ep, vp, E, k, lane);
   else if (E <= 512)
-    wave_select_n<8>(l, E, k, lane, sel_e, sel_v);
+    wave_select_n<8, NT>(lp, ep, vp, E, k, lane);
   else
-    wave_select_n<16>(l, E, k, lane, sel_e, sel_v);
+    wave_select_n<16, NT>(lp, ep, vp, E, k, lane);
+}
+
+__device__ inline void wave_select(const float* l, int E, int k, int lane, int* sel_e, float* sel_v) {
+  wave_select_t<1>([&](int) { return l; }, [&](int) { return sel_e; }, [&](int) { return sel_v; }, E, k, lane);
 }
 
 // Gate weight of selected slot j: softmax over the k selected logits,
@@ -242,8 +261,9 @@ __device__ inline void route_finish_one(RL& R, const float* logits, int E, int k
 // (slots t*k + j by expert, then token), inv, and the distinct-expert table.
 // COH: the partials were written by other blocks of the running kernel (read
 // them with coherent loads).
-// KLF: logits a thread sums at a time (1 keeps the one-token finish's
-// register footprint).
+// KLF: logits a thread sums at a time; above 1 the selection also runs two
+// tokens per wave at once (1 keeps the one-token finish's register
+// footprint).
 template <bool COH = false, int KLF = 4, typename RL>
 __device__ inline void route_finish_block(RL& R, const float* __restrict__ plog, int nparts,
                                           const float* __restrict__ bias, int E, int k, int T, const RouteOut& o) {
@@ -258,23 +278,23 @@ __device__ inline void route_finish_block(RL& R, const float* __restrict__ plog,
   // latency-bound chain.
   const bool in_lds = T * E <= (int)(sizeof(R.logit) / sizeof(float));
   float* logits = in_lds ? R.logit : o.logits;
-  // kLf logits per thread at a time, 16 partials each, all loads in flight
+  // kLf logits per thread at a time, kPb partials each, all loads in flight
   // before the first add (a loop that waits for each load, or for each
   // logit's loads, would pay one memory round trip per partial or per
   // logit); each logit summed in ascending p
-  constexpr int kLf = KLF;
+  constexpr int kLf = KLF, kPb = KLF > 1 ? 8 : 16;
   const int n = T * E;
   for (int i0 = threadIdx.x; i0 < n; i0 += kLf * nthr) {
     float a[kLf];
 #pragma unroll
     for (int u = 0; u < kLf; ++u) a[u] = 0.0f;
-    for (int p0 = 0; p0 < nparts; p0 += 16) {
-      float v[kLf][16];
+    for (int p0 = 0; p0 < nparts; p0 += kPb) {
+      float v[kLf][kPb];
 #pragma unroll
       for (int u = 0; u < kLf; ++u) {
         const int i = i0 + u * nthr;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
+        for (int j = 0; j < kPb; ++j) {
           if (i < n && p0 + j < nparts) {
             const float* src = plog + (int64_t)(p0 + j) * n + i;
             v[u][j] = COH ? __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : *src;
@@ -284,7 +304,7 @@ __device__ inline void route_finish_block(RL& R, const float* __restrict__ plog,
 #pragma unroll
       for (int u = 0; u < kLf; ++u)
 #pragma unroll
-        for (int j = 0; j < 16; ++j)
+        for (int j = 0; j < kPb; ++j)
           if (i0 + u * nthr < n && p0 + j < nparts) a[u] += v[u][j];
     }
 #pragma unroll
@@ -302,7 +322,26 @@ __device__ inline void route_finish_block(RL& R, const float* __restrict__ plog,
     route_finish_one(R, R.logit, E, k, o);
     return;
   }
-  for (int t = wave; t < T; t += nwaves) wave_select(logits + (int64_t)t * E, E, k, lane, R.sel_e[t], R.sel_v[t]);
+  if constexpr (KLF > 1) {
+    // tokens two at a time per wave (t and t + nwaves), one when it is the last
+    for (int t = wave; t < T; t += 2 * nwaves) {
+      if (t + nwaves < T && E <= 512) {  // (past 512 experts two tokens' keys outgrow the registers)
+        const int tt[2] = {t, t + nwaves};
+        const auto lp = [&](int u) { return logits + (int64_t)tt[u] * E; };
+        const auto ep = [&](int u) { return R.sel_e[tt[u]]; };
+        const auto vp = [&](int u) { return R.sel_v[tt[u]]; };
+        if (E <= 256) wave_select_n<4, 2>(lp, ep, vp, E, k, lane);
+        else wave_select_n<8, 2>(lp, ep, vp, E, k, lane);
+      } else if (t + nwaves < T) {
+        wave_select(logits + (int64_t)t * E, E, k, lane, R.sel_e[t], R.sel_v[t]);
+        wave_select(logits + (int64_t)(t + nwaves) * E, E, k, lane, R.sel_e[t + nwaves], R.sel_v[t + nwaves]);
+      } else {
+        wave_select(logits + (int64_t)t * E, E, k, lane, R.sel_e[t], R.sel_v[t]);
+      }
+    }
+  } else {
+    for (int t = wave; t < T; t += nwaves) wave_select(logits + (int64_t)t * E, E, k, lane, R.sel_e[t], R.sel_v[t]);
+  }
   __syncthreads();
   // per slot: gate weight, and the expert/token bitmaps
   for (int s = threadIdx.x; s < S; s += nthr) {
