@@ -50,6 +50,7 @@ __constant__ GridTables c_dec_tables = make_grid_tables();
 
 constexpr int kW = 4;           // waves per block
 constexpr int kStageHalves = 4096;        // binary16 activations a stage-1/2 block may stage (per hi/lo part)
+constexpr int kStageHalvesGroup = 16384;  // the same for a group of tokens (T d <= 16384: 4 tokens of 4096)
 constexpr size_t kStage3Bytes = 32 * 1024;  // stage 3 LDS for staged activations and sums
 constexpr size_t kStage3OneBytes = 40 * 1024;  // the same for the one-token form
 
@@ -320,12 +321,14 @@ constexpr int kSbRows = kDecodeGroup * kSbRow;
 
 // BL: the group's whole x staged once per block (bh, bl); otherwise each
 // wave stages the super-block it is about to decode (xw, xwl).
-template <bool LO, bool BL>
+// NS: binary16 activations the block stages when BL (T rows of d_model,
+// each padded by 8 halves, T <= 16).
+template <bool LO, bool BL, int NS = kStageHalves>
 struct Stage2Lds {
   uint32_t mag[256 * 4];
   uint32_t sgn[128 * 4];
-  _Float16 bh[BL ? kStageHalves + 16 * 8 : 8];
-  _Float16 bl[BL ? kStageHalves + 16 * 8 : 8];
+  _Float16 bh[BL ? NS + 16 * 8 : 8];
+  _Float16 bl[BL && LO ? NS + 16 * 8 : 8];
   _Float16 xw[BL ? 8 : kW * kSbRows];
   _Float16 xwl[BL || !LO ? 8 : kW * kSbRows];
   float4_t red[kW][64];
@@ -403,25 +406,28 @@ __device__ inline half8_t q4k_step(const Q4kSb& W, const Q4kS& S, int s2) {
 // dispatched behind the routed blocks.
 // Waves per SIMD that stage 2's LDS allows: 4 blocks per CU with x staged
 // whole, 3 with the per-wave super-block buffers, fewer with fp32 input.
-constexpr int stage2_waves(bool lo, bool bl) { return bl ? (lo ? 2 : 4) : (lo ? 1 : 3); }
+constexpr int stage2_waves(bool lo, bool bl, int ns = kStageHalves) {
+  return bl ? (lo ? 2 : (ns > kStageHalves ? 3 : 4)) : (lo ? 1 : 3);
+}
 
-template <bool LO, bool BL, bool Q4>
+template <bool LO, bool BL, bool Q4, int NS>
 __device__ void routed_gateup_mx(const ds4moe_layer& L, int T, const RouteOut& ro, const _Float16* __restrict__ xh,
-                                 const _Float16* __restrict__ xl, _Float16* __restrict__ hw16, Stage2Lds<LO, BL>& lds);
+                                 const _Float16* __restrict__ xl, _Float16* __restrict__ hw16,
+                                 Stage2Lds<LO, BL, NS>& lds);
 
-template <bool LO, bool BL, bool MX, bool Q4 = false>
-__global__ __launch_bounds__(kW * 64) __attribute__((amdgpu_waves_per_eu(stage2_waves(LO, BL)))) void k_dec_stage2(
+template <bool LO, bool BL, bool MX, bool Q4 = false, int NS = kStageHalves>
+__global__ __launch_bounds__(kW * 64) __attribute__((amdgpu_waves_per_eu(stage2_waves(LO, BL, NS)))) void k_dec_stage2(
     ds4moe_layer L, int T, RouteOut ro, const _Float16* __restrict__ xh,
     const _Float16* __restrict__ xl, _Float16* __restrict__ hw16, _Float16* __restrict__ hsum, int rtiles,
     float* __restrict__ gu_part, _Float16* __restrict__ hs16, int32_t* __restrict__ ctrl) {
-  __shared__ Stage2Lds<LO, BL> lds;
+  __shared__ Stage2Lds<LO, BL, NS> lds;
   if ((int)blockIdx.x >= rtiles) {
     shared_gateup_block<LO, BL>(L, T, xh, xl, blockIdx.x - rtiles, gu_part, hs16, ctrl, lds.bh, lds.bl, lds.red,
                                 lds.last);
     return;
   }
   if constexpr (MX || Q4) {
-    routed_gateup_mx<LO, BL, Q4>(L, T, ro, xh, xl, hw16, lds);
+    routed_gateup_mx<LO, BL, Q4, NS>(L, T, ro, xh, xl, hw16, lds);
     return;
   }
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -641,9 +647,10 @@ __global__ __launch_bounds__(kW * 64) __attribute__((amdgpu_waves_per_eu(stage2_
 template <bool Q4>
 constexpr int sb_batch() { return Q4 ? 2 : 4; }
 
-template <bool LO, bool BL, bool Q4>
+template <bool LO, bool BL, bool Q4, int NS>
 __device__ void routed_gateup_mx(const ds4moe_layer& L, int T, const RouteOut& ro, const _Float16* __restrict__ xh,
-                                 const _Float16* __restrict__ xl, _Float16* __restrict__ hw16, Stage2Lds<LO, BL>& lds) {
+                                 const _Float16* __restrict__ xl, _Float16* __restrict__ hw16,
+                                 Stage2Lds<LO, BL, NS>& lds) {
   constexpr int kSbMx = sb_batch<Q4>();
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = lane & 15, q = lane >> 4;
@@ -1228,7 +1235,7 @@ __global__ __launch_bounds__(kW3 * 64) __attribute__((amdgpu_waves_per_eu(4))) v
 }
 
 // ============================================================== launcher
-template <bool LO, bool BL, bool MX, bool Q4>
+template <bool LO, bool BL, bool MX, bool Q4, int NS = kStageHalves>
 static void launch_stages12(const Fwd& f, int rblocks, int nsh, int maxd, int nr, const RouteOut& ro) {
   const ds4moe_layer& L = f.L;
   const WsLayout& y = f.lay;
@@ -1247,8 +1254,8 @@ static void launch_stages12(const Fwd& f, int rblocks, int nsh, int maxd, int nr
     DS4_LAUNCH((k_dec_stage1<LO, true>), dim3(rblocks), blk, 0, f.st, L, T, f.x, rblocks, plog, ro, xh, xl, ctrl);
   else
     DS4_LAUNCH((k_dec_stage1<LO, false>), dim3(rblocks), blk, 0, f.st, L, T, f.x, rblocks, plog, ro, xh, xl, ctrl);
-  DS4_LAUNCH((k_dec_stage2<LO, BL, MX, Q4>), dim3(maxd * nr + 2 * nsh), blk, 0, f.st, L, T, ro, xh, xl, hw16, hsum,
-             maxd * nr, gu, hs16, ctrl);
+  DS4_LAUNCH((k_dec_stage2<LO, BL, MX, Q4, NS>), dim3(maxd * nr + 2 * nsh), blk, 0, f.st, L, T, ro, xh, xl, hw16,
+             hsum, maxd * nr, gu, hs16, ctrl);
 }
 
 hipError_t launch_decode(const Fwd& f) {
@@ -1261,19 +1268,23 @@ hipError_t launch_decode(const Fwd& f) {
   const int nsh = fs / 16, nr = L.d_ff / 16, ndt = d / 16;
   const int maxd = std::min(E, T * L.top_k);
   const RouteOut ro = route_out(f);
-  // stage the activations in LDS when every staged row set fits: the x
-  // halves (stages 1 and 2) and x (stage 2 routed)
+  // stage 2 stages the group's x in LDS once per block when it fits: one
+  // token (kStageHalves) or, with a larger block footprint of its own, a few
+  // (kStageHalvesGroup, binary16 x only); else each wave stages the
+  // super-block it decodes next
   const bool bl = (int64_t)T * d <= kStageHalves;
+  const bool blg = !bl && !f.lo && (int64_t)T * d <= kStageHalvesGroup;
   const bool mx = L.expert_fmt == DS4MOE_EXPERTS_MXFP4, q4 = L.expert_fmt == DS4MOE_EXPERTS_Q4K;
-#define DS4_S12(LO_, BL_)                                                            \
-  (mx   ? launch_stages12<LO_, BL_, true, false>(f, rblocks, nsh, maxd, nr, ro)    \
-   : q4 ? launch_stages12<LO_, BL_, false, true>(f, rblocks, nsh, maxd, nr, ro)    \
-        : launch_stages12<LO_, BL_, false, false>(f, rblocks, nsh, maxd, nr, ro))
+#define DS4_S12(LO_, BL_, ...)                                                                   \
+  (mx   ? launch_stages12<LO_, BL_, true, false, ##__VA_ARGS__>(f, rblocks, nsh, maxd, nr, ro)   \
+   : q4 ? launch_stages12<LO_, BL_, false, true, ##__VA_ARGS__>(f, rblocks, nsh, maxd, nr, ro)   \
+        : launch_stages12<LO_, BL_, false, false, ##__VA_ARGS__>(f, rblocks, nsh, maxd, nr, ro))
   if (f.lo) {
     if (bl) DS4_S12(true, true);
     else DS4_S12(true, false);
   } else {
     if (bl) DS4_S12(false, true);
+    else if (blg) DS4_S12(false, true, kStageHalvesGroup);
     else DS4_S12(false, false);
   }
 #undef DS4_S12
