@@ -51,7 +51,10 @@ __constant__ GridTables c_dec_tables = make_grid_tables();
 constexpr int kW = 4;           // waves per block
 constexpr int kStageHalves = 4096;        // binary16 activations a stage-1/2 block may stage (per hi/lo part)
 constexpr int kStageHalvesGroup = 16384;  // the same for a group of tokens (T d <= 16384: 4 tokens of 4096)
-constexpr size_t kStage3Bytes = 32 * 1024;  // stage 3 LDS for staged activations and sums
+// Stage 3 LDS for staged activations and sums (dynamic, beside 32 KB of
+// static reduction buffers within the CU's 160 KB; one 16-wave block per
+// CU): T = 1 (MXFP4, Q4K) and groups up to T = 4 at the decode1 layer shape.
+constexpr size_t kStage3Bytes = 128 * 1024;
 constexpr size_t kStage3OneBytes = 40 * 1024;  // the same for the one-token form
 
 __device__ inline int cb2_boff(int q, int s) { return 32 * (2 * q + (s >> 2)) + 8 * (s & 3); }
