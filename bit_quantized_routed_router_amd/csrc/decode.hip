@@ -141,6 +141,19 @@ __device__ inline void dma_rows(const _Float16* src, int ld, int R, int K, _Floa
   }
 }
 
+// Rows of the tokens in tmask (bit t: token t; wave-uniform), ascending,
+// into consecutive LDS rows of stride st: 256 halves each from src + t ld,
+// one wave instruction a row (lanes 0..31).
+__device__ inline void dma_token_rows(const _Float16* src, int ld, uint32_t tmask, _Float16* dst, int st, int lane) {
+  int r = 0;
+  for (uint32_t m = tmask; m != 0u; m &= m - 1u, ++r) {
+    const int t = __builtin_ctz(m);
+    if (lane < QK / 8)
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src + (int64_t)t * ld + lane * 8),
+                                       (__attribute__((address_space(3))) void*)(dst + r * st), 16, 0, 0);
+  }
+}
+
 // Same for a contiguous run of n 16-byte pieces.
 __device__ inline void dma_pieces(const void* src, int n, void* dst, int wave, int nw, int lane) {
   for (int ch = wave; ch * 64 < n; ch += nw) {
@@ -498,30 +511,41 @@ __global__ __launch_bounds__(kW * 64) __attribute__((amdgpu_waves_per_eu(stage2_
     }
   };
   load_batch(sb0);
+  // !BL: the tokens that chose expert i (bit t; a distinct expert has at
+  // least one), compacted: MFMA row j is the j-th of them, so only their
+  // activation rows are staged
+  uint32_t tmask = 0u;
+  int ntok = T;
+  if constexpr (!BL) {
+    const int slc = c < T ? ro.tok_slot[i * kDecodeGroup + c] : -1;
+    tmask = (uint32_t)__ballot(slc >= 0) & 0xFFFFu;  // lanes 0..15 (c = lane)
+    ntok = max(1, __popc(tmask));
+  }
   wait_all();  // the copies (and the first batch)
   __syncthreads();
   if constexpr (!BL) {
     // Each wave stages the activations of the super-block it decodes next
-    // (16 token rows x 256 inputs) and waits for its own copies; the
-    // buffer is its own, so no block barrier is needed.  Rows at or beyond
-    // T are never read (the MFMA rows of those tokens repeat token T - 1).
+    // (the expert's token rows x 256 inputs) and waits for its own copies;
+    // the buffer is its own, so no block barrier is needed.  Rows at or
+    // beyond ntok are never read (those MFMA rows repeat row ntok - 1).
     _Float16* xw = lds.xw + wave * kSbRows;
     _Float16* xwl = LO ? lds.xwl + wave * kSbRows : nullptr;
+    const int tcx = min(c, ntok - 1);
     for (int b0 = sb0; b0 < sb1; b0 += kSb2) {
       if (b0 != sb0) load_batch(b0);
 #pragma unroll
       for (int j = 0; j < kSb2; ++j) {
         if (b0 + j >= sb1) break;  // wave-uniform
         pin();
-        dma_rows(xh + (int64_t)(b0 + j) * QK, d, T, QK, xw, kSbRow, 0, 1, lane);
-        if (LO) dma_rows(xl + (int64_t)(b0 + j) * QK, d, T, QK, xwl, kSbRow, 0, 1, lane);
+        dma_token_rows(xh + (int64_t)(b0 + j) * QK, d, tmask, xw, kSbRow, lane);
+        if (LO) dma_token_rows(xl + (int64_t)(b0 + j) * QK, d, tmask, xwl, kSbRow, lane);
         wait_all();
         pin();
         Cb2Step F[2];
         auto fetch = [&](Cb2Step& G, int s2) {
           const int kk = cb2_boff(q, s2);
-          G.bh = *(const half8_t*)(xw + tc * kSbRow + kk);
-          if (LO) G.bl = *(const half8_t*)(xwl + tc * kSbRow + kk);
+          G.bh = *(const half8_t*)(xw + tcx * kSbRow + kk);
+          if (LO) G.bl = *(const half8_t*)(xwl + tcx * kSbRow + kk);
           cb2_lookup(G.g, (s2 & 4) ? cg[j].z : cg[j].x, (s2 & 4) ? cg[j].w : cg[j].y, s2 & 3, lds.mag, lds.sgn);
           cb2_lookup(G.u, (s2 & 4) ? cu[j].z : cu[j].x, (s2 & 4) ? cu[j].w : cu[j].y, s2 & 3, lds.mag, lds.sgn);
         };
@@ -609,14 +633,29 @@ __global__ __launch_bounds__(kW * 64) __attribute__((amdgpu_waves_per_eu(stage2_
     ag += lds.red[w][lane];
     au += lds.red2[w][lane];
   }
-  // tokens 4q..4q+3: their slots for this expert; h = w * silu(g) * u as
-  // binary16 into hw16[slot][row], and the 16-row sums into hsum
-  const int4 sl4 = *(const int4*)(ro.tok_slot + i * kDecodeGroup + 4 * q);
-  const int slots[4] = {sl4.x, sl4.y, sl4.z, sl4.w};
+  // MFMA rows 4q..4q+3: their tokens' slots for this expert (BL: row j is
+  // token j; else the j-th token of tmask); h = w * silu(g) * u as binary16
+  // into hw16[slot][row], and the 16-row sums into hsum
+  int slots[4];
+  if constexpr (BL) {
+    const int4 sl4 = *(const int4*)(ro.tok_slot + i * kDecodeGroup + 4 * q);
+    slots[0] = sl4.x;
+    slots[1] = sl4.y;
+    slots[2] = sl4.z;
+    slots[3] = sl4.w;
+  } else {
+    uint32_t m = tmask;
+    for (int x = 0; x < 4 * q; ++x) m &= m - 1u;  // drop the first 4q tokens
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      slots[r] = m != 0u ? ro.tok_slot[i * kDecodeGroup + __builtin_ctz(m)] : -1;
+      m &= m - 1u;
+    }
+  }
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int slot = slots[r];
-    const bool has = 4 * q + r < T && slot >= 0 && slot < T * k;
+    const bool has = (BL ? 4 * q + r < T : 4 * q + r < ntok) && slot >= 0 && slot < T * k;
     float hv = 0.0f;
     if (has) {
       const _Float16 h16 = (_Float16)(ro.w[slot] * (silu(ag[r]) * au[r]));
