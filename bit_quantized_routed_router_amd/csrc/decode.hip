@@ -855,11 +855,21 @@ struct Q2kA {
 
 // bcol: the activation row of the lane's token at the unit's super-block
 // (LDS or global); csh/csl: binary16 hi/lo of its 16 sub-block sums.
-__device__ inline void q2k_act(Q2kA& A, const _Float16* bcol, const _Float16* csh, const _Float16* csl, int q) {
+// (on: the lane's token has a slot for the unit's expert; a lane without
+// one takes zeros and issues no loads, its products being masked anyway)
+__device__ inline void q2k_act(Q2kA& A, const _Float16* bcol, const _Float16* csh, const _Float16* csl, int q,
+                               bool on = true) {
+  if (on) {
 #pragma unroll
-  for (int s = 0; s < 8; ++s) A.b[s] = *(const half8_t*)(bcol + q2k_boff(q, s));
-  A.bh = *(const half8_t*)(csh + 8 * (q & 1));
-  A.bl = *(const half8_t*)(csl + 8 * (q & 1));
+    for (int s = 0; s < 8; ++s) A.b[s] = *(const half8_t*)(bcol + q2k_boff(q, s));
+    A.bh = *(const half8_t*)(csh + 8 * (q & 1));
+    A.bl = *(const half8_t*)(csl + 8 * (q & 1));
+  } else {
+#pragma unroll
+    for (int s = 0; s < 8; ++s) A.b[s] = zero_half8();
+    A.bh = zero_half8();
+    A.bl = zero_half8();
+  }
 }
 
 // One unit, transposed: the activations are the MFMA's A operand (row c' =
@@ -1051,7 +1061,7 @@ __global__ __launch_bounds__(kW3 * 64) __attribute__((amdgpu_waves_per_eu(4))) v
       if constexpr (MX || Q4) {
         const _Float16* bcol = (BL ? s_h : hw16) + (size_t)row * f + b * QK;
 #pragma unroll
-        for (int s2 = 0; s2 < 8; ++s2) A.b[s2] = *(const half8_t*)(bcol + q2k_boff(q, s2));
+        for (int s2 = 0; s2 < 8; ++s2) A.b[s2] = has ? *(const half8_t*)(bcol + q2k_boff(q, s2)) : zero_half8();
         if constexpr (Q4) q4k_unit(WQ[j], A, vmask, q, acc);
         else mx4_unit(WM[j], A, vmask, acc);
       } else {
@@ -1060,7 +1070,7 @@ __global__ __launch_bounds__(kW3 * 64) __attribute__((amdgpu_waves_per_eu(4))) v
                   s_cs + (size_t)(S + row) * fs16 + b * 16, q);
         else
           q2k_act(A, hw16 + (size_t)row * f + b * QK, hsum + (size_t)row * fs16 + b * 16,
-                  hsum + (size_t)(S + row) * fs16 + b * 16, q);
+                  hsum + (size_t)(S + row) * fs16 + b * 16, q, has);
         q2k_unit(W[j], A, vmask, q, acc);
       }
     }
