@@ -531,21 +531,40 @@ __global__ __launch_bounds__(kW * 64) __attribute__((amdgpu_waves_per_eu(stage2_
     _Float16* xw = lds.xw + wave * kSbRows;
     _Float16* xwl = LO ? lds.xwl + wave * kSbRows : nullptr;
     const int tcx = min(c, ntok - 1);
+    // with at most kDecodeGroup / kSb2 tokens, the whole batch's rows fit
+    // the buffer (super-block j at rows j ntok ..): one copy pass and one
+    // wait per batch instead of one per super-block
+    const bool whole = ntok * kSb2 <= kDecodeGroup;  // wave-uniform
     for (int b0 = sb0; b0 < sb1; b0 += kSb2) {
       if (b0 != sb0) load_batch(b0);
+      if (whole) {
+        pin();
+#pragma unroll
+        for (int j = 0; j < kSb2; ++j) {
+          if (b0 + j < sb1) {
+            dma_token_rows(xh + (int64_t)(b0 + j) * QK, d, tmask, xw + j * ntok * kSbRow, kSbRow, lane);
+            if (LO) dma_token_rows(xl + (int64_t)(b0 + j) * QK, d, tmask, xwl + j * ntok * kSbRow, kSbRow, lane);
+          }
+        }
+        wait_all();
+      }
 #pragma unroll
       for (int j = 0; j < kSb2; ++j) {
         if (b0 + j >= sb1) break;  // wave-uniform
         pin();
-        dma_token_rows(xh + (int64_t)(b0 + j) * QK, d, tmask, xw, kSbRow, lane);
-        if (LO) dma_token_rows(xl + (int64_t)(b0 + j) * QK, d, tmask, xwl, kSbRow, lane);
-        wait_all();
+        if (!whole) {
+          dma_token_rows(xh + (int64_t)(b0 + j) * QK, d, tmask, xw, kSbRow, lane);
+          if (LO) dma_token_rows(xl + (int64_t)(b0 + j) * QK, d, tmask, xwl, kSbRow, lane);
+          wait_all();
+        }
         pin();
+        const _Float16* xj = xw + (whole ? j * ntok * kSbRow : 0);
+        const _Float16* xjl = LO ? xwl + (whole ? j * ntok * kSbRow : 0) : nullptr;
         Cb2Step F[2];
         auto fetch = [&](Cb2Step& G, int s2) {
           const int kk = cb2_boff(q, s2);
-          G.bh = *(const half8_t*)(xw + tcx * kSbRow + kk);
-          if (LO) G.bl = *(const half8_t*)(xwl + tcx * kSbRow + kk);
+          G.bh = *(const half8_t*)(xj + tcx * kSbRow + kk);
+          if (LO) G.bl = *(const half8_t*)(xjl + tcx * kSbRow + kk);
           cb2_lookup(G.g, (s2 & 4) ? cg[j].z : cg[j].x, (s2 & 4) ? cg[j].w : cg[j].y, s2 & 3, lds.mag, lds.sgn);
           cb2_lookup(G.u, (s2 & 4) ? cu[j].z : cu[j].x, (s2 & 4) ? cu[j].w : cu[j].y, s2 & 3, lds.mag, lds.sgn);
         };
