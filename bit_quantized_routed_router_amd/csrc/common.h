@@ -192,35 +192,6 @@ __device__ inline void q2k_pairs(uint32_t v, uint32_t (&pr)[4]) {
   for (int p = 0; p < 4; ++p) pr[p] = __builtin_amdgcn_bitop3_b32(v >> (4 * p), 0x00030003u, 0x64006400u, 0xEA);
 }
 
-// Both A fragments of one Q2K sub-block (its u32 of 16 codes): binary16
-// s * q for codes 0..7 (lo) and 8..15 (hi), exact; one scale conversion.
-__device__ inline void q2k_subblock(uint32_t u, uint32_t s, half8_t& lo, half8_t& hi) {
-  const _Float16 S = (_Float16)(uint16_t)s;
-  const half2_t S2 = {S, S};
-  const half2_t C2 = S2 * (half2_t){(_Float16)-1024.0f, (_Float16)-1024.0f};
-  const uint32_t h16 = u >> 16;
-  uint32_t pl[4], ph[4];
-  q2k_pairs((u & 0xFFFFu) | (u << 14), pl);
-  q2k_pairs(h16 | (h16 << 14), ph);
-  u32x4_t a, b;
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    a[p] = as_u32(__builtin_elementwise_fma(as_half2(pl[p]), S2, C2));
-    b[p] = as_u32(__builtin_elementwise_fma(as_half2(ph[p]), S2, C2));
-  }
-  lo = as_half8(a);
-  hi = as_half8(b);
-}
-
-// binary16 (1024 + n) trick for a byte's high nibble, pairs of bytes.
-__device__ inline uint32_t nib_hi_pair_f16(uint32_t w, int byte0) {
-  uint32_t a = (w >> (8 * byte0 + 4)) & 0xFu;
-  uint32_t b = (w >> (8 * byte0 + 12)) & 0xFu;
-  half2_t t = as_half2(a | (b << 16) | 0x64006400u);
-  half2_t off = {(_Float16)1024.0f, (_Float16)1024.0f};
-  return as_u32(t - off);
-}
-
 // MXFP4 fragment: the 8 elements of one 32-bit code word (element 2i in the
 // low nibble of byte i) as binary16 with the block scale folded in, by the
 // FP4 conversion instruction; exact for scale codes 104..140 (every product
@@ -297,6 +268,34 @@ __device__ inline void st_coh(float* p, float v) {
 }
 __device__ inline void wait_stores() { __builtin_amdgcn_s_waitcnt(0); }
 __device__ inline int ld_uniform(const int32_t* p) { return *(const __attribute__((address_space(4))) int32_t*)p; }
+
+// Raw buffer (stride 0) over n bytes at p, 32-bit data format.  The hardware
+// range-checks each lane's offset: a load at an offset of n or more returns
+// zeros and reads no memory, so a lane with nothing to load passes kOob and
+// gets a zero operand without a branch or a register clear.  vo is the
+// lane's byte offset, so a wave-uniform one (an SGPR) added to it; both stay
+// below 2^31.
+constexpr uint32_t kOob = 0x80000000u;
+__device__ inline __amdgpu_buffer_rsrc_t buf_rsrc(const void* p, uint32_t n) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)n, 0x00020000);
+}
+constexpr int kBufNt = 2;  // cache policy: streamed once (non-temporal)
+template <int AUX = 0>
+__device__ inline u32x4_t buf_ld128(__amdgpu_buffer_rsrc_t r, uint32_t vo, uint32_t so) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)vo, (int)so, AUX));
+}
+__device__ inline u32x3_t buf_ld96(__amdgpu_buffer_rsrc_t r, uint32_t vo, uint32_t so) {
+  return __builtin_bit_cast(u32x3_t, __builtin_amdgcn_raw_buffer_load_b96(r, (int)vo, (int)so, 0));
+}
+__device__ inline u32x2_t buf_ld64(__amdgpu_buffer_rsrc_t r, uint32_t vo, uint32_t so) {
+  return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(r, (int)vo, (int)so, 0));
+}
+__device__ inline uint32_t buf_ld32(__amdgpu_buffer_rsrc_t r, uint32_t vo, uint32_t so) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_raw_buffer_load_b32(r, (int)vo, (int)so, 0));
+}
+__device__ inline uint32_t buf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t vo, uint32_t so) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, __builtin_amdgcn_raw_buffer_load_b16(r, (int)vo, (int)so, 0));
+}
 
 __device__ inline float silu(float g) { return g / (1.0f + __expf(-g)); }
 

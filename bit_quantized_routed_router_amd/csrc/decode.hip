@@ -40,6 +40,7 @@
 
 #include "common.h"
 #include "internal.h"
+#include "ring.h"
 #include "routefin.h"
 #include "tiles.h"
 #include "trace.h"
@@ -59,6 +60,13 @@ constexpr size_t kStage3OneBytes = 40 * 1024;  // the same for the one-token for
 
 __device__ inline int cb2_boff(int q, int s) { return 32 * (2 * q + (s >> 2)) + 8 * (s & 3); }
 __device__ inline int q2k_boff(int q, int s) { return 16 * (4 * q + (s >> 1)) + 8 * (s & 1); }
+
+// Decode's h keeps each 16-row sub-block pair-interleaved for the Q2K down
+// product: row r of the sub-block is stored at q2k_pair_pos(r), i.e. in the
+// order 0, 8, 1, 9, ..., 7, 15, so binary16 pair i of the activations holds
+// rows i and i + 8, the two codes of weight pair i.
+__host__ __device__ constexpr int q2k_pair_pos(int r) { return 2 * (r & 7) + (r >> 3); }
+
 __device__ inline int clamp_index(int v, int n) { return (unsigned)v < (unsigned)n ? v : 0; }
 
 // 8 activations x[t][k0 .. k0+7] (bf16 bits or fp32) as binary16 hi and lo parts.
@@ -654,7 +662,8 @@ __global__ __launch_bounds__(kW * 64) __attribute__((amdgpu_waves_per_eu(stage2_
   }
   // MFMA rows 4q..4q+3: their tokens' slots for this expert (BL: row j is
   // token j; else the j-th token of tmask); h = w * silu(g) * u as binary16
-  // into hw16[slot][row], and the 16-row sums into hsum
+  // into hw16[slot][row] (pair-interleaved within the 16-row tile), and the
+  // 16-row sums into hsum
   int slots[4];
   if constexpr (BL) {
     const int4 sl4 = *(const int4*)(ro.tok_slot + i * kDecodeGroup + 4 * q);
@@ -678,7 +687,7 @@ __global__ __launch_bounds__(kW * 64) __attribute__((amdgpu_waves_per_eu(stage2_
     float hv = 0.0f;
     if (has) {
       const _Float16 h16 = (_Float16)(ro.w[slot] * (silu(ag[r]) * au[r]));
-      hw16[(int64_t)slot * f + row0 + c] = h16;
+      hw16[(int64_t)slot * f + row0 + q2k_pair_pos(c)] = h16;  // pair-interleaved for the Q2K down product
       hv = (float)h16;
     }
     // sum over the 16 rows (lanes 16q..16q+15): quad, half-row and row mirrors
@@ -858,14 +867,6 @@ __device__ inline Q2kOff q2k_offsets(size_t mb, int nb, int row0, int c, int q) 
   return o;
 }
 
-// base: the expert's packed down matrix (wave-uniform); b: super-block (wave-uniform).
-__device__ inline void q2k_wload(Q2kW& U, const uint8_t* base, const Q2kOff& o, int b) {
-  U.codes = __builtin_nontemporal_load((const u32x4_t*)(base + o.codes + b * 64));
-  U.sc4 = *(const uint32_t*)(base + o.sc + b * 16);
-  U.mins = *(const u32x2_t*)(base + o.mins + b * 16);
-  U.sup = *(const uint32_t*)(base + o.sup + b * 4);
-}
-
 // Activation operands of one unit for lane (c, q): its token's binary16 h at
 // the lane's K offsets and the hi/lo sums of the 16 sub-blocks.
 struct Q2kA {
@@ -873,53 +874,109 @@ struct Q2kA {
 };
 
 // bcol: the activation row of the lane's token at the unit's super-block
-// (LDS or global); csh/csl: binary16 hi/lo of its 16 sub-block sums.
-// (on: the lane's token has a slot for the unit's expert; a lane without
-// one takes zeros and issues no loads, its products being masked anyway)
-__device__ inline void q2k_act(Q2kA& A, const _Float16* bcol, const _Float16* csh, const _Float16* csl, int q,
-                               bool on = true) {
-  if (on) {
+// (LDS); csh/csl: binary16 hi/lo of its 16 sub-block sums.
+__device__ inline void q2k_act(Q2kA& A, const _Float16* bcol, const _Float16* csh, const _Float16* csl, int q) {
 #pragma unroll
-    for (int s = 0; s < 8; ++s) A.b[s] = *(const half8_t*)(bcol + q2k_boff(q, s));
-    A.bh = *(const half8_t*)(csh + 8 * (q & 1));
-    A.bl = *(const half8_t*)(csl + 8 * (q & 1));
-  } else {
+  for (int s = 0; s < 8; ++s) A.b[s] = *(const half8_t*)(bcol + q2k_boff(q, s));
+  A.bh = *(const half8_t*)(csh + 8 * (q & 1));
+  A.bl = *(const half8_t*)(csl + 8 * (q & 1));
+}
+
+// Q2K codes at unit weight.  The two codes of pair i of a sub-block (codes i
+// and i + 8: bits 2i and 2i + 16 of its u32 u, the same bits of the word's
+// two 16-bit halves) are taken by one three-input bit operation from u << 4,
+// u >> 2 or u >> 8, which puts them at mantissa bit 4, 6 or 8 under an
+// exponent that gives that bit weight one: each binary16 half reads
+// base + q exactly, base 64, 16 or 4.
+//   pairs 0, 3, 6 -> bit 4 (base 64), 1, 4, 7 -> bit 6 (base 16), 2, 5 -> bit 8 (base 4).
+__host__ __device__ constexpr int q2k_pair_base(int i) { return i % 3 == 0 ? 64 : (i % 3 == 1 ? 16 : 4); }
+
+__device__ inline void q2k_pairs_unit_weight(uint32_t u, uint32_t (&w)[8]) {
+  const uint32_t a = u << 4, b = u >> 2, c = u >> 8;
+  // (x & mask) | magic: 0x5400 = 64, 0x4C00 = 16, 0x4400 = 4 (binary16)
+  w[0] = __builtin_amdgcn_bitop3_b32(a, 0x00300030u, 0x54005400u, 0xEA);
+  w[1] = __builtin_amdgcn_bitop3_b32(a, 0x00C000C0u, 0x4C004C00u, 0xEA);
+  w[2] = __builtin_amdgcn_bitop3_b32(a, 0x03000300u, 0x44004400u, 0xEA);
+  w[3] = __builtin_amdgcn_bitop3_b32(b, 0x00300030u, 0x54005400u, 0xEA);
+  w[4] = __builtin_amdgcn_bitop3_b32(b, 0x00C000C0u, 0x4C004C00u, 0xEA);
+  w[5] = __builtin_amdgcn_bitop3_b32(b, 0x03000300u, 0x44004400u, 0xEA);
+  w[6] = __builtin_amdgcn_bitop3_b32(c, 0x00300030u, 0x54005400u, 0xEA);
+  w[7] = __builtin_amdgcn_bitop3_b32(c, 0x00C000C0u, 0x4C004C00u, 0xEA);
+}
+
+// Both B fragments of one Q2K sub-block in pair order (dwords 0..3: pairs
+// 0..3, then 4..7), as binary16 s q, exact: one fma per pair scales the
+// unit-weight pair and removes its base, (base + q) s - base s.
+__device__ inline void q2k_subblock_paired(uint32_t u, uint32_t s, half8_t& lo, half8_t& hi) {
+  uint32_t w[8];
+  q2k_pairs_unit_weight(u, w);
+  const _Float16 S = (_Float16)(uint16_t)s;
+  const half2_t S2 = {S, S};
+  const half2_t C[3] = {S2 * (half2_t){(_Float16)-64.0f, (_Float16)-64.0f},
+                        S2 * (half2_t){(_Float16)-16.0f, (_Float16)-16.0f},
+                        S2 * (half2_t){(_Float16)-4.0f, (_Float16)-4.0f}};  // -base s, by pair i % 3
+  u32x4_t a, b;
 #pragma unroll
-    for (int s = 0; s < 8; ++s) A.b[s] = zero_half8();
-    A.bh = zero_half8();
-    A.bl = zero_half8();
+  for (int i = 0; i < 4; ++i) {
+    a[i] = as_u32(__builtin_elementwise_fma(as_half2(w[i]), S2, C[i % 3]));
+    b[i] = as_u32(__builtin_elementwise_fma(as_half2(w[4 + i]), S2, C[(4 + i) % 3]));
   }
+  lo = as_half8(a);
+  hi = as_half8(b);
+}
+
+// The high nibbles (the 4-bit mins) of bytes j and j + 1 of w as a binary16
+// pair: one byte permute puts byte j in the low half and byte j + 1 in the
+// high half, the bit operation sets the exponent that gives bit 4 weight one
+// (64 + m), and one subtraction removes the 64.
+template <int J>
+__device__ inline uint32_t min_pair_f16(uint32_t w) {
+  constexpr uint32_t sel = J == 0 ? 0x01010000u : 0x03030202u;
+  const uint32_t x = __builtin_amdgcn_bitop3_b32(__builtin_amdgcn_perm(0u, w, sel), 0x00F000F0u, 0x54005400u, 0xEA);
+  return as_u32(as_half2(x) - (half2_t){(_Float16)64.0f, (_Float16)64.0f});
 }
 
 // One unit, transposed: the activations are the MFMA's A operand (row c' =
 // token c'), the weights its B operand, so lane (c, q) ends with tokens
-// 4q..4q+3 of row row0 + c.  vmask: bit r set when token 4q + r has a slot
-// for this expert.
+// 4q..4q+3 of row row0 + c.  The activations are pair-interleaved
+// (q2k_pair_pos).  MASKED: bit r of vmask set when token 4q + r has a slot
+// for this expert, the other tokens' products are dropped; else those
+// tokens' activations (and the sums of lanes q >= 2) are zeros already, so
+// their products are exactly zero.
+template <bool MASKED>
 __device__ inline void q2k_unit(const Q2kW& U, const Q2kA& A, uint32_t vmask, int q, float4_t& acc) {
   float4_t p = {0.f, 0.f, 0.f, 0.f}, pm = p;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {  // sub-block 4q + j: two MFMA steps share its scale
     half8_t alo, ahi;
-    q2k_subblock(U.codes[j], (U.sc4 >> (8 * j)) & 15u, alo, ahi);
+    q2k_subblock_paired(U.codes[j], (U.sc4 >> (8 * j)) & 15u, alo, ahi);
     p = mfma16x16x32(A.b[2 * j], alo, p);
     p = mfma16x16x32(A.b[2 * j + 1], ahi, p);
   }
   // min term: K-slots 0..15 are the 16 sub-blocks (lane groups q >= 2 add zeros)
   u32x4_t t;
-  t.x = nib_hi_pair_f16(U.mins.x, 0);
-  t.y = nib_hi_pair_f16(U.mins.x, 2);
-  t.z = nib_hi_pair_f16(U.mins.y, 0);
-  t.w = nib_hi_pair_f16(U.mins.y, 2);
-  const half8_t am = q < 2 ? as_half8(t) : zero_half8();
+  t.x = min_pair_f16<0>(U.mins.x);
+  t.y = min_pair_f16<1>(U.mins.x);
+  t.z = min_pair_f16<0>(U.mins.y);
+  t.w = min_pair_f16<1>(U.mins.y);
+  const half8_t am = !MASKED || q < 2 ? as_half8(t) : zero_half8();
   pm = mfma16x16x32(A.bh, am, pm);
   pm = mfma16x16x32(A.bl, am, pm);
   const float dd = h2f((uint16_t)(U.sup & 0xFFFFu)), dm = h2f((uint16_t)(U.sup >> 16));
 #pragma unroll
-  for (int r = 0; r < 4; ++r) acc[r] += ((vmask >> r) & 1u) ? dd * p[r] - dm * pm[r] : 0.0f;
+  for (int r = 0; r < 4; ++r) {
+    if constexpr (MASKED) {
+      acc[r] += ((vmask >> r) & 1u) ? dd * p[r] - dm * pm[r] : 0.0f;
+    } else {
+      acc[r] = __builtin_fmaf(dd, p[r], acc[r]);
+      acc[r] = __builtin_fmaf(-dm, pm[r], acc[r]);
+    }
+  }
 }
 
 constexpr int kW3 = 16;     // waves per stage-3 block: 4 per SIMD, few units each
 constexpr int kUnits3 = 3;  // units whose weight loads a wave keeps in flight
+constexpr int kRing3 = 3;   // stage-3 ring slots per wave: one unit computing, the next two requested
 
 // Block `tile`: output rows tile*16 .. tile*16+15 of the shared expert's
 // down product and of every (distinct expert, super-block) unit, so the
@@ -944,7 +1001,7 @@ __device__ inline void q4k_unit(const Q4kSb& U, const Q2kA& A, uint32_t vmask, i
   for (int r = 0; r < 4; ++r) acc[r] += ((vmask >> r) & 1u) ? p[r] : 0.0f;
 }
 
-template <bool BL, bool MX, bool Q4 = false>
+template <bool BL, bool MX, bool Q4 = false, bool PH = false>
 __global__ __launch_bounds__(kW3 * 64) __attribute__((amdgpu_waves_per_eu(4))) void k_dec_stage3(
     ds4moe_layer L, int T, const int32_t* __restrict__ ndist, const int32_t* __restrict__ distinct,
     const int32_t* __restrict__ tok_slot, const _Float16* __restrict__ hw16, const _Float16* __restrict__ hsum,
@@ -966,6 +1023,36 @@ __global__ __launch_bounds__(kW3 * 64) __attribute__((amdgpu_waves_per_eu(4))) v
   _Float16* s_h = (_Float16*)s_dyn;
   _Float16* s_cs = s_h + (size_t)S * f;
   _Float16* s_hs = s_cs + (size_t)2 * S * fs16;
+  // phased (PH): super-block p's activation columns [S][QK] and (Q2K) their
+  // sums [2S][16] in LDS buffer p % 2 (h rows padded to an even count, sum
+  // rows to a multiple of 32), the next super-block's copy in flight into
+  // the other buffer while this one computes.  A phase is copied in 1 KB
+  // chunks, buffer loads straight into LDS: h chunk ch = rows 2ch, 2ch + 1
+  // (32 lanes a row), sums chunk cs = rows 32cs .. 32cs + 31 (2 lanes a row);
+  // rows past the last read zeros (the buffer's range check) into the
+  // padding.  Chunks ch and cs are wave ch % kW3's and cs % kW3's.
+  const int ph_hrows = (S + 1) & ~1, ph_srows = MX || Q4 ? 0 : (2 * S + 31) & ~31;
+  const int ph_hch = ph_hrows / 2, ph_sch = ph_srows / 32;
+  const uint32_t ph_bytes = (uint32_t)(ph_hrows * QK * 2 + ph_srows * 32);
+  auto ph_h = [&](int p) { return (_Float16*)(s_dyn + (p & 1) * ph_bytes); };
+  auto ph_cs = [&](int p) { return ph_h(p) + (size_t)ph_hrows * QK; };
+  unsigned char* ph_sink = s_dyn + 2 * ph_bytes;  // 1 KB that chunks past the last land in (reading nothing)
+  const uint32_t ph_vh = (uint32_t)(lane >> 5) * (uint32_t)(2 * f) + (uint32_t)(lane & 31) * 16u;
+  const uint32_t ph_vs = (uint32_t)(lane >> 1) * (uint32_t)(2 * fs16) + (uint32_t)(lane & 1) * 16u;
+  const __amdgpu_buffer_rsrc_t rh = buf_rsrc(hw16, (uint32_t)(S * f * 2));
+  const __amdgpu_buffer_rsrc_t rs = buf_rsrc(hsum, (uint32_t)(2 * S * fs16 * 2));
+  auto dma_h = [&](int p, int ch) {  // h chunk ch of phase p; none past the last
+    const bool in = ch < ph_hch;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rh, (__attribute__((address_space(3))) void*)(in ? (unsigned char*)(ph_h(p) + ch * 512) : ph_sink), 16,
+        in ? ph_vh + (uint32_t)ch * (uint32_t)(4 * f) : kOob, (uint32_t)p * (2 * QK), 0, 0);
+  };
+  auto dma_s = [&](int p, int cs) {  // sums chunk cs of phase p; none past the last
+    const bool in = cs < ph_sch;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rs, (__attribute__((address_space(3))) void*)(in ? (unsigned char*)(ph_cs(p) + cs * 512) : ph_sink), 16,
+        in ? ph_vs + (uint32_t)cs * (uint32_t)(64 * fs16) : kOob, (uint32_t)p * 32u, 0, 0);
+  };
   if (blockIdx.x == 0)
     for (int i = threadIdx.x; i < nctrl1; i += blockDim.x) ctrl[i] = 0;
   // copies of the activations into LDS; one barrier publishes them
@@ -974,84 +1061,99 @@ __global__ __launch_bounds__(kW3 * 64) __attribute__((amdgpu_waves_per_eu(4))) v
     if (!MX && !Q4) dma_rows(hsum, fs16, 2 * S, fs16, s_cs, fs16, wave, kW3, lane);
     dma_rows(hs16, fs, T, fs, s_hs, fs, wave, kW3, lane);
   }
+  if (PH) {
+    for (int ch = wave; ch < ph_hch; ch += kW3) dma_h(0, ch);
+    for (int cs = wave; cs < ph_sch; cs += kW3) dma_s(0, cs);
+  }
   // routing tables: expert ids by scalar loads, which do not wait for the
   // copies, so the first weight batch goes out while they are in flight
   const int nd = max(1, min(ld_uniform(ndist), maxd));  // a call selects at least one expert
-  const int nunits = nd * nb;  // only the selected experts' units: their weights alone are read
-  // units u = (expert slot u / nb, super-block u % nb); wave w takes
-  // u = w, w + kW3, ... in batches of kUnits3
-  int sj[kUnits3], bsb[kUnits3];  // per unit: slot of token c, super-block
-  Q2kW W[kUnits3];
-  Mx4Sb WM[kUnits3];  // MXFP4: the lane's two blocks of the unit's super-block
-  Q4kSb WQ[kUnits3];  // Q4K: the same, with the block's scale words
+  // PH pads the experts to at least 32 (see below): units of padding slots
+  // read the last expert's weights again and take no token
+  const int nde = PH ? max(nd, 32) : nd;
+  const int nunits = nde * nb;  // only the selected experts' units: their weights alone are read
+  // units u = (expert slot u / nb, super-block u % nb), or with PH
+  // super-block major, (u % nd, u / nd); wave w takes
+  // u = w, w + kW3, ...  Its m-th unit sits in ring slot m % kRing3 and its
+  // weights are requested kRing3 - 1 units before that unit computes, so a
+  // wave always has the next units' loads in flight behind the current one.
+  int sj[kRing3], bsb[kRing3];  // per slot: slot of token c, super-block
+  bool rl[kRing3];              // per slot: a selected expert's unit (not padding)
+  Q2kW W[kRing3];
+  Mx4Sb WM[kRing3];  // MXFP4: the lane's two blocks of the unit's super-block
+  Q4kSb WQ[kRing3];  // Q4K: the same, with the block's scale words
   const Q2kOff off = q2k_offsets(mb, nb, row0, c, q);
   const size_t mx_bytes = Q4 ? mb * 144 : (size_t)d * f * 17 / 32;  // one packed MXFP4 / Q4K [d, f] matrix
   const uint32_t mx_codes = (uint32_t)((size_t)(row0 + c) * (f / 2) + 32 * q);
   const uint32_t mx_sc = (uint32_t)((size_t)d * f / 2 + (size_t)(row0 + c) * (f / 32) + 2 * q);
   const uint32_t q4_sc = (uint32_t)(mb * 128 + (size_t)(row0 + c) * nb * 12);
   const uint32_t q4_sp = (uint32_t)(mb * 140 + (size_t)(row0 + c) * nb * 4);
-  // unit u -> (expert slot u / nb, super-block u % nb), stepped by kW3
+  const uint32_t ebytes = (uint32_t)(MX || Q4 ? mx_bytes : mb * 84);  // one expert's packed down matrix
+  // unstaged activations come from the buffers rh and rs: a lane whose
+  // token has no slot for the unit's expert reads zeros (offset kOob), so
+  // its products are zero and need no mask
+  // the unit to request next as (major, minor) index, stepped by kW3
   // without a division per unit
-  const int di = kW3 / nb, db = kW3 % nb;
-  auto unit_at = [&](int u, int& i, int& b) {
-    i = u / nb;
-    b = u - i * nb;
-  };
-  auto step_unit = [&](int& i, int& b) {
-    i += di;
-    b += db;
-    if (b >= nb) {
-      b -= nb;
-      ++i;
+  const int nmin = PH ? nde : nb;
+  const int dmaj = kW3 / nmin, dmin = kW3 % nmin;
+  int pmaj = wave / nmin, pmin = wave - (wave / nmin) * nmin;
+  auto load_unit = [&](int r) {  // r: ring slot, fixed once unrolled
+    int i = PH ? pmin : pmaj, b = PH ? pmaj : pmin;
+    if (PH ? b >= nb : i >= nd) {  // units past the end repeat the last one
+      i = nd - 1;
+      b = nb - 1;
+    }
+    rl[r] = i < nd;
+    i = min(i, nd - 1);
+    const int e = clamp_index(ld_uniform(distinct + i), L.n_experts);
+    // the expert's matrix as a buffer: the lane's offsets stay in VGPRs, the
+    // super-block's goes in an SGPR, so no per-unit address arithmetic
+    const __amdgpu_buffer_rsrc_t rw = buf_rsrc(down + (size_t)e * ebytes, ebytes);
+    if constexpr (Q4) {
+      WQ[r].c0 = buf_ld128<kBufNt>(rw, mx_codes, 128 * b);
+      WQ[r].c1 = buf_ld128<kBufNt>(rw, mx_codes + 16, 128 * b);
+      const u32x3_t sw = buf_ld96(rw, q4_sc, 12 * b);  // one 12-byte load
+      WQ[r].w0 = sw.x;
+      WQ[r].w1 = sw.y;
+      WQ[r].w2 = sw.z;
+      WQ[r].sup = buf_ld32(rw, q4_sp, 4 * b);
+    } else if constexpr (MX) {
+      WM[r].c0 = buf_ld128<kBufNt>(rw, mx_codes, 128 * b);
+      WM[r].c1 = buf_ld128<kBufNt>(rw, mx_codes + 16, 128 * b);
+      WM[r].sc = buf_ld16(rw, mx_sc, 8 * b);
+    } else {
+      W[r].codes = buf_ld128<kBufNt>(rw, off.codes, 64 * b);
+      W[r].sc4 = buf_ld32(rw, off.sc, 16 * b);
+      W[r].mins = buf_ld64(rw, off.mins, 16 * b);
+      W[r].sup = buf_ld32(rw, off.sup, 4 * b);
+    }
+    sj[r] = tok_slot[i * kDecodeGroup + c];
+    bsb[r] = b;
+    pmaj += dmaj;
+    pmin += dmin;
+    if (pmin >= nmin) {
+      pmin -= nmin;
+      ++pmaj;
     }
   };
-  auto load_batch = [&](int u0) {
-    int ij[kUnits3], bj[kUnits3], ej[kUnits3];
-    unit_at(u0, ij[0], bj[0]);
 #pragma unroll
-    for (int j = 1; j < kUnits3; ++j) {
-      ij[j] = ij[j - 1];
-      bj[j] = bj[j - 1];
-      step_unit(ij[j], bj[j]);
-    }
+  for (int r = 0; r < kRing3 - 1; ++r) load_unit(r);
 #pragma unroll
-    for (int j = 0; j < kUnits3; ++j) {  // units past the end repeat the last one
-      if (ij[j] >= nd) {
-        ij[j] = nd - 1;
-        bj[j] = nb - 1;
-      }
-      ej[j] = ld_uniform(distinct + ij[j]);  // all expert ids in flight before the first address needs one
-    }
-    pin();
-#pragma unroll
-    for (int j = 0; j < kUnits3; ++j) {
-      if constexpr (Q4) {
-        const uint8_t* base = down + (size_t)clamp_index(ej[j], L.n_experts) * mx_bytes;
-        WQ[j].c0 = __builtin_nontemporal_load((const u32x4_t*)(base + mx_codes + 128 * bj[j]));
-        WQ[j].c1 = __builtin_nontemporal_load((const u32x4_t*)(base + mx_codes + 128 * bj[j] + 16));
-        const u32x3_t sw = *(const u32x3_a4_t*)(base + q4_sc + 12 * bj[j]);  // one 12-byte load
-        WQ[j].w0 = sw.x;
-        WQ[j].w1 = sw.y;
-        WQ[j].w2 = sw.z;
-        WQ[j].sup = *(const uint32_t*)(base + q4_sp + 4 * bj[j]);
-      } else if constexpr (MX) {
-        const uint8_t* base = down + (size_t)clamp_index(ej[j], L.n_experts) * mx_bytes;
-        WM[j].c0 = __builtin_nontemporal_load((const u32x4_t*)(base + mx_codes + 128 * bj[j]));
-        WM[j].c1 = __builtin_nontemporal_load((const u32x4_t*)(base + mx_codes + 128 * bj[j] + 16));
-        WM[j].sc = *(const uint16_t*)(base + mx_sc + 8 * bj[j]);
-      } else {
-        q2k_wload(W[j], down + (size_t)clamp_index(ej[j], L.n_experts) * mb * 84, off, bj[j]);
-      }
-      sj[j] = tok_slot[ij[j] * kDecodeGroup + c];
-      bsb[j] = bj[j];
-    }
-  };
-  load_batch(wave);
-#pragma unroll
-  for (int j = 0; j < kUnits3; ++j) asm volatile("" ::"v"(sj[j]));  // keeps these loads ahead of the barrier
+  for (int r = 0; r < kRing3 - 1; ++r) asm volatile("" ::"v"(sj[r]));  // keeps these loads ahead of the barrier
   asm volatile("" ::"s"(nd));
-  wait_all();  // the copies (and the first batch)
+  wait_all();  // the copies (and the first units)
   __syncthreads();
+  // PH, with the experts padded to at least 32: every wave has at least two
+  // units a phase and meets at most one phase change a unit.  Each unit step sends
+  // two h chunks and one sums chunk of the next phase (a wave has at most 4
+  // and 1 a phase) ahead of its kLdU weight loads, so at a phase change this wave's
+  // copies are done once all but the last kLdU loads are; the barrier then
+  // publishes everyone's and shows every wave done with the buffer the next
+  // phase's copy overwrites.
+  const bool phased = PH;
+  constexpr int kLdU = MX ? 4 : 5;  // vector-memory instructions of load_unit (after the copies)
+  int cur = 0;  // phased: the phase (super-block) in LDS buffer cur % 2
+  int pj = 0;   // phased: h chunks of phase cur + 1 this wave has sent
   // the shared expert's down rows (this wave's K-steps) stream in while the
   // routed units compute: issued after the barrier, so no wait above
   // includes them
@@ -1064,35 +1166,91 @@ __global__ __launch_bounds__(kW3 * 64) __attribute__((amdgpu_waves_per_eu(4))) v
   for (int j = 0; j < kBatchS; ++j) sa[j] = *(const half8_t*)(srow + max(min(sk0 + j, sk1 - 1), 0) * 32 + 8 * q);
   pin();
   float4_t acc = {0.f, 0.f, 0.f, 0.f};
-  for (int u0 = wave; u0 < nunits; u0 += kW3 * kUnits3) {
-    if (u0 != wave) load_batch(u0);
-    pin();
-    // units past the end and tokens without a slot add nothing
+  // one step: activations of the slot's unit, the request of the unit
+  // kRing3 - 1 ahead into the slot freed last step, then the products.
+  // Global activations go out before that request (a wait for them then
+  // leaves it in flight); LDS ones after it (the expert id's scalar load
+  // is waited for with a count that would include them).
+  auto routed = [&](auto phased_tag) {
+    constexpr bool P = decltype(phased_tag)::value;  // activations from the phase buffers
+    for (int m0 = 0;; m0 += kRing3) {
 #pragma unroll
-    for (int j = 0; j < kUnits3; ++j) {
-      const int u = u0 + j * kW3;
-      const int slot = sj[j];  // slot of token c for this unit's expert
-      const bool has = u < nunits && slot >= 0 && slot < S;
-      const uint32_t vmask = (uint32_t)(__ballot(has) >> (4 * q)) & 15u;  // tokens 4q..4q+3
-      const int row = has ? slot : 0;
-      const int b = bsb[j];  // super-block
-      Q2kA A;
-      if constexpr (MX || Q4) {
-        const _Float16* bcol = (BL ? s_h : hw16) + (size_t)row * f + b * QK;
+      for (int r = 0; r < kRing3; ++r) {
+        if (wave + (m0 + r) * kW3 >= nunits) return;
+        if constexpr (P) {
+          if (bsb[r] != cur) {  // the next phase (wave-uniform)
+            vm_wait<kLdU>();
+            ring_barrier();
+            cur = bsb[r];
+            pj = 0;
+          }
+          const int pn = min(cur + 1, nb - 1);  // in the last phase: its own chunks again, unchanged data
+          dma_h(pn, wave + kW3 * pj);
+          dma_h(pn, wave + kW3 * (pj + 1));
+          if constexpr (!MX && !Q4) dma_s(pn, wave);
+          pj += 2;
+          pin();
+        }
+        const int slot = sj[r];  // slot of token c for this unit's expert
+        const bool has = rl[r] && slot >= 0 && slot < S;  // tokens without a slot add nothing
+        // staged: every lane reads a valid row and the products of tokens
+        // without a slot are masked (tokens 4q..4q+3); unstaged: those
+        // tokens read zeros, which leaves Q2K products exactly zero (its
+        // weights are small integers), while MXFP4 and Q4K weights, scaled
+        // in binary16, keep the mask in case a scale overflowed to inf
+        const uint32_t vmask = BL || P || MX || Q4 ? (uint32_t)(__ballot(has) >> (4 * q)) & 15u : 15u;
+        const int row = has ? slot : 0;
+        const int b = bsb[r];  // super-block
+        Q2kA A;
+        auto act = [&]() {
+          if constexpr (BL || P) {
+            const _Float16* bcol = BL ? s_h + (size_t)row * f + b * QK : ph_h(b) + (size_t)row * QK;
+            if constexpr (MX || Q4) {
 #pragma unroll
-        for (int s2 = 0; s2 < 8; ++s2) A.b[s2] = has ? *(const half8_t*)(bcol + q2k_boff(q, s2)) : zero_half8();
-        if constexpr (Q4) q4k_unit(WQ[j], A, vmask, q, acc);
-        else mx4_unit(WM[j], A, vmask, acc);
-      } else {
-        if (BL)
-          q2k_act(A, s_h + (size_t)row * f + b * QK, s_cs + (size_t)row * fs16 + b * 16,
-                  s_cs + (size_t)(S + row) * fs16 + b * 16, q);
-        else
-          q2k_act(A, hw16 + (size_t)row * f + b * QK, hsum + (size_t)row * fs16 + b * 16,
-                  hsum + (size_t)(S + row) * fs16 + b * 16, q, has);
-        q2k_unit(W[j], A, vmask, q, acc);
+              for (int s2 = 0; s2 < 8; ++s2) A.b[s2] = *(const half8_t*)(bcol + q2k_boff(q, s2));
+            } else if constexpr (BL) {
+              q2k_act(A, bcol, s_cs + (size_t)row * fs16 + b * 16, s_cs + (size_t)(S + row) * fs16 + b * 16, q);
+            } else {
+              q2k_act(A, bcol, ph_cs(b) + (size_t)row * 16, ph_cs(b) + (size_t)(S + row) * 16, q);
+            }
+          } else {
+            // byte offsets: row * 2f + 2 q2k_boff(q, s2) in the activations,
+            // row * 2 fs16 + 16 (q & 1) in the hi sums, S * 2 fs16 further on
+            // in the lo sums; the super-block's part is wave-uniform
+            const uint32_t vo = has ? (uint32_t)row * (uint32_t)(2 * f) + 128u * q : kOob;
+#pragma unroll
+            for (int s2 = 0; s2 < 8; ++s2) A.b[s2] = as_half8(buf_ld128(rh, vo + 16u * s2, (uint32_t)b * (2 * QK)));
+            if constexpr (!MX && !Q4) {  // lane groups q >= 2 take zero sums (their min operand is unused)
+              const uint32_t vs = has && q < 2 ? (uint32_t)row * (uint32_t)(2 * fs16) + 16u * q : kOob;
+              A.bh = as_half8(buf_ld128(rs, vs, (uint32_t)b * 32u));
+              A.bl = as_half8(buf_ld128(rs, vs, (uint32_t)b * 32u + (uint32_t)(S * fs16 * 2)));
+            }
+          }
+        };
+        if (!BL && !P) act();
+        pin();
+        load_unit((r + kRing3 - 1) % kRing3);
+        pin();
+        if (BL || P) act();
+        if constexpr (Q4) q4k_unit(WQ[r], A, vmask, q, acc);
+        else if constexpr (MX) mx4_unit(WM[r], A, vmask, acc);
+        else q2k_unit<BL || P>(W[r], A, vmask, q, acc);
       }
     }
+  };
+  if (phased) {
+    routed(std::true_type{});
+    // every wave meets every phase's barrier and sends its chunks of each
+    while (cur < nb - 1) {
+      for (int j = pj; wave + kW3 * j < ph_hch; ++j) dma_h(cur + 1, wave + kW3 * j);
+      if (!MX && !Q4 && wave < ph_sch) dma_s(cur + 1, wave);
+      vm_wait<0>();
+      ring_barrier();
+      ++cur;
+      pj = 0;
+    }
+  } else {
+    if constexpr (!PH) routed(std::false_type{});
   }
   // shared expert, transposed like the routed units: lane (c, q) ends with
   // tokens 4q..4q+3 of row row0 + c
@@ -1131,25 +1289,6 @@ __global__ __launch_bounds__(kW3 * 64) __attribute__((amdgpu_waves_per_eu(4))) v
 // sum_k q_k h_k + OFF, OFF = sum_k base_k h_k, and the sub-block adds
 // d s (dot - OFF) - dmin m HS with HS = sum_k h_k.  OFF and HS come from the
 // same binary16 h, once per block.
-//
-// Pair i of sub-block u32 u (codes at bits 2i and 2i + 16) is taken from
-// u << 4, u >> 2 or u >> 8, which moves it to mantissa bit 4, 6 or 8:
-//   pairs 0, 3, 6 -> bit 4 (base 64), 1, 4, 7 -> bit 6 (base 16), 2, 5 -> bit 8 (base 4).
-__host__ __device__ constexpr int q2k_pair_base(int i) { return i % 3 == 0 ? 64 : (i % 3 == 1 ? 16 : 4); }
-
-__device__ inline void q2k_pairs_unit_weight(uint32_t u, uint32_t (&w)[8]) {
-  const uint32_t a = u << 4, b = u >> 2, c = u >> 8;
-  // (x & mask) | magic: 0x5400 = 64, 0x4C00 = 16, 0x4400 = 4 (binary16)
-  w[0] = __builtin_amdgcn_bitop3_b32(a, 0x00300030u, 0x54005400u, 0xEA);
-  w[1] = __builtin_amdgcn_bitop3_b32(a, 0x00C000C0u, 0x4C004C00u, 0xEA);
-  w[2] = __builtin_amdgcn_bitop3_b32(a, 0x03000300u, 0x44004400u, 0xEA);
-  w[3] = __builtin_amdgcn_bitop3_b32(b, 0x00300030u, 0x54005400u, 0xEA);
-  w[4] = __builtin_amdgcn_bitop3_b32(b, 0x00C000C0u, 0x4C004C00u, 0xEA);
-  w[5] = __builtin_amdgcn_bitop3_b32(b, 0x03000300u, 0x44004400u, 0xEA);
-  w[6] = __builtin_amdgcn_bitop3_b32(c, 0x00300030u, 0x54005400u, 0xEA);
-  w[7] = __builtin_amdgcn_bitop3_b32(c, 0x00C000C0u, 0x4C004C00u, 0xEA);
-}
-
 __device__ inline float dot2(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2(as_half2(a), as_half2(b), c, false);
 }
@@ -1218,20 +1357,18 @@ __global__ __launch_bounds__(kW3 * 64) __attribute__((amdgpu_waves_per_eu(4))) v
   // (slot, sub-block) per thread; the shared expert's h by copy
   dma_rows(hs16, fs, 1, fs, s_sh, fs, wave, kW3, lane);
   for (int t = threadIdx.x; t < S * nsb; t += blockDim.x) {
-    const u32x4_t lo = *(const u32x4_t*)(hw16 + (size_t)t * 16), hi = *(const u32x4_t*)(hw16 + (size_t)t * 16 + 8);
-    const half8_t hl = as_half8(lo), hh = as_half8(hi);
+    // h is pair-interleaved already: binary16 pair i holds rows i and i + 8
+    const u32x4_t p0 = *(const u32x4_t*)(hw16 + (size_t)t * 16), p1 = *(const u32x4_t*)(hw16 + (size_t)t * 16 + 8);
+    const half8_t h0 = as_half8(p0), h1 = as_half8(p1);
+    auto row_i = [&](int i) { return (float)(i < 4 ? h0[2 * i] : h1[2 * (i - 4)]); };             // row i
+    auto row_i8 = [&](int i) { return (float)(i < 4 ? h0[2 * i + 1] : h1[2 * (i - 4) + 1]); };  // row i + 8
     float off = 0.0f, hs = 0.0f;
-    u32x4_t p0, p1;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const half2_t pr = {hl[i], hh[i]};
-      if (i < 4) p0[i] = as_u32(pr); else p1[i - 4] = as_u32(pr);
-      off += (float)q2k_pair_base(i) * ((float)hl[i] + (float)hh[i]);
-    }
+    for (int i = 0; i < 8; ++i) off += (float)q2k_pair_base(i) * (row_i(i) + row_i8(i));
 #pragma unroll
-    for (int i = 0; i < 8; ++i) hs += (float)hl[i];
+    for (int i = 0; i < 8; ++i) hs += row_i(i);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) hs += (float)hh[i];
+    for (int i = 0; i < 8; ++i) hs += row_i8(i);
     *(u32x4_t*)(s_pair + (size_t)t * 8) = p0;
     *(u32x4_t*)(s_pair + (size_t)t * 8 + 4) = p1;
     s_off[t] = off;
@@ -1377,13 +1514,23 @@ hipError_t launch_decode(const Fwd& f) {
                hs16, ctrl, ctrl_ints(L), maxd, f.y);
     return hipGetLastError();
   }
-#define DS4_S3(BL_, MX_, Q4_, BYTES)                                                                  \
-  DS4_LAUNCH((k_dec_stage3<BL_, MX_, Q4_>), dim3(ndt), blk3, BYTES, f.st, L, T, ro.ndist, ro.distinct, \
+#define DS4_S3(BL_, MX_, Q4_, BYTES, ...)                                                                        \
+  DS4_LAUNCH((k_dec_stage3<BL_, MX_, Q4_, ##__VA_ARGS__>), dim3(ndt), blk3, BYTES, f.st, L, T, ro.ndist, ro.distinct, \
              ro.tok_slot, hw16, hsum, hs16, ctrl, ctrl_ints(L), maxd, f.y)
+  // else one super-block's columns at a time, double-buffered (rows padded
+  // as the kernel pads them, its 1 KB sink; at most 4 h and 1 sums copy
+  // chunks a wave and phase)
+  const int ph_hrows = (S + 1) & ~1, ph_srows = mx || q4 ? 0 : (2 * S + 31) & ~31;
+  const size_t phase_bytes = (size_t)2 * (ph_hrows * QK * 2 + ph_srows * 32) + 1024;
+  const bool ph_fits = phase_bytes <= kStage3Bytes && ph_hrows / 2 <= 4 * kW3 && ph_srows / 32 <= kW3;
   if (stage_bytes <= kStage3Bytes) {
     if (mx) DS4_S3(true, true, false, stage_bytes);
     else if (q4) DS4_S3(true, false, true, stage_bytes);
     else DS4_S3(true, false, false, stage_bytes);
+  } else if (ph_fits) {
+    if (mx) DS4_S3(false, true, false, phase_bytes, true);
+    else if (q4) DS4_S3(false, false, true, phase_bytes, true);
+    else DS4_S3(false, false, false, phase_bytes, true);
   } else {
     if (mx) DS4_S3(false, true, false, 0);
     else if (q4) DS4_S3(false, false, true, 0);
