@@ -1024,14 +1024,15 @@ __global__ __launch_bounds__(kW3 * 64) __attribute__((amdgpu_waves_per_eu(4))) v
   _Float16* s_cs = s_h + (size_t)S * f;
   _Float16* s_hs = s_cs + (size_t)2 * S * fs16;
   // phased (PH): super-block p's activation columns [S][QK] and (Q2K) their
-  // sums [2S][16] in LDS buffer p % 2 (h rows padded to an even count, sum
-  // rows to a multiple of 32), the next super-block's copy in flight into
-  // the other buffer while this one computes.  A phase is copied in 1 KB
-  // chunks, buffer loads straight into LDS: h chunk ch = rows 2ch, 2ch + 1
-  // (32 lanes a row), sums chunk cs = rows 32cs .. 32cs + 31 (2 lanes a row);
-  // rows past the last read zeros (the buffer's range check) into the
-  // padding.  Chunks ch and cs are wave ch % kW3's and cs % kW3's.
-  const int ph_hrows = (S + 1) & ~1, ph_srows = MX || Q4 ? 0 : (2 * S + 31) & ~31;
+  // sums [2S][16] in LDS buffer p % 2, the next super-block's copy in flight
+  // into the other buffer while this one computes.  A phase is copied in
+  // 1 KB chunks, buffer loads straight into LDS: h chunk ch = rows 2ch,
+  // 2ch + 1 (32 lanes a row), sums chunk cs = rows 32cs .. 32cs + 31 (2
+  // lanes a row); rows past the last read zeros (the buffer's range check).
+  // Padding: h to S + 1 rows rounded up to even, the sums to 2S + 1 rounded
+  // up to 32, so h row S and sums row 2S are zero rows.  Chunks ch and cs are
+  // wave ch % kW3's and cs % kW3's.
+  const int ph_hrows = (S + 2) & ~1, ph_srows = MX || Q4 ? 0 : (2 * S + 32) & ~31;
   const int ph_hch = ph_hrows / 2, ph_sch = ph_srows / 32;
   const uint32_t ph_bytes = (uint32_t)(ph_hrows * QK * 2 + ph_srows * 32);
   auto ph_h = [&](int p) { return (_Float16*)(s_dyn + (p & 1) * ph_bytes); };
@@ -1053,6 +1054,13 @@ __global__ __launch_bounds__(kW3 * 64) __attribute__((amdgpu_waves_per_eu(4))) v
         rs, (__attribute__((address_space(3))) void*)(in ? (unsigned char*)(ph_cs(p) + cs * 512) : ph_sink), 16,
         in ? ph_vs + (uint32_t)cs * (uint32_t)(64 * fs16) : kOob, (uint32_t)p * 32u, 0, 0);
   };
+  // this wave's chunks of phase p: a fixed number of instructions (at most
+  // 4 h chunks and 1 sums chunk are its own)
+  auto send_phase = [&](int p) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dma_h(p, wave + kW3 * j);
+    if constexpr (!MX && !Q4) dma_s(p, wave);
+  };
   if (blockIdx.x == 0)
     for (int i = threadIdx.x; i < nctrl1; i += blockDim.x) ctrl[i] = 0;
   // copies of the activations into LDS; one barrier publishes them
@@ -1061,10 +1069,7 @@ __global__ __launch_bounds__(kW3 * 64) __attribute__((amdgpu_waves_per_eu(4))) v
     if (!MX && !Q4) dma_rows(hsum, fs16, 2 * S, fs16, s_cs, fs16, wave, kW3, lane);
     dma_rows(hs16, fs, T, fs, s_hs, fs, wave, kW3, lane);
   }
-  if (PH) {
-    for (int ch = wave; ch < ph_hch; ch += kW3) dma_h(0, ch);
-    for (int cs = wave; cs < ph_sch; cs += kW3) dma_s(0, cs);
-  }
+  if (PH) send_phase(0);
   // routing tables: expert ids by scalar loads, which do not wait for the
   // copies, so the first weight batch goes out while they are in flight
   const int nd = max(1, min(ld_uniform(ndist), maxd));  // a call selects at least one expert
@@ -1144,27 +1149,23 @@ __global__ __launch_bounds__(kW3 * 64) __attribute__((amdgpu_waves_per_eu(4))) v
   wait_all();  // the copies (and the first units)
   __syncthreads();
   // PH, with the experts padded to at least 32: every wave has at least two
-  // units a phase and meets at most one phase change a unit.  Each unit step sends
-  // two h chunks and one sums chunk of the next phase (a wave has at most 4
-  // and 1 a phase) ahead of its kLdU weight loads, so at a phase change this wave's
-  // copies are done once all but the last kLdU loads are; the barrier then
-  // publishes everyone's and shows every wave done with the buffer the next
-  // phase's copy overwrites.
+  // units a phase and meets at most one phase change a unit.  Entering
+  // phase p, a wave sends its chunks of phase p + 1; at least two units'
+  // kLdU weight loads follow them before it enters p + 1, so its copies are
+  // done once all but the last 2 kLdU loads are (the weights of the next
+  // two units stay in flight).  The barrier then publishes everyone's copies
+  // and shows every wave done with the buffer the next phase's copy
+  // overwrites.
   const bool phased = PH;
-  constexpr int kLdU = MX ? 4 : 5;  // vector-memory instructions of load_unit (after the copies)
+  constexpr int kLdU = MX ? 4 : 5;  // vector-memory instructions of load_unit
   int cur = 0;  // phased: the phase (super-block) in LDS buffer cur % 2
-  int pj = 0;   // phased: h chunks of phase cur + 1 this wave has sent
-  // the shared expert's down rows (this wave's K-steps) stream in while the
-  // routed units compute: issued after the barrier, so no wait above
-  // includes them
+  if (PH) send_phase(min(1, nb - 1));  // one phase only: its own chunks again, unchanged data
+  // the shared expert's down rows (this wave's K-steps)
   const uint16_t* srow = L.sh_down + (int64_t)(row0 + c) * fs;
   int sk0, sk1;
   split_range(fs / 32, kW3, wave, sk0, sk1);
   constexpr int kBatchS = 4;
   half8_t sa[kBatchS];
-#pragma unroll
-  for (int j = 0; j < kBatchS; ++j) sa[j] = *(const half8_t*)(srow + max(min(sk0 + j, sk1 - 1), 0) * 32 + 8 * q);
-  pin();
   float4_t acc = {0.f, 0.f, 0.f, 0.f};
   // one step: activations of the slot's unit, the request of the unit
   // kRing3 - 1 ahead into the slot freed last step, then the products.
@@ -1179,16 +1180,11 @@ __global__ __launch_bounds__(kW3 * 64) __attribute__((amdgpu_waves_per_eu(4))) v
         if (wave + (m0 + r) * kW3 >= nunits) return;
         if constexpr (P) {
           if (bsb[r] != cur) {  // the next phase (wave-uniform)
-            vm_wait<kLdU>();
+            vm_wait<2 * kLdU>();
             ring_barrier();
             cur = bsb[r];
-            pj = 0;
+            send_phase(min(cur + 1, nb - 1));  // in the last phase: its own chunks again, unchanged data
           }
-          const int pn = min(cur + 1, nb - 1);  // in the last phase: its own chunks again, unchanged data
-          dma_h(pn, wave + kW3 * pj);
-          dma_h(pn, wave + kW3 * (pj + 1));
-          if constexpr (!MX && !Q4) dma_s(pn, wave);
-          pj += 2;
           pin();
         }
         const int slot = sj[r];  // slot of token c for this unit's expert
@@ -1198,8 +1194,12 @@ __global__ __launch_bounds__(kW3 * 64) __attribute__((amdgpu_waves_per_eu(4))) v
         // tokens read zeros, which leaves Q2K products exactly zero (its
         // weights are small integers), while MXFP4 and Q4K weights, scaled
         // in binary16, keep the mask in case a scale overflowed to inf
-        const uint32_t vmask = BL || P || MX || Q4 ? (uint32_t)(__ballot(has) >> (4 * q)) & 15u : 15u;
-        const int row = has ? slot : 0;
+        // Q2K, phased: tokens without a slot (and the min sums of lane
+        // groups q >= 2) read the buffer's zero rows, whose products are
+        // exactly zero, so no mask
+        constexpr bool kZeroRows = P && !MX && !Q4;
+        const uint32_t vmask = (BL || P || MX || Q4) && !kZeroRows ? (uint32_t)(__ballot(has) >> (4 * q)) & 15u : 15u;
+        const int row = has ? slot : (kZeroRows ? S : 0);
         const int b = bsb[r];  // super-block
         Q2kA A;
         auto act = [&]() {
@@ -1211,7 +1211,9 @@ __global__ __launch_bounds__(kW3 * 64) __attribute__((amdgpu_waves_per_eu(4))) v
             } else if constexpr (BL) {
               q2k_act(A, bcol, s_cs + (size_t)row * fs16 + b * 16, s_cs + (size_t)(S + row) * fs16 + b * 16, q);
             } else {
-              q2k_act(A, bcol, ph_cs(b) + (size_t)row * 16, ph_cs(b) + (size_t)(S + row) * 16, q);
+              const bool sm = has && q < 2;  // hi and lo sum rows, else the zero row
+              q2k_act(A, bcol, ph_cs(b) + (size_t)(sm ? row : 2 * S) * 16, ph_cs(b) + (size_t)(sm ? S + row : 2 * S) * 16,
+                      q);
             }
           } else {
             // byte offsets: row * 2f + 2 q2k_boff(q, s2) in the activations,
@@ -1234,7 +1236,7 @@ __global__ __launch_bounds__(kW3 * 64) __attribute__((amdgpu_waves_per_eu(4))) v
         if (BL || P) act();
         if constexpr (Q4) q4k_unit(WQ[r], A, vmask, q, acc);
         else if constexpr (MX) mx4_unit(WM[r], A, vmask, acc);
-        else q2k_unit<BL || P>(W[r], A, vmask, q, acc);
+        else q2k_unit<BL>(W[r], A, vmask, q, acc);
       }
     }
   };
@@ -1242,18 +1244,20 @@ __global__ __launch_bounds__(kW3 * 64) __attribute__((amdgpu_waves_per_eu(4))) v
     routed(std::true_type{});
     // every wave meets every phase's barrier and sends its chunks of each
     while (cur < nb - 1) {
-      for (int j = pj; wave + kW3 * j < ph_hch; ++j) dma_h(cur + 1, wave + kW3 * j);
-      if (!MX && !Q4 && wave < ph_sch) dma_s(cur + 1, wave);
       vm_wait<0>();
       ring_barrier();
       ++cur;
-      pj = 0;
+      send_phase(min(cur + 1, nb - 1));
     }
   } else {
     if constexpr (!PH) routed(std::false_type{});
   }
   // shared expert, transposed like the routed units: lane (c, q) ends with
-  // tokens 4q..4q+3 of row row0 + c
+  // tokens 4q..4q+3 of row row0 + c (its first rows requested here: in
+  // flight during the routed loop they would hold registers it needs)
+#pragma unroll
+  for (int j = 0; j < kBatchS; ++j) sa[j] = *(const half8_t*)(srow + max(min(sk0 + j, sk1 - 1), 0) * 32 + 8 * q);
+  pin();
   float4_t accs = {0.f, 0.f, 0.f, 0.f};
   {
     auto getb = [&](int kk, half8_t& bh, half8_t&) {
@@ -1520,7 +1524,7 @@ hipError_t launch_decode(const Fwd& f) {
   // else one super-block's columns at a time, double-buffered (rows padded
   // as the kernel pads them, its 1 KB sink; at most 4 h and 1 sums copy
   // chunks a wave and phase)
-  const int ph_hrows = (S + 1) & ~1, ph_srows = mx || q4 ? 0 : (2 * S + 31) & ~31;
+  const int ph_hrows = (S + 2) & ~1, ph_srows = mx || q4 ? 0 : (2 * S + 32) & ~31;
   const size_t phase_bytes = (size_t)2 * (ph_hrows * QK * 2 + ph_srows * 32) + 1024;
   const bool ph_fits = phase_bytes <= kStage3Bytes && ph_hrows / 2 <= 4 * kW3 && ph_srows / 32 <= kW3;
   if (stage_bytes <= kStage3Bytes) {

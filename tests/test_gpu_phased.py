@@ -31,7 +31,7 @@ def stage3_mode(T):
     full = Sl * CFG.f * 2 + 2 * Sl * (CFG.f // 16) * 2 + T * CFG.fs * 2
     if full <= 128 * 1024:
         return "full"
-    hrows, srows = (Sl + 1) & ~1, (2 * Sl + 31) & ~31
+    hrows, srows = (Sl + 2) & ~1, (2 * Sl + 32) & ~31  # with the zero rows
     ph = 2 * (hrows * 256 * 2 + srows * 32) + 1024
     return "phased" if ph <= 128 * 1024 and hrows // 2 <= 64 and srows // 32 <= 16 else "unstaged"
 
