@@ -57,7 +57,7 @@ WsLayout ws_layout(const ds4moe_layer& L, int64_t T, int mode) {
     y.hsum = take(S * (f / 16) * 4);
     if (mode == DS4MOE_MODE_PREFILL) y.yp = take(S * d * 4);
     if (mode == DS4MOE_MODE_DECODE) {
-      y.gu_part = take((fs / 16) * 2 * 16 * Tdec * 4);
+      y.gu_part = take((fs / 16) * 2 * kShSplit * 16 * Tdec * 4);
     }
   }
   y.total = o;

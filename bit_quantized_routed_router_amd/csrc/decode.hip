@@ -69,7 +69,43 @@ __host__ __device__ constexpr int q2k_pair_pos(int r) { return 2 * (r & 7) + (r 
 
 __device__ inline int clamp_index(int v, int n) { return (unsigned)v < (unsigned)n ? v : 0; }
 
-// 8 activations x[t][k0 .. k0+7] (bf16 bits or fp32) as binary16 hi and lo parts.
+// 8 activations x[t][k0 .. k0+7] (bf16 bits or fp32), loaded (load_x8_raw)
+// and turned into binary16 hi and lo parts (cvt_x8) as separate steps.
+struct X8Raw {
+  u32x4_t u;    // bf16
+  float4 a, b;  // fp32
+};
+template <bool LO>
+__device__ inline X8Raw load_x8_raw(const void* x, int d, int t, int k0) {
+  X8Raw r;
+  if (!LO) {
+    r.u = *(const u32x4_t*)((const uint16_t*)x + (int64_t)t * d + k0);
+  } else {
+    const float4* src = (const float4*)((const float*)x + (int64_t)t * d + k0);
+    r.a = src[0];
+    r.b = src[1];
+  }
+  return r;
+}
+template <bool LO>
+__device__ inline void cvt_x8(const X8Raw& r, half8_t& h, half8_t& l) {
+  float v[8];
+  if (!LO) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      v[2 * p] = __builtin_bit_cast(float, r.u[p] << 16);
+      v[2 * p + 1] = __builtin_bit_cast(float, r.u[p] & 0xFFFF0000u);
+    }
+  } else {
+    v[0] = r.a.x; v[1] = r.a.y; v[2] = r.a.z; v[3] = r.a.w;
+    v[4] = r.b.x; v[5] = r.b.y; v[6] = r.b.z; v[7] = r.b.w;
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    h[e] = (_Float16)v[e];
+    l[e] = LO ? (_Float16)(v[e] - (float)h[e]) : (_Float16)0.0f;
+  }
+}
 template <bool LO>
 __device__ inline void load_x8(const void* x, int d, int t, int k0, half8_t& h, half8_t& l) {
   float v[8];
@@ -211,16 +247,133 @@ __device__ inline void f16_steps(const uint16_t* __restrict__ rowp, int ks0, int
   }
 }
 
+// Shared expert gate and up, block sb = (tile, part, half): part 0 is the
+// gate, part 1 the up product of 16 rows, over input part `half` of KS;
+// the last of a tile's 2 KS blocks to arrive forms h = silu(g) * u as
+// binary16.  It does not depend on routing: for a group of tokens these
+// blocks run beside the router's (XR: x read as the input itself and
+// turned into binary16 hi/lo parts as the router's blocks do, KS =
+// kShSplit); for one token behind the routed gate/up blocks, whose stream
+// they overlap best (x as the binary16 copy xh, xl the router wrote, staged
+// in LDS (bhs, bls) when BL; KS = 1).  red: the wave reduction, last: one
+// LDS int.
+template <bool LO, bool BL, bool XR, int KS>
+__device__ inline void shared_gateup_block(const ds4moe_layer& L, int T, const void* __restrict__ x,
+                                           const _Float16* __restrict__ xh, const _Float16* __restrict__ xl, int sb,
+                                           float* __restrict__ gu_part, _Float16* __restrict__ hs16,
+                                           int32_t* __restrict__ ctrl, _Float16* bhs, _Float16* bls,
+                                           float4_t (*red)[64], int& last) {
+  static_assert(KS <= kShSplit && !(XR && BL), "shared gate/up block form");
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c = lane & 15, q = lane >> 4;
+  const int tc = min(c, T - 1);  // token feeding MFMA column c
+  const int d = L.d_model, fs = L.d_ff_shared;
+  float4_t acc = {0.f, 0.f, 0.f, 0.f};
+  const int tile = sb / (2 * KS), part = (sb / KS) & 1, half = sb % KS;
+  const uint16_t* rp = (part == 0 ? L.sh_gate : L.sh_up) + (int64_t)(tile * 16 + c) * d;
+  const int nks = d / 32 / KS;  // K-steps of one part
+  int ks0, ks1;
+  split_range(nks, kW, wave, ks0, ks1);
+  ks0 += half * nks;
+  ks1 += half * nks;
+  if constexpr (!XR) {
+    const int st = stage_stride(d);
+    if (BL) dma_rows(xh, d, T, d, bhs, st, wave, kW, lane);
+    if (BL && LO) dma_rows(xl, d, T, d, bls, st, wave, kW, lane);
+    constexpr int kBatch = 16;
+    half8_t a[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) a[j] = *(const half8_t*)(rp + max(min(ks0 + j, ks1 - 1), 0) * 32 + 8 * q);
+    if (BL) {
+      wait_all();
+      __syncthreads();
+    }
+    f16_steps<LO, BL, kBatch>(rp, ks0, ks1, q, a,
+                              [&](int kk, half8_t& bh, half8_t& bl) {
+                                if (BL) {
+                                  bh = *(const half8_t*)(bhs + tc * st + kk);
+                                  if (LO) bl = *(const half8_t*)(bls + tc * st + kk);
+                                } else {
+                                  bh = *(const half8_t*)(xh + (int64_t)tc * d + kk);
+                                  if (LO) bl = *(const half8_t*)(xl + (int64_t)tc * d + kk);
+                                }
+                              },
+                              acc);
+  }
+  // XR: batches of kBatch K-steps, the weights and the raw x of a batch
+  // requested together and waited for once (an x read at its step would
+  // wait behind every weight load requested before it)
+  constexpr int kBatch = 8;
+  for (int ks = ks0; XR && ks < ks1; ks += kBatch) {
+    half8_t a[kBatch];
+    X8Raw xr[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int kk = max(min(ks + j, ks1 - 1), 0) * 32 + 8 * q;
+      a[j] = *(const half8_t*)(rp + kk);
+      xr[j] = load_x8_raw<LO>(x, d, tc, kk);
+    }
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {  // steps past the range multiply a zero A fragment
+      half8_t bh, bl;
+      cvt_x8<LO>(xr[j], bh, bl);
+      const half8_t aj = ks + j < ks1 ? a[j] : zero_half8();
+      acc = mfma16x16x32(aj, bh, acc);
+      if (LO) acc = mfma16x16x32(aj, bl, acc);
+    }
+  }
+  acc = reduce_waves<kW>(acc, red, wave, lane);
+  float* tp = gu_part + (size_t)tile * 2 * KS * 16 * T;  // [part][half][row][t]
+  if (wave == 0) {
+    if (c < T) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) st_coh(&tp[((size_t)(part * KS + half) * 16 + 4 * q + r) * T + c], acc[r]);
+    }
+    wait_stores();
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) last = atomicAdd(&ctrl[1 + tile], 1) == 2 * KS - 1;
+  __syncthreads();
+  if (!last || wave != 0) return;
+  if (c < T) {
+    float pv[2][KS][4];  // [part][half][r]: every coherent load in flight before the first use
+#pragma unroll
+    for (int pt = 0; pt < 2; ++pt)
+#pragma unroll
+      for (int hf = 0; hf < KS; ++hf)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) pv[pt][hf][r] = ld_coh(&tp[((size_t)(pt * KS + hf) * 16 + 4 * q + r) * T + c]);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float g = pv[0][0][r], u = pv[1][0][r];
+#pragma unroll
+      for (int hf = 1; hf < KS; ++hf) {
+        g += pv[0][hf][r];
+        u += pv[1][hf][r];
+      }
+      hs16[(int64_t)c * fs + tile * 16 + 4 * q + r] = (_Float16)(silu(g) * u);
+    }
+  }
+  if (lane == 0) ctrl[1 + tile] = 0;
+}
+
 // One block per (expert tile, input chunk) of the router, chunk-major; the
 // last block to arrive finishes routing.  GRP: a group of tokens (T >= 2),
 // whose finish keeps 4096 logits in LDS and sums eight logits' partials at
-// a time; one token keeps the smaller footprint.
+// a time; one token keeps the smaller footprint.  With GRP, blocks from
+// rblocks on are the shared expert's gate/up blocks.
 template <bool LO, bool GRP>
 __global__ __launch_bounds__(kW * 64) void k_dec_stage1(ds4moe_layer L, int T, const void* __restrict__ x,
                                                         int rblocks, float* __restrict__ plog, RouteOut ro,
                                                         _Float16* __restrict__ xh, _Float16* __restrict__ xl,
+                                                        float* __restrict__ gu_part, _Float16* __restrict__ hs16,
                                                         int32_t* __restrict__ ctrl) {
   __shared__ Stage1Lds<GRP> lds;
+  if (GRP && (int)blockIdx.x >= rblocks) {
+    shared_gateup_block<LO, false, true, kShSplit>(L, T, x, nullptr, nullptr, blockIdx.x - rblocks, gu_part, hs16,
+                                                   ctrl, nullptr, nullptr, lds.red, lds.last);
+    return;
+  }
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = lane & 15, q = lane >> 4;
   const int tc = min(c, T - 1);  // token feeding MFMA column c
@@ -269,72 +422,6 @@ __global__ __launch_bounds__(kW * 64) void k_dec_stage1(ds4moe_layer L, int T, c
     __syncthreads();
     if (lds.last) route_finish_block<true, GRP ? 8 : 1>(lds.route, plog, d / ck, L.router_bias, E, L.top_k, T, ro);
   }
-}
-
-// Shared expert gate and up, block sb = (tile, part): part 0 is the gate,
-// part 1 the up product of 16 rows over the whole input; the second of a
-// tile's two blocks to arrive forms h = silu(g) * u as binary16.  x comes as
-// the binary16 hi/lo copy (xh, xl) that the router blocks wrote; bhs/bls:
-// LDS staging of it when BL, red: the wave reduction, last: one LDS int.
-template <bool LO, bool BL>
-__device__ inline void shared_gateup_block(const ds4moe_layer& L, int T, const _Float16* __restrict__ xh,
-                                           const _Float16* __restrict__ xl, int sb, float* __restrict__ gu_part,
-                                           _Float16* __restrict__ hs16, int32_t* __restrict__ ctrl, _Float16* bhs,
-                                           _Float16* bls, float4_t (*red)[64], int& last) {
-  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int c = lane & 15, q = lane >> 4;
-  const int tc = min(c, T - 1);  // token feeding MFMA column c
-  const int d = L.d_model, fs = L.d_ff_shared;
-  float4_t acc = {0.f, 0.f, 0.f, 0.f};
-  const int tile = sb >> 1, part = sb & 1;
-  const uint16_t* rp = (part == 0 ? L.sh_gate : L.sh_up) + (int64_t)(tile * 16 + c) * d;
-  int ks0, ks1;
-  split_range(d / 32, kW, wave, ks0, ks1);
-  const int st = stage_stride(d);
-  if (BL) dma_rows(xh, d, T, d, bhs, st, wave, kW, lane);
-  if (BL && LO) dma_rows(xl, d, T, d, bls, st, wave, kW, lane);
-  constexpr int kBatch = 16;
-  half8_t a[kBatch];
-#pragma unroll
-  for (int j = 0; j < kBatch; ++j) a[j] = *(const half8_t*)(rp + max(min(ks0 + j, ks1 - 1), 0) * 32 + 8 * q);
-  if (BL) {
-    wait_all();
-    __syncthreads();
-  }
-  f16_steps<LO, BL, kBatch>(rp, ks0, ks1, q, a,
-                            [&](int kk, half8_t& bh, half8_t& bl) {
-                              if (BL) {
-                                bh = *(const half8_t*)(bhs + tc * st + kk);
-                                if (LO) bl = *(const half8_t*)(bls + tc * st + kk);
-                              } else {
-                                bh = *(const half8_t*)(xh + (int64_t)tc * d + kk);
-                                if (LO) bl = *(const half8_t*)(xl + (int64_t)tc * d + kk);
-                              }
-                            },
-                            acc);
-  acc = reduce_waves<kW>(acc, red, wave, lane);
-  float* tp = gu_part + (size_t)tile * 2 * 16 * T;  // [part][row][t]
-  if (wave == 0) {
-    if (c < T) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) st_coh(&tp[((size_t)part * 16 + 4 * q + r) * T + c], acc[r]);
-    }
-    wait_stores();
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) last = atomicAdd(&ctrl[1 + tile], 1) == 1;
-  __syncthreads();
-  if (!last || wave != 0) return;
-  if (c < T) {
-    float pv[2][4];  // [part][r]: every coherent load in flight before the first use
-#pragma unroll
-    for (int pt = 0; pt < 2; ++pt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) pv[pt][r] = ld_coh(&tp[((size_t)pt * 16 + 4 * q + r) * T + c]);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) hs16[(int64_t)c * fs + tile * 16 + 4 * q + r] = (_Float16)(silu(pv[0][r]) * pv[1][r]);
-  }
-  if (lane == 0) ctrl[1 + tile] = 0;
 }
 
 // ============================================================== stage 2
@@ -439,6 +526,8 @@ __device__ void routed_gateup_mx(const ds4moe_layer& L, int T, const RouteOut& r
                                  const _Float16* __restrict__ xl, _Float16* __restrict__ hw16,
                                  Stage2Lds<LO, BL, NS>& lds);
 
+// Blocks from rtiles on (launched for one token) are the shared expert's
+// gate/up blocks.
 template <bool LO, bool BL, bool MX, bool Q4 = false, int NS = kStageHalves>
 __global__ __launch_bounds__(kW * 64) __attribute__((amdgpu_waves_per_eu(stage2_waves(LO, BL, NS)))) void k_dec_stage2(
     ds4moe_layer L, int T, RouteOut ro, const _Float16* __restrict__ xh,
@@ -446,8 +535,8 @@ __global__ __launch_bounds__(kW * 64) __attribute__((amdgpu_waves_per_eu(stage2_
     float* __restrict__ gu_part, _Float16* __restrict__ hs16, int32_t* __restrict__ ctrl) {
   __shared__ Stage2Lds<LO, BL, NS> lds;
   if ((int)blockIdx.x >= rtiles) {
-    shared_gateup_block<LO, BL>(L, T, xh, xl, blockIdx.x - rtiles, gu_part, hs16, ctrl, lds.bh, lds.bl, lds.red,
-                                lds.last);
+    shared_gateup_block<LO, BL, false, 1>(L, T, nullptr, xh, xl, blockIdx.x - rtiles, gu_part, hs16, ctrl, lds.bh,
+                                          lds.bl, lds.red, lds.last);
     return;
   }
   if constexpr (MX || Q4) {
@@ -1462,12 +1551,20 @@ static void launch_stages12(const Fwd& f, int rblocks, int nsh, int maxd, int nr
   auto hw16 = (_Float16*)(ws + y.hw16);
   auto hsum = (_Float16*)(ws + y.hsum);
   const dim3 blk(kW * 64);
-  if (T > 1)
-    DS4_LAUNCH((k_dec_stage1<LO, true>), dim3(rblocks), blk, 0, f.st, L, T, f.x, rblocks, plog, ro, xh, xl, ctrl);
-  else
-    DS4_LAUNCH((k_dec_stage1<LO, false>), dim3(rblocks), blk, 0, f.st, L, T, f.x, rblocks, plog, ro, xh, xl, ctrl);
-  DS4_LAUNCH((k_dec_stage2<LO, BL, MX, Q4, NS>), dim3(maxd * nr + 2 * nsh), blk, 0, f.st, L, T, ro, xh, xl, hw16,
-             hsum, maxd * nr, gu, hs16, ctrl);
+  // the shared expert's gate/up blocks: for a group of tokens behind the
+  // router's in stage 1 (its 2 MB leave the chip idle), for one token behind
+  // the routed gate/up blocks of stage 2 (whose stream they overlap best)
+  if (T > 1) {
+    DS4_LAUNCH((k_dec_stage1<LO, true>), dim3(rblocks + 2 * kShSplit * nsh), blk, 0, f.st, L, T, f.x, rblocks, plog,
+               ro, xh, xl, gu, hs16, ctrl);
+    DS4_LAUNCH((k_dec_stage2<LO, BL, MX, Q4, NS>), dim3(maxd * nr), blk, 0, f.st, L, T, ro, xh, xl, hw16, hsum,
+               maxd * nr, gu, hs16, ctrl);
+  } else {
+    DS4_LAUNCH((k_dec_stage1<LO, false>), dim3(rblocks), blk, 0, f.st, L, T, f.x, rblocks, plog, ro, xh, xl, gu, hs16,
+               ctrl);
+    DS4_LAUNCH((k_dec_stage2<LO, BL, MX, Q4, NS>), dim3(maxd * nr + 2 * nsh), blk, 0, f.st, L, T, ro, xh, xl, hw16,
+               hsum, maxd * nr, gu, hs16, ctrl);
+  }
 }
 
 hipError_t launch_decode(const Fwd& f) {
