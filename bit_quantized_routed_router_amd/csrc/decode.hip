@@ -1193,7 +1193,16 @@ __global__ __launch_bounds__(kW3 * 64) __attribute__((amdgpu_waves_per_eu(4))) v
   int pmaj = wave / nmin, pmin = wave - (wave / nmin) * nmin;
   auto load_unit = [&](int r) {  // r: ring slot, fixed once unrolled
     int i = PH ? pmin : pmaj, b = PH ? pmaj : pmin;
-    if (PH ? b >= nb : i >= nd) {  // units past the end repeat the last one
+    if (!PH && i >= nd) {  // past the end and never computed: no loads
+      pmaj += dmaj;
+      pmin += dmin;
+      if (pmin >= nmin) {
+        pmin -= nmin;
+        ++pmaj;
+      }
+      return;
+    }
+    if (PH && b >= nb) {  // past the end: the last unit again (the phased walk sends a fixed count)
       i = nd - 1;
       b = nb - 1;
     }
@@ -1255,6 +1264,14 @@ __global__ __launch_bounds__(kW3 * 64) __attribute__((amdgpu_waves_per_eu(4))) v
   split_range(fs / 32, kW3, wave, sk0, sk1);
   constexpr int kBatchS = 4;
   half8_t sa[kBatchS];
+  auto load_sa = [&]() {
+#pragma unroll
+    for (int j = 0; j < kBatchS; ++j) sa[j] = *(const half8_t*)(srow + max(min(sk0 + j, sk1 - 1), 0) * 32 + 8 * q);
+    pin();
+  };
+  // they stream in while the routed units compute, except in the phased
+  // form, where their registers are worth more to the routed loop
+  if constexpr (!PH) load_sa();
   float4_t acc = {0.f, 0.f, 0.f, 0.f};
   // one step: activations of the slot's unit, the request of the unit
   // kRing3 - 1 ahead into the slot freed last step, then the products.
@@ -1342,11 +1359,8 @@ __global__ __launch_bounds__(kW3 * 64) __attribute__((amdgpu_waves_per_eu(4))) v
     if constexpr (!PH) routed(std::false_type{});
   }
   // shared expert, transposed like the routed units: lane (c, q) ends with
-  // tokens 4q..4q+3 of row row0 + c (its first rows requested here: in
-  // flight during the routed loop they would hold registers it needs)
-#pragma unroll
-  for (int j = 0; j < kBatchS; ++j) sa[j] = *(const half8_t*)(srow + max(min(sk0 + j, sk1 - 1), 0) * 32 + 8 * q);
-  pin();
+  // tokens 4q..4q+3 of row row0 + c
+  if constexpr (PH) load_sa();
   float4_t accs = {0.f, 0.f, 0.f, 0.f};
   {
     auto getb = [&](int kk, half8_t& bh, half8_t&) {
