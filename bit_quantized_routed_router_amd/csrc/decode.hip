@@ -252,11 +252,11 @@ __device__ inline void f16_steps(const uint16_t* __restrict__ rowp, int ks0, int
 // the last of a tile's 2 KS blocks to arrive forms h = silu(g) * u as
 // binary16.  It does not depend on routing: for a group of tokens these
 // blocks run beside the router's (XR: x read as the input itself and
-// turned into binary16 hi/lo parts as the router's blocks do, KS =
-// kShSplit); for one token behind the routed gate/up blocks, whose stream
-// they overlap best (x as the binary16 copy xh, xl the router wrote, staged
-// in LDS (bhs, bls) when BL; KS = 1).  red: the wave reduction, last: one
-// LDS int.
+// turned into binary16 hi/lo parts as the router's blocks do); for one
+// token behind the routed gate/up blocks, whose stream they overlap best (x
+// as the binary16 copy xh, xl the router wrote, staged in LDS (bhs, bls)
+// when BL).  KS = kShSplit: a wave's K-steps are one batch of loads at
+// d_model 4096.  red: the wave reduction, last: one LDS int.
 template <bool LO, bool BL, bool XR, int KS>
 __device__ inline void shared_gateup_block(const ds4moe_layer& L, int T, const void* __restrict__ x,
                                            const _Float16* __restrict__ xh, const _Float16* __restrict__ xl, int sb,
@@ -535,8 +535,8 @@ __global__ __launch_bounds__(kW * 64) __attribute__((amdgpu_waves_per_eu(stage2_
     float* __restrict__ gu_part, _Float16* __restrict__ hs16, int32_t* __restrict__ ctrl) {
   __shared__ Stage2Lds<LO, BL, NS> lds;
   if ((int)blockIdx.x >= rtiles) {
-    shared_gateup_block<LO, BL, false, 1>(L, T, nullptr, xh, xl, blockIdx.x - rtiles, gu_part, hs16, ctrl, lds.bh,
-                                          lds.bl, lds.red, lds.last);
+    shared_gateup_block<LO, BL, false, kShSplit>(L, T, nullptr, xh, xl, blockIdx.x - rtiles, gu_part, hs16, ctrl,
+                                                 lds.bh, lds.bl, lds.red, lds.last);
     return;
   }
   if constexpr (MX || Q4) {
@@ -1576,8 +1576,8 @@ static void launch_stages12(const Fwd& f, int rblocks, int nsh, int maxd, int nr
   } else {
     DS4_LAUNCH((k_dec_stage1<LO, false>), dim3(rblocks), blk, 0, f.st, L, T, f.x, rblocks, plog, ro, xh, xl, gu, hs16,
                ctrl);
-    DS4_LAUNCH((k_dec_stage2<LO, BL, MX, Q4, NS>), dim3(maxd * nr + 2 * nsh), blk, 0, f.st, L, T, ro, xh, xl, hw16,
-               hsum, maxd * nr, gu, hs16, ctrl);
+    DS4_LAUNCH((k_dec_stage2<LO, BL, MX, Q4, NS>), dim3(maxd * nr + 2 * kShSplit * nsh), blk, 0, f.st, L, T, ro, xh,
+               xl, hw16, hsum, maxd * nr, gu, hs16, ctrl);
   }
 }
 

@@ -45,9 +45,8 @@ WsLayout ws_layout(const ds4moe_layer& L, int64_t T, int mode);
 // start zeroed.
 constexpr int kCtrlInts = 1 + kMaxDim / 16;
 inline int ctrl_ints(const ds4moe_layer& L) { return 1 + L.d_ff_shared / 16; }  // router + shared tiles
-// decode, groups of tokens: blocks a shared-expert gate or up row tile is
-// split into along its input (contiguous parts), so that a wave has few
-// K-steps to load at once
+// decode: blocks a shared-expert gate or up row tile is split into along its
+// input (contiguous parts), so that a wave has few K-steps to load at once
 constexpr int kShSplit = 2;
 
 // Everything a forward launch needs, resolved on the host.
