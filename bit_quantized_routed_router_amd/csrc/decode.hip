@@ -360,9 +360,11 @@ __device__ inline void shared_gateup_block(const ds4moe_layer& L, int T, const v
 // One block per (expert tile, input chunk) of the router, chunk-major; the
 // last block to arrive finishes routing.  GRP: a group of tokens (T >= 2),
 // whose finish keeps 4096 logits in LDS and sums eight logits' partials at
-// a time; one token keeps the smaller footprint.  With GRP, blocks from
-// rblocks on are the shared expert's gate/up blocks.
-template <bool LO, bool GRP>
+// a time (KLF; 16 for large groups, whose partials then all go out in one
+// pass at the cost of the kernel's register budget); one token keeps the
+// smaller footprint.  With GRP, blocks from rblocks on are the shared
+// expert's gate/up blocks.
+template <bool LO, bool GRP, int KLF = GRP ? 8 : 1>
 __global__ __launch_bounds__(kW * 64) void k_dec_stage1(ds4moe_layer L, int T, const void* __restrict__ x,
                                                         int rblocks, float* __restrict__ plog, RouteOut ro,
                                                         _Float16* __restrict__ xh, _Float16* __restrict__ xl,
@@ -420,7 +422,7 @@ __global__ __launch_bounds__(kW * 64) void k_dec_stage1(ds4moe_layer L, int T, c
     __syncthreads();
     if (threadIdx.x == 0) lds.last = atomicAdd(&ctrl[0], 1) == rblocks - 1;  // cleared by stage 3
     __syncthreads();
-    if (lds.last) route_finish_block<true, GRP ? 8 : 1>(lds.route, plog, d / ck, L.router_bias, E, L.top_k, T, ro);
+    if (lds.last) route_finish_block<true, KLF>(lds.route, plog, d / ck, L.router_bias, E, L.top_k, T, ro);
   }
 }
 
@@ -1568,7 +1570,12 @@ static void launch_stages12(const Fwd& f, int rblocks, int nsh, int maxd, int nr
   // the shared expert's gate/up blocks: for a group of tokens behind the
   // router's in stage 1 (its 2 MB leave the chip idle), for one token behind
   // the routed gate/up blocks of stage 2 (whose stream they overlap best)
-  if (T > 1) {
+  if (T >= 12) {  // the finish sums 16 logits' partials at a time
+    DS4_LAUNCH((k_dec_stage1<LO, true, 16>), dim3(rblocks + 2 * kShSplit * nsh), blk, 0, f.st, L, T, f.x, rblocks,
+               plog, ro, xh, xl, gu, hs16, ctrl);
+    DS4_LAUNCH((k_dec_stage2<LO, BL, MX, Q4, NS>), dim3(maxd * nr), blk, 0, f.st, L, T, ro, xh, xl, hw16, hsum,
+               maxd * nr, gu, hs16, ctrl);
+  } else if (T > 1) {
     DS4_LAUNCH((k_dec_stage1<LO, true>), dim3(rblocks + 2 * kShSplit * nsh), blk, 0, f.st, L, T, f.x, rblocks, plog,
                ro, xh, xl, gu, hs16, ctrl);
     DS4_LAUNCH((k_dec_stage2<LO, BL, MX, Q4, NS>), dim3(maxd * nr), blk, 0, f.st, L, T, ro, xh, xl, hw16, hsum,
