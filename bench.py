@@ -60,8 +60,8 @@ METRIC = "routed-MoE layer decode tok/s + % HBM peak; 2048-tok prefill tok/s + %
 # 128-byte request at 128 bytes) and WRITE_SIZE, both checked against a
 # 256 MiB device copy (factor 1.000); valid for the kernel sources with this
 # hash only (profiles/decode_hbm_traffic.md holds the commands and counts).
-TRAFFIC_SOURCE_HASH = "e8af9ed5446c50bb"
-TRAFFIC_BYTES = {"k_dec_stage1": 2.26e6, "k_dec_stage2": 60.03e6, "k_dec_stage3": 33.60e6}
+TRAFFIC_SOURCE_HASH = "2f97323b2e9606f4"
+TRAFFIC_BYTES = {"k_dec_stage1": 2.26e6, "k_dec_stage2": 60.09e6, "k_dec_stage3": 33.60e6}
 
 
 def kernel_source_hash(csrc=None):

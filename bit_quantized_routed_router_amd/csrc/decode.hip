@@ -436,10 +436,18 @@ constexpr int kSbRows = kDecodeGroup * kSbRow;
 // wave stages the super-block it is about to decode (xw, xwl).
 // NS: binary16 activations the block stages when BL (T rows of d_model,
 // each padded by 8 halves, T <= 16).
+// Codebook form of a routed CB2 gate/up kernel: byte tables (half the LDS
+// bytes, two byte permutes more per weight pair) for groups of tokens, whose
+// gate/up is bound by LDS reads; binary16 pairs for the one-token form,
+// whose decode hides behind its weight stream.
+template <bool BL, int NS>
+constexpr bool cb2_bytes() { return !BL || NS != kStageHalves; }
+
 template <bool LO, bool BL, int NS = kStageHalves>
 struct Stage2Lds {
-  uint32_t mag[256 * 4];
-  uint32_t sgn[128 * 4];
+  static constexpr int kEnt = cb2_bytes<BL, NS>() ? 2 : 4;  // words per table entry
+  uint32_t mag[256 * kEnt];  // sgn right after mag
+  uint32_t sgn[128 * kEnt];
   _Float16 bh[BL ? NS + 16 * 8 : 8];
   _Float16 bl[BL && LO ? NS + 16 * 8 : 8];
   _Float16 xw[BL ? 8 : kW * kSbRows];
@@ -452,28 +460,47 @@ struct Stage2Lds {
 constexpr int kSb2 = 4;  // CB2 super-blocks a wave loads at once
 
 // One CB2 group's codebook entries, read ahead of their use: magnitudes and
-// sign masks of the 8 weights (binary16 bit patterns).
+// signs of the 8 weights.  B8 (byte form): byte k is the high byte of
+// binary16 m_k (its low byte is zero for m in {1, 3, 5}), and 0x80 in the
+// sign entry's byte k if weight k is negative.  Else binary16 pairs and
+// their sign masks (bits 15 and 31).
+template <bool B8>
 struct Cb2Raw {
-  u32x4_t m, s;
+  using V = std::conditional_t<B8, u32x2_t, u32x4_t>;
+  V m, s;
 };
+template <bool B8>
 struct Cb2Step {  // one sub-block step of a routed gate/up wave
-  Cb2Raw g, u;
+  Cb2Raw<B8> g, u;
   half8_t bh, bl;
 };
-__device__ inline void cb2_lookup(Cb2Raw& R, uint32_t idxw, uint32_t aux, int q, const uint32_t* mag,
+template <bool B8>
+__device__ inline void cb2_lookup(Cb2Raw<B8>& R, uint32_t idxw, uint32_t aux, int q, const uint32_t* mag,
                                   const uint32_t* sgn) {
-  R.m = *(const u32x4_t*)(mag + 4 * ((idxw >> (8 * q)) & 0xFFu));
-  R.s = *(const u32x4_t*)(sgn + 4 * ((aux >> (7 * q)) & 0x7Fu));
+  using V = typename Cb2Raw<B8>::V;
+  constexpr int kEnt = B8 ? 2 : 4;
+  R.m = *(const V*)(mag + kEnt * ((idxw >> (8 * q)) & 0xFFu));
+  R.s = *(const V*)(sgn + kEnt * ((aux >> (7 * q)) & 0x7Fu));
 }
 // sign * (2s+1) * m as binary16 (exact integers <= 155), s from aux bits 28..31
-__device__ inline half8_t cb2_apply(const Cb2Raw& R, uint32_t aux) {
+template <bool B8>
+__device__ inline half8_t cb2_apply(const Cb2Raw<B8>& R, uint32_t aux) {
   const _Float16 S = (_Float16)(float)(2 * (aux >> 28) + 1);
   const half2_t S2 = {S, S};
   u32x4_t r;
-  r.x = as_u32(as_half2(R.m.x ^ R.s.x) * S2);
-  r.y = as_u32(as_half2(R.m.y ^ R.s.y) * S2);
-  r.z = as_u32(as_half2(R.m.z ^ R.s.z) * S2);
-  r.w = as_u32(as_half2(R.m.w ^ R.s.w) * S2);
+  if constexpr (B8) {
+    const uint32_t b0 = R.m.x ^ R.s.x, b1 = R.m.y ^ R.s.y;
+    // bytes 2p, 2p + 1 -> high bytes of a binary16 pair (selector 0x0C: zero)
+    r.x = as_u32(as_half2(__builtin_amdgcn_perm(0u, b0, 0x010C000Cu)) * S2);
+    r.y = as_u32(as_half2(__builtin_amdgcn_perm(0u, b0, 0x030C020Cu)) * S2);
+    r.z = as_u32(as_half2(__builtin_amdgcn_perm(0u, b1, 0x010C000Cu)) * S2);
+    r.w = as_u32(as_half2(__builtin_amdgcn_perm(0u, b1, 0x030C020Cu)) * S2);
+  } else {
+    r.x = as_u32(as_half2(R.m.x ^ R.s.x) * S2);
+    r.y = as_u32(as_half2(R.m.y ^ R.s.y) * S2);
+    r.z = as_u32(as_half2(R.m.z ^ R.s.z) * S2);
+    r.w = as_u32(as_half2(R.m.w ^ R.s.w) * S2);
+  }
   return as_half8(r);
 }
 
@@ -559,7 +586,11 @@ __global__ __launch_bounds__(kW * 64) __attribute__((amdgpu_waves_per_eu(stage2_
   const int st = stage_stride(d);
   if (BL) dma_rows(xh, d, T, d, lds.bh, st, wave, kW, lane);
   if (BL && LO) dma_rows(xl, d, T, d, lds.bl, st, wave, kW, lane);
-  dma_pieces(&c_dec_tables.mag[0][0], 384, lds.mag, wave, kW, lane);  // mag (256 pieces), then sgn
+  constexpr bool B8 = cb2_bytes<BL, NS>();
+  static_assert(offsetof(GridTables, sgn) == sizeof(GridTables::mag) &&
+                offsetof(GridTables, sgn8) == offsetof(GridTables, mag8) + sizeof(GridTables::mag8));
+  // mag, then sgn (in 16-byte pieces: 256 + 128, or 128 + 64 in byte form)
+  dma_pieces(B8 ? &c_dec_tables.mag8[0][0] : &c_dec_tables.mag[0][0], B8 ? 192 : 384, lds.mag, wave, kW, lane);
   // phase 2: routing tables by scalar loads, which do not wait for the
   // copies: the first weight batch goes out while they are in flight
   const int nd = ld_uniform(ro.ndist);
@@ -659,8 +690,8 @@ __global__ __launch_bounds__(kW * 64) __attribute__((amdgpu_waves_per_eu(stage2_
         pin();
         const _Float16* xj = xw + (whole ? j * ntok * kSbRow : 0);
         const _Float16* xjl = LO ? xwl + (whole ? j * ntok * kSbRow : 0) : nullptr;
-        Cb2Step F[2];
-        auto fetch = [&](Cb2Step& G, int s2) {
+        Cb2Step<B8> F[2];
+        auto fetch = [&](Cb2Step<B8>& G, int s2) {
           const int kk = cb2_boff(q, s2);
           G.bh = *(const half8_t*)(xj + tcx * kSbRow + kk);
           if (LO) G.bl = *(const half8_t*)(xjl + tcx * kSbRow + kk);
@@ -673,7 +704,7 @@ __global__ __launch_bounds__(kW * 64) __attribute__((amdgpu_waves_per_eu(stage2_
         for (int s2 = 0; s2 < 8; ++s2) {
           if (s2 + 1 < 8) fetch(F[(s2 + 1) & 1], s2 + 1);
           pin();
-          const Cb2Step& G = F[s2 & 1];
+          const Cb2Step<B8>& G = F[s2 & 1];
           const half8_t a0 = cb2_apply(G.g, (s2 & 4) ? cg[j].w : cg[j].y);
           const half8_t a1 = cb2_apply(G.u, (s2 & 4) ? cu[j].w : cu[j].y);
           pg = mfma16x16x32(G.bh, a0, pg);
@@ -697,8 +728,8 @@ __global__ __launch_bounds__(kW * 64) __attribute__((amdgpu_waves_per_eu(stage2_
     pin();
     // 8 steps per super-block (one per sub-block); each step's LDS reads
     // (activations, codebook magnitudes and signs) are issued one step ahead
-    Cb2Step F[2];
-    auto fetch = [&](Cb2Step& G, int t) {
+    Cb2Step<B8> F[2];
+    auto fetch = [&](Cb2Step<B8>& G, int t) {
       const int j = t >> 3, s2 = t & 7;
       const int kk = min(b0 + j, sb1 - 1) * QK + cb2_boff(q, s2);
       if (BL) {
@@ -717,7 +748,7 @@ __global__ __launch_bounds__(kW * 64) __attribute__((amdgpu_waves_per_eu(stage2_
     for (int t = 0; t < 8 * kSb2; ++t) {
       if (t + 1 < 8 * kSb2) fetch(F[(t + 1) & 1], t + 1);
       pin();
-      const Cb2Step& G = F[t & 1];
+      const Cb2Step<B8>& G = F[t & 1];
       const int j = t >> 3, s2 = t & 7;
       const half8_t a0 = cb2_apply(G.g, (s2 & 4) ? cg[j].w : cg[j].y);
       const half8_t a1 = cb2_apply(G.u, (s2 & 4) ? cu[j].w : cu[j].y);
