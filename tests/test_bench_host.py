@@ -55,3 +55,20 @@ def test_bench_refuses_more_than_one_gpu():
                        text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_profiles_and_traffic_figure_name_one_source_hash():
+    """The rocprofv3 summaries under profiles/ and the HBM traffic figure in
+    bench.py come from one set of kernel sources: every summary names the
+    same source hash, and it is the hash the traffic figure was taken at."""
+    import re
+    pdir = os.path.join(bench.ROOT, "profiles")
+    hashes = {}
+    for name in sorted(os.listdir(pdir)):
+        if name.endswith(".md"):
+            m = re.search(r"Kernel source hash \(bit_quantized_routed_router_amd/csrc\): `([0-9a-f]{16})`",
+                          open(os.path.join(pdir, name)).read())
+            assert m, f"{name} names no kernel source hash"
+            hashes[name] = m.group(1)
+    assert hashes and len(set(hashes.values())) == 1, hashes
+    assert set(hashes.values()) == {bench.TRAFFIC_SOURCE_HASH}
